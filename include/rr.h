@@ -1,0 +1,226 @@
+/*
+ * rr.h -- deterministic row reductions on AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels.  Three operations:
+ *
+ *   rr_reduce_rows       sum / max / min of every row over its last axis, on
+ *                        float32 or int32 values, through one of five tiers
+ *                        (wave, block, tiled, serial, split-K).
+ *   rr_softmax_rows      two-pass softmax of every row (pass 1: the online
+ *                        (max, sum) monoid; pass 2: a map that writes y).
+ *   rr_splitk_lse_merge  combine P split-K partial attention outputs by their
+ *                        per-row (max, sum) statistics into bf16 or f32 rows.
+ *
+ * Sources (Modular API pages, cited by title and section):
+ *   "reduce" (algorithm.gpu.rowwise): the tier semantics list and the
+ *       state-carrying overload -- a monoid state folded along the reduce
+ *       axis, and the two-pass softmax whose second pass is a pure map.
+ *   "cluster_allreduce": description and Parameters -- a combine_fn that is an
+ *       associative add/max/min over 32-bit elements, and a cross-group fold
+ *       that visits peers in rank order so every run gives the same bits.
+ *   "fa4_splitk_reduce_scatter_write": the per-band steps -- each partition's
+ *       output is scaled by its weight, the partitions are accumulated, and
+ *       the result is packed to bf16; every partition, empty or not, joins.
+ *
+ * Conventions for every call below
+ *   - Pointers named x, y, o_part, m_part, l_part, out and workspace are
+ *     DEVICE pointers on the current HIP device.  The caller owns them.  The
+ *     library never allocates or frees device memory and never synchronises.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every launch is asynchronous on that stream.
+ *   - Arguments are validated before any launch: on any error status nothing
+ *     has been launched and no output byte has been written.  After a launch
+ *     the HIP launch status is checked and reported as RR_ERR_HIP.
+ *   - Rows are laid out with a stride `ld` (in elements) between row starts;
+ *     the last axis is contiguous (stride 1).  128-bit vector loads are used
+ *     when the base pointer is 16-byte aligned and ld * element size is a
+ *     multiple of 16; otherwise the same kernels run with scalar loads.
+ *   - Results are bit-identical from run to run for the same device, shape,
+ *     strides, alignment, tier and library build.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef RR_H
+#define RR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RR_VERSION 1
+
+typedef enum {
+    RR_OK = 0,
+    RR_ERR_NULL = 1,      /* a required pointer is NULL */
+    RR_ERR_SHAPE = 2,     /* negative size, ld < cols, P out of range, ... */
+    RR_ERR_DTYPE = 3,     /* unsupported dtype or dtype combination */
+    RR_ERR_TIER = 4,      /* forced tier is not legal for this shape / kind */
+    RR_ERR_WORKSPACE = 5, /* split-K workspace missing or too small */
+    RR_ERR_HIP = 6,       /* a HIP runtime call or launch failed */
+    RR_ERR_OP = 7         /* unknown reduction op */
+} rr_status;
+
+typedef enum { RR_F32 = 0, RR_I32 = 1, RR_BF16 = 2 } rr_dtype;
+
+typedef enum { RR_SUM = 0, RR_MAX = 1, RR_MIN = 2 } rr_op;
+
+/* Tiers of "reduce" (algorithm.gpu.rowwise), tier semantics. */
+typedef enum {
+    RR_TIER_AUTO = 0,   /* pick by the rule documented at rr_plan_reduce */
+    RR_TIER_WAVE = 1,   /* a group of lanes of one 64-wide wavefront per row (cols <= 64) */
+    RR_TIER_BLOCK = 2,  /* one workgroup per row, strided 128-bit loads */
+    RR_TIER_TILED = 3,  /* one thread owns RR_TILED_ROWS adjacent rows, no cross-thread combine */
+    RR_TIER_SERIAL = 4, /* one thread per row, element by element */
+    RR_TIER_SPLITK = 5  /* several workgroups per row, rank-order fold of partials */
+} rr_tier;
+
+typedef enum { RR_KIND_REDUCE = 0, RR_KIND_SOFTMAX = 1 } rr_kind;
+
+/* Rows owned by one thread in the tiled tier (the page's emit_tile_width). */
+#define RR_TILED_ROWS 4
+/* Largest partition count accepted by rr_splitk_lse_merge. */
+#define RR_MERGE_MAX_P 256
+
+/*
+ * Launch plan: what the library will run for a shape.  Host-only, no device
+ * work; filled by rr_plan_reduce / rr_plan_softmax.
+ */
+typedef struct {
+    int32_t tier;            /* rr_tier actually used (never RR_TIER_AUTO) */
+    int32_t block;           /* threads per workgroup */
+    int64_t grid;            /* workgroups launched */
+    int32_t lanes_per_row;   /* wave tier: lanes that share one row; else 0 */
+    int32_t slices;          /* split-K: workgroups per row (G); else 1 */
+    int64_t slice_cols;      /* split-K: columns per slice (last slice may be shorter) */
+    uint64_t workspace_bytes;/* bytes of workspace the call needs (0 if none) */
+} rr_plan;
+
+/*
+ * rr_plan_reduce -- tier selection and launch geometry for rr_reduce_rows.
+ * Pure host computation (no HIP call), deterministic in its arguments.
+ * cu_count is the device's compute-unit count (256 on MI355X).
+ *
+ * "reduce" (algorithm.gpu.rowwise), tier semantics, gives each tier's shape
+ * of work but no thresholds; this library picks, first match wins:
+ *   forced tier (if legal for the shape)
+ *   SPLITK  if rows < cu_count and cols >= 65536
+ *   TILED   if cols <= 8
+ *   WAVE    if cols <= 64
+ *   BLOCK   otherwise
+ * SERIAL is used only when forced.  WAVE is legal for cols <= 64 only.
+ * SPLITK: G = clamp(ceil(4*cu_count/rows), 1, min(256, ceil(cols/16384))).
+ * Returns RR_ERR_SHAPE for negative sizes or ld < cols, RR_ERR_DTYPE/OP for
+ * unsupported dtype/op, RR_ERR_TIER for an illegal forced tier.
+ */
+rr_status rr_plan_reduce(int64_t rows, int64_t cols, int64_t ld, rr_dtype dtype, rr_op op,
+                         rr_tier tier, int32_t cu_count, rr_plan* plan_out);
+
+/*
+ * rr_plan_softmax -- tier selection for rr_softmax_rows (same rule as reduce
+ * without SPLITK, which is rejected with RR_ERR_TIER).
+ */
+rr_status rr_plan_softmax(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype y_dtype,
+                          rr_tier tier, int32_t cu_count, rr_plan* plan_out);
+
+/*
+ * rr_reduce_rows -- y[r] = fold of x[r*ld + 0 .. r*ld + cols-1].
+ * "reduce" (algorithm.gpu.rowwise), state-carrying overload and tier
+ * semantics; "cluster_allreduce", description (rank-order fold).
+ *
+ *   x      device, [rows][ld] of dtype (cols elements of each row are read)
+ *   y      device, [rows] of dtype (written)
+ *   dtype  RR_F32 or RR_I32 (same type in and out)
+ *   op     RR_SUM, RR_MAX or RR_MIN
+ *   tier   RR_TIER_AUTO or a forced tier
+ *   workspace, workspace_bytes
+ *          device scratch for RR_TIER_SPLITK (ignored otherwise; may be NULL
+ *          when the plan needs 0 bytes).  Size: rr_workspace_bytes.  It must
+ *          hold zeros before its first use; every completed call leaves it
+ *          zero again.  One workspace must not serve two calls in flight.
+ *
+ * Arithmetic: float SUM accumulates in double and rounds once to float
+ * (nearest even); int32 SUM wraps modulo 2^32; MAX/MIN on float use the
+ * IEEE 754 totalOrder (-0 < +0, NaNs ordered by sign and payload); cols == 0
+ * writes the identity (0, -inf / INT32_MIN for MAX, +inf / INT32_MAX for MIN).
+ * The split-K tier writes one partial per (row, slice) into the workspace and
+ * the last workgroup of a row to arrive folds the partials in ascending slice
+ * order, so the result does not depend on arrival order.
+ * rows == 0 is a no-op.
+ */
+rr_status rr_reduce_rows(const void* x, void* y, int64_t rows, int64_t cols, int64_t ld,
+                         rr_dtype dtype, rr_op op, rr_tier tier, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
+ * rr_softmax_rows -- y[r][j] = exp(x[r][j] - m_r) / s_r with
+ * m_r = max_j x[r][j] and s_r = sum_j exp(x[r][j] - m_r).
+ * "reduce" (algorithm.gpu.rowwise), description: pass 1 folds the online
+ * (max, sum) monoid, pass 2 is a pure map that writes y.
+ *
+ *   x        device, [rows][ld_x] of x_dtype (RR_BF16 or RR_F32)
+ *   y        device, [rows][ld_y] of y_dtype (RR_BF16 or RR_F32)
+ *   tier     RR_TIER_AUTO, WAVE, BLOCK, TILED or SERIAL
+ * Arithmetic in float32; bf16 results are rounded to nearest even.  y may
+ * alias x only when ld_y == ld_x and the dtypes match.  cols == 0 or
+ * rows == 0 is a no-op.
+ */
+rr_status rr_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols, int64_t ld_x,
+                          int64_t ld_y, rr_dtype x_dtype, rr_dtype y_dtype, rr_tier tier,
+                          void* stream);
+
+/*
+ * rr_splitk_lse_merge -- combine P split-K partitions of an attention output.
+ * "fa4_splitk_reduce_scatter_write", the per-band steps: each partition's
+ * output is scaled by its weight w[b], the partitions are accumulated, and
+ * the result is packed to bf16; every partition joins, empty or not.
+ *
+ *   o_part  device, float32 [P][rows][depth]: partition p's NORMALISED output
+ *           O_p (already divided by its own l_p)
+ *   m_part  device, float32 [P][rows]: row max m_p of partition p's scores
+ *   l_part  device, float32 [P][rows]: row sum l_p = sum exp(score - m_p)
+ *   out     device, [rows][depth] of out_dtype (RR_BF16 or RR_F32)
+ *   P       1 .. RR_MERGE_MAX_P;  rows >= 0;  depth >= 1
+ *   scale   multiplies (m_p - M) inside the exponent (1.0 when m_p are
+ *           already in natural-log units)
+ * Per row: partition p is empty when l_p <= 0 or m_p == -inf; M = max m_p
+ * over the non-empty ones; w_p = exp(scale*(m_p - M)) * l_p; W = sum w_p;
+ * out = sum over non-empty p, in ascending p, of (w_p / W) * O_p, with
+ * weights and accumulation in double and one rounding to out_dtype.  Empty
+ * partitions are skipped (their O_p never enters the sum); a row with no
+ * non-empty partition is written as zeros.  P == 1 reproduces O_1 exactly
+ * (rounded once to out_dtype).
+ */
+rr_status rr_splitk_lse_merge(const float* o_part, const float* m_part, const float* l_part,
+                              void* out, int32_t P, int64_t rows, int32_t depth, float scale,
+                              rr_dtype out_dtype, void* stream);
+
+/* Bytes of workspace rr_reduce_rows needs for this shape on the current
+ * device (0 unless the plan is split-K).  kind must be RR_KIND_REDUCE. */
+rr_status rr_workspace_bytes(rr_kind kind, int64_t rows, int64_t cols, rr_dtype dtype,
+                             rr_op op, rr_tier tier, size_t* bytes_out);
+
+/* Tier AUTO would pick for this shape on the current device. */
+rr_status rr_select_tier(rr_kind kind, int64_t rows, int64_t cols, rr_dtype dtype, rr_op op,
+                         rr_tier* tier_out);
+
+/* Zero `bytes` of a workspace on `stream` with a fill kernel (no memset
+ * node, so the call may be captured into a HIP graph).  Use it to recover a
+ * workspace after an aborted call. */
+rr_status rr_workspace_reset(void* workspace, size_t bytes, void* stream);
+
+/* Compute units of the current device, as the library sees them. */
+rr_status rr_device_cu_count(int32_t* cu_out);
+
+/* Static text for a status code; never NULL. */
+const char* rr_status_string(rr_status s);
+
+/* RR_VERSION of the built library. */
+int rr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RR_H */

@@ -1,0 +1,320 @@
+/*
+ * rro.c -- CPU oracle for the deterministic row-reduce path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the plain, slow, obviously correct
+ * definition that the GPU library is checked against.  Only the test suite,
+ * the package smoke check and the benchmark's CPU-baseline leg may load it.
+ * It shares no code, header, table or constant with the GPU library.
+ *
+ * Every float result is computed in IEEE double and rounded once at the end.
+ * Build: gcc -O2 (no -ffast-math, no FMA contraction), single threaded.
+ *
+ * Sources (Modular API pages; section names as printed on the pages):
+ *   [CA]  "cluster_allreduce" -- description and Parameters (combine_fn is an
+ *         associative add/max/min over 32-bit elements; the fold visits ranks
+ *         in ascending order).
+ *   [RW]  "reduce" (algorithm.gpu.rowwise) -- tier semantics and the
+ *         state-carrying overload (a monoid state folded tile by tile along
+ *         the last axis); the two-pass softmax (pass 1 a monoid, pass 2 a map).
+ *   [FA4] "fa4_splitk_reduce_scatter_write" -- the split-K combine: partials
+ *         carry a per-row (max, sum); the combine scales each partition's
+ *         output by its weight w[b], accumulates partitions and packs bf16;
+ *         every partition, empty or not, takes part.
+ *
+ * Readings of the pages used here (each is restated where it is used):
+ *   - float SUM accumulates in double in index order, rounds once (RNE).
+ *   - int32 SUM wraps modulo 2^32.
+ *   - float MAX/MIN order values by IEEE 754 totalOrder (so -0 < +0; a NaN
+ *     with the sign bit clear is above +inf, one with it set below -inf).
+ *   - softmax pass 1 is (max, sum exp(x - max)), pass 2 is exp(x - max)/sum,
+ *     rounded once from double to the output type.
+ *   - the LSE merge takes normalised partials O_p with row statistics
+ *     (m_p, l_p); weight w_p = exp(scale*(m_p - M)) * l_p over the non-empty
+ *     partitions (l_p > 0 and m_p > -inf), M their largest m_p; the output is
+ *     sum_p (w_p / W) O_p with W = sum_p w_p; a row with no non-empty
+ *     partition is zero; empty partitions are skipped, so their O_p is never
+ *     read into the sum.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* dtype codes used by this file's callers */
+#define RRO_F32 0
+#define RRO_I32 1
+#define RRO_BF16 2
+/* op codes */
+#define RRO_SUM 0
+#define RRO_MAX 1
+#define RRO_MIN 2
+
+#define RRO_OK 0
+#define RRO_BAD 1
+
+/* ------------------------------------------------------------------ bf16 */
+
+/* Value of a bf16 bit pattern: bf16 is the top half of a binary32. */
+double rro_bf16_to_double(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/*
+ * Round a double to the nearest bf16, ties to even (one rounding).
+ * bf16: 1 sign bit, 8 exponent bits (bias 127), 7 fraction bits; normal
+ * numbers carry 8 significant bits; the subnormal quantum is 2^-133; the
+ * largest finite value is (2 - 2^-7) * 2^127.  NaN maps to a quiet NaN with
+ * the same sign.
+ */
+uint16_t rro_bf16_from_double(double v)
+{
+    uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    if (isnan(v))
+        return (uint16_t)(sign | 0x7FC0u);
+    double a = fabs(v);
+    if (isinf(a))
+        return (uint16_t)(sign | 0x7F80u);
+    if (a == 0.0)
+        return sign;
+
+    int e;
+    frexp(a, &e);               /* a = f * 2^e, 0.5 <= f < 1: leading bit is 2^(e-1) */
+    int q = (e - 1) - 7;        /* weight of the last kept bit for a normal result */
+    if (q < -133)
+        q = -133;               /* subnormal range: fixed quantum */
+    double n = rint(ldexp(a, -q));          /* default mode: nearest, ties to even */
+    double r = ldexp(n, q);                 /* rounded magnitude */
+    if (r > 0x1.FEp127)
+        return (uint16_t)(sign | 0x7F80u);  /* rounds past the largest finite */
+    if (r == 0.0)
+        return sign;
+
+    int e2;
+    double f2 = frexp(r, &e2);
+    if (e2 - 1 < -126)                      /* subnormal: r = k * 2^-133, k < 128 */
+        return (uint16_t)(sign | (uint16_t)ldexp(r, 133));
+    uint16_t exp_field = (uint16_t)(e2 - 1 + 127);
+    uint16_t frac = (uint16_t)(ldexp(f2, 8) - 128.0);  /* f2 * 2^8 in [128, 256) */
+    return (uint16_t)(sign | (exp_field << 7) | frac);
+}
+
+/* ------------------------------------------------------------ element I/O */
+
+static double load_real(const void* base, int dtype, int64_t idx)
+{
+    if (dtype == RRO_F32)
+        return (double)((const float*)base)[idx];
+    return rro_bf16_to_double(((const uint16_t*)base)[idx]);
+}
+
+static void store_real(void* base, int dtype, int64_t idx, double v)
+{
+    if (dtype == RRO_F32)
+        ((float*)base)[idx] = (float)v;     /* C conversion: round to nearest even */
+    else
+        ((uint16_t*)base)[idx] = rro_bf16_from_double(v);
+}
+
+/* --------------------------------------------------------- totalOrder */
+
+/*
+ * IEEE 754 totalOrder restricted to "a strictly before b" for binary32.
+ * Every value whose sign bit is set precedes every value whose sign bit is
+ * clear (this puts -0 before +0).  With equal signs, compare magnitudes: a
+ * NaN's magnitude is above infinity and NaNs compare by payload; the larger
+ * magnitude comes last for positive values and first for negative ones.
+ */
+static int f32_total_before(float a, float b)
+{
+    int sa = signbit(a) != 0, sb = signbit(b) != 0;
+    if (sa != sb)
+        return sa;
+    int mag_less; /* |a| before |b| in magnitude order */
+    int na = isnan(a), nb = isnan(b);
+    if (!na && !nb) {
+        mag_less = fabsf(a) < fabsf(b);
+    } else if (na != nb) {
+        mag_less = nb;  /* the NaN has the larger magnitude */
+    } else {
+        uint32_t ua, ub;
+        memcpy(&ua, &a, 4);
+        memcpy(&ub, &b, 4);
+        mag_less = (ua & 0x007FFFFFu) < (ub & 0x007FFFFFu);
+        if ((ua & 0x007FFFFFu) == (ub & 0x007FFFFFu))
+            return 0;
+    }
+    if (!na && !nb && fabsf(a) == fabsf(b))
+        return 0;
+    return sa ? !mag_less : mag_less;
+}
+
+/* ----------------------------------------------------------------- reduce */
+
+/*
+ * y[r] = combine over j = 0..cols-1 (index order) of x[r*ld + j].
+ * [CA] combine_fn: associative add / max / min on 32-bit elements.
+ * [RW] the state-carrying reduce folds each element into the monoid state.
+ * MAX/MIN start from the row's first element, so a non-empty row always
+ * yields one of its own elements; cols == 0 gives the identity (0 for SUM,
+ * -inf / INT32_MIN for MAX, +inf / INT32_MAX for MIN).
+ */
+int rro_reduce_rows(const void* x, void* y, int64_t rows, int64_t cols, int64_t ld,
+                    int dtype, int op)
+{
+    if (rows < 0 || cols < 0 || ld < cols)
+        return RRO_BAD;
+    if (op != RRO_SUM && op != RRO_MAX && op != RRO_MIN)
+        return RRO_BAD;
+    for (int64_t r = 0; r < rows; ++r) {
+        if (dtype == RRO_I32) {
+            const int32_t* row = (const int32_t*)x + r * ld;
+            int32_t out;
+            if (op == RRO_SUM) {
+                uint32_t acc = 0;                   /* wraps modulo 2^32 */
+                for (int64_t j = 0; j < cols; ++j)
+                    acc += (uint32_t)row[j];
+                out = (int32_t)acc;
+            } else if (op == RRO_MAX) {
+                int32_t acc = cols ? row[0] : INT32_MIN;
+                for (int64_t j = 1; j < cols; ++j)
+                    if (row[j] > acc)
+                        acc = row[j];
+                out = acc;
+            } else {
+                int32_t acc = cols ? row[0] : INT32_MAX;
+                for (int64_t j = 1; j < cols; ++j)
+                    if (row[j] < acc)
+                        acc = row[j];
+                out = acc;
+            }
+            ((int32_t*)y)[r] = out;
+        } else if (dtype == RRO_F32) {
+            const float* row = (const float*)x + r * ld;
+            float out;
+            if (op == RRO_SUM) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < cols; ++j)
+                    acc += (double)row[j];
+                out = (float)acc;
+            } else if (op == RRO_MAX) {
+                float acc = cols ? row[0] : -INFINITY;
+                for (int64_t j = 1; j < cols; ++j)
+                    if (f32_total_before(acc, row[j]))
+                        acc = row[j];
+                out = acc;
+            } else {
+                float acc = cols ? row[0] : INFINITY;
+                for (int64_t j = 1; j < cols; ++j)
+                    if (f32_total_before(row[j], acc))
+                        acc = row[j];
+                out = acc;
+            }
+            ((float*)y)[r] = out;
+        } else {
+            return RRO_BAD;
+        }
+    }
+    return RRO_OK;
+}
+
+/* ---------------------------------------------------------------- softmax */
+
+/*
+ * [RW] two-pass softmax.  Pass 1: m = max_j x_j, s = sum_j exp(x_j - m).
+ * Pass 2 (a pure map): y_j = exp(x_j - m) / s, rounded once to y's type.
+ * cols == 0 writes nothing.
+ */
+int rro_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols,
+                     int64_t ld_x, int64_t ld_y, int x_dtype, int y_dtype)
+{
+    if (rows < 0 || cols < 0 || ld_x < cols || ld_y < cols)
+        return RRO_BAD;
+    if ((x_dtype != RRO_F32 && x_dtype != RRO_BF16) || (y_dtype != RRO_F32 && y_dtype != RRO_BF16))
+        return RRO_BAD;
+    for (int64_t r = 0; r < rows; ++r) {
+        if (cols == 0)
+            continue;
+        double m = load_real(x, x_dtype, r * ld_x);
+        for (int64_t j = 1; j < cols; ++j) {
+            double v = load_real(x, x_dtype, r * ld_x + j);
+            if (v > m)
+                m = v;
+        }
+        double s = 0.0;
+        for (int64_t j = 0; j < cols; ++j)
+            s += exp(load_real(x, x_dtype, r * ld_x + j) - m);
+        for (int64_t j = 0; j < cols; ++j) {
+            double e = exp(load_real(x, x_dtype, r * ld_x + j) - m);
+            store_real(y, y_dtype, r * ld_y + j, e / s);
+        }
+    }
+    return RRO_OK;
+}
+
+/* --------------------------------------------------------------- LSE merge */
+
+/*
+ * [FA4] split-K combine of P partition outputs.
+ *   o   [P][rows][depth]  normalised partial outputs O_p
+ *   m   [P][rows]         per-row max m_p of partition p's scores
+ *   l   [P][rows]         per-row sum l_p = sum exp(score - m_p)
+ *   out [rows][depth]     f32 or bf16
+ * Partition p is empty when l_p <= 0 or m_p == -inf; empty partitions take
+ * part but contribute nothing (their O_p is not read into the sum).
+ */
+int rro_splitk_lse_merge(const float* o, const float* m, const float* l, void* out,
+                         int32_t P, int64_t rows, int32_t depth, float scale, int out_dtype)
+{
+    if (P < 1 || rows < 0 || depth < 1)
+        return RRO_BAD;
+    if (out_dtype != RRO_F32 && out_dtype != RRO_BF16)
+        return RRO_BAD;
+    double* w = (double*)malloc(sizeof(double) * (size_t)P);
+    int* live = (int*)malloc(sizeof(int) * (size_t)P);
+    if (!w || !live) {
+        free(w);
+        free(live);
+        return RRO_BAD;
+    }
+    for (int64_t r = 0; r < rows; ++r) {
+        /* which partitions are non-empty, and the largest of their maxima */
+        int any = 0;
+        double M = -INFINITY;
+        for (int32_t p = 0; p < P; ++p) {
+            double mp = (double)m[(int64_t)p * rows + r];
+            double lp = (double)l[(int64_t)p * rows + r];
+            live[p] = (lp > 0.0 && mp > -INFINITY);
+            if (live[p]) {
+                if (!any || mp > M)
+                    M = mp;
+                any = 1;
+            }
+        }
+        /* weights w_p = exp(scale * (m_p - M)) * l_p and their total W */
+        double W = 0.0;
+        for (int32_t p = 0; p < P; ++p) {
+            w[p] = 0.0;
+            if (live[p]) {
+                double mp = (double)m[(int64_t)p * rows + r];
+                double lp = (double)l[(int64_t)p * rows + r];
+                w[p] = exp((double)scale * (mp - M)) * lp;
+                W += w[p];
+            }
+        }
+        /* out = sum over non-empty p, in ascending p, of (w_p / W) * O_p */
+        for (int32_t d = 0; d < depth; ++d) {
+            double acc = 0.0;
+            for (int32_t p = 0; p < P; ++p)
+                if (live[p])
+                    acc += (w[p] / W) * (double)o[((int64_t)p * rows + r) * depth + d];
+            store_real(out, out_dtype, r * depth + d, acc);
+        }
+    }
+    free(w);
+    free(live);
+    return RRO_OK;
+}

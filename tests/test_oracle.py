@@ -1,0 +1,386 @@
+"""Pins for the CPU oracle, against things other than the oracle itself.
+
+Each test checks the oracle against an independent source: hand-worked
+fixtures under tests/golden/ (cited there), exact rational arithmetic,
+Python integer arithmetic, numpy / torch library routines, closed forms,
+and invariants the mathematics fixes.  CPU only.
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from split_deterministic_combine_amd import synth
+from tests.exact import (bf16_ulp_diff, bf16_value, bits_f32, f32_bits, round_to_bf16,
+                         round_to_f32)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden_lines(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                yield line
+
+
+def _num(s):
+    s = s.strip()
+    return {"inf": math.inf, "-inf": -math.inf, "nan": math.nan}.get(s, None) if s in (
+        "inf", "-inf", "nan") else float(s)
+
+
+# ---------------------------------------------------------------- bf16 rounding
+
+def test_bf16_golden_cases():
+    for line in _golden_lines("bf16_rounding.txt"):
+        val, bits = line.split()
+        assert int(oracle.bf16_from_double([float(val)])[0]) == int(bits, 16), val
+
+
+def test_bf16_matches_torch_on_float32_inputs():
+    # torch's float32 -> bfloat16 cast rounds to nearest even: for inputs that
+    # are float32 values the double path must give the same pattern.
+    rng = np.random.default_rng(101)
+    raw = rng.integers(0, 2 ** 32, 20000, dtype=np.uint64).astype(np.uint32)
+    f = raw.view(np.float32)
+    f = f[np.isfinite(f)]
+    specials = np.array([0.0, -0.0, 1.0, -1.0, 3.0e38, -3.4e38, 1e-40, -1e-45, 1e-38,
+                         np.inf, -np.inf], dtype=np.float32)
+    f = np.concatenate([f, specials])
+    want = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle.bf16_from_double(f.astype(np.float64))
+    assert np.array_equal(got, want)
+
+
+def test_bf16_matches_exact_rational_rounding_on_doubles():
+    rng = np.random.default_rng(102)
+    vals = list(rng.standard_normal(3000) * np.exp2(rng.integers(-140, 128, 3000)))
+    # values sitting exactly on and next to bf16 ties at many binades
+    for e in range(-130, 127, 7):
+        for k in (128, 129, 200, 255):
+            tie = (k + 0.5) * 2.0 ** (e - 7)
+            vals += [tie, math.nextafter(tie, math.inf), math.nextafter(tie, -math.inf), -tie]
+    for v in vals:
+        if not math.isfinite(v):
+            continue
+        want = round_to_bf16(Fraction(v))
+        got = int(oracle.bf16_from_double([v])[0])
+        if v < 0 and want & 0x7FFF == 0:
+            want = 0x8000
+        assert got == want, (v, hex(got), hex(want))
+
+
+def test_bf16_nan_is_quiet_and_keeps_sign():
+    assert int(oracle.bf16_from_double([math.nan])[0]) & 0x7FC0 == 0x7FC0
+    neg_nan = -abs(math.nan) if math.copysign(1, -abs(math.nan)) < 0 else math.copysign(math.nan, -1)
+    assert int(oracle.bf16_from_double([neg_nan])[0]) & 0x8000
+
+
+def test_bf16_to_double_is_top_half_of_float32():
+    bits = np.arange(0, 65536, 97, dtype=np.uint16)
+    got = oracle.bf16_to_double(bits)
+    for b, g in zip(bits, got):
+        want = bits_f32(int(b) << 16)
+        assert (math.isnan(g) and math.isnan(want)) or g == want
+
+
+# --------------------------------------------------------------------- reduce
+
+def test_reduce_golden_cases():
+    for line in _golden_lines("reduce_small.txt"):
+        head, values, want = [s.strip() for s in line.split("|")]
+        dt, op = head.split()
+        if dt == "i32":
+            x = np.array([[int(v) for v in values.split()]], dtype=np.int32)
+            got = int(oracle.reduce_rows(x, op)[0]) & 0xFFFFFFFF
+        else:
+            x = np.array([[float(v) for v in values.split()]], dtype=np.float32)
+            got = f32_bits(oracle.reduce_rows(x, op)[0])
+        assert got == int(want, 16), line
+
+
+def test_i32_sum_matches_python_integers_with_wrap():
+    rng = np.random.default_rng(201)
+    x = rng.integers(-(2 ** 31), 2 ** 31, (40, 257), dtype=np.int64).astype(np.int32)
+    got = oracle.reduce_rows(x, "sum")
+    for r in range(x.shape[0]):
+        s = sum(int(v) for v in x[r]) & 0xFFFFFFFF
+        want = s - (1 << 32) if s >= 1 << 31 else s
+        assert int(got[r]) == want
+
+
+def test_i32_max_min_match_python():
+    x = synth.ints_i32(202, (33, 129), -(2 ** 31), 2 ** 31 - 1)
+    gmax, gmin = oracle.reduce_rows(x, "max"), oracle.reduce_rows(x, "min")
+    for r in range(x.shape[0]):
+        assert int(gmax[r]) == max(int(v) for v in x[r])
+        assert int(gmin[r]) == min(int(v) for v in x[r])
+
+
+def test_i32_sum_is_column_permutation_invariant():
+    x = synth.ints_i32(203, (16, 1000), -(2 ** 31), 2 ** 31 - 1)
+    perm = np.random.default_rng(204).permutation(x.shape[1])
+    assert np.array_equal(oracle.reduce_rows(x, "sum"), oracle.reduce_rows(x[:, perm].copy(), "sum"))
+
+
+def test_f32_sum_exact_for_dyadic_values():
+    # multiples of 2^-10 below 2^4: every partial sum is exact in double, so
+    # the oracle must return the exact sum rounded once to float32.
+    rng = np.random.default_rng(205)
+    k = rng.integers(-(2 ** 14), 2 ** 14, (20, 700))
+    x = (k / 1024.0).astype(np.float32)
+    got = oracle.reduce_rows(x, "sum")
+    for r in range(x.shape[0]):
+        exact = sum(Fraction(int(v), 1024) for v in k[r])
+        assert got[r] == round_to_f32(exact)
+
+
+def test_f32_sum_within_one_ulp_of_exact_sum():
+    x = synth.uniform_f32(206, (60, 1024))
+    got = oracle.reduce_rows(x, "sum")
+    equal = 0
+    for r in range(x.shape[0]):
+        exact = round_to_f32(sum(Fraction(float(v)) for v in x[r]))
+        d = abs(int(f32_bits(got[r])) - int(f32_bits(exact)))
+        assert d <= 1
+        equal += d == 0
+    assert equal >= 57  # double accumulation of 1024 terms: almost always correctly rounded
+
+
+def test_f32_sum_of_opposite_pairs_is_zero():
+    x = synth.normal_f32(207, (8, 300))
+    both = np.concatenate([x, -x[:, ::-1]], axis=1)
+    assert np.all(oracle.reduce_rows(both, "sum") == 0.0)
+
+
+def test_f32_max_min_match_numpy_and_are_elements():
+    x = synth.normal_f32(208, (50, 777))
+    gmax, gmin = oracle.reduce_rows(x, "max"), oracle.reduce_rows(x, "min")
+    assert np.array_equal(gmax, x.max(axis=1))
+    assert np.array_equal(gmin, x.min(axis=1))
+    for r in range(x.shape[0]):
+        assert gmax[r] in x[r] and gmin[r] in x[r]
+
+
+def test_f32_max_min_total_order_on_nan():
+    qnan = np.float32(np.nan)
+    neg_nan = np.array([0xFFC00000], dtype=np.uint32).view(np.float32)[0]
+    row = np.array([[1.0, qnan, -3.0]], dtype=np.float32)
+    assert np.isnan(oracle.reduce_rows(row, "max")[0])          # +NaN is above +inf
+    assert oracle.reduce_rows(row, "min")[0] == -3.0
+    row = np.array([[1.0, neg_nan, -3.0]], dtype=np.float32)
+    assert oracle.reduce_rows(row, "max")[0] == 1.0
+    assert f32_bits(oracle.reduce_rows(row, "min")[0]) == 0xFFC00000  # -NaN is below -inf
+
+
+def test_reduce_degenerate_sizes():
+    e = np.zeros((3, 0), dtype=np.float32)
+    assert np.all(oracle.reduce_rows(e, "sum") == 0)
+    assert np.all(oracle.reduce_rows(e, "max") == -np.inf)
+    assert np.all(oracle.reduce_rows(e, "min") == np.inf)
+    ei = np.zeros((2, 0), dtype=np.int32)
+    assert np.all(oracle.reduce_rows(ei, "max") == np.iinfo(np.int32).min)
+    assert np.all(oracle.reduce_rows(ei, "min") == np.iinfo(np.int32).max)
+    one = synth.normal_f32(209, (5, 1))
+    for op in ("sum", "max", "min"):
+        assert np.array_equal(oracle.reduce_rows(one, op), one[:, 0])
+    assert oracle.reduce_rows(np.zeros((0, 4), dtype=np.float32), "sum").shape == (0,)
+
+
+def test_reduce_strided_rows_read_only_cols():
+    big = synth.normal_f32(210, (9, 40))
+    view = big[:, :33]
+    assert view.strides[0] == 40 * 4
+    assert np.array_equal(oracle.reduce_rows(view, "sum"), oracle.reduce_rows(view.copy(), "sum"))
+
+
+# -------------------------------------------------------------------- softmax
+
+def _f32_to_bf16_bits(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(
+        torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_softmax_golden_cases():
+    for line in _golden_lines("softmax_small.txt"):
+        xs, ys = [s.strip() for s in line.split("|")]
+        x = np.array([[float(v) for v in xs.split(",")]], dtype=np.float32)
+        want = np.array([float(v) for v in ys.split(",")], dtype=np.float32)
+        assert np.array_equal(oracle.softmax_rows(x, "f32")[0], want), line
+        assert np.array_equal(oracle.softmax_rows(x, "bf16")[0], _f32_to_bf16_bits(want)), line
+
+
+def test_softmax_uniform_row_8192_is_exactly_2_pow_minus_13():
+    x = np.full((2, 8192), 0x4040, dtype=np.uint16)  # bf16 3.0
+    y = oracle.softmax_rows(x, "bf16")
+    assert np.all(y == 0x3900)
+
+
+def test_softmax_rows_sum_to_one():
+    x = synth.normal_f32(301, (20, 1000), std=3.0)
+    y = oracle.softmax_rows(x, "f32").astype(np.float64)
+    assert np.all(np.abs(y.sum(axis=1) - 1.0) < 1e-5)
+    yb = oracle.bf16_to_double(oracle.softmax_rows(x, "bf16"))
+    assert np.all(np.abs(yb.sum(axis=1) - 1.0) < 2.0 ** -8)
+
+
+def test_softmax_two_element_closed_form():
+    rng = np.random.default_rng(302)
+    for _ in range(200):
+        a, b = (float(v) for v in rng.uniform(-10, 10, 2).astype(np.float32))
+        x = np.array([[a, b]], dtype=np.float32)
+        y = oracle.softmax_rows(x, "f32")[0]
+        want = 1.0 / (1.0 + math.exp(float(np.float32(b)) - float(np.float32(a))))
+        assert abs(float(y[0]) - want) <= 2 * 2.0 ** -24 * max(want, 2.0 ** -126)
+        assert abs(float(y[1]) - (1.0 - want)) <= 4e-7
+
+
+def test_softmax_shift_invariance_exact():
+    # multiples of 1/8 in [-8, 8) shifted by small integers stay exact in bf16,
+    # and x - max is then exact, so the outputs must be bit-identical.
+    k = np.random.default_rng(303).integers(-64, 64, (6, 100))
+    x = (k / 8.0).astype(np.float32)
+    for c in (1.0, -3.0, 5.0):
+        xb, xcb = _f32_to_bf16_bits(x), _f32_to_bf16_bits(x + np.float32(c))
+        assert np.array_equal(oracle.softmax_rows(xb, "bf16"), oracle.softmax_rows(xcb, "bf16"))
+
+
+def test_softmax_matches_torch_double_softmax():
+    x = synth.normal_f32(304, (12, 333), std=3.0)
+    ref = torch.softmax(torch.from_numpy(x).double(), dim=1).numpy()
+    y = oracle.softmax_rows(x, "f32")
+    rel = np.abs(y.astype(np.float64) - ref) / ref
+    assert np.all(rel <= 2.0 ** -24 * 1.01)  # one rounding of a value correct to ~1e-15
+    yb = oracle.softmax_rows(x, "bf16")
+    want = np.array([round_to_bf16(Fraction(float(v))) for v in ref[:3].ravel()]).reshape(3, -1)
+    assert bf16_ulp_diff(yb[:3], want).max() == 0
+
+
+def test_softmax_permutation_equivariant():
+    x = synth.normal_f32(305, (4, 50))
+    perm = np.random.default_rng(306).permutation(50)
+    y = oracle.softmax_rows(x, "f32")
+    yp = oracle.softmax_rows(x[:, perm].copy(), "f32")
+    assert np.max(np.abs(y[:, perm] - yp)) <= 1e-7
+
+
+def test_softmax_bf16_input_strided_and_empty():
+    x = synth.normal_bf16(307, (5, 70))
+    assert np.array_equal(oracle.softmax_rows(x[:, :64], "bf16"),
+                          oracle.softmax_rows(x[:, :64].copy(), "bf16"))
+    assert oracle.softmax_rows(np.zeros((3, 0), dtype=np.float32), "f32").shape == (3, 0)
+
+
+# ------------------------------------------------------------------ LSE merge
+
+def _parse_floats(s):
+    return [float(v) for v in s.split()]
+
+
+def test_merge_golden_cases():
+    for line in _golden_lines("lse_merge_small.txt"):
+        name, geo, ms, ls, os_, want = [s.strip() for s in line.split("|")]
+        P, depth, scale = geo.split()
+        P, depth, scale = int(P), int(depth), float(scale)
+        m = np.array(_parse_floats(ms), dtype=np.float32).reshape(P, 1)
+        l = np.array(_parse_floats(ls), dtype=np.float32).reshape(P, 1)
+        o = np.array([_parse_floats(r) for r in os_.split(";")], dtype=np.float32).reshape(
+            P, 1, depth)
+        want = np.array(_parse_floats(want), dtype=np.float32)
+        got = oracle.splitk_lse_merge(o, m, l, scale, "f32")[0]
+        assert np.array_equal(got, want), name
+        gotb = oracle.splitk_lse_merge(o, m, l, scale, "bf16")[0]
+        assert np.array_equal(gotb, _f32_to_bf16_bits(want)), name
+
+
+def test_merge_single_partition_is_identity():
+    o, m, l = synth.lse_merge(401, P=1, batch=1, heads=2, q_rows=16, depth=64)
+    o3, m2, l2 = o.reshape(1, 32, 64), m.reshape(1, 32), l.reshape(1, 32)
+    assert np.array_equal(oracle.splitk_lse_merge(o3, m2, l2, 1.0, "f32"), o3[0])
+    assert np.array_equal(oracle.splitk_lse_merge(o3, m2, l2, 1.0, "bf16"), _f32_to_bf16_bits(o3[0]))
+
+
+def test_merge_weights_sum_to_one():
+    _, m, l = synth.lse_merge(402, P=8, batch=1, heads=4, q_rows=32, depth=16)
+    m2, l2 = m.reshape(8, -1), l.reshape(8, -1)
+    ones = np.ones((8, m2.shape[1], 3), dtype=np.float32)
+    assert np.all(oracle.splitk_lse_merge(ones, m2, l2, 1.0, "f32") == 1.0)
+
+
+def test_merge_equal_stats_give_the_mean():
+    o = synth.normal_f32(403, (4, 10, 8))
+    m = np.full((4, 10), 1.5, dtype=np.float32)
+    l = np.full((4, 10), 7.0, dtype=np.float32)
+    got = oracle.splitk_lse_merge(o, m, l, 1.0, "f32")
+    want = np.array([[round_to_f32(sum(Fraction(float(o[p, r, d])) for p in range(4)) / 4)
+                      for d in range(8)] for r in range(10)], dtype=np.float32)
+    assert np.array_equal(got, want)
+
+
+def test_merge_equals_full_attention_closed_form():
+    # Split-K attention: scores s_j = q.k_j, split the keys into P chunks; each
+    # chunk gives m_p = max s, l_p = sum exp(s - m_p), O_p = sum exp(s - m_p) v / l_p.
+    # The merge of the chunks must equal softmax(s) @ V over all keys.
+    rng = np.random.default_rng(404)
+    rows, keys, depth, P = 6, 96, 16, 4
+    q = rng.standard_normal((rows, depth))
+    k = rng.standard_normal((keys, depth))
+    v = rng.standard_normal((keys, depth))
+    s = q @ k.T
+    full = (np.exp(s - s.max(1, keepdims=True)) /
+            np.exp(s - s.max(1, keepdims=True)).sum(1, keepdims=True)) @ v
+    chunks = np.array_split(np.arange(keys), P)
+    o = np.zeros((P, rows, depth))
+    m = np.zeros((P, rows))
+    l = np.zeros((P, rows))
+    for p, idx in enumerate(chunks):
+        sp = s[:, idx]
+        m[p] = sp.max(1)
+        e = np.exp(sp - m[p][:, None])
+        l[p] = e.sum(1)
+        o[p] = (e @ v[idx]) / l[p][:, None]
+    got = oracle.splitk_lse_merge(o.astype(np.float32), m.astype(np.float32),
+                                  l.astype(np.float32), 1.0, "f32")
+    # inputs were rounded to float32 (relative 2^-24 each), so allow a few e-7
+    assert np.max(np.abs(got - full)) <= 2e-6 * max(1.0, np.abs(full).max())
+    # and with a softmax scale folded in: exp(scale * (m_p - M))
+    scale = 0.125
+    m_s = (m / scale).astype(np.float32)
+    l_s = l.astype(np.float32)
+    got_s = oracle.splitk_lse_merge(o.astype(np.float32), m_s, l_s, scale, "f32")
+    assert np.max(np.abs(got_s - full)) <= 2e-6 * max(1.0, np.abs(full).max())
+
+
+def test_merge_partition_permutation_invariant():
+    o, m, l = synth.lse_merge(405, P=8, batch=1, heads=2, q_rows=8, depth=32)
+    o3, m2, l2 = o.reshape(8, 16, 32), m.reshape(8, 16), l.reshape(8, 16)
+    perm = np.random.default_rng(406).permutation(8)
+    a = oracle.splitk_lse_merge(o3, m2, l2, 1.0, "f32")
+    b = oracle.splitk_lse_merge(o3[perm].copy(), m2[perm].copy(), l2[perm].copy(), 1.0, "f32")
+    assert np.max(np.abs(a.view(np.int32).astype(np.int64) - b.view(np.int32))) <= 1
+
+
+def test_merge_empty_partition_is_ignored_even_with_nan():
+    o, m, l = synth.lse_merge(407, P=4, batch=1, heads=1, q_rows=12, depth=8)
+    o3, m2, l2 = o.reshape(4, 12, 8), m.reshape(4, 12), l.reshape(4, 12)
+    base = oracle.splitk_lse_merge(o3, m2, l2, 1.0, "f32")
+    o5 = np.concatenate([o3[:2], np.full((1, 12, 8), np.nan, np.float32), o3[2:]])
+    m5 = np.concatenate([m2[:2], np.full((1, 12), 3.0, np.float32), m2[2:]])
+    l5 = np.concatenate([l2[:2], np.zeros((1, 12), np.float32), l2[2:]])
+    assert np.array_equal(oracle.splitk_lse_merge(o5, m5, l5, 1.0, "f32"), base)
+    m5[2] = -np.inf
+    l5[2] = 5.0
+    assert np.array_equal(oracle.splitk_lse_merge(o5, m5, l5, 1.0, "f32"), base)
+
+
+def test_merge_config_shape_smoke():
+    o, m, l = synth.lse_merge(408, P=8, batch=1, heads=1, q_rows=4, depth=128)
+    out = oracle.splitk_lse_merge(o.reshape(8, 4, 128), m.reshape(8, 4), l.reshape(8, 4), 1.0,
+                                  "bf16")
+    assert out.shape == (4, 128) and out.dtype == np.uint16
