@@ -1,0 +1,276 @@
+"""Benchmark of the row-reduce hot path on one MI355X.
+
+One step runs every operation of the path once on its synthetic workload:
+  short_rows  f32 row sum and row max over [1048576, 48]     (wave tier)
+  softmax     bf16 softmax over [8192, 8192]                  (block tier)
+  long_rows   f32 row sum and int32 row max over [16, 2^24]   (split-K tier)
+  lse_merge   P = 8 merge of O [8, 8, 32, 128, 128] -> bf16 [8, 32, 128, 128]
+
+Inputs are resident in HBM before timing.  Buffer sets rotate from one step
+to the next so that the data touched by consecutive launches exceeds the
+~256 MB Infinity Cache (the long-row inputs are 1 GiB each by themselves).
+
+`value` is whole-step throughput in GB/s: algorithmic bytes of all launches
+(each input element read once, each output written once) divided by the
+measured step time.  Per-launch durations come from HIP events recorded on
+the stream the kernels are launched on.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "achieved HBM GB/s and % of peak for rowwise reduce/softmax/split-K merge"
+CSRC = os.path.join(ROOT, "split_deterministic_combine_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--only", default=None, help="comma list of ops to run (profiling)")
+    return ap.parse_args()
+
+
+def bf16_ulp_diff(a, b):
+    """Distance in bf16 units in the last place (sign-magnitude patterns ordered)."""
+    def ordered(u):
+        u = u.astype(np.int64) & 0xFFFF
+        return np.where(u & 0x8000, -(u & 0x7FFF), u & 0x7FFF)
+    return np.abs(ordered(a) - ordered(b))
+
+
+def log(msg):
+    sys.stderr.write("[bench] %s\n" % msg)
+    sys.stderr.flush()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import split_deterministic_combine_amd as rr
+    from split_deterministic_combine_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def gpu(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    # ------------------------------------------------------------ inputs
+    t0 = time.time()
+    log("generating inputs")
+    host = {}
+    host["short"] = synth.short_rows()
+    host["softmax"] = synth.softmax_rows()
+    host["long_f"], host["long_i"] = synth.long_rows()
+    host["merge"] = synth.lse_merge()
+    log("inputs generated in %.1f s" % (time.time() - t0))
+
+    sets = {"short": 5, "softmax": 4, "long_f": 1, "long_i": 1, "merge": 8}
+    dx = {}
+    base = gpu(host["short"])
+    dx["short"] = [base] + [base.clone() for _ in range(sets["short"] - 1)]
+    base = gpu(host["softmax"])
+    dx["softmax"] = [base] + [base.clone() for _ in range(sets["softmax"] - 1)]
+    dx["softmax_out"] = [torch.empty_like(base) for _ in range(sets["softmax"])]
+    dx["long_f"] = [gpu(host["long_f"])]
+    dx["long_i"] = [gpu(host["long_i"])]
+    o, m, l = (gpu(a) for a in host["merge"])
+    dx["merge"] = [(o, m, l)] + [(o.clone(), m.clone(), l.clone()) for _ in range(sets["merge"] - 1)]
+    dx["merge_out"] = [torch.empty((8, 32, 128, 128), dtype=torch.bfloat16, device=dev)
+                       for _ in range(sets["merge"])]
+    y_short = torch.empty(1048576, dtype=torch.float32, device=dev)
+    y_long_f = torch.empty(16, dtype=torch.float32, device=dev)
+    y_long_i = torch.empty(16, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+
+    # algorithmic bytes per launch (inputs read once, outputs written once)
+    B = {
+        "short_sum": 1048576 * 48 * 4 + 1048576 * 4,
+        "short_max": 1048576 * 48 * 4 + 1048576 * 4,
+        "softmax": 8192 * 8192 * 2 * 2,
+        "long_sum": 16 * (1 << 24) * 4 + 16 * 4,
+        "long_max": 16 * (1 << 24) * 4 + 16 * 4,
+        "merge": 8 * 32768 * 128 * 4 + 2 * 8 * 32768 * 4 + 32768 * 128 * 2,
+    }
+    ops = {
+        "short_sum": lambda i: rr.reduce_rows(dx["short"][i % 5], "sum", out=y_short),
+        "short_max": lambda i: rr.reduce_rows(dx["short"][i % 5], "max", out=y_short),
+        "softmax": lambda i: rr.softmax_rows(dx["softmax"][i % 4], out=dx["softmax_out"][i % 4]),
+        "long_sum": lambda i: rr.reduce_rows(dx["long_f"][0], "sum", out=y_long_f),
+        "long_max": lambda i: rr.reduce_rows(dx["long_i"][0], "max", out=y_long_i),
+        "merge": lambda i: rr.splitk_lse_merge(*dx["merge"][i % 8], 1.0, torch.bfloat16,
+                                               out=dx["merge_out"][i % 8]),
+    }
+    names = list(ops) if not args.only else args.only.split(",")
+
+    # ------------------------------------------------------------ parity
+    parity = "skipped"
+    if not args.no_parity:
+        import oracle
+
+        log("parity check on sampled rows")
+        for n in names:
+            ops[n](0)
+        torch.cuda.synchronize()
+        ok = True
+        if "short_sum" in names or "short_max" in names:
+            xs = host["short"][:4096]
+            for op in ("sum", "max"):
+                y = rr.reduce_rows(dx["short"][0][:4096], op).cpu().numpy()
+                r = oracle.reduce_rows(xs, op)
+                ok &= bool(np.all(np.abs(y - r) <= 1e-6 + 1e-5 * np.abs(r)))
+        if "long_sum" in names:
+            y = y_long_f.cpu().numpy()
+            r = oracle.reduce_rows(host["long_f"][:2], "sum")
+            ok &= bool(np.all(np.abs(y[:2] - r) <= 1e-6 + 1e-5 * np.abs(r)))
+        if "long_max" in names:
+            ok &= bool(np.array_equal(y_long_i.cpu().numpy()[:2], oracle.reduce_rows(host["long_i"][:2], "max")))
+        if "softmax" in names:
+            y = dx["softmax_out"][0][:8].cpu().view(torch.int16).numpy().view(np.uint16)
+            r = oracle.softmax_rows(host["softmax"][:8], "bf16")
+            ok &= bool(bf16_ulp_diff(y, r).max() <= 1)
+        if "merge" in names:
+            oh, mh, lh = host["merge"]
+            y = dx["merge_out"][0].reshape(-1, 128)[:256].cpu().view(torch.int16).numpy().view(np.uint16)
+            r = oracle.splitk_lse_merge(np.ascontiguousarray(oh.reshape(8, -1, 128)[:, :256]),
+                                        np.ascontiguousarray(mh.reshape(8, -1)[:, :256]),
+                                        np.ascontiguousarray(lh.reshape(8, -1)[:, :256]), 1.0, "bf16")
+            ok &= bool(bf16_ulp_diff(y, r).max() <= 1)
+        parity = "ok" if ok else "FAILED"
+        log("parity %s" % parity)
+        if not ok:
+            sys.exit(1)
+
+    # ------------------------------------------------------------ timing
+    stream = torch.cuda.current_stream(dev)
+    log("warmup %d steps" % args.warmup)
+    for i in range(args.warmup):
+        for n in names:
+            ops[n](i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(K)] for n in names}
+    log("timing %d steps" % K)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(K):
+        for n in names:
+            a, b = ev[n][i]
+            a.record(stream)
+            ops[n](i)
+            b.record(stream)
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+    ms_per_step = t_total * 1e3 / K
+
+    per_op = {}
+    for n in names:
+        ts = sorted(a.elapsed_time(b) for a, b in ev[n])
+        mean = sum(ts) / len(ts)
+        per_op[n] = {"ms_mean": round(mean, 5), "ms_median": round(ts[len(ts) // 2], 5),
+                     "ms_min": round(ts[0], 5), "bytes": B[n],
+                     "GBps": round(B[n] / (mean * 1e-3) / 1e9, 1),
+                     "pct_peak": round(100 * B[n] / (mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 1)}
+    step_bytes = sum(B[n] for n in names)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # dominant kernel: the launch with the largest share of the step
+    dom = max(names, key=lambda n: per_op[n]["ms_mean"])
+    achieved = per_op[dom]["GBps"]
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        ent = tr.get("kernels", {}).get(dom)
+        if ent and tr.get("source_hash") == kernel_source_hash():
+            traffic = ent.get("bytes_per_launch")
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                "algorithmic_bytes": B[dom]}
+
+    # ------------------------------------------------------------ CPU baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        log("timing the oracle on a sample")
+        sample = {"short_rows": 1048576, "softmax_rows": 8192, "long_rows": 16, "lse_merge_rows": 32768}
+        oh, mh, lh = host["merge"]
+        o_s = np.ascontiguousarray(oh.reshape(8, -1, 128)[:, :sample["lse_merge_rows"]])
+        m_s = np.ascontiguousarray(mh.reshape(8, -1)[:, :sample["lse_merge_rows"]])
+        l_s = np.ascontiguousarray(lh.reshape(8, -1)[:, :sample["lse_merge_rows"]])
+        xs = host["short"][:sample["short_rows"]]
+        xsm = host["softmax"][:sample["softmax_rows"]]
+        xlf = host["long_f"][:sample["long_rows"]]
+        xli = host["long_i"][:sample["long_rows"]]
+        c0 = time.perf_counter()
+        oracle.reduce_rows(xs, "sum")
+        oracle.reduce_rows(xs, "max")
+        oracle.softmax_rows(xsm, "bf16")
+        oracle.reduce_rows(xlf, "sum")
+        oracle.reduce_rows(xli, "max")
+        oracle.splitk_lse_merge(o_s, m_s, l_s, 1.0, "bf16")
+        c_s = time.perf_counter() - c0
+        nb = (2 * (xs.nbytes + 4 * xs.shape[0]) + 2 * xsm.nbytes + xlf.nbytes + 4 + xli.nbytes + 4
+              + o_s.nbytes + m_s.nbytes + l_s.nbytes + o_s.shape[1] * 128 * 2)
+        cpu = {"value": round(nb / c_s / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "seconds": round(c_s, 2),
+               "sample": "one full step of the same workload (short_rows %d of 1048576 rows "
+                         "sum+max, softmax %d of 8192 rows, long_rows %d of 16 rows f32 sum + "
+                         "i32 max, lse_merge %d of 32768 rows); single-threaded C oracle"
+                         % (sample["short_rows"], sample["softmax_rows"], sample["long_rows"],
+                            sample["lse_merge_rows"])}
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32/f64 acc, bf16 io, i32",
+        "data": "synthetic (seeded generators in split_deterministic_combine_amd/synth.py)",
+        "config": {"workload": "rowwise suite: f32 sum+max [1048576,48] wave tier; bf16 softmax "
+                               "[8192,8192] block tier; f32 sum + i32 max [16,2^24] split-K; "
+                               "LSE merge P=8 O[8,32,128,128] -> bf16",
+                   "ops": names, "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBS, 1),
+                   "step_bytes": step_bytes, "parity": parity},
+        "per_op": per_op,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

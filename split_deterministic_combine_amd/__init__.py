@@ -1,1 +1,288 @@
-"""Deterministic row reductions on MI355X (binding placeholder)."""
+"""Deterministic row reductions on AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over ``librr.so`` (the C ABI in ``include/rr.h``).  This
+module only marshals arguments -- shapes, strides, dtypes, device pointers and
+the current stream -- and every step of the computation runs in the HIP
+kernels of the library.  There is no CPU fallback: if the library is not built
+the first call raises.
+
+Operations (names as in the C ABI):
+  reduce_rows        sum / max / min over the last axis (float32, int32)
+  softmax_rows       two-pass softmax over the last axis (bf16 / float32)
+  splitk_lse_merge   merge of P split-K partial attention outputs by their
+                     per-row (max, sum) statistics
+"""
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = [
+    "RRError", "reduce_rows", "softmax_rows", "splitk_lse_merge", "plan_reduce",
+    "plan_softmax", "select_tier", "workspace_bytes", "workspace_reset", "device_cu_count",
+    "version", "lib_path", "TIERS", "OPS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "librr.so")
+
+RR_OK = 0
+_DTYPES = {torch.float32: 0, torch.int32: 1, torch.bfloat16: 2}
+OPS = {"sum": 0, "max": 1, "min": 2}
+TIERS = {"auto": 0, "wave": 1, "block": 2, "tiled": 3, "serial": 4, "splitk": 5}
+TIER_NAMES = {v: k for k, v in TIERS.items()}
+KIND_REDUCE, KIND_SOFTMAX = 0, 1
+
+
+class RRError(RuntimeError):
+    """A librr call returned an error status."""
+
+    def __init__(self, status, msg):
+        super().__init__(msg)
+        self.status = status
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [
+        ("tier", ctypes.c_int32), ("block", ctypes.c_int32), ("grid", ctypes.c_int64),
+        ("lanes_per_row", ctypes.c_int32), ("slices", ctypes.c_int32),
+        ("slice_cols", ctypes.c_int64), ("workspace_bytes", ctypes.c_uint64),
+    ]
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def lib_path():
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lib_lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                "librr.so is not built (%s); build it with "
+                "`python -m split_deterministic_combine_amd.build`" % _LIB_PATH)
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp, i64, i32, st = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int
+        lib.rr_reduce_rows.argtypes = [vp, vp, i64, i64, i64, st, st, st, vp, ctypes.c_size_t, vp]
+        lib.rr_softmax_rows.argtypes = [vp, vp, i64, i64, i64, i64, st, st, st, vp]
+        lib.rr_splitk_lse_merge.argtypes = [vp, vp, vp, vp, i32, i64, i32, ctypes.c_float, st, vp]
+        lib.rr_plan_reduce.argtypes = [i64, i64, i64, st, st, st, i32, ctypes.POINTER(_Plan)]
+        lib.rr_plan_softmax.argtypes = [i64, i64, st, st, st, i32, ctypes.POINTER(_Plan)]
+        lib.rr_workspace_bytes.argtypes = [st, i64, i64, st, st, st, ctypes.POINTER(ctypes.c_size_t)]
+        lib.rr_select_tier.argtypes = [st, i64, i64, st, st, ctypes.POINTER(ctypes.c_int)]
+        lib.rr_workspace_reset.argtypes = [vp, ctypes.c_size_t, vp]
+        lib.rr_device_cu_count.argtypes = [ctypes.POINTER(ctypes.c_int32)]
+        lib.rr_status_string.argtypes = [st]
+        lib.rr_status_string.restype = ctypes.c_char_p
+        lib.rr_version.restype = ctypes.c_int
+        lib.rr_test_set_splitk_skew.argtypes = [i32]
+        lib.rr_test_set_splitk_skew.restype = None
+        for name in ("rr_reduce_rows", "rr_softmax_rows", "rr_splitk_lse_merge", "rr_plan_reduce",
+                     "rr_plan_softmax", "rr_workspace_bytes", "rr_select_tier",
+                     "rr_workspace_reset", "rr_device_cu_count"):
+            getattr(lib, name).restype = st
+        _lib = lib
+    return _lib
+
+
+def _check(status):
+    if status != RR_OK:
+        lib = _load()
+        raise RRError(status, lib.rr_status_string(status).decode())
+
+
+def version():
+    return _load().rr_version()
+
+
+def _stream_ptr(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _as_rows(x, name="x"):
+    """View ``x`` as [rows, cols] with a row stride; the last axis must be contiguous."""
+    if not isinstance(x, torch.Tensor) or not x.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if x.dim() == 0:
+        raise ValueError("%s must have at least one dimension" % name)
+    cols = x.shape[-1]
+    if x.dim() == 1:
+        x2 = x.reshape(1, cols)
+    else:
+        x2 = x.reshape(-1, cols) if not (x.dim() == 2) else x
+    if cols > 1 and x2.stride(1) != 1:
+        raise ValueError("%s: the last axis must be contiguous" % name)
+    rows = x2.shape[0]
+    ld = x2.stride(0) if rows > 1 else cols
+    return x2, rows, cols, max(ld, cols)
+
+
+def _dtype_code(t):
+    try:
+        return _DTYPES[t]
+    except KeyError:
+        raise TypeError("unsupported dtype %s" % t) from None
+
+
+# split-K workspaces, one per (device, stream); tickets reset themselves, so a
+# workspace stays zero between calls on its stream.
+_workspaces = {}
+
+
+def _workspace(device, stream_id, nbytes):
+    key = (device.index, stream_id)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 4096), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def reduce_rows(x, op="sum", tier="auto", out=None):
+    """Reduce every row of ``x`` over its last axis; returns shape ``x.shape[:-1]``.
+
+    ``op`` is "sum", "max" or "min"; ``x`` is float32 or int32 on the GPU.
+    ``tier`` is "auto" or one of "wave", "block", "tiled", "serial", "splitk".
+    """
+    lib = _load()
+    x2, rows, cols, ld = _as_rows(x)
+    dt = _dtype_code(x.dtype)
+    lead = x.shape[:-1]
+    if out is None:
+        out = torch.empty(lead, dtype=x.dtype, device=x.device)
+    if out.dtype != x.dtype or out.numel() != rows or not out.is_contiguous():
+        raise ValueError("out must be a contiguous %s tensor of %d elements" % (x.dtype, rows))
+    with torch.cuda.device(x.device):
+        stream = _stream_ptr(x.device)
+        plan = _Plan()
+        cu = ctypes.c_int32(0)
+        _check(lib.rr_device_cu_count(ctypes.byref(cu)))
+        _check(lib.rr_plan_reduce(rows, cols, ld, dt, OPS[op], TIERS[tier], cu.value,
+                                  ctypes.byref(plan)))
+        ws_ptr, ws_len = None, 0
+        if plan.workspace_bytes:
+            ws = _workspace(x.device, stream.value, plan.workspace_bytes)
+            ws_ptr, ws_len = ctypes.c_void_p(ws.data_ptr()), ws.numel()
+        _check(lib.rr_reduce_rows(ctypes.c_void_p(x2.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                  rows, cols, ld, dt, OPS[op], TIERS[tier], ws_ptr, ws_len, stream))
+    return out
+
+
+def softmax_rows(x, out_dtype=None, tier="auto", out=None):
+    """Softmax of every row of ``x`` over its last axis (x: bfloat16 or float32)."""
+    lib = _load()
+    x2, rows, cols, ld_x = _as_rows(x)
+    out_dtype = x.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty(x.shape, dtype=out_dtype, device=x.device)
+    if out.dtype != out_dtype or out.shape != x.shape:
+        raise ValueError("out must be a %s tensor of shape %s" % (out_dtype, tuple(x.shape)))
+    y2, _, _, ld_y = _as_rows(out, "out")
+    with torch.cuda.device(x.device):
+        _check(lib.rr_softmax_rows(ctypes.c_void_p(x2.data_ptr()), ctypes.c_void_p(y2.data_ptr()),
+                                   rows, cols, ld_x, ld_y, _dtype_code(x.dtype),
+                                   _dtype_code(out_dtype), TIERS[tier], _stream_ptr(x.device)))
+    return out
+
+
+def splitk_lse_merge(o_part, m_part, l_part, scale=1.0, out_dtype=torch.bfloat16, out=None):
+    """Merge P split-K partitions: o_part [P, *rows, depth], m_part / l_part [P, *rows].
+
+    Returns [*rows, depth] in ``out_dtype`` (bfloat16 or float32).
+    """
+    lib = _load()
+    for t, n in ((o_part, "o_part"), (m_part, "m_part"), (l_part, "l_part")):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.float32:
+            raise ValueError("%s must be a float32 GPU tensor" % n)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % n)
+    P, depth = o_part.shape[0], o_part.shape[-1]
+    rows_shape = o_part.shape[1:-1]
+    rows = 1
+    for s in rows_shape:
+        rows *= s
+    if tuple(m_part.shape) != (P, *rows_shape) or tuple(l_part.shape) != (P, *rows_shape):
+        raise ValueError("m_part and l_part must have shape %s" % ((P, *rows_shape),))
+    if out is None:
+        out = torch.empty((*rows_shape, depth), dtype=out_dtype, device=o_part.device)
+    if out.dtype != out_dtype or not out.is_contiguous() or out.numel() != rows * depth:
+        raise ValueError("out must be a contiguous %s tensor of %d elements" % (out_dtype, rows * depth))
+    with torch.cuda.device(o_part.device):
+        _check(lib.rr_splitk_lse_merge(ctypes.c_void_p(o_part.data_ptr()),
+                                       ctypes.c_void_p(m_part.data_ptr()),
+                                       ctypes.c_void_p(l_part.data_ptr()),
+                                       ctypes.c_void_p(out.data_ptr()), P, rows, depth,
+                                       float(scale), _dtype_code(out_dtype),
+                                       _stream_ptr(o_part.device)))
+    return out
+
+
+def _plan_dict(plan):
+    return {"tier": TIER_NAMES[plan.tier], "block": plan.block, "grid": plan.grid,
+            "lanes_per_row": plan.lanes_per_row, "slices": plan.slices,
+            "slice_cols": plan.slice_cols, "workspace_bytes": plan.workspace_bytes}
+
+
+def plan_reduce(rows, cols, dtype=torch.float32, op="sum", tier="auto", cu_count=256, ld=None):
+    """Host-only launch plan of rr_reduce_rows (needs no GPU)."""
+    lib = _load()
+    plan = _Plan()
+    _check(lib.rr_plan_reduce(rows, cols, cols if ld is None else ld, _dtype_code(dtype), OPS[op],
+                              TIERS[tier], cu_count, ctypes.byref(plan)))
+    return _plan_dict(plan)
+
+
+def plan_softmax(rows, cols, x_dtype=torch.bfloat16, y_dtype=None, tier="auto", cu_count=256):
+    """Host-only launch plan of rr_softmax_rows (needs no GPU)."""
+    lib = _load()
+    plan = _Plan()
+    y_dtype = x_dtype if y_dtype is None else y_dtype
+    _check(lib.rr_plan_softmax(rows, cols, _dtype_code(x_dtype), _dtype_code(y_dtype),
+                               TIERS[tier], cu_count, ctypes.byref(plan)))
+    return _plan_dict(plan)
+
+
+def select_tier(kind, rows, cols, dtype=torch.float32, op="sum"):
+    """Tier AUTO picks on the current device; kind is "reduce" or "softmax"."""
+    lib = _load()
+    t = ctypes.c_int(0)
+    k = {"reduce": KIND_REDUCE, "softmax": KIND_SOFTMAX}[kind]
+    _check(lib.rr_select_tier(k, rows, cols, _dtype_code(dtype), OPS[op], ctypes.byref(t)))
+    return TIER_NAMES[t.value]
+
+
+def workspace_bytes(rows, cols, dtype=torch.float32, op="sum", tier="auto"):
+    lib = _load()
+    n = ctypes.c_size_t(0)
+    _check(lib.rr_workspace_bytes(KIND_REDUCE, rows, cols, _dtype_code(dtype), OPS[op],
+                                  TIERS[tier], ctypes.byref(n)))
+    return n.value
+
+
+def workspace_reset(ws):
+    """Zero a workspace tensor on the current stream (fill kernel, no memset)."""
+    lib = _load()
+    with torch.cuda.device(ws.device):
+        _check(lib.rr_workspace_reset(ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
+                                      _stream_ptr(ws.device)))
+
+
+def device_cu_count():
+    lib = _load()
+    cu = ctypes.c_int32(0)
+    _check(lib.rr_device_cu_count(ctypes.byref(cu)))
+    return cu.value
+
+
+def _set_splitk_skew(sleeps_per_rank):
+    """Test hook: arrival-order skew for the split-K tier (0 turns it off)."""
+    _load().rr_test_set_splitk_skew(int(sleeps_per_rank))

@@ -1,0 +1,171 @@
+// rr_api.cpp -- the C ABI entry points of librr (see include/rr.h).
+//
+// Every entry point validates its arguments completely before it launches
+// anything, then launches on the caller's stream and returns without
+// synchronising.  No C++ exception leaves this file.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+
+#include "../../include/rr.h"
+#include "../../include/rr_test.h"
+#include "rr_config.hpp"
+#include "rr_launch.hpp"
+#include "rr_plan.hpp"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int32_t> g_cu_count[kMaxDevices];
+std::atomic<int32_t> g_splitk_skew{0};
+
+rr_status current_cu(int32_t* cu)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return RR_ERR_HIP;
+    if (dev >= 0 && dev < kMaxDevices) {
+        int32_t c = g_cu_count[dev].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *cu = c;
+            return RR_OK;
+        }
+    }
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1)
+        return RR_ERR_HIP;
+    if (dev >= 0 && dev < kMaxDevices) g_cu_count[dev].store(v, std::memory_order_relaxed);
+    *cu = v;
+    return RR_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Rows of `elem` bytes at stride `ld` elements start 16-byte aligned when the
+// base is and the stride is a multiple of 16 bytes (or there is one row).
+bool rows_aligned16(const void* p, int64_t ld, int64_t rows, int elem)
+{
+    return aligned(p, 16) && (rows <= 1 || ((ld * elem) % 16) == 0);
+}
+
+int elem_size(rr_dtype d) { return d == RR_BF16 ? 2 : 4; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" rr_status rr_device_cu_count(int32_t* cu_out)
+{
+    if (!cu_out) return RR_ERR_NULL;
+    return current_cu(cu_out);
+}
+
+extern "C" rr_status rr_reduce_rows(const void* x, void* y, int64_t rows, int64_t cols,
+                                    int64_t ld, rr_dtype dtype, rr_op op, rr_tier tier,
+                                    void* workspace, size_t workspace_bytes, void* stream)
+{
+    // Shape / type / tier checks that need no device.
+    rr_plan p;
+    rr_status st = rr::plan_reduce(rows, cols, ld, dtype, op, tier, 1, true, &p);
+    if (st != RR_OK) return st;
+    if (rows == 0) return RR_OK;
+    if (!y || (!x && cols > 0)) return RR_ERR_NULL;
+    int32_t cu = 0;
+    if ((st = current_cu(&cu)) != RR_OK) return st;
+    const bool vec = rows_aligned16(x, ld, rows, 4);
+    if ((st = rr::plan_reduce(rows, cols, ld, dtype, op, tier, cu, vec, &p)) != RR_OK) return st;
+
+    rr::ReduceLaunch a{x, y, rows, cols, ld, dtype, op, vec, workspace,
+                       g_splitk_skew.load(std::memory_order_relaxed), as_stream(stream)};
+    if (cols == 0) return rr::launch_reduce_identity(a);
+    if (p.tier == RR_TIER_SPLITK) {
+        if (!workspace || workspace_bytes < p.workspace_bytes || !aligned(workspace, 8))
+            return RR_ERR_WORKSPACE;
+    }
+    return rr::launch_reduce(p, a);
+}
+
+extern "C" rr_status rr_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols,
+                                     int64_t ld_x, int64_t ld_y, rr_dtype x_dtype,
+                                     rr_dtype y_dtype, rr_tier tier, void* stream)
+{
+    rr_plan p;
+    rr_status st = rr::plan_softmax(rows, cols, x_dtype, y_dtype, tier, 1, true, &p);
+    if (st != RR_OK) return st;
+    if (ld_x < cols || ld_y < cols) return RR_ERR_SHAPE;
+    if (rows == 0 || cols == 0) return RR_OK;
+    if (!x || !y) return RR_ERR_NULL;
+    if (x == y && (ld_x != ld_y || x_dtype != y_dtype)) return RR_ERR_SHAPE;
+    int32_t cu = 0;
+    if ((st = current_cu(&cu)) != RR_OK) return st;
+    const bool vec = rows_aligned16(x, ld_x, rows, elem_size(x_dtype)) &&
+                     rows_aligned16(y, ld_y, rows, elem_size(y_dtype));
+    if ((st = rr::plan_softmax(rows, cols, x_dtype, y_dtype, tier, cu, vec, &p)) != RR_OK)
+        return st;
+    rr::SoftmaxLaunch a{x, y, rows, cols, ld_x, ld_y, x_dtype, y_dtype, vec, as_stream(stream)};
+    return rr::launch_softmax(p, a);
+}
+
+extern "C" rr_status rr_splitk_lse_merge(const float* o_part, const float* m_part,
+                                         const float* l_part, void* out, int32_t P, int64_t rows,
+                                         int32_t depth, float scale, rr_dtype out_dtype,
+                                         void* stream)
+{
+    if (P < 1 || P > RR_MERGE_MAX_P || rows < 0 || depth < 1) return RR_ERR_SHAPE;
+    if (out_dtype != RR_BF16 && out_dtype != RR_F32) return RR_ERR_DTYPE;
+    if (rows == 0) return RR_OK;
+    if (!o_part || !m_part || !l_part || !out) return RR_ERR_NULL;
+    const bool vec = (depth % 4) == 0 && aligned(o_part, 16) &&
+                     aligned(out, out_dtype == RR_F32 ? 16 : 8);
+    rr::MergeLaunch a{o_part, m_part, l_part, out, P, rows, depth, scale, out_dtype, vec,
+                      as_stream(stream)};
+    return rr::launch_merge(a);
+}
+
+extern "C" rr_status rr_workspace_bytes(rr_kind kind, int64_t rows, int64_t cols, rr_dtype dtype,
+                                        rr_op op, rr_tier tier, size_t* bytes_out)
+{
+    if (!bytes_out) return RR_ERR_NULL;
+    if (kind == RR_KIND_SOFTMAX) {
+        *bytes_out = 0;
+        return RR_OK;
+    }
+    if (kind != RR_KIND_REDUCE) return RR_ERR_TIER;
+    int32_t cu = 0;
+    rr_status st = current_cu(&cu);
+    if (st != RR_OK) return st;
+    rr_plan p;
+    if ((st = rr::plan_reduce(rows, cols, cols, dtype, op, tier, cu, true, &p)) != RR_OK) return st;
+    *bytes_out = (size_t)p.workspace_bytes;
+    return RR_OK;
+}
+
+extern "C" rr_status rr_select_tier(rr_kind kind, int64_t rows, int64_t cols, rr_dtype dtype,
+                                    rr_op op, rr_tier* tier_out)
+{
+    if (!tier_out) return RR_ERR_NULL;
+    int32_t cu = 0;
+    rr_status st = current_cu(&cu);
+    if (st != RR_OK) return st;
+    rr_plan p;
+    if (kind == RR_KIND_REDUCE)
+        st = rr::plan_reduce(rows, cols, cols, dtype, op, RR_TIER_AUTO, cu, true, &p);
+    else if (kind == RR_KIND_SOFTMAX)
+        st = rr::plan_softmax(rows, cols, dtype, dtype, RR_TIER_AUTO, cu, true, &p);
+    else
+        return RR_ERR_TIER;
+    if (st != RR_OK) return st;
+    *tier_out = (rr_tier)p.tier;
+    return RR_OK;
+}
+
+extern "C" rr_status rr_workspace_reset(void* workspace, size_t bytes, void* stream)
+{
+    if (bytes == 0) return RR_OK;
+    if (!workspace) return RR_ERR_NULL;
+    return rr::launch_fill_zero(workspace, bytes, as_stream(stream));
+}
+
+extern "C" void rr_test_set_splitk_skew(int32_t sleeps_per_rank)
+{
+    g_splitk_skew.store(sleeps_per_rank < 0 ? 0 : sleeps_per_rank, std::memory_order_relaxed);
+}

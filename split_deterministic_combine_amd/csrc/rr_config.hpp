@@ -1,0 +1,59 @@
+// rr_config.hpp -- launch constants shared by the host planner and the
+// kernels.  Plain C++ (no HIP), so the planner builds and runs on any host.
+#pragma once
+
+#include <stdint.h>
+
+namespace rr {
+
+// Threads per workgroup for the block, split-K and softmax block tiers, and
+// for the wave / tiled / serial tiers (which pack rows into a workgroup).
+constexpr int kBlockThreads = 256;
+constexpr int kWavesPerBlock = kBlockThreads / 64;
+
+// Wave tier: row groups handled by one wavefront per launch (independent
+// loads in flight per lane).
+constexpr int kWaveRowGroups = 4;
+
+// Tiled tier: rows owned by one thread (the page's emit_tile_width).
+constexpr int kTiledRows = 4;
+
+// Split-K trigger and slice sizing.
+constexpr int64_t kSplitKMinCols = 65536;
+constexpr int64_t kSplitKMinSliceCols = 16384;
+constexpr int kSplitKMaxSlices = 256;
+constexpr int kSplitKBlocksPerCU = 4;  // G aims at this many workgroups per CU in total
+
+// Block-tier loads in flight per thread (128-bit each).
+constexpr int kBlockUnroll = 4;
+constexpr int kSplitKUnroll = 8;
+
+// Softmax block tier: 16-byte chunks per thread held in registers.  Rows
+// needing more than kSoftmaxMaxChunks chunks per thread use the streaming
+// variant that reads x twice.
+constexpr int kSoftmaxMaxChunks = 8;
+
+// LSE merge: partitions staged per batch of loads, and workgroup size.
+constexpr int kMergeBatch = 8;
+constexpr int kMergeMaxP = 256;
+
+// Largest grid.x the launchers use; kernels loop over the remainder.
+constexpr int64_t kMaxGrid = 1 << 30;
+
+// Workspace layout for split-K: per-row tickets (uint32), padded to 256 B,
+// then per-(row, slice) partials of 8 bytes.
+constexpr int64_t kWorkspaceAlign = 256;
+
+constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+constexpr int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+// Lanes sharing one row in the wave tier, from the number of 128-bit (or
+// scalar) chunks a row spans.
+constexpr int wave_lanes_for_chunks(int64_t chunks)
+{
+    if (chunks <= 4) return 4;
+    if (chunks <= 16) return 16;
+    return 64;
+}
+
+}  // namespace rr

@@ -1,0 +1,283 @@
+// rr_device.hpp -- device building blocks for the gfx950 row-reduce kernels.
+//
+// Monoid states, 64-lane wavefront combines (DPP within 16-lane rows, then a
+// fixed-order fold of the four rows), the cross-wavefront LDS combine with a
+// broadcast result, 128-bit loads and bf16 packing.
+//
+// Every combine here has a fixed shape that depends only on the launch
+// geometry, never on timing, so a kernel built from these pieces returns the
+// same bits on every run.  Every combine function is commutative bit for bit
+// (a+b == b+a in IEEE arithmetic, max/min are symmetric, and the online
+// softmax pair below is written symmetrically), which the mirror-pattern DPP
+// steps rely on: after each step all lanes of a group hold the same bits.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rr {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+
+// ------------------------------------------------------------------ DPP
+// DPP16 controls (GCN/CDNA): quad_perm selects within groups of 4 lanes;
+// row_half_mirror reverses each 8-lane half row; row_mirror reverses each
+// 16-lane row.
+enum : int {
+    kDppQuadSwap1 = 0xB1,  // quad_perm [1,0,3,2]
+    kDppQuadSwap2 = 0x4E,  // quad_perm [2,3,0,1]
+    kDppHalfMirror = 0x141,
+    kDppMirror = 0x140,
+};
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// DPP move of any 4- or 8-byte trivially copyable value.
+template <int CTRL, class T>
+__device__ __forceinline__ T dpp(T v)
+{
+    static_assert(sizeof(T) == 4 || sizeof(T) == 8, "dpp of 4 or 8 bytes");
+    if constexpr (sizeof(T) == 4) {
+        return __builtin_bit_cast(T, dpp_u32<CTRL>(__builtin_bit_cast(uint32_t, v)));
+    } else {
+        struct P { uint32_t lo, hi; };
+        P p = __builtin_bit_cast(P, v);
+        p.lo = dpp_u32<CTRL>(p.lo);
+        p.hi = dpp_u32<CTRL>(p.hi);
+        return __builtin_bit_cast(T, p);
+    }
+}
+
+template <class T>
+__device__ __forceinline__ T readlane(T v, int lane)
+{
+    static_assert(sizeof(T) == 4 || sizeof(T) == 8, "readlane of 4 or 8 bytes");
+    if constexpr (sizeof(T) == 4) {
+        return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+    } else {
+        struct P { int lo, hi; };
+        P p = __builtin_bit_cast(P, v);
+        p.lo = __builtin_amdgcn_readlane(p.lo, lane);
+        p.hi = __builtin_amdgcn_readlane(p.hi, lane);
+        return __builtin_bit_cast(T, p);
+    }
+}
+
+// ------------------------------------------------------------- monoids
+// IEEE 754 totalOrder as a signed-integer key: non-negative patterns keep
+// their order, negative patterns reverse their magnitude bits.  The map is
+// its own inverse and puts -0 below +0 and NaNs by sign and payload.
+__device__ __forceinline__ int32_t f32_order_key(float x)
+{
+    int32_t b = __float_as_int(x);
+    return b ^ ((b >> 31) & 0x7FFFFFFF);
+}
+__device__ __forceinline__ float f32_from_order_key(int32_t k)
+{
+    return __int_as_float(k ^ ((k >> 31) & 0x7FFFFFFF));
+}
+
+// float SUM: double accumulator, one rounding at the end.
+struct SumF32 {
+    using in_t = float;
+    using acc_t = double;
+    __device__ static acc_t identity() { return 0.0; }
+    __device__ static acc_t lift(float x) { return (double)x; }
+    __device__ static acc_t combine(acc_t a, acc_t b) { return a + b; }
+    __device__ static float finish(acc_t a) { return (float)a; }
+};
+// float MAX / MIN over totalOrder keys (identities are the extreme keys).
+struct MaxF32 {
+    using in_t = float;
+    using acc_t = int32_t;
+    __device__ static acc_t identity() { return INT32_MIN; }
+    __device__ static acc_t lift(float x) { return f32_order_key(x); }
+    __device__ static acc_t combine(acc_t a, acc_t b) { return a > b ? a : b; }
+    __device__ static float finish(acc_t a) { return f32_from_order_key(a); }
+};
+struct MinF32 {
+    using in_t = float;
+    using acc_t = int32_t;
+    __device__ static acc_t identity() { return INT32_MAX; }
+    __device__ static acc_t lift(float x) { return f32_order_key(x); }
+    __device__ static acc_t combine(acc_t a, acc_t b) { return a < b ? a : b; }
+    __device__ static float finish(acc_t a) { return f32_from_order_key(a); }
+};
+// int32 SUM wraps modulo 2^32 (unsigned arithmetic), so order never matters.
+struct SumI32 {
+    using in_t = int32_t;
+    using acc_t = uint32_t;
+    __device__ static acc_t identity() { return 0u; }
+    __device__ static acc_t lift(int32_t x) { return (uint32_t)x; }
+    __device__ static acc_t combine(acc_t a, acc_t b) { return a + b; }
+    __device__ static int32_t finish(acc_t a) { return (int32_t)a; }
+};
+struct MaxI32 {
+    using in_t = int32_t;
+    using acc_t = int32_t;
+    __device__ static acc_t identity() { return INT32_MIN; }
+    __device__ static acc_t lift(int32_t x) { return x; }
+    __device__ static acc_t combine(acc_t a, acc_t b) { return a > b ? a : b; }
+    __device__ static int32_t finish(acc_t a) { return a; }
+};
+struct MinI32 {
+    using in_t = int32_t;
+    using acc_t = int32_t;
+    __device__ static acc_t identity() { return INT32_MAX; }
+    __device__ static acc_t lift(int32_t x) { return x; }
+    __device__ static acc_t combine(acc_t a, acc_t b) { return a < b ? a : b; }
+    __device__ static int32_t finish(acc_t a) { return a; }
+};
+
+// Online softmax state (m, s): m the largest value seen, s = sum exp(x - m).
+// (m1, s1) + (m2, s2) = (M, s1 exp(m1 - M) + s2 exp(m2 - M)), M = max(m1, m2);
+// the identity is (-inf, 0) and two identities combine without evaluating
+// exp(-inf - -inf).  Exponentials are base 2 on pre-scaled differences.
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct MS {
+    float m;
+    float s;
+};
+
+__device__ __forceinline__ float exp2_f32(float t) { return exp2f(t); }
+
+struct SoftmaxMS {
+    using acc_t = MS;
+    __device__ static acc_t identity() { return MS{-__builtin_inff(), 0.0f}; }
+    __device__ static acc_t combine(acc_t a, acc_t b)
+    {
+        float M = fmaxf(a.m, b.m);
+        if (M == -__builtin_inff())
+            return MS{M, 0.0f};
+        float s = a.s * exp2_f32((a.m - M) * kLog2e) + b.s * exp2_f32((b.m - M) * kLog2e);
+        return MS{M, s};
+    }
+};
+
+// ----------------------------------------------------- wavefront combines
+
+// Combine within aligned groups of S lanes (S in {1, 2, 4, 8, 16}); every
+// lane of a group ends with the group's result.
+template <class M, int S>
+__device__ __forceinline__ typename M::acc_t group_reduce(typename M::acc_t v)
+{
+    static_assert(S == 1 || S == 2 || S == 4 || S == 8 || S == 16, "group of 1..16 lanes");
+    if constexpr (S >= 2) v = M::combine(v, dpp<kDppQuadSwap1>(v));
+    if constexpr (S >= 4) v = M::combine(v, dpp<kDppQuadSwap2>(v));
+    if constexpr (S >= 8) v = M::combine(v, dpp<kDppHalfMirror>(v));
+    if constexpr (S >= 16) v = M::combine(v, dpp<kDppMirror>(v));
+    return v;
+}
+
+// Combine all 64 lanes; the result is wave-uniform.  The four 16-lane rows
+// are folded in ascending row order.
+template <class M>
+__device__ __forceinline__ typename M::acc_t wave_reduce(typename M::acc_t v)
+{
+    v = group_reduce<M, 16>(v);
+    typename M::acc_t r = readlane(v, 0);
+    r = M::combine(r, readlane(v, 16));
+    r = M::combine(r, readlane(v, 32));
+    r = M::combine(r, readlane(v, 48));
+    return r;
+}
+
+// Groups of S in {32, 64}: two or four rows folded in ascending order via
+// cross-lane reads; every lane of a group gets the group's result.
+template <class M, int S>
+__device__ __forceinline__ typename M::acc_t group_reduce_wide(typename M::acc_t v)
+{
+    static_assert(S == 32 || S == 64, "wide group");
+    using A = typename M::acc_t;
+    if constexpr (S == 64) {
+        return wave_reduce<M>(v);
+    } else {
+        v = group_reduce<M, 16>(v);
+        A r0 = readlane(v, 0), r1 = readlane(v, 16), r2 = readlane(v, 32), r3 = readlane(v, 48);
+        A lo = M::combine(r0, r1), hi = M::combine(r2, r3);
+        return lane_id() < 32 ? lo : hi;
+    }
+}
+
+template <class M, int S>
+__device__ __forceinline__ typename M::acc_t segment_reduce(typename M::acc_t v)
+{
+    if constexpr (S <= 16)
+        return group_reduce<M, S>(v);
+    else
+        return group_reduce_wide<M, S>(v);
+}
+
+// Workgroup combine of NT threads: wave combine, then each wave's lane 0
+// writes its result to an LDS slot and every thread folds the slots in wave
+// order after one barrier, so all threads return identical bits.  The caller
+// alternates between two slot arrays from one call to the next: a wave that
+// runs ahead can then only write the array its peers are not reading.
+template <class M, int NT>
+__device__ __forceinline__ typename M::acc_t block_reduce(typename M::acc_t v,
+                                                          typename M::acc_t* slot)
+{
+    constexpr int NW = NT / kWave;
+    v = wave_reduce<M>(v);
+    if constexpr (NW == 1) {
+        return v;
+    } else {
+        if (lane_id() == 0)
+            slot[threadIdx.x / kWave] = v;
+        __syncthreads();
+        typename M::acc_t r = slot[0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w)
+            r = M::combine(r, slot[w]);
+        return r;
+    }
+}
+
+// ---------------------------------------------------------------- memory
+
+template <class T, int N>
+struct Vec {
+    T v[N];
+};
+
+// One 128-bit load of N elements of 4 bytes.
+template <class T>
+__device__ __forceinline__ Vec<T, 4> load4(const T* p)
+{
+    static_assert(sizeof(T) == 4, "4-byte elements");
+    uint4 u = *reinterpret_cast<const uint4*>(p);
+    Vec<T, 4> r;
+    r.v[0] = __builtin_bit_cast(T, u.x);
+    r.v[1] = __builtin_bit_cast(T, u.y);
+    r.v[2] = __builtin_bit_cast(T, u.z);
+    r.v[3] = __builtin_bit_cast(T, u.w);
+    return r;
+}
+
+// bf16 <-> f32.  bf16 is the top half of a binary32, so widening is a shift;
+// narrowing rounds to nearest even in hardware (v_cvt_pk_bf16_f32).
+typedef float rr_f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 rr_bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
+{
+    rr_f32x2 f = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, rr_bf16x2));
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float a)
+{
+    return __builtin_bit_cast(uint16_t, (__bf16)a);
+}
+
+}  // namespace rr

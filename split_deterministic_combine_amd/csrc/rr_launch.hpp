@@ -1,0 +1,52 @@
+// rr_launch.hpp -- internal interface between the ABI entry points and the
+// kernel launchers (one launcher per operation, in its own translation unit).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/rr.h"
+
+namespace rr {
+
+struct ReduceLaunch {
+    const void* x;
+    void* y;
+    int64_t rows, cols, ld;
+    rr_dtype dtype;
+    rr_op op;
+    bool vec;             // 128-bit loads allowed (alignment checked by the caller)
+    void* workspace;      // split-K only
+    int skew;             // test hook: split-K arrival skew (0 = off)
+    hipStream_t stream;
+};
+
+struct SoftmaxLaunch {
+    const void* x;
+    void* y;
+    int64_t rows, cols, ld_x, ld_y;
+    rr_dtype x_dtype, y_dtype;
+    bool vec;
+    hipStream_t stream;
+};
+
+struct MergeLaunch {
+    const float* o;
+    const float* m;
+    const float* l;
+    void* out;
+    int32_t P;
+    int64_t rows;
+    int32_t depth;
+    float scale;
+    rr_dtype out_dtype;
+    bool vec;
+    hipStream_t stream;
+};
+
+rr_status launch_reduce(const rr_plan& plan, const ReduceLaunch& a);
+rr_status launch_reduce_identity(const ReduceLaunch& a);  // cols == 0
+rr_status launch_softmax(const rr_plan& plan, const SoftmaxLaunch& a);
+rr_status launch_merge(const MergeLaunch& a);
+rr_status launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
+
+}  // namespace rr

@@ -1,0 +1,249 @@
+// rr_merge.hip -- split-K log-sum-exp merge of partial attention outputs.
+//
+// "fa4_splitk_reduce_scatter_write", per-band steps: each partition's output
+// is scaled by its weight w[b], the other partitions' outputs are
+// accumulated onto it, and the result is packed to bf16; every partition
+// joins, and an empty one contributes nothing.  The pages' statistics are the
+// row max and row sum of each partition (own_max, own_sum).
+//
+// Per row: partition p is empty when l_p <= 0 or m_p == -inf; M is the
+// largest m_p of the non-empty ones; w_p = exp(scale * (m_p - M)) * l_p;
+// W = sum w_p; out = sum over non-empty p (ascending) of (w_p / W) * O_p.
+// Weights and the accumulation are double precision with fused multiply-add.
+//
+// One workgroup takes `rw` rows.  Phase 1 stages (m_p, l_p) of those rows in
+// LDS, phase 2 forms w_p, phase 3 the coefficients c_p = w_p / W (or -1 for
+// an empty partition, which is then skipped -- a NaN O_p of an empty
+// partition never enters the sum).  The depth axis is spread over LPR lanes
+// per row with 128-bit loads; the first batch of partial outputs is loaded
+// before the weight phases so its latency overlaps them.
+#include <hip/hip_runtime.h>
+
+#include "rr_config.hpp"
+#include "rr_device.hpp"
+#include "rr_launch.hpp"
+#include "rr_launch_util.hpp"
+
+namespace rr {
+
+template <class YT>
+struct MergeOut;
+template <>
+struct MergeOut<uint16_t> {
+    __device__ static void four(uint16_t* p, const double* a)
+    {
+        uint2 u;
+        u.x = pack_bf16x2((float)a[0], (float)a[1]);
+        u.y = pack_bf16x2((float)a[2], (float)a[3]);
+        *reinterpret_cast<uint2*>(p) = u;
+    }
+    __device__ static void one(uint16_t* p, double a) { *p = f32_to_bf16_bits((float)a); }
+};
+template <>
+struct MergeOut<float> {
+    __device__ static void four(float* p, const double* a)
+    {
+        *reinterpret_cast<float4*>(p) = make_float4((float)a[0], (float)a[1], (float)a[2], (float)a[3]);
+    }
+    __device__ static void one(float* p, double a) { *p = (float)a; }
+};
+
+template <int VE>
+struct OChunk {
+    float v[VE];
+};
+
+template <int VE>
+__device__ __forceinline__ OChunk<VE> load_o(const float* p)
+{
+    OChunk<VE> c;
+    if constexpr (VE == 4) {
+        float4 u = *reinterpret_cast<const float4*>(p);
+        c.v[0] = u.x; c.v[1] = u.y; c.v[2] = u.z; c.v[3] = u.w;
+    } else {
+        c.v[0] = *p;
+    }
+    return c;
+}
+
+// LDS per workgroup: per (row, partition) one double w and one 8-byte cell
+// that first holds (m_p, l_p) as two floats and then the coefficient c_p
+// (the cell array has at least one entry per thread).
+template <class YT, int VE, int LPR>
+__global__ __launch_bounds__(kBlockThreads) void k_lse_merge(const float* __restrict__ o,
+                                                             const float* __restrict__ m,
+                                                             const float* __restrict__ l,
+                                                             YT* __restrict__ out, int32_t P,
+                                                             int64_t rows, int32_t depth,
+                                                             float scale, int32_t rw)
+{
+    constexpr int B = kMergeBatch;
+    extern __shared__ double lds[];
+    const int32_t npairs = rw * P;
+    double* wd = lds;                                      // [npairs]
+    double* cell = lds + npairs;                           // [max(npairs, block)]
+    float2* stat = reinterpret_cast<float2*>(cell);        // same cells as (m, l)
+
+    const int q = threadIdx.x / LPR;       // row of this lane within the workgroup
+    const int li = threadIdx.x % LPR;      // lane within the row
+    const int64_t nblocks = ceil_div(rows, rw);
+
+    for (int64_t blk = blockIdx.x; blk < nblocks; blk += gridDim.x) {
+        const int64_t row_base = blk * rw;
+        const int64_t r = row_base + q;
+        const bool row_ok = q < rw && r < rows;
+        const int64_t d_first = (int64_t)li * VE;
+        const bool lane_ok = row_ok && d_first < depth;
+
+        // (m_p, l_p) of this thread's first (row, partition) pair ...  The
+        // loads below are unconditional at clamped, always valid addresses
+        // (branch-free code keeps the later waits partial); values loaded
+        // for lanes without work are discarded.
+        const int32_t i0 = (int32_t)threadIdx.x < npairs ? (int32_t)threadIdx.x : npairs - 1;
+        const int32_t q0 = i0 / P, p0i = i0 - q0 * P;
+        const int64_t r0 = row_base + q0 < rows ? row_base + q0 : rows - 1;
+        const float m0 = m[(int64_t)p0i * rows + r0];
+        const float l0 = l[(int64_t)p0i * rows + r0];
+        __builtin_amdgcn_sched_barrier(0);  // issue (m, l) before the partial outputs
+        // ... then the first batch of partial outputs, consumed after the
+        // weight phases, so the HBM latency of both overlaps them.
+        const int64_t rc = r < rows ? r : rows - 1;
+        const int64_t dc = lane_ok ? d_first : 0;
+        OChunk<VE> ch[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+            ch[b] = load_o<VE>(o + ((int64_t)(b < P ? b : P - 1) * rows + rc) * depth + dc);
+        const bool st0_ok = (int32_t)threadIdx.x < npairs && row_base + q0 < rows;
+
+        // Phase 1: stage (m_p, l_p) in LDS.  Every thread writes its cell
+        // (cells past npairs are never read), so no branch separates the
+        // loads above from this use.
+        stat[threadIdx.x] = make_float2(st0_ok ? m0 : -__builtin_inff(), st0_ok ? l0 : 0.0f);
+        for (int32_t i = threadIdx.x + kBlockThreads; i < npairs; i += kBlockThreads) {
+            const int32_t qq = i / P, p = i - qq * P;
+            float2 st = make_float2(-__builtin_inff(), 0.0f);
+            if (row_base + qq < rows)
+                st = make_float2(m[(int64_t)p * rows + row_base + qq],
+                                 l[(int64_t)p * rows + row_base + qq]);
+            stat[i] = st;
+        }
+        __syncthreads();
+        // Phase 2: M over the non-empty partitions of the row, then w_p.
+        for (int32_t i = threadIdx.x; i < npairs; i += kBlockThreads) {
+            const int32_t qq = i / P;
+            const float2* rs = stat + (int64_t)qq * P;
+            bool any = false;
+            double M = 0.0;
+            for (int32_t pp = 0; pp < P; ++pp) {
+                const float2 s = rs[pp];
+                if (s.y > 0.0f && s.x > -__builtin_inff()) {
+                    if (!any || (double)s.x > M)
+                        M = (double)s.x;
+                    any = true;
+                }
+            }
+            const float2 s = stat[i];
+            const bool live = s.y > 0.0f && s.x > -__builtin_inff();
+            wd[i] = live ? exp((double)scale * ((double)s.x - M)) * (double)s.y : 0.0;
+        }
+        __syncthreads();
+        // Phase 3: W in ascending partition order, then c_p (or -1 if empty).
+        for (int32_t i = threadIdx.x; i < npairs; i += kBlockThreads) {
+            const int32_t qq = i / P;
+            const double* wrow = wd + (int64_t)qq * P;
+            double W = 0.0;
+            for (int32_t pp = 0; pp < P; ++pp)
+                W += wrow[pp];
+            const float2 s = stat[i];
+            const bool live = s.y > 0.0f && s.x > -__builtin_inff();
+            cell[i] = live ? wd[i] / W : -1.0;
+        }
+        __syncthreads();
+
+        // Accumulate: out[d] = sum_p c_p * O_p[d], ascending p, empty p skipped.
+        if (row_ok) {
+            const double* c = cell + (int64_t)q * P;
+            for (int64_t d0 = d_first; d0 < depth; d0 += (int64_t)LPR * VE) {
+                double acc[VE];
+#pragma unroll
+                for (int e = 0; e < VE; ++e)
+                    acc[e] = 0.0;
+                for (int32_t p0 = 0; p0 < P; p0 += B) {
+                    if (d0 != d_first || p0 != 0) {
+#pragma unroll
+                        for (int b = 0; b < B; ++b)
+                            ch[b] = load_o<VE>(o + ((int64_t)(p0 + b < P ? p0 + b : P - 1) * rows + r) * depth + d0);
+                    }
+#pragma unroll
+                    for (int b = 0; b < B; ++b) {
+                        if (p0 + b < P) {
+                            const double cp = c[p0 + b];
+                            if (cp >= 0.0) {
+#pragma unroll
+                                for (int e = 0; e < VE; ++e)
+                                    acc[e] = fma(cp, (double)ch[b].v[e], acc[e]);
+                            }
+                        }
+                    }
+                }
+                YT* orow = out + r * depth + d0;
+                if (VE == 4 && d0 + 4 <= depth) {
+                    MergeOut<YT>::four(orow, acc);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < VE; ++e)
+                        if (d0 + e < depth)
+                            MergeOut<YT>::one(orow + e, acc[e]);
+                }
+            }
+        }
+        __syncthreads();  // LDS is reused by the next row block
+    }
+}
+
+static int lanes_per_row(int32_t depth, int ve)
+{
+    const int64_t chunks = ceil_div(depth, ve);
+    int lpr = 4;
+    while (lpr < 64 && lpr < chunks)
+        lpr *= 2;
+    return lpr;
+}
+
+template <class YT, int VE, int LPR>
+static rr_status launch_lpr(const MergeLaunch& a)
+{
+    constexpr int RW = kBlockThreads / LPR;
+    // 16 bytes of LDS per (row, partition); keep a workgroup within 32 KiB.
+    int32_t rw = (int32_t)(32768 / (16 * (int64_t)a.P));
+    if (rw > RW) rw = RW;
+    if (rw < 1) rw = 1;
+    int64_t grid = ceil_div(a.rows, rw);
+    if (grid > kMaxGrid) grid = kMaxGrid;
+    const int64_t npairs = (int64_t)rw * a.P;
+    const size_t lds = (size_t)8 * npairs + (size_t)8 * (npairs > kBlockThreads ? npairs : kBlockThreads);
+    return launch_kernel(k_lse_merge<YT, VE, LPR>, dim3((unsigned)grid), dim3(kBlockThreads), lds,
+                         a.stream, a.o, a.m, a.l, static_cast<YT*>(a.out), a.P, a.rows, a.depth,
+                         a.scale, rw);
+}
+
+template <class YT, int VE>
+static rr_status launch_ve(const MergeLaunch& a)
+{
+    switch (lanes_per_row(a.depth, VE)) {
+    case 4: return launch_lpr<YT, VE, 4>(a);
+    case 8: return launch_lpr<YT, VE, 8>(a);
+    case 16: return launch_lpr<YT, VE, 16>(a);
+    case 32: return launch_lpr<YT, VE, 32>(a);
+    default: return launch_lpr<YT, VE, 64>(a);
+    }
+}
+
+rr_status launch_merge(const MergeLaunch& a)
+{
+    if (a.out_dtype == RR_BF16)
+        return a.vec ? launch_ve<uint16_t, 4>(a) : launch_ve<uint16_t, 1>(a);
+    return a.vec ? launch_ve<float, 4>(a) : launch_ve<float, 1>(a);
+}
+
+}  // namespace rr

@@ -1,0 +1,145 @@
+// rr_plan.cpp -- tier selection and launch geometry (host only, no HIP).
+//
+// "reduce" (algorithm.gpu.rowwise), tier semantics, describes what each tier
+// does -- a wavefront per short row, a workgroup striding along a row, a
+// thread owning several adjacent rows, one thread per row, and several
+// workgroups per row when there are fewer rows than compute units -- but
+// gives no thresholds.  The thresholds below are this library's.
+#include "rr_plan.hpp"
+
+#include <string.h>
+
+#include "rr_config.hpp"
+
+namespace rr {
+
+uint64_t splitk_workspace_bytes(int64_t rows, int32_t slices)
+{
+    return (uint64_t)(round_up(rows * 4, kWorkspaceAlign) + rows * (int64_t)slices * 8);
+}
+
+static rr_tier auto_tier_reduce(int64_t rows, int64_t cols, int32_t cu)
+{
+    if (rows < cu && cols >= kSplitKMinCols) return RR_TIER_SPLITK;
+    if (cols <= 8) return RR_TIER_TILED;
+    if (cols <= 64) return RR_TIER_WAVE;
+    return RR_TIER_BLOCK;
+}
+
+static void fill_rowwise_geometry(rr_tier tier, int64_t rows, int64_t cols, int vec_elems,
+                                  rr_plan* p)
+{
+    p->tier = tier;
+    p->block = kBlockThreads;
+    p->lanes_per_row = 0;
+    p->slices = 1;
+    p->slice_cols = cols;
+    p->workspace_bytes = 0;
+    switch (tier) {
+    case RR_TIER_WAVE: {
+        int s = wave_lanes_for_chunks(ceil_div(cols, vec_elems));
+        p->lanes_per_row = s;
+        int64_t rows_per_block = (int64_t)kWavesPerBlock * (64 / s) * kWaveRowGroups;
+        p->grid = ceil_div(rows, rows_per_block);
+        break;
+    }
+    case RR_TIER_TILED:
+        p->grid = ceil_div(rows, (int64_t)kBlockThreads * kTiledRows);
+        break;
+    case RR_TIER_SERIAL:
+        p->grid = ceil_div(rows, (int64_t)kBlockThreads);
+        break;
+    default:  // BLOCK: one workgroup per row
+        p->grid = rows;
+        break;
+    }
+    if (p->grid > kMaxGrid) p->grid = kMaxGrid;
+}
+
+rr_status plan_reduce(int64_t rows, int64_t cols, int64_t ld, rr_dtype dtype, rr_op op,
+                      rr_tier tier, int32_t cu_count, bool vec, rr_plan* out)
+{
+    if (!out) return RR_ERR_NULL;
+    if (rows < 0 || cols < 0 || ld < cols) return RR_ERR_SHAPE;
+    if (dtype != RR_F32 && dtype != RR_I32) return RR_ERR_DTYPE;
+    if (op != RR_SUM && op != RR_MAX && op != RR_MIN) return RR_ERR_OP;
+    if (cu_count < 1) return RR_ERR_SHAPE;
+    if ((int)tier < RR_TIER_AUTO || (int)tier > RR_TIER_SPLITK) return RR_ERR_TIER;
+
+    rr_tier t = tier == RR_TIER_AUTO ? auto_tier_reduce(rows, cols, cu_count) : tier;
+    if (t == RR_TIER_WAVE && cols > 64) return RR_ERR_TIER;
+
+    memset(out, 0, sizeof *out);
+    const int vec_elems = vec ? 4 : 1;
+    if (t != RR_TIER_SPLITK) {
+        fill_rowwise_geometry(t, rows, cols, vec_elems, out);
+        return RR_OK;
+    }
+    // Split-K: G slices per row, each a multiple of 4 columns.
+    int64_t g = ceil_div((int64_t)kSplitKBlocksPerCU * cu_count, rows > 0 ? rows : 1);
+    int64_t g_cap = ceil_div(cols, kSplitKMinSliceCols);
+    if (g_cap > kSplitKMaxSlices) g_cap = kSplitKMaxSlices;
+    if (g > g_cap) g = g_cap;
+    if (g < 1) g = 1;
+    int64_t slice = round_up(ceil_div(cols > 0 ? cols : 1, g), 4);
+    g = ceil_div(cols > 0 ? cols : 1, slice);  // every slice non-empty
+    out->tier = RR_TIER_SPLITK;
+    out->block = kBlockThreads;
+    out->lanes_per_row = 0;
+    out->slices = (int32_t)g;
+    out->slice_cols = slice;
+    out->grid = rows * g;
+    out->workspace_bytes = splitk_workspace_bytes(rows, (int32_t)g);
+    return RR_OK;
+}
+
+rr_status plan_softmax(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype y_dtype,
+                       rr_tier tier, int32_t cu_count, bool vec, rr_plan* out)
+{
+    if (!out) return RR_ERR_NULL;
+    if (rows < 0 || cols < 0) return RR_ERR_SHAPE;
+    if ((x_dtype != RR_F32 && x_dtype != RR_BF16) || (y_dtype != RR_F32 && y_dtype != RR_BF16))
+        return RR_ERR_DTYPE;
+    if (cu_count < 1) return RR_ERR_SHAPE;
+    if ((int)tier < RR_TIER_AUTO || (int)tier > RR_TIER_SPLITK) return RR_ERR_TIER;
+    rr_tier t = tier;
+    if (t == RR_TIER_AUTO) t = cols <= 8 ? RR_TIER_TILED : cols <= 64 ? RR_TIER_WAVE : RR_TIER_BLOCK;
+    if (t == RR_TIER_SPLITK) return RR_ERR_TIER;
+    if (t == RR_TIER_WAVE && cols > 64) return RR_ERR_TIER;
+    memset(out, 0, sizeof *out);
+    const int vec_elems = vec ? (x_dtype == RR_BF16 ? 8 : 4) : 1;
+    fill_rowwise_geometry(t, rows, cols, vec_elems, out);
+    return RR_OK;
+}
+
+}  // namespace rr
+
+extern "C" rr_status rr_plan_reduce(int64_t rows, int64_t cols, int64_t ld, rr_dtype dtype,
+                                    rr_op op, rr_tier tier, int32_t cu_count, rr_plan* plan_out)
+{
+    return rr::plan_reduce(rows, cols, ld, dtype, op, tier, cu_count, true, plan_out);
+}
+
+extern "C" rr_status rr_plan_softmax(int64_t rows, int64_t cols, rr_dtype x_dtype,
+                                     rr_dtype y_dtype, rr_tier tier, int32_t cu_count,
+                                     rr_plan* plan_out)
+{
+    return rr::plan_softmax(rows, cols, x_dtype, y_dtype, tier, cu_count, true, plan_out);
+}
+
+extern "C" const char* rr_status_string(rr_status s)
+{
+    switch (s) {
+    case RR_OK: return "ok";
+    case RR_ERR_NULL: return "a required pointer is NULL";
+    case RR_ERR_SHAPE: return "invalid shape (negative size, ld < cols, or P/depth out of range)";
+    case RR_ERR_DTYPE: return "unsupported dtype or dtype combination";
+    case RR_ERR_TIER: return "forced tier is not legal for this shape or operation";
+    case RR_ERR_WORKSPACE: return "split-K workspace missing or too small";
+    case RR_ERR_HIP: return "HIP runtime error";
+    case RR_ERR_OP: return "unknown reduction op";
+    }
+    return "unknown status";
+}
+
+extern "C" int rr_version(void) { return RR_VERSION; }

@@ -1,0 +1,15 @@
+// rr_plan.hpp -- host-side validation and planning (no HIP).
+#pragma once
+
+#include "../../include/rr.h"
+
+namespace rr {
+
+// Shared by the ABI entry points and the planner queries.
+rr_status plan_reduce(int64_t rows, int64_t cols, int64_t ld, rr_dtype dtype, rr_op op,
+                      rr_tier tier, int32_t cu_count, bool vec, rr_plan* out);
+rr_status plan_softmax(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype y_dtype,
+                       rr_tier tier, int32_t cu_count, bool vec, rr_plan* out);
+uint64_t splitk_workspace_bytes(int64_t rows, int32_t slices);
+
+}  // namespace rr

@@ -1,0 +1,371 @@
+// rr_reduce.hip -- row reductions over the last axis, five tiers, gfx950.
+//
+// Tier shapes follow "reduce" (algorithm.gpu.rowwise), tier semantics:
+//   wave    a group of lanes of one wavefront owns a short row (cols <= 64);
+//   block   one workgroup strides along a row with 128-bit loads, scalar tail;
+//   tiled   one thread owns kTiledRows adjacent rows, no cross-thread combine;
+//   serial  one thread per row, element by element;
+//   split-K several workgroups per row; the cross-workgroup combine follows
+//           "cluster_allreduce" (description): each group reduces inside
+//           itself first, then the groups' values are folded in rank order,
+//           so the bits do not depend on which group finishes first.
+// The monoids (sum / max / min on 32-bit values) are the page's combine_fn.
+#include <hip/hip_runtime.h>
+
+#include "rr_config.hpp"
+#include "rr_device.hpp"
+#include "rr_launch.hpp"
+#include "rr_launch_util.hpp"
+
+namespace rr {
+
+// Fold row[begin, end) into acc, thread t of NT.  With VEC == 4 the thread
+// visits 128-bit chunks t, t+NT, t+2NT, ... (U chunks in flight), then the
+// scalar tail; begin must then be a multiple of 4 elements from a 16-byte
+// aligned row start.  Elements are folded in ascending index order per
+// thread.
+template <class M, int VEC, int NT, int U>
+__device__ __forceinline__ typename M::acc_t thread_fold(const typename M::in_t* __restrict__ row,
+                                                         int64_t begin, int64_t end, int t,
+                                                         typename M::acc_t acc)
+{
+    using T = typename M::in_t;
+    const T* base = row + begin;
+    const int64_t n = end - begin;
+    if constexpr (VEC == 4) {
+        const int64_t nchunks = n >> 2;
+        int64_t c = t;
+        for (; c + (int64_t)(U - 1) * NT < nchunks; c += (int64_t)U * NT) {
+            Vec<T, 4> v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                v[u] = load4(base + (c + (int64_t)u * NT) * 4);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc = M::combine(acc, M::lift(v[u].v[i]));
+        }
+        for (; c < nchunks; c += NT) {
+            Vec<T, 4> v = load4(base + c * 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc = M::combine(acc, M::lift(v.v[i]));
+        }
+        for (int64_t j = nchunks * 4 + t; j < n; j += NT)
+            acc = M::combine(acc, M::lift(base[j]));
+    } else {
+        int64_t j = t;
+        for (; j + (int64_t)(U - 1) * NT < n; j += (int64_t)U * NT) {
+            T v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                v[u] = base[j + (int64_t)u * NT];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                acc = M::combine(acc, M::lift(v[u]));
+        }
+        for (; j < n; j += NT)
+            acc = M::combine(acc, M::lift(base[j]));
+    }
+    return acc;
+}
+
+// ------------------------------------------------------------ block tier
+template <class M, int VEC>
+__global__ __launch_bounds__(kBlockThreads) void k_reduce_block(
+    const typename M::in_t* __restrict__ x, typename M::in_t* __restrict__ y, int64_t rows,
+    int64_t cols, int64_t ld)
+{
+    using A = typename M::acc_t;
+    __shared__ A slot[2][kWavesPerBlock];
+    int par = 0;
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+        A acc = thread_fold<M, VEC, kBlockThreads, kBlockUnroll>(x + r * ld, 0, cols,
+                                                                  threadIdx.x, M::identity());
+        acc = block_reduce<M, kBlockThreads>(acc, slot[par]);
+        par ^= 1;
+        if (threadIdx.x == 0)
+            y[r] = M::finish(acc);
+    }
+}
+
+// ------------------------------------------------------------- wave tier
+// S lanes per row (S >= ceil(cols / VEC)); 64 / S rows per group and
+// kWaveRowGroups groups per wavefront task.  Lane l of a row owns columns
+// [(l % S) * VEC, (l % S) * VEC + VEC).  All loads of a task are issued
+// before any is folded, at clamped addresses that stay inside the row (rows
+// past the end read the last row; the values are then masked off), so the
+// wavefront has kWaveRowGroups loads in flight without branches between.
+template <class M, int VEC, int S>
+__global__ __launch_bounds__(kBlockThreads) void k_reduce_wave(
+    const typename M::in_t* __restrict__ x, typename M::in_t* __restrict__ y, int64_t rows,
+    int64_t cols, int64_t ld)
+{
+    using T = typename M::in_t;
+    using A = typename M::acc_t;
+    constexpr int RPG = kWave / S;
+    constexpr int U = kWaveRowGroups;
+    const int lane = lane_id();
+    const int seg = lane / S;
+    const int64_t c0 = (int64_t)(lane % S) * VEC;
+    const bool full = c0 + VEC <= cols;               // lane owns a whole chunk
+    const int64_t ntail = cols - c0;                  // 1 .. VEC-1 on the partial-chunk lane
+    const bool tail = VEC > 1 && !full && ntail > 0;
+    const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
+    for (int64_t w = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+         w * RPG * U < rows; w += nwaves) {
+        const int64_t row0 = w * RPG * U;
+        Vec<T, VEC> v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            int64_t r = row0 + (int64_t)u * RPG + seg;
+            r = r < rows ? r : rows - 1;
+            const T* p = x + r * ld + (full ? c0 : 0);
+            if constexpr (VEC == 4) {
+                if (cols >= 4)
+                    v[u] = load4(p);
+            } else {
+                v[u].v[0] = *p;
+            }
+        }
+        A acc[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            acc[u] = M::identity();
+#pragma unroll
+            for (int i = 0; i < VEC; ++i)
+                acc[u] = full ? M::combine(acc[u], M::lift(v[u].v[i])) : acc[u];
+        }
+        if (VEC > 1 && (cols % VEC) != 0) {
+            // the lane holding the partial last chunk folds it element by element
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                int64_t r = row0 + (int64_t)u * RPG + seg;
+                r = r < rows ? r : rows - 1;
+                if (tail)
+                    for (int64_t i = 0; i < ntail; ++i)
+                        acc[u] = M::combine(acc[u], M::lift(x[r * ld + c0 + i]));
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            A t = segment_reduce<M, S>(acc[u]);
+            const int64_t r = row0 + (int64_t)u * RPG + seg;
+            if ((lane % S) == 0 && r < rows)
+                y[r] = M::finish(t);
+        }
+    }
+}
+
+// ------------------------------------------------- tiled and serial tiers
+// Thread owns R adjacent rows; each axis step loads the step's element (or
+// 128-bit chunk) of all R rows and folds each into its own state.  R == 1 is
+// the serial tier.  No cross-thread combine.  Rows past the end are clamped
+// to the last row (loads stay in bounds, results are not stored).
+template <class M, int VEC, int R>
+__global__ __launch_bounds__(kBlockThreads) void k_reduce_tiled(
+    const typename M::in_t* __restrict__ x, typename M::in_t* __restrict__ y, int64_t rows,
+    int64_t cols, int64_t ld)
+{
+    using T = typename M::in_t;
+    using A = typename M::acc_t;
+    const int64_t nthreads = (int64_t)gridDim.x * kBlockThreads;
+    for (int64_t tid = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x; tid * R < rows;
+         tid += nthreads) {
+        const int64_t r0 = tid * R;
+        const T* rp[R];
+        A acc[R];
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+            rp[k] = x + (r0 + k < rows ? r0 + k : rows - 1) * ld;
+            acc[k] = M::identity();
+        }
+        const int64_t nfull = VEC == 4 ? (cols >> 2) : 0;
+        for (int64_t c = 0; c < nfull; ++c) {
+            Vec<T, 4> v[R];
+#pragma unroll
+            for (int k = 0; k < R; ++k)
+                v[k] = load4(rp[k] + c * 4);
+#pragma unroll
+            for (int k = 0; k < R; ++k)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[k] = M::combine(acc[k], M::lift(v[k].v[i]));
+        }
+        for (int64_t j = nfull * 4; j < cols; ++j) {
+            T v[R];
+#pragma unroll
+            for (int k = 0; k < R; ++k)
+                v[k] = rp[k][j];
+#pragma unroll
+            for (int k = 0; k < R; ++k)
+                acc[k] = M::combine(acc[k], M::lift(v[k]));
+        }
+#pragma unroll
+        for (int k = 0; k < R; ++k)
+            if (r0 + k < rows)
+                y[r0 + k] = M::finish(acc[k]);
+    }
+}
+
+// ----------------------------------------------------------- split-K tier
+// Workgroup (r, g) folds slice g of row r, writes its partial to
+// part[r * G + g], releases it at device scope and takes a ticket on row r.
+// The workgroup that draws ticket G - 1 is the last to arrive: it acquires,
+// folds part[r * G + 0 .. G - 1] in ascending g, writes y[r] and resets the
+// ticket to zero for the next call.  `skew` (a test hook, normally 0) makes
+// slice g wait about (G - 1 - g) * skew sleep periods before publishing, so
+// arrival order runs against rank order.
+template <class M, int VEC>
+__global__ __launch_bounds__(kBlockThreads) void k_reduce_splitk(
+    const typename M::in_t* __restrict__ x, typename M::in_t* __restrict__ y, int64_t rows,
+    int64_t cols, int64_t ld, int32_t G, int64_t slice_cols, typename M::acc_t* part,
+    uint32_t* ticket, int32_t skew)
+{
+    using A = typename M::acc_t;
+    __shared__ A slot[2][kWavesPerBlock];
+    int par = 0;
+    const int64_t total = rows * G;
+    for (int64_t b = blockIdx.x; b < total; b += gridDim.x) {
+        const int64_t r = b / G;
+        const int32_t g = (int32_t)(b - r * G);
+        const int64_t begin = (int64_t)g * slice_cols;
+        const int64_t end = begin + slice_cols < cols ? begin + slice_cols : cols;
+        A acc = thread_fold<M, VEC, kBlockThreads, kSplitKUnroll>(x + r * ld, begin, end,
+                                                                   threadIdx.x, M::identity());
+        acc = block_reduce<M, kBlockThreads>(acc, slot[par]);
+        par ^= 1;
+        if (threadIdx.x == 0) {
+            if (skew > 0) {
+                const int n = (G - 1 - g) * skew;
+                for (int i = 0; i < n; ++i)
+                    __builtin_amdgcn_s_sleep(8);
+            }
+            part[r * G + g] = acc;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            const uint32_t t = __hip_atomic_fetch_add(&ticket[r], 1u, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+            if (t == (uint32_t)(G - 1)) {
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                A a = part[r * G];
+                for (int32_t k = 1; k < G; ++k)
+                    a = M::combine(a, part[r * G + k]);
+                y[r] = M::finish(a);
+                __hip_atomic_store(&ticket[r], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------- small utilities
+__global__ __launch_bounds__(kBlockThreads) void k_fill_u32(uint32_t* __restrict__ p, int64_t n,
+                                                             uint32_t v)
+{
+    for (int64_t i = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * kBlockThreads)
+        p[i] = v;
+}
+
+__global__ __launch_bounds__(kBlockThreads) void k_fill_zero_bytes(uint8_t* __restrict__ p,
+                                                                    int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * kBlockThreads)
+        p[i] = 0;
+}
+
+static unsigned grid_for(int64_t n)
+{
+    int64_t g = ceil_div(n, kBlockThreads);
+    if (g > 4096) g = 4096;
+    return (unsigned)(g < 1 ? 1 : g);
+}
+
+rr_status launch_fill_zero(void* p, size_t bytes, hipStream_t stream)
+{
+    if (bytes == 0) return RR_OK;
+    return launch_kernel(k_fill_zero_bytes, dim3(grid_for((int64_t)bytes)), dim3(kBlockThreads),
+                         0, stream, (uint8_t*)p, (int64_t)bytes);
+}
+
+// ---------------------------------------------------------------- launch
+template <class M>
+static rr_status launch_monoid(const rr_plan& p, const ReduceLaunch& a)
+{
+    using T = typename M::in_t;
+    using A = typename M::acc_t;
+    const T* x = static_cast<const T*>(a.x);
+    T* y = static_cast<T*>(a.y);
+    const dim3 grid((unsigned)p.grid), block(kBlockThreads);
+    const hipStream_t s = a.stream;
+    switch (p.tier) {
+    case RR_TIER_BLOCK:
+        return a.vec ? launch_kernel(k_reduce_block<M, 4>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld)
+                     : launch_kernel(k_reduce_block<M, 1>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld);
+    case RR_TIER_WAVE:
+        switch (p.lanes_per_row) {
+        case 4:
+            return a.vec ? launch_kernel(k_reduce_wave<M, 4, 4>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld)
+                         : launch_kernel(k_reduce_wave<M, 1, 4>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld);
+        case 16:
+            return a.vec ? launch_kernel(k_reduce_wave<M, 4, 16>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld)
+                         : launch_kernel(k_reduce_wave<M, 1, 16>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld);
+        case 64:
+            return a.vec ? launch_kernel(k_reduce_wave<M, 4, 64>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld)
+                         : launch_kernel(k_reduce_wave<M, 1, 64>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld);
+        default:
+            return RR_ERR_TIER;
+        }
+    case RR_TIER_TILED:
+        return a.vec ? launch_kernel(k_reduce_tiled<M, 4, kTiledRows>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld)
+                     : launch_kernel(k_reduce_tiled<M, 1, kTiledRows>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld);
+    case RR_TIER_SERIAL:
+        return a.vec ? launch_kernel(k_reduce_tiled<M, 4, 1>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld)
+                     : launch_kernel(k_reduce_tiled<M, 1, 1>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld);
+    case RR_TIER_SPLITK: {
+        uint32_t* ticket = static_cast<uint32_t*>(a.workspace);
+        A* part = reinterpret_cast<A*>(static_cast<char*>(a.workspace) +
+                                       round_up(a.rows * 4, kWorkspaceAlign));
+        const dim3 g2((unsigned)(p.grid > kMaxGrid ? kMaxGrid : p.grid));
+        return a.vec ? launch_kernel(k_reduce_splitk<M, 4>, g2, block, 0, s, x, y, a.rows, a.cols, a.ld,
+                                     p.slices, p.slice_cols, part, ticket, a.skew)
+                     : launch_kernel(k_reduce_splitk<M, 1>, g2, block, 0, s, x, y, a.rows, a.cols, a.ld,
+                                     p.slices, p.slice_cols, part, ticket, a.skew);
+    }
+    default:
+        return RR_ERR_TIER;
+    }
+}
+
+rr_status launch_reduce(const rr_plan& p, const ReduceLaunch& a)
+{
+    if (a.dtype == RR_F32) {
+        switch (a.op) {
+        case RR_SUM: return launch_monoid<SumF32>(p, a);
+        case RR_MAX: return launch_monoid<MaxF32>(p, a);
+        case RR_MIN: return launch_monoid<MinF32>(p, a);
+        }
+    } else if (a.dtype == RR_I32) {
+        switch (a.op) {
+        case RR_SUM: return launch_monoid<SumI32>(p, a);
+        case RR_MAX: return launch_monoid<MaxI32>(p, a);
+        case RR_MIN: return launch_monoid<MinI32>(p, a);
+        }
+    }
+    return RR_ERR_DTYPE;
+}
+
+// cols == 0: every row gets the monoid identity.
+rr_status launch_reduce_identity(const ReduceLaunch& a)
+{
+    uint32_t v = 0;
+    if (a.dtype == RR_F32)
+        v = a.op == RR_SUM ? 0u : a.op == RR_MAX ? 0xFF800000u : 0x7F800000u;
+    else
+        v = a.op == RR_SUM ? 0u : a.op == RR_MAX ? 0x80000000u : 0x7FFFFFFFu;
+    return launch_kernel(k_fill_u32, dim3(grid_for(a.rows)), dim3(kBlockThreads), 0, a.stream,
+                         static_cast<uint32_t*>(a.y), a.rows, v);
+}
+
+}  // namespace rr

@@ -1,0 +1,358 @@
+// rr_softmax.hip -- two-pass row softmax over the last axis, gfx950.
+//
+// "reduce" (algorithm.gpu.rowwise), description: softmax is two passes;
+// pass 1 folds a monoid over the row -- here the online (max, sum) pair --
+// and pass 2 is a pure map that writes y = exp(x - max) / sum.  The tiers
+// reuse the row-reduce shapes (wave / block / tiled / serial).
+//
+// Block tier, row held in registers: each thread keeps its chunks of the row
+// in VGPRs through both passes, so x is read from HBM once.  Pass 1 takes the
+// thread's own maximum m_t, turns every element into p = exp(x - m_t) and sums
+// them (one exponential per element); the (m_t, s_t) pairs are then combined
+// across the workgroup, and pass 2 writes p * exp(m_t - M) / S.
+// Exponentials are exp2 of (x - m) * log2(e).
+#include <hip/hip_runtime.h>
+
+#include "rr_config.hpp"
+#include "rr_device.hpp"
+#include "rr_launch.hpp"
+#include "rr_launch_util.hpp"
+
+namespace rr {
+
+constexpr float kNegInf = -__builtin_inff();
+
+// Element access: XT is uint16_t (bf16 bits) or float.
+template <class XT>
+struct XIn;
+template <>
+struct XIn<uint16_t> {
+    static constexpr int kChunk = 8;  // elements per 128-bit load
+    __device__ static void chunk(const uint16_t* p, float* v)
+    {
+        uint4 u = *reinterpret_cast<const uint4*>(p);
+        v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x);
+        v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
+        v[4] = bf16_lo(u.z); v[5] = bf16_hi(u.z);
+        v[6] = bf16_lo(u.w); v[7] = bf16_hi(u.w);
+    }
+    __device__ static float one(const uint16_t* p) { return bf16_bits_to_f32(*p); }
+};
+template <>
+struct XIn<float> {
+    static constexpr int kChunk = 4;
+    __device__ static void chunk(const float* p, float* v)
+    {
+        float4 u = *reinterpret_cast<const float4*>(p);
+        v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+    }
+    __device__ static float one(const float* p) { return *p; }
+};
+
+template <class YT>
+struct YOut;
+template <>
+struct YOut<uint16_t> {
+    template <int E>
+    __device__ static void chunk(uint16_t* p, const float* v)
+    {
+        if constexpr (E == 8) {
+            uint4 u;
+            u.x = pack_bf16x2(v[0], v[1]); u.y = pack_bf16x2(v[2], v[3]);
+            u.z = pack_bf16x2(v[4], v[5]); u.w = pack_bf16x2(v[6], v[7]);
+            *reinterpret_cast<uint4*>(p) = u;
+        } else {
+            static_assert(E == 4, "chunk of 4 or 8");
+            uint2 u;
+            u.x = pack_bf16x2(v[0], v[1]); u.y = pack_bf16x2(v[2], v[3]);
+            *reinterpret_cast<uint2*>(p) = u;
+        }
+    }
+    __device__ static void one(uint16_t* p, float v) { *p = f32_to_bf16_bits(v); }
+};
+template <>
+struct YOut<float> {
+    template <int E>
+    __device__ static void chunk(float* p, const float* v)
+    {
+#pragma unroll
+        for (int i = 0; i < E; i += 4)
+            *reinterpret_cast<float4*>(p + i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
+    }
+    __device__ static void one(float* p, float v) { *p = v; }
+};
+
+// Load chunk j0 .. j0+E-1 of a row (E == 1 for the scalar variant), padding
+// past `cols` with -inf.
+template <class XT, int E, bool VEC>
+__device__ __forceinline__ void load_padded(const XT* row, int64_t j0, int64_t cols, float* v)
+{
+    if constexpr (VEC) {
+        if (j0 + E <= cols) {
+            XIn<XT>::chunk(row + j0, v);
+            return;
+        }
+    }
+    {
+#pragma unroll
+        for (int i = 0; i < E; ++i)
+            v[i] = j0 + i < cols ? XIn<XT>::one(row + j0 + i) : kNegInf;
+    }
+}
+
+template <class YT, int E, bool VEC>
+__device__ __forceinline__ void store_masked(YT* row, int64_t j0, int64_t cols, const float* v)
+{
+    if constexpr (VEC) {
+        if (j0 + E <= cols) {
+            YOut<YT>::template chunk<E>(row + j0, v);
+            return;
+        }
+    }
+    {
+#pragma unroll
+        for (int i = 0; i < E; ++i)
+            if (j0 + i < cols)
+                YOut<YT>::one(row + j0 + i, v[i]);
+    }
+}
+
+// Pass 1 on values held by one thread: m = max, v <- exp(v - m), s = sum v.
+// With m == -inf (nothing but -inf / padding) every p is 0.
+template <int N>
+__device__ __forceinline__ MS local_exp_sum(float* v)
+{
+    float m = kNegInf;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        m = fmaxf(m, v[i]);
+    float s = 0.0f;
+    if (m != kNegInf) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            v[i] = exp2_f32((v[i] - m) * kLog2e);
+            s += v[i];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            v[i] = 0.0f;
+    }
+    return MS{m, s};
+}
+
+// ------------------------------------------- block tier, row in registers
+template <class XT, class YT, int NCH, bool VEC>
+__global__ __launch_bounds__(kBlockThreads) void k_softmax_block(const XT* __restrict__ x,
+                                                                 YT* __restrict__ y, int64_t rows,
+                                                                 int64_t cols, int64_t ldx,
+                                                                 int64_t ldy)
+{
+    constexpr int E = VEC ? XIn<XT>::kChunk : 1;
+    __shared__ MS slot[2][kWavesPerBlock];
+    int par = 0;
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+        const XT* xr = x + r * ldx;
+        YT* yr = y + r * ldy;
+        float v[NCH * E];
+#pragma unroll
+        for (int k = 0; k < NCH; ++k)
+            load_padded<XT, E, VEC>(xr, ((int64_t)threadIdx.x + (int64_t)k * kBlockThreads) * E,
+                                    cols, v + k * E);
+        const MS own = local_exp_sum<NCH * E>(v);
+        const MS tot = block_reduce<SoftmaxMS, kBlockThreads>(own, slot[par]);
+        par ^= 1;
+        const float sc = exp2_f32((own.m - tot.m) * kLog2e) / tot.s;
+#pragma unroll
+        for (int i = 0; i < NCH * E; ++i)
+            v[i] *= sc;
+#pragma unroll
+        for (int k = 0; k < NCH; ++k)
+            store_masked<YT, E, VEC>(yr, ((int64_t)threadIdx.x + (int64_t)k * kBlockThreads) * E,
+                                     cols, v + k * E);
+    }
+}
+
+// ---------------------------------------- block tier, streaming long rows
+// Pass 1 folds (m, s) chunk by chunk; pass 2 reads x again.
+template <class XT, class YT, bool VEC>
+__global__ __launch_bounds__(kBlockThreads) void k_softmax_stream(const XT* __restrict__ x,
+                                                                  YT* __restrict__ y,
+                                                                  int64_t rows, int64_t cols,
+                                                                  int64_t ldx, int64_t ldy)
+{
+    constexpr int E = VEC ? XIn<XT>::kChunk : 1;
+    __shared__ MS slot[2][kWavesPerBlock];
+    int par = 0;
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+        const XT* xr = x + r * ldx;
+        YT* yr = y + r * ldy;
+        // per-thread running (m, s); s is kept in double because a thread
+        // adds many terms in sequence on long rows
+        float tm = kNegInf;
+        double ts = 0.0;
+        for (int64_t j0 = (int64_t)threadIdx.x * E; j0 < cols; j0 += (int64_t)kBlockThreads * E) {
+            float v[E];
+            load_padded<XT, E, VEC>(xr, j0, cols, v);
+            float cm = kNegInf;
+#pragma unroll
+            for (int i = 0; i < E; ++i)
+                cm = fmaxf(cm, v[i]);
+            const float M = fmaxf(tm, cm);
+            if (M != kNegInf) {
+                double s = ts * (double)exp2_f32((tm - M) * kLog2e);
+#pragma unroll
+                for (int i = 0; i < E; ++i)
+                    s += (double)exp2_f32((v[i] - M) * kLog2e);
+                tm = M;
+                ts = s;
+            }
+        }
+        const MS tot = block_reduce<SoftmaxMS, kBlockThreads>(MS{tm, (float)ts}, slot[par]);
+        par ^= 1;
+        const float inv = 1.0f / tot.s;
+        for (int64_t j0 = (int64_t)threadIdx.x * E; j0 < cols; j0 += (int64_t)kBlockThreads * E) {
+            float v[E];
+            load_padded<XT, E, VEC>(xr, j0, cols, v);
+#pragma unroll
+            for (int i = 0; i < E; ++i)
+                v[i] = exp2_f32((v[i] - tot.m) * kLog2e) * inv;
+            store_masked<YT, E, VEC>(yr, j0, cols, v);
+        }
+    }
+}
+
+// -------------------------------------------------------------- wave tier
+// S lanes per row, one chunk per lane (S * E >= cols).
+template <class XT, class YT, bool VEC, int S>
+__global__ __launch_bounds__(kBlockThreads) void k_softmax_wave(const XT* __restrict__ x,
+                                                                YT* __restrict__ y, int64_t rows,
+                                                                int64_t cols, int64_t ldx,
+                                                                int64_t ldy)
+{
+    constexpr int E = VEC ? XIn<XT>::kChunk : 1;
+    constexpr int RPG = kWave / S;
+    constexpr int U = kWaveRowGroups;
+    const int lane = lane_id();
+    const int seg = lane / S;
+    const int64_t j0 = (int64_t)(lane % S) * E;
+    const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
+    for (int64_t w = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+         w * RPG * U < rows; w += nwaves) {
+        const int64_t row0 = w * RPG * U;
+        float v[U][E];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t r = row0 + (int64_t)u * RPG + seg;
+            if (r < rows) {
+                load_padded<XT, E, VEC>(x + r * ldx, j0, cols, v[u]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < E; ++i)
+                    v[u][i] = kNegInf;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const MS own = local_exp_sum<E>(v[u]);
+            const MS tot = segment_reduce<SoftmaxMS, S>(own);
+            const float sc = exp2_f32((own.m - tot.m) * kLog2e) / tot.s;
+#pragma unroll
+            for (int i = 0; i < E; ++i)
+                v[u][i] *= sc;
+            const int64_t r = row0 + (int64_t)u * RPG + seg;
+            if (r < rows)
+                store_masked<YT, E, VEC>(y + r * ldy, j0, cols, v[u]);
+        }
+    }
+}
+
+// ---------------------------------------------- tiled and serial tiers
+// Thread owns R adjacent rows and walks each row element by element:
+// max, then sum of exp, then the map.  R == 1 is the serial tier.
+template <class XT, class YT, int R>
+__global__ __launch_bounds__(kBlockThreads) void k_softmax_tiled(const XT* __restrict__ x,
+                                                                 YT* __restrict__ y,
+                                                                 int64_t rows, int64_t cols,
+                                                                 int64_t ldx, int64_t ldy)
+{
+    const int64_t nthreads = (int64_t)gridDim.x * kBlockThreads;
+    for (int64_t tid = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x; tid * R < rows;
+         tid += nthreads) {
+        for (int k = 0; k < R; ++k) {
+            const int64_t r = tid * R + k;
+            if (r >= rows)
+                break;
+            const XT* xr = x + r * ldx;
+            YT* yr = y + r * ldy;
+            float m = kNegInf;
+            for (int64_t j = 0; j < cols; ++j)
+                m = fmaxf(m, XIn<XT>::one(xr + j));
+            // one thread adds every term of the row in sequence: accumulate
+            // in double so the sum stays accurate for long rows
+            double s = 0.0;
+            if (m != kNegInf)
+                for (int64_t j = 0; j < cols; ++j)
+                    s += (double)exp2_f32((XIn<XT>::one(xr + j) - m) * kLog2e);
+            const float inv = (float)(1.0 / s);
+            for (int64_t j = 0; j < cols; ++j)
+                YOut<YT>::one(yr + j, exp2_f32((XIn<XT>::one(xr + j) - m) * kLog2e) * inv);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- launch
+template <class XT, class YT, bool VEC>
+static rr_status launch_typed(const rr_plan& p, const SoftmaxLaunch& a)
+{
+    const XT* x = static_cast<const XT*>(a.x);
+    YT* y = static_cast<YT*>(a.y);
+    const dim3 grid((unsigned)p.grid), block(kBlockThreads);
+    const hipStream_t s = a.stream;
+    constexpr int E = VEC ? XIn<XT>::kChunk : 1;
+    switch (p.tier) {
+    case RR_TIER_BLOCK: {
+        const int64_t chunks = ceil_div(a.cols, E);
+        const int64_t nch = ceil_div(chunks, kBlockThreads);
+        if (nch <= 1)
+            return launch_kernel(k_softmax_block<XT, YT, 1, VEC>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
+        if (nch <= 2)
+            return launch_kernel(k_softmax_block<XT, YT, 2, VEC>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
+        if (nch <= 4)
+            return launch_kernel(k_softmax_block<XT, YT, 4, VEC>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
+        if (nch <= kSoftmaxMaxChunks)
+            return launch_kernel(k_softmax_block<XT, YT, kSoftmaxMaxChunks, VEC>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
+        return launch_kernel(k_softmax_stream<XT, YT, VEC>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
+    }
+    case RR_TIER_WAVE:
+        switch (p.lanes_per_row) {
+        case 4: return launch_kernel(k_softmax_wave<XT, YT, VEC, 4>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
+        case 16: return launch_kernel(k_softmax_wave<XT, YT, VEC, 16>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
+        case 64: return launch_kernel(k_softmax_wave<XT, YT, VEC, 64>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
+        default: return RR_ERR_TIER;
+        }
+    case RR_TIER_TILED:
+        return launch_kernel(k_softmax_tiled<XT, YT, kTiledRows>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
+    case RR_TIER_SERIAL:
+        return launch_kernel(k_softmax_tiled<XT, YT, 1>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
+    default:
+        return RR_ERR_TIER;
+    }
+}
+
+template <class XT, class YT>
+static rr_status launch_xy(const rr_plan& p, const SoftmaxLaunch& a)
+{
+    return a.vec ? launch_typed<XT, YT, true>(p, a) : launch_typed<XT, YT, false>(p, a);
+}
+
+rr_status launch_softmax(const rr_plan& p, const SoftmaxLaunch& a)
+{
+    const bool xb = a.x_dtype == RR_BF16, yb = a.y_dtype == RR_BF16;
+    if (xb && yb) return launch_xy<uint16_t, uint16_t>(p, a);
+    if (xb) return launch_xy<uint16_t, float>(p, a);
+    if (yb) return launch_xy<float, uint16_t>(p, a);
+    return launch_xy<float, float>(p, a);
+}
+
+}  // namespace rr

@@ -20,3 +20,11 @@ def _oracle_built():
     if not os.path.exists(LIB):
         build_oracle()
     yield
+
+
+def pytest_runtest_logstart(nodeid, location):
+    # Name the case on the raw stderr before it runs, so a run that dies on
+    # the GPU still says which test it was in.
+    if "gpu" in nodeid or "parity" in nodeid or "determinism" in nodeid:
+        sys.__stderr__.write("[start] %s\n" % nodeid)
+        sys.__stderr__.flush()

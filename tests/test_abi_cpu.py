@@ -1,0 +1,158 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+headers declare, plans tiers by the documented rule and rejects bad
+arguments before it touches the device."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import split_deterministic_combine_amd as rr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("rr.h", "rr_test.h")]
+
+
+def _declared_functions():
+    names = set()
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"\b(rr_[a-z0-9_]+)\s*\(", text):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+def test_library_is_built_for_gfx950_and_loads():
+    assert os.path.exists(rr.lib_path()), "run python -m split_deterministic_combine_amd.build"
+    lib = ctypes.CDLL(rr.lib_path())
+    assert lib.rr_version() == 1
+    blob = open(rr.lib_path(), "rb").read()
+    assert b"gfx950" in blob
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(rr.lib_path())
+    declared = _declared_functions()
+    assert {"rr_reduce_rows", "rr_softmax_rows", "rr_splitk_lse_merge"} <= set(declared)
+    missing = [n for n in declared if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_status_strings_are_distinct():
+    lib = ctypes.CDLL(rr.lib_path())
+    lib.rr_status_string.restype = ctypes.c_char_p
+    texts = {lib.rr_status_string(s) for s in range(8)}
+    assert len(texts) == 8 and all(texts)
+
+
+# ------------------------------------------------------------- tier rules
+
+@pytest.mark.parametrize("rows,cols,tier", [
+    (64, 1024, "block"),           # small rows
+    (1048576, 48, "wave"),         # short rows
+    (16, 1 << 24, "splitk"),       # rows < CU and long rows
+    (255, 65536, "splitk"),
+    (256, 65536, "block"),         # rows == CU: not split-K
+    (100, 65535, "block"),         # too short for split-K
+    (1000, 8, "tiled"),
+    (1000, 1, "tiled"),
+    (1000, 9, "wave"),
+    (1000, 64, "wave"),
+    (1000, 65, "block"),
+    (3, 0, "tiled"),
+])
+def test_auto_tier_rule(rows, cols, tier):
+    assert rr.plan_reduce(rows, cols, cu_count=256)["tier"] == tier
+
+
+def test_splitk_geometry_for_the_long_row_workload():
+    p = rr.plan_reduce(16, 1 << 24, cu_count=256)
+    assert p["slices"] == 64 and p["grid"] == 1024 and p["slice_cols"] == 1 << 18
+    assert p["workspace_bytes"] == 256 + 16 * 64 * 8
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 65536), (7, 100003), (200, 1 << 20), (3, 70001),
+                                       (16, 1 << 24), (1, 1 << 30)])
+def test_splitk_slices_cover_the_row_and_are_non_empty(rows, cols):
+    p = rr.plan_reduce(rows, cols, tier="splitk", cu_count=256)
+    g, s = p["slices"], p["slice_cols"]
+    assert 1 <= g <= 256 and s % 4 == 0
+    assert (g - 1) * s < cols <= g * s
+
+
+def test_splitk_forced_on_short_rows_has_one_slice():
+    p = rr.plan_reduce(64, 1000, tier="splitk", cu_count=256)
+    assert p["slices"] == 1 and p["grid"] == 64
+
+
+def test_wave_lanes_per_row():
+    assert rr.plan_reduce(10, 48)["lanes_per_row"] == 16
+    assert rr.plan_reduce(10, 16, tier="wave")["lanes_per_row"] == 4
+    assert rr.plan_reduce(10, 17, tier="wave")["lanes_per_row"] == 16
+    assert rr.plan_reduce(10, 64, tier="wave")["lanes_per_row"] == 16
+    assert rr.plan_softmax(10, 64, tier="wave")["lanes_per_row"] == 16   # bf16: 8 per chunk
+
+
+def test_softmax_tier_rule():
+    assert rr.plan_softmax(8192, 8192)["tier"] == "block"
+    assert rr.plan_softmax(100, 40)["tier"] == "wave"
+    assert rr.plan_softmax(100, 4)["tier"] == "tiled"
+    with pytest.raises(rr.RRError) as e:
+        rr.plan_softmax(4, 1 << 20, tier="splitk")
+    assert e.value.status == 4
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(rows=-1, cols=4), 2),
+    (dict(rows=4, cols=-1), 2),
+    (dict(rows=4, cols=8, ld=7), 2),
+    (dict(rows=4, cols=65, tier="wave"), 4),
+    (dict(rows=4, cols=8, dtype=torch.bfloat16), 3),
+    (dict(rows=4, cols=8, cu_count=0), 2),
+])
+def test_plan_rejects_bad_arguments(kw, status):
+    with pytest.raises(rr.RRError) as e:
+        rr.plan_reduce(**kw)
+    assert e.value.status == status
+
+
+def test_entry_points_validate_before_touching_the_device():
+    # Invalid shapes come back as status codes with no HIP call (no GPU here).
+    lib = ctypes.CDLL(rr.lib_path())
+    vp = ctypes.c_void_p
+    lib.rr_reduce_rows.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, ctypes.c_size_t, vp]
+    lib.rr_softmax_rows.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                    ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+    lib.rr_splitk_lse_merge.argtypes = [vp, vp, vp, vp, ctypes.c_int32, ctypes.c_int64,
+                                        ctypes.c_int32, ctypes.c_float, ctypes.c_int, vp]
+    assert lib.rr_reduce_rows(None, None, -1, 4, 4, 0, 0, 0, None, 0, None) == 2
+    assert lib.rr_reduce_rows(None, None, 4, 8, 4, 0, 0, 0, None, 0, None) == 2
+    assert lib.rr_reduce_rows(None, None, 4, 8, 8, 2, 0, 0, None, 0, None) == 3
+    assert lib.rr_reduce_rows(None, None, 4, 8, 8, 0, 9, 0, None, 0, None) == 7
+    assert lib.rr_reduce_rows(None, None, 4, 100, 100, 0, 0, 1, None, 0, None) == 4
+    assert lib.rr_reduce_rows(None, None, 0, 8, 8, 0, 0, 0, None, 0, None) == 0   # no-op
+    assert lib.rr_reduce_rows(None, None, 4, 8, 8, 0, 0, 0, None, 0, None) == 1   # NULL
+    assert lib.rr_softmax_rows(None, None, 4, 8, 8, 8, 1, 1, 0, None) == 3        # int32 softmax
+    assert lib.rr_softmax_rows(None, None, 4, 8, 8, 8, 2, 2, 5, None) == 4        # split-K softmax
+    assert lib.rr_softmax_rows(None, None, 4, 8, 4, 8, 2, 2, 0, None) == 2        # ld_x < cols
+    assert lib.rr_softmax_rows(None, None, 4, 0, 8, 8, 2, 2, 0, None) == 0        # cols 0: no-op
+    assert lib.rr_splitk_lse_merge(None, None, None, None, 0, 4, 8, 1.0, 2, None) == 2
+    assert lib.rr_splitk_lse_merge(None, None, None, None, 257, 4, 8, 1.0, 2, None) == 2
+    assert lib.rr_splitk_lse_merge(None, None, None, None, 8, 4, 0, 1.0, 2, None) == 2
+    assert lib.rr_splitk_lse_merge(None, None, None, None, 8, 4, 8, 1.0, 1, None) == 3
+    assert lib.rr_splitk_lse_merge(None, None, None, None, 8, 0, 8, 1.0, 2, None) == 0
+    assert lib.rr_splitk_lse_merge(None, None, None, None, 8, 4, 8, 1.0, 2, None) == 1
+
+
+def test_product_path_has_no_cpu_fallback():
+    # The binding must refuse CPU tensors rather than compute on the host.
+    x = torch.zeros(4, 8)
+    with pytest.raises(ValueError):
+        rr.reduce_rows(x)
+    with pytest.raises(ValueError):
+        rr.softmax_rows(x.bfloat16())
+    src = open(os.path.join(ROOT, "split_deterministic_combine_amd", "__init__.py")).read()
+    assert "oracle" not in src

@@ -1,0 +1,401 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle,
+element by element, on seeded inputs from the shared generators.
+
+Bars: int32 results and float max/min bit-exact; float32 results within
+rel 1e-5 / abs 1e-6 of the oracle; bf16 results within 1 bf16 ulp.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import split_deterministic_combine_amd as rr
+from split_deterministic_combine_amd import synth
+from tests.gpu_util import (assert_bf16_within_1ulp, assert_close_f32, assert_exact, to_gpu,
+                            to_host)
+
+pytestmark = pytest.mark.gpu
+
+REDUCE_OPS = [(np.float32, "sum"), (np.float32, "max"), (np.float32, "min"),
+              (np.int32, "sum"), (np.int32, "max"), (np.int32, "min")]
+
+
+def _legal_tiers(cols):
+    tiers = ["auto", "block", "tiled", "serial", "splitk"]
+    if cols <= 64:
+        tiers.append("wave")
+    return tiers
+
+
+def _make_reduce_input(dtype, rows, cols, seed):
+    if dtype == np.int32:
+        return synth.ints_i32(seed, (rows, cols), -(2 ** 31), 2 ** 31 - 1)
+    return synth.normal_f32(seed, (rows, cols))
+
+
+def _check_reduce(gpu, ref, dtype, op, what):
+    if dtype == np.float32 and op == "sum":
+        assert_close_f32(gpu, ref, what)
+    else:
+        assert_exact(gpu, ref, what)
+
+
+def _run_reduce(x_host, op, tier, pad=0, offset=0):
+    """Run rr.reduce_rows on a copy of x_host whose rows sit at stride
+    cols + pad + offset, starting `offset` elements into each row."""
+    rows, cols = x_host.shape
+    if pad or offset:
+        big = np.zeros((rows, cols + pad + offset), dtype=x_host.dtype)
+        big[:, offset:offset + cols] = x_host
+        g = to_gpu(big)[:, offset:offset + cols]
+    else:
+        g = to_gpu(x_host)
+    y = rr.reduce_rows(g, op, tier)
+    torch.cuda.synchronize()
+    return to_host(y)
+
+
+# ------------------------------------------------------------------ reduce
+
+@pytest.mark.parametrize("tier", ["auto", "block", "tiled", "serial", "splitk"])
+def test_reduce_small_rows_config(tier):
+    xf, xi = synth.small_rows()
+    for x in (xf, xi):
+        for op in ("sum", "max", "min"):
+            _check_reduce(_run_reduce(x, op, tier), oracle.reduce_rows(x, op), x.dtype.type, op,
+                          "small_rows %s %s %s" % (x.dtype, op, tier))
+
+
+EDGE_COLS = [0, 1, 2, 3, 4, 5, 7, 8, 15, 16, 17, 47, 48, 63, 64, 65, 127, 128, 1000, 1024, 4097]
+
+
+@pytest.mark.parametrize("cols", EDGE_COLS)
+@pytest.mark.parametrize("dtype,op", REDUCE_OPS)
+def test_reduce_edge_widths_all_tiers(cols, dtype, op):
+    x = _make_reduce_input(dtype, 37, cols, 1000 + cols)
+    ref = oracle.reduce_rows(x, op)
+    for tier in _legal_tiers(cols):
+        _check_reduce(_run_reduce(x, op, tier), ref, dtype, op, "cols %d %s" % (cols, tier))
+
+
+@pytest.mark.parametrize("pad,offset", [(3, 0), (0, 1), (5, 2), (4, 0)])
+@pytest.mark.parametrize("cols", [5, 48, 61, 1000, 70001])
+def test_reduce_strided_and_misaligned_rows(pad, offset, cols):
+    rows = 6 if cols > 10000 else 29
+    for dtype, op in REDUCE_OPS:
+        x = _make_reduce_input(dtype, rows, cols, 77 + cols + pad)
+        ref = oracle.reduce_rows(x, op)
+        for tier in _legal_tiers(cols):
+            if tier == "serial" and cols > 10000:
+                continue
+            got = _run_reduce(x, op, tier, pad, offset)
+            _check_reduce(got, ref, dtype, op, "cols %d pad %d off %d %s" % (cols, pad, offset, tier))
+
+
+def test_reduce_short_rows_config_full_size():
+    x = synth.short_rows()
+    g = to_gpu(x)
+    for op in ("sum", "max"):
+        y = to_host(rr.reduce_rows(g, op))
+        _check_reduce(y, oracle.reduce_rows(x, op), np.float32, op, "short_rows " + op)
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 65536), (3, 70001), (7, 100003), (5, 1 << 20), (255, 65536)])
+def test_reduce_splitk_shapes(rows, cols):
+    for dtype, op in REDUCE_OPS:
+        x = _make_reduce_input(dtype, rows, cols, rows * 7 + cols)
+        ref = oracle.reduce_rows(x, op)
+        for tier in ("auto", "splitk", "block"):
+            _check_reduce(_run_reduce(x, op, tier), ref, dtype, op, "%dx%d %s" % (rows, cols, tier))
+
+
+def test_splitk_with_one_slice_equals_block_tier_bitwise():
+    for cols in (100, 1000, 4097, 16384):
+        x = synth.uniform_f32(cols, (40, cols))
+        assert rr.plan_reduce(40, cols, tier="splitk")["slices"] == 1
+        for op in ("sum", "max"):
+            assert_exact(_run_reduce(x, op, "splitk"), _run_reduce(x, op, "block"), "G=1 %d" % cols)
+
+
+def test_int_results_identical_across_tiers():
+    x = synth.ints_i32(5, (50, 64), -(2 ** 31), 2 ** 31 - 1)
+    for op in ("sum", "max", "min"):
+        outs = [_run_reduce(x, op, t) for t in ("wave", "block", "tiled", "serial", "splitk")]
+        for o in outs[1:]:
+            assert_exact(o, outs[0], op)
+
+
+def test_reduce_rows_zero_is_noop_and_empty_rows_get_identity():
+    g = torch.zeros((0, 16), device="cuda")
+    assert rr.reduce_rows(g).shape == (0,)
+    e = torch.zeros((5, 0), device="cuda")
+    assert torch.all(rr.reduce_rows(e, "max") == -float("inf"))
+    assert torch.all(rr.reduce_rows(e, "min") == float("inf"))
+    assert torch.all(rr.reduce_rows(e, "sum") == 0)
+    ei = torch.zeros((5, 0), dtype=torch.int32, device="cuda")
+    assert torch.all(rr.reduce_rows(ei, "max") == -(2 ** 31))
+
+
+def test_reduce_float_max_min_total_order_cases():
+    rows = np.array([[-0.0, 0.0, -0.0], [0.0, -0.0, 0.0], [1.0, np.nan, -2.0], [-np.inf, -1.0, -5.0]],
+                    dtype=np.float32)
+    neg_nan = np.array([0xFFC00000], dtype=np.uint32).view(np.float32)[0]
+    rows = np.concatenate([rows, np.array([[3.0, neg_nan, 1.0]], dtype=np.float32)])
+    for op in ("max", "min"):
+        ref = oracle.reduce_rows(rows, op)
+        for tier in ("wave", "block", "tiled", "serial", "splitk"):
+            assert_exact(_run_reduce(rows, op, tier), ref, "%s %s" % (op, tier))
+
+
+# ----------------------------------------------------- long rows (split-K)
+
+@pytest.fixture(scope="module")
+def long_rows_data():
+    xf, xi = synth.long_rows()
+    return xf, xi, to_gpu(xf), to_gpu(xi)
+
+
+def test_long_rows_config_matches_oracle(long_rows_data):
+    xf, xi, gf, gi = long_rows_data
+    assert rr.plan_reduce(16, 1 << 24)["tier"] == "splitk"
+    assert_close_f32(to_host(rr.reduce_rows(gf, "sum")), oracle.reduce_rows(xf, "sum"), "f32 sum")
+    assert_exact(to_host(rr.reduce_rows(gi, "max")), oracle.reduce_rows(xi, "max"), "i32 max")
+
+
+def test_long_rows_bit_identical_across_ten_runs(long_rows_data):
+    _, _, gf, gi = long_rows_data
+    first_f = rr.reduce_rows(gf, "sum").clone()
+    first_i = rr.reduce_rows(gi, "max").clone()
+    for _ in range(9):
+        assert torch.equal(rr.reduce_rows(gf, "sum").view(torch.int32), first_f.view(torch.int32))
+        assert torch.equal(rr.reduce_rows(gi, "max"), first_i)
+
+
+def test_long_rows_bits_do_not_depend_on_arrival_order(long_rows_data):
+    # Slices publish in (roughly) descending rank order under the skew hook;
+    # the last-arriver fold still visits ranks in ascending order.
+    _, _, gf, gi = long_rows_data
+    plain_f = rr.reduce_rows(gf, "sum").clone()
+    plain_i = rr.reduce_rows(gi, "max").clone()
+    try:
+        rr._set_splitk_skew(16)
+        skew_f = rr.reduce_rows(gf, "sum").clone()
+        skew_i = rr.reduce_rows(gi, "max").clone()
+        torch.cuda.synchronize()
+    finally:
+        rr._set_splitk_skew(0)
+    assert torch.equal(skew_f.view(torch.int32), plain_f.view(torch.int32))
+    assert torch.equal(skew_i, plain_i)
+
+
+def test_splitk_tickets_are_left_zero():
+    # The last workgroup of each row resets its ticket, so the same workspace
+    # serves the next call without a clearing pass.
+    x = to_gpu(synth.uniform_f32(9, (3, 200000)))
+    rr.reduce_rows(x, "sum", "splitk")
+    torch.cuda.synchronize()
+    assert rr._workspaces
+    for ws in rr._workspaces.values():
+        assert int(ws[:256].count_nonzero()) == 0
+
+
+# ----------------------------------------------------------------- softmax
+
+SOFTMAX_COLS = [1, 2, 3, 5, 8, 9, 16, 31, 33, 64, 65, 100, 1000, 2047, 2048, 2049, 4096, 8191,
+                8192, 8200, 16384, 16385, 20000]
+SOFTMAX_TYPES = [("bf16", "bf16"), ("f32", "f32"), ("bf16", "f32"), ("f32", "bf16")]
+
+
+def _softmax_input(xt, rows, cols, seed, std=3.0):
+    return synth.normal_bf16(seed, (rows, cols), std) if xt == "bf16" else synth.normal_f32(
+        seed, (rows, cols), std)
+
+
+def _check_softmax(gpu, ref, yt, what):
+    if yt == "bf16":
+        assert_bf16_within_1ulp(gpu, ref, what)
+    else:
+        assert_close_f32(gpu, ref, what)
+
+
+def _softmax_tiers(cols):
+    tiers = ["auto", "block", "tiled", "serial"]
+    if cols <= 64:
+        tiers.append("wave")
+    return tiers
+
+
+@pytest.mark.parametrize("cols", SOFTMAX_COLS)
+@pytest.mark.parametrize("xt,yt", SOFTMAX_TYPES)
+def test_softmax_edge_widths_all_tiers(cols, xt, yt):
+    rows = 13
+    x = _softmax_input(xt, rows, cols, 500 + cols)
+    ref = oracle.softmax_rows(x, yt)
+    ydt = torch.bfloat16 if yt == "bf16" else torch.float32
+    for tier in _softmax_tiers(cols):
+        if tier == "serial" and cols > 5000:
+            continue
+        y = to_host(rr.softmax_rows(to_gpu(x), ydt, tier))
+        _check_softmax(y, ref, yt, "cols %d %s->%s %s" % (cols, xt, yt, tier))
+
+
+@pytest.mark.parametrize("pad,offset", [(8, 0), (0, 1), (3, 5)])
+@pytest.mark.parametrize("cols", [7, 40, 1000, 8192])
+def test_softmax_strided_and_misaligned_rows(pad, offset, cols):
+    rows = 11
+    x = _softmax_input("bf16", rows, cols, 900 + cols)
+    ref = oracle.softmax_rows(x, "bf16")
+    big = np.zeros((rows, cols + pad + offset), dtype=np.uint16)
+    big[:, offset:offset + cols] = x
+    g = to_gpu(big)[:, offset:offset + cols]
+    for tier in _softmax_tiers(cols):
+        out = torch.empty((rows, cols + pad + offset), dtype=torch.bfloat16, device="cuda")
+        yv = out[:, offset:offset + cols]
+        rr.softmax_rows(g, torch.bfloat16, tier, out=yv)
+        _check_softmax(to_host(yv), ref, "bf16", "cols %d pad %d off %d %s" % (cols, pad, offset, tier))
+
+
+def test_softmax_uniform_row_is_exactly_2_pow_minus_13():
+    x = torch.full((4, 8192), 3.0, dtype=torch.bfloat16, device="cuda")
+    y = to_host(rr.softmax_rows(x))
+    assert np.all(y == 0x3900)
+
+
+def test_softmax_special_values():
+    x = np.array([[0.0, -np.inf, 1.0, 2.0] * 16,
+                  [-np.inf] * 64,
+                  [-100.0, 0.0, 100.0, -50.0] * 16,
+                  [87.0, -87.0, 0.0, 60.0] * 16], dtype=np.float32)
+    for xt in ("f32", "bf16"):
+        xin = x if xt == "f32" else synth._bf16_bits(x)
+        for yt in ("f32", "bf16"):
+            ref = oracle.softmax_rows(xin, yt)
+            ydt = torch.bfloat16 if yt == "bf16" else torch.float32
+            for tier in ("wave", "block", "tiled", "serial"):
+                y = to_host(rr.softmax_rows(to_gpu(xin), ydt, tier))
+                _check_softmax(y, ref, yt, "special %s->%s %s" % (xt, yt, tier))
+
+
+def test_softmax_wide_logit_range():
+    # exp of differences below -87 lands in the float32 subnormal range
+    x = synth.uniform_f32(31, (16, 3000), -120.0, 20.0)
+    for yt in ("f32", "bf16"):
+        ref = oracle.softmax_rows(x, yt)
+        ydt = torch.bfloat16 if yt == "bf16" else torch.float32
+        y = to_host(rr.softmax_rows(to_gpu(x), ydt))
+        _check_softmax(y, ref, yt, "wide range " + yt)
+
+
+def test_softmax_in_place():
+    x = _softmax_input("bf16", 9, 3000, 41)
+    ref = oracle.softmax_rows(x, "bf16")
+    g = to_gpu(x)
+    rr.softmax_rows(g, torch.bfloat16, "block", out=g)
+    assert_bf16_within_1ulp(to_host(g), ref, "in place")
+
+
+def test_softmax_rows_config_full_size():
+    x = synth.softmax_rows()
+    g = to_gpu(x)
+    y = rr.softmax_rows(g)
+    torch.cuda.synchronize()
+    sample = np.linspace(0, x.shape[0] - 1, 97).astype(np.int64)
+    ref = oracle.softmax_rows(np.ascontiguousarray(x[sample]), "bf16")
+    yh = to_host(y)
+    assert_bf16_within_1ulp(yh[sample], ref, "softmax_rows sample")
+    # every row: the bf16 outputs sum to 1 within the rounding of each output
+    s = y.float().sum(dim=1)
+    assert float((s - 1).abs().max()) <= 2.0 ** -8
+
+
+def test_softmax_bit_identical_across_runs():
+    g = to_gpu(synth.normal_bf16(3, (1024, 8192)))
+    first = rr.softmax_rows(g).clone()
+    for _ in range(4):
+        assert torch.equal(rr.softmax_rows(g).view(torch.int16), first.view(torch.int16))
+
+
+# --------------------------------------------------------------- LSE merge
+
+def _merge_case(P, rows, depth, seed):
+    o, m, l = synth.lse_merge(seed, P=P, batch=1, heads=1, q_rows=rows, depth=depth)
+    return o.reshape(P, rows, depth), m.reshape(P, rows), l.reshape(P, rows)
+
+
+def _run_merge(o, m, l, scale=1.0, out="bf16"):
+    odt = torch.bfloat16 if out == "bf16" else torch.float32
+    y = rr.splitk_lse_merge(to_gpu(o), to_gpu(m), to_gpu(l), scale, odt)
+    torch.cuda.synchronize()
+    return to_host(y)
+
+
+def _check_merge(o, m, l, scale, what):
+    for out in ("bf16", "f32"):
+        ref = oracle.splitk_lse_merge(o, m, l, scale, out)
+        got = _run_merge(o, m, l, scale, out)
+        if out == "bf16":
+            assert_bf16_within_1ulp(got, ref, what + " bf16")
+        else:
+            assert_close_f32(got, ref, what + " f32")
+
+
+@pytest.mark.parametrize("P", [1, 2, 3, 8, 9, 16, 64, 256])
+@pytest.mark.parametrize("depth", [1, 3, 4, 64, 100, 128, 129, 300])
+def test_merge_partition_counts_and_depths(P, depth):
+    rows = 37
+    o, m, l = _merge_case(P, rows, depth, P * 1000 + depth)
+    _check_merge(o, m, l, 1.0, "P %d depth %d" % (P, depth))
+
+
+def test_merge_single_partition_is_bit_exact_identity():
+    o, m, l = _merge_case(1, 300, 128, 7)
+    assert_exact(_run_merge(o, m, l, 1.0, "f32"), o[0], "P=1 f32")
+    want = o[0].astype(np.float32)
+    want_bits = torch.from_numpy(want).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert_exact(_run_merge(o, m, l, 1.0, "bf16"), want_bits, "P=1 bf16")
+
+
+def test_merge_empty_partitions_and_rows():
+    P, rows, depth = 8, 64, 128
+    o, m, l = _merge_case(P, rows, depth, 11)
+    rng = np.random.default_rng(12)
+    empty = rng.random((P, rows)) < 0.3
+    o[empty] = np.nan                       # poison: must never enter the sum
+    l[empty & (rng.random((P, rows)) < 0.5)] = 0.0
+    m[empty & (l != 0)] = -np.inf
+    m[:, 5], l[:, 5] = -np.inf, 1.0         # row 5: every partition empty
+    l[:, 9] = 0.0                           # row 9: every partition empty
+    _check_merge(o, m, l, 1.0, "empties")
+    got = _run_merge(o, m, l, 1.0, "f32")
+    assert np.all(got[5] == 0) and np.all(got[9] == 0)
+
+
+@pytest.mark.parametrize("scale", [0.0, 0.125, 1.0, 2.5])
+def test_merge_scales(scale):
+    o, m, l = _merge_case(8, 50, 128, 21)
+    _check_merge(o, m, l, scale, "scale %g" % scale)
+
+
+def test_merge_large_spread_of_maxima():
+    o, m, l = _merge_case(4, 40, 64, 23)
+    m[1] += 900.0   # exp(scale * (m_p - M)) underflows for every other partition
+    _check_merge(o, m, l, 1.0, "spread")
+
+
+def test_merge_config_full_size():
+    o, m, l = synth.lse_merge()
+    P, depth = o.shape[0], o.shape[-1]
+    g = rr.splitk_lse_merge(to_gpu(o), to_gpu(m), to_gpu(l), 1.0, torch.bfloat16)
+    torch.cuda.synchronize()
+    assert tuple(g.shape) == (8, 32, 128, 128)
+    ref = oracle.splitk_lse_merge(o.reshape(P, -1, depth), m.reshape(P, -1), l.reshape(P, -1), 1.0,
+                                  "bf16")
+    assert_bf16_within_1ulp(to_host(g).reshape(-1, depth), ref, "lse_merge config")
+
+
+def test_merge_bit_identical_across_runs():
+    o, m, l = synth.lse_merge(P=8, batch=2, heads=8, q_rows=128, depth=128)
+    go, gm, gl = to_gpu(o), to_gpu(m), to_gpu(l)
+    first = rr.splitk_lse_merge(go, gm, gl).clone()
+    for _ in range(4):
+        assert torch.equal(rr.splitk_lse_merge(go, gm, gl).view(torch.int16), first.view(torch.int16))
