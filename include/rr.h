@@ -93,7 +93,9 @@ typedef struct {
     int64_t grid;            /* workgroups launched */
     int32_t lanes_per_row;   /* wave tier: lanes that share one row; else 0 */
     int32_t slices;          /* split-K: workgroups per row (G); else 1 */
-    int64_t slice_cols;      /* split-K: columns per slice (last slice may be shorter) */
+    int64_t tile_cols;       /* split-K: columns per tile; workgroup g of a row folds
+                                tiles g, g+G, g+2G, ... (the last tile may be shorter);
+                                else 0 */
     uint64_t workspace_bytes;/* bytes of workspace the call needs (0 if none) */
 } rr_plan;
 
@@ -110,7 +112,8 @@ typedef struct {
  *   WAVE    if cols <= 64
  *   BLOCK   otherwise
  * SERIAL is used only when forced.  WAVE is legal for cols <= 64 only.
- * SPLITK: G = clamp(ceil(4*cu_count/rows), 1, min(256, ceil(cols/16384))).
+ * SPLITK: G = clamp(ceil(4*cu_count/rows), 1, min(256, ceil(cols/16384), tiles))
+ * with tiles = ceil(cols / tile_cols), tile_cols = 8192 (2048 on the scalar path).
  * Returns RR_ERR_SHAPE for negative sizes or ld < cols, RR_ERR_DTYPE/OP for
  * unsupported dtype/op, RR_ERR_TIER for an illegal forced tier.
  */
@@ -136,17 +139,19 @@ rr_status rr_plan_softmax(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype
  *   tier   RR_TIER_AUTO or a forced tier
  *   workspace, workspace_bytes
  *          device scratch for RR_TIER_SPLITK (ignored otherwise; may be NULL
- *          when the plan needs 0 bytes).  Size: rr_workspace_bytes.  It must
- *          hold zeros before its first use; every completed call leaves it
- *          zero again.  One workspace must not serve two calls in flight.
+ *          when the plan needs 0 bytes).  Size: rr_workspace_bytes.  Its
+ *          ticket words (the first bytes) must be zero before its first use;
+ *          every completed call leaves them zero again (the partial slots
+ *          keep stale values, which a call always writes before it reads
+ *          them).  One workspace must not serve two calls in flight.
  *
  * Arithmetic: float SUM accumulates in double and rounds once to float
  * (nearest even); int32 SUM wraps modulo 2^32; MAX/MIN on float use the
  * IEEE 754 totalOrder (-0 < +0, NaNs ordered by sign and payload); cols == 0
  * writes the identity (0, -inf / INT32_MIN for MAX, +inf / INT32_MAX for MIN).
- * The split-K tier writes one partial per (row, slice) into the workspace and
- * the last workgroup of a row to arrive folds the partials in ascending slice
- * order, so the result does not depend on arrival order.
+ * The split-K tier writes one partial per (row, workgroup) into the workspace
+ * and the last workgroup of a row to arrive folds the partials in ascending
+ * workgroup order, so the result does not depend on arrival order.
  * rows == 0 is a no-op.
  */
 rr_status rr_reduce_rows(const void* x, void* y, int64_t rows, int64_t cols, int64_t ld,

@@ -47,7 +47,7 @@ class _Plan(ctypes.Structure):
     _fields_ = [
         ("tier", ctypes.c_int32), ("block", ctypes.c_int32), ("grid", ctypes.c_int64),
         ("lanes_per_row", ctypes.c_int32), ("slices", ctypes.c_int32),
-        ("slice_cols", ctypes.c_int64), ("workspace_bytes", ctypes.c_uint64),
+        ("tile_cols", ctypes.c_int64), ("workspace_bytes", ctypes.c_uint64),
     ]
 
 
@@ -229,7 +229,7 @@ def splitk_lse_merge(o_part, m_part, l_part, scale=1.0, out_dtype=torch.bfloat16
 def _plan_dict(plan):
     return {"tier": TIER_NAMES[plan.tier], "block": plan.block, "grid": plan.grid,
             "lanes_per_row": plan.lanes_per_row, "slices": plan.slices,
-            "slice_cols": plan.slice_cols, "workspace_bytes": plan.workspace_bytes}
+            "tile_cols": plan.tile_cols, "workspace_bytes": plan.workspace_bytes}
 
 
 def plan_reduce(rows, cols, dtype=torch.float32, op="sum", tier="auto", cu_count=256, ld=None):

@@ -18,9 +18,10 @@ constexpr int kWaveRowGroups = 4;
 // Tiled tier: rows owned by one thread (the page's emit_tile_width).
 constexpr int kTiledRows = 4;
 
-// Split-K trigger and slice sizing.
+// Split-K trigger and workgroups per row: at least kSplitKMinColsPerGroup
+// columns per workgroup.
 constexpr int64_t kSplitKMinCols = 65536;
-constexpr int64_t kSplitKMinSliceCols = 16384;
+constexpr int64_t kSplitKMinColsPerGroup = 16384;
 constexpr int kSplitKMaxSlices = 256;
 constexpr int kSplitKBlocksPerCU = 4;  // G aims at this many workgroups per CU in total
 
@@ -41,7 +42,7 @@ constexpr int kMergeMaxP = 256;
 constexpr int64_t kMaxGrid = 1 << 30;
 
 // Workspace layout for split-K: per-row tickets (uint32), padded to 256 B,
-// then per-(row, slice) partials of 8 bytes.
+// then per-(row, workgroup) partials of 8 bytes.
 constexpr int64_t kWorkspaceAlign = 256;
 
 constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -35,7 +35,7 @@ struct MergeOut<uint16_t> {
         uint2 u;
         u.x = pack_bf16x2((float)a[0], (float)a[1]);
         u.y = pack_bf16x2((float)a[2], (float)a[3]);
-        *reinterpret_cast<uint2*>(p) = u;
+        store8_nt(p, u);
     }
     __device__ static void one(uint16_t* p, double a) { *p = f32_to_bf16_bits((float)a); }
 };
@@ -43,7 +43,8 @@ template <>
 struct MergeOut<float> {
     __device__ static void four(float* p, const double* a)
     {
-        *reinterpret_cast<float4*>(p) = make_float4((float)a[0], (float)a[1], (float)a[2], (float)a[3]);
+        store16_nt(p, make_uint4(__float_as_uint((float)a[0]), __float_as_uint((float)a[1]),
+                                 __float_as_uint((float)a[2]), __float_as_uint((float)a[3])));
     }
     __device__ static void one(float* p, double a) { *p = (float)a; }
 };
@@ -58,8 +59,9 @@ __device__ __forceinline__ OChunk<VE> load_o(const float* p)
 {
     OChunk<VE> c;
     if constexpr (VE == 4) {
-        float4 u = *reinterpret_cast<const float4*>(p);
-        c.v[0] = u.x; c.v[1] = u.y; c.v[2] = u.z; c.v[3] = u.w;
+        uint4 u = load16_nt(p);
+        c.v[0] = __uint_as_float(u.x); c.v[1] = __uint_as_float(u.y);
+        c.v[2] = __uint_as_float(u.z); c.v[3] = __uint_as_float(u.w);
     } else {
         c.v[0] = *p;
     }

@@ -33,7 +33,7 @@ static void fill_rowwise_geometry(rr_tier tier, int64_t rows, int64_t cols, int 
     p->block = kBlockThreads;
     p->lanes_per_row = 0;
     p->slices = 1;
-    p->slice_cols = cols;
+    p->tile_cols = 0;
     p->workspace_bytes = 0;
     switch (tier) {
     case RR_TIER_WAVE: {
@@ -75,19 +75,21 @@ rr_status plan_reduce(int64_t rows, int64_t cols, int64_t ld, rr_dtype dtype, rr
         fill_rowwise_geometry(t, rows, cols, vec_elems, out);
         return RR_OK;
     }
-    // Split-K: G slices per row, each a multiple of 4 columns.
+    // Split-K: G workgroups per row; the row is cut into tiles of one
+    // unrolled load round of a workgroup, dealt to the G workgroups in turn.
+    const int64_t tile = (int64_t)kSplitKUnroll * kBlockThreads * vec_elems;
+    const int64_t ntiles = ceil_div(cols > 0 ? cols : 1, tile);
     int64_t g = ceil_div((int64_t)kSplitKBlocksPerCU * cu_count, rows > 0 ? rows : 1);
-    int64_t g_cap = ceil_div(cols, kSplitKMinSliceCols);
+    int64_t g_cap = ceil_div(cols, kSplitKMinColsPerGroup);
     if (g_cap > kSplitKMaxSlices) g_cap = kSplitKMaxSlices;
+    if (g_cap > ntiles) g_cap = ntiles;  // every workgroup gets at least one tile
     if (g > g_cap) g = g_cap;
     if (g < 1) g = 1;
-    int64_t slice = round_up(ceil_div(cols > 0 ? cols : 1, g), 4);
-    g = ceil_div(cols > 0 ? cols : 1, slice);  // every slice non-empty
     out->tier = RR_TIER_SPLITK;
     out->block = kBlockThreads;
     out->lanes_per_row = 0;
     out->slices = (int32_t)g;
-    out->slice_cols = slice;
+    out->tile_cols = tile;
     out->grid = rows * g;
     out->workspace_bytes = splitk_workspace_bytes(rows, (int32_t)g);
     return RR_OK;

@@ -39,7 +39,7 @@ __device__ __forceinline__ typename M::acc_t thread_fold(const typename M::in_t*
             Vec<T, 4> v[U];
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                v[u] = load4(base + (c + (int64_t)u * NT) * 4);
+                v[u] = load4<T, true>(base + (c + (int64_t)u * NT) * 4);
 #pragma unroll
             for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -47,7 +47,7 @@ __device__ __forceinline__ typename M::acc_t thread_fold(const typename M::in_t*
                     acc = M::combine(acc, M::lift(v[u].v[i]));
         }
         for (; c < nchunks; c += NT) {
-            Vec<T, 4> v = load4(base + c * 4);
+            Vec<T, 4> v = load4<T, true>(base + c * 4);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 acc = M::combine(acc, M::lift(v.v[i]));
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce_wave(
             const T* p = x + r * ld + (full ? c0 : 0);
             if constexpr (VEC == 4) {
                 if (cols >= 4)
-                    v[u] = load4(p);
+                    v[u] = load4<T, true>(p);
             } else {
                 v[u].v[0] = *p;
             }
@@ -209,31 +209,110 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce_tiled(
     }
 }
 
+// One unrolled load round of a thread: chunks p, p + NT*VEC, ... (U of them).
+template <int VEC, int NT, int U, class T>
+__device__ __forceinline__ void load_tile(const T* p, Vec<T, VEC>* v)
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if constexpr (VEC == 4) {
+            v[u] = load4<T, true>(p + (int64_t)u * NT * 4);
+        } else {
+            v[u].v[0] = p[(int64_t)u * NT];
+        }
+    }
+}
+
+// Fold a load round in ascending index order.
+template <class M, int VEC, int U>
+__device__ __forceinline__ typename M::acc_t fold_tile(typename M::acc_t acc,
+                                                       const Vec<typename M::in_t, VEC>* v)
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int i = 0; i < VEC; ++i)
+            acc = M::combine(acc, M::lift(v[u].v[i]));
+    return acc;
+}
+
 // ----------------------------------------------------------- split-K tier
-// Workgroup (r, g) folds slice g of row r, writes its partial to
-// part[r * G + g], releases it at device scope and takes a ticket on row r.
-// The workgroup that draws ticket G - 1 is the last to arrive: it acquires,
-// folds part[r * G + 0 .. G - 1] in ascending g, writes y[r] and resets the
-// ticket to zero for the next call.  `skew` (a test hook, normally 0) makes
-// slice g wait about (G - 1 - g) * skew sleep periods before publishing, so
-// arrival order runs against rank order.
+// Publishing a partial across workgroups (and across the eight XCDs, whose
+// L2 caches are not coherent with each other).  The partial is written with a
+// device-scope atomic store, which writes through the XCD's L2 to the
+// device-coherent level, and s_waitcnt vmcnt(0) holds the wave until that
+// store is acknowledged; only then is the ticket incremented.  This is the
+// agent-scope release of the AMDGPU memory model without its L2 writeback
+// (buffer_wbl2), which exists to push data written by ordinary stores and
+// costs tens of microseconds when a thousand workgroups issue it at the end
+// of a streaming pass.  The last workgroup reads the partials with
+// device-scope atomic loads, which are served coherently without an L2
+// invalidate.  The signal fences keep the compiler from moving the memory
+// operations across the wait.
+template <class A>
+__device__ __forceinline__ void publish_partial(A* slot, A v)
+{
+    __hip_atomic_store(slot, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+template <class A>
+__device__ __forceinline__ A read_partial(const A* slot)
+{
+    return __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A row is cut into tiles of kSplitKUnroll * kBlockThreads * VEC columns
+// (one unrolled load round of the workgroup); workgroup (r, g) folds tiles
+// g, g + G, g + 2G, ... of row r, so at any moment the G workgroups of a row
+// stream adjacent memory.  It then publishes its partial to part[r * G + g]
+// and takes a ticket on row r.  The workgroup that draws ticket G - 1 is the
+// last to arrive: it folds part[r * G + 0 .. G - 1] in ascending g, writes
+// y[r] and resets the ticket to zero for the next call.  `skew` (a test hook, normally 0) makes
+// workgroup g wait about (G - 1 - g) * skew sleep periods before publishing,
+// so arrival order runs against rank order.
 template <class M, int VEC>
 __global__ __launch_bounds__(kBlockThreads) void k_reduce_splitk(
     const typename M::in_t* __restrict__ x, typename M::in_t* __restrict__ y, int64_t rows,
-    int64_t cols, int64_t ld, int32_t G, int64_t slice_cols, typename M::acc_t* part,
-    uint32_t* ticket, int32_t skew)
+    int64_t cols, int64_t ld, int32_t G, typename M::acc_t* part, uint32_t* ticket, int32_t skew)
 {
     using A = typename M::acc_t;
+    constexpr int64_t kTile = (int64_t)kSplitKUnroll * kBlockThreads * VEC;
+    static_assert(kSplitKMaxSlices <= kBlockThreads, "one partial per thread when gathering");
     __shared__ A slot[2][kWavesPerBlock];
+    __shared__ A gathered[kSplitKMaxSlices];
+    __shared__ bool last;
     int par = 0;
+    if (threadIdx.x == 0)
+        last = false;
     const int64_t total = rows * G;
+    const int64_t ntiles = ceil_div(cols, kTile);
     for (int64_t b = blockIdx.x; b < total; b += gridDim.x) {
         const int64_t r = b / G;
         const int32_t g = (int32_t)(b - r * G);
-        const int64_t begin = (int64_t)g * slice_cols;
-        const int64_t end = begin + slice_cols < cols ? begin + slice_cols : cols;
-        A acc = thread_fold<M, VEC, kBlockThreads, kSplitKUnroll>(x + r * ld, begin, end,
-                                                                   threadIdx.x, M::identity());
+        const typename M::in_t* row = x + r * ld;
+        A acc = M::identity();
+        // Whole tiles: each round issues the thread's kSplitKUnroll loads of
+        // one tile, then folds them.  Tile indices are uniform across the
+        // workgroup, so the loop branch is scalar.
+        const int64_t nfull = cols / kTile;
+        int64_t t = g;
+        {
+            using T = typename M::in_t;
+            const T* p = row + (int64_t)threadIdx.x * VEC;
+            for (; t < nfull; t += G) {
+                Vec<T, VEC> v[kSplitKUnroll];
+                load_tile<VEC, kBlockThreads, kSplitKUnroll>(p + t * kTile, v);
+                acc = fold_tile<M, VEC, kSplitKUnroll>(acc, v);
+            }
+        }
+        // The partial last tile, if this workgroup owns it.
+        for (; t < ntiles; t += G) {
+            const int64_t begin = t * kTile;
+            const int64_t end = begin + kTile < cols ? begin + kTile : cols;
+            acc = thread_fold<M, VEC, kBlockThreads, kSplitKUnroll>(row, begin, end, threadIdx.x, acc);
+        }
         acc = block_reduce<M, kBlockThreads>(acc, slot[par]);
         par ^= 1;
         if (threadIdx.x == 0) {
@@ -242,19 +321,28 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce_splitk(
                 for (int i = 0; i < n; ++i)
                     __builtin_amdgcn_s_sleep(8);
             }
-            part[r * G + g] = acc;
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            publish_partial(&part[r * G + g], acc);
             const uint32_t t = __hip_atomic_fetch_add(&ticket[r], 1u, __ATOMIC_RELAXED,
                                                       __HIP_MEMORY_SCOPE_AGENT);
-            if (t == (uint32_t)(G - 1)) {
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-                A a = part[r * G];
+            last = t == (uint32_t)(G - 1);
+        }
+        __syncthreads();
+        if (last) {
+            // The whole workgroup gathers the G partials at once (G <= the
+            // block size), then thread 0 folds them in ascending rank order.
+            for (int32_t k = threadIdx.x; k < G; k += kBlockThreads)
+                gathered[k] = read_partial(&part[r * G + k]);
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                A a = gathered[0];
                 for (int32_t k = 1; k < G; ++k)
-                    a = M::combine(a, part[r * G + k]);
+                    a = M::combine(a, gathered[k]);
                 y[r] = M::finish(a);
+                last = false;
                 __hip_atomic_store(&ticket[r], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
+        __syncthreads();
     }
 }
 
@@ -329,9 +417,9 @@ static rr_status launch_monoid(const rr_plan& p, const ReduceLaunch& a)
                                        round_up(a.rows * 4, kWorkspaceAlign));
         const dim3 g2((unsigned)(p.grid > kMaxGrid ? kMaxGrid : p.grid));
         return a.vec ? launch_kernel(k_reduce_splitk<M, 4>, g2, block, 0, s, x, y, a.rows, a.cols, a.ld,
-                                     p.slices, p.slice_cols, part, ticket, a.skew)
+                                     p.slices, part, ticket, a.skew)
                      : launch_kernel(k_reduce_splitk<M, 1>, g2, block, 0, s, x, y, a.rows, a.cols, a.ld,
-                                     p.slices, p.slice_cols, part, ticket, a.skew);
+                                     p.slices, part, ticket, a.skew);
     }
     default:
         return RR_ERR_TIER;

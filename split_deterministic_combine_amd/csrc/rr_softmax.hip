@@ -22,7 +22,8 @@ namespace rr {
 
 constexpr float kNegInf = -__builtin_inff();
 
-// Element access: XT is uint16_t (bf16 bits) or float.
+// Element access: XT is uint16_t (bf16 bits) or float.  Whole 16-byte chunks
+// move with non-temporal loads and stores (every byte is touched once).
 template <class XT>
 struct XIn;
 template <>
@@ -30,7 +31,7 @@ struct XIn<uint16_t> {
     static constexpr int kChunk = 8;  // elements per 128-bit load
     __device__ static void chunk(const uint16_t* p, float* v)
     {
-        uint4 u = *reinterpret_cast<const uint4*>(p);
+        uint4 u = load16_nt(p);
         v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x);
         v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
         v[4] = bf16_lo(u.z); v[5] = bf16_hi(u.z);
@@ -43,8 +44,9 @@ struct XIn<float> {
     static constexpr int kChunk = 4;
     __device__ static void chunk(const float* p, float* v)
     {
-        float4 u = *reinterpret_cast<const float4*>(p);
-        v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+        uint4 u = load16_nt(p);
+        v[0] = __uint_as_float(u.x); v[1] = __uint_as_float(u.y);
+        v[2] = __uint_as_float(u.z); v[3] = __uint_as_float(u.w);
     }
     __device__ static float one(const float* p) { return *p; }
 };
@@ -60,12 +62,12 @@ struct YOut<uint16_t> {
             uint4 u;
             u.x = pack_bf16x2(v[0], v[1]); u.y = pack_bf16x2(v[2], v[3]);
             u.z = pack_bf16x2(v[4], v[5]); u.w = pack_bf16x2(v[6], v[7]);
-            *reinterpret_cast<uint4*>(p) = u;
+            store16_nt(p, u);
         } else {
             static_assert(E == 4, "chunk of 4 or 8");
             uint2 u;
             u.x = pack_bf16x2(v[0], v[1]); u.y = pack_bf16x2(v[2], v[3]);
-            *reinterpret_cast<uint2*>(p) = u;
+            store8_nt(p, u);
         }
     }
     __device__ static void one(uint16_t* p, float v) { *p = f32_to_bf16_bits(v); }
@@ -77,7 +79,8 @@ struct YOut<float> {
     {
 #pragma unroll
         for (int i = 0; i < E; i += 4)
-            *reinterpret_cast<float4*>(p + i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
+            store16_nt(p + i, make_uint4(__float_as_uint(v[i]), __float_as_uint(v[i + 1]),
+                                         __float_as_uint(v[i + 2]), __float_as_uint(v[i + 3])));
     }
     __device__ static void one(float* p, float v) { *p = v; }
 };

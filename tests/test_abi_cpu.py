@@ -69,17 +69,18 @@ def test_auto_tier_rule(rows, cols, tier):
 
 def test_splitk_geometry_for_the_long_row_workload():
     p = rr.plan_reduce(16, 1 << 24, cu_count=256)
-    assert p["slices"] == 64 and p["grid"] == 1024 and p["slice_cols"] == 1 << 18
+    assert p["slices"] == 64 and p["grid"] == 1024 and p["tile_cols"] == 8192
     assert p["workspace_bytes"] == 256 + 16 * 64 * 8
 
 
 @pytest.mark.parametrize("rows,cols", [(1, 65536), (7, 100003), (200, 1 << 20), (3, 70001),
                                        (16, 1 << 24), (1, 1 << 30)])
-def test_splitk_slices_cover_the_row_and_are_non_empty(rows, cols):
+def test_splitk_every_workgroup_gets_a_tile(rows, cols):
     p = rr.plan_reduce(rows, cols, tier="splitk", cu_count=256)
-    g, s = p["slices"], p["slice_cols"]
-    assert 1 <= g <= 256 and s % 4 == 0
-    assert (g - 1) * s < cols <= g * s
+    g, t = p["slices"], p["tile_cols"]
+    assert 1 <= g <= 256 and t % 4 == 0
+    assert g <= -(-cols // t)          # tiles g, g+G, ... : workgroup G-1 has tile G-1
+    assert p["grid"] == rows * g
 
 
 def test_splitk_forced_on_short_rows_has_one_slice():
