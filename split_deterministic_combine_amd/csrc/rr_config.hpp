@@ -33,6 +33,16 @@ constexpr int kSplitKUnroll = 8;
 // needing more than kSoftmaxMaxChunks chunks per thread use the streaming
 // variant that reads x twice.
 constexpr int kSoftmaxMaxChunks = 8;
+// Rows too long to stay in the registers of kBlockThreads threads (more
+// than kBlockThreads * kSoftmaxMaxChunks 16-byte chunks) run on workgroups of
+// kSoftmaxWideThreads threads, which keeps rows up to twice as long resident
+// instead of reading them twice.
+constexpr int kSoftmaxWideThreads = 512;
+// Block-tier softmax on whole-chunk, 16-byte aligned rows runs persistent
+// workgroups (each walks rows b, b + grid, ... with a one-row prefetch):
+// this many per CU.
+constexpr int kSoftmaxRowBlocksPerCU = 2;
+constexpr int64_t kSoftmaxWideMinChunks = (int64_t)kBlockThreads * kSoftmaxMaxChunks;
 
 // LSE merge: partitions staged per batch of loads, and workgroup size.
 constexpr int kMergeBatch = 8;

@@ -146,17 +146,29 @@ struct MS {
     float s;
 };
 
+// exp2 with correct subnormal results (the library function scales the
+// argument range itself).
 __device__ __forceinline__ float exp2_f32(float t) { return exp2f(t); }
+
+// The hardware instruction v_exp_f32 alone: equal to exp2f wherever the
+// result is a normal number (checked on MI355X over the whole normal range
+// boundary), but it flushes results below 2^-126 to zero.  Used where such
+// a result cannot change anything, or behind a check for that range.
+__device__ __forceinline__ float exp2_hw(float t) { return __builtin_amdgcn_exp2f(t); }
 
 struct SoftmaxMS {
     using acc_t = MS;
     __device__ static acc_t identity() { return MS{-__builtin_inff(), 0.0f}; }
+    // Every non-identity state has s >= 1 (its own maximum contributes
+    // exp(0) = 1), so a term flushed by exp2_hw -- below 2^-126 times s <=
+    // 2^24 -- lies far under half an ulp of the other term and the hardware
+    // exponential gives the same sum.
     __device__ static acc_t combine(acc_t a, acc_t b)
     {
         float M = fmaxf(a.m, b.m);
         if (M == -__builtin_inff())
             return MS{M, 0.0f};
-        float s = a.s * exp2_f32((a.m - M) * kLog2e) + b.s * exp2_f32((b.m - M) * kLog2e);
+        float s = a.s * exp2_hw((a.m - M) * kLog2e) + b.s * exp2_hw((b.m - M) * kLog2e);
         return MS{M, s};
     }
 };

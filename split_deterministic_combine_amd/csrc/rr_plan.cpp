@@ -111,6 +111,17 @@ rr_status plan_softmax(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype y_
     memset(out, 0, sizeof *out);
     const int vec_elems = vec ? (x_dtype == RR_BF16 ? 8 : 4) : 1;
     fill_rowwise_geometry(t, rows, cols, vec_elems, out);
+    if (t == RR_TIER_BLOCK) {
+        const int64_t chunks = ceil_div(cols, vec_elems);
+        if (chunks > kSoftmaxWideMinChunks)
+            out->block = kSoftmaxWideThreads;
+        // Rows of whole 16-byte chunks that stay in registers: persistent
+        // workgroups with a one-row prefetch.
+        if (vec && cols % vec_elems == 0 && ceil_div(chunks, out->block) <= kSoftmaxMaxChunks) {
+            const int64_t g = (int64_t)cu_count * kSoftmaxRowBlocksPerCU;
+            out->grid = rows < g ? rows : g;
+        }
+    }
     return RR_OK;
 }
 

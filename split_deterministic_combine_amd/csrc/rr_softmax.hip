@@ -122,6 +122,10 @@ __device__ __forceinline__ void store_masked(YT* row, int64_t j0, int64_t cols, 
 
 // Pass 1 on values held by one thread: m = max, v <- exp(v - m), s = sum v.
 // With m == -inf (nothing but -inf / padding) every p is 0.
+// The exponent argument is x*log2(e) - m*log2(e) in one fused multiply-add.
+// The hardware exponential is exact for normal results; when any argument
+// falls below -126 (a subnormal or vanishing result, or a -inf entry) the
+// thread recomputes its values with exp2f, which scales the range itself.
 template <int N>
 __device__ __forceinline__ MS local_exp_sum(float* v)
 {
@@ -131,11 +135,25 @@ __device__ __forceinline__ MS local_exp_sum(float* v)
         m = fmaxf(m, v[i]);
     float s = 0.0f;
     if (m != kNegInf) {
+        const float mb = -m * kLog2e;
+        float tmin = 0.0f;
 #pragma unroll
         for (int i = 0; i < N; ++i) {
-            v[i] = exp2_f32((v[i] - m) * kLog2e);
-            s += v[i];
+            v[i] = __builtin_fmaf(v[i], kLog2e, mb);
+            tmin = fminf(tmin, v[i]);
         }
+        if (tmin >= -126.0f) {
+#pragma unroll
+            for (int i = 0; i < N; ++i)
+                v[i] = exp2_hw(v[i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < N; ++i)
+                v[i] = exp2_f32(v[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            s += v[i];
     } else {
 #pragma unroll
         for (int i = 0; i < N; ++i)
@@ -145,14 +163,13 @@ __device__ __forceinline__ MS local_exp_sum(float* v)
 }
 
 // ------------------------------------------- block tier, row in registers
-template <class XT, class YT, int NCH, bool VEC>
-__global__ __launch_bounds__(kBlockThreads) void k_softmax_block(const XT* __restrict__ x,
-                                                                 YT* __restrict__ y, int64_t rows,
-                                                                 int64_t cols, int64_t ldx,
-                                                                 int64_t ldy)
+template <class XT, class YT, int NCH, bool VEC, int NT>
+__global__ __launch_bounds__(NT) void k_softmax_block(const XT* __restrict__ x,
+                                                      YT* __restrict__ y, int64_t rows,
+                                                      int64_t cols, int64_t ldx, int64_t ldy)
 {
     constexpr int E = VEC ? XIn<XT>::kChunk : 1;
-    __shared__ MS slot[2][kWavesPerBlock];
+    __shared__ MS slot[2][NT / kWave];
     int par = 0;
     for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
         const XT* xr = x + r * ldx;
@@ -160,10 +177,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_softmax_block(const XT* __res
         float v[NCH * E];
 #pragma unroll
         for (int k = 0; k < NCH; ++k)
-            load_padded<XT, E, VEC>(xr, ((int64_t)threadIdx.x + (int64_t)k * kBlockThreads) * E,
-                                    cols, v + k * E);
+            load_padded<XT, E, VEC>(xr, ((int64_t)threadIdx.x + (int64_t)k * NT) * E, cols,
+                                    v + k * E);
         const MS own = local_exp_sum<NCH * E>(v);
-        const MS tot = block_reduce<SoftmaxMS, kBlockThreads>(own, slot[par]);
+        const MS tot = block_reduce<SoftmaxMS, NT>(own, slot[par]);
         par ^= 1;
         const float sc = exp2_f32((own.m - tot.m) * kLog2e) / tot.s;
 #pragma unroll
@@ -171,21 +188,112 @@ __global__ __launch_bounds__(kBlockThreads) void k_softmax_block(const XT* __res
             v[i] *= sc;
 #pragma unroll
         for (int k = 0; k < NCH; ++k)
-            store_masked<YT, E, VEC>(yr, ((int64_t)threadIdx.x + (int64_t)k * kBlockThreads) * E,
-                                     cols, v + k * E);
+            store_masked<YT, E, VEC>(yr, ((int64_t)threadIdx.x + (int64_t)k * NT) * E, cols,
+                                     v + k * E);
+    }
+}
+
+// ------------------------- block tier, persistent rows with prefetch
+// Whole-chunk rows (cols a multiple of the chunk, 16-byte aligned rows):
+// workgroup b takes rows b, b + grid, b + 2*grid, ... and loads the next
+// row's chunks while it computes the current one, so each workgroup keeps a
+// row's worth of loads in flight through its compute phase.  Two register
+// buffers alternate; when there is no next row the prefetch re-reads the
+// current one (an L2 hit) and is dropped, so no load sits behind a branch.
+template <class XT>
+__device__ __forceinline__ void unpack_chunk(uint4 u, float* v)
+{
+    if constexpr (sizeof(XT) == 2) {
+        v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x);
+        v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
+        v[4] = bf16_lo(u.z); v[5] = bf16_hi(u.z);
+        v[6] = bf16_lo(u.w); v[7] = bf16_hi(u.w);
+    } else {
+        v[0] = __uint_as_float(u.x); v[1] = __uint_as_float(u.y);
+        v[2] = __uint_as_float(u.z); v[3] = __uint_as_float(u.w);
+    }
+}
+
+template <class XT, class YT, int NCH, int NT>
+__device__ __forceinline__ void softmax_row_from_chunks(const uint4* raw, YT* yr, int64_t cols,
+                                                        MS* slot)
+{
+    constexpr int E = XIn<XT>::kChunk;
+    float v[NCH * E];
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+        const int64_t j0 = ((int64_t)threadIdx.x + (int64_t)k * NT) * E;
+        if (j0 < cols) {
+            unpack_chunk<XT>(raw[k], v + k * E);
+        } else {
+#pragma unroll
+            for (int i = 0; i < E; ++i)
+                v[k * E + i] = kNegInf;
+        }
+    }
+    const MS own = local_exp_sum<NCH * E>(v);
+    const MS tot = block_reduce<SoftmaxMS, NT>(own, slot);
+    const float sc = exp2_f32((own.m - tot.m) * kLog2e) / tot.s;
+#pragma unroll
+    for (int i = 0; i < NCH * E; ++i)
+        v[i] *= sc;
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+        const int64_t j0 = ((int64_t)threadIdx.x + (int64_t)k * NT) * E;
+        if (j0 < cols)
+            YOut<YT>::template chunk<E>(yr + j0, v + k * E);
+    }
+}
+
+template <class XT, int NCH, int NT>
+__device__ __forceinline__ void load_row_chunks(const XT* xr, int64_t cols, uint4* raw)
+{
+    constexpr int E = XIn<XT>::kChunk;
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+        int64_t j0 = ((int64_t)threadIdx.x + (int64_t)k * NT) * E;
+        j0 = j0 < cols ? j0 : 0;  // chunks past the row end read chunk 0 (ignored)
+        raw[k] = load16_nt(xr + j0);
+    }
+}
+
+template <class XT, class YT, int NCH, int NT>
+__global__ __launch_bounds__(NT) void k_softmax_rows_pf(const XT* __restrict__ x,
+                                                        YT* __restrict__ y, int64_t rows,
+                                                        int64_t cols, int64_t ldx, int64_t ldy)
+{
+    __shared__ MS slot[2][NT / kWave];
+    int64_t r = blockIdx.x;
+    if (r >= rows)
+        return;
+    const int64_t step = gridDim.x;
+    uint4 a[NCH], b[NCH];
+    load_row_chunks<XT, NCH, NT>(x + r * ldx, cols, a);
+    for (;;) {
+        const bool more = r + step < rows;
+        load_row_chunks<XT, NCH, NT>(x + (more ? r + step : r) * ldx, cols, b);
+        softmax_row_from_chunks<XT, YT, NCH, NT>(a, y + r * ldy, cols, slot[0]);
+        if (!more)
+            break;
+        r += step;
+        const bool more2 = r + step < rows;
+        load_row_chunks<XT, NCH, NT>(x + (more2 ? r + step : r) * ldx, cols, a);
+        softmax_row_from_chunks<XT, YT, NCH, NT>(b, y + r * ldy, cols, slot[1]);
+        if (!more2)
+            break;
+        r += step;
     }
 }
 
 // ---------------------------------------- block tier, streaming long rows
 // Pass 1 folds (m, s) chunk by chunk; pass 2 reads x again.
-template <class XT, class YT, bool VEC>
-__global__ __launch_bounds__(kBlockThreads) void k_softmax_stream(const XT* __restrict__ x,
-                                                                  YT* __restrict__ y,
-                                                                  int64_t rows, int64_t cols,
-                                                                  int64_t ldx, int64_t ldy)
+template <class XT, class YT, bool VEC, int NT>
+__global__ __launch_bounds__(NT) void k_softmax_stream(const XT* __restrict__ x,
+                                                       YT* __restrict__ y, int64_t rows,
+                                                       int64_t cols, int64_t ldx, int64_t ldy)
 {
     constexpr int E = VEC ? XIn<XT>::kChunk : 1;
-    __shared__ MS slot[2][kWavesPerBlock];
+    __shared__ MS slot[2][NT / kWave];
     int par = 0;
     for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
         const XT* xr = x + r * ldx;
@@ -194,7 +302,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_softmax_stream(const XT* __re
         // adds many terms in sequence on long rows
         float tm = kNegInf;
         double ts = 0.0;
-        for (int64_t j0 = (int64_t)threadIdx.x * E; j0 < cols; j0 += (int64_t)kBlockThreads * E) {
+        for (int64_t j0 = (int64_t)threadIdx.x * E; j0 < cols; j0 += (int64_t)NT * E) {
             float v[E];
             load_padded<XT, E, VEC>(xr, j0, cols, v);
             float cm = kNegInf;
@@ -211,10 +319,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_softmax_stream(const XT* __re
                 ts = s;
             }
         }
-        const MS tot = block_reduce<SoftmaxMS, kBlockThreads>(MS{tm, (float)ts}, slot[par]);
+        const MS tot = block_reduce<SoftmaxMS, NT>(MS{tm, (float)ts}, slot[par]);
         par ^= 1;
         const float inv = 1.0f / tot.s;
-        for (int64_t j0 = (int64_t)threadIdx.x * E; j0 < cols; j0 += (int64_t)kBlockThreads * E) {
+        for (int64_t j0 = (int64_t)threadIdx.x * E; j0 < cols; j0 += (int64_t)NT * E) {
             float v[E];
             load_padded<XT, E, VEC>(xr, j0, cols, v);
 #pragma unroll
@@ -305,6 +413,41 @@ __global__ __launch_bounds__(kBlockThreads) void k_softmax_tiled(const XT* __res
 }
 
 // ---------------------------------------------------------------- launch
+// Block tier: the row stays in registers when each of the NT threads holds
+// at most kSoftmaxMaxChunks chunks; longer rows stream twice.
+template <class XT, class YT, bool VEC, int NT>
+static rr_status launch_block(const rr_plan& p, const SoftmaxLaunch& a)
+{
+    const XT* x = static_cast<const XT*>(a.x);
+    YT* y = static_cast<YT*>(a.y);
+    const dim3 grid((unsigned)p.grid), block(NT);
+    const hipStream_t s = a.stream;
+    constexpr int E = VEC ? XIn<XT>::kChunk : 1;
+    const int64_t nch = ceil_div(ceil_div(a.cols, E), NT);
+    if constexpr (VEC) {
+        if (a.cols % E == 0 && nch <= kSoftmaxMaxChunks) {
+            // persistent rows with prefetch; the plan sized the grid
+            const dim3 pg((unsigned)p.grid);
+            if (nch <= 1)
+                return launch_kernel(k_softmax_rows_pf<XT, YT, 1, NT>, pg, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
+            if (nch <= 2)
+                return launch_kernel(k_softmax_rows_pf<XT, YT, 2, NT>, pg, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
+            if (nch <= 4)
+                return launch_kernel(k_softmax_rows_pf<XT, YT, 4, NT>, pg, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
+            return launch_kernel(k_softmax_rows_pf<XT, YT, kSoftmaxMaxChunks, NT>, pg, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
+        }
+    }
+    if (nch <= 1)
+        return launch_kernel(k_softmax_block<XT, YT, 1, VEC, NT>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
+    if (nch <= 2)
+        return launch_kernel(k_softmax_block<XT, YT, 2, VEC, NT>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
+    if (nch <= 4)
+        return launch_kernel(k_softmax_block<XT, YT, 4, VEC, NT>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
+    if (nch <= kSoftmaxMaxChunks)
+        return launch_kernel(k_softmax_block<XT, YT, kSoftmaxMaxChunks, VEC, NT>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
+    return launch_kernel(k_softmax_stream<XT, YT, VEC, NT>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
+}
+
 template <class XT, class YT, bool VEC>
 static rr_status launch_typed(const rr_plan& p, const SoftmaxLaunch& a)
 {
@@ -312,21 +455,10 @@ static rr_status launch_typed(const rr_plan& p, const SoftmaxLaunch& a)
     YT* y = static_cast<YT*>(a.y);
     const dim3 grid((unsigned)p.grid), block(kBlockThreads);
     const hipStream_t s = a.stream;
-    constexpr int E = VEC ? XIn<XT>::kChunk : 1;
     switch (p.tier) {
-    case RR_TIER_BLOCK: {
-        const int64_t chunks = ceil_div(a.cols, E);
-        const int64_t nch = ceil_div(chunks, kBlockThreads);
-        if (nch <= 1)
-            return launch_kernel(k_softmax_block<XT, YT, 1, VEC>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
-        if (nch <= 2)
-            return launch_kernel(k_softmax_block<XT, YT, 2, VEC>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
-        if (nch <= 4)
-            return launch_kernel(k_softmax_block<XT, YT, 4, VEC>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
-        if (nch <= kSoftmaxMaxChunks)
-            return launch_kernel(k_softmax_block<XT, YT, kSoftmaxMaxChunks, VEC>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
-        return launch_kernel(k_softmax_stream<XT, YT, VEC>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
-    }
+    case RR_TIER_BLOCK:
+        return p.block == kSoftmaxWideThreads ? launch_block<XT, YT, VEC, kSoftmaxWideThreads>(p, a)
+                                              : launch_block<XT, YT, VEC, kBlockThreads>(p, a);
     case RR_TIER_WAVE:
         switch (p.lanes_per_row) {
         case 4: return launch_kernel(k_softmax_wave<XT, YT, VEC, 4>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);

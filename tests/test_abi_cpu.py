@@ -98,6 +98,11 @@ def test_wave_lanes_per_row():
 
 def test_softmax_tier_rule():
     assert rr.plan_softmax(8192, 8192)["tier"] == "block"
+    assert rr.plan_softmax(8192, 8192)["block"] == 256
+    assert rr.plan_softmax(8192, 8192)["grid"] == 512        # persistent rows: 2 per CU
+    assert rr.plan_softmax(8192, 8191)["grid"] == 8192       # ragged rows: one per workgroup
+    assert rr.plan_softmax(64, 16384)["block"] == 256        # 256 threads x 8 chunks x 8 bf16
+    assert rr.plan_softmax(64, 16385)["block"] == 512        # longer rows: wider workgroups
     assert rr.plan_softmax(100, 40)["tier"] == "wave"
     assert rr.plan_softmax(100, 4)["tier"] == "tiled"
     with pytest.raises(rr.RRError) as e:
