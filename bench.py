@@ -43,6 +43,127 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+# op name -> substring of the kernel symbol that runs it at the benchmark shapes
+KERNEL_OF_OP = {
+    "short_sum": "k_reduce_wave<rr::SumF32, 4, 16>",
+    "short_max": "k_reduce_wave<rr::MaxF32, 4, 16>",
+    "softmax": "k_softmax_rows_pf<unsigned short, unsigned short, 4, 256>",
+    "long_sum": "k_reduce_splitk<rr::SumF32, 4>",
+    "long_max": "k_reduce_splitk<rr::MaxI32, 4>",
+    "merge": "k_lse_merge<unsigned short, 4, 32>",
+}
+ALGO_BYTES = {
+    "short_sum": 1048576 * 48 * 4 + 1048576 * 4,
+    "short_max": 1048576 * 48 * 4 + 1048576 * 4,
+    "softmax": 8192 * 8192 * 2 * 2,
+    "long_sum": 16 * (1 << 24) * 4 + 16 * 4,
+    "long_max": 16 * (1 << 24) * 4 + 16 * 4,
+    "merge": 8 * 32768 * 128 * 4 + 2 * 8 * 32768 * 4 + 32768 * 128 * 2,
+}
+COPY_BYTES = 512 << 20
+
+
+def _csv_rows(directory, suffix):
+    import csv
+    import glob
+
+    rows = []
+    for f in sorted(glob.glob(os.path.join(directory, "**", "*" + suffix), recursive=True)):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def ingest_counters(trace_dir, fetch_dir, write_dir):
+    """Turn rocprofv3 CSVs into profiles/traffic.json and markdown summaries."""
+    stats = _csv_rows(trace_dir, "kernel_stats.csv")
+    per_counter = {}
+    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        vals = {}
+        for r in _csv_rows(d, "counter_collection.csv"):
+            if r.get("Counter_Name") != name:
+                continue
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        per_counter[name] = vals
+
+    def mean_for(vals, pattern):
+        hits = [v for k, vs in vals.items() if pattern in k for v in vs]
+        return sum(hits) / len(hits) if hits else None
+
+    copy_pat = "neg"  # torch's elementwise negation kernel run by --calibrate-copy
+    copy_fetch = [v for k, vs in per_counter["FETCH_SIZE"].items() if copy_pat in k.lower() for v in vs]
+    copy_write = [v for k, vs in per_counter["WRITE_SIZE"].items() if copy_pat in k.lower() for v in vs]
+    # counters are in KiB per dispatch; the calibration copy moves COPY_BYTES each way
+    fetch_scale = COPY_BYTES / (1024.0 * max(copy_fetch)) if copy_fetch else None
+    write_scale = COPY_BYTES / (1024.0 * max(copy_write)) if copy_write else None
+    kernels = {}
+    for op, pat in KERNEL_OF_OP.items():
+        f = mean_for(per_counter["FETCH_SIZE"], pat)
+        w = mean_for(per_counter["WRITE_SIZE"], pat)
+        if f is None or w is None or fetch_scale is None or write_scale is None:
+            continue
+        fb, wb = f * 1024.0 * fetch_scale, w * 1024.0 * write_scale
+        kernels[op] = {"kernel": pat, "fetch_kib_raw": round(f, 1), "write_kib_raw": round(w, 1),
+                       "fetch_bytes": int(fb), "write_bytes": int(wb),
+                       "bytes_per_launch": int(fb + wb), "algorithmic_bytes": ALGO_BYTES[op],
+                       "traffic_over_algorithmic": round((fb + wb) / ALGO_BYTES[op], 3)}
+    out = {"source_hash": kernel_source_hash(),
+           "calibration": {"copy_bytes_each_way": COPY_BYTES,
+                           "copy_fetch_kib_raw": max(copy_fetch) if copy_fetch else None,
+                           "copy_write_kib_raw": max(copy_write) if copy_write else None,
+                           "fetch_scale": fetch_scale, "write_scale": write_scale},
+           "kernels": kernels}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    lines = ["| kernel (op) | calls | avg us | min us | max us | algorithmic GB/s | % of 8 TB/s |",
+             "|---|---|---|---|---|---|---|"]
+    for op, pat in KERNEL_OF_OP.items():
+        for r in stats:
+            if pat in r.get("Name", ""):
+                avg = float(r["AverageNs"]) / 1e3
+                gbs = ALGO_BYTES[op] / (avg * 1e-6) / 1e9
+                lines.append("| `%s` (%s) | %s | %.1f | %.1f | %.1f | %.0f | %.1f |" % (
+                    pat, op, r["Calls"], avg, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, gbs,
+                    100 * gbs / PEAK_HBM_GBS))
+    table = "\n".join(lines)
+    prof = os.path.dirname(TRAFFIC_FILE)
+    with open(os.path.join(prof, "kernels_rowwise_suite.md"), "w") as f:
+        f.write("# Kernel durations, row-wise suite (one MI355X)\n\n"
+                "Command (from the repository root on the GPU host):\n\n"
+                "    cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -f csv "
+                "-d $R/gpurun_out/prof_trace -o trace -- python3 $R/bench.py\n\n"
+                "with `R` the repository root; summarised by `python bench.py --ingest-counters "
+                "gpurun_out/prof_trace gpurun_out/prof_fetch gpurun_out/prof_write`.\n"
+                "GB/s = algorithmic bytes per launch / average kernel duration.\n\n" + table + "\n")
+    tl = ["| op | kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (scaled) | algorithmic bytes | ratio |",
+          "|---|---|---|---|---|---|---|"]
+    for op, k in kernels.items():
+        tl.append("| %s | `%s` | %.1f | %.1f | %d | %d | %.3f |" % (
+            op, k["kernel"], k["fetch_kib_raw"], k["write_kib_raw"], k["bytes_per_launch"],
+            k["algorithmic_bytes"], k["traffic_over_algorithmic"]))
+    cal = out["calibration"]
+    with open(os.path.join(prof, "traffic_rowwise_suite.md"), "w") as f:
+        f.write("# HBM traffic per launch, row-wise suite (one MI355X)\n\n"
+                "Two counter passes, one counter each (from the repository root `R`):\n\n"
+                "    cd /tmp && export TMPDIR=/tmp && timeout -s KILL 240 rocprofv3 --pmc FETCH_SIZE "
+                "-f csv -d $R/gpurun_out/prof_fetch -o fetch -- python3 $R/bench.py --steps 2 "
+                "--warmup 1 --no-cpu-baseline --no-parity --calibrate-copy\n"
+                "    cd /tmp && export TMPDIR=/tmp && timeout -s KILL 240 rocprofv3 --pmc WRITE_SIZE "
+                "-f csv -d $R/gpurun_out/prof_write -o write -- python3 $R/bench.py --steps 2 "
+                "--warmup 1 --no-cpu-baseline --no-parity --calibrate-copy\n\n"
+                "Counters are KiB per dispatch (mean over dispatches).  `--calibrate-copy` runs a "
+                "plain elementwise pass (torch `neg`) that reads and writes %d bytes; its readings "
+                "(FETCH %.1f KiB, WRITE %.1f KiB) give the scale factors %.4f (fetch) and %.4f "
+                "(write) applied to every kernel.\n\n" % (
+                    cal["copy_bytes_each_way"], cal["copy_fetch_kib_raw"] or 0,
+                    cal["copy_write_kib_raw"] or 0, cal["fetch_scale"] or 0, cal["write_scale"] or 0)
+                + "\n".join(tl) + "\n\nKernel sources hash: `%s` (bench.py reports `traffic` only "
+                "while the sources match).\n" % out["source_hash"])
+    return out, table
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -51,6 +172,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--only", default=None, help="comma list of ops to run (profiling)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain 512 MiB elementwise copy (negation) three times: "
+                         "the known-size reference for scaling FETCH_SIZE / WRITE_SIZE")
+    ap.add_argument("--ingest-counters", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="host only: read rocprofv3 CSV output (kernel stats, FETCH_SIZE run, "
+                         "WRITE_SIZE run) and write profiles/traffic.json and summaries")
     return ap.parse_args()
 
 
@@ -69,6 +196,11 @@ def log(msg):
 
 def main():
     args = parse()
+    if args.ingest_counters:
+        out, table = ingest_counters(*args.ingest_counters)
+        print(json.dumps(out, indent=1))
+        print(table)
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -81,6 +213,14 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        # a plain elementwise pass of known size: reads and writes COPY_BYTES once
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     def gpu(a):
         if a.dtype == np.uint16:
@@ -110,23 +250,17 @@ def main():
     dx["merge"] = [(o, m, l)] + [(o.clone(), m.clone(), l.clone()) for _ in range(sets["merge"] - 1)]
     dx["merge_out"] = [torch.empty((8, 32, 128, 128), dtype=torch.bfloat16, device=dev)
                        for _ in range(sets["merge"])]
-    y_short = torch.empty(1048576, dtype=torch.float32, device=dev)
+    y_short_sum = torch.empty(1048576, dtype=torch.float32, device=dev)
+    y_short_max = torch.empty(1048576, dtype=torch.float32, device=dev)
     y_long_f = torch.empty(16, dtype=torch.float32, device=dev)
     y_long_i = torch.empty(16, dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
 
     # algorithmic bytes per launch (inputs read once, outputs written once)
-    B = {
-        "short_sum": 1048576 * 48 * 4 + 1048576 * 4,
-        "short_max": 1048576 * 48 * 4 + 1048576 * 4,
-        "softmax": 8192 * 8192 * 2 * 2,
-        "long_sum": 16 * (1 << 24) * 4 + 16 * 4,
-        "long_max": 16 * (1 << 24) * 4 + 16 * 4,
-        "merge": 8 * 32768 * 128 * 4 + 2 * 8 * 32768 * 4 + 32768 * 128 * 2,
-    }
+    B = dict(ALGO_BYTES)
     ops = {
-        "short_sum": lambda i: rr.reduce_rows(dx["short"][i % 5], "sum", out=y_short),
-        "short_max": lambda i: rr.reduce_rows(dx["short"][i % 5], "max", out=y_short),
+        "short_sum": lambda i: rr.reduce_rows(dx["short"][i % 5], "sum", out=y_short_sum),
+        "short_max": lambda i: rr.reduce_rows(dx["short"][i % 5], "max", out=y_short_max),
         "softmax": lambda i: rr.softmax_rows(dx["softmax"][i % 4], out=dx["softmax_out"][i % 4]),
         "long_sum": lambda i: rr.reduce_rows(dx["long_f"][0], "sum", out=y_long_f),
         "long_max": lambda i: rr.reduce_rows(dx["long_i"][0], "max", out=y_long_i),
@@ -145,12 +279,14 @@ def main():
             ops[n](0)
         torch.cuda.synchronize()
         ok = True
-        if "short_sum" in names or "short_max" in names:
-            xs = host["short"][:4096]
-            for op in ("sum", "max"):
-                y = rr.reduce_rows(dx["short"][0][:4096], op).cpu().numpy()
-                r = oracle.reduce_rows(xs, op)
-                ok &= bool(np.all(np.abs(y - r) <= 1e-6 + 1e-5 * np.abs(r)))
+        # sampled rows of the full-size outputs of the pass above (no extra launches)
+        xs = host["short"][:4096]
+        if "short_sum" in names:
+            y = y_short_sum[:4096].cpu().numpy()
+            r = oracle.reduce_rows(xs, "sum")
+            ok &= bool(np.all(np.abs(y - r) <= 1e-6 + 1e-5 * np.abs(r)))
+        if "short_max" in names:
+            ok &= bool(np.array_equal(y_short_max[:4096].cpu().numpy(), oracle.reduce_rows(xs, "max")))
         if "long_sum" in names:
             y = y_long_f.cpu().numpy()
             r = oracle.reduce_rows(host["long_f"][:2], "sum")
@@ -218,7 +354,8 @@ def main():
         ent = tr.get("kernels", {}).get(dom)
         if ent and tr.get("source_hash") == kernel_source_hash():
             traffic = ent.get("bytes_per_launch")
-    roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBS,
+    roofline = {"bound": "hbm", "kernel": dom, "kernel_symbol": KERNEL_OF_OP[dom],
+                "achieved": achieved, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                 "algorithmic_bytes": B[dom]}
 
@@ -237,18 +374,23 @@ def main():
         xsm = host["softmax"][:sample["softmax_rows"]]
         xlf = host["long_f"][:sample["long_rows"]]
         xli = host["long_i"][:sample["long_rows"]]
-        c0 = time.perf_counter()
-        oracle.reduce_rows(xs, "sum")
-        oracle.reduce_rows(xs, "max")
-        oracle.softmax_rows(xsm, "bf16")
-        oracle.reduce_rows(xlf, "sum")
-        oracle.reduce_rows(xli, "max")
-        oracle.splitk_lse_merge(o_s, m_s, l_s, 1.0, "bf16")
-        c_s = time.perf_counter() - c0
+        # one full step of the oracle, repeated until ~10 s of CPU time (at most 8 times)
+        reps, c_s = 0, 0.0
+        while reps < 8 and c_s < 10.0:
+            c0 = time.perf_counter()
+            oracle.reduce_rows(xs, "sum")
+            oracle.reduce_rows(xs, "max")
+            oracle.softmax_rows(xsm, "bf16")
+            oracle.reduce_rows(xlf, "sum")
+            oracle.reduce_rows(xli, "max")
+            oracle.splitk_lse_merge(o_s, m_s, l_s, 1.0, "bf16")
+            c_s += time.perf_counter() - c0
+            reps += 1
+        c_s /= reps
         nb = (2 * (xs.nbytes + 4 * xs.shape[0]) + 2 * xsm.nbytes + xlf.nbytes + 4 + xli.nbytes + 4
               + o_s.nbytes + m_s.nbytes + l_s.nbytes + o_s.shape[1] * 128 * 2)
         cpu = {"value": round(nb / c_s / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-               "seconds": round(c_s, 2),
+               "seconds_per_step": round(c_s, 3), "repetitions": reps,
                "sample": "one full step of the same workload (short_rows %d of 1048576 rows "
                          "sum+max, softmax %d of 8192 rows, long_rows %d of 16 rows f32 sum + "
                          "i32 max, lse_merge %d of 32768 rows); single-threaded C oracle"

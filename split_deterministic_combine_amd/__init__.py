@@ -108,6 +108,26 @@ def _stream_ptr(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+class _OnDevice:
+    """Make ``device`` current only when it is not already (the common case)."""
+
+    __slots__ = ("dev", "prev")
+
+    def __init__(self, device):
+        self.dev = device.index
+        self.prev = None
+
+    def __enter__(self):
+        cur = torch.cuda.current_device()
+        if cur != self.dev:
+            self.prev = cur
+            torch.cuda.set_device(self.dev)
+
+    def __exit__(self, *exc):
+        if self.prev is not None:
+            torch.cuda.set_device(self.prev)
+
+
 def _as_rows(x, name="x"):
     """View ``x`` as [rows, cols] with a row stride; the last axis must be contiguous."""
     if not isinstance(x, torch.Tensor) or not x.is_cuda:
@@ -133,6 +153,32 @@ def _dtype_code(t):
         raise TypeError("unsupported dtype %s" % t) from None
 
 
+_cu_counts = {}
+
+
+def _cu_count(device):
+    n = _cu_counts.get(device.index)
+    if n is None:
+        with _OnDevice(device):
+            n = device_cu_count()
+        _cu_counts[device.index] = n
+    return n
+
+
+_ws_need = {}
+
+
+def _workspace_need(rows, cols, ld, dt, op, tier, cu):
+    """Split-K workspace bytes of a shape (host-only plan, cached)."""
+    key = (rows, cols, ld, dt, op, tier, cu)
+    n = _ws_need.get(key)
+    if n is None:
+        plan = _Plan()
+        _check(_load().rr_plan_reduce(rows, cols, ld, dt, op, tier, cu, ctypes.byref(plan)))
+        n = _ws_need[key] = plan.workspace_bytes
+    return n
+
+
 # split-K workspaces, one per (device, stream); tickets reset themselves, so a
 # workspace stays zero between calls on its stream.
 _workspaces = {}
@@ -153,33 +199,29 @@ def reduce_rows(x, op="sum", tier="auto", out=None):
     ``op`` is "sum", "max" or "min"; ``x`` is float32 or int32 on the GPU.
     ``tier`` is "auto" or one of "wave", "block", "tiled", "serial", "splitk".
     """
-    lib = _load()
+    lib = _lib or _load()
     x2, rows, cols, ld = _as_rows(x)
     dt = _dtype_code(x.dtype)
-    lead = x.shape[:-1]
     if out is None:
-        out = torch.empty(lead, dtype=x.dtype, device=x.device)
+        out = torch.empty(x.shape[:-1], dtype=x.dtype, device=x.device)
     if out.dtype != x.dtype or out.numel() != rows or not out.is_contiguous():
         raise ValueError("out must be a contiguous %s tensor of %d elements" % (x.dtype, rows))
-    with torch.cuda.device(x.device):
+    o, t = OPS[op], TIERS[tier]
+    with _OnDevice(x.device):
         stream = _stream_ptr(x.device)
-        plan = _Plan()
-        cu = ctypes.c_int32(0)
-        _check(lib.rr_device_cu_count(ctypes.byref(cu)))
-        _check(lib.rr_plan_reduce(rows, cols, ld, dt, OPS[op], TIERS[tier], cu.value,
-                                  ctypes.byref(plan)))
+        need = _workspace_need(rows, cols, ld, dt, o, t, _cu_count(x.device))
         ws_ptr, ws_len = None, 0
-        if plan.workspace_bytes:
-            ws = _workspace(x.device, stream.value, plan.workspace_bytes)
+        if need:
+            ws = _workspace(x.device, stream.value, need)
             ws_ptr, ws_len = ctypes.c_void_p(ws.data_ptr()), ws.numel()
         _check(lib.rr_reduce_rows(ctypes.c_void_p(x2.data_ptr()), ctypes.c_void_p(out.data_ptr()),
-                                  rows, cols, ld, dt, OPS[op], TIERS[tier], ws_ptr, ws_len, stream))
+                                  rows, cols, ld, dt, o, t, ws_ptr, ws_len, stream))
     return out
 
 
 def softmax_rows(x, out_dtype=None, tier="auto", out=None):
     """Softmax of every row of ``x`` over its last axis (x: bfloat16 or float32)."""
-    lib = _load()
+    lib = _lib or _load()
     x2, rows, cols, ld_x = _as_rows(x)
     out_dtype = x.dtype if out_dtype is None else out_dtype
     if out is None:
@@ -187,7 +229,7 @@ def softmax_rows(x, out_dtype=None, tier="auto", out=None):
     if out.dtype != out_dtype or out.shape != x.shape:
         raise ValueError("out must be a %s tensor of shape %s" % (out_dtype, tuple(x.shape)))
     y2, _, _, ld_y = _as_rows(out, "out")
-    with torch.cuda.device(x.device):
+    with _OnDevice(x.device):
         _check(lib.rr_softmax_rows(ctypes.c_void_p(x2.data_ptr()), ctypes.c_void_p(y2.data_ptr()),
                                    rows, cols, ld_x, ld_y, _dtype_code(x.dtype),
                                    _dtype_code(out_dtype), TIERS[tier], _stream_ptr(x.device)))
@@ -216,7 +258,7 @@ def splitk_lse_merge(o_part, m_part, l_part, scale=1.0, out_dtype=torch.bfloat16
         out = torch.empty((*rows_shape, depth), dtype=out_dtype, device=o_part.device)
     if out.dtype != out_dtype or not out.is_contiguous() or out.numel() != rows * depth:
         raise ValueError("out must be a contiguous %s tensor of %d elements" % (out_dtype, rows * depth))
-    with torch.cuda.device(o_part.device):
+    with _OnDevice(o_part.device):
         _check(lib.rr_splitk_lse_merge(ctypes.c_void_p(o_part.data_ptr()),
                                        ctypes.c_void_p(m_part.data_ptr()),
                                        ctypes.c_void_p(l_part.data_ptr()),
@@ -271,7 +313,7 @@ def workspace_bytes(rows, cols, dtype=torch.float32, op="sum", tier="auto"):
 def workspace_reset(ws):
     """Zero a workspace tensor on the current stream (fill kernel, no memset)."""
     lib = _load()
-    with torch.cuda.device(ws.device):
+    with _OnDevice(ws.device):
         _check(lib.rr_workspace_reset(ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
                                       _stream_ptr(ws.device)))
 
