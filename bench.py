@@ -47,7 +47,7 @@ def kernel_source_hash():
 KERNEL_OF_OP = {
     "short_sum": "k_reduce_wave<rr::SumF32, 4, 16>",
     "short_max": "k_reduce_wave<rr::MaxF32, 4, 16>",
-    "softmax": "k_softmax_rows_pf<unsigned short, unsigned short, 4, 256>",
+    "softmax": "k_softmax_rows_pf<unsigned short, unsigned short, 4, 256, true>",
     "long_sum": "k_reduce_splitk<rr::SumF32, 4>",
     "long_max": "k_reduce_splitk<rr::MaxI32, 4>",
     "merge": "k_lse_merge<unsigned short, 4, 32>",

@@ -173,6 +173,17 @@ struct SoftmaxMS {
     }
 };
 
+// Plain float max / sum monoids for the cheap wave-level steps of the
+// softmax statistics (both are commutative bit for bit).
+struct MaxFloat {
+    using acc_t = float;
+    __device__ static acc_t combine(acc_t a, acc_t b) { return fmaxf(a, b); }
+};
+struct SumFloat {
+    using acc_t = float;
+    __device__ static acc_t combine(acc_t a, acc_t b) { return a + b; }
+};
+
 // ----------------------------------------------------- wavefront combines
 
 // Combine within aligned groups of S lanes (S in {1, 2, 4, 8, 16}); every

@@ -162,6 +162,34 @@ __device__ __forceinline__ MS local_exp_sum(float* v)
     return MS{m, s};
 }
 
+// Row statistics (M, S) over the workgroup from each thread's (m_t, s_t),
+// identical bits in every thread, and the thread's own factor
+// e_t = exp(m_t - M).  Inside a wavefront only the cheap monoids run: a max
+// of m_t, one exponential per lane to bring s_t to the wavefront max, and a
+// sum; the per-wavefront pairs are then folded in wave order with the online
+// (max, sum) combine.  Fixed shapes throughout, so the bits do not change
+// from run to run.
+template <int NT>
+__device__ __forceinline__ MS block_softmax_stats(MS own, MS* slot, float* e_t)
+{
+    constexpr int NW = NT / kWave;
+    const float mw = wave_reduce<MaxFloat>(own.m);
+    const float ew = mw == kNegInf ? 0.0f : exp2_hw((own.m - mw) * kLog2e);
+    const float sw = wave_reduce<SumFloat>(own.s * ew);
+    MS tot = MS{mw, sw};
+    if constexpr (NW > 1) {
+        if (lane_id() == 0)
+            slot[threadIdx.x / kWave] = tot;
+        __syncthreads();
+        tot = slot[0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w)
+            tot = SoftmaxMS::combine(tot, slot[w]);
+    }
+    *e_t = exp2_f32((own.m - tot.m) * kLog2e);
+    return tot;
+}
+
 // ------------------------------------------- block tier, row in registers
 template <class XT, class YT, int NCH, bool VEC, int NT>
 __global__ __launch_bounds__(NT) void k_softmax_block(const XT* __restrict__ x,
@@ -180,9 +208,10 @@ __global__ __launch_bounds__(NT) void k_softmax_block(const XT* __restrict__ x,
             load_padded<XT, E, VEC>(xr, ((int64_t)threadIdx.x + (int64_t)k * NT) * E, cols,
                                     v + k * E);
         const MS own = local_exp_sum<NCH * E>(v);
-        const MS tot = block_reduce<SoftmaxMS, NT>(own, slot[par]);
+        float e_t;
+        const MS tot = block_softmax_stats<NT>(own, slot[par], &e_t);
         par ^= 1;
-        const float sc = exp2_f32((own.m - tot.m) * kLog2e) / tot.s;
+        const float sc = e_t / tot.s;
 #pragma unroll
         for (int i = 0; i < NCH * E; ++i)
             v[i] *= sc;
@@ -214,7 +243,9 @@ __device__ __forceinline__ void unpack_chunk(uint4 u, float* v)
     }
 }
 
-template <class XT, class YT, int NCH, int NT>
+// EXACT: cols == NT * NCH * chunk, so every chunk of every thread is in the
+// row and no per-chunk bound check is emitted.
+template <class XT, class YT, int NCH, int NT, bool EXACT>
 __device__ __forceinline__ void softmax_row_from_chunks(const uint4* raw, YT* yr, int64_t cols,
                                                         MS* slot)
 {
@@ -223,7 +254,7 @@ __device__ __forceinline__ void softmax_row_from_chunks(const uint4* raw, YT* yr
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
         const int64_t j0 = ((int64_t)threadIdx.x + (int64_t)k * NT) * E;
-        if (j0 < cols) {
+        if (EXACT || j0 < cols) {
             unpack_chunk<XT>(raw[k], v + k * E);
         } else {
 #pragma unroll
@@ -232,32 +263,34 @@ __device__ __forceinline__ void softmax_row_from_chunks(const uint4* raw, YT* yr
         }
     }
     const MS own = local_exp_sum<NCH * E>(v);
-    const MS tot = block_reduce<SoftmaxMS, NT>(own, slot);
-    const float sc = exp2_f32((own.m - tot.m) * kLog2e) / tot.s;
+    float e_t;
+    const MS tot = block_softmax_stats<NT>(own, slot, &e_t);
+    const float sc = e_t / tot.s;
 #pragma unroll
     for (int i = 0; i < NCH * E; ++i)
         v[i] *= sc;
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
         const int64_t j0 = ((int64_t)threadIdx.x + (int64_t)k * NT) * E;
-        if (j0 < cols)
+        if (EXACT || j0 < cols)
             YOut<YT>::template chunk<E>(yr + j0, v + k * E);
     }
 }
 
-template <class XT, int NCH, int NT>
+template <class XT, int NCH, int NT, bool EXACT>
 __device__ __forceinline__ void load_row_chunks(const XT* xr, int64_t cols, uint4* raw)
 {
     constexpr int E = XIn<XT>::kChunk;
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
         int64_t j0 = ((int64_t)threadIdx.x + (int64_t)k * NT) * E;
-        j0 = j0 < cols ? j0 : 0;  // chunks past the row end read chunk 0 (ignored)
+        if (!EXACT)
+            j0 = j0 < cols ? j0 : 0;  // chunks past the row end read chunk 0 (ignored)
         raw[k] = load16_nt(xr + j0);
     }
 }
 
-template <class XT, class YT, int NCH, int NT>
+template <class XT, class YT, int NCH, int NT, bool EXACT>
 __global__ __launch_bounds__(NT) void k_softmax_rows_pf(const XT* __restrict__ x,
                                                         YT* __restrict__ y, int64_t rows,
                                                         int64_t cols, int64_t ldx, int64_t ldy)
@@ -268,17 +301,17 @@ __global__ __launch_bounds__(NT) void k_softmax_rows_pf(const XT* __restrict__ x
         return;
     const int64_t step = gridDim.x;
     uint4 a[NCH], b[NCH];
-    load_row_chunks<XT, NCH, NT>(x + r * ldx, cols, a);
+    load_row_chunks<XT, NCH, NT, EXACT>(x + r * ldx, cols, a);
     for (;;) {
         const bool more = r + step < rows;
-        load_row_chunks<XT, NCH, NT>(x + (more ? r + step : r) * ldx, cols, b);
-        softmax_row_from_chunks<XT, YT, NCH, NT>(a, y + r * ldy, cols, slot[0]);
+        load_row_chunks<XT, NCH, NT, EXACT>(x + (more ? r + step : r) * ldx, cols, b);
+        softmax_row_from_chunks<XT, YT, NCH, NT, EXACT>(a, y + r * ldy, cols, slot[0]);
         if (!more)
             break;
         r += step;
         const bool more2 = r + step < rows;
-        load_row_chunks<XT, NCH, NT>(x + (more2 ? r + step : r) * ldx, cols, a);
-        softmax_row_from_chunks<XT, YT, NCH, NT>(b, y + r * ldy, cols, slot[1]);
+        load_row_chunks<XT, NCH, NT, EXACT>(x + (more2 ? r + step : r) * ldx, cols, a);
+        softmax_row_from_chunks<XT, YT, NCH, NT, EXACT>(b, y + r * ldy, cols, slot[1]);
         if (!more2)
             break;
         r += step;
@@ -413,6 +446,17 @@ __global__ __launch_bounds__(kBlockThreads) void k_softmax_tiled(const XT* __res
 }
 
 // ---------------------------------------------------------------- launch
+template <class XT, class YT, int NCH, int NT>
+static rr_status launch_pf(dim3 grid, hipStream_t s, const XT* x, YT* y, const SoftmaxLaunch& a)
+{
+    constexpr int64_t kExactCols = (int64_t)NT * NCH * XIn<XT>::kChunk;
+    if (a.cols == kExactCols)
+        return launch_kernel(k_softmax_rows_pf<XT, YT, NCH, NT, true>, grid, dim3(NT), 0, s, x, y,
+                             a.rows, a.cols, a.ld_x, a.ld_y);
+    return launch_kernel(k_softmax_rows_pf<XT, YT, NCH, NT, false>, grid, dim3(NT), 0, s, x, y,
+                         a.rows, a.cols, a.ld_x, a.ld_y);
+}
+
 // Block tier: the row stays in registers when each of the NT threads holds
 // at most kSoftmaxMaxChunks chunks; longer rows stream twice.
 template <class XT, class YT, bool VEC, int NT>
@@ -429,12 +473,12 @@ static rr_status launch_block(const rr_plan& p, const SoftmaxLaunch& a)
             // persistent rows with prefetch; the plan sized the grid
             const dim3 pg((unsigned)p.grid);
             if (nch <= 1)
-                return launch_kernel(k_softmax_rows_pf<XT, YT, 1, NT>, pg, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
+                return launch_pf<XT, YT, 1, NT>(pg, s, x, y, a);
             if (nch <= 2)
-                return launch_kernel(k_softmax_rows_pf<XT, YT, 2, NT>, pg, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
+                return launch_pf<XT, YT, 2, NT>(pg, s, x, y, a);
             if (nch <= 4)
-                return launch_kernel(k_softmax_rows_pf<XT, YT, 4, NT>, pg, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
-            return launch_kernel(k_softmax_rows_pf<XT, YT, kSoftmaxMaxChunks, NT>, pg, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
+                return launch_pf<XT, YT, 4, NT>(pg, s, x, y, a);
+            return launch_pf<XT, YT, kSoftmaxMaxChunks, NT>(pg, s, x, y, a);
         }
     }
     if (nch <= 1)
