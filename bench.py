@@ -50,7 +50,7 @@ KERNEL_OF_OP = {
     "softmax": "k_softmax_rows_pf<unsigned short, unsigned short, 4, 256, true>",
     "long_sum": "k_reduce_splitk<rr::SumF32, 4>",
     "long_max": "k_reduce_splitk<rr::MaxI32, 4>",
-    "merge": "k_lse_merge<unsigned short, 4, 32>",
+    "merge": "k_lse_merge_po<unsigned short, 32, 4>",
 }
 ALGO_BYTES = {
     "short_sum": 1048576 * 48 * 4 + 1048576 * 4,

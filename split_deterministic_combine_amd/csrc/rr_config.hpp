@@ -47,6 +47,10 @@ constexpr int64_t kSoftmaxWideMinChunks = (int64_t)kBlockThreads * kSoftmaxMaxCh
 // LSE merge: partitions staged per batch of loads, and workgroup size.
 constexpr int kMergeBatch = 8;
 constexpr int kMergeMaxP = 256;
+// Partition-outer merge (one 128-bit chunk per lane): rows per lane and the
+// largest partition count it takes (its LDS holds 16 B per row and partition).
+constexpr int kMergePOuterRowsPerLane = 4;
+constexpr int kMergePOuterMaxP = 32;
 
 // Largest grid.x the launchers use; kernels loop over the remainder.
 constexpr int64_t kMaxGrid = 1 << 30;

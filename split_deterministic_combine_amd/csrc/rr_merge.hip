@@ -203,6 +203,178 @@ __global__ __launch_bounds__(kBlockThreads) void k_lse_merge(const float* __rest
     }
 }
 
+// ------------------------------------------- partition-outer fast path
+// depth == LPR * 4 (one 128-bit chunk per lane per row), P <= kMergePOuterMaxP.
+// A workgroup takes RW = (256 / LPR) * K rows; lane group q owns rows
+// q, q + 256/LPR, ... (K of them).  After the weight phases it walks the
+// partitions in ascending order and, for each, reads that partition's chunk
+// of its K rows -- so the workgroup reads K * 4 KiB (LPR = 32) of one
+// partition at a time instead of one row of all partitions -- with the next
+// partition's loads in flight (two alternating buffers, clamped look-ahead).
+// Per output element the arithmetic and its order are those of k_lse_merge.
+template <int K>
+struct Chunks {
+    OChunk<4> c[K];
+};
+
+template <int LPR, int K>
+__device__ __forceinline__ void po_load(const float* __restrict__ o, int64_t rows, int32_t depth,
+                                        int32_t p, const int64_t* rk, Chunks<K>& dst)
+{
+    const int64_t d = (int64_t)(threadIdx.x % LPR) * 4;
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+        dst.c[k] = load_o<4>(o + ((int64_t)p * rows + rk[k]) * depth + d);
+}
+
+template <int K>
+__device__ __forceinline__ void po_fold(double (*acc)[4], const Chunks<K>& ch, const double* cell,
+                                        const int* qk, int32_t P, int32_t p)
+{
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const double cp = cell[qk[k] * P + p];
+        if (cp >= 0.0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                acc[k][e] = fma(cp, (double)ch.c[k].v[e], acc[k][e]);
+        }
+    }
+}
+
+template <class YT, int LPR, int K>
+__global__ __launch_bounds__(kBlockThreads) void k_lse_merge_po(const float* __restrict__ o,
+                                                                const float* __restrict__ m,
+                                                                const float* __restrict__ l,
+                                                                YT* __restrict__ out, int32_t P,
+                                                                int64_t rows, int32_t depth,
+                                                                float scale)
+{
+    constexpr int GR = kBlockThreads / LPR;  // rows per lane-group pass
+    constexpr int RW = GR * K;                // rows per workgroup
+    extern __shared__ double lds[];
+    const int32_t npairs = RW * P;
+    double* wd = lds;                                  // [npairs]
+    double* cell = lds + npairs;                       // [max(npairs, block)]
+    float2* stat = reinterpret_cast<float2*>(cell);
+    const int q = threadIdx.x / LPR;
+    const int64_t nblocks = ceil_div(rows, RW);
+
+    for (int64_t blk = blockIdx.x; blk < nblocks; blk += gridDim.x) {
+        const int64_t row_base = blk * RW;
+        int qk[K];
+        int64_t rk[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            qk[k] = q + GR * k;
+            const int64_t r = row_base + qk[k];
+            rk[k] = r < rows ? r : rows - 1;
+        }
+        // statistics of this thread's first pair, then partition 0's chunks
+        const int32_t i0 = (int32_t)threadIdx.x < npairs ? (int32_t)threadIdx.x : npairs - 1;
+        const int32_t q0 = i0 / P, p0i = i0 - q0 * P;
+        const int64_t r0 = row_base + q0 < rows ? row_base + q0 : rows - 1;
+        const float m0 = m[(int64_t)p0i * rows + r0];
+        const float l0 = l[(int64_t)p0i * rows + r0];
+        __builtin_amdgcn_sched_barrier(0);
+        Chunks<K> A, B;
+        po_load<LPR, K>(o, rows, depth, 0, rk, A);
+        const bool st0_ok = (int32_t)threadIdx.x < npairs && row_base + q0 < rows;
+
+        // Phase 1: stage (m_p, l_p) (cells past npairs are never read).
+        stat[threadIdx.x] = make_float2(st0_ok ? m0 : -__builtin_inff(), st0_ok ? l0 : 0.0f);
+        for (int32_t i = threadIdx.x + kBlockThreads; i < npairs; i += kBlockThreads) {
+            const int32_t qq = i / P, p = i - qq * P;
+            float2 st = make_float2(-__builtin_inff(), 0.0f);
+            if (row_base + qq < rows)
+                st = make_float2(m[(int64_t)p * rows + row_base + qq],
+                                 l[(int64_t)p * rows + row_base + qq]);
+            stat[i] = st;
+        }
+        __syncthreads();
+        // Phase 2: M over the non-empty partitions of the row, then w_p.
+        for (int32_t i = threadIdx.x; i < npairs; i += kBlockThreads) {
+            const int32_t qq = i / P;
+            const float2* rs = stat + (int64_t)qq * P;
+            bool any = false;
+            double M = 0.0;
+            for (int32_t pp = 0; pp < P; ++pp) {
+                const float2 st = rs[pp];
+                if (st.y > 0.0f && st.x > -__builtin_inff()) {
+                    if (!any || (double)st.x > M)
+                        M = (double)st.x;
+                    any = true;
+                }
+            }
+            const float2 st = stat[i];
+            const bool live = st.y > 0.0f && st.x > -__builtin_inff();
+            wd[i] = live ? exp((double)scale * ((double)st.x - M)) * (double)st.y : 0.0;
+        }
+        __syncthreads();
+        // Phase 3: W in ascending partition order, then c_p (or -1 if empty).
+        for (int32_t i = threadIdx.x; i < npairs; i += kBlockThreads) {
+            const int32_t qq = i / P;
+            const double* wrow = wd + (int64_t)qq * P;
+            double W = 0.0;
+            for (int32_t pp = 0; pp < P; ++pp)
+                W += wrow[pp];
+            const float2 st = stat[i];
+            const bool live = st.y > 0.0f && st.x > -__builtin_inff();
+            cell[i] = live ? wd[i] / W : -1.0;
+        }
+        __syncthreads();
+
+        // Accumulate partition by partition, ascending p.
+        double acc[K][4];
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                acc[k][e] = 0.0;
+        for (int32_t p = 0;;) {
+            const int32_t pn = p + 1 < P ? p + 1 : p;
+            po_load<LPR, K>(o, rows, depth, pn, rk, B);
+            po_fold<K>(acc, A, cell, qk, P, p);
+            if (++p >= P)
+                break;
+            const int32_t pn2 = p + 1 < P ? p + 1 : p;
+            po_load<LPR, K>(o, rows, depth, pn2, rk, A);
+            po_fold<K>(acc, B, cell, qk, P, p);
+            if (++p >= P)
+                break;
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            if (row_base + qk[k] < rows)
+                MergeOut<YT>::four(out + (row_base + qk[k]) * depth +
+                                       (int64_t)(threadIdx.x % LPR) * 4, acc[k]);
+        __syncthreads();  // LDS is reused by the next row block
+    }
+}
+
+// The partition-outer path holds 16 bytes of LDS per (row, partition) of a
+// workgroup; it is taken when that fits in 32 KiB.
+template <int LPR>
+static bool po_fits(int32_t P)
+{
+    constexpr int RW = (kBlockThreads / LPR) * kMergePOuterRowsPerLane;
+    return (int64_t)RW * P * 16 <= 32768;
+}
+
+template <class YT, int LPR>
+static rr_status launch_po(const MergeLaunch& a)
+{
+    constexpr int K = kMergePOuterRowsPerLane;
+    constexpr int RW = (kBlockThreads / LPR) * K;
+    int64_t grid = ceil_div(a.rows, RW);
+    if (grid > kMaxGrid) grid = kMaxGrid;
+    const int64_t npairs = (int64_t)RW * a.P;
+    const size_t lds = (size_t)8 * npairs + (size_t)8 * (npairs > kBlockThreads ? npairs : kBlockThreads);
+    return launch_kernel(k_lse_merge_po<YT, LPR, K>, dim3((unsigned)grid), dim3(kBlockThreads), lds,
+                         a.stream, a.o, a.m, a.l, static_cast<YT*>(a.out), a.P, a.rows, a.depth,
+                         a.scale);
+}
+
 static int lanes_per_row(int32_t depth, int ve)
 {
     const int64_t chunks = ceil_div(depth, ve);
@@ -232,6 +404,18 @@ static rr_status launch_lpr(const MergeLaunch& a)
 template <class YT, int VE>
 static rr_status launch_ve(const MergeLaunch& a)
 {
+    if constexpr (VE == 4) {
+        if (a.P <= kMergePOuterMaxP) {
+            switch (a.depth) {  // one 128-bit chunk per lane
+            case 16: if (po_fits<4>(a.P)) return launch_po<YT, 4>(a); break;
+            case 32: if (po_fits<8>(a.P)) return launch_po<YT, 8>(a); break;
+            case 64: if (po_fits<16>(a.P)) return launch_po<YT, 16>(a); break;
+            case 128: if (po_fits<32>(a.P)) return launch_po<YT, 32>(a); break;
+            case 256: if (po_fits<64>(a.P)) return launch_po<YT, 64>(a); break;
+            default: break;
+            }
+        }
+    }
     switch (lanes_per_row(a.depth, VE)) {
     case 4: return launch_lpr<YT, VE, 4>(a);
     case 8: return launch_lpr<YT, VE, 8>(a);
