@@ -399,3 +399,19 @@ def test_merge_bit_identical_across_runs():
     first = rr.splitk_lse_merge(go, gm, gl).clone()
     for _ in range(4):
         assert torch.equal(rr.splitk_lse_merge(go, gm, gl).view(torch.int16), first.view(torch.int16))
+
+
+# ------------------------------------------------------------- large sizes
+
+def test_reduce_beyond_32bit_element_offsets():
+    # The second row starts 2^30 + 3 elements (> 4 GiB) into the buffer, so any
+    # 32-bit element or byte offset in a kernel would read the wrong data.
+    rows, cols = 2, (1 << 30) + 3
+    x = synth.ints_i32(77, (rows, cols), -1000, 1000)
+    g = to_gpu(x)
+    for op in ("sum", "max"):
+        ref = oracle.reduce_rows(x, op)
+        for tier in ("auto", "block"):
+            assert_exact(to_host(rr.reduce_rows(g, op, tier)), ref, "large %s %s" % (op, tier))
+    del g
+    torch.cuda.empty_cache()
