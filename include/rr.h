@@ -121,8 +121,10 @@ rr_status rr_plan_reduce(int64_t rows, int64_t cols, int64_t ld, rr_dtype dtype,
                          rr_tier tier, int32_t cu_count, rr_plan* plan_out);
 
 /*
- * rr_plan_softmax -- tier selection for rr_softmax_rows (same rule as reduce
- * without SPLITK, which is rejected with RR_ERR_TIER).
+ * rr_plan_softmax -- tier selection for rr_softmax_rows: the reduce rule
+ * (SPLITK when rows < cu_count and cols >= 65536, then TILED / WAVE /
+ * BLOCK).  SPLITK uses tiles of 4 * 256 * 16-byte chunks and needs the
+ * workspace reported in workspace_bytes.
  */
 rr_status rr_plan_softmax(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype y_dtype,
                           rr_tier tier, int32_t cu_count, rr_plan* plan_out);
@@ -166,14 +168,24 @@ rr_status rr_reduce_rows(const void* x, void* y, int64_t rows, int64_t cols, int
  *
  *   x        device, [rows][ld_x] of x_dtype (RR_BF16 or RR_F32)
  *   y        device, [rows][ld_y] of y_dtype (RR_BF16 or RR_F32)
- *   tier     RR_TIER_AUTO, WAVE, BLOCK, TILED or SERIAL
+ *   tier     RR_TIER_AUTO, WAVE, BLOCK, TILED, SERIAL or SPLITK
+ *   workspace, workspace_bytes
+ *            device scratch for RR_TIER_SPLITK, as for rr_reduce_rows (size:
+ *            rr_workspace_bytes with RR_KIND_SOFTMAX; tickets zero before
+ *            first use, left zero by every completed call).  Ignored by the
+ *            other tiers (may be NULL).
+ * Split-K ("reduce", tier semantics: several blocks per row; and
+ * "cluster_allreduce", description: the groups' values folded in rank
+ * order) runs two launches: G workgroups per row fold (max, sum) over their
+ * tiles, the last to arrive folds the G pairs in ascending rank into the
+ * row's (M, S); then a map pass writes y.
  * Arithmetic in float32; bf16 results are rounded to nearest even.  y may
  * alias x only when ld_y == ld_x and the dtypes match.  cols == 0 or
  * rows == 0 is a no-op.
  */
 rr_status rr_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols, int64_t ld_x,
                           int64_t ld_y, rr_dtype x_dtype, rr_dtype y_dtype, rr_tier tier,
-                          void* stream);
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * rr_splitk_lse_merge -- combine P split-K partitions of an attention output.
@@ -201,8 +213,9 @@ rr_status rr_splitk_lse_merge(const float* o_part, const float* m_part, const fl
                               void* out, int32_t P, int64_t rows, int32_t depth, float scale,
                               rr_dtype out_dtype, void* stream);
 
-/* Bytes of workspace rr_reduce_rows needs for this shape on the current
- * device (0 unless the plan is split-K).  kind must be RR_KIND_REDUCE. */
+/* Bytes of workspace rr_reduce_rows (RR_KIND_REDUCE) or rr_softmax_rows
+ * (RR_KIND_SOFTMAX, dtype = x_dtype) needs for this shape on the current
+ * device (0 unless the plan is split-K). */
 rr_status rr_workspace_bytes(rr_kind kind, int64_t rows, int64_t cols, rr_dtype dtype,
                              rr_op op, rr_tier tier, size_t* bytes_out);
 

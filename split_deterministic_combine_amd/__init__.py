@@ -73,7 +73,8 @@ def _load():
         lib = ctypes.CDLL(_LIB_PATH)
         vp, i64, i32, st = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int
         lib.rr_reduce_rows.argtypes = [vp, vp, i64, i64, i64, st, st, st, vp, ctypes.c_size_t, vp]
-        lib.rr_softmax_rows.argtypes = [vp, vp, i64, i64, i64, i64, st, st, st, vp]
+        lib.rr_softmax_rows.argtypes = [vp, vp, i64, i64, i64, i64, st, st, st, vp,
+                                        ctypes.c_size_t, vp]
         lib.rr_splitk_lse_merge.argtypes = [vp, vp, vp, vp, i32, i64, i32, ctypes.c_float, st, vp]
         lib.rr_plan_reduce.argtypes = [i64, i64, i64, st, st, st, i32, ctypes.POINTER(_Plan)]
         lib.rr_plan_softmax.argtypes = [i64, i64, st, st, st, i32, ctypes.POINTER(_Plan)]
@@ -169,12 +170,23 @@ _ws_need = {}
 
 
 def _workspace_need(rows, cols, ld, dt, op, tier, cu):
-    """Split-K workspace bytes of a shape (host-only plan, cached)."""
-    key = (rows, cols, ld, dt, op, tier, cu)
+    """Split-K workspace bytes of a reduction (host-only plan, cached)."""
+    key = ("reduce", rows, cols, ld, dt, op, tier, cu)
     n = _ws_need.get(key)
     if n is None:
         plan = _Plan()
         _check(_load().rr_plan_reduce(rows, cols, ld, dt, op, tier, cu, ctypes.byref(plan)))
+        n = _ws_need[key] = plan.workspace_bytes
+    return n
+
+
+def _softmax_workspace_need(rows, cols, xdt, ydt, tier, cu):
+    """Split-K workspace bytes of a softmax (host-only plan, cached)."""
+    key = ("softmax", rows, cols, xdt, ydt, tier, cu)
+    n = _ws_need.get(key)
+    if n is None:
+        plan = _Plan()
+        _check(_load().rr_plan_softmax(rows, cols, xdt, ydt, tier, cu, ctypes.byref(plan)))
         n = _ws_need[key] = plan.workspace_bytes
     return n
 
@@ -229,10 +241,16 @@ def softmax_rows(x, out_dtype=None, tier="auto", out=None):
     if out.dtype != out_dtype or out.shape != x.shape:
         raise ValueError("out must be a %s tensor of shape %s" % (out_dtype, tuple(x.shape)))
     y2, _, _, ld_y = _as_rows(out, "out")
+    xdt, ydt, t = _dtype_code(x.dtype), _dtype_code(out_dtype), TIERS[tier]
     with _OnDevice(x.device):
+        stream = _stream_ptr(x.device)
+        need = _softmax_workspace_need(rows, cols, xdt, ydt, t, _cu_count(x.device))
+        ws_ptr, ws_len = None, 0
+        if need:
+            ws = _workspace(x.device, stream.value, need)
+            ws_ptr, ws_len = ctypes.c_void_p(ws.data_ptr()), ws.numel()
         _check(lib.rr_softmax_rows(ctypes.c_void_p(x2.data_ptr()), ctypes.c_void_p(y2.data_ptr()),
-                                   rows, cols, ld_x, ld_y, _dtype_code(x.dtype),
-                                   _dtype_code(out_dtype), TIERS[tier], _stream_ptr(x.device)))
+                                   rows, cols, ld_x, ld_y, xdt, ydt, t, ws_ptr, ws_len, stream))
     return out
 
 

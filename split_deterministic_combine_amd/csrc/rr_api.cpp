@@ -86,7 +86,8 @@ extern "C" rr_status rr_reduce_rows(const void* x, void* y, int64_t rows, int64_
 
 extern "C" rr_status rr_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols,
                                      int64_t ld_x, int64_t ld_y, rr_dtype x_dtype,
-                                     rr_dtype y_dtype, rr_tier tier, void* stream)
+                                     rr_dtype y_dtype, rr_tier tier, void* workspace,
+                                     size_t workspace_bytes, void* stream)
 {
     rr_plan p;
     rr_status st = rr::plan_softmax(rows, cols, x_dtype, y_dtype, tier, 1, true, &p);
@@ -101,7 +102,12 @@ extern "C" rr_status rr_softmax_rows(const void* x, void* y, int64_t rows, int64
                      rows_aligned16(y, ld_y, rows, elem_size(y_dtype));
     if ((st = rr::plan_softmax(rows, cols, x_dtype, y_dtype, tier, cu, vec, &p)) != RR_OK)
         return st;
-    rr::SoftmaxLaunch a{x, y, rows, cols, ld_x, ld_y, x_dtype, y_dtype, vec, as_stream(stream)};
+    if (p.tier == RR_TIER_SPLITK) {
+        if (!workspace || workspace_bytes < p.workspace_bytes || !aligned(workspace, 8))
+            return RR_ERR_WORKSPACE;
+    }
+    rr::SoftmaxLaunch a{x, y, rows, cols, ld_x, ld_y, x_dtype, y_dtype, vec, workspace,
+                        g_splitk_skew.load(std::memory_order_relaxed), as_stream(stream)};
     return rr::launch_softmax(p, a);
 }
 
@@ -125,16 +131,16 @@ extern "C" rr_status rr_workspace_bytes(rr_kind kind, int64_t rows, int64_t cols
                                         rr_op op, rr_tier tier, size_t* bytes_out)
 {
     if (!bytes_out) return RR_ERR_NULL;
-    if (kind == RR_KIND_SOFTMAX) {
-        *bytes_out = 0;
-        return RR_OK;
-    }
-    if (kind != RR_KIND_REDUCE) return RR_ERR_TIER;
+    if (kind != RR_KIND_REDUCE && kind != RR_KIND_SOFTMAX) return RR_ERR_TIER;
     int32_t cu = 0;
     rr_status st = current_cu(&cu);
     if (st != RR_OK) return st;
     rr_plan p;
-    if ((st = rr::plan_reduce(rows, cols, cols, dtype, op, tier, cu, true, &p)) != RR_OK) return st;
+    if (kind == RR_KIND_REDUCE)
+        st = rr::plan_reduce(rows, cols, cols, dtype, op, tier, cu, true, &p);
+    else
+        st = rr::plan_softmax(rows, cols, dtype, dtype, tier, cu, true, &p);
+    if (st != RR_OK) return st;
     *bytes_out = (size_t)p.workspace_bytes;
     return RR_OK;
 }

@@ -44,6 +44,10 @@ constexpr int kSoftmaxWideThreads = 512;
 constexpr int kSoftmaxRowBlocksPerCU = 2;
 constexpr int64_t kSoftmaxWideMinChunks = (int64_t)kBlockThreads * kSoftmaxMaxChunks;
 
+// Split-K softmax: 16-byte chunks per thread per tile (a tile is one load
+// round of the workgroup).
+constexpr int kSoftmaxSplitKUnroll = 4;
+
 // LSE merge: partitions staged per batch of loads, and workgroup size.
 constexpr int kMergeBatch = 8;
 constexpr int kMergeMaxP = 256;

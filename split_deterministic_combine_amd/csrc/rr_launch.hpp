@@ -26,6 +26,8 @@ struct SoftmaxLaunch {
     int64_t rows, cols, ld_x, ld_y;
     rr_dtype x_dtype, y_dtype;
     bool vec;
+    void* workspace;      // split-K only
+    int32_t skew;         // split-K arrival-order test hook (0 = off)
     hipStream_t stream;
 };
 

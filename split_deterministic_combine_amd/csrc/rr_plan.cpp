@@ -18,6 +18,33 @@ uint64_t splitk_workspace_bytes(int64_t rows, int32_t slices)
     return (uint64_t)(round_up(rows * 4, kWorkspaceAlign) + rows * (int64_t)slices * 8);
 }
 
+uint64_t softmax_splitk_workspace_bytes(int64_t rows, int32_t slices)
+{
+    // tickets, then one (m, s) pair per (row, workgroup), then one per row
+    return splitk_workspace_bytes(rows, slices) + (uint64_t)rows * 8;
+}
+
+// Split-K geometry shared by the reduce and softmax tiers: G workgroups per
+// row; the row is cut into tiles of one load round of a workgroup, dealt to
+// the G workgroups in turn.
+static void fill_splitk_geometry(int64_t rows, int64_t cols, int64_t tile, int32_t cu_count,
+                                 rr_plan* out)
+{
+    const int64_t ntiles = ceil_div(cols > 0 ? cols : 1, tile);
+    int64_t g = ceil_div((int64_t)kSplitKBlocksPerCU * cu_count, rows > 0 ? rows : 1);
+    int64_t g_cap = ceil_div(cols, kSplitKMinColsPerGroup);
+    if (g_cap > kSplitKMaxSlices) g_cap = kSplitKMaxSlices;
+    if (g_cap > ntiles) g_cap = ntiles;  // every workgroup gets at least one tile
+    if (g > g_cap) g = g_cap;
+    if (g < 1) g = 1;
+    out->tier = RR_TIER_SPLITK;
+    out->block = kBlockThreads;
+    out->lanes_per_row = 0;
+    out->slices = (int32_t)g;
+    out->tile_cols = tile;
+    out->grid = rows * g;
+}
+
 static rr_tier auto_tier_reduce(int64_t rows, int64_t cols, int32_t cu)
 {
     if (rows < cu && cols >= kSplitKMinCols) return RR_TIER_SPLITK;
@@ -75,25 +102,19 @@ rr_status plan_reduce(int64_t rows, int64_t cols, int64_t ld, rr_dtype dtype, rr
         fill_rowwise_geometry(t, rows, cols, vec_elems, out);
         return RR_OK;
     }
-    // Split-K: G workgroups per row; the row is cut into tiles of one
-    // unrolled load round of a workgroup, dealt to the G workgroups in turn.
-    const int64_t tile = (int64_t)kSplitKUnroll * kBlockThreads * vec_elems;
-    const int64_t ntiles = ceil_div(cols > 0 ? cols : 1, tile);
-    int64_t g = ceil_div((int64_t)kSplitKBlocksPerCU * cu_count, rows > 0 ? rows : 1);
-    int64_t g_cap = ceil_div(cols, kSplitKMinColsPerGroup);
-    if (g_cap > kSplitKMaxSlices) g_cap = kSplitKMaxSlices;
-    if (g_cap > ntiles) g_cap = ntiles;  // every workgroup gets at least one tile
-    if (g > g_cap) g = g_cap;
-    if (g < 1) g = 1;
-    out->tier = RR_TIER_SPLITK;
-    out->block = kBlockThreads;
-    out->lanes_per_row = 0;
-    out->slices = (int32_t)g;
-    out->tile_cols = tile;
-    out->grid = rows * g;
-    out->workspace_bytes = splitk_workspace_bytes(rows, (int32_t)g);
+    fill_splitk_geometry(rows, cols, (int64_t)kSplitKUnroll * kBlockThreads * vec_elems, cu_count,
+                         out);
+    out->workspace_bytes = splitk_workspace_bytes(rows, out->slices);
     return RR_OK;
 }
+
+// The workspace must not depend on row alignment (the binding sizes it before
+// it knows the pointers): a tile never exceeds the columns that justify one
+// more workgroup, so the tile count never caps G below that bound.
+static_assert((int64_t)kSoftmaxSplitKUnroll * kBlockThreads * 8 <= kSplitKMinColsPerGroup,
+              "softmax split-K tile larger than the per-workgroup column minimum");
+static_assert((int64_t)kSplitKUnroll * kBlockThreads * 4 <= kSplitKMinColsPerGroup,
+              "reduce split-K tile larger than the per-workgroup column minimum");
 
 rr_status plan_softmax(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype y_dtype,
                        rr_tier tier, int32_t cu_count, bool vec, rr_plan* out)
@@ -105,11 +126,21 @@ rr_status plan_softmax(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype y_
     if (cu_count < 1) return RR_ERR_SHAPE;
     if ((int)tier < RR_TIER_AUTO || (int)tier > RR_TIER_SPLITK) return RR_ERR_TIER;
     rr_tier t = tier;
-    if (t == RR_TIER_AUTO) t = cols <= 8 ? RR_TIER_TILED : cols <= 64 ? RR_TIER_WAVE : RR_TIER_BLOCK;
-    if (t == RR_TIER_SPLITK) return RR_ERR_TIER;
+    if (t == RR_TIER_AUTO) {
+        if (rows < cu_count && cols >= kSplitKMinCols)
+            t = RR_TIER_SPLITK;
+        else
+            t = cols <= 8 ? RR_TIER_TILED : cols <= 64 ? RR_TIER_WAVE : RR_TIER_BLOCK;
+    }
     if (t == RR_TIER_WAVE && cols > 64) return RR_ERR_TIER;
     memset(out, 0, sizeof *out);
     const int vec_elems = vec ? (x_dtype == RR_BF16 ? 8 : 4) : 1;
+    if (t == RR_TIER_SPLITK) {
+        fill_splitk_geometry(rows, cols, (int64_t)kSoftmaxSplitKUnroll * kBlockThreads * vec_elems,
+                             cu_count, out);
+        out->workspace_bytes = softmax_splitk_workspace_bytes(rows, out->slices);
+        return RR_OK;
+    }
     fill_rowwise_geometry(t, rows, cols, vec_elems, out);
     if (t == RR_TIER_BLOCK) {
         const int64_t chunks = ceil_div(cols, vec_elems);

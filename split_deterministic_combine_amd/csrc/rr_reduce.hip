@@ -237,32 +237,6 @@ __device__ __forceinline__ typename M::acc_t fold_tile(typename M::acc_t acc,
 }
 
 // ----------------------------------------------------------- split-K tier
-// Publishing a partial across workgroups (and across the eight XCDs, whose
-// L2 caches are not coherent with each other).  The partial is written with a
-// device-scope atomic store, which writes through the XCD's L2 to the
-// device-coherent level, and s_waitcnt vmcnt(0) holds the wave until that
-// store is acknowledged; only then is the ticket incremented.  This is the
-// agent-scope release of the AMDGPU memory model without its L2 writeback
-// (buffer_wbl2), which exists to push data written by ordinary stores and
-// costs tens of microseconds when a thousand workgroups issue it at the end
-// of a streaming pass.  The last workgroup reads the partials with
-// device-scope atomic loads, which are served coherently without an L2
-// invalidate.  The signal fences keep the compiler from moving the memory
-// operations across the wait.
-template <class A>
-__device__ __forceinline__ void publish_partial(A* slot, A v)
-{
-    __hip_atomic_store(slot, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0)
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-template <class A>
-__device__ __forceinline__ A read_partial(const A* slot)
-{
-    return __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // A row is cut into tiles of kSplitKUnroll * kBlockThreads * VEC columns
 // (one unrolled load round of the workgroup); workgroup (r, g) folds tiles
 // g, g + G, g + 2G, ... of row r, so at any moment the G workgroups of a row

@@ -445,6 +445,174 @@ __global__ __launch_bounds__(kBlockThreads) void k_softmax_tiled(const XT* __res
     }
 }
 
+// ----------------------------------------------------------- split-K tier
+// For rows < CUs with long rows ("reduce", tier semantics: each block takes
+// a slice of one row).  Two launches:
+//   statistics: workgroup (r, g) folds (max, sum) over tiles g, g+G, ... of
+//     row r, publishes its pair and takes a ticket; the last to arrive folds
+//     the G pairs in ascending g ("cluster_allreduce", description: rank
+//     order) into the row's (M, S) in the workspace and resets the ticket;
+//   map: every workgroup re-reads its tiles and writes exp(x - M) / S.
+// A tile is kSoftmaxSplitKUnroll 16-byte chunks per thread.
+
+// Exponentials of a thread's arguments t: the hardware instruction when
+// every t >= -126 (exact there), else exp2f (subnormal results).
+template <int N>
+__device__ __forceinline__ void exp2_values(float* t)
+{
+    float tmin = 0.0f;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        tmin = fminf(tmin, t[i]);
+    if (tmin >= -126.0f) {
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            t[i] = exp2_hw(t[i]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            t[i] = exp2_f32(t[i]);
+    }
+}
+
+template <class XT, bool VEC>
+__global__ __launch_bounds__(kBlockThreads) void k_softmax_splitk_stats(
+    const XT* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, int32_t G,
+    uint64_t* part, uint32_t* ticket, MS* rowstat, int32_t skew)
+{
+    constexpr int E = VEC ? XIn<XT>::kChunk : 1;
+    constexpr int U = kSoftmaxSplitKUnroll;
+    constexpr int64_t kTile = (int64_t)U * kBlockThreads * E;
+    static_assert(kSplitKMaxSlices <= kBlockThreads, "one partial per thread when gathering");
+    __shared__ MS slot[2][kWavesPerBlock];
+    __shared__ MS gathered[kSplitKMaxSlices];
+    __shared__ bool last;
+    int par = 0;
+    if (threadIdx.x == 0)
+        last = false;
+    const int64_t total = rows * G;
+    const int64_t ntiles = ceil_div(cols, kTile);
+    for (int64_t b = blockIdx.x; b < total; b += gridDim.x) {
+        const int64_t r = b / G;
+        const int32_t g = (int32_t)(b - r * G);
+        const XT* xr = x + r * ldx;
+        // per-thread running (m, s); s in double (a thread adds many terms)
+        float tm = kNegInf;
+        double ts = 0.0;
+        for (int64_t t = g; t < ntiles; t += G) {
+            float v[U * E];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                load_padded<XT, E, VEC>(
+                    xr, t * kTile + ((int64_t)u * kBlockThreads + threadIdx.x) * E, cols, v + u * E);
+            float cm = kNegInf;
+#pragma unroll
+            for (int i = 0; i < U * E; ++i)
+                cm = fmaxf(cm, v[i]);
+            const float M = fmaxf(tm, cm);
+            if (M != kNegInf) {
+                const float mb = -M * kLog2e;
+#pragma unroll
+                for (int i = 0; i < U * E; ++i)
+                    v[i] = __builtin_fmaf(v[i], kLog2e, mb);
+                exp2_values<U * E>(v);
+                double sacc = ts * (double)exp2_f32((tm - M) * kLog2e);
+#pragma unroll
+                for (int i = 0; i < U * E; ++i)
+                    sacc += (double)v[i];
+                tm = M;
+                ts = sacc;
+            }
+        }
+        float e_t;
+        const MS tot = block_softmax_stats<kBlockThreads>(MS{tm, (float)ts}, slot[par], &e_t);
+        par ^= 1;
+        if (threadIdx.x == 0) {
+            if (skew > 0) {  // test hook: arrival order against rank order
+                const int n = (G - 1 - g) * skew;
+                for (int i = 0; i < n; ++i)
+                    __builtin_amdgcn_s_sleep(8);
+            }
+            publish_partial(&part[r * G + g], pack_ms(tot));
+            const uint32_t tk = __hip_atomic_fetch_add(&ticket[r], 1u, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
+            last = tk == (uint32_t)(G - 1);
+        }
+        __syncthreads();
+        if (last) {
+            for (int32_t k = threadIdx.x; k < G; k += kBlockThreads)
+                gathered[k] = unpack_ms(read_partial(&part[r * G + k]));
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                MS a = gathered[0];
+                for (int32_t k = 1; k < G; ++k)
+                    a = SoftmaxMS::combine(a, gathered[k]);
+                rowstat[r] = a;
+                last = false;
+                __hip_atomic_store(&ticket[r], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        __syncthreads();
+    }
+}
+
+template <class XT, class YT, bool VEC>
+__global__ __launch_bounds__(kBlockThreads) void k_softmax_splitk_map(
+    const XT* __restrict__ x, YT* __restrict__ y, int64_t rows, int64_t cols, int64_t ldx,
+    int64_t ldy, int32_t G, const MS* __restrict__ rowstat)
+{
+    constexpr int E = VEC ? XIn<XT>::kChunk : 1;
+    constexpr int U = kSoftmaxSplitKUnroll;
+    constexpr int64_t kTile = (int64_t)U * kBlockThreads * E;
+    const int64_t total = rows * G;
+    const int64_t ntiles = ceil_div(cols, kTile);
+    for (int64_t b = blockIdx.x; b < total; b += gridDim.x) {
+        const int64_t r = b / G;
+        const int32_t g = (int32_t)(b - r * G);
+        const XT* xr = x + r * ldx;
+        YT* yr = y + r * ldy;
+        const MS st = rowstat[r];
+        const float mb = -st.m * kLog2e;
+        const float inv = 1.0f / st.s;
+        for (int64_t t = g; t < ntiles; t += G) {
+            float v[U * E];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                load_padded<XT, E, VEC>(
+                    xr, t * kTile + ((int64_t)u * kBlockThreads + threadIdx.x) * E, cols, v + u * E);
+#pragma unroll
+            for (int i = 0; i < U * E; ++i)
+                v[i] = __builtin_fmaf(v[i], kLog2e, mb);
+            exp2_values<U * E>(v);
+#pragma unroll
+            for (int i = 0; i < U * E; ++i)
+                v[i] *= inv;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                store_masked<YT, E, VEC>(
+                    yr, t * kTile + ((int64_t)u * kBlockThreads + threadIdx.x) * E, cols, v + u * E);
+        }
+    }
+}
+
+template <class XT, class YT, bool VEC>
+static rr_status launch_splitk(const rr_plan& p, const SoftmaxLaunch& a)
+{
+    const XT* x = static_cast<const XT*>(a.x);
+    YT* y = static_cast<YT*>(a.y);
+    uint32_t* ticket = static_cast<uint32_t*>(a.workspace);
+    uint64_t* part = reinterpret_cast<uint64_t*>(static_cast<char*>(a.workspace) +
+                                                 round_up(a.rows * 4, kWorkspaceAlign));
+    MS* rowstat = reinterpret_cast<MS*>(part + a.rows * p.slices);
+    const dim3 grid((unsigned)(p.grid > kMaxGrid ? kMaxGrid : p.grid)), block(kBlockThreads);
+    rr_status st = launch_kernel(k_softmax_splitk_stats<XT, VEC>, grid, block, 0, a.stream, x,
+                                 a.rows, a.cols, a.ld_x, p.slices, part, ticket, rowstat, a.skew);
+    if (st != RR_OK)
+        return st;
+    return launch_kernel(k_softmax_splitk_map<XT, YT, VEC>, grid, block, 0, a.stream, x, y, a.rows,
+                         a.cols, a.ld_x, a.ld_y, p.slices, (const MS*)rowstat);
+}
+
 // ---------------------------------------------------------------- launch
 template <class XT, class YT, int NCH, int NT>
 static rr_status launch_pf(dim3 grid, hipStream_t s, const XT* x, YT* y, const SoftmaxLaunch& a)
@@ -510,6 +678,8 @@ static rr_status launch_typed(const rr_plan& p, const SoftmaxLaunch& a)
         case 64: return launch_kernel(k_softmax_wave<XT, YT, VEC, 64>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
         default: return RR_ERR_TIER;
         }
+    case RR_TIER_SPLITK:
+        return launch_splitk<XT, YT, VEC>(p, a);
     case RR_TIER_TILED:
         return launch_kernel(k_softmax_tiled<XT, YT, kTiledRows>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
     case RR_TIER_SERIAL:

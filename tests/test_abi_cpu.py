@@ -105,9 +105,27 @@ def test_softmax_tier_rule():
     assert rr.plan_softmax(64, 16385)["block"] == 512        # longer rows: wider workgroups
     assert rr.plan_softmax(100, 40)["tier"] == "wave"
     assert rr.plan_softmax(100, 4)["tier"] == "tiled"
-    with pytest.raises(rr.RRError) as e:
-        rr.plan_softmax(4, 1 << 20, tier="splitk")
-    assert e.value.status == 4
+    assert rr.plan_softmax(16, 1 << 20)["tier"] == "splitk"    # rows < CU and long rows
+    assert rr.plan_softmax(256, 1 << 20)["tier"] == "block"
+    assert rr.plan_softmax(16, 65535)["tier"] == "block"
+
+
+def test_softmax_splitk_geometry():
+    # bf16 rows of 2^20: tiles of 4 x 256 threads x 8 elements; 64 workgroups
+    # per row (16 rows x 64 = 4 per CU), 16 tiles each
+    p = rr.plan_softmax(16, 1 << 20, cu_count=256)
+    assert p["slices"] == 64 and p["grid"] == 1024 and p["tile_cols"] == 8192
+    assert p["workspace_bytes"] == 256 + 16 * 64 * 8 + 16 * 8
+    # float32 input: 4 elements per 16-byte chunk
+    p = rr.plan_softmax(16, 1 << 20, x_dtype=torch.float32, cu_count=256)
+    assert p["tile_cols"] == 4096 and p["slices"] == 64
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 65536), (3, 70001), (200, 1 << 20), (1, 1 << 30)])
+def test_softmax_splitk_every_workgroup_gets_a_tile(rows, cols):
+    p = rr.plan_softmax(rows, cols, tier="splitk", cu_count=256)
+    g, t = p["slices"], p["tile_cols"]
+    assert 1 <= g <= 256 and g <= -(-cols // t) and p["grid"] == rows * g
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -131,7 +149,8 @@ def test_entry_points_validate_before_touching_the_device():
     lib.rr_reduce_rows.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, ctypes.c_size_t, vp]
     lib.rr_softmax_rows.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
-                                    ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+                                    ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp,
+                                    ctypes.c_size_t, vp]
     lib.rr_splitk_lse_merge.argtypes = [vp, vp, vp, vp, ctypes.c_int32, ctypes.c_int64,
                                         ctypes.c_int32, ctypes.c_float, ctypes.c_int, vp]
     assert lib.rr_reduce_rows(None, None, -1, 4, 4, 0, 0, 0, None, 0, None) == 2
@@ -141,10 +160,11 @@ def test_entry_points_validate_before_touching_the_device():
     assert lib.rr_reduce_rows(None, None, 4, 100, 100, 0, 0, 1, None, 0, None) == 4
     assert lib.rr_reduce_rows(None, None, 0, 8, 8, 0, 0, 0, None, 0, None) == 0   # no-op
     assert lib.rr_reduce_rows(None, None, 4, 8, 8, 0, 0, 0, None, 0, None) == 1   # NULL
-    assert lib.rr_softmax_rows(None, None, 4, 8, 8, 8, 1, 1, 0, None) == 3        # int32 softmax
-    assert lib.rr_softmax_rows(None, None, 4, 8, 8, 8, 2, 2, 5, None) == 4        # split-K softmax
-    assert lib.rr_softmax_rows(None, None, 4, 8, 4, 8, 2, 2, 0, None) == 2        # ld_x < cols
-    assert lib.rr_softmax_rows(None, None, 4, 0, 8, 8, 2, 2, 0, None) == 0        # cols 0: no-op
+    assert lib.rr_softmax_rows(None, None, 4, 8, 8, 8, 1, 1, 0, None, 0, None) == 3   # int32
+    assert lib.rr_softmax_rows(None, None, 4, 8, 8, 8, 2, 2, 6, None, 0, None) == 4   # bad tier
+    assert lib.rr_softmax_rows(None, None, 4, 8, 8, 8, 2, 2, 5, None, 0, None) == 1   # NULL
+    assert lib.rr_softmax_rows(None, None, 4, 8, 4, 8, 2, 2, 0, None, 0, None) == 2   # ld_x < cols
+    assert lib.rr_softmax_rows(None, None, 4, 0, 8, 8, 2, 2, 0, None, 0, None) == 0   # no-op
     assert lib.rr_splitk_lse_merge(None, None, None, None, 0, 4, 8, 1.0, 2, None) == 2
     assert lib.rr_splitk_lse_merge(None, None, None, None, 257, 4, 8, 1.0, 2, None) == 2
     assert lib.rr_splitk_lse_merge(None, None, None, None, 8, 4, 0, 1.0, 2, None) == 2

@@ -219,7 +219,7 @@ def _check_softmax(gpu, ref, yt, what):
 
 
 def _softmax_tiers(cols):
-    tiers = ["auto", "block", "tiled", "serial"]
+    tiers = ["auto", "block", "tiled", "serial", "splitk"]
     if cols <= 64:
         tiers.append("wave")
     return tiers
@@ -271,7 +271,7 @@ def test_softmax_special_values():
         for yt in ("f32", "bf16"):
             ref = oracle.softmax_rows(xin, yt)
             ydt = torch.bfloat16 if yt == "bf16" else torch.float32
-            for tier in ("wave", "block", "tiled", "serial"):
+            for tier in ("wave", "block", "tiled", "serial", "splitk"):
                 y = to_host(rr.softmax_rows(to_gpu(xin), ydt, tier))
                 _check_softmax(y, ref, yt, "special %s->%s %s" % (xt, yt, tier))
 
@@ -289,9 +289,85 @@ def test_softmax_wide_logit_range():
 def test_softmax_in_place():
     x = _softmax_input("bf16", 9, 3000, 41)
     ref = oracle.softmax_rows(x, "bf16")
-    g = to_gpu(x)
-    rr.softmax_rows(g, torch.bfloat16, "block", out=g)
-    assert_bf16_within_1ulp(to_host(g), ref, "in place")
+    for tier in ("block", "splitk"):
+        g = to_gpu(x)
+        rr.softmax_rows(g, torch.bfloat16, tier, out=g)
+        assert_bf16_within_1ulp(to_host(g), ref, "in place " + tier)
+
+
+# split-K softmax: rows < CU with long rows, several workgroups per row
+SPLITK_SOFTMAX_SHAPES = [(1, 65536), (3, 70001), (7, 100003), (2, 262144 + 8), (5, 131072 - 1)]
+
+
+@pytest.mark.parametrize("rows,cols", SPLITK_SOFTMAX_SHAPES)
+@pytest.mark.parametrize("xt,yt", SOFTMAX_TYPES)
+def test_softmax_splitk_parity(rows, cols, xt, yt):
+    x = _softmax_input(xt, rows, cols, 1700 + cols + rows)
+    ref = oracle.softmax_rows(x, yt)
+    ydt = torch.bfloat16 if yt == "bf16" else torch.float32
+    xtd = torch.bfloat16 if xt == "bf16" else torch.float32
+    plan = rr.plan_softmax(rows, cols, xtd, ydt, "splitk", rr.device_cu_count())
+    assert plan["slices"] > 1
+    assert rr.select_tier("softmax", rows, cols, xtd) == "splitk"
+    for tier in ("auto", "splitk"):
+        y = to_host(rr.softmax_rows(to_gpu(x), ydt, tier))
+        _check_softmax(y, ref, yt, "splitk %dx%d %s->%s %s" % (rows, cols, xt, yt, tier))
+
+
+@pytest.mark.parametrize("offset", [1, 3])
+def test_softmax_splitk_misaligned_rows(offset):
+    rows, cols = 3, 90001
+    for xt in ("bf16", "f32"):
+        x = _softmax_input(xt, rows, cols, 77 + offset)
+        ref = oracle.softmax_rows(x, "f32")
+        big = np.zeros((rows, cols + 8 + offset), dtype=x.dtype)
+        big[:, offset:offset + cols] = x
+        g = to_gpu(big)[:, offset:offset + cols]
+        y = to_host(rr.softmax_rows(g, torch.float32, "splitk"))
+        assert_close_f32(y, ref, "splitk misaligned %s off %d" % (xt, offset))
+
+
+def test_softmax_splitk_wide_range_and_special_rows():
+    rows, cols = 4, 80000
+    x = synth.uniform_f32(33, (rows, cols), -120.0, 20.0)
+    x[1, :] = -np.inf                      # whole row -inf: NaN, as in the definition
+    x[2, ::7] = -np.inf                    # -inf entries give exact zeros
+    x[3, 12345] = 200.0                    # one dominant entry in the middle slice
+    for yt in ("f32", "bf16"):
+        ref = oracle.softmax_rows(x, yt)
+        ydt = torch.bfloat16 if yt == "bf16" else torch.float32
+        y = to_host(rr.softmax_rows(to_gpu(x), ydt, "splitk"))
+        _check_softmax(y, ref, yt, "splitk special " + yt)
+
+
+def test_softmax_splitk_bits_do_not_depend_on_arrival_order():
+    g = to_gpu(synth.normal_bf16(12, (16, 1 << 20)))
+    assert rr.plan_softmax(16, 1 << 20, cu_count=rr.device_cu_count())["tier"] == "splitk"
+    first = rr.softmax_rows(g).clone()
+    for _ in range(3):
+        assert torch.equal(rr.softmax_rows(g).view(torch.int16), first.view(torch.int16))
+    try:
+        rr._set_splitk_skew(16)
+        skewed = rr.softmax_rows(g).clone()
+        torch.cuda.synchronize()
+    finally:
+        rr._set_splitk_skew(0)
+    assert torch.equal(skewed.view(torch.int16), first.view(torch.int16))
+    # every row sums to 1 within the bf16 rounding of its outputs
+    s = first.float().sum(dim=1)
+    assert float((s - 1).abs().max()) <= 2.0 ** -8
+    sample = np.array([0, 5, 15])
+    ref = oracle.softmax_rows(np.ascontiguousarray(to_host(g)[sample]), "bf16")
+    assert_bf16_within_1ulp(to_host(first)[sample], ref, "splitk 16 x 2^20 sample rows")
+
+
+def test_softmax_splitk_tickets_are_left_zero():
+    x = to_gpu(synth.normal_f32(10, (3, 200000)))
+    rr.softmax_rows(x, torch.float32, "splitk")
+    torch.cuda.synchronize()
+    assert rr._workspaces
+    for ws in rr._workspaces.values():
+        assert int(ws[:256].count_nonzero()) == 0
 
 
 def test_softmax_rows_config_full_size():
