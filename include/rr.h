@@ -123,8 +123,9 @@ rr_status rr_plan_reduce(int64_t rows, int64_t cols, int64_t ld, rr_dtype dtype,
 /*
  * rr_plan_softmax -- tier selection for rr_softmax_rows: the reduce rule
  * (SPLITK when rows < cu_count and cols >= 65536, then TILED / WAVE /
- * BLOCK).  SPLITK uses tiles of 4 * 256 * 16-byte chunks and needs the
- * workspace reported in workspace_bytes.
+ * BLOCK).  SPLITK uses tiles of 4 * 256 * 16-byte chunks (4 * 256 elements
+ * on the scalar path), G as for rr_plan_reduce with that tile, and needs the
+ * workspace reported in workspace_bytes (rows * G * 8).
  */
 rr_status rr_plan_softmax(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype y_dtype,
                           rr_tier tier, int32_t cu_count, rr_plan* plan_out);
@@ -170,15 +171,22 @@ rr_status rr_reduce_rows(const void* x, void* y, int64_t rows, int64_t cols, int
  *   y        device, [rows][ld_y] of y_dtype (RR_BF16 or RR_F32)
  *   tier     RR_TIER_AUTO, WAVE, BLOCK, TILED, SERIAL or SPLITK
  *   workspace, workspace_bytes
- *            device scratch for RR_TIER_SPLITK, as for rr_reduce_rows (size:
- *            rr_workspace_bytes with RR_KIND_SOFTMAX; tickets zero before
- *            first use, left zero by every completed call).  Ignored by the
- *            other tiers (may be NULL).
+ *            device scratch for RR_TIER_SPLITK: rows * G * 8 bytes, 8-byte
+ *            aligned (size: rr_workspace_bytes with RR_KIND_SOFTMAX).  No
+ *            initial contents are needed; every call writes before it reads.
+ *            Ignored by the other tiers (may be NULL).  One workspace must
+ *            not serve two calls in flight, and a buffer used here must be
+ *            zeroed (rr_workspace_reset) before it serves rr_reduce_rows,
+ *            whose tickets live where this call writes its pairs.
  * Split-K ("reduce", tier semantics: several blocks per row; and
- * "cluster_allreduce", description: the groups' values folded in rank
- * order) runs two launches: G workgroups per row fold (max, sum) over their
- * tiles, the last to arrive folds the G pairs in ascending rank into the
- * row's (M, S); then a map pass writes y.
+ * "cluster_allreduce", description: the all-gather variant, where every
+ * group needs the folded value) runs two launches on the stream: G
+ * workgroups per row fold (max, sum) over their tiles and store the pair;
+ * then every workgroup of the map pass folds its row's G pairs in rank order
+ * (M = max of the m_g, S = sum of s_g * exp(m_g - M) over a fixed tree with
+ * the ranks as leaves, in double) and writes y over its tiles.  All
+ * workgroups of a row fold the same pairs the same way, so they use the same
+ * (M, S), and the result does not depend on scheduling.
  * Arithmetic in float32; bf16 results are rounded to nearest even.  y may
  * alias x only when ld_y == ld_x and the dtypes match.  cols == 0 or
  * rows == 0 is a no-op.

@@ -11,8 +11,7 @@ extern "C" {
 #endif
 
 /*
- * Arrival-order skew for the split-K tiers of rr_reduce_rows and of
- * rr_softmax_rows (its statistics pass).  With a value
+ * Arrival-order skew for the split-K tier of rr_reduce_rows.  With a value
  * k > 0, the workgroup folding slice g of a row sleeps about (G - 1 - g) * k
  * short periods before it publishes its partial, so slices tend to arrive in
  * descending rank order.  The cross-workgroup fold of "cluster_allreduce"

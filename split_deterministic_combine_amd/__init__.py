@@ -191,13 +191,14 @@ def _softmax_workspace_need(rows, cols, xdt, ydt, tier, cu):
     return n
 
 
-# split-K workspaces, one per (device, stream); tickets reset themselves, so a
-# workspace stays zero between calls on its stream.
+# split-K workspaces, one per (kind, device, stream).  A reduction's tickets
+# reset themselves, so its workspace stays zero between calls on its stream;
+# the softmax workspace holds only pairs that each call writes before reading.
 _workspaces = {}
 
 
-def _workspace(device, stream_id, nbytes):
-    key = (device.index, stream_id)
+def _workspace(kind, device, stream_id, nbytes):
+    key = (kind, device.index, stream_id)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(max(nbytes, 4096), dtype=torch.uint8, device=device)
@@ -224,7 +225,7 @@ def reduce_rows(x, op="sum", tier="auto", out=None):
         need = _workspace_need(rows, cols, ld, dt, o, t, _cu_count(x.device))
         ws_ptr, ws_len = None, 0
         if need:
-            ws = _workspace(x.device, stream.value, need)
+            ws = _workspace("reduce", x.device, stream.value, need)
             ws_ptr, ws_len = ctypes.c_void_p(ws.data_ptr()), ws.numel()
         _check(lib.rr_reduce_rows(ctypes.c_void_p(x2.data_ptr()), ctypes.c_void_p(out.data_ptr()),
                                   rows, cols, ld, dt, o, t, ws_ptr, ws_len, stream))
@@ -247,7 +248,7 @@ def softmax_rows(x, out_dtype=None, tier="auto", out=None):
         need = _softmax_workspace_need(rows, cols, xdt, ydt, t, _cu_count(x.device))
         ws_ptr, ws_len = None, 0
         if need:
-            ws = _workspace(x.device, stream.value, need)
+            ws = _workspace("softmax", x.device, stream.value, need)
             ws_ptr, ws_len = ctypes.c_void_p(ws.data_ptr()), ws.numel()
         _check(lib.rr_softmax_rows(ctypes.c_void_p(x2.data_ptr()), ctypes.c_void_p(y2.data_ptr()),
                                    rows, cols, ld_x, ld_y, xdt, ydt, t, ws_ptr, ws_len, stream))

@@ -107,7 +107,7 @@ extern "C" rr_status rr_softmax_rows(const void* x, void* y, int64_t rows, int64
             return RR_ERR_WORKSPACE;
     }
     rr::SoftmaxLaunch a{x, y, rows, cols, ld_x, ld_y, x_dtype, y_dtype, vec, workspace,
-                        g_splitk_skew.load(std::memory_order_relaxed), as_stream(stream)};
+                        as_stream(stream)};
     return rr::launch_softmax(p, a);
 }
 

@@ -27,7 +27,6 @@ struct SoftmaxLaunch {
     rr_dtype x_dtype, y_dtype;
     bool vec;
     void* workspace;      // split-K only
-    int32_t skew;         // split-K arrival-order test hook (0 = off)
     hipStream_t stream;
 };
 

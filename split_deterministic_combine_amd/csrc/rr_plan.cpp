@@ -20,8 +20,8 @@ uint64_t splitk_workspace_bytes(int64_t rows, int32_t slices)
 
 uint64_t softmax_splitk_workspace_bytes(int64_t rows, int32_t slices)
 {
-    // tickets, then one (m, s) pair per (row, workgroup), then one per row
-    return splitk_workspace_bytes(rows, slices) + (uint64_t)rows * 8;
+    // one (m, s) pair per (row, workgroup); no counters
+    return (uint64_t)(rows * (int64_t)slices * 8);
 }
 
 // Split-K geometry shared by the reduce and softmax tiers: G workgroups per

@@ -446,16 +446,21 @@ __global__ __launch_bounds__(kBlockThreads) void k_softmax_tiled(const XT* __res
 }
 
 // ----------------------------------------------------------- split-K tier
-// For rows < CUs with long rows ("reduce", tier semantics: each block takes
-// a slice of one row).  Two launches:
-//   statistics: workgroup (r, g) folds (max, sum) over tiles g, g+G, ... of
-//     row r, publishes its pair and takes a ticket; the last to arrive folds
-//     the G pairs in ascending g ("cluster_allreduce", description: rank
-//     order) into the row's (M, S) in the workspace and resets the ticket;
-//   map: every workgroup re-reads its tiles and writes exp(x - M) / S.
-// A tile is kSoftmaxSplitKUnroll 16-byte chunks per thread.
+// For fewer rows than compute units, with long rows: G workgroups per row
+// ("reduce", tier semantics), each owning tiles g, g + G, ... of the row.
+// Two launches on one stream:
+//   statistics: workgroup (r, g) folds (max, sum) over its tiles and stores
+//     the pair to part[r * G + g];
+//   map: every workgroup of row r reads the row's G pairs and folds them in
+//     rank order into (M, S) -- the same inputs in the same order, so every
+//     workgroup of the row holds the same bits ("cluster_allreduce",
+//     description: the all-gather variant, where every block needs the
+//     result) -- then writes exp(x - M) / S over its tiles.
+// The kernel boundary makes the statistics pass's stores visible to the map
+// pass; no atomics and no counters are needed.  A tile is
+// kSoftmaxSplitKUnroll 16-byte chunks per thread.
 
-// Exponentials of a thread's arguments t: the hardware instruction when
+// Exponentials of a thread's map arguments t: the hardware instruction when
 // every t >= -126 (exact there), else exp2f (subnormal results).
 template <int N>
 __device__ __forceinline__ void exp2_values(float* t)
@@ -475,123 +480,272 @@ __device__ __forceinline__ void exp2_values(float* t)
     }
 }
 
+// One split-K tile of a thread: U chunks of E elements, chunk u at element
+// offset (u * kBlockThreads + threadIdx.x) * E of the tile.
+template <class XT, int E, bool VEC, int U>
+__device__ __forceinline__ void load_tile_full(const XT* tile, float* v)
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const XT* p = tile + ((int64_t)u * kBlockThreads + threadIdx.x) * E;
+        if constexpr (VEC)
+            XIn<XT>::chunk(p, v + u * E);
+        else
+            v[u] = XIn<XT>::one(p);
+    }
+}
+
+template <class XT, int E, bool VEC, int U>
+__device__ __forceinline__ void load_tile_padded(const XT* row, int64_t begin, int64_t cols, float* v)
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        load_padded<XT, E, VEC>(row, begin + ((int64_t)u * kBlockThreads + threadIdx.x) * E, cols,
+                                v + u * E);
+}
+
+template <class YT, int E, bool VEC, int U>
+__device__ __forceinline__ void store_tile_full(YT* tile, const float* v)
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        YT* p = tile + ((int64_t)u * kBlockThreads + threadIdx.x) * E;
+        if constexpr (VEC)
+            YOut<YT>::template chunk<E>(p, v + u * E);
+        else
+            YOut<YT>::one(p, v[u]);
+    }
+}
+
+template <class YT, int E, bool VEC, int U>
+__device__ __forceinline__ void store_tile_masked(YT* row, int64_t begin, int64_t cols, const float* v)
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        store_masked<YT, E, VEC>(row, begin + ((int64_t)u * kBlockThreads + threadIdx.x) * E, cols,
+                                 v + u * E);
+}
+
+// Fold one tile's N values into the thread's running (tm, ts): exponentials
+// relative to the new running maximum, summed pairwise in float (N is a
+// power of two), added to the running sum in double.  The hardware
+// exponential is used without a range check: the running sum always holds
+// the 1 of its own maximum, so a term it flushes (below 2^-126) lies far
+// below the double's resolution there and the sum comes out the same.
+template <int N>
+__device__ __forceinline__ void stats_fold_tile(float* v, float& tm, double& ts)
+{
+    static_assert((N & (N - 1)) == 0, "pairwise sum over a power of two");
+    float cm = kNegInf;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        cm = fmaxf(cm, v[i]);
+    const float M = fmaxf(tm, cm);
+    if (M == kNegInf)
+        return;
+    const float mb = -M * kLog2e;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        v[i] = exp2_hw(__builtin_fmaf(v[i], kLog2e, mb));
+#pragma unroll
+    for (int w = N / 2; w >= 1; w /= 2)
+#pragma unroll
+        for (int i = 0; i < w; ++i)
+            v[i] += v[i + w];
+    ts = ts * (double)exp2_f32((tm - M) * kLog2e) + (double)v[0];
+    tm = M;
+}
+
+// A thread's share of one whole tile as loaded, before conversion to float,
+// so that the next tile's loads can be in flight while this one is folded.
+// Plain (cached) loads: the map pass re-reads the same rows soon after.
+template <class XT, bool VEC, int U>
+struct RawTile;
+template <class XT, int U>
+struct RawTile<XT, true, U> {
+    uint4 c[U];
+    __device__ void load(const XT* tile)
+    {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            c[u] = *reinterpret_cast<const uint4*>(
+                tile + ((int64_t)u * kBlockThreads + threadIdx.x) * XIn<XT>::kChunk);
+    }
+    __device__ void unpack(float* v) const
+    {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if constexpr (sizeof(XT) == 2) {
+                float* o = v + u * 8;
+                o[0] = bf16_lo(c[u].x); o[1] = bf16_hi(c[u].x);
+                o[2] = bf16_lo(c[u].y); o[3] = bf16_hi(c[u].y);
+                o[4] = bf16_lo(c[u].z); o[5] = bf16_hi(c[u].z);
+                o[6] = bf16_lo(c[u].w); o[7] = bf16_hi(c[u].w);
+            } else {
+                float* o = v + u * 4;
+                o[0] = __uint_as_float(c[u].x); o[1] = __uint_as_float(c[u].y);
+                o[2] = __uint_as_float(c[u].z); o[3] = __uint_as_float(c[u].w);
+            }
+        }
+    }
+};
+template <class XT, int U>
+struct RawTile<XT, false, U> {
+    float c[U];
+    __device__ void load(const XT* tile)
+    {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            c[u] = XIn<XT>::one(tile + (int64_t)u * kBlockThreads + threadIdx.x);
+    }
+    __device__ void unpack(float* v) const
+    {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            v[u] = c[u];
+    }
+};
+
+template <int N, class R>
+__device__ __forceinline__ void stats_fold_raw(const R& raw, float& tm, double& ts)
+{
+    float v[N];
+    raw.unpack(v);
+    stats_fold_tile<N>(v, tm, ts);
+}
+
 template <class XT, bool VEC>
 __global__ __launch_bounds__(kBlockThreads) void k_softmax_splitk_stats(
     const XT* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, int32_t G,
-    uint64_t* part, uint32_t* ticket, MS* rowstat, int32_t skew)
+    uint64_t* __restrict__ part)
 {
     constexpr int E = VEC ? XIn<XT>::kChunk : 1;
     constexpr int U = kSoftmaxSplitKUnroll;
-    constexpr int64_t kTile = (int64_t)U * kBlockThreads * E;
-    static_assert(kSplitKMaxSlices <= kBlockThreads, "one partial per thread when gathering");
+    constexpr int N = U * E;
+    constexpr int64_t kTile = (int64_t)N * kBlockThreads;
     __shared__ MS slot[2][kWavesPerBlock];
-    __shared__ MS gathered[kSplitKMaxSlices];
-    __shared__ bool last;
     int par = 0;
-    if (threadIdx.x == 0)
-        last = false;
     const int64_t total = rows * G;
     const int64_t ntiles = ceil_div(cols, kTile);
+    const int64_t nfull = cols / kTile;
     for (int64_t b = blockIdx.x; b < total; b += gridDim.x) {
         const int64_t r = b / G;
         const int32_t g = (int32_t)(b - r * G);
         const XT* xr = x + r * ldx;
-        // per-thread running (m, s); s in double (a thread adds many terms)
         float tm = kNegInf;
         double ts = 0.0;
-        for (int64_t t = g; t < ntiles; t += G) {
-            float v[U * E];
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                load_padded<XT, E, VEC>(
-                    xr, t * kTile + ((int64_t)u * kBlockThreads + threadIdx.x) * E, cols, v + u * E);
-            float cm = kNegInf;
-#pragma unroll
-            for (int i = 0; i < U * E; ++i)
-                cm = fmaxf(cm, v[i]);
-            const float M = fmaxf(tm, cm);
-            if (M != kNegInf) {
-                const float mb = -M * kLog2e;
-#pragma unroll
-                for (int i = 0; i < U * E; ++i)
-                    v[i] = __builtin_fmaf(v[i], kLog2e, mb);
-                exp2_values<U * E>(v);
-                double sacc = ts * (double)exp2_f32((tm - M) * kLog2e);
-#pragma unroll
-                for (int i = 0; i < U * E; ++i)
-                    sacc += (double)v[i];
-                tm = M;
-                ts = sacc;
+        // Whole tiles g, g + G, ...: n of them.  Two register buffers; the
+        // next tile's loads are issued before the current one is folded.
+        // Trip counts are uniform over the workgroup (scalar branches).
+        const int64_t n = g < nfull ? (nfull - 1 - g) / G + 1 : 0;
+        if (n > 0) {
+            const int64_t step = (int64_t)G * kTile;
+            const XT* tp = xr + (int64_t)g * kTile;
+            RawTile<XT, VEC, U> A, B;
+            A.load(tp);
+            int64_t k = 0;
+            // sched_barrier: keep the folds' first uses of the older buffer
+            // below the younger loads, so those are issued without waiting
+            for (; k + 2 < n; k += 2) {
+                B.load(tp + (k + 1) * step);
+                __builtin_amdgcn_sched_barrier(0);
+                stats_fold_raw<N>(A, tm, ts);
+                A.load(tp + (k + 2) * step);
+                __builtin_amdgcn_sched_barrier(0);
+                stats_fold_raw<N>(B, tm, ts);
             }
+            if (k + 1 < n) {
+                B.load(tp + (k + 1) * step);
+                __builtin_amdgcn_sched_barrier(0);
+                stats_fold_raw<N>(A, tm, ts);
+                stats_fold_raw<N>(B, tm, ts);
+            } else {
+                stats_fold_raw<N>(A, tm, ts);
+            }
+        }
+        for (int64_t t = g + n * G; t < ntiles; t += G) {  // ragged last tile, -inf padded
+            float v[N];
+            load_tile_padded<XT, E, VEC, U>(xr, t * kTile, cols, v);
+            stats_fold_tile<N>(v, tm, ts);
         }
         float e_t;
         const MS tot = block_softmax_stats<kBlockThreads>(MS{tm, (float)ts}, slot[par], &e_t);
         par ^= 1;
-        if (threadIdx.x == 0) {
-            if (skew > 0) {  // test hook: arrival order against rank order
-                const int n = (G - 1 - g) * skew;
-                for (int i = 0; i < n; ++i)
-                    __builtin_amdgcn_s_sleep(8);
-            }
-            publish_partial(&part[r * G + g], pack_ms(tot));
-            const uint32_t tk = __hip_atomic_fetch_add(&ticket[r], 1u, __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_AGENT);
-            last = tk == (uint32_t)(G - 1);
-        }
-        __syncthreads();
-        if (last) {
-            for (int32_t k = threadIdx.x; k < G; k += kBlockThreads)
-                gathered[k] = unpack_ms(read_partial(&part[r * G + k]));
-            __syncthreads();
-            if (threadIdx.x == 0) {
-                MS a = gathered[0];
-                for (int32_t k = 1; k < G; ++k)
-                    a = SoftmaxMS::combine(a, gathered[k]);
-                rowstat[r] = a;
-                last = false;
-                __hip_atomic_store(&ticket[r], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
-        __syncthreads();
+        if (threadIdx.x == 0)
+            part[r * G + g] = pack_ms(tot);
     }
+}
+
+// y = exp(x - M) / S on the tile's values, in place.
+template <int N>
+__device__ __forceinline__ void map_tile(float* v, float mb, float inv)
+{
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        v[i] = __builtin_fmaf(v[i], kLog2e, mb);
+    exp2_values<N>(v);
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        v[i] *= inv;
+}
+
+// Row statistics from the row's G pairs (p: this thread's pair, the
+// identity for threads >= G), in rank order: M = max over g of m_g (exact,
+// so the order does not matter), then S = sum over g of s_g * exp(m_g - M),
+// the G terms taken in parallel and added in double over a fixed tree whose
+// leaves are the ranks in order.  Every workgroup computing it from the same
+// pairs gets the same bits.
+__device__ __forceinline__ MS fold_row_partials(MS p, float* fslot, double* dslot)
+{
+    const float M = block_reduce<MaxFloat, kBlockThreads>(p.m, fslot);
+    const double w = p.m == kNegInf ? 0.0 : (double)p.s * (double)exp2_f32((p.m - M) * kLog2e);
+    const double S = block_reduce<SumF32, kBlockThreads>(w, dslot);
+    return MS{M, (float)S};
 }
 
 template <class XT, class YT, bool VEC>
 __global__ __launch_bounds__(kBlockThreads) void k_softmax_splitk_map(
     const XT* __restrict__ x, YT* __restrict__ y, int64_t rows, int64_t cols, int64_t ldx,
-    int64_t ldy, int32_t G, const MS* __restrict__ rowstat)
+    int64_t ldy, int32_t G, const uint64_t* __restrict__ part)
 {
     constexpr int E = VEC ? XIn<XT>::kChunk : 1;
     constexpr int U = kSoftmaxSplitKUnroll;
     constexpr int64_t kTile = (int64_t)U * kBlockThreads * E;
+    static_assert(kSplitKMaxSlices <= kBlockThreads, "one pair per thread in the row fold");
+    __shared__ float fslot[kWavesPerBlock];
+    __shared__ double dslot[kWavesPerBlock];
     const int64_t total = rows * G;
     const int64_t ntiles = ceil_div(cols, kTile);
+    const int64_t nfull = cols / kTile;
     for (int64_t b = blockIdx.x; b < total; b += gridDim.x) {
         const int64_t r = b / G;
         const int32_t g = (int32_t)(b - r * G);
         const XT* xr = x + r * ldx;
         YT* yr = y + r * ldy;
-        const MS st = rowstat[r];
+        // the row's pairs first, then the first tile: the fold waits only
+        // for the pairs while the tile is in flight
+        MS p = MS{kNegInf, 0.0f};
+        if ((int32_t)threadIdx.x < G)
+            p = unpack_ms(part[r * G + threadIdx.x]);
+        int64_t t = g;
+        float v[U * E];
+        if (t < nfull)
+            load_tile_full<XT, E, VEC, U>(xr + t * kTile, v);
+        const MS st = fold_row_partials(p, fslot, dslot);
         const float mb = -st.m * kLog2e;
         const float inv = 1.0f / st.s;
-        for (int64_t t = g; t < ntiles; t += G) {
-            float v[U * E];
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                load_padded<XT, E, VEC>(
-                    xr, t * kTile + ((int64_t)u * kBlockThreads + threadIdx.x) * E, cols, v + u * E);
-#pragma unroll
-            for (int i = 0; i < U * E; ++i)
-                v[i] = __builtin_fmaf(v[i], kLog2e, mb);
-            exp2_values<U * E>(v);
-#pragma unroll
-            for (int i = 0; i < U * E; ++i)
-                v[i] *= inv;
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                store_masked<YT, E, VEC>(
-                    yr, t * kTile + ((int64_t)u * kBlockThreads + threadIdx.x) * E, cols, v + u * E);
+        for (; t < nfull; t += G) {
+            map_tile<U * E>(v, mb, inv);
+            store_tile_full<YT, E, VEC, U>(yr + t * kTile, v);
+            if (t + G < nfull)
+                load_tile_full<XT, E, VEC, U>(xr + (t + G) * kTile, v);
         }
+        for (; t < ntiles; t += G) {
+            load_tile_padded<XT, E, VEC, U>(xr, t * kTile, cols, v);
+            map_tile<U * E>(v, mb, inv);
+            store_tile_masked<YT, E, VEC, U>(yr, t * kTile, cols, v);
+        }
+        __syncthreads();  // the fold's LDS slots are reused by the next row
     }
 }
 
@@ -600,17 +754,14 @@ static rr_status launch_splitk(const rr_plan& p, const SoftmaxLaunch& a)
 {
     const XT* x = static_cast<const XT*>(a.x);
     YT* y = static_cast<YT*>(a.y);
-    uint32_t* ticket = static_cast<uint32_t*>(a.workspace);
-    uint64_t* part = reinterpret_cast<uint64_t*>(static_cast<char*>(a.workspace) +
-                                                 round_up(a.rows * 4, kWorkspaceAlign));
-    MS* rowstat = reinterpret_cast<MS*>(part + a.rows * p.slices);
+    uint64_t* part = static_cast<uint64_t*>(a.workspace);
     const dim3 grid((unsigned)(p.grid > kMaxGrid ? kMaxGrid : p.grid)), block(kBlockThreads);
     rr_status st = launch_kernel(k_softmax_splitk_stats<XT, VEC>, grid, block, 0, a.stream, x,
-                                 a.rows, a.cols, a.ld_x, p.slices, part, ticket, rowstat, a.skew);
+                                 a.rows, a.cols, a.ld_x, p.slices, part);
     if (st != RR_OK)
         return st;
     return launch_kernel(k_softmax_splitk_map<XT, YT, VEC>, grid, block, 0, a.stream, x, y, a.rows,
-                         a.cols, a.ld_x, a.ld_y, p.slices, (const MS*)rowstat);
+                         a.cols, a.ld_x, a.ld_y, p.slices, (const uint64_t*)part);
 }
 
 // ---------------------------------------------------------------- launch

@@ -115,7 +115,7 @@ def test_softmax_splitk_geometry():
     # per row (16 rows x 64 = 4 per CU), 16 tiles each
     p = rr.plan_softmax(16, 1 << 20, cu_count=256)
     assert p["slices"] == 64 and p["grid"] == 1024 and p["tile_cols"] == 8192
-    assert p["workspace_bytes"] == 256 + 16 * 64 * 8 + 16 * 8
+    assert p["workspace_bytes"] == 16 * 64 * 8
     # float32 input: 4 elements per 16-byte chunk
     p = rr.plan_softmax(16, 1 << 20, x_dtype=torch.float32, cu_count=256)
     assert p["tile_cols"] == 4096 and p["slices"] == 64
