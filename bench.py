@@ -6,6 +6,10 @@ One step runs every operation of the path once on its synthetic workload:
   long_rows   f32 row sum and int32 row max over [16, 2^24]   (split-K tier)
   lse_merge   P = 8 merge of O [8, 8, 32, 128, 128] -> bf16 [8, 32, 128, 128]
 
+Outside the step (and outside `value`), the operations built after it are
+timed on their own workloads and reported under "next_rows":
+  softmax_long  bf16 softmax over [16, 2^22]                 (split-K tier)
+
 Inputs are resident in HBM before timing.  Buffer sets rotate from one step
 to the next so that the data touched by consecutive launches exceeds the
 ~256 MB Infinity Cache (the long-row inputs are 1 GiB each by themselves).
@@ -51,7 +55,10 @@ KERNEL_OF_OP = {
     "long_sum": "k_reduce_splitk<rr::SumF32, 4>",
     "long_max": "k_reduce_splitk<rr::MaxI32, 4>",
     "merge": "k_lse_merge_po<unsigned short, 32, 4>",
+    "softmax_long_stats": "k_softmax_splitk_stats<unsigned short, true>",
+    "softmax_long_map": "k_softmax_splitk_map<unsigned short, unsigned short, true>",
 }
+SOFTMAX_LONG = (16, 1 << 22)
 ALGO_BYTES = {
     "short_sum": 1048576 * 48 * 4 + 1048576 * 4,
     "short_max": 1048576 * 48 * 4 + 1048576 * 4,
@@ -59,7 +66,14 @@ ALGO_BYTES = {
     "long_sum": 16 * (1 << 24) * 4 + 16 * 4,
     "long_max": 16 * (1 << 24) * 4 + 16 * 4,
     "merge": 8 * 32768 * 128 * 4 + 2 * 8 * 32768 * 4 + 32768 * 128 * 2,
+    # split-K softmax, per kernel: the statistics pass reads x and stores
+    # 16 x 64 (max, sum) pairs; the map pass reads the pairs and x, writes y
+    "softmax_long_stats": 16 * (1 << 22) * 2 + 16 * 64 * 8,
+    "softmax_long_map": 16 * (1 << 22) * 2 * 2 + 16 * 64 * 64 * 8,
 }
+# next-row operations as a whole: x read once and y written once
+NEXT_BYTES = {"softmax_long": 16 * (1 << 22) * 2 * 2}
+STEP_OPS = ("short_sum", "short_max", "softmax", "long_sum", "long_max", "merge")
 COPY_BYTES = 512 << 20
 
 
@@ -171,6 +185,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the operations outside the step (next_rows)")
     ap.add_argument("--only", default=None, help="comma list of ops to run (profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 512 MiB elementwise copy (negation) three times: "
@@ -235,6 +251,8 @@ def main():
     host["softmax"] = synth.softmax_rows()
     host["long_f"], host["long_i"] = synth.long_rows()
     host["merge"] = synth.lse_merge()
+    if not args.no_next:
+        host["softmax_long"] = synth.softmax_long_rows()
     log("inputs generated in %.1f s" % (time.time() - t0))
 
     sets = {"short": 5, "softmax": 4, "long_f": 1, "long_i": 1, "merge": 8}
@@ -250,6 +268,10 @@ def main():
     dx["merge"] = [(o, m, l)] + [(o.clone(), m.clone(), l.clone()) for _ in range(sets["merge"] - 1)]
     dx["merge_out"] = [torch.empty((8, 32, 128, 128), dtype=torch.bfloat16, device=dev)
                        for _ in range(sets["merge"])]
+    if not args.no_next:
+        base = gpu(host["softmax_long"])
+        dx["softmax_long"] = [base] + [base.clone() for _ in range(2)]
+        dx["softmax_long_out"] = [torch.empty_like(base) for _ in range(3)]
     y_short_sum = torch.empty(1048576, dtype=torch.float32, device=dev)
     y_short_max = torch.empty(1048576, dtype=torch.float32, device=dev)
     y_long_f = torch.empty(16, dtype=torch.float32, device=dev)
@@ -267,7 +289,13 @@ def main():
         "merge": lambda i: rr.splitk_lse_merge(*dx["merge"][i % 8], 1.0, torch.bfloat16,
                                                out=dx["merge_out"][i % 8]),
     }
-    names = list(ops) if not args.only else args.only.split(",")
+    next_ops = {
+        "softmax_long": lambda i: rr.softmax_rows(dx["softmax_long"][i % 3],
+                                                  out=dx["softmax_long_out"][i % 3]),
+    }
+    only = args.only.split(",") if args.only else None
+    names = [n for n in ops if only is None or n in only]
+    next_names = [] if args.no_next else [n for n in next_ops if only is None or n in only]
 
     # ------------------------------------------------------------ parity
     parity = "skipped"
@@ -277,8 +305,15 @@ def main():
         log("parity check on sampled rows")
         for n in names:
             ops[n](0)
+        for n in next_names:
+            next_ops[n](0)
         torch.cuda.synchronize()
         ok = True
+        if "softmax_long" in next_names:
+            pick = [0, SOFTMAX_LONG[0] - 1]
+            y = dx["softmax_long_out"][0][pick].cpu().view(torch.int16).numpy().view(np.uint16)
+            r = oracle.softmax_rows(np.ascontiguousarray(host["softmax_long"][pick]), "bf16")
+            ok &= bool(bf16_ulp_diff(y, r).max() <= 1)
         # sampled rows of the full-size outputs of the pass above (no extra launches)
         xs = host["short"][:4096]
         if "short_sum" in names:
@@ -327,6 +362,8 @@ def main():
 
     # Warmup with every launch instrumented: it also picks the dominant op.
     log("warmup %d steps" % args.warmup)
+    if not names:
+        sys.exit("bench.py: --only selected no operation of the step")
     warm = instrumented(max(args.warmup, 1), 0)
     dom = max(names, key=lambda n: sum(warm[n]) / len(warm[n]))
 
@@ -364,6 +401,39 @@ def main():
                      "GBps": round(B[n] / (mean * 1e-3) / 1e9, 1),
                      "pct_peak": round(100 * B[n] / (mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 1),
                      "timed_in": "timed region" if n == dom else "instrumented pass"}
+    # Operations outside the step: each timed alone with HIP events on the stream.
+    next_rows = {}
+    if next_names:
+        log("timing next-row operations")
+        for i in range(max(args.warmup, 1)):
+            for n in next_names:
+                next_ops[n](i)
+        reps = max(K, 10)
+        evs = {n: [] for n in next_names}
+        for i in range(reps):
+            for n in next_names:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                next_ops[n](i)
+                b.record(stream)
+                evs[n].append((a, b))
+        torch.cuda.synchronize()
+        for n in next_names:
+            ts = sorted(a.elapsed_time(b) for a, b in evs[n])
+            mean = sum(ts) / len(ts)
+            gbs = NEXT_BYTES[n] / (mean * 1e-3) / 1e9
+            next_rows[n] = {"ms_mean": round(mean, 5), "ms_median": round(ts[len(ts) // 2], 5),
+                            "ms_min": round(ts[0], 5), "bytes": NEXT_BYTES[n],
+                            "GBps": round(gbs, 1), "pct_peak": round(100 * gbs / PEAK_HBM_GBS, 1)}
+        if "softmax_long" in next_rows:
+            r, c = SOFTMAX_LONG
+            next_rows["softmax_long"].update({
+                "config": "bf16 softmax [%d, %d] -> bf16, split-K tier (G = 64)" % (r, c),
+                "kernels": [KERNEL_OF_OP["softmax_long_stats"], KERNEL_OF_OP["softmax_long_map"]],
+                "bytes_note": "bytes = x read once + y written once; the two-launch design reads "
+                              "x twice (%d bytes moved)" % (ALGO_BYTES["softmax_long_stats"]
+                                                            + ALGO_BYTES["softmax_long_map"])})
+
     step_bytes = sum(B[n] for n in names)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
@@ -430,6 +500,7 @@ def main():
                    "ops": names, "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBS, 1),
                    "step_bytes": step_bytes, "parity": parity},
         "per_op": per_op,
+        "next_rows": next_rows,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

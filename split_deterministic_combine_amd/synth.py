@@ -16,6 +16,7 @@ Workloads (sizes are the defaults; smaller sizes keep the distributions):
   long_rows    f32 uniform(-1, 1) and int32 uniform in [-2^30, 2^30], [16, 2^24]
   lse_merge    P = 8 partitions of O [8, 32, 128, 128] standard normal,
                m = 4 * standard normal, l = uniform(1, 4096), scale 1.0
+  softmax_long_rows  bf16 of 3 * standard normal, [16, 2^22] (split-K softmax)
 """
 import numpy as np
 
@@ -24,6 +25,7 @@ SEED_SHORT_ROWS = 2
 SEED_SOFTMAX_ROWS = 3
 SEED_LONG_ROWS = 4
 SEED_LSE_MERGE = 5
+SEED_SOFTMAX_LONG_ROWS = 6
 
 
 def _bf16_bits(x_f32):
@@ -63,6 +65,11 @@ def long_rows(seed=SEED_LONG_ROWS, rows=16, cols=1 << 24):
     xf -= np.float32(1.0)
     xi = rng.integers(-(2 ** 30), 2 ** 30, (rows, cols), endpoint=True, dtype=np.int32)
     return xf, xi
+
+
+def softmax_long_rows(seed=SEED_SOFTMAX_LONG_ROWS, rows=16, cols=1 << 22, std=3.0):
+    """Few very long softmax rows (fewer rows than compute units)."""
+    return normal_bf16(seed, (rows, cols), std)
 
 
 def lse_merge(seed=SEED_LSE_MERGE, P=8, batch=8, heads=32, q_rows=128, depth=128):
