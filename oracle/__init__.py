@@ -11,7 +11,7 @@ as ``numpy.uint16`` bit patterns.
 Sources: the Modular API pages "cluster_allreduce" (associative add/max/min
 over 32-bit values, folded in ascending rank order), "reduce" from
 algorithm.gpu.rowwise (the monoid fold along the last axis and the two-pass
-softmax) and "fa4_splitk_reduce_scatter_write" (the split-K (max, sum)
+softmax and layernorm) and "fa4_splitk_reduce_scatter_write" (the split-K (max, sum)
 reweighting of partial outputs into bf16 rows).  See rro.c for the readings.
 """
 import ctypes
@@ -41,6 +41,10 @@ def _load():
         lib.rro_splitk_lse_merge.argtypes = [vp, vp, vp, vp, i32, i64, i32, ctypes.c_float,
                                              ctypes.c_int]
         lib.rro_splitk_lse_merge.restype = ctypes.c_int
+        lib.rro_layernorm_rows.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                           ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_double]
+        lib.rro_layernorm_rows.restype = ctypes.c_int
         lib.rro_bf16_from_double.argtypes = [ctypes.c_double]
         lib.rro_bf16_from_double.restype = ctypes.c_uint16
         lib.rro_bf16_to_double.argtypes = [ctypes.c_uint16]
@@ -107,6 +111,50 @@ def softmax_rows(x, out_dtype="bf16", x_is_bf16=None):
     if rc:
         raise ValueError("rro_softmax_rows rejected its arguments")
     return y
+
+
+def _real_code(a, what):
+    if a.dtype == np.uint16:
+        return BF16
+    if a.dtype == np.float32:
+        return F32
+    raise TypeError("%s must be float32 or bf16 (uint16 bits)" % what)
+
+
+def layernorm_rows(x, gamma=None, beta=None, eps=1e-5, out_dtype="bf16"):
+    """Layer normalisation over the last axis (population variance).
+
+    ``x``: float32 or uint16 bf16 bits, 2-D.  ``gamma`` / ``beta``: [cols] of
+    one type (float32 or bf16 bits), or None for 1 / 0.  ``eps`` is taken as
+    the float32 value the GPU path receives.  Returns (y, mean, rstd): y as
+    float32 or uint16 bf16 bits, mean and rstd float32 [rows].
+    """
+    lib = _load()
+    xd = _real_code(x, "x")
+    rows, cols, ld = _rows_view(x)
+    wd = F32
+    ws = [w for w in (gamma, beta) if w is not None]
+    if ws:
+        wd = _real_code(ws[0], "gamma/beta")
+        for w in ws:
+            if _real_code(w, "gamma/beta") != wd or w.shape != (cols,):
+                raise ValueError("gamma and beta must share one type and have shape [cols]")
+    gamma = None if gamma is None else np.ascontiguousarray(gamma)
+    beta = None if beta is None else np.ascontiguousarray(beta)
+    if out_dtype == "bf16":
+        y = np.empty((rows, cols), dtype=np.uint16)
+        yd = BF16
+    else:
+        y = np.empty((rows, cols), dtype=np.float32)
+        yd = F32
+    mean = np.full(rows, np.nan, dtype=np.float32)
+    rstd = np.full(rows, np.nan, dtype=np.float32)
+    rc = lib.rro_layernorm_rows(_ptr(x), _ptr(y), None if gamma is None else _ptr(gamma),
+                                None if beta is None else _ptr(beta), _ptr(mean), _ptr(rstd),
+                                rows, cols, ld, cols, xd, yd, wd, float(np.float32(eps)))
+    if rc:
+        raise ValueError("rro_layernorm_rows rejected its arguments")
+    return y, mean, rstd
 
 
 def splitk_lse_merge(o, m, l, scale=1.0, out_dtype="bf16"):

@@ -28,6 +28,10 @@
  *     with the sign bit clear is above +inf, one with it set below -inf).
  *   - softmax pass 1 is (max, sum exp(x - max)), pass 2 is exp(x - max)/sum,
  *     rounded once from double to the output type.
+ *   - layernorm (named by [RW] as a two-pass algorithm: a statistics pass,
+ *     then a pure map) is the usual per-row normalisation: mean, population
+ *     variance (divide by n), rstd = 1 / sqrt(var + eps), then
+ *     y = (x - mean) * rstd * gamma + beta per column, rounded once.
  *   - the LSE merge takes normalised partials O_p with row statistics
  *     (m_p, l_p); weight w_p = exp(scale*(m_p - M)) * l_p over the non-empty
  *     partitions (l_p > 0 and m_p > -inf), M their largest m_p; the output is
@@ -251,6 +255,59 @@ int rro_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols,
             double e = exp(load_real(x, x_dtype, r * ld_x + j) - m);
             store_real(y, y_dtype, r * ld_y + j, e / s);
         }
+    }
+    return RRO_OK;
+}
+
+/* --------------------------------------------------------------- layernorm */
+
+/*
+ * [RW] description: layernorm is one of the two-pass algorithms -- pass 1
+ * reduces the row's statistics, pass 2 is a pure map over the row.  The
+ * page names it without a formula; this is the standard one:
+ *   mean = (sum_j x_j) / n
+ *   var  = (sum_j (x_j - mean)^2) / n          (population variance)
+ *   rstd = 1 / sqrt(var + eps)
+ *   y_j  = (x_j - mean) * rstd * gamma_j + beta_j
+ * gamma == NULL means gamma_j = 1, beta == NULL means beta_j = 0; both are
+ * [cols] of w_dtype.  mean_out / rstd_out (float [rows], may be NULL)
+ * receive mean and rstd rounded once to float.  cols == 0 writes nothing.
+ * Everything in double, each output rounded once.
+ */
+int rro_layernorm_rows(const void* x, void* y, const void* gamma, const void* beta,
+                       float* mean_out, float* rstd_out, int64_t rows, int64_t cols,
+                       int64_t ld_x, int64_t ld_y, int x_dtype, int y_dtype, int w_dtype,
+                       double eps)
+{
+    if (rows < 0 || cols < 0 || ld_x < cols || ld_y < cols)
+        return RRO_BAD;
+    if ((x_dtype != RRO_F32 && x_dtype != RRO_BF16) || (y_dtype != RRO_F32 && y_dtype != RRO_BF16) ||
+        (w_dtype != RRO_F32 && w_dtype != RRO_BF16))
+        return RRO_BAD;
+    for (int64_t r = 0; r < rows; ++r) {
+        if (cols == 0)
+            continue;
+        double sum = 0.0;
+        for (int64_t j = 0; j < cols; ++j)
+            sum += load_real(x, x_dtype, r * ld_x + j);
+        const double mean = sum / (double)cols;
+        double sq = 0.0;
+        for (int64_t j = 0; j < cols; ++j) {
+            const double d = load_real(x, x_dtype, r * ld_x + j) - mean;
+            sq += d * d;
+        }
+        const double var = sq / (double)cols;
+        const double rstd = 1.0 / sqrt(var + eps);
+        for (int64_t j = 0; j < cols; ++j) {
+            const double g = gamma ? load_real(gamma, w_dtype, j) : 1.0;
+            const double b = beta ? load_real(beta, w_dtype, j) : 0.0;
+            const double v = (load_real(x, x_dtype, r * ld_x + j) - mean) * rstd * g + b;
+            store_real(y, y_dtype, r * ld_y + j, v);
+        }
+        if (mean_out)
+            mean_out[r] = (float)mean;
+        if (rstd_out)
+            rstd_out[r] = (float)rstd;
     }
     return RRO_OK;
 }

@@ -277,6 +277,111 @@ def test_softmax_bf16_input_strided_and_empty():
     assert oracle.softmax_rows(np.zeros((3, 0), dtype=np.float32), "f32").shape == (3, 0)
 
 
+# ------------------------------------------------------------------ layernorm
+
+def _f32_ulp_close(got, want, ulps=1):
+    """|got - want| within `ulps` float32 ulps of want (NaN matches NaN)."""
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    both_nan = np.isnan(got) & np.isnan(want)
+    same_inf = np.isinf(want) & (got == want)
+    fin = np.isfinite(want)
+    ulp = np.zeros_like(want)
+    ulp[fin] = np.spacing(np.abs(want[fin]).astype(np.float32)).astype(np.float64)
+    ulp[fin & (want == 0)] = 2.0 ** -149
+    with np.errstate(invalid="ignore"):
+        close = np.abs(got - want) <= ulps * ulp
+    ok = both_nan | same_inf | (fin & close)
+    return bool(ok.all())
+
+
+def test_layernorm_golden_cases():
+    for line in _golden_lines("layernorm_small.txt"):
+        xs, eps, gs, bs, ys, ms, rs = [t.strip() for t in line.split("|")]
+        x = np.array([[_num(v) for v in xs.split(",")]], dtype=np.float32)
+        g = None if gs == "-" else np.array([_num(v) for v in gs.split(",")], dtype=np.float32)
+        b = None if bs == "-" else np.array([_num(v) for v in bs.split(",")], dtype=np.float32)
+        want = np.array([_num(v) for v in ys.split(",")])
+        y, mean, rstd = oracle.layernorm_rows(x, g, b, float(eps), "f32")
+        assert _f32_ulp_close(y[0], want), (line, y)
+        assert _f32_ulp_close(mean, [_num(ms)]), (line, mean)
+        assert _f32_ulp_close(rstd, [_num(rs)]), (line, rstd)
+        # bf16 output: the same values rounded once
+        yb, _, _ = oracle.layernorm_rows(x, g, b, float(eps), "bf16")
+        wb = [round_to_bf16(Fraction(v)) if math.isfinite(v) else None for v in want]
+        for got, w in zip(yb[0], wb):
+            if w is None:
+                assert (got & 0x7F80) == 0x7F80 and (got & 0x7F), line
+            else:
+                assert int(got) == w, line
+
+
+def test_layernorm_matches_torch_double_layer_norm():
+    x = synth.normal_f32(401, (9, 777), std=2.0) + np.float32(3.0)
+    g = synth.normal_f32(402, (777,))
+    b = synth.normal_f32(403, (777,))
+    for eps in (1e-5, 0.5):
+        ref = torch.nn.functional.layer_norm(torch.from_numpy(x).double(), (777,),
+                                             torch.from_numpy(g).double(),
+                                             torch.from_numpy(b).double(),
+                                             float(np.float32(eps))).numpy()
+        y, _, _ = oracle.layernorm_rows(x, g, b, eps, "f32")
+        assert _f32_ulp_close(y, ref)
+        yb, _, _ = oracle.layernorm_rows(x, g, b, eps, "bf16")
+        want = np.array([round_to_bf16(Fraction(float(v))) for v in ref[:2].ravel()]).reshape(2, -1)
+        assert bf16_ulp_diff(yb[:2], want).max() == 0
+
+
+def test_layernorm_statistics_match_numpy():
+    x = synth.normal_bf16(404, (7, 1000), std=5.0)
+    xd = oracle.bf16_to_double(x)
+    _, mean, rstd = oracle.layernorm_rows(x, eps=1e-3, out_dtype="f32")
+    assert _f32_ulp_close(mean, xd.mean(axis=1))
+    assert _f32_ulp_close(rstd, 1.0 / np.sqrt(xd.var(axis=1) + float(np.float32(1e-3))))
+
+
+def test_layernorm_shift_and_scale_invariance_exact():
+    # multiples of 1/8 over 64 columns: sums, the mean and the squared
+    # deviations are exact in double, so a shift by an integer, or a scale by
+    # a power of two with eps = 0, leaves every output bit unchanged
+    k = np.random.default_rng(405).integers(-64, 64, (5, 64))
+    x = (k / 8.0).astype(np.float32)
+    y0, _, _ = oracle.layernorm_rows(x, eps=0.0, out_dtype="f32")
+    for c in (1.0, -7.0):
+        y, _, _ = oracle.layernorm_rows(x + np.float32(c), eps=0.0, out_dtype="f32")
+        assert np.array_equal(y, y0)
+    y, _, _ = oracle.layernorm_rows(x * np.float32(4.0), eps=0.0, out_dtype="f32")
+    assert np.array_equal(y, y0)
+
+
+def test_layernorm_affine_is_applied_per_column():
+    x = synth.normal_f32(406, (3, 50))
+    g = synth.uniform_f32(407, (50,), 0.5, 2.0)
+    b = synth.uniform_f32(408, (50,), -1.0, 1.0)
+    plain, _, _ = oracle.layernorm_rows(x, eps=1e-5, out_dtype="f32")
+    y, _, _ = oracle.layernorm_rows(x, g, b, eps=1e-5, out_dtype="f32")
+    want = plain.astype(np.float64) * g + b
+    assert np.max(np.abs(y - want)) <= 4e-7 * (1 + np.abs(want).max())
+    # rows are standardised: mean 0 and mean square var / (var + eps) ~ 1
+    assert np.all(np.abs(plain.astype(np.float64).mean(axis=1)) < 1e-6)
+    assert np.all(np.abs((plain.astype(np.float64) ** 2).mean(axis=1) - 1) < 1e-4)
+
+
+def test_layernorm_bf16_weights_and_degenerate_sizes():
+    x = synth.normal_f32(409, (4, 33))
+    g = synth.normal_bf16(410, (33,), 1.0)
+    b = synth.normal_bf16(411, (33,), 1.0)
+    y, _, _ = oracle.layernorm_rows(x, g, b, 1e-5, "f32")
+    ref = torch.nn.functional.layer_norm(
+        torch.from_numpy(x).double(), (33,), torch.from_numpy(oracle.bf16_to_double(g)),
+        torch.from_numpy(oracle.bf16_to_double(b)), float(np.float32(1e-5))).numpy()
+    assert _f32_ulp_close(y, ref)
+    y, mean, rstd = oracle.layernorm_rows(np.zeros((3, 0), dtype=np.float32), out_dtype="f32")
+    assert y.shape == (3, 0) and np.isnan(mean).all() and np.isnan(rstd).all()  # nothing written
+    y, mean, _ = oracle.layernorm_rows(np.zeros((0, 5), dtype=np.float32), out_dtype="f32")
+    assert y.shape == (0, 5) and mean.shape == (0,)
+
+
 # ------------------------------------------------------------------ LSE merge
 
 def _parse_floats(s):
