@@ -1,13 +1,15 @@
 /*
  * rr.h -- deterministic row reductions on AMD Instinct MI355X (gfx950).
  *
- * A C ABI over hand-written HIP kernels.  Three operations:
+ * A C ABI over hand-written HIP kernels.  Four operations:
  *
  *   rr_reduce_rows       sum / max / min of every row over its last axis, on
  *                        float32 or int32 values, through one of five tiers
  *                        (wave, block, tiled, serial, split-K).
  *   rr_softmax_rows      two-pass softmax of every row (pass 1: the online
  *                        (max, sum) monoid; pass 2: a map that writes y).
+ *   rr_layernorm_rows    two-pass layer normalisation of every row (pass 1:
+ *                        mean and variance; pass 2: a map that writes y).
  *   rr_splitk_lse_merge  combine P split-K partial attention outputs by their
  *                        per-row (max, sum) statistics into bf16 or f32 rows.
  *
@@ -23,7 +25,8 @@
  *       the result is packed to bf16; every partition, empty or not, joins.
  *
  * Conventions for every call below
- *   - Pointers named x, y, o_part, m_part, l_part, out and workspace are
+ *   - Pointers named x, y, gamma, beta, mean_out, rstd_out, o_part, m_part,
+ *     l_part, out and workspace are
  *     DEVICE pointers on the current HIP device.  The caller owns them.  The
  *     library never allocates or frees device memory and never synchronises.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
@@ -76,7 +79,7 @@ typedef enum {
     RR_TIER_SPLITK = 5  /* several workgroups per row, rank-order fold of partials */
 } rr_tier;
 
-typedef enum { RR_KIND_REDUCE = 0, RR_KIND_SOFTMAX = 1 } rr_kind;
+typedef enum { RR_KIND_REDUCE = 0, RR_KIND_SOFTMAX = 1, RR_KIND_LAYERNORM = 2 } rr_kind;
 
 /* Rows owned by one thread in the tiled tier (the page's emit_tile_width). */
 #define RR_TILED_ROWS 4
@@ -129,6 +132,16 @@ rr_status rr_plan_reduce(int64_t rows, int64_t cols, int64_t ld, rr_dtype dtype,
  */
 rr_status rr_plan_softmax(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype y_dtype,
                           rr_tier tier, int32_t cu_count, rr_plan* plan_out);
+
+/*
+ * rr_plan_layernorm -- tier selection for rr_layernorm_rows: the softmax rule.
+ * BLOCK keeps rows of whole 16-byte chunks, up to 8 chunks per thread of 256,
+ * in registers on persistent workgroups (2 per CU); longer or unaligned rows
+ * are read twice.  SPLITK tiles are 4 * 256 16-byte chunks; its workspace is
+ * rows * G * 16 bytes (workspace_bytes).
+ */
+rr_status rr_plan_layernorm(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype y_dtype,
+                            rr_dtype w_dtype, rr_tier tier, int32_t cu_count, rr_plan* plan_out);
 
 /*
  * rr_reduce_rows -- y[r] = fold of x[r*ld + 0 .. r*ld + cols-1].
@@ -196,6 +209,49 @@ rr_status rr_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols, in
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * rr_layernorm_rows -- layer normalisation of every row over its last axis.
+ * "reduce" (algorithm.gpu.rowwise), description: layernorm is a two-pass
+ * algorithm -- pass 1 reduces the row's statistics, each state combined
+ * across threads on its own, pass 2 is a pure map.  The page gives no
+ * formula; the standard one is used:
+ *   mean_r = sum_j x[r][j] / cols
+ *   var_r  = sum_j (x[r][j] - mean_r)^2 / cols        (population variance)
+ *   rstd_r = 1 / sqrt(var_r + eps)
+ *   y[r][j] = (x[r][j] - mean_r) * rstd_r * gamma[j] + beta[j]
+ *
+ *   x        device, [rows][ld_x] of x_dtype (RR_BF16 or RR_F32)
+ *   y        device, [rows][ld_y] of y_dtype (RR_BF16 or RR_F32); may alias x
+ *            only when ld_y == ld_x and the dtypes match
+ *   gamma, beta  device, [cols] of w_dtype (RR_F32 or RR_BF16), or NULL
+ *            (gamma 1, beta 0)
+ *   mean_out, rstd_out  device, float [rows] (written), or NULL; must not
+ *            overlap x or y
+ *   eps      finite and >= 0 (else RR_ERR_SHAPE)
+ *   tier     RR_TIER_AUTO, WAVE, BLOCK, TILED, SERIAL or SPLITK
+ *   workspace, workspace_bytes
+ *            device scratch for RR_TIER_SPLITK: rows * G * 16 bytes, 8-byte
+ *            aligned (rr_workspace_bytes with RR_KIND_LAYERNORM); no initial
+ *            contents needed.  Ignored by the other tiers (may be NULL).  As
+ *            for rr_softmax_rows, a buffer used here must be zeroed before it
+ *            serves rr_reduce_rows.
+ * Statistics are formed in double (rows held in registers: the sum of x,
+ * then the sum of squared deviations from the mean; streamed rows: sums of
+ * x - x[r][0] and its square, whose cancellation Samuelson's inequality
+ * bounds by log2(cols) bits), each combined over a fixed-shape tree so the
+ * result does not change from run to run.  The map runs in float; bf16
+ * results are rounded to nearest even.  Split-K (rows < CU and long rows):
+ * G workgroups per row store their two sums, then every workgroup of the map
+ * pass sums its row's G pairs over a fixed tree ("cluster_allreduce",
+ * description: the all-gather variant) and maps its tiles.  rows == 0 or
+ * cols == 0 is a no-op (nothing is written).
+ */
+rr_status rr_layernorm_rows(const void* x, void* y, const void* gamma, const void* beta,
+                            float* mean_out, float* rstd_out, int64_t rows, int64_t cols,
+                            int64_t ld_x, int64_t ld_y, rr_dtype x_dtype, rr_dtype y_dtype,
+                            rr_dtype w_dtype, float eps, rr_tier tier, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
  * rr_splitk_lse_merge -- combine P split-K partitions of an attention output.
  * "fa4_splitk_reduce_scatter_write", the per-band steps: each partition's
  * output is scaled by its weight w[b], the partitions are accumulated, and
@@ -221,8 +277,9 @@ rr_status rr_splitk_lse_merge(const float* o_part, const float* m_part, const fl
                               void* out, int32_t P, int64_t rows, int32_t depth, float scale,
                               rr_dtype out_dtype, void* stream);
 
-/* Bytes of workspace rr_reduce_rows (RR_KIND_REDUCE) or rr_softmax_rows
- * (RR_KIND_SOFTMAX, dtype = x_dtype) needs for this shape on the current
+/* Bytes of workspace rr_reduce_rows (RR_KIND_REDUCE), rr_softmax_rows
+ * (RR_KIND_SOFTMAX, dtype = x_dtype) or rr_layernorm_rows (RR_KIND_LAYERNORM,
+ * dtype = x_dtype) needs for this shape on the current
  * device (0 unless the plan is split-K). */
 rr_status rr_workspace_bytes(rr_kind kind, int64_t rows, int64_t cols, rr_dtype dtype,
                              rr_op op, rr_tier tier, size_t* bytes_out);

@@ -9,6 +9,7 @@ the first call raises.
 Operations (names as in the C ABI):
   reduce_rows        sum / max / min over the last axis (float32, int32)
   softmax_rows       two-pass softmax over the last axis (bf16 / float32)
+  layernorm_rows     two-pass layer normalisation over the last axis
   splitk_lse_merge   merge of P split-K partial attention outputs by their
                      per-row (max, sum) statistics
 """
@@ -19,8 +20,8 @@ import threading
 import torch
 
 __all__ = [
-    "RRError", "reduce_rows", "softmax_rows", "splitk_lse_merge", "plan_reduce",
-    "plan_softmax", "select_tier", "workspace_bytes", "workspace_reset", "device_cu_count",
+    "RRError", "reduce_rows", "softmax_rows", "layernorm_rows", "splitk_lse_merge",
+    "plan_reduce", "plan_softmax", "plan_layernorm", "select_tier", "workspace_bytes", "workspace_reset", "device_cu_count",
     "version", "lib_path", "TIERS", "OPS",
 ]
 
@@ -32,7 +33,7 @@ _DTYPES = {torch.float32: 0, torch.int32: 1, torch.bfloat16: 2}
 OPS = {"sum": 0, "max": 1, "min": 2}
 TIERS = {"auto": 0, "wave": 1, "block": 2, "tiled": 3, "serial": 4, "splitk": 5}
 TIER_NAMES = {v: k for k, v in TIERS.items()}
-KIND_REDUCE, KIND_SOFTMAX = 0, 1
+KIND_REDUCE, KIND_SOFTMAX, KIND_LAYERNORM = 0, 1, 2
 
 
 class RRError(RuntimeError):
@@ -76,6 +77,9 @@ def _load():
         lib.rr_softmax_rows.argtypes = [vp, vp, i64, i64, i64, i64, st, st, st, vp,
                                         ctypes.c_size_t, vp]
         lib.rr_splitk_lse_merge.argtypes = [vp, vp, vp, vp, i32, i64, i32, ctypes.c_float, st, vp]
+        lib.rr_layernorm_rows.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, st, st, st,
+                                          ctypes.c_float, st, vp, ctypes.c_size_t, vp]
+        lib.rr_plan_layernorm.argtypes = [i64, i64, st, st, st, st, i32, ctypes.POINTER(_Plan)]
         lib.rr_plan_reduce.argtypes = [i64, i64, i64, st, st, st, i32, ctypes.POINTER(_Plan)]
         lib.rr_plan_softmax.argtypes = [i64, i64, st, st, st, i32, ctypes.POINTER(_Plan)]
         lib.rr_workspace_bytes.argtypes = [st, i64, i64, st, st, st, ctypes.POINTER(ctypes.c_size_t)]
@@ -88,7 +92,8 @@ def _load():
         lib.rr_test_set_splitk_skew.argtypes = [i32]
         lib.rr_test_set_splitk_skew.restype = None
         for name in ("rr_reduce_rows", "rr_softmax_rows", "rr_splitk_lse_merge", "rr_plan_reduce",
-                     "rr_plan_softmax", "rr_workspace_bytes", "rr_select_tier",
+                     "rr_plan_softmax", "rr_layernorm_rows", "rr_plan_layernorm",
+                     "rr_workspace_bytes", "rr_select_tier",
                      "rr_workspace_reset", "rr_device_cu_count"):
             getattr(lib, name).restype = st
         _lib = lib
@@ -255,6 +260,70 @@ def softmax_rows(x, out_dtype=None, tier="auto", out=None):
     return out
 
 
+def _layernorm_workspace_need(rows, cols, xdt, ydt, wdt, tier, cu):
+    """Split-K workspace bytes of a layernorm (host-only plan, cached)."""
+    key = ("layernorm", rows, cols, xdt, ydt, wdt, tier, cu)
+    n = _ws_need.get(key)
+    if n is None:
+        plan = _Plan()
+        _check(_load().rr_plan_layernorm(rows, cols, xdt, ydt, wdt, tier, cu, ctypes.byref(plan)))
+        n = _ws_need[key] = plan.workspace_bytes
+    return n
+
+
+def _vector_arg(t, n, dtypes, name):
+    """Device pointer of an optional contiguous [n] tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if t.dtype not in dtypes or t.numel() != n or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous tensor of %d elements of %s" % (
+            name, n, " or ".join(str(d) for d in dtypes)))
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def layernorm_rows(x, gamma=None, beta=None, eps=1e-5, out_dtype=None, tier="auto", out=None,
+                   mean_out=None, rstd_out=None):
+    """Layer normalisation of every row of ``x`` over its last axis.
+
+    y = (x - mean) / sqrt(var + eps) * gamma + beta with the population
+    variance; ``x`` is bfloat16 or float32, ``gamma`` / ``beta`` are [cols]
+    (one dtype, float32 or bfloat16) or None.  ``mean_out`` / ``rstd_out``:
+    optional float32 tensors of ``x.shape[:-1]`` elements that receive the
+    row statistics.  Returns ``out``.
+    """
+    lib = _load()
+    x2, rows, cols, ld_x = _as_rows(x)
+    out_dtype = x.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty(x.shape, dtype=out_dtype, device=x.device)
+    if out.dtype != out_dtype or out.shape != x.shape:
+        raise ValueError("out must be a %s tensor of shape %s" % (out_dtype, tuple(x.shape)))
+    y2, _, _, ld_y = _as_rows(out, "out")
+    wts = [w for w in (gamma, beta) if w is not None]
+    w_dtype = wts[0].dtype if wts else torch.float32
+    if any(w.dtype != w_dtype for w in wts):
+        raise ValueError("gamma and beta must have the same dtype")
+    wdt = _dtype_code(w_dtype)
+    g_ptr = _vector_arg(gamma, cols, (torch.float32, torch.bfloat16), "gamma")
+    b_ptr = _vector_arg(beta, cols, (torch.float32, torch.bfloat16), "beta")
+    m_ptr = _vector_arg(mean_out, rows, (torch.float32,), "mean_out")
+    r_ptr = _vector_arg(rstd_out, rows, (torch.float32,), "rstd_out")
+    xdt, ydt, t = _dtype_code(x.dtype), _dtype_code(out_dtype), TIERS[tier]
+    with _OnDevice(x.device):
+        stream = _stream_ptr(x.device)
+        need = _layernorm_workspace_need(rows, cols, xdt, ydt, wdt, t, _cu_count(x.device))
+        ws_ptr, ws_len = None, 0
+        if need:
+            ws = _workspace("layernorm", x.device, stream.value, need)
+            ws_ptr, ws_len = ctypes.c_void_p(ws.data_ptr()), ws.numel()
+        _check(lib.rr_layernorm_rows(ctypes.c_void_p(x2.data_ptr()), ctypes.c_void_p(y2.data_ptr()),
+                                     g_ptr, b_ptr, m_ptr, r_ptr, rows, cols, ld_x, ld_y, xdt, ydt,
+                                     wdt, float(eps), t, ws_ptr, ws_len, stream))
+    return out
+
+
 def splitk_lse_merge(o_part, m_part, l_part, scale=1.0, out_dtype=torch.bfloat16, out=None):
     """Merge P split-K partitions: o_part [P, *rows, depth], m_part / l_part [P, *rows].
 
@@ -312,11 +381,22 @@ def plan_softmax(rows, cols, x_dtype=torch.bfloat16, y_dtype=None, tier="auto", 
     return _plan_dict(plan)
 
 
+def plan_layernorm(rows, cols, x_dtype=torch.bfloat16, y_dtype=None, w_dtype=torch.float32,
+                   tier="auto", cu_count=256):
+    """Host-only launch plan of rr_layernorm_rows (needs no GPU)."""
+    lib = _load()
+    plan = _Plan()
+    y_dtype = x_dtype if y_dtype is None else y_dtype
+    _check(lib.rr_plan_layernorm(rows, cols, _dtype_code(x_dtype), _dtype_code(y_dtype),
+                                 _dtype_code(w_dtype), TIERS[tier], cu_count, ctypes.byref(plan)))
+    return _plan_dict(plan)
+
+
 def select_tier(kind, rows, cols, dtype=torch.float32, op="sum"):
     """Tier AUTO picks on the current device; kind is "reduce" or "softmax"."""
     lib = _load()
     t = ctypes.c_int(0)
-    k = {"reduce": KIND_REDUCE, "softmax": KIND_SOFTMAX}[kind]
+    k = {"reduce": KIND_REDUCE, "softmax": KIND_SOFTMAX, "layernorm": KIND_LAYERNORM}[kind]
     _check(lib.rr_select_tier(k, rows, cols, _dtype_code(dtype), OPS[op], ctypes.byref(t)))
     return TIER_NAMES[t.value]
 

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <math.h>
 
 #include "../../include/rr.h"
 #include "../../include/rr_test.h"
@@ -111,6 +112,38 @@ extern "C" rr_status rr_softmax_rows(const void* x, void* y, int64_t rows, int64
     return rr::launch_softmax(p, a);
 }
 
+extern "C" rr_status rr_layernorm_rows(const void* x, void* y, const void* gamma,
+                                       const void* beta, float* mean_out, float* rstd_out,
+                                       int64_t rows, int64_t cols, int64_t ld_x, int64_t ld_y,
+                                       rr_dtype x_dtype, rr_dtype y_dtype, rr_dtype w_dtype,
+                                       float eps, rr_tier tier, void* workspace,
+                                       size_t workspace_bytes, void* stream)
+{
+    rr_plan p;
+    rr_status st = rr::plan_layernorm(rows, cols, x_dtype, y_dtype, w_dtype, tier, 1, true, &p);
+    if (st != RR_OK) return st;
+    if (ld_x < cols || ld_y < cols) return RR_ERR_SHAPE;
+    if (!(eps >= 0.0f) || isinf(eps)) return RR_ERR_SHAPE;
+    if (rows == 0 || cols == 0) return RR_OK;
+    if (!x || !y) return RR_ERR_NULL;
+    if (x == y && (ld_x != ld_y || x_dtype != y_dtype)) return RR_ERR_SHAPE;
+    int32_t cu = 0;
+    if ((st = current_cu(&cu)) != RR_OK) return st;
+    const bool vec = rows_aligned16(x, ld_x, rows, elem_size(x_dtype)) &&
+                     rows_aligned16(y, ld_y, rows, elem_size(y_dtype)) &&
+                     (!gamma || aligned(gamma, 16)) && (!beta || aligned(beta, 16));
+    if ((st = rr::plan_layernorm(rows, cols, x_dtype, y_dtype, w_dtype, tier, cu, vec, &p)) !=
+        RR_OK)
+        return st;
+    if (p.tier == RR_TIER_SPLITK) {
+        if (!workspace || workspace_bytes < p.workspace_bytes || !aligned(workspace, 8))
+            return RR_ERR_WORKSPACE;
+    }
+    rr::LayernormLaunch a{x, y, gamma, beta, mean_out, rstd_out, rows, cols, ld_x, ld_y,
+                          x_dtype, y_dtype, w_dtype, eps, vec, workspace, as_stream(stream)};
+    return rr::launch_layernorm(p, a);
+}
+
 extern "C" rr_status rr_splitk_lse_merge(const float* o_part, const float* m_part,
                                          const float* l_part, void* out, int32_t P, int64_t rows,
                                          int32_t depth, float scale, rr_dtype out_dtype,
@@ -131,15 +164,18 @@ extern "C" rr_status rr_workspace_bytes(rr_kind kind, int64_t rows, int64_t cols
                                         rr_op op, rr_tier tier, size_t* bytes_out)
 {
     if (!bytes_out) return RR_ERR_NULL;
-    if (kind != RR_KIND_REDUCE && kind != RR_KIND_SOFTMAX) return RR_ERR_TIER;
+    if (kind != RR_KIND_REDUCE && kind != RR_KIND_SOFTMAX && kind != RR_KIND_LAYERNORM)
+        return RR_ERR_TIER;
     int32_t cu = 0;
     rr_status st = current_cu(&cu);
     if (st != RR_OK) return st;
     rr_plan p;
     if (kind == RR_KIND_REDUCE)
         st = rr::plan_reduce(rows, cols, cols, dtype, op, tier, cu, true, &p);
-    else
+    else if (kind == RR_KIND_SOFTMAX)
         st = rr::plan_softmax(rows, cols, dtype, dtype, tier, cu, true, &p);
+    else
+        st = rr::plan_layernorm(rows, cols, dtype, dtype, RR_F32, tier, cu, true, &p);
     if (st != RR_OK) return st;
     *bytes_out = (size_t)p.workspace_bytes;
     return RR_OK;
@@ -157,6 +193,8 @@ extern "C" rr_status rr_select_tier(rr_kind kind, int64_t rows, int64_t cols, rr
         st = rr::plan_reduce(rows, cols, cols, dtype, op, RR_TIER_AUTO, cu, true, &p);
     else if (kind == RR_KIND_SOFTMAX)
         st = rr::plan_softmax(rows, cols, dtype, dtype, RR_TIER_AUTO, cu, true, &p);
+    else if (kind == RR_KIND_LAYERNORM)
+        st = rr::plan_layernorm(rows, cols, dtype, dtype, RR_F32, RR_TIER_AUTO, cu, true, &p);
     else
         return RR_ERR_TIER;
     if (st != RR_OK) return st;

@@ -47,6 +47,13 @@ constexpr int64_t kSoftmaxWideMinChunks = (int64_t)kBlockThreads * kSoftmaxMaxCh
 // Split-K softmax: 16-byte chunks per thread per tile (a tile is one load
 // round of the workgroup).
 constexpr int kSoftmaxSplitKUnroll = 4;
+// Layernorm: rows of up to kLnMaxChunks 16-byte chunks per thread (256
+// threads) stay in registers on persistent workgroups, kLnRowBlocksPerCU per
+// CU; longer rows stream twice.  Split-K tiles are kLnSplitKUnroll chunks per
+// thread.
+constexpr int kLnMaxChunks = 8;
+constexpr int kLnRowBlocksPerCU = 2;
+constexpr int kLnSplitKUnroll = 4;
 
 // LSE merge: partitions staged per batch of loads, and workgroup size.
 constexpr int kMergeBatch = 8;

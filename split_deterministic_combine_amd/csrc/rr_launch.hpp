@@ -30,6 +30,21 @@ struct SoftmaxLaunch {
     hipStream_t stream;
 };
 
+struct LayernormLaunch {
+    const void* x;
+    void* y;
+    const void* gamma;    // [cols] of w_dtype, or NULL (1)
+    const void* beta;     // [cols] of w_dtype, or NULL (0)
+    float* mean_out;      // [rows] or NULL
+    float* rstd_out;      // [rows] or NULL
+    int64_t rows, cols, ld_x, ld_y;
+    rr_dtype x_dtype, y_dtype, w_dtype;
+    float eps;
+    bool vec;
+    void* workspace;      // split-K only
+    hipStream_t stream;
+};
+
 struct MergeLaunch {
     const float* o;
     const float* m;
@@ -48,6 +63,7 @@ rr_status launch_reduce(const rr_plan& plan, const ReduceLaunch& a);
 rr_status launch_reduce_identity(const ReduceLaunch& a);  // cols == 0
 rr_status launch_softmax(const rr_plan& plan, const SoftmaxLaunch& a);
 rr_status launch_merge(const MergeLaunch& a);
+rr_status launch_layernorm(const rr_plan& plan, const LayernormLaunch& a);
 rr_status launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
 
 }  // namespace rr

@@ -1,0 +1,651 @@
+// rr_layernorm.hip -- two-pass layer normalisation over the last axis, gfx950.
+//
+// "reduce" (algorithm.gpu.rowwise), description: layernorm is one of the
+// two-pass algorithms -- pass 1 reduces the row's statistics, each state
+// combined across threads on its own, and pass 2 is a pure map:
+//   mean = sum x / n,  var = sum (x - mean)^2 / n,  rstd = 1 / sqrt(var + eps)
+//   y = (x - mean) * rstd * gamma + beta      (gamma / beta per column)
+//
+// Statistics, by how much of the row a thread holds:
+//   * rows in registers (block tier up to kLnMaxChunks 16-byte chunks per
+//     thread, wave tier): the exact two-pass form.  The sum of x is taken in
+//     double; then every thread forms d = (x - mean_f) - c, with mean_f the
+//     float mean and c = (float)(mean - mean_f), and the sum of d^2 is taken
+//     (float inside a chunk, double across chunks and threads).  d stays in
+//     registers for the map.
+//   * rows streamed from memory (long rows, split-K): one statistics read with
+//     sums shifted by the row's first element K: s1 = sum (x - K),
+//     s2 = sum (x - K)^2, in double.  Then mean = K + s1/n and
+//     n var = s2 - s1^2/n.  Since K is an element of the row,
+//     |K - mean| <= sqrt(n - 1) * sd (Samuelson's inequality), so the
+//     cancellation costs at most log2(n) bits of the double's 53.
+// Each state is combined across threads by its own fixed-shape sum
+// (wave DPP tree, then waves in order), so every run gives the same bits.
+#include <hip/hip_runtime.h>
+
+#include "rr_config.hpp"
+#include "rr_device.hpp"
+#include "rr_launch.hpp"
+#include "rr_launch_util.hpp"
+#include "rr_rowio.hpp"
+
+namespace rr {
+
+// Per-column weights: gamma (default 1) or beta (default 0), float or bf16.
+struct Weights {
+    const void* p;  // NULL: every column takes `dflt`
+    bool bf16;
+    float dflt;
+};
+
+// Row statistics from the two reduced states.
+struct LnRow {
+    double mean;
+    float rstd;
+};
+
+namespace {
+
+__device__ __forceinline__ float weight_one(const Weights& w, int64_t j)
+{
+    if (!w.p)
+        return w.dflt;
+    return w.bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(w.p)[j])
+                  : static_cast<const float*>(w.p)[j];
+}
+
+// E weights of columns j0 .. j0+E-1 (past `cols`: the default).  With VEC the
+// base is 16-byte aligned and a whole chunk inside the row is loaded with
+// vector loads (cached: every row reads the same weights).
+template <int E, bool VEC>
+__device__ __forceinline__ void load_weights(const Weights& w, int64_t j0, int64_t cols, float* o)
+{
+    if (!w.p) {
+#pragma unroll
+        for (int i = 0; i < E; ++i)
+            o[i] = w.dflt;
+        return;
+    }
+    if constexpr (VEC) {
+        if (j0 + E <= cols) {
+            if (w.bf16) {
+                const uint16_t* p = static_cast<const uint16_t*>(w.p) + j0;
+                if constexpr (E == 8) {
+                    const uint4 u = *reinterpret_cast<const uint4*>(p);
+                    o[0] = bf16_lo(u.x); o[1] = bf16_hi(u.x);
+                    o[2] = bf16_lo(u.y); o[3] = bf16_hi(u.y);
+                    o[4] = bf16_lo(u.z); o[5] = bf16_hi(u.z);
+                    o[6] = bf16_lo(u.w); o[7] = bf16_hi(u.w);
+                } else {
+                    static_assert(E == 4, "chunks of 4 or 8 elements");
+                    const uint2 u = *reinterpret_cast<const uint2*>(p);
+                    o[0] = bf16_lo(u.x); o[1] = bf16_hi(u.x);
+                    o[2] = bf16_lo(u.y); o[3] = bf16_hi(u.y);
+                }
+            } else {
+                const float* p = static_cast<const float*>(w.p) + j0;
+#pragma unroll
+                for (int k = 0; k < E; k += 4) {
+                    const uint4 u = *reinterpret_cast<const uint4*>(p + k);
+                    o[k] = __uint_as_float(u.x); o[k + 1] = __uint_as_float(u.y);
+                    o[k + 2] = __uint_as_float(u.z); o[k + 3] = __uint_as_float(u.w);
+                }
+            }
+            return;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < E; ++i)
+        o[i] = j0 + i < cols ? weight_one(w, j0 + i) : w.dflt;
+}
+
+// y = d * rstd * gamma + beta on E values of columns j0.. (in place).
+template <int E, bool VEC>
+__device__ __forceinline__ void affine(float* d, float rstd, const Weights& g, const Weights& b,
+                                       int64_t j0, int64_t cols)
+{
+    if (!g.p && !b.p) {
+#pragma unroll
+        for (int i = 0; i < E; ++i)
+            d[i] *= rstd;
+        return;
+    }
+    float gw[E], bw[E];
+    load_weights<E, VEC>(g, j0, cols, gw);
+    load_weights<E, VEC>(b, j0, cols, bw);
+#pragma unroll
+    for (int i = 0; i < E; ++i)
+        d[i] = __builtin_fmaf(d[i] * rstd, gw[i], bw[i]);
+}
+
+__device__ __forceinline__ float rstd_of(double m2, int64_t n, float eps)
+{
+    const double var = (m2 > 0.0 ? m2 : 0.0) / (double)n;
+    return (float)(1.0 / sqrt(var + (double)eps));
+}
+
+// Shifted sums (s1 = sum (x - K), s2 = sum (x - K)^2) to (mean, rstd).
+__device__ __forceinline__ LnRow row_from_shifted(double K, double s1, double s2, int64_t n,
+                                                  float eps)
+{
+    const double dn = (double)n;
+    return LnRow{K + s1 / dn, rstd_of(s2 - s1 * (s1 / dn), n, eps)};
+}
+
+// The centred value of x: (x - mean_f) - c with mean_f = (float)mean and
+// c = (float)(mean - mean_f).
+struct Centre {
+    float mf, c;
+    __device__ explicit Centre(double mean)
+        : mf((float)mean), c((float)(mean - (double)(float)mean)) {}
+    __device__ float operator()(float x) const { return (x - mf) - c; }
+};
+
+__device__ __forceinline__ void write_stats(float* mean_out, float* rstd_out, int64_t r,
+                                            const LnRow& st)
+{
+    if (mean_out)
+        mean_out[r] = (float)st.mean;
+    if (rstd_out)
+        rstd_out[r] = st.rstd;
+}
+
+// ------------------------------------------------ block tier, row in registers
+// One row at a time per workgroup; the thread's chunks are k = 0 .. NCH-1 at
+// columns (threadIdx.x + k * NT) * E.  `valid(k, i)` says whether element i
+// of chunk k lies in the row; invalid elements hold 0 and are left out.
+template <int NCH, int E, int NT, class Valid>
+__device__ __forceinline__ LnRow row_stats_in_registers(float* v, int64_t cols, float eps,
+                                                        double* slot_a, double* slot_b,
+                                                        Valid valid)
+{
+    double s = 0.0;  // invalid elements hold 0
+#pragma unroll
+    for (int i = 0; i < NCH * E; ++i)
+        s += (double)v[i];
+    const double S = block_reduce<SumF32, NT>(s, slot_a);
+    const double mean = S / (double)cols;
+    const Centre centre(mean);
+    double q = 0.0;
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+        float cq = 0.0f;
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+            const float d = valid(k, i) ? centre(v[k * E + i]) : 0.0f;
+            v[k * E + i] = d;
+            cq = __builtin_fmaf(d, d, cq);
+        }
+        q += (double)cq;
+    }
+    const double Q = block_reduce<SumF32, NT>(q, slot_b);
+    return LnRow{mean, rstd_of(Q, cols, eps)};
+}
+
+}  // namespace
+
+template <class XT, class YT, int NCH, int NT, bool EXACT>
+__device__ __forceinline__ void ln_row_from_chunks(const uint4* raw, YT* yr, int64_t r,
+                                                   int64_t cols, float eps, const Weights& g,
+                                                   const Weights& b, float* mean_out,
+                                                   float* rstd_out, double* slot_a,
+                                                   double* slot_b)
+{
+    constexpr int E = XIn<XT>::kChunk;
+    float v[NCH * E];
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+        const int64_t j0 = ((int64_t)threadIdx.x + (int64_t)k * NT) * E;
+        if (EXACT || j0 < cols) {
+            unpack_chunk<XT>(raw[k], v + k * E);
+        } else {
+#pragma unroll
+            for (int i = 0; i < E; ++i)
+                v[k * E + i] = 0.0f;
+        }
+    }
+    const LnRow st = row_stats_in_registers<NCH, E, NT>(
+        v, cols, eps, slot_a, slot_b, [&](int k, int) {
+            return EXACT || ((int64_t)threadIdx.x + (int64_t)k * NT) * E < cols;
+        });
+    if (threadIdx.x == 0)
+        write_stats(mean_out, rstd_out, r, st);
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+        const int64_t j0 = ((int64_t)threadIdx.x + (int64_t)k * NT) * E;
+        if (EXACT || j0 < cols) {
+            affine<E, true>(v + k * E, st.rstd, g, b, j0, cols);
+            YOut<YT>::template chunk<E>(yr + j0, v + k * E);
+        }
+    }
+}
+
+template <class XT, int NCH, int NT, bool EXACT>
+__device__ __forceinline__ void ln_load_row_chunks(const XT* xr, int64_t cols, uint4* raw)
+{
+    constexpr int E = XIn<XT>::kChunk;
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+        int64_t j0 = ((int64_t)threadIdx.x + (int64_t)k * NT) * E;
+        if (!EXACT)
+            j0 = j0 < cols ? j0 : 0;  // chunks past the row end read chunk 0 (ignored)
+        raw[k] = load16_nt(xr + j0);
+    }
+}
+
+// Persistent rows with a one-row prefetch: workgroup b takes rows b, b + grid,
+// ... and loads the next row's chunks while it computes the current one (two
+// register buffers; with no next row the prefetch re-reads the current one,
+// an L2 hit, and is dropped, so no load sits behind a branch).  Rows are
+// whole 16-byte chunks, 16-byte aligned.
+template <class XT, class YT, int NCH, int NT, bool EXACT>
+__global__ __launch_bounds__(NT) void k_layernorm_rows_pf(
+    const XT* __restrict__ x, YT* __restrict__ y, Weights g, Weights b, float* mean_out,
+    float* rstd_out, int64_t rows, int64_t cols, int64_t ldx, int64_t ldy, float eps)
+{
+    __shared__ double slot[2][NT / kWave];
+    int64_t r = blockIdx.x;
+    if (r >= rows)
+        return;
+    const int64_t step = gridDim.x;
+    uint4 a[NCH], c[NCH];
+    ln_load_row_chunks<XT, NCH, NT, EXACT>(x + r * ldx, cols, a);
+    for (;;) {
+        const bool more = r + step < rows;
+        ln_load_row_chunks<XT, NCH, NT, EXACT>(x + (more ? r + step : r) * ldx, cols, c);
+        ln_row_from_chunks<XT, YT, NCH, NT, EXACT>(a, y + r * ldy, r, cols, eps, g, b, mean_out,
+                                                   rstd_out, slot[0], slot[1]);
+        if (!more)
+            break;
+        r += step;
+        const bool more2 = r + step < rows;
+        ln_load_row_chunks<XT, NCH, NT, EXACT>(x + (more2 ? r + step : r) * ldx, cols, a);
+        ln_row_from_chunks<XT, YT, NCH, NT, EXACT>(c, y + r * ldy, r, cols, eps, g, b, mean_out,
+                                                   rstd_out, slot[0], slot[1]);
+        if (!more2)
+            break;
+        r += step;
+    }
+}
+
+// Any alignment and any column count (masked chunks), one row per workgroup
+// at a time, the row in registers.
+template <class XT, class YT, int NCH, bool VEC, int NT>
+__global__ __launch_bounds__(NT) void k_layernorm_block(
+    const XT* __restrict__ x, YT* __restrict__ y, Weights g, Weights b, float* mean_out,
+    float* rstd_out, int64_t rows, int64_t cols, int64_t ldx, int64_t ldy, float eps)
+{
+    constexpr int E = VEC ? XIn<XT>::kChunk : 1;
+    __shared__ double slot[2][NT / kWave];
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+        const XT* xr = x + r * ldx;
+        YT* yr = y + r * ldy;
+        float v[NCH * E];
+#pragma unroll
+        for (int k = 0; k < NCH; ++k)
+            load_padded<XT, E, VEC>(xr, ((int64_t)threadIdx.x + (int64_t)k * NT) * E, cols,
+                                    v + k * E, 0.0f);
+        const LnRow st = row_stats_in_registers<NCH, E, NT>(
+            v, cols, eps, slot[0], slot[1], [&](int k, int i) {
+                return ((int64_t)threadIdx.x + (int64_t)k * NT) * E + i < cols;
+            });
+        if (threadIdx.x == 0)
+            write_stats(mean_out, rstd_out, r, st);
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) {
+            const int64_t j0 = ((int64_t)threadIdx.x + (int64_t)k * NT) * E;
+            affine<E, VEC>(v + k * E, st.rstd, g, b, j0, cols);
+            store_masked<YT, E, VEC>(yr, j0, cols, v + k * E);
+        }
+    }
+}
+
+// ---------------------------------------- block tier, streaming long rows
+// Statistics read with shifted sums (padding with K adds nothing), then a
+// second read for the map.
+template <class XT, class YT, bool VEC, int NT>
+__global__ __launch_bounds__(NT) void k_layernorm_stream(
+    const XT* __restrict__ x, YT* __restrict__ y, Weights g, Weights b, float* mean_out,
+    float* rstd_out, int64_t rows, int64_t cols, int64_t ldx, int64_t ldy, float eps)
+{
+    constexpr int E = VEC ? XIn<XT>::kChunk : 1;
+    __shared__ double slot[2][NT / kWave];
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+        const XT* xr = x + r * ldx;
+        YT* yr = y + r * ldy;
+        const float kf = XIn<XT>::one(xr);
+        const double K = (double)kf;
+        double s1 = 0.0, s2 = 0.0;
+        for (int64_t j0 = (int64_t)threadIdx.x * E; j0 < cols; j0 += (int64_t)NT * E) {
+            float v[E];
+            load_padded<XT, E, VEC>(xr, j0, cols, v, kf);
+#pragma unroll
+            for (int i = 0; i < E; ++i) {
+                const double d = (double)v[i] - K;
+                s1 += d;
+                s2 = __builtin_fma(d, d, s2);
+            }
+        }
+        const double S1 = block_reduce<SumF32, NT>(s1, slot[0]);
+        const double S2 = block_reduce<SumF32, NT>(s2, slot[1]);
+        const LnRow st = row_from_shifted(K, S1, S2, cols, eps);
+        if (threadIdx.x == 0)
+            write_stats(mean_out, rstd_out, r, st);
+        const Centre centre(st.mean);
+        for (int64_t j0 = (int64_t)threadIdx.x * E; j0 < cols; j0 += (int64_t)NT * E) {
+            float v[E];
+            load_padded<XT, E, VEC>(xr, j0, cols, v, 0.0f);
+#pragma unroll
+            for (int i = 0; i < E; ++i)
+                v[i] = centre(v[i]);
+            affine<E, VEC>(v, st.rstd, g, b, j0, cols);
+            store_masked<YT, E, VEC>(yr, j0, cols, v);
+        }
+        __syncthreads();  // slot reuse by the next row
+    }
+}
+
+// -------------------------------------------------------------- wave tier
+// S lanes per row, one chunk per lane (S * E >= cols), kWaveRowGroups row
+// groups per wavefront step.
+template <class XT, class YT, bool VEC, int S>
+__global__ __launch_bounds__(kBlockThreads) void k_layernorm_wave(
+    const XT* __restrict__ x, YT* __restrict__ y, Weights g, Weights b, float* mean_out,
+    float* rstd_out, int64_t rows, int64_t cols, int64_t ldx, int64_t ldy, float eps)
+{
+    constexpr int E = VEC ? XIn<XT>::kChunk : 1;
+    constexpr int RPG = kWave / S;
+    constexpr int U = kWaveRowGroups;
+    const int lane = lane_id();
+    const int seg = lane / S;
+    const int64_t j0 = (int64_t)(lane % S) * E;
+    const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
+    // the weights of this lane's columns are the same for every row
+    float gw[E], bw[E];
+    load_weights<E, VEC>(g, j0, cols, gw);
+    load_weights<E, VEC>(b, j0, cols, bw);
+    for (int64_t w = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+         w * RPG * U < rows; w += nwaves) {
+        const int64_t row0 = w * RPG * U;
+        float v[U][E];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t r = row0 + (int64_t)u * RPG + seg;
+            if (r < rows) {
+                load_padded<XT, E, VEC>(x + r * ldx, j0, cols, v[u], 0.0f);
+            } else {
+#pragma unroll
+                for (int i = 0; i < E; ++i)
+                    v[u][i] = 0.0f;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            double s = 0.0;
+#pragma unroll
+            for (int i = 0; i < E; ++i)
+                s += (double)v[u][i];
+            const double mean = segment_reduce<SumF32, S>(s) / (double)cols;
+            const Centre centre(mean);
+            float cq = 0.0f;
+#pragma unroll
+            for (int i = 0; i < E; ++i) {
+                const float d = j0 + i < cols ? centre(v[u][i]) : 0.0f;
+                v[u][i] = d;
+                cq = __builtin_fmaf(d, d, cq);
+            }
+            const double Q = segment_reduce<SumF32, S>((double)cq);
+            const LnRow st{mean, rstd_of(Q, cols, eps)};
+            const int64_t r = row0 + (int64_t)u * RPG + seg;
+            if (r < rows) {
+                if (lane % S == 0)
+                    write_stats(mean_out, rstd_out, r, st);
+#pragma unroll
+                for (int i = 0; i < E; ++i)
+                    v[u][i] = __builtin_fmaf(v[u][i] * st.rstd, gw[i], bw[i]);
+                store_masked<YT, E, VEC>(y + r * ldy, j0, cols, v[u]);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------- tiled and serial tiers
+// A thread owns R adjacent rows and walks each row three times (sum, sum of
+// squared deviations, map), in double.  R == 1 is the serial tier.
+template <class XT, class YT, int R>
+__global__ __launch_bounds__(kBlockThreads) void k_layernorm_tiled(
+    const XT* __restrict__ x, YT* __restrict__ y, Weights g, Weights b, float* mean_out,
+    float* rstd_out, int64_t rows, int64_t cols, int64_t ldx, int64_t ldy, float eps)
+{
+    const int64_t nthreads = (int64_t)gridDim.x * kBlockThreads;
+    for (int64_t tid = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x; tid * R < rows;
+         tid += nthreads) {
+        for (int k = 0; k < R; ++k) {
+            const int64_t r = tid * R + k;
+            if (r >= rows)
+                break;
+            const XT* xr = x + r * ldx;
+            YT* yr = y + r * ldy;
+            double s = 0.0;
+            for (int64_t j = 0; j < cols; ++j)
+                s += (double)XIn<XT>::one(xr + j);
+            const double mean = s / (double)cols;
+            double q = 0.0;
+            for (int64_t j = 0; j < cols; ++j) {
+                const double d = (double)XIn<XT>::one(xr + j) - mean;
+                q = __builtin_fma(d, d, q);
+            }
+            const LnRow st{mean, rstd_of(q, cols, eps)};
+            write_stats(mean_out, rstd_out, r, st);
+            const Centre centre(mean);
+            for (int64_t j = 0; j < cols; ++j) {
+                const float d = centre(XIn<XT>::one(xr + j));
+                YOut<YT>::one(yr + j, __builtin_fmaf(d * st.rstd, weight_one(g, j),
+                                                     weight_one(b, j)));
+            }
+        }
+    }
+}
+
+// ----------------------------------------------------------- split-K tier
+// G workgroups per row, tiles g, g + G, ... (kLnSplitKUnroll 16-byte chunks
+// per thread).  Statistics pass: workgroup (r, g) stores its shifted sums
+// (s1, s2) to part[(r * G + g) * 2 + {0, 1}].  Map pass: every workgroup of
+// row r reads the row's G pairs, sums each state over a fixed tree whose
+// leaves are the ranks in order (so every workgroup of the row gets the same
+// bits: "cluster_allreduce", description, the all-gather variant), and maps
+// its tiles.  Workgroup 0 of the row writes mean / rstd.
+template <class XT, bool VEC>
+__global__ __launch_bounds__(kBlockThreads) void k_layernorm_splitk_stats(
+    const XT* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, int32_t G,
+    double* __restrict__ part)
+{
+    constexpr int E = VEC ? XIn<XT>::kChunk : 1;
+    constexpr int U = kLnSplitKUnroll;
+    constexpr int64_t kTile = (int64_t)U * kBlockThreads * E;
+    __shared__ double slot[2][kWavesPerBlock];
+    const int64_t total = rows * G;
+    const int64_t ntiles = ceil_div(cols, kTile);
+    for (int64_t blk = blockIdx.x; blk < total; blk += gridDim.x) {
+        const int64_t r = blk / G;
+        const int32_t gi = (int32_t)(blk - r * G);
+        const XT* xr = x + r * ldx;
+        const float kf = XIn<XT>::one(xr);
+        const double K = (double)kf;
+        double s1 = 0.0, s2 = 0.0;
+        for (int64_t t = gi; t < ntiles; t += G) {
+            float v[U * E];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                load_padded<XT, E, VEC>(
+                    xr, t * kTile + ((int64_t)u * kBlockThreads + threadIdx.x) * E, cols,
+                    v + u * E, kf);
+#pragma unroll
+            for (int i = 0; i < U * E; ++i) {
+                const double d = (double)v[i] - K;
+                s1 += d;
+                s2 = __builtin_fma(d, d, s2);
+            }
+        }
+        const double S1 = block_reduce<SumF32, kBlockThreads>(s1, slot[0]);
+        const double S2 = block_reduce<SumF32, kBlockThreads>(s2, slot[1]);
+        if (threadIdx.x == 0) {
+            part[(r * G + gi) * 2] = S1;
+            part[(r * G + gi) * 2 + 1] = S2;
+        }
+        __syncthreads();  // slot reuse by the next (row, slice)
+    }
+}
+
+template <class XT, class YT, bool VEC>
+__global__ __launch_bounds__(kBlockThreads) void k_layernorm_splitk_map(
+    const XT* __restrict__ x, YT* __restrict__ y, Weights g, Weights b, float* mean_out,
+    float* rstd_out, int64_t rows, int64_t cols, int64_t ldx, int64_t ldy, float eps, int32_t G,
+    const double* __restrict__ part)
+{
+    constexpr int E = VEC ? XIn<XT>::kChunk : 1;
+    constexpr int U = kLnSplitKUnroll;
+    constexpr int64_t kTile = (int64_t)U * kBlockThreads * E;
+    static_assert(kSplitKMaxSlices <= kBlockThreads, "one pair per thread in the row fold");
+    __shared__ double slot[2][kWavesPerBlock];
+    const int64_t total = rows * G;
+    const int64_t ntiles = ceil_div(cols, kTile);
+    for (int64_t blk = blockIdx.x; blk < total; blk += gridDim.x) {
+        const int64_t r = blk / G;
+        const int32_t gi = (int32_t)(blk - r * G);
+        const XT* xr = x + r * ldx;
+        YT* yr = y + r * ldy;
+        double p1 = 0.0, p2 = 0.0;
+        if ((int32_t)threadIdx.x < G) {
+            p1 = part[(r * G + threadIdx.x) * 2];
+            p2 = part[(r * G + threadIdx.x) * 2 + 1];
+        }
+        const double K = (double)XIn<XT>::one(xr);
+        const double S1 = block_reduce<SumF32, kBlockThreads>(p1, slot[0]);
+        const double S2 = block_reduce<SumF32, kBlockThreads>(p2, slot[1]);
+        const LnRow st = row_from_shifted(K, S1, S2, cols, eps);
+        if (gi == 0 && threadIdx.x == 0)
+            write_stats(mean_out, rstd_out, r, st);
+        const Centre centre(st.mean);
+        for (int64_t t = gi; t < ntiles; t += G) {
+            float v[U * E];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                load_padded<XT, E, VEC>(
+                    xr, t * kTile + ((int64_t)u * kBlockThreads + threadIdx.x) * E, cols,
+                    v + u * E, 0.0f);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t j0 = t * kTile + ((int64_t)u * kBlockThreads + threadIdx.x) * E;
+#pragma unroll
+                for (int i = 0; i < E; ++i)
+                    v[u * E + i] = centre(v[u * E + i]);
+                affine<E, VEC>(v + u * E, st.rstd, g, b, j0, cols);
+                store_masked<YT, E, VEC>(yr, j0, cols, v + u * E);
+            }
+        }
+        __syncthreads();  // slot reuse by the next (row, slice)
+    }
+}
+
+// ---------------------------------------------------------------- launch
+template <class XT, class YT, int NCH, int NT>
+static rr_status launch_pf(dim3 grid, const XT* x, YT* y, const Weights& g, const Weights& b,
+                           const LayernormLaunch& a)
+{
+    constexpr int64_t kExactCols = (int64_t)NT * NCH * XIn<XT>::kChunk;
+    if (a.cols == kExactCols)
+        return launch_kernel(k_layernorm_rows_pf<XT, YT, NCH, NT, true>, grid, dim3(NT), 0,
+                             a.stream, x, y, g, b, a.mean_out, a.rstd_out, a.rows, a.cols, a.ld_x,
+                             a.ld_y, a.eps);
+    return launch_kernel(k_layernorm_rows_pf<XT, YT, NCH, NT, false>, grid, dim3(NT), 0, a.stream,
+                         x, y, g, b, a.mean_out, a.rstd_out, a.rows, a.cols, a.ld_x, a.ld_y,
+                         a.eps);
+}
+
+#define RR_LN_ARGS x, y, g, b, a.mean_out, a.rstd_out, a.rows, a.cols, a.ld_x, a.ld_y, a.eps
+
+template <class XT, class YT, bool VEC>
+static rr_status launch_block(const rr_plan& p, const XT* x, YT* y, const Weights& g,
+                              const Weights& b, const LayernormLaunch& a)
+{
+    constexpr int NT = kBlockThreads;
+    constexpr int E = VEC ? XIn<XT>::kChunk : 1;
+    const dim3 grid((unsigned)p.grid), block(NT);
+    const hipStream_t s = a.stream;
+    const int64_t nch = ceil_div(ceil_div(a.cols, E), NT);
+    if constexpr (VEC) {
+        if (a.cols % E == 0 && nch <= kLnMaxChunks) {
+            if (nch <= 1) return launch_pf<XT, YT, 1, NT>(grid, x, y, g, b, a);
+            if (nch <= 2) return launch_pf<XT, YT, 2, NT>(grid, x, y, g, b, a);
+            if (nch <= 4) return launch_pf<XT, YT, 4, NT>(grid, x, y, g, b, a);
+            return launch_pf<XT, YT, kLnMaxChunks, NT>(grid, x, y, g, b, a);
+        }
+    }
+    if (nch <= 1)
+        return launch_kernel(k_layernorm_block<XT, YT, 1, VEC, NT>, grid, block, 0, s, RR_LN_ARGS);
+    if (nch <= 2)
+        return launch_kernel(k_layernorm_block<XT, YT, 2, VEC, NT>, grid, block, 0, s, RR_LN_ARGS);
+    if (nch <= 4)
+        return launch_kernel(k_layernorm_block<XT, YT, 4, VEC, NT>, grid, block, 0, s, RR_LN_ARGS);
+    if (nch <= kLnMaxChunks)
+        return launch_kernel(k_layernorm_block<XT, YT, kLnMaxChunks, VEC, NT>, grid, block, 0, s,
+                             RR_LN_ARGS);
+    return launch_kernel(k_layernorm_stream<XT, YT, VEC, NT>, grid, block, 0, s, RR_LN_ARGS);
+}
+
+template <class XT, class YT, bool VEC>
+static rr_status launch_typed(const rr_plan& p, const LayernormLaunch& a)
+{
+    const XT* x = static_cast<const XT*>(a.x);
+    YT* y = static_cast<YT*>(a.y);
+    const Weights g{a.gamma, a.w_dtype == RR_BF16, 1.0f};
+    const Weights b{a.beta, a.w_dtype == RR_BF16, 0.0f};
+    const dim3 grid((unsigned)(p.grid > kMaxGrid ? kMaxGrid : p.grid)), block(kBlockThreads);
+    const hipStream_t s = a.stream;
+    switch (p.tier) {
+    case RR_TIER_BLOCK:
+        return launch_block<XT, YT, VEC>(p, x, y, g, b, a);
+    case RR_TIER_WAVE:
+        switch (p.lanes_per_row) {
+        case 4: return launch_kernel(k_layernorm_wave<XT, YT, VEC, 4>, grid, block, 0, s, RR_LN_ARGS);
+        case 16: return launch_kernel(k_layernorm_wave<XT, YT, VEC, 16>, grid, block, 0, s, RR_LN_ARGS);
+        case 64: return launch_kernel(k_layernorm_wave<XT, YT, VEC, 64>, grid, block, 0, s, RR_LN_ARGS);
+        default: return RR_ERR_TIER;
+        }
+    case RR_TIER_TILED:
+        return launch_kernel(k_layernorm_tiled<XT, YT, kTiledRows>, grid, block, 0, s, RR_LN_ARGS);
+    case RR_TIER_SERIAL:
+        return launch_kernel(k_layernorm_tiled<XT, YT, 1>, grid, block, 0, s, RR_LN_ARGS);
+    case RR_TIER_SPLITK: {
+        double* part = static_cast<double*>(a.workspace);
+        rr_status st = launch_kernel(k_layernorm_splitk_stats<XT, VEC>, grid, block, 0, s, x,
+                                     a.rows, a.cols, a.ld_x, p.slices, part);
+        if (st != RR_OK)
+            return st;
+        return launch_kernel(k_layernorm_splitk_map<XT, YT, VEC>, grid, block, 0, s, RR_LN_ARGS,
+                             p.slices, (const double*)part);
+    }
+    default:
+        return RR_ERR_TIER;
+    }
+}
+
+#undef RR_LN_ARGS
+
+template <class XT, class YT>
+static rr_status launch_xy(const rr_plan& p, const LayernormLaunch& a)
+{
+    return a.vec ? launch_typed<XT, YT, true>(p, a) : launch_typed<XT, YT, false>(p, a);
+}
+
+rr_status launch_layernorm(const rr_plan& p, const LayernormLaunch& a)
+{
+    const bool xb = a.x_dtype == RR_BF16, yb = a.y_dtype == RR_BF16;
+    if (xb && yb) return launch_xy<uint16_t, uint16_t>(p, a);
+    if (xb) return launch_xy<uint16_t, float>(p, a);
+    if (yb) return launch_xy<float, uint16_t>(p, a);
+    return launch_xy<float, float>(p, a);
+}
+
+}  // namespace rr

@@ -115,6 +115,8 @@ static_assert((int64_t)kSoftmaxSplitKUnroll * kBlockThreads * 8 <= kSplitKMinCol
               "softmax split-K tile larger than the per-workgroup column minimum");
 static_assert((int64_t)kSplitKUnroll * kBlockThreads * 4 <= kSplitKMinColsPerGroup,
               "reduce split-K tile larger than the per-workgroup column minimum");
+static_assert((int64_t)kLnSplitKUnroll * kBlockThreads * 8 <= kSplitKMinColsPerGroup,
+              "layernorm split-K tile larger than the per-workgroup column minimum");
 
 rr_status plan_softmax(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype y_dtype,
                        rr_tier tier, int32_t cu_count, bool vec, rr_plan* out)
@@ -156,7 +158,55 @@ rr_status plan_softmax(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype y_
     return RR_OK;
 }
 
+// Layernorm: the softmax's tier rule; the block tier keeps rows of up to
+// kLnMaxChunks chunks per thread in registers on persistent workgroups.
+rr_status plan_layernorm(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype y_dtype,
+                         rr_dtype w_dtype, rr_tier tier, int32_t cu_count, bool vec,
+                         rr_plan* out)
+{
+    if (!out) return RR_ERR_NULL;
+    if (rows < 0 || cols < 0) return RR_ERR_SHAPE;
+    if ((x_dtype != RR_F32 && x_dtype != RR_BF16) || (y_dtype != RR_F32 && y_dtype != RR_BF16) ||
+        (w_dtype != RR_F32 && w_dtype != RR_BF16))
+        return RR_ERR_DTYPE;
+    if (cu_count < 1) return RR_ERR_SHAPE;
+    if ((int)tier < RR_TIER_AUTO || (int)tier > RR_TIER_SPLITK) return RR_ERR_TIER;
+    rr_tier t = tier;
+    if (t == RR_TIER_AUTO) {
+        if (rows < cu_count && cols >= kSplitKMinCols)
+            t = RR_TIER_SPLITK;
+        else
+            t = cols <= 8 ? RR_TIER_TILED : cols <= 64 ? RR_TIER_WAVE : RR_TIER_BLOCK;
+    }
+    if (t == RR_TIER_WAVE && cols > 64) return RR_ERR_TIER;
+    memset(out, 0, sizeof *out);
+    const int vec_elems = vec ? (x_dtype == RR_BF16 ? 8 : 4) : 1;
+    if (t == RR_TIER_SPLITK) {
+        fill_splitk_geometry(rows, cols, (int64_t)kLnSplitKUnroll * kBlockThreads * vec_elems,
+                             cu_count, out);
+        out->workspace_bytes = (uint64_t)(rows * (int64_t)out->slices * 16);
+        return RR_OK;
+    }
+    fill_rowwise_geometry(t, rows, cols, vec_elems, out);
+    if (t == RR_TIER_BLOCK) {
+        const int64_t chunks = ceil_div(cols, vec_elems);
+        if (vec && cols % vec_elems == 0 && ceil_div(chunks, (int64_t)kBlockThreads) <= kLnMaxChunks) {
+            const int64_t g = (int64_t)cu_count * kLnRowBlocksPerCU;
+            out->grid = rows < g ? rows : g;
+        }
+    }
+    return RR_OK;
+}
+
 }  // namespace rr
+
+extern "C" rr_status rr_plan_layernorm(int64_t rows, int64_t cols, rr_dtype x_dtype,
+                                       rr_dtype y_dtype, rr_dtype w_dtype, rr_tier tier,
+                                       int32_t cu_count, rr_plan* plan_out)
+{
+    return rr::plan_layernorm(rows, cols, x_dtype, y_dtype, w_dtype, tier, cu_count, true,
+                              plan_out);
+}
 
 extern "C" rr_status rr_plan_reduce(int64_t rows, int64_t cols, int64_t ld, rr_dtype dtype,
                                     rr_op op, rr_tier tier, int32_t cu_count, rr_plan* plan_out)
@@ -176,7 +226,7 @@ extern "C" const char* rr_status_string(rr_status s)
     switch (s) {
     case RR_OK: return "ok";
     case RR_ERR_NULL: return "a required pointer is NULL";
-    case RR_ERR_SHAPE: return "invalid shape (negative size, ld < cols, or P/depth out of range)";
+    case RR_ERR_SHAPE: return "invalid shape or value (negative size, ld < cols, P/depth out of range, or eps negative or not finite)";
     case RR_ERR_DTYPE: return "unsupported dtype or dtype combination";
     case RR_ERR_TIER: return "forced tier is not legal for this shape or operation";
     case RR_ERR_WORKSPACE: return "split-K workspace missing or too small";

@@ -10,6 +10,9 @@ rr_status plan_reduce(int64_t rows, int64_t cols, int64_t ld, rr_dtype dtype, rr
                       rr_tier tier, int32_t cu_count, bool vec, rr_plan* out);
 rr_status plan_softmax(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype y_dtype,
                        rr_tier tier, int32_t cu_count, bool vec, rr_plan* out);
+rr_status plan_layernorm(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype y_dtype,
+                         rr_dtype w_dtype, rr_tier tier, int32_t cu_count, bool vec,
+                         rr_plan* out);
 uint64_t splitk_workspace_bytes(int64_t rows, int32_t slices);
 uint64_t softmax_splitk_workspace_bytes(int64_t rows, int32_t slices);
 

@@ -17,108 +17,11 @@
 #include "rr_device.hpp"
 #include "rr_launch.hpp"
 #include "rr_launch_util.hpp"
+#include "rr_rowio.hpp"
 
 namespace rr {
 
 constexpr float kNegInf = -__builtin_inff();
-
-// Element access: XT is uint16_t (bf16 bits) or float.  Whole 16-byte chunks
-// move with non-temporal loads and stores (every byte is touched once).
-template <class XT>
-struct XIn;
-template <>
-struct XIn<uint16_t> {
-    static constexpr int kChunk = 8;  // elements per 128-bit load
-    __device__ static void chunk(const uint16_t* p, float* v)
-    {
-        uint4 u = load16_nt(p);
-        v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x);
-        v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
-        v[4] = bf16_lo(u.z); v[5] = bf16_hi(u.z);
-        v[6] = bf16_lo(u.w); v[7] = bf16_hi(u.w);
-    }
-    __device__ static float one(const uint16_t* p) { return bf16_bits_to_f32(*p); }
-};
-template <>
-struct XIn<float> {
-    static constexpr int kChunk = 4;
-    __device__ static void chunk(const float* p, float* v)
-    {
-        uint4 u = load16_nt(p);
-        v[0] = __uint_as_float(u.x); v[1] = __uint_as_float(u.y);
-        v[2] = __uint_as_float(u.z); v[3] = __uint_as_float(u.w);
-    }
-    __device__ static float one(const float* p) { return *p; }
-};
-
-template <class YT>
-struct YOut;
-template <>
-struct YOut<uint16_t> {
-    template <int E>
-    __device__ static void chunk(uint16_t* p, const float* v)
-    {
-        if constexpr (E == 8) {
-            uint4 u;
-            u.x = pack_bf16x2(v[0], v[1]); u.y = pack_bf16x2(v[2], v[3]);
-            u.z = pack_bf16x2(v[4], v[5]); u.w = pack_bf16x2(v[6], v[7]);
-            store16_nt(p, u);
-        } else {
-            static_assert(E == 4, "chunk of 4 or 8");
-            uint2 u;
-            u.x = pack_bf16x2(v[0], v[1]); u.y = pack_bf16x2(v[2], v[3]);
-            store8_nt(p, u);
-        }
-    }
-    __device__ static void one(uint16_t* p, float v) { *p = f32_to_bf16_bits(v); }
-};
-template <>
-struct YOut<float> {
-    template <int E>
-    __device__ static void chunk(float* p, const float* v)
-    {
-#pragma unroll
-        for (int i = 0; i < E; i += 4)
-            store16_nt(p + i, make_uint4(__float_as_uint(v[i]), __float_as_uint(v[i + 1]),
-                                         __float_as_uint(v[i + 2]), __float_as_uint(v[i + 3])));
-    }
-    __device__ static void one(float* p, float v) { *p = v; }
-};
-
-// Load chunk j0 .. j0+E-1 of a row (E == 1 for the scalar variant), padding
-// past `cols` with -inf.
-template <class XT, int E, bool VEC>
-__device__ __forceinline__ void load_padded(const XT* row, int64_t j0, int64_t cols, float* v)
-{
-    if constexpr (VEC) {
-        if (j0 + E <= cols) {
-            XIn<XT>::chunk(row + j0, v);
-            return;
-        }
-    }
-    {
-#pragma unroll
-        for (int i = 0; i < E; ++i)
-            v[i] = j0 + i < cols ? XIn<XT>::one(row + j0 + i) : kNegInf;
-    }
-}
-
-template <class YT, int E, bool VEC>
-__device__ __forceinline__ void store_masked(YT* row, int64_t j0, int64_t cols, const float* v)
-{
-    if constexpr (VEC) {
-        if (j0 + E <= cols) {
-            YOut<YT>::template chunk<E>(row + j0, v);
-            return;
-        }
-    }
-    {
-#pragma unroll
-        for (int i = 0; i < E; ++i)
-            if (j0 + i < cols)
-                YOut<YT>::one(row + j0 + i, v[i]);
-    }
-}
 
 // Pass 1 on values held by one thread: m = max, v <- exp(v - m), s = sum v.
 // With m == -inf (nothing but -inf / padding) every p is 0.
@@ -229,20 +132,6 @@ __global__ __launch_bounds__(NT) void k_softmax_block(const XT* __restrict__ x,
 // row's worth of loads in flight through its compute phase.  Two register
 // buffers alternate; when there is no next row the prefetch re-reads the
 // current one (an L2 hit) and is dropped, so no load sits behind a branch.
-template <class XT>
-__device__ __forceinline__ void unpack_chunk(uint4 u, float* v)
-{
-    if constexpr (sizeof(XT) == 2) {
-        v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x);
-        v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
-        v[4] = bf16_lo(u.z); v[5] = bf16_hi(u.z);
-        v[6] = bf16_lo(u.w); v[7] = bf16_hi(u.w);
-    } else {
-        v[0] = __uint_as_float(u.x); v[1] = __uint_as_float(u.y);
-        v[2] = __uint_as_float(u.z); v[3] = __uint_as_float(u.w);
-    }
-}
-
 // EXACT: cols == NT * NCH * chunk, so every chunk of every thread is in the
 // row and no per-chunk bound check is emitted.
 template <class XT, class YT, int NCH, int NT, bool EXACT>

@@ -17,6 +17,9 @@ Workloads (sizes are the defaults; smaller sizes keep the distributions):
   lse_merge    P = 8 partitions of O [8, 32, 128, 128] standard normal,
                m = 4 * standard normal, l = uniform(1, 4096), scale 1.0
   softmax_long_rows  bf16 of 3 * standard normal, [16, 2^22] (split-K softmax)
+  layernorm_rows     bf16 of 0.5 + 2 * standard normal, [16384, 4096], with
+                     float32 gamma = 1 + 0.1 * standard normal and
+                     beta = 0.1 * standard normal over the columns
 """
 import numpy as np
 
@@ -26,6 +29,7 @@ SEED_SOFTMAX_ROWS = 3
 SEED_LONG_ROWS = 4
 SEED_LSE_MERGE = 5
 SEED_SOFTMAX_LONG_ROWS = 6
+SEED_LAYERNORM_ROWS = 7
 
 
 def _bf16_bits(x_f32):
@@ -70,6 +74,17 @@ def long_rows(seed=SEED_LONG_ROWS, rows=16, cols=1 << 24):
 def softmax_long_rows(seed=SEED_SOFTMAX_LONG_ROWS, rows=16, cols=1 << 22, std=3.0):
     """Few very long softmax rows (fewer rows than compute units)."""
     return normal_bf16(seed, (rows, cols), std)
+
+
+def layernorm_rows(seed=SEED_LAYERNORM_ROWS, rows=16384, cols=4096):
+    """(x bf16 bits [rows, cols], gamma f32 [cols], beta f32 [cols])."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, cols), dtype=np.float32)
+    x *= np.float32(2.0)
+    x += np.float32(0.5)
+    gamma = np.float32(1.0) + np.float32(0.1) * rng.standard_normal(cols, dtype=np.float32)
+    beta = np.float32(0.1) * rng.standard_normal(cols, dtype=np.float32)
+    return _bf16_bits(x), gamma.astype(np.float32), beta.astype(np.float32)
 
 
 def lse_merge(seed=SEED_LSE_MERGE, P=8, batch=8, heads=32, q_rows=128, depth=128):

@@ -128,6 +128,54 @@ def test_softmax_splitk_every_workgroup_gets_a_tile(rows, cols):
     assert 1 <= g <= 256 and g <= -(-cols // t) and p["grid"] == rows * g
 
 
+def test_layernorm_tier_rule_and_geometry():
+    assert rr.plan_layernorm(16384, 4096)["tier"] == "block"
+    assert rr.plan_layernorm(16384, 4096)["grid"] == 512       # persistent rows: 2 per CU
+    assert rr.plan_layernorm(16384, 4095)["grid"] == 16384     # ragged rows: one per workgroup
+    assert rr.plan_layernorm(100, 40)["tier"] == "wave"
+    assert rr.plan_layernorm(100, 8)["tier"] == "tiled"
+    assert rr.plan_layernorm(16, 1 << 20)["tier"] == "splitk"
+    p = rr.plan_layernorm(16, 1 << 20, cu_count=256)
+    assert p["slices"] == 64 and p["tile_cols"] == 8192 and p["grid"] == 1024
+    assert p["workspace_bytes"] == 16 * 64 * 16
+    p = rr.plan_layernorm(16, 1 << 20, x_dtype=torch.float32, cu_count=256)
+    assert p["tile_cols"] == 4096 and p["slices"] == 64
+    assert rr.plan_layernorm(4, 1000, tier="splitk", cu_count=256)["slices"] == 1
+    with pytest.raises(rr.RRError) as e:
+        rr.plan_layernorm(4, 65, tier="wave")
+    assert e.value.status == 4
+    with pytest.raises(rr.RRError) as e:
+        rr.plan_layernorm(4, 8, x_dtype=torch.int32)
+    assert e.value.status == 3
+    with pytest.raises(rr.RRError) as e:
+        rr.plan_layernorm(4, 8, w_dtype=torch.int32)
+    assert e.value.status == 3
+
+
+def test_layernorm_entry_point_validates_before_touching_the_device():
+    lib = ctypes.CDLL(rr.lib_path())
+    vp, i64, it = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.rr_layernorm_rows.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, it, it, it,
+                                      ctypes.c_float, it, vp, ctypes.c_size_t, vp]
+
+    def call(rows=4, cols=8, ldx=8, ldy=8, xd=2, yd=2, wd=0, eps=1e-5, tier=0):
+        return lib.rr_layernorm_rows(None, None, None, None, None, None, rows, cols, ldx, ldy,
+                                     xd, yd, wd, eps, tier, None, 0, None)
+    assert call(rows=-1) == 2
+    assert call(ldx=7) == 2
+    assert call(ldy=7) == 2
+    assert call(eps=-1.0) == 2
+    assert call(eps=float("nan")) == 2
+    assert call(eps=float("inf")) == 2
+    assert call(xd=1) == 3
+    assert call(wd=1) == 3
+    assert call(tier=6) == 4
+    assert call(cols=65, ldx=65, ldy=65, tier=1) == 4
+    assert call(rows=0) == 0          # no-op
+    assert call(cols=0) == 0          # no-op
+    assert call() == 1                # NULL x / y
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(rows=-1, cols=4), 2),
     (dict(rows=4, cols=-1), 2),
