@@ -47,13 +47,33 @@ constexpr int64_t kSoftmaxWideMinChunks = (int64_t)kBlockThreads * kSoftmaxMaxCh
 // Split-K softmax: 16-byte chunks per thread per tile (a tile is one load
 // round of the workgroup).
 constexpr int kSoftmaxSplitKUnroll = 4;
-// Layernorm: rows of up to kLnMaxChunks 16-byte chunks per thread (256
-// threads) stay in registers on persistent workgroups, kLnRowBlocksPerCU per
-// CU; longer rows stream twice.  Split-K tiles are kLnSplitKUnroll chunks per
-// thread.
+// Layernorm.  Rows of whole aligned 16-byte chunks, up to kLnPfMaxChunks of
+// them, stay in registers on persistent workgroups whose size follows the
+// row (ln_pf_shape), kLnPfWavesPerCU wavefronts per CU in all.  Other rows
+// of up to kLnMaxChunks chunks per thread of 256 stay in registers one row
+// per workgroup; longer rows stream twice.  Split-K tiles are
+// kLnSplitKUnroll chunks per thread.
 constexpr int kLnMaxChunks = 8;
-constexpr int kLnRowBlocksPerCU = 2;
+constexpr int64_t kLnPfMaxChunks = 2048;
+constexpr int kLnPfWavesPerCU = 8;
 constexpr int kLnSplitKUnroll = 4;
+
+// Threads per row (nt) and chunks per thread (nch) of the persistent
+// layernorm for a row of `chunks` chunks; nt == 0 when the row is too long.
+struct LnPfShape {
+    int nt;
+    int nch;
+};
+constexpr LnPfShape ln_pf_shape(int64_t chunks)
+{
+    return chunks <= 64     ? LnPfShape{64, 1}
+           : chunks <= 128  ? LnPfShape{64, 2}
+           : chunks <= 256  ? LnPfShape{128, 2}
+           : chunks <= 512  ? LnPfShape{256, 2}
+           : chunks <= 1024 ? LnPfShape{256, 4}
+           : chunks <= kLnPfMaxChunks ? LnPfShape{512, 4}
+                                      : LnPfShape{0, 0};
+}
 
 // LSE merge: partitions staged per batch of loads, and workgroup size.
 constexpr int kMergeBatch = 8;

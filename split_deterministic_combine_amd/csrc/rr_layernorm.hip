@@ -7,8 +7,9 @@
 //   y = (x - mean) * rstd * gamma + beta      (gamma / beta per column)
 //
 // Statistics, by how much of the row a thread holds:
-//   * rows in registers (block tier up to kLnMaxChunks 16-byte chunks per
-//     thread, wave tier): the exact two-pass form.  The sum of x is taken in
+//   * rows in registers (block tier: persistent workgroups of 64 to 512
+//     threads holding up to 4 chunks each, or up to kLnMaxChunks chunks per
+//     thread of 256 for unaligned rows; wave tier): the exact two-pass form.  The sum of x is taken in
 //     double; then every thread forms d = (x - mean_f) - c, with mean_f the
 //     float mean and c = (float)(mean - mean_f), and the sum of d^2 is taken
 //     (float inside a chunk, double across chunks and threads).  d stays in
@@ -184,10 +185,12 @@ __device__ __forceinline__ LnRow row_stats_in_registers(float* v, int64_t cols, 
 
 }  // namespace
 
-template <class XT, class YT, int NCH, int NT, bool EXACT>
+// One row from its raw chunks; gw / bw hold this thread's gamma / beta
+// (AFF), loaded once per workgroup.
+template <class XT, class YT, int NCH, int NT, bool EXACT, bool AFF>
 __device__ __forceinline__ void ln_row_from_chunks(const uint4* raw, YT* yr, int64_t r,
-                                                   int64_t cols, float eps, const Weights& g,
-                                                   const Weights& b, float* mean_out,
+                                                   int64_t cols, float eps, const float* gw,
+                                                   const float* bw, float* mean_out,
                                                    float* rstd_out, double* slot_a,
                                                    double* slot_b)
 {
@@ -214,7 +217,11 @@ __device__ __forceinline__ void ln_row_from_chunks(const uint4* raw, YT* yr, int
     for (int k = 0; k < NCH; ++k) {
         const int64_t j0 = ((int64_t)threadIdx.x + (int64_t)k * NT) * E;
         if (EXACT || j0 < cols) {
-            affine<E, true>(v + k * E, st.rstd, g, b, j0, cols);
+#pragma unroll
+            for (int i = 0; i < E; ++i) {
+                const float t = v[k * E + i] * st.rstd;
+                v[k * E + i] = AFF ? __builtin_fmaf(t, gw[k * E + i], bw[k * E + i]) : t;
+            }
             YOut<YT>::template chunk<E>(yr + j0, v + k * E);
         }
     }
@@ -237,12 +244,14 @@ __device__ __forceinline__ void ln_load_row_chunks(const XT* xr, int64_t cols, u
 // ... and loads the next row's chunks while it computes the current one (two
 // register buffers; with no next row the prefetch re-reads the current one,
 // an L2 hit, and is dropped, so no load sits behind a branch).  Rows are
-// whole 16-byte chunks, 16-byte aligned.
-template <class XT, class YT, int NCH, int NT, bool EXACT>
+// whole 16-byte chunks, 16-byte aligned.  A thread's columns are the same in
+// every row, so its gamma / beta are loaded into registers once.
+template <class XT, class YT, int NCH, int NT, bool EXACT, bool AFF>
 __global__ __launch_bounds__(NT) void k_layernorm_rows_pf(
     const XT* __restrict__ x, YT* __restrict__ y, Weights g, Weights b, float* mean_out,
     float* rstd_out, int64_t rows, int64_t cols, int64_t ldx, int64_t ldy, float eps)
 {
+    constexpr int E = XIn<XT>::kChunk;
     __shared__ double slot[2][NT / kWave];
     int64_t r = blockIdx.x;
     if (r >= rows)
@@ -250,18 +259,27 @@ __global__ __launch_bounds__(NT) void k_layernorm_rows_pf(
     const int64_t step = gridDim.x;
     uint4 a[NCH], c[NCH];
     ln_load_row_chunks<XT, NCH, NT, EXACT>(x + r * ldx, cols, a);
+    float gw[AFF ? NCH * E : 1], bw[AFF ? NCH * E : 1];
+    if constexpr (AFF) {
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) {
+            const int64_t j0 = ((int64_t)threadIdx.x + (int64_t)k * NT) * E;
+            load_weights<E, true>(g, j0, cols, gw + k * E);
+            load_weights<E, true>(b, j0, cols, bw + k * E);
+        }
+    }
     for (;;) {
         const bool more = r + step < rows;
         ln_load_row_chunks<XT, NCH, NT, EXACT>(x + (more ? r + step : r) * ldx, cols, c);
-        ln_row_from_chunks<XT, YT, NCH, NT, EXACT>(a, y + r * ldy, r, cols, eps, g, b, mean_out,
-                                                   rstd_out, slot[0], slot[1]);
+        ln_row_from_chunks<XT, YT, NCH, NT, EXACT, AFF>(a, y + r * ldy, r, cols, eps, gw, bw,
+                                                        mean_out, rstd_out, slot[0], slot[1]);
         if (!more)
             break;
         r += step;
         const bool more2 = r + step < rows;
         ln_load_row_chunks<XT, NCH, NT, EXACT>(x + (more2 ? r + step : r) * ldx, cols, a);
-        ln_row_from_chunks<XT, YT, NCH, NT, EXACT>(c, y + r * ldy, r, cols, eps, g, b, mean_out,
-                                                   rstd_out, slot[0], slot[1]);
+        ln_row_from_chunks<XT, YT, NCH, NT, EXACT, AFF>(c, y + r * ldy, r, cols, eps, gw, bw,
+                                                        mean_out, rstd_out, slot[0], slot[1]);
         if (!more2)
             break;
         r += step;
@@ -549,18 +567,28 @@ __global__ __launch_bounds__(kBlockThreads) void k_layernorm_splitk_map(
 }
 
 // ---------------------------------------------------------------- launch
-template <class XT, class YT, int NCH, int NT>
-static rr_status launch_pf(dim3 grid, const XT* x, YT* y, const Weights& g, const Weights& b,
-                           const LayernormLaunch& a)
+template <class XT, class YT, int NCH, int NT, bool AFF>
+static rr_status launch_pf_aff(const XT* x, YT* y, const Weights& g, const Weights& b,
+                               const rr_plan& p, const LayernormLaunch& a)
 {
     constexpr int64_t kExactCols = (int64_t)NT * NCH * XIn<XT>::kChunk;
+    const dim3 grid((unsigned)p.grid), block(NT);
     if (a.cols == kExactCols)
-        return launch_kernel(k_layernorm_rows_pf<XT, YT, NCH, NT, true>, grid, dim3(NT), 0,
+        return launch_kernel(k_layernorm_rows_pf<XT, YT, NCH, NT, true, AFF>, grid, block, 0,
                              a.stream, x, y, g, b, a.mean_out, a.rstd_out, a.rows, a.cols, a.ld_x,
                              a.ld_y, a.eps);
-    return launch_kernel(k_layernorm_rows_pf<XT, YT, NCH, NT, false>, grid, dim3(NT), 0, a.stream,
-                         x, y, g, b, a.mean_out, a.rstd_out, a.rows, a.cols, a.ld_x, a.ld_y,
-                         a.eps);
+    return launch_kernel(k_layernorm_rows_pf<XT, YT, NCH, NT, false, AFF>, grid, block, 0,
+                         a.stream, x, y, g, b, a.mean_out, a.rstd_out, a.rows, a.cols, a.ld_x,
+                         a.ld_y, a.eps);
+}
+
+template <class XT, class YT, int NCH, int NT>
+static rr_status launch_pf(const XT* x, YT* y, const Weights& g, const Weights& b,
+                           const rr_plan& p, const LayernormLaunch& a)
+{
+    if (g.p || b.p)
+        return launch_pf_aff<XT, YT, NCH, NT, true>(x, y, g, b, p, a);
+    return launch_pf_aff<XT, YT, NCH, NT, false>(x, y, g, b, p, a);
 }
 
 #define RR_LN_ARGS x, y, g, b, a.mean_out, a.rstd_out, a.rows, a.cols, a.ld_x, a.ld_y, a.eps
@@ -575,11 +603,20 @@ static rr_status launch_block(const rr_plan& p, const XT* x, YT* y, const Weight
     const hipStream_t s = a.stream;
     const int64_t nch = ceil_div(ceil_div(a.cols, E), NT);
     if constexpr (VEC) {
-        if (a.cols % E == 0 && nch <= kLnMaxChunks) {
-            if (nch <= 1) return launch_pf<XT, YT, 1, NT>(grid, x, y, g, b, a);
-            if (nch <= 2) return launch_pf<XT, YT, 2, NT>(grid, x, y, g, b, a);
-            if (nch <= 4) return launch_pf<XT, YT, 4, NT>(grid, x, y, g, b, a);
-            return launch_pf<XT, YT, kLnMaxChunks, NT>(grid, x, y, g, b, a);
+        if (a.cols % E == 0) {
+            // persistent rows; the plan chose the shape and sized the grid
+            const LnPfShape sh = ln_pf_shape(a.cols / E);
+            if (sh.nt > 0 && sh.nt != p.block)
+                return RR_ERR_TIER;  // plan and launch disagree: refuse, launch nothing
+            switch (sh.nt * 16 + sh.nch) {
+            case 64 * 16 + 1: return launch_pf<XT, YT, 1, 64>(x, y, g, b, p, a);
+            case 64 * 16 + 2: return launch_pf<XT, YT, 2, 64>(x, y, g, b, p, a);
+            case 128 * 16 + 2: return launch_pf<XT, YT, 2, 128>(x, y, g, b, p, a);
+            case 256 * 16 + 2: return launch_pf<XT, YT, 2, 256>(x, y, g, b, p, a);
+            case 256 * 16 + 4: return launch_pf<XT, YT, 4, 256>(x, y, g, b, p, a);
+            case 512 * 16 + 4: return launch_pf<XT, YT, 4, 512>(x, y, g, b, p, a);
+            default: break;  // too long for registers: stream below
+            }
         }
     }
     if (nch <= 1)

@@ -158,8 +158,9 @@ rr_status plan_softmax(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype y_
     return RR_OK;
 }
 
-// Layernorm: the softmax's tier rule; the block tier keeps rows of up to
-// kLnMaxChunks chunks per thread in registers on persistent workgroups.
+// Layernorm: the softmax's tier rule.  The block tier keeps rows of whole
+// aligned chunks in registers on persistent workgroups sized by ln_pf_shape,
+// kLnPfWavesPerCU wavefronts per CU.
 rr_status plan_layernorm(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype y_dtype,
                          rr_dtype w_dtype, rr_tier tier, int32_t cu_count, bool vec,
                          rr_plan* out)
@@ -188,10 +189,11 @@ rr_status plan_layernorm(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype 
         return RR_OK;
     }
     fill_rowwise_geometry(t, rows, cols, vec_elems, out);
-    if (t == RR_TIER_BLOCK) {
-        const int64_t chunks = ceil_div(cols, vec_elems);
-        if (vec && cols % vec_elems == 0 && ceil_div(chunks, (int64_t)kBlockThreads) <= kLnMaxChunks) {
-            const int64_t g = (int64_t)cu_count * kLnRowBlocksPerCU;
+    if (t == RR_TIER_BLOCK && vec && cols % vec_elems == 0) {
+        const LnPfShape sh = ln_pf_shape(cols / vec_elems);
+        if (sh.nt > 0) {
+            out->block = sh.nt;
+            const int64_t g = (int64_t)cu_count * (kLnPfWavesPerCU * 64 / sh.nt);
             out->grid = rows < g ? rows : g;
         }
     }
