@@ -140,7 +140,7 @@ extern "C" rr_status rr_layernorm_rows(const void* x, void* y, const void* gamma
             return RR_ERR_WORKSPACE;
     }
     rr::LayernormLaunch a{x, y, gamma, beta, mean_out, rstd_out, rows, cols, ld_x, ld_y,
-                          x_dtype, y_dtype, w_dtype, eps, vec, workspace, as_stream(stream)};
+                          x_dtype, y_dtype, w_dtype, eps, vec, workspace, cu, as_stream(stream)};
     return rr::launch_layernorm(p, a);
 }
 

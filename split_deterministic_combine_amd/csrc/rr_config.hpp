@@ -49,13 +49,15 @@ constexpr int64_t kSoftmaxWideMinChunks = (int64_t)kBlockThreads * kSoftmaxMaxCh
 constexpr int kSoftmaxSplitKUnroll = 4;
 // Layernorm.  Rows of whole aligned 16-byte chunks, up to kLnPfMaxChunks of
 // them, stay in registers on persistent workgroups whose size follows the
-// row (ln_pf_shape), kLnPfWavesPerCU wavefronts per CU in all.  Other rows
-// of up to kLnMaxChunks chunks per thread of 256 stay in registers one row
-// per workgroup; longer rows stream twice.  Split-K tiles are
-// kLnSplitKUnroll chunks per thread.
+// row (ln_pf_shape).  A CU gets kLnPfLoadsPerCU / (wavefronts per workgroup *
+// chunks per thread) of them (at least one): that many 16-byte loads per
+// lane in flight per CU, the measured optimum (fewer starve HBM, more
+// contend).  Other rows of up to kLnMaxChunks chunks per thread of 256 stay
+// in registers one row per workgroup; longer rows stream twice.  Split-K
+// tiles are kLnSplitKUnroll chunks per thread.
 constexpr int kLnMaxChunks = 8;
 constexpr int64_t kLnPfMaxChunks = 2048;
-constexpr int kLnPfWavesPerCU = 8;
+constexpr int kLnPfLoadsPerCU = 32;
 constexpr int kLnSplitKUnroll = 4;
 
 // Threads per row (nt) and chunks per thread (nch) of the persistent
@@ -68,11 +70,16 @@ constexpr LnPfShape ln_pf_shape(int64_t chunks)
 {
     return chunks <= 64     ? LnPfShape{64, 1}
            : chunks <= 128  ? LnPfShape{64, 2}
-           : chunks <= 256  ? LnPfShape{128, 2}
-           : chunks <= 512  ? LnPfShape{256, 2}
+           : chunks <= 256  ? LnPfShape{64, 4}
+           : chunks <= 512  ? LnPfShape{128, 4}
            : chunks <= 1024 ? LnPfShape{256, 4}
            : chunks <= kLnPfMaxChunks ? LnPfShape{512, 4}
                                       : LnPfShape{0, 0};
+}
+constexpr int ln_pf_blocks_per_cu(LnPfShape sh)
+{
+    return kLnPfLoadsPerCU / (sh.nt / 64 * sh.nch) > 0 ? kLnPfLoadsPerCU / (sh.nt / 64 * sh.nch)
+                                                       : 1;
 }
 
 // LSE merge: partitions staged per batch of loads, and workgroup size.

@@ -42,6 +42,7 @@ struct LayernormLaunch {
     float eps;
     bool vec;
     void* workspace;      // split-K only
+    int32_t cu;           // compute units of the current device
     hipStream_t stream;
 };
 

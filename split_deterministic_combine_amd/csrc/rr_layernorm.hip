@@ -567,19 +567,36 @@ __global__ __launch_bounds__(kBlockThreads) void k_layernorm_splitk_map(
 }
 
 // ---------------------------------------------------------------- launch
+// Persistent grid: the plan's, lowered to the workgroups that can be resident
+// at once (the kernel's occupancy times the CUs), so that no workgroup of a
+// persistent grid waits for another to finish before it starts.
+template <class K>
+static rr_status persistent_grid(K kernel, int nt, const rr_plan& p, const LayernormLaunch& a,
+                                 dim3* grid)
+{
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, nt, 0) != hipSuccess ||
+        per_cu < 1)
+        return RR_ERR_HIP;
+    const int64_t cap = (int64_t)per_cu * a.cu;
+    *grid = dim3((unsigned)(p.grid < cap ? p.grid : cap));
+    return RR_OK;
+}
+
 template <class XT, class YT, int NCH, int NT, bool AFF>
 static rr_status launch_pf_aff(const XT* x, YT* y, const Weights& g, const Weights& b,
                                const rr_plan& p, const LayernormLaunch& a)
 {
     constexpr int64_t kExactCols = (int64_t)NT * NCH * XIn<XT>::kChunk;
-    const dim3 grid((unsigned)p.grid), block(NT);
-    if (a.cols == kExactCols)
-        return launch_kernel(k_layernorm_rows_pf<XT, YT, NCH, NT, true, AFF>, grid, block, 0,
-                             a.stream, x, y, g, b, a.mean_out, a.rstd_out, a.rows, a.cols, a.ld_x,
-                             a.ld_y, a.eps);
-    return launch_kernel(k_layernorm_rows_pf<XT, YT, NCH, NT, false, AFF>, grid, block, 0,
-                         a.stream, x, y, g, b, a.mean_out, a.rstd_out, a.rows, a.cols, a.ld_x,
-                         a.ld_y, a.eps);
+    const bool exact = a.cols == kExactCols;
+    auto kernel = exact ? k_layernorm_rows_pf<XT, YT, NCH, NT, true, AFF>
+                        : k_layernorm_rows_pf<XT, YT, NCH, NT, false, AFF>;
+    dim3 grid;
+    const rr_status st = persistent_grid(kernel, NT, p, a, &grid);
+    if (st != RR_OK)
+        return st;
+    return launch_kernel(kernel, grid, dim3(NT), 0, a.stream, x, y, g, b, a.mean_out, a.rstd_out,
+                         a.rows, a.cols, a.ld_x, a.ld_y, a.eps);
 }
 
 template <class XT, class YT, int NCH, int NT>
@@ -611,8 +628,8 @@ static rr_status launch_block(const rr_plan& p, const XT* x, YT* y, const Weight
             switch (sh.nt * 16 + sh.nch) {
             case 64 * 16 + 1: return launch_pf<XT, YT, 1, 64>(x, y, g, b, p, a);
             case 64 * 16 + 2: return launch_pf<XT, YT, 2, 64>(x, y, g, b, p, a);
-            case 128 * 16 + 2: return launch_pf<XT, YT, 2, 128>(x, y, g, b, p, a);
-            case 256 * 16 + 2: return launch_pf<XT, YT, 2, 256>(x, y, g, b, p, a);
+            case 64 * 16 + 4: return launch_pf<XT, YT, 4, 64>(x, y, g, b, p, a);
+            case 128 * 16 + 4: return launch_pf<XT, YT, 4, 128>(x, y, g, b, p, a);
             case 256 * 16 + 4: return launch_pf<XT, YT, 4, 256>(x, y, g, b, p, a);
             case 512 * 16 + 4: return launch_pf<XT, YT, 4, 512>(x, y, g, b, p, a);
             default: break;  // too long for registers: stream below

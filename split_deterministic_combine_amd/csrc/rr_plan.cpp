@@ -160,7 +160,8 @@ rr_status plan_softmax(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype y_
 
 // Layernorm: the softmax's tier rule.  The block tier keeps rows of whole
 // aligned chunks in registers on persistent workgroups sized by ln_pf_shape,
-// kLnPfWavesPerCU wavefronts per CU.
+// ln_pf_blocks_per_cu of them per CU (the launch lowers that to what the
+// kernel's occupancy allows, so a persistent grid never queues).
 rr_status plan_layernorm(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype y_dtype,
                          rr_dtype w_dtype, rr_tier tier, int32_t cu_count, bool vec,
                          rr_plan* out)
@@ -193,7 +194,7 @@ rr_status plan_layernorm(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype 
         const LnPfShape sh = ln_pf_shape(cols / vec_elems);
         if (sh.nt > 0) {
             out->block = sh.nt;
-            const int64_t g = (int64_t)cu_count * (kLnPfWavesPerCU * 64 / sh.nt);
+            const int64_t g = (int64_t)cu_count * ln_pf_blocks_per_cu(sh);
             out->grid = rows < g ? rows : g;
         }
     }

@@ -129,8 +129,15 @@ def test_softmax_splitk_every_workgroup_gets_a_tile(rows, cols):
 
 
 def test_layernorm_tier_rule_and_geometry():
-    assert rr.plan_layernorm(16384, 4096)["tier"] == "block"
-    assert rr.plan_layernorm(16384, 4096)["grid"] == 512       # persistent rows: 2 per CU
+    p = rr.plan_layernorm(16384, 4096)
+    # 512 chunks: 128 threads x 4 chunks; 32 loads per lane in flight per CU
+    # = 4 workgroups of 2 wavefronts x 4 chunks per CU
+    assert p["tier"] == "block" and p["block"] == 128 and p["grid"] == 1024
+    p = rr.plan_layernorm(262144, 512)
+    assert p["block"] == 64 and p["grid"] == 256 * 32            # 64 chunks: 1 per lane
+    p = rr.plan_layernorm(4096, 16384)
+    assert p["block"] == 512 and p["grid"] == 256                # 2048 chunks: 4 per lane
+    assert rr.plan_layernorm(4096, 16392)["grid"] == 4096        # too long: one row per workgroup
     assert rr.plan_layernorm(16384, 4095)["grid"] == 16384     # ragged rows: one per workgroup
     assert rr.plan_layernorm(100, 40)["tier"] == "wave"
     assert rr.plan_layernorm(100, 8)["tier"] == "tiled"
