@@ -9,6 +9,8 @@ One step runs every operation of the path once on its synthetic workload:
 Outside the step (and outside `value`), the operations built after it are
 timed on their own workloads and reported under "next_rows":
   softmax_long  bf16 softmax over [16, 2^22]                 (split-K tier)
+  layernorm     bf16 layernorm over [16384, 4096], float32 gamma/beta,
+                float32 mean/rstd written                      (block tier)
 
 Inputs are resident in HBM before timing.  Buffer sets rotate from one step
 to the next so that the data touched by consecutive launches exceeds the
@@ -57,7 +59,9 @@ KERNEL_OF_OP = {
     "merge": "k_lse_merge_po<unsigned short, 32, 4>",
     "softmax_long_stats": "k_softmax_splitk_stats<unsigned short, true>",
     "softmax_long_map": "k_softmax_splitk_map<unsigned short, unsigned short, true>",
+    "layernorm": "k_layernorm_rows_pf<unsigned short, unsigned short, 4, 128, true, true>",
 }
+LAYERNORM = (16384, 4096)
 SOFTMAX_LONG = (16, 1 << 22)
 ALGO_BYTES = {
     "short_sum": 1048576 * 48 * 4 + 1048576 * 4,
@@ -70,9 +74,12 @@ ALGO_BYTES = {
     # 16 x 64 (max, sum) pairs; the map pass reads the pairs and x, writes y
     "softmax_long_stats": 16 * (1 << 22) * 2 + 16 * 64 * 8,
     "softmax_long_map": 16 * (1 << 22) * 2 * 2 + 16 * 64 * 64 * 8,
+    # x read and y written once (bf16), gamma/beta read once, mean/rstd written
+    "layernorm": 16384 * 4096 * 2 * 2 + 2 * 4096 * 4 + 2 * 16384 * 4,
 }
 # next-row operations as a whole: x read once and y written once
-NEXT_BYTES = {"softmax_long": 16 * (1 << 22) * 2 * 2}
+NEXT_BYTES = {"softmax_long": 16 * (1 << 22) * 2 * 2,
+              "layernorm": 16384 * 4096 * 2 * 2 + 2 * 4096 * 4 + 2 * 16384 * 4}
 STEP_OPS = ("short_sum", "short_max", "softmax", "long_sum", "long_max", "merge")
 COPY_BYTES = 512 << 20
 
@@ -253,6 +260,7 @@ def main():
     host["merge"] = synth.lse_merge()
     if not args.no_next:
         host["softmax_long"] = synth.softmax_long_rows()
+        host["layernorm"] = synth.layernorm_rows()
     log("inputs generated in %.1f s" % (time.time() - t0))
 
     sets = {"short": 5, "softmax": 4, "long_f": 1, "long_i": 1, "merge": 8}
@@ -272,6 +280,13 @@ def main():
         base = gpu(host["softmax_long"])
         dx["softmax_long"] = [base] + [base.clone() for _ in range(2)]
         dx["softmax_long_out"] = [torch.empty_like(base) for _ in range(3)]
+        xl, gl, bl = host["layernorm"]
+        base = gpu(xl)
+        dx["layernorm"] = [base] + [base.clone() for _ in range(3)]
+        dx["layernorm_out"] = [torch.empty_like(base) for _ in range(4)]
+        dx["layernorm_w"] = (gpu(gl), gpu(bl))
+        dx["layernorm_stats"] = [(torch.empty(LAYERNORM[0], device=dev),
+                                  torch.empty(LAYERNORM[0], device=dev)) for _ in range(4)]
     y_short_sum = torch.empty(1048576, dtype=torch.float32, device=dev)
     y_short_max = torch.empty(1048576, dtype=torch.float32, device=dev)
     y_long_f = torch.empty(16, dtype=torch.float32, device=dev)
@@ -292,6 +307,10 @@ def main():
     next_ops = {
         "softmax_long": lambda i: rr.softmax_rows(dx["softmax_long"][i % 3],
                                                   out=dx["softmax_long_out"][i % 3]),
+        "layernorm": lambda i: rr.layernorm_rows(dx["layernorm"][i % 4], *dx["layernorm_w"], 1e-5,
+                                                 out=dx["layernorm_out"][i % 4],
+                                                 mean_out=dx["layernorm_stats"][i % 4][0],
+                                                 rstd_out=dx["layernorm_stats"][i % 4][1]),
     }
     only = args.only.split(",") if args.only else None
     names = [n for n in ops if only is None or n in only]
@@ -314,6 +333,19 @@ def main():
             y = dx["softmax_long_out"][0][pick].cpu().view(torch.int16).numpy().view(np.uint16)
             r = oracle.softmax_rows(np.ascontiguousarray(host["softmax_long"][pick]), "bf16")
             ok &= bool(bf16_ulp_diff(y, r).max() <= 1)
+        if "layernorm" in next_names:
+            xl, gl, bl = host["layernorm"]
+            pick = np.linspace(0, LAYERNORM[0] - 1, 8).astype(np.int64)
+            y = dx["layernorm_out"][0][pick].cpu().view(torch.int16).numpy().view(np.uint16)
+            r, rm, rs = oracle.layernorm_rows(np.ascontiguousarray(xl[pick]), gl, bl, 1e-5, "bf16")
+            yv = (y.astype(np.uint32) << 16).view(np.float32)
+            rv = (r.astype(np.uint32) << 16).view(np.float32)
+            # 1 bf16 ulp, or the float32 bar's absolute 1e-6 (cancellation near zero)
+            ok &= bool(np.all((bf16_ulp_diff(y, r) <= 1) | (np.abs(yv - rv) <= 1e-6)))
+            gm = dx["layernorm_stats"][0][0][pick].cpu().numpy()
+            gs = dx["layernorm_stats"][0][1][pick].cpu().numpy()
+            ok &= bool(np.all(np.abs(gm - rm) <= 1e-6 + 1e-5 * np.abs(rm)))
+            ok &= bool(np.all(np.abs(gs - rs) <= 1e-6 + 1e-5 * np.abs(rs)))
         # sampled rows of the full-size outputs of the pass above (no extra launches)
         xs = host["short"][:4096]
         if "short_sum" in names:
@@ -425,6 +457,11 @@ def main():
             next_rows[n] = {"ms_mean": round(mean, 5), "ms_median": round(ts[len(ts) // 2], 5),
                             "ms_min": round(ts[0], 5), "bytes": NEXT_BYTES[n],
                             "GBps": round(gbs, 1), "pct_peak": round(100 * gbs / PEAK_HBM_GBS, 1)}
+        if "layernorm" in next_rows:
+            next_rows["layernorm"].update({
+                "config": "bf16 layernorm [%d, %d] -> bf16, float32 gamma/beta, float32 "
+                          "mean/rstd, block tier (persistent)" % LAYERNORM,
+                "kernels": [KERNEL_OF_OP["layernorm"]]})
         if "softmax_long" in next_rows:
             r, c = SOFTMAX_LONG
             next_rows["softmax_long"].update({
