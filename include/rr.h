@@ -1,11 +1,12 @@
 /*
  * rr.h -- deterministic row reductions on AMD Instinct MI355X (gfx950).
  *
- * A C ABI over hand-written HIP kernels.  Four operations:
+ * A C ABI over hand-written HIP kernels.  Five operations:
  *
  *   rr_reduce_rows       sum / max / min of every row over its last axis, on
  *                        float32 or int32 values, through one of five tiers
  *                        (wave, block, tiled, serial, split-K).
+ *   rr_reduce_rows_multi sum, max and min of every row over one read.
  *   rr_softmax_rows      two-pass softmax of every row (pass 1: the online
  *                        (max, sum) monoid; pass 2: a map that writes y).
  *   rr_layernorm_rows    two-pass layer normalisation of every row (pass 1:
@@ -67,7 +68,10 @@ typedef enum {
 
 typedef enum { RR_F32 = 0, RR_I32 = 1, RR_BF16 = 2 } rr_dtype;
 
-typedef enum { RR_SUM = 0, RR_MAX = 1, RR_MIN = 2 } rr_op;
+/* RR_SUM_MAX_MIN names the three statistics of rr_reduce_rows_multi in the
+ * planner queries (rr_plan_reduce, rr_workspace_bytes); rr_reduce_rows rejects
+ * it with RR_ERR_OP. */
+typedef enum { RR_SUM = 0, RR_MAX = 1, RR_MIN = 2, RR_SUM_MAX_MIN = 3 } rr_op;
 
 /* Tiers of "reduce" (algorithm.gpu.rowwise), tier semantics. */
 typedef enum {
@@ -117,6 +121,8 @@ typedef struct {
  * SERIAL is used only when forced.  WAVE is legal for cols <= 64 only.
  * SPLITK: G = clamp(ceil(4*cu_count/rows), 1, min(256, ceil(cols/16384), tiles))
  * with tiles = ceil(cols / tile_cols), tile_cols = 8192 (2048 on the scalar path).
+ * Workspace: rows * 4 ticket bytes padded to 256, then rows * G partials of 8
+ * bytes (16 for RR_SUM_MAX_MIN).
  * Returns RR_ERR_SHAPE for negative sizes or ld < cols, RR_ERR_DTYPE/OP for
  * unsupported dtype/op, RR_ERR_TIER for an illegal forced tier.
  */
@@ -155,11 +161,12 @@ rr_status rr_plan_layernorm(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dty
  *   tier   RR_TIER_AUTO or a forced tier
  *   workspace, workspace_bytes
  *          device scratch for RR_TIER_SPLITK (ignored otherwise; may be NULL
- *          when the plan needs 0 bytes).  Size: rr_workspace_bytes.  Its
- *          ticket words (the first bytes) must be zero before its first use;
- *          every completed call leaves them zero again (the partial slots
- *          keep stale values, which a call always writes before it reads
- *          them).  One workspace must not serve two calls in flight.
+ *          when the plan needs 0 bytes).  Size: rr_workspace_bytes.  It must
+ *          be all zero before its first use (rr_workspace_reset); every
+ *          completed call leaves every byte it used zero again (the last
+ *          workgroup of a row resets the row's ticket and clears the partial
+ *          slots it read), so calls of any shape may share one workspace.
+ *          One workspace must not serve two calls in flight.
  *
  * Arithmetic: float SUM accumulates in double and rounds once to float
  * (nearest even); int32 SUM wraps modulo 2^32; MAX/MIN on float use the
@@ -173,6 +180,30 @@ rr_status rr_plan_layernorm(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dty
 rr_status rr_reduce_rows(const void* x, void* y, int64_t rows, int64_t cols, int64_t ld,
                          rr_dtype dtype, rr_op op, rr_tier tier, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/*
+ * rr_reduce_rows_multi -- the sum, the maximum and the minimum of every row
+ * over one read of x.  "reduce" (algorithm.gpu.rowwise), description: the
+ * body combines each state that needs a cross-thread combine on its own;
+ * here the three states travel together through every fold, each combined
+ * by its own operation with the arithmetic of rr_reduce_rows (so each output
+ * equals, bit for bit, what rr_reduce_rows gives for that op on the same
+ * tier).
+ *
+ *   x                   device, [rows][ld] of dtype (RR_F32 or RR_I32)
+ *   y_sum, y_max, y_min device, [rows] of dtype, or NULL (not computed into
+ *                       memory); at least one must be non-NULL (RR_ERR_NULL)
+ *   tier, workspace, workspace_bytes
+ *                       as rr_reduce_rows; the split-K workspace holds
+ *                       16-byte partials (rr_workspace_bytes with op
+ *                       RR_SUM_MAX_MIN), tickets zero before first use and
+ *                       left zero by every completed call.
+ * rows == 0 is a no-op; cols == 0 writes each identity.
+ */
+rr_status rr_reduce_rows_multi(const void* x, void* y_sum, void* y_max, void* y_min,
+                               int64_t rows, int64_t cols, int64_t ld, rr_dtype dtype,
+                               rr_tier tier, void* workspace, size_t workspace_bytes,
+                               void* stream);
 
 /*
  * rr_softmax_rows -- y[r][j] = exp(x[r][j] - m_r) / s_r with

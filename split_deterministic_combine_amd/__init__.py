@@ -8,6 +8,7 @@ the first call raises.
 
 Operations (names as in the C ABI):
   reduce_rows        sum / max / min over the last axis (float32, int32)
+  reduce_rows_multi  sum, max and min over the last axis from one read
   softmax_rows       two-pass softmax over the last axis (bf16 / float32)
   layernorm_rows     two-pass layer normalisation over the last axis
   splitk_lse_merge   merge of P split-K partial attention outputs by their
@@ -20,7 +21,7 @@ import threading
 import torch
 
 __all__ = [
-    "RRError", "reduce_rows", "softmax_rows", "layernorm_rows", "splitk_lse_merge",
+    "RRError", "reduce_rows", "reduce_rows_multi", "softmax_rows", "layernorm_rows", "splitk_lse_merge",
     "plan_reduce", "plan_softmax", "plan_layernorm", "select_tier", "workspace_bytes", "workspace_reset", "device_cu_count",
     "version", "lib_path", "TIERS", "OPS",
 ]
@@ -31,6 +32,7 @@ _LIB_PATH = os.path.join(_HERE, "librr.so")
 RR_OK = 0
 _DTYPES = {torch.float32: 0, torch.int32: 1, torch.bfloat16: 2}
 OPS = {"sum": 0, "max": 1, "min": 2}
+OP_SUM_MAX_MIN = 3  # the three statistics of reduce_rows_multi (planner queries)
 TIERS = {"auto": 0, "wave": 1, "block": 2, "tiled": 3, "serial": 4, "splitk": 5}
 TIER_NAMES = {v: k for k, v in TIERS.items()}
 KIND_REDUCE, KIND_SOFTMAX, KIND_LAYERNORM = 0, 1, 2
@@ -74,6 +76,8 @@ def _load():
         lib = ctypes.CDLL(_LIB_PATH)
         vp, i64, i32, st = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int
         lib.rr_reduce_rows.argtypes = [vp, vp, i64, i64, i64, st, st, st, vp, ctypes.c_size_t, vp]
+        lib.rr_reduce_rows_multi.argtypes = [vp, vp, vp, vp, i64, i64, i64, st, st, vp,
+                                             ctypes.c_size_t, vp]
         lib.rr_softmax_rows.argtypes = [vp, vp, i64, i64, i64, i64, st, st, st, vp,
                                         ctypes.c_size_t, vp]
         lib.rr_splitk_lse_merge.argtypes = [vp, vp, vp, vp, i32, i64, i32, ctypes.c_float, st, vp]
@@ -91,7 +95,7 @@ def _load():
         lib.rr_version.restype = ctypes.c_int
         lib.rr_test_set_splitk_skew.argtypes = [i32]
         lib.rr_test_set_splitk_skew.restype = None
-        for name in ("rr_reduce_rows", "rr_softmax_rows", "rr_splitk_lse_merge", "rr_plan_reduce",
+        for name in ("rr_reduce_rows", "rr_reduce_rows_multi", "rr_softmax_rows", "rr_splitk_lse_merge", "rr_plan_reduce",
                      "rr_plan_softmax", "rr_layernorm_rows", "rr_plan_layernorm",
                      "rr_workspace_bytes", "rr_select_tier",
                      "rr_workspace_reset", "rr_device_cu_count"):
@@ -237,6 +241,46 @@ def reduce_rows(x, op="sum", tier="auto", out=None):
     return out
 
 
+def reduce_rows_multi(x, stats=("sum", "max", "min"), tier="auto", out=None):
+    """Several row statistics of ``x`` over its last axis from one read.
+
+    ``stats`` is any non-empty subset of ("sum", "max", "min"); returns a dict
+    from each requested name to a tensor of shape ``x.shape[:-1]`` (``out``, a
+    dict of such tensors, may supply them).  Each result equals, bit for bit,
+    ``reduce_rows`` of that op on the same tier.
+    """
+    lib = _load()
+    stats = tuple(stats)
+    if not stats or any(k not in OPS for k in stats):
+        raise ValueError("stats must be a non-empty subset of %s" % (tuple(OPS),))
+    x2, rows, cols, ld = _as_rows(x)
+    dt = _dtype_code(x.dtype)
+    out = dict(out or {})
+    ptrs = []
+    for k in ("sum", "max", "min"):
+        if k not in stats:
+            ptrs.append(None)
+            continue
+        t = out.get(k)
+        if t is None:
+            t = out[k] = torch.empty(x.shape[:-1], dtype=x.dtype, device=x.device)
+        if t.dtype != x.dtype or t.numel() != rows or not t.is_contiguous():
+            raise ValueError("out[%r] must be a contiguous %s tensor of %d elements" % (
+                k, x.dtype, rows))
+        ptrs.append(ctypes.c_void_p(t.data_ptr()))
+    t = TIERS[tier]
+    with _OnDevice(x.device):
+        stream = _stream_ptr(x.device)
+        need = _workspace_need(rows, cols, ld, dt, OP_SUM_MAX_MIN, t, _cu_count(x.device))
+        ws_ptr, ws_len = None, 0
+        if need:
+            ws = _workspace("reduce", x.device, stream.value, need)
+            ws_ptr, ws_len = ctypes.c_void_p(ws.data_ptr()), ws.numel()
+        _check(lib.rr_reduce_rows_multi(ctypes.c_void_p(x2.data_ptr()), *ptrs, rows, cols, ld, dt,
+                                        t, ws_ptr, ws_len, stream))
+    return {k: out[k] for k in stats}
+
+
 def softmax_rows(x, out_dtype=None, tier="auto", out=None):
     """Softmax of every row of ``x`` over its last axis (x: bfloat16 or float32)."""
     lib = _lib or _load()
@@ -363,10 +407,12 @@ def _plan_dict(plan):
 
 
 def plan_reduce(rows, cols, dtype=torch.float32, op="sum", tier="auto", cu_count=256, ld=None):
-    """Host-only launch plan of rr_reduce_rows (needs no GPU)."""
+    """Host-only launch plan of rr_reduce_rows (op "sum_max_min": of
+    rr_reduce_rows_multi); needs no GPU."""
     lib = _load()
     plan = _Plan()
-    _check(lib.rr_plan_reduce(rows, cols, cols if ld is None else ld, _dtype_code(dtype), OPS[op],
+    code = OP_SUM_MAX_MIN if op == "sum_max_min" else OPS[op]
+    _check(lib.rr_plan_reduce(rows, cols, cols if ld is None else ld, _dtype_code(dtype), code,
                               TIERS[tier], cu_count, ctypes.byref(plan)))
     return _plan_dict(plan)
 

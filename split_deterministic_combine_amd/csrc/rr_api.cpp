@@ -64,6 +64,7 @@ extern "C" rr_status rr_reduce_rows(const void* x, void* y, int64_t rows, int64_
                                     int64_t ld, rr_dtype dtype, rr_op op, rr_tier tier,
                                     void* workspace, size_t workspace_bytes, void* stream)
 {
+    if (op == RR_SUM_MAX_MIN) return RR_ERR_OP;  // that is rr_reduce_rows_multi
     // Shape / type / tier checks that need no device.
     rr_plan p;
     rr_status st = rr::plan_reduce(rows, cols, ld, dtype, op, tier, 1, true, &p);
@@ -75,8 +76,36 @@ extern "C" rr_status rr_reduce_rows(const void* x, void* y, int64_t rows, int64_
     const bool vec = rows_aligned16(x, ld, rows, 4);
     if ((st = rr::plan_reduce(rows, cols, ld, dtype, op, tier, cu, vec, &p)) != RR_OK) return st;
 
-    rr::ReduceLaunch a{x, y, rows, cols, ld, dtype, op, vec, workspace,
-                       g_splitk_skew.load(std::memory_order_relaxed), as_stream(stream)};
+    rr::ReduceLaunch a{x, y, rows, cols, ld, dtype, op, false, {nullptr, nullptr, nullptr}, vec,
+                       workspace, g_splitk_skew.load(std::memory_order_relaxed),
+                       as_stream(stream)};
+    if (cols == 0) return rr::launch_reduce_identity(a);
+    if (p.tier == RR_TIER_SPLITK) {
+        if (!workspace || workspace_bytes < p.workspace_bytes || !aligned(workspace, 8))
+            return RR_ERR_WORKSPACE;
+    }
+    return rr::launch_reduce(p, a);
+}
+
+extern "C" rr_status rr_reduce_rows_multi(const void* x, void* y_sum, void* y_max, void* y_min,
+                                          int64_t rows, int64_t cols, int64_t ld, rr_dtype dtype,
+                                          rr_tier tier, void* workspace, size_t workspace_bytes,
+                                          void* stream)
+{
+    rr_plan p;
+    rr_status st = rr::plan_reduce(rows, cols, ld, dtype, RR_SUM_MAX_MIN, tier, 1, true, &p);
+    if (st != RR_OK) return st;
+    if (rows == 0) return RR_OK;
+    if (!y_sum && !y_max && !y_min) return RR_ERR_NULL;
+    if (!x && cols > 0) return RR_ERR_NULL;
+    int32_t cu = 0;
+    if ((st = current_cu(&cu)) != RR_OK) return st;
+    const bool vec = rows_aligned16(x, ld, rows, 4);
+    if ((st = rr::plan_reduce(rows, cols, ld, dtype, RR_SUM_MAX_MIN, tier, cu, vec, &p)) != RR_OK)
+        return st;
+    rr::ReduceLaunch a{x, nullptr, rows, cols, ld, dtype, RR_SUM, true, {y_sum, y_max, y_min},
+                       vec, workspace, g_splitk_skew.load(std::memory_order_relaxed),
+                       as_stream(stream)};
     if (cols == 0) return rr::launch_reduce_identity(a);
     if (p.tier == RR_TIER_SPLITK) {
         if (!workspace || workspace_bytes < p.workspace_bytes || !aligned(workspace, 8))

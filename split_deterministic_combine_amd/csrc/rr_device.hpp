@@ -38,35 +38,33 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
     return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
 
-// DPP move of any 4- or 8-byte trivially copyable value.
+// A trivially copyable value as 32-bit words (for cross-lane moves).
+template <class T>
+struct Words {
+    static_assert(sizeof(T) % 4 == 0, "values move as whole 32-bit words");
+    uint32_t w[sizeof(T) / 4];
+};
+
+// DPP move of any trivially copyable value of whole 32-bit words, word by
+// word (a tuple state moves each of its states on its own).
 template <int CTRL, class T>
 __device__ __forceinline__ T dpp(T v)
 {
-    static_assert(sizeof(T) == 4 || sizeof(T) == 8, "dpp of 4 or 8 bytes");
-    if constexpr (sizeof(T) == 4) {
-        return __builtin_bit_cast(T, dpp_u32<CTRL>(__builtin_bit_cast(uint32_t, v)));
-    } else {
-        struct P { uint32_t lo, hi; };
-        P p = __builtin_bit_cast(P, v);
-        p.lo = dpp_u32<CTRL>(p.lo);
-        p.hi = dpp_u32<CTRL>(p.hi);
-        return __builtin_bit_cast(T, p);
-    }
+    Words<T> p = __builtin_bit_cast(Words<T>, v);
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(T) / 4); ++i)
+        p.w[i] = dpp_u32<CTRL>(p.w[i]);
+    return __builtin_bit_cast(T, p);
 }
 
 template <class T>
 __device__ __forceinline__ T readlane(T v, int lane)
 {
-    static_assert(sizeof(T) == 4 || sizeof(T) == 8, "readlane of 4 or 8 bytes");
-    if constexpr (sizeof(T) == 4) {
-        return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
-    } else {
-        struct P { int lo, hi; };
-        P p = __builtin_bit_cast(P, v);
-        p.lo = __builtin_amdgcn_readlane(p.lo, lane);
-        p.hi = __builtin_amdgcn_readlane(p.hi, lane);
-        return __builtin_bit_cast(T, p);
-    }
+    Words<T> p = __builtin_bit_cast(Words<T>, v);
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(T) / 4); ++i)
+        p.w[i] = (uint32_t)__builtin_amdgcn_readlane((int)p.w[i], lane);
+    return __builtin_bit_cast(T, p);
 }
 
 // ------------------------------------------------------------- monoids
@@ -83,56 +81,127 @@ __device__ __forceinline__ float f32_from_order_key(int32_t k)
     return __int_as_float(k ^ ((k >> 31) & 0x7FFFFFFF));
 }
 
+// Every monoid writes its result with store(out, r, acc); out_t is the
+// output pointer (a tuple of pointers for the tuple monoids below).
 // float SUM: double accumulator, one rounding at the end.
 struct SumF32 {
     using in_t = float;
     using acc_t = double;
+    using out_t = float*;
     __device__ static acc_t identity() { return 0.0; }
     __device__ static acc_t lift(float x) { return (double)x; }
     __device__ static acc_t combine(acc_t a, acc_t b) { return a + b; }
     __device__ static float finish(acc_t a) { return (float)a; }
+    __device__ static void store(out_t y, int64_t r, acc_t a) { y[r] = finish(a); }
 };
 // float MAX / MIN over totalOrder keys (identities are the extreme keys).
 struct MaxF32 {
     using in_t = float;
     using acc_t = int32_t;
+    using out_t = float*;
     __device__ static acc_t identity() { return INT32_MIN; }
     __device__ static acc_t lift(float x) { return f32_order_key(x); }
     __device__ static acc_t combine(acc_t a, acc_t b) { return a > b ? a : b; }
     __device__ static float finish(acc_t a) { return f32_from_order_key(a); }
+    __device__ static void store(out_t y, int64_t r, acc_t a) { y[r] = finish(a); }
 };
 struct MinF32 {
     using in_t = float;
     using acc_t = int32_t;
+    using out_t = float*;
     __device__ static acc_t identity() { return INT32_MAX; }
     __device__ static acc_t lift(float x) { return f32_order_key(x); }
     __device__ static acc_t combine(acc_t a, acc_t b) { return a < b ? a : b; }
     __device__ static float finish(acc_t a) { return f32_from_order_key(a); }
+    __device__ static void store(out_t y, int64_t r, acc_t a) { y[r] = finish(a); }
 };
 // int32 SUM wraps modulo 2^32 (unsigned arithmetic), so order never matters.
 struct SumI32 {
     using in_t = int32_t;
     using acc_t = uint32_t;
+    using out_t = int32_t*;
     __device__ static acc_t identity() { return 0u; }
     __device__ static acc_t lift(int32_t x) { return (uint32_t)x; }
     __device__ static acc_t combine(acc_t a, acc_t b) { return a + b; }
     __device__ static int32_t finish(acc_t a) { return (int32_t)a; }
+    __device__ static void store(out_t y, int64_t r, acc_t a) { y[r] = finish(a); }
 };
 struct MaxI32 {
     using in_t = int32_t;
     using acc_t = int32_t;
+    using out_t = int32_t*;
     __device__ static acc_t identity() { return INT32_MIN; }
     __device__ static acc_t lift(int32_t x) { return x; }
     __device__ static acc_t combine(acc_t a, acc_t b) { return a > b ? a : b; }
     __device__ static int32_t finish(acc_t a) { return a; }
+    __device__ static void store(out_t y, int64_t r, acc_t a) { y[r] = finish(a); }
 };
 struct MinI32 {
     using in_t = int32_t;
     using acc_t = int32_t;
+    using out_t = int32_t*;
     __device__ static acc_t identity() { return INT32_MAX; }
     __device__ static acc_t lift(int32_t x) { return x; }
     __device__ static acc_t combine(acc_t a, acc_t b) { return a < b ? a : b; }
     __device__ static int32_t finish(acc_t a) { return a; }
+    __device__ static void store(out_t y, int64_t r, acc_t a) { y[r] = finish(a); }
+};
+
+// Several statistics over one read ("reduce", algorithm.gpu.rowwise: the body
+// combines each state needing a cross-thread combine on its own): the tuple
+// of the SUM, MAX and MIN states, each folded and combined by its own
+// operation, so the tuple combine is bit-commutative because each part is.
+// Outputs may be NULL (that statistic is not written).
+template <class T>
+struct Outs3 {
+    T* sum;
+    T* max;
+    T* min;
+};
+struct MultiF32 {
+    using in_t = float;
+    struct acc_t {
+        double sum;
+        int32_t maxk, mink;  // totalOrder keys
+    };
+    using out_t = Outs3<float>;
+    __device__ static acc_t identity() { return acc_t{0.0, INT32_MIN, INT32_MAX}; }
+    __device__ static acc_t lift(float x)
+    {
+        const int32_t k = f32_order_key(x);
+        return acc_t{(double)x, k, k};
+    }
+    __device__ static acc_t combine(acc_t a, acc_t b)
+    {
+        return acc_t{a.sum + b.sum, a.maxk > b.maxk ? a.maxk : b.maxk,
+                     a.mink < b.mink ? a.mink : b.mink};
+    }
+    __device__ static void store(out_t y, int64_t r, acc_t a)
+    {
+        if (y.sum) y.sum[r] = (float)a.sum;
+        if (y.max) y.max[r] = f32_from_order_key(a.maxk);
+        if (y.min) y.min[r] = f32_from_order_key(a.mink);
+    }
+};
+struct MultiI32 {
+    using in_t = int32_t;
+    struct acc_t {
+        uint32_t sum;  // wraps modulo 2^32
+        int32_t max, min;
+    };
+    using out_t = Outs3<int32_t>;
+    __device__ static acc_t identity() { return acc_t{0u, INT32_MIN, INT32_MAX}; }
+    __device__ static acc_t lift(int32_t x) { return acc_t{(uint32_t)x, x, x}; }
+    __device__ static acc_t combine(acc_t a, acc_t b)
+    {
+        return acc_t{a.sum + b.sum, a.max > b.max ? a.max : b.max, a.min < b.min ? a.min : b.min};
+    }
+    __device__ static void store(out_t y, int64_t r, acc_t a)
+    {
+        if (y.sum) y.sum[r] = (int32_t)a.sum;
+        if (y.max) y.max[r] = a.max;
+        if (y.min) y.min[r] = a.min;
+    }
 };
 
 // Online softmax state (m, s): m the largest value seen, s = sum exp(x - m).
@@ -342,7 +411,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float a)
 template <class A>
 __device__ __forceinline__ void publish_partial(A* slot, A v)
 {
-    __hip_atomic_store(slot, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if constexpr (sizeof(A) == 4 || sizeof(A) == 8) {
+        __hip_atomic_store(slot, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {  // a tuple state: word by word, all acknowledged before the ticket
+        const Words<A> p = __builtin_bit_cast(Words<A>, v);
+        uint32_t* s = reinterpret_cast<uint32_t*>(slot);
+#pragma unroll
+        for (int i = 0; i < (int)(sizeof(A) / 4); ++i)
+            __hip_atomic_store(s + i, p.w[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0)
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -350,7 +427,27 @@ __device__ __forceinline__ void publish_partial(A* slot, A v)
 template <class A>
 __device__ __forceinline__ A read_partial(const A* slot)
 {
-    return __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if constexpr (sizeof(A) == 4 || sizeof(A) == 8) {
+        return __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+        Words<A> p;
+        const uint32_t* s = reinterpret_cast<const uint32_t*>(slot);
+#pragma unroll
+        for (int i = 0; i < (int)(sizeof(A) / 4); ++i)
+            p.w[i] = __hip_atomic_load(s + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return __builtin_bit_cast(A, p);
+    }
+}
+
+// Zero a partial slot (plain stores, word by word; the next kernel on the
+// stream sees them).
+template <class A>
+__device__ __forceinline__ void clear_partial(A* slot)
+{
+    uint32_t* s = reinterpret_cast<uint32_t*>(slot);
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(A) / 4); ++i)
+        s[i] = 0u;
 }
 
 // An (m, s) pair travels as one 64-bit word.

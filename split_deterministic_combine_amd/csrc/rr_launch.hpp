@@ -10,10 +10,12 @@ namespace rr {
 
 struct ReduceLaunch {
     const void* x;
-    void* y;
+    void* y;              // single statistic
     int64_t rows, cols, ld;
     rr_dtype dtype;
     rr_op op;
+    bool multi;           // sum, max and min over one read into ys (NULL: not written)
+    void* ys[3];
     bool vec;             // 128-bit loads allowed (alignment checked by the caller)
     void* workspace;      // split-K only
     int skew;             // test hook: split-K arrival skew (0 = off)

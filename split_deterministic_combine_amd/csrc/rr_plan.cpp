@@ -13,9 +13,9 @@
 
 namespace rr {
 
-uint64_t splitk_workspace_bytes(int64_t rows, int32_t slices)
+uint64_t splitk_workspace_bytes(int64_t rows, int32_t slices, int partial_bytes)
 {
-    return (uint64_t)(round_up(rows * 4, kWorkspaceAlign) + rows * (int64_t)slices * 8);
+    return (uint64_t)(round_up(rows * 4, kWorkspaceAlign) + rows * (int64_t)slices * partial_bytes);
 }
 
 uint64_t softmax_splitk_workspace_bytes(int64_t rows, int32_t slices)
@@ -89,7 +89,7 @@ rr_status plan_reduce(int64_t rows, int64_t cols, int64_t ld, rr_dtype dtype, rr
     if (!out) return RR_ERR_NULL;
     if (rows < 0 || cols < 0 || ld < cols) return RR_ERR_SHAPE;
     if (dtype != RR_F32 && dtype != RR_I32) return RR_ERR_DTYPE;
-    if (op != RR_SUM && op != RR_MAX && op != RR_MIN) return RR_ERR_OP;
+    if (op != RR_SUM && op != RR_MAX && op != RR_MIN && op != RR_SUM_MAX_MIN) return RR_ERR_OP;
     if (cu_count < 1) return RR_ERR_SHAPE;
     if ((int)tier < RR_TIER_AUTO || (int)tier > RR_TIER_SPLITK) return RR_ERR_TIER;
 
@@ -104,7 +104,7 @@ rr_status plan_reduce(int64_t rows, int64_t cols, int64_t ld, rr_dtype dtype, rr
     }
     fill_splitk_geometry(rows, cols, (int64_t)kSplitKUnroll * kBlockThreads * vec_elems, cu_count,
                          out);
-    out->workspace_bytes = splitk_workspace_bytes(rows, out->slices);
+    out->workspace_bytes = splitk_workspace_bytes(rows, out->slices, op == RR_SUM_MAX_MIN ? 16 : 8);
     return RR_OK;
 }
 

@@ -13,7 +13,7 @@ rr_status plan_softmax(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype y_
 rr_status plan_layernorm(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype y_dtype,
                          rr_dtype w_dtype, rr_tier tier, int32_t cu_count, bool vec,
                          rr_plan* out);
-uint64_t splitk_workspace_bytes(int64_t rows, int32_t slices);
+uint64_t splitk_workspace_bytes(int64_t rows, int32_t slices, int partial_bytes);
 uint64_t softmax_splitk_workspace_bytes(int64_t rows, int32_t slices);
 
 }  // namespace rr

@@ -12,6 +12,8 @@
 // The monoids (sum / max / min on 32-bit values) are the page's combine_fn.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "rr_config.hpp"
 #include "rr_device.hpp"
 #include "rr_launch.hpp"
@@ -74,7 +76,7 @@ __device__ __forceinline__ typename M::acc_t thread_fold(const typename M::in_t*
 // ------------------------------------------------------------ block tier
 template <class M, int VEC>
 __global__ __launch_bounds__(kBlockThreads) void k_reduce_block(
-    const typename M::in_t* __restrict__ x, typename M::in_t* __restrict__ y, int64_t rows,
+    const typename M::in_t* __restrict__ x, typename M::out_t y, int64_t rows,
     int64_t cols, int64_t ld)
 {
     using A = typename M::acc_t;
@@ -86,7 +88,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce_block(
         acc = block_reduce<M, kBlockThreads>(acc, slot[par]);
         par ^= 1;
         if (threadIdx.x == 0)
-            y[r] = M::finish(acc);
+            M::store(y, r, acc);
     }
 }
 
@@ -99,7 +101,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce_block(
 // wavefront has kWaveRowGroups loads in flight without branches between.
 template <class M, int VEC, int S>
 __global__ __launch_bounds__(kBlockThreads) void k_reduce_wave(
-    const typename M::in_t* __restrict__ x, typename M::in_t* __restrict__ y, int64_t rows,
+    const typename M::in_t* __restrict__ x, typename M::out_t y, int64_t rows,
     int64_t cols, int64_t ld)
 {
     using T = typename M::in_t;
@@ -153,7 +155,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce_wave(
             A t = segment_reduce<M, S>(acc[u]);
             const int64_t r = row0 + (int64_t)u * RPG + seg;
             if ((lane % S) == 0 && r < rows)
-                y[r] = M::finish(t);
+                M::store(y, r, t);
         }
     }
 }
@@ -165,7 +167,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce_wave(
 // to the last row (loads stay in bounds, results are not stored).
 template <class M, int VEC, int R>
 __global__ __launch_bounds__(kBlockThreads) void k_reduce_tiled(
-    const typename M::in_t* __restrict__ x, typename M::in_t* __restrict__ y, int64_t rows,
+    const typename M::in_t* __restrict__ x, typename M::out_t y, int64_t rows,
     int64_t cols, int64_t ld)
 {
     using T = typename M::in_t;
@@ -205,7 +207,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce_tiled(
 #pragma unroll
         for (int k = 0; k < R; ++k)
             if (r0 + k < rows)
-                y[r0 + k] = M::finish(acc[k]);
+                M::store(y, r0 + k, acc[k]);
     }
 }
 
@@ -243,12 +245,13 @@ __device__ __forceinline__ typename M::acc_t fold_tile(typename M::acc_t acc,
 // stream adjacent memory.  It then publishes its partial to part[r * G + g]
 // and takes a ticket on row r.  The workgroup that draws ticket G - 1 is the
 // last to arrive: it folds part[r * G + 0 .. G - 1] in ascending g, writes
-// y[r] and resets the ticket to zero for the next call.  `skew` (a test hook, normally 0) makes
+// y[r] and resets the ticket and the row's partial slots to zero for the
+// next call.  `skew` (a test hook, normally 0) makes
 // workgroup g wait about (G - 1 - g) * skew sleep periods before publishing,
 // so arrival order runs against rank order.
 template <class M, int VEC>
 __global__ __launch_bounds__(kBlockThreads) void k_reduce_splitk(
-    const typename M::in_t* __restrict__ x, typename M::in_t* __restrict__ y, int64_t rows,
+    const typename M::in_t* __restrict__ x, typename M::out_t y, int64_t rows,
     int64_t cols, int64_t ld, int32_t G, typename M::acc_t* part, uint32_t* ticket, int32_t skew)
 {
     using A = typename M::acc_t;
@@ -304,14 +307,19 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce_splitk(
         if (last) {
             // The whole workgroup gathers the G partials at once (G <= the
             // block size), then thread 0 folds them in ascending rank order.
-            for (int32_t k = threadIdx.x; k < G; k += kBlockThreads)
+            // Each slot is cleared once read, so a completed call leaves
+            // every workspace byte it used zero: a later call with more rows
+            // keeps its tickets where this one kept partials.
+            for (int32_t k = threadIdx.x; k < G; k += kBlockThreads) {
                 gathered[k] = read_partial(&part[r * G + k]);
+                clear_partial(&part[r * G + k]);
+            }
             __syncthreads();
             if (threadIdx.x == 0) {
                 A a = gathered[0];
                 for (int32_t k = 1; k < G; ++k)
                     a = M::combine(a, gathered[k]);
-                y[r] = M::finish(a);
+                M::store(y, r, a);
                 last = false;
                 __hip_atomic_store(&ticket[r], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
@@ -352,13 +360,26 @@ rr_status launch_fill_zero(void* p, size_t bytes, hipStream_t stream)
 }
 
 // ---------------------------------------------------------------- launch
+// The output argument of monoid M's kernels.
+template <class M>
+static typename M::out_t outputs_of(const ReduceLaunch& a)
+{
+    using O = typename M::out_t;
+    if constexpr (std::is_pointer<O>::value) {
+        return static_cast<O>(a.y);
+    } else {
+        using T = typename M::in_t;
+        return O{static_cast<T*>(a.ys[0]), static_cast<T*>(a.ys[1]), static_cast<T*>(a.ys[2])};
+    }
+}
+
 template <class M>
 static rr_status launch_monoid(const rr_plan& p, const ReduceLaunch& a)
 {
     using T = typename M::in_t;
     using A = typename M::acc_t;
     const T* x = static_cast<const T*>(a.x);
-    T* y = static_cast<T*>(a.y);
+    const typename M::out_t y = outputs_of<M>(a);
     const dim3 grid((unsigned)p.grid), block(kBlockThreads);
     const hipStream_t s = a.stream;
     switch (p.tier) {
@@ -402,6 +423,9 @@ static rr_status launch_monoid(const rr_plan& p, const ReduceLaunch& a)
 
 rr_status launch_reduce(const rr_plan& p, const ReduceLaunch& a)
 {
+    if (a.multi)
+        return a.dtype == RR_F32 ? launch_monoid<MultiF32>(p, a)
+                                 : a.dtype == RR_I32 ? launch_monoid<MultiI32>(p, a) : RR_ERR_DTYPE;
     if (a.dtype == RR_F32) {
         switch (a.op) {
         case RR_SUM: return launch_monoid<SumF32>(p, a);
@@ -418,16 +442,32 @@ rr_status launch_reduce(const rr_plan& p, const ReduceLaunch& a)
     return RR_ERR_DTYPE;
 }
 
-// cols == 0: every row gets the monoid identity.
+// cols == 0: every row gets the monoid identity (each requested output of a
+// tuple reduction its own).
+static uint32_t identity_bits(rr_dtype dtype, rr_op op)
+{
+    if (dtype == RR_F32)
+        return op == RR_SUM ? 0u : op == RR_MAX ? 0xFF800000u : 0x7F800000u;
+    return op == RR_SUM ? 0u : op == RR_MAX ? 0x80000000u : 0x7FFFFFFFu;
+}
+
 rr_status launch_reduce_identity(const ReduceLaunch& a)
 {
-    uint32_t v = 0;
-    if (a.dtype == RR_F32)
-        v = a.op == RR_SUM ? 0u : a.op == RR_MAX ? 0xFF800000u : 0x7F800000u;
-    else
-        v = a.op == RR_SUM ? 0u : a.op == RR_MAX ? 0x80000000u : 0x7FFFFFFFu;
-    return launch_kernel(k_fill_u32, dim3(grid_for(a.rows)), dim3(kBlockThreads), 0, a.stream,
-                         static_cast<uint32_t*>(a.y), a.rows, v);
+    const dim3 grid(grid_for(a.rows)), block(kBlockThreads);
+    if (!a.multi)
+        return launch_kernel(k_fill_u32, grid, block, 0, a.stream, static_cast<uint32_t*>(a.y),
+                             a.rows, identity_bits(a.dtype, a.op));
+    const rr_op ops[3] = {RR_SUM, RR_MAX, RR_MIN};
+    for (int i = 0; i < 3; ++i) {
+        if (!a.ys[i])
+            continue;
+        const rr_status st = launch_kernel(k_fill_u32, grid, block, 0, a.stream,
+                                           static_cast<uint32_t*>(a.ys[i]), a.rows,
+                                           identity_bits(a.dtype, ops[i]));
+        if (st != RR_OK)
+            return st;
+    }
+    return RR_OK;
 }
 
 }  // namespace rr

@@ -83,6 +83,31 @@ def test_splitk_every_workgroup_gets_a_tile(rows, cols):
     assert p["grid"] == rows * g
 
 
+def test_multi_stat_plan_uses_16_byte_partials():
+    p = rr.plan_reduce(16, 1 << 24, op="sum_max_min", cu_count=256)
+    assert p["tier"] == "splitk" and p["slices"] == 64
+    assert p["workspace_bytes"] == 256 + 16 * 64 * 16
+    assert rr.plan_reduce(1000, 48, op="sum_max_min")["tier"] == "wave"
+
+
+def test_multi_stat_entry_point_validates_before_touching_the_device():
+    lib = ctypes.CDLL(rr.lib_path())
+    vp, i64, it = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.rr_reduce_rows_multi.argtypes = [vp, vp, vp, vp, i64, i64, i64, it, it, vp,
+                                         ctypes.c_size_t, vp]
+    lib.rr_reduce_rows.argtypes = [vp, vp, i64, i64, i64, it, it, it, vp, ctypes.c_size_t, vp]
+    one = ctypes.c_void_p(16)  # never dereferenced: validation fails or no-ops first
+    assert lib.rr_reduce_rows_multi(None, one, None, None, -1, 4, 4, 0, 0, None, 0, None) == 2
+    assert lib.rr_reduce_rows_multi(None, one, None, None, 4, 8, 4, 0, 0, None, 0, None) == 2
+    assert lib.rr_reduce_rows_multi(None, one, None, None, 4, 8, 8, 2, 0, None, 0, None) == 3
+    assert lib.rr_reduce_rows_multi(None, one, None, None, 4, 100, 100, 0, 1, None, 0, None) == 4
+    assert lib.rr_reduce_rows_multi(None, one, None, None, 0, 8, 8, 0, 0, None, 0, None) == 0
+    assert lib.rr_reduce_rows_multi(None, None, None, None, 4, 8, 8, 0, 0, None, 0, None) == 1
+    assert lib.rr_reduce_rows_multi(None, one, None, None, 4, 8, 8, 0, 0, None, 0, None) == 1
+    # the tuple op is only for the planner queries
+    assert lib.rr_reduce_rows(None, None, 4, 8, 8, 0, 3, 0, None, 0, None) == 7
+
+
 def test_splitk_forced_on_short_rows_has_one_slice():
     p = rr.plan_reduce(64, 1000, tier="splitk", cu_count=256)
     assert p["slices"] == 1 and p["grid"] == 64

@@ -188,11 +188,19 @@ def test_long_rows_bits_do_not_depend_on_arrival_order(long_rows_data):
     assert torch.equal(skew_i, plain_i)
 
 
-def test_splitk_tickets_are_left_zero():
-    # The last workgroup of each row resets its ticket, so the same workspace
-    # serves the next call without a clearing pass.
-    x = to_gpu(synth.uniform_f32(9, (3, 200000)))
-    rr.reduce_rows(x, "sum", "splitk")
+def test_splitk_workspace_is_left_zero_for_any_next_shape():
+    # The last workgroup of each row resets its ticket and clears the partial
+    # slots it read, so the whole workspace is zero after every call and a
+    # call with more rows (tickets where the last call kept partials) works.
+    x = synth.uniform_f32(9, (3, 200000))
+    rr.reduce_rows(to_gpu(x), "sum", "splitk")
+    torch.cuda.synchronize()
+    for key, ws in rr._workspaces.items():
+        if key[0] == "reduce":
+            assert int(ws.count_nonzero()) == 0
+    xb = synth.uniform_f32(10, (255, 65536))
+    y = rr.reduce_rows(to_gpu(xb), "sum", "splitk")
+    assert_close_f32(to_host(y), oracle.reduce_rows(xb, "sum"), "more rows after fewer")
     torch.cuda.synchronize()
     reduce_ws = [ws for key, ws in rr._workspaces.items() if key[0] == "reduce"]
     assert reduce_ws
