@@ -11,6 +11,7 @@ timed on their own workloads and reported under "next_rows":
   softmax_long  bf16 softmax over [16, 2^22]                 (split-K tier)
   layernorm     bf16 layernorm over [16384, 4096], float32 gamma/beta,
                 float32 mean/rstd written                      (block tier)
+  multi_long    f32 sum, max and min over [16, 2^24] from one read (split-K)
 
 Inputs are resident in HBM before timing.  Buffer sets rotate from one step
 to the next so that the data touched by consecutive launches exceeds the
@@ -60,6 +61,7 @@ KERNEL_OF_OP = {
     "softmax_long_stats": "k_softmax_splitk_stats<unsigned short, true>",
     "softmax_long_map": "k_softmax_splitk_map<unsigned short, unsigned short, true>",
     "layernorm": "k_layernorm_rows_pf<unsigned short, unsigned short, 4, 128, true, true>",
+    "multi_long": "k_reduce_splitk<rr::MultiF32, 4>",
 }
 LAYERNORM = (16384, 4096)
 SOFTMAX_LONG = (16, 1 << 22)
@@ -76,9 +78,11 @@ ALGO_BYTES = {
     "softmax_long_map": 16 * (1 << 22) * 2 * 2 + 16 * 64 * 64 * 8,
     # x read and y written once (bf16), gamma/beta read once, mean/rstd written
     "layernorm": 16384 * 4096 * 2 * 2 + 2 * 4096 * 4 + 2 * 16384 * 4,
+    "multi_long": 16 * (1 << 24) * 4 + 3 * 16 * 4,
 }
 # next-row operations as a whole: x read once and y written once
-NEXT_BYTES = {"softmax_long": 16 * (1 << 22) * 2 * 2,
+NEXT_BYTES = {"multi_long": 16 * (1 << 24) * 4 + 3 * 16 * 4,
+              "softmax_long": 16 * (1 << 22) * 2 * 2,
               "layernorm": 16384 * 4096 * 2 * 2 + 2 * 4096 * 4 + 2 * 16384 * 4}
 STEP_OPS = ("short_sum", "short_max", "softmax", "long_sum", "long_max", "merge")
 COPY_BYTES = 512 << 20
@@ -304,7 +308,9 @@ def main():
         "merge": lambda i: rr.splitk_lse_merge(*dx["merge"][i % 8], 1.0, torch.bfloat16,
                                                out=dx["merge_out"][i % 8]),
     }
+    y_multi = {k: torch.empty(16, dtype=torch.float32, device=dev) for k in ("sum", "max", "min")}
     next_ops = {
+        "multi_long": lambda i: rr.reduce_rows_multi(dx["long_f"][0], out=y_multi),
         "softmax_long": lambda i: rr.softmax_rows(dx["softmax_long"][i % 3],
                                                   out=dx["softmax_long_out"][i % 3]),
         "layernorm": lambda i: rr.layernorm_rows(dx["layernorm"][i % 4], *dx["layernorm_w"], 1e-5,
@@ -333,6 +339,12 @@ def main():
             y = dx["softmax_long_out"][0][pick].cpu().view(torch.int16).numpy().view(np.uint16)
             r = oracle.softmax_rows(np.ascontiguousarray(host["softmax_long"][pick]), "bf16")
             ok &= bool(bf16_ulp_diff(y, r).max() <= 1)
+        if "multi_long" in next_names:
+            for k in ("sum", "max", "min"):
+                y = y_multi[k][:2].cpu().numpy()
+                r = oracle.reduce_rows(host["long_f"][:2], k)
+                ok &= bool(np.all(np.abs(y - r) <= 1e-6 + 1e-5 * np.abs(r)) if k == "sum"
+                           else np.array_equal(y, r))
         if "layernorm" in next_names:
             xl, gl, bl = host["layernorm"]
             pick = np.linspace(0, LAYERNORM[0] - 1, 8).astype(np.int64)
@@ -457,6 +469,11 @@ def main():
             next_rows[n] = {"ms_mean": round(mean, 5), "ms_median": round(ts[len(ts) // 2], 5),
                             "ms_min": round(ts[0], 5), "bytes": NEXT_BYTES[n],
                             "GBps": round(gbs, 1), "pct_peak": round(100 * gbs / PEAK_HBM_GBS, 1)}
+        if "multi_long" in next_rows:
+            next_rows["multi_long"].update({
+                "config": "f32 sum, max and min over [16, 16777216] from one read, split-K "
+                          "(G = 64, 16-byte partials)",
+                "kernels": [KERNEL_OF_OP["multi_long"]]})
         if "layernorm" in next_rows:
             next_rows["layernorm"].update({
                 "config": "bf16 layernorm [%d, %d] -> bf16, float32 gamma/beta, float32 "

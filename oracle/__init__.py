@@ -41,6 +41,8 @@ def _load():
         lib.rro_splitk_lse_merge.argtypes = [vp, vp, vp, vp, i32, i64, i32, ctypes.c_float,
                                              ctypes.c_int]
         lib.rro_splitk_lse_merge.restype = ctypes.c_int
+        lib.rro_reduce_axis.argtypes = [vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int]
+        lib.rro_reduce_axis.restype = ctypes.c_int
         lib.rro_layernorm_rows.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                            ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                            ctypes.c_double]
@@ -85,6 +87,27 @@ def reduce_rows(x, op):
     rc = lib.rro_reduce_rows(_ptr(x), _ptr(y), rows, cols, ld, dt, _OPS[op])
     if rc:
         raise ValueError("rro_reduce_rows rejected its arguments")
+    return y
+
+
+def reduce_axis(x, op):
+    """Sum/max/min over the middle axis of a contiguous [outer, axis, inner]
+    float32 or int32 array; returns [outer, inner]."""
+    lib = _load()
+    if x.dtype == np.float32:
+        dt = F32
+    elif x.dtype == np.int32:
+        dt = I32
+    else:
+        raise TypeError("reduce_axis takes float32 or int32")
+    if x.ndim != 3:
+        raise ValueError("expected [outer, axis, inner]")
+    x = np.ascontiguousarray(x)
+    outer, axis, inner = x.shape
+    y = np.empty((outer, inner), dtype=x.dtype)
+    rc = lib.rro_reduce_axis(_ptr(x), _ptr(y), outer, axis, inner, dt, _OPS[op])
+    if rc:
+        raise ValueError("rro_reduce_axis rejected its arguments")
     return y
 
 

@@ -225,6 +225,70 @@ int rro_reduce_rows(const void* x, void* y, int64_t rows, int64_t cols, int64_t 
     return RRO_OK;
 }
 
+/* ------------------------------------------------------ non-last axis */
+
+/*
+ * [RW] reduce, Args (ctx.axis is the reduce axis; the other dims are pinned)
+ * and tier semantics (the tiled tier owns adjacent output rows): the same
+ * fold as rro_reduce_rows, along the middle axis of x laid out
+ * [outer][axis][inner] (contiguous), into y [outer][inner]:
+ *   y[o][i] = fold over a = 0 .. axis-1, in that order, of x[o][a][i].
+ * Same arithmetic as rro_reduce_rows; axis == 0 writes the identity.
+ */
+int rro_reduce_axis(const void* x, void* y, int64_t outer, int64_t axis, int64_t inner,
+                    int dtype, int op)
+{
+    if (outer < 0 || axis < 0 || inner < 0)
+        return RRO_BAD;
+    if (op != RRO_SUM && op != RRO_MAX && op != RRO_MIN)
+        return RRO_BAD;
+    if (dtype != RRO_F32 && dtype != RRO_I32)
+        return RRO_BAD;
+    for (int64_t o = 0; o < outer; ++o) {
+        for (int64_t i = 0; i < inner; ++i) {
+            const int64_t base = o * axis * inner + i;  /* x[o][0][i]; step inner */
+            if (dtype == RRO_I32) {
+                const int32_t* xs = (const int32_t*)x;
+                int32_t out;
+                if (op == RRO_SUM) {
+                    uint32_t acc = 0;
+                    for (int64_t a = 0; a < axis; ++a)
+                        acc += (uint32_t)xs[base + a * inner];
+                    out = (int32_t)acc;
+                } else {
+                    int32_t acc = axis ? xs[base] : (op == RRO_MAX ? INT32_MIN : INT32_MAX);
+                    for (int64_t a = 1; a < axis; ++a) {
+                        const int32_t v = xs[base + a * inner];
+                        if (op == RRO_MAX ? v > acc : v < acc)
+                            acc = v;
+                    }
+                    out = acc;
+                }
+                ((int32_t*)y)[o * inner + i] = out;
+            } else {
+                const float* xs = (const float*)x;
+                float out;
+                if (op == RRO_SUM) {
+                    double acc = 0.0;
+                    for (int64_t a = 0; a < axis; ++a)
+                        acc += (double)xs[base + a * inner];
+                    out = (float)acc;
+                } else {
+                    float acc = axis ? xs[base] : (op == RRO_MAX ? -INFINITY : INFINITY);
+                    for (int64_t a = 1; a < axis; ++a) {
+                        const float v = xs[base + a * inner];
+                        if (op == RRO_MAX ? f32_total_before(acc, v) : f32_total_before(v, acc))
+                            acc = v;
+                    }
+                    out = acc;
+                }
+                ((float*)y)[o * inner + i] = out;
+            }
+        }
+    }
+    return RRO_OK;
+}
+
 /* ---------------------------------------------------------------- softmax */
 
 /*

@@ -277,6 +277,78 @@ def test_softmax_bf16_input_strided_and_empty():
     assert oracle.softmax_rows(np.zeros((3, 0), dtype=np.float32), "f32").shape == (3, 0)
 
 
+# ------------------------------------------------------------ non-last axis
+
+def test_reduce_axis_f32_sum_within_one_ulp_of_exact_column_sums():
+    x = synth.normal_f32(501, (3, 57, 11))
+    y = oracle.reduce_axis(x, "sum")
+    for o in range(3):
+        for i in range(11):
+            exact = sum((Fraction(float(v)) for v in x[o, :, i]), Fraction(0))
+            want = round_to_f32(exact)
+            got = float(y[o, i])
+            assert abs(got - want) <= float(np.spacing(np.float32(abs(want)))), (o, i)
+
+
+def test_reduce_axis_f32_sum_matches_numpy_double():
+    x = synth.normal_f32(502, (4, 300, 33))
+    want = x.astype(np.float64).sum(axis=1)
+    got = oracle.reduce_axis(x, "sum").astype(np.float64)
+    assert np.all(np.abs(got - want) <= np.spacing(np.abs(want).astype(np.float32)))
+
+
+def test_reduce_axis_int_sum_wraps_like_python_integers():
+    x = synth.ints_i32(503, (2, 40, 7), -(2 ** 31), 2 ** 31 - 1)
+    got = oracle.reduce_axis(x, "sum")
+    for o in range(2):
+        for i in range(7):
+            s = sum(int(v) for v in x[o, :, i]) % (1 << 32)
+            s = s - (1 << 32) if s >= (1 << 31) else s
+            assert int(got[o, i]) == s
+
+
+def test_reduce_axis_max_min_match_numpy():
+    for x in (synth.normal_f32(504, (5, 17, 9)), synth.ints_i32(505, (5, 17, 9), -9, 9)):
+        assert np.array_equal(oracle.reduce_axis(x, "max"), x.max(axis=1))
+        assert np.array_equal(oracle.reduce_axis(x, "min"), x.min(axis=1))
+
+
+def test_reduce_axis_int_extremes():
+    big, small = np.iinfo(np.int32).max, np.iinfo(np.int32).min
+    x = np.array([[[big, small], [5, -5], [big, small], [-7, 7]]], dtype=np.int32)
+    assert list(oracle.reduce_axis(x, "max")[0]) == [big, 7]
+    assert list(oracle.reduce_axis(x, "min")[0]) == [-7, small]
+    def wrap(v):
+        return (v + 2 ** 31) % 2 ** 32 - 2 ** 31
+    assert list(oracle.reduce_axis(x, "sum")[0]) == [wrap(2 * int(big) - 2), wrap(2 * int(small) + 2)]
+
+
+def test_reduce_axis_total_order_and_identities():
+    # column 0: -0 and +0 (max +0, min -0); column 1: a positive NaN is above
+    # +inf, a negative NaN below -inf
+    pnan = np.float32(np.nan)
+    nnan = -np.float32(np.nan)
+    x = np.array([[[-0.0, 1.0], [0.0, pnan], [-0.0, -np.inf]],
+                  [[0.0, nnan], [-0.0, np.inf], [0.0, 1.0]]], dtype=np.float32)
+    mx = oracle.reduce_axis(x, "max")
+    mn = oracle.reduce_axis(x, "min")
+    assert f32_bits(mx[0, 0]) == 0x00000000 and f32_bits(mn[0, 0]) == 0x80000000
+    assert np.isnan(mx[0, 1]) and not np.signbit(mx[0, 1]) and mn[0, 1] == -np.inf
+    assert mx[1, 1] == np.inf and np.isnan(mn[1, 1]) and np.signbit(mn[1, 1])
+    e = oracle.reduce_axis(np.zeros((2, 0, 3), dtype=np.float32), "max")
+    assert np.all(e == -np.inf)
+    e = oracle.reduce_axis(np.zeros((2, 0, 3), dtype=np.int32), "min")
+    assert np.all(e == np.iinfo(np.int32).max)
+    assert oracle.reduce_axis(np.zeros((0, 4, 3), dtype=np.float32), "sum").shape == (0, 3)
+
+
+def test_reduce_axis_with_one_inner_is_a_row_reduce():
+    x = synth.normal_f32(506, (6, 123, 1))
+    for op in ("sum", "max", "min"):
+        assert np.array_equal(oracle.reduce_axis(x, op)[:, 0],
+                              oracle.reduce_rows(np.ascontiguousarray(x[:, :, 0]), op))
+
+
 # ------------------------------------------------------------------ layernorm
 
 def _f32_ulp_close(got, want, ulps=1):
