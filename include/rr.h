@@ -1,12 +1,14 @@
 /*
  * rr.h -- deterministic row reductions on AMD Instinct MI355X (gfx950).
  *
- * A C ABI over hand-written HIP kernels.  Five operations:
+ * A C ABI over hand-written HIP kernels.  Six operations:
  *
  *   rr_reduce_rows       sum / max / min of every row over its last axis, on
  *                        float32 or int32 values, through one of five tiers
  *                        (wave, block, tiled, serial, split-K).
  *   rr_reduce_rows_multi sum, max and min of every row over one read.
+ *   rr_reduce_axis       sum / max / min over the middle axis of
+ *                        [outer][axis][inner] (a non-last axis).
  *   rr_softmax_rows      two-pass softmax of every row (pass 1: the online
  *                        (max, sum) monoid; pass 2: a map that writes y).
  *   rr_layernorm_rows    two-pass layer normalisation of every row (pass 1:
@@ -204,6 +206,46 @@ rr_status rr_reduce_rows_multi(const void* x, void* y_sum, void* y_max, void* y_
                                int64_t rows, int64_t cols, int64_t ld, rr_dtype dtype,
                                rr_tier tier, void* workspace, size_t workspace_bytes,
                                void* stream);
+
+/*
+ * rr_plan_axis -- tier selection and geometry for rr_reduce_axis (host only).
+ * Legal tiers: AUTO, TILED, SERIAL, SPLITK (others: RR_ERR_TIER).  With g the
+ * output groups (outer * inner / 4 when inner % 4 == 0, else outer * inner)
+ * and B = ceil(g / 256): AUTO picks SPLITK when B < 2 * cu_count and
+ * axis >= 512, else TILED.  SPLITK: G = clamp(ceil(4 * cu_count / B), 1,
+ * min(256, ceil(axis / 128))) slices of ceil(axis / G) steps (tile_cols);
+ * workspace G * outer * inner * 8 bytes.  lanes_per_row holds the outputs
+ * per thread (4 or 1).  The planner assumes 16-byte aligned pointers.
+ */
+rr_status rr_plan_axis(int64_t outer, int64_t axis, int64_t inner, rr_dtype dtype, rr_op op,
+                       rr_tier tier, int32_t cu_count, rr_plan* plan_out);
+
+/*
+ * rr_reduce_axis -- y[o][i] = fold over a of x[o][a][i]: a reduction over a
+ * non-last axis.  "reduce" (algorithm.gpu.rowwise), Args (ctx.axis is the
+ * reduce axis, the other dims pinned) and tier semantics (the tiled tier's
+ * thread owns emit_tile_width adjacent output rows and sends each lane of a
+ * tile to its own state).  Same arithmetic as rr_reduce_rows.
+ *
+ *   x       device, [outer][axis][inner] of dtype, contiguous
+ *   y       device, [outer][inner] of dtype (written)
+ *   dtype   RR_F32 or RR_I32;  op  RR_SUM, RR_MAX or RR_MIN
+ *   tier    AUTO, TILED (a thread owns 4 adjacent outputs -- 1 when inner is
+ *           not a multiple of 4 or a pointer is not 16-byte aligned -- and
+ *           walks the whole axis in order), SERIAL (a thread per output), or
+ *           SPLITK (G axis slices: partials, then a fold in ascending slice
+ *           order, two launches)
+ *   workspace, workspace_bytes
+ *           device scratch for SPLITK, 8-byte aligned, size from
+ *           rr_plan_axis; no initial contents needed.  Ignored otherwise.
+ * TILED and SERIAL fold each output in the index order of the axis, so a
+ * float sum equals the double sum in that order rounded once.  outer or
+ * inner == 0 is a no-op; axis == 0 writes the identity.  inner == 1 is a
+ * row reduction, which rr_reduce_rows does faster.
+ */
+rr_status rr_reduce_axis(const void* x, void* y, int64_t outer, int64_t axis, int64_t inner,
+                         rr_dtype dtype, rr_op op, rr_tier tier, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 /*
  * rr_softmax_rows -- y[r][j] = exp(x[r][j] - m_r) / s_r with

@@ -9,6 +9,7 @@ the first call raises.
 Operations (names as in the C ABI):
   reduce_rows        sum / max / min over the last axis (float32, int32)
   reduce_rows_multi  sum, max and min over the last axis from one read
+  reduce_axis        sum / max / min over a non-last axis
   softmax_rows       two-pass softmax over the last axis (bf16 / float32)
   layernorm_rows     two-pass layer normalisation over the last axis
   splitk_lse_merge   merge of P split-K partial attention outputs by their
@@ -21,7 +22,7 @@ import threading
 import torch
 
 __all__ = [
-    "RRError", "reduce_rows", "reduce_rows_multi", "softmax_rows", "layernorm_rows", "splitk_lse_merge",
+    "RRError", "reduce_rows", "reduce_rows_multi", "reduce_axis", "plan_axis", "softmax_rows", "layernorm_rows", "splitk_lse_merge",
     "plan_reduce", "plan_softmax", "plan_layernorm", "select_tier", "workspace_bytes", "workspace_reset", "device_cu_count",
     "version", "lib_path", "TIERS", "OPS",
 ]
@@ -81,6 +82,8 @@ def _load():
         lib.rr_softmax_rows.argtypes = [vp, vp, i64, i64, i64, i64, st, st, st, vp,
                                         ctypes.c_size_t, vp]
         lib.rr_splitk_lse_merge.argtypes = [vp, vp, vp, vp, i32, i64, i32, ctypes.c_float, st, vp]
+        lib.rr_reduce_axis.argtypes = [vp, vp, i64, i64, i64, st, st, st, vp, ctypes.c_size_t, vp]
+        lib.rr_plan_axis.argtypes = [i64, i64, i64, st, st, st, i32, ctypes.POINTER(_Plan)]
         lib.rr_layernorm_rows.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, st, st, st,
                                           ctypes.c_float, st, vp, ctypes.c_size_t, vp]
         lib.rr_plan_layernorm.argtypes = [i64, i64, st, st, st, st, i32, ctypes.POINTER(_Plan)]
@@ -95,7 +98,8 @@ def _load():
         lib.rr_version.restype = ctypes.c_int
         lib.rr_test_set_splitk_skew.argtypes = [i32]
         lib.rr_test_set_splitk_skew.restype = None
-        for name in ("rr_reduce_rows", "rr_reduce_rows_multi", "rr_softmax_rows", "rr_splitk_lse_merge", "rr_plan_reduce",
+        for name in ("rr_reduce_rows", "rr_reduce_rows_multi", "rr_reduce_axis", "rr_plan_axis",
+                     "rr_softmax_rows", "rr_splitk_lse_merge", "rr_plan_reduce",
                      "rr_plan_softmax", "rr_layernorm_rows", "rr_plan_layernorm",
                      "rr_workspace_bytes", "rr_select_tier",
                      "rr_workspace_reset", "rr_device_cu_count"):
@@ -281,6 +285,51 @@ def reduce_rows_multi(x, stats=("sum", "max", "min"), tier="auto", out=None):
     return {k: out[k] for k in stats}
 
 
+def reduce_axis(x, dim, op="sum", tier="auto", out=None):
+    """Reduce a contiguous tensor ``x`` over dimension ``dim`` (any axis).
+
+    The tensor is viewed as [outer, axis, inner] around ``dim``; the result
+    has ``x``'s shape without ``dim``.  ``op`` is "sum", "max" or "min";
+    ``tier`` is "auto", "tiled", "serial" or "splitk".
+    """
+    lib = _load()
+    if not isinstance(x, torch.Tensor) or not x.is_cuda:
+        raise ValueError("x must be a GPU tensor")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    dim = dim % x.dim()
+    shape = tuple(x.shape)
+    outer = 1
+    for d in shape[:dim]:
+        outer *= d
+    inner = 1
+    for d in shape[dim + 1:]:
+        inner *= d
+    axis = shape[dim]
+    oshape = shape[:dim] + shape[dim + 1:]
+    dt = _dtype_code(x.dtype)
+    if out is None:
+        out = torch.empty(oshape, dtype=x.dtype, device=x.device)
+    if out.dtype != x.dtype or tuple(out.shape) != oshape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous %s tensor of shape %s" % (x.dtype, oshape))
+    o, t = OPS[op], TIERS[tier]
+    with _OnDevice(x.device):
+        stream = _stream_ptr(x.device)
+        key = ("axis", outer, axis, inner, dt, o, t, _cu_count(x.device))
+        need = _ws_need.get(key)
+        if need is None:
+            plan = _Plan()
+            _check(lib.rr_plan_axis(outer, axis, inner, dt, o, t, key[-1], ctypes.byref(plan)))
+            need = _ws_need[key] = plan.workspace_bytes
+        ws_ptr, ws_len = None, 0
+        if need:
+            ws = _workspace("axis", x.device, stream.value, need)
+            ws_ptr, ws_len = ctypes.c_void_p(ws.data_ptr()), ws.numel()
+        _check(lib.rr_reduce_axis(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                  outer, axis, inner, dt, o, t, ws_ptr, ws_len, stream))
+    return out
+
+
 def softmax_rows(x, out_dtype=None, tier="auto", out=None):
     """Softmax of every row of ``x`` over its last axis (x: bfloat16 or float32)."""
     lib = _lib or _load()
@@ -424,6 +473,15 @@ def plan_softmax(rows, cols, x_dtype=torch.bfloat16, y_dtype=None, tier="auto", 
     y_dtype = x_dtype if y_dtype is None else y_dtype
     _check(lib.rr_plan_softmax(rows, cols, _dtype_code(x_dtype), _dtype_code(y_dtype),
                                TIERS[tier], cu_count, ctypes.byref(plan)))
+    return _plan_dict(plan)
+
+
+def plan_axis(outer, axis, inner, dtype=torch.float32, op="sum", tier="auto", cu_count=256):
+    """Host-only launch plan of rr_reduce_axis (needs no GPU)."""
+    lib = _load()
+    plan = _Plan()
+    _check(lib.rr_plan_axis(outer, axis, inner, _dtype_code(dtype), OPS[op], TIERS[tier],
+                            cu_count, ctypes.byref(plan)))
     return _plan_dict(plan)
 
 

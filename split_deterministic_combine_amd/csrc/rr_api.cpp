@@ -114,6 +114,34 @@ extern "C" rr_status rr_reduce_rows_multi(const void* x, void* y_sum, void* y_ma
     return rr::launch_reduce(p, a);
 }
 
+extern "C" rr_status rr_reduce_axis(const void* x, void* y, int64_t outer, int64_t axis,
+                                    int64_t inner, rr_dtype dtype, rr_op op, rr_tier tier,
+                                    void* workspace, size_t workspace_bytes, void* stream)
+{
+    rr_plan p;
+    rr_status st = rr::plan_axis(outer, axis, inner, dtype, op, tier, 1, true, &p);
+    if (st != RR_OK) return st;
+    if (outer == 0 || inner == 0) return RR_OK;
+    if (!y || (!x && axis > 0)) return RR_ERR_NULL;
+    if (axis == 0) {  // every output is the identity
+        rr::ReduceLaunch a{x, y, outer * inner, 0, 0, dtype, op, false,
+                           {nullptr, nullptr, nullptr}, false, nullptr, 0, as_stream(stream)};
+        return rr::launch_reduce_identity(a);
+    }
+    int32_t cu = 0;
+    if ((st = current_cu(&cu)) != RR_OK) return st;
+    const bool vec = aligned(x, 16) && aligned(y, 16) && inner % 4 == 0;
+    if ((st = rr::plan_axis(outer, axis, inner, dtype, op, tier, cu, vec, &p)) != RR_OK)
+        return st;
+    if (p.tier == RR_TIER_SPLITK) {
+        if (!workspace || workspace_bytes < p.workspace_bytes || !aligned(workspace, 8))
+            return RR_ERR_WORKSPACE;
+    }
+    rr::AxisLaunch a{x, y, outer, axis, inner, dtype, op, p.lanes_per_row == 4, workspace,
+                     as_stream(stream)};
+    return rr::launch_reduce_axis(p, a);
+}
+
 extern "C" rr_status rr_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols,
                                      int64_t ld_x, int64_t ld_y, rr_dtype x_dtype,
                                      rr_dtype y_dtype, rr_tier tier, void* workspace,

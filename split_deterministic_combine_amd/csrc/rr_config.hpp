@@ -47,6 +47,15 @@ constexpr int64_t kSoftmaxWideMinChunks = (int64_t)kBlockThreads * kSoftmaxMaxCh
 // Split-K softmax: 16-byte chunks per thread per tile (a tile is one load
 // round of the workgroup).
 constexpr int kSoftmaxSplitKUnroll = 4;
+// Reduction over a non-last axis: 16-byte loads in flight per thread (one
+// per axis step), split-K when there are fewer than kAxisSplitKMaxBlocksPerCU
+// workgroups of outputs per CU and the axis has at least kAxisSplitKMinAxis
+// steps, with slices of at least kAxisMinSlice steps.
+constexpr int kAxisUnroll = 8;
+constexpr int kAxisSplitKMaxBlocksPerCU = 2;
+constexpr int64_t kAxisSplitKMinAxis = 512;
+constexpr int64_t kAxisMinSlice = 128;
+
 // Layernorm.  Rows of whole aligned 16-byte chunks, up to kLnPfMaxChunks of
 // them, stay in registers on persistent workgroups whose size follows the
 // row (ln_pf_shape).  A CU gets kLnPfLoadsPerCU / (wavefronts per workgroup *

@@ -32,6 +32,17 @@ struct SoftmaxLaunch {
     hipStream_t stream;
 };
 
+struct AxisLaunch {
+    const void* x;        // [outer][axis][inner]
+    void* y;              // [outer][inner]
+    int64_t outer, axis, inner;
+    rr_dtype dtype;
+    rr_op op;
+    bool vec;             // 4 adjacent outputs per thread, 16-byte loads
+    void* workspace;      // split-K only
+    hipStream_t stream;
+};
+
 struct LayernormLaunch {
     const void* x;
     void* y;
@@ -67,6 +78,7 @@ rr_status launch_reduce_identity(const ReduceLaunch& a);  // cols == 0
 rr_status launch_softmax(const rr_plan& plan, const SoftmaxLaunch& a);
 rr_status launch_merge(const MergeLaunch& a);
 rr_status launch_layernorm(const rr_plan& plan, const LayernormLaunch& a);
+rr_status launch_reduce_axis(const rr_plan& plan, const AxisLaunch& a);
 rr_status launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
 
 }  // namespace rr

@@ -201,7 +201,60 @@ rr_status plan_layernorm(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype 
     return RR_OK;
 }
 
+// Reduction over the middle axis of [outer][axis][inner].  TILED: a thread
+// per 4 adjacent outputs (1 on the scalar path); SERIAL: a thread per output;
+// SPLITK: the axis cut into G slices (partials, then a fold).  Block and
+// wave have no meaning here.
+rr_status plan_axis(int64_t outer, int64_t axis, int64_t inner, rr_dtype dtype, rr_op op,
+                    rr_tier tier, int32_t cu_count, bool vec, rr_plan* out)
+{
+    if (!out) return RR_ERR_NULL;
+    if (outer < 0 || axis < 0 || inner < 0) return RR_ERR_SHAPE;
+    int64_t n = 0;
+    if (__builtin_mul_overflow(outer, inner, &n) || __builtin_mul_overflow(n, axis, &n))
+        return RR_ERR_SHAPE;
+    if (dtype != RR_F32 && dtype != RR_I32) return RR_ERR_DTYPE;
+    if (op != RR_SUM && op != RR_MAX && op != RR_MIN) return RR_ERR_OP;
+    if (cu_count < 1) return RR_ERR_SHAPE;
+    if (tier != RR_TIER_AUTO && tier != RR_TIER_TILED && tier != RR_TIER_SERIAL &&
+        tier != RR_TIER_SPLITK)
+        return RR_ERR_TIER;
+    memset(out, 0, sizeof *out);
+    const int64_t v = (vec && inner % 4 == 0 && tier != RR_TIER_SERIAL) ? 4 : 1;
+    const int64_t groups = outer * (inner / v);
+    const int64_t nblk = ceil_div(groups, (int64_t)kBlockThreads);
+    rr_tier t = tier;
+    if (t == RR_TIER_AUTO)
+        t = (nblk < (int64_t)kAxisSplitKMaxBlocksPerCU * cu_count && axis >= kAxisSplitKMinAxis)
+                ? RR_TIER_SPLITK
+                : RR_TIER_TILED;
+    out->tier = t;
+    out->block = kBlockThreads;
+    out->lanes_per_row = (int32_t)v;
+    out->slices = 1;
+    out->grid = nblk;
+    if (t == RR_TIER_SPLITK) {
+        int64_t g = ceil_div((int64_t)kSplitKBlocksPerCU * cu_count, nblk > 0 ? nblk : 1);
+        int64_t cap = ceil_div(axis, kAxisMinSlice);
+        if (cap > kSplitKMaxSlices) cap = kSplitKMaxSlices;
+        if (g > cap) g = cap;
+        if (g < 1) g = 1;
+        out->slices = (int32_t)g;
+        out->tile_cols = ceil_div(axis > 0 ? axis : 1, g);
+        out->grid = nblk * g;
+        out->workspace_bytes = (uint64_t)(g * outer * inner * 8);
+    }
+    if (out->grid > kMaxGrid) out->grid = kMaxGrid;
+    return RR_OK;
+}
+
 }  // namespace rr
+
+extern "C" rr_status rr_plan_axis(int64_t outer, int64_t axis, int64_t inner, rr_dtype dtype,
+                                  rr_op op, rr_tier tier, int32_t cu_count, rr_plan* plan_out)
+{
+    return rr::plan_axis(outer, axis, inner, dtype, op, tier, cu_count, true, plan_out);
+}
 
 extern "C" rr_status rr_plan_layernorm(int64_t rows, int64_t cols, rr_dtype x_dtype,
                                        rr_dtype y_dtype, rr_dtype w_dtype, rr_tier tier,

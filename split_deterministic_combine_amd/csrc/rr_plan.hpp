@@ -13,6 +13,8 @@ rr_status plan_softmax(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype y_
 rr_status plan_layernorm(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype y_dtype,
                          rr_dtype w_dtype, rr_tier tier, int32_t cu_count, bool vec,
                          rr_plan* out);
+rr_status plan_axis(int64_t outer, int64_t axis, int64_t inner, rr_dtype dtype, rr_op op,
+                    rr_tier tier, int32_t cu_count, bool vec, rr_plan* out);
 uint64_t splitk_workspace_bytes(int64_t rows, int32_t slices, int partial_bytes);
 uint64_t softmax_splitk_workspace_bytes(int64_t rows, int32_t slices);
 

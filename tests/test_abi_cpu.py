@@ -108,6 +108,41 @@ def test_multi_stat_entry_point_validates_before_touching_the_device():
     assert lib.rr_reduce_rows(None, None, 4, 8, 8, 0, 3, 0, None, 0, None) == 7
 
 
+def test_axis_plan():
+    # many outputs: tiled, 4 adjacent outputs per thread
+    p = rr.plan_axis(1, 4096, 1 << 20)
+    assert p["tier"] == "tiled" and p["lanes_per_row"] == 4 and p["grid"] == (1 << 20) // 4 // 256
+    # few outputs, long axis: split-K over the axis
+    p = rr.plan_axis(1, 1 << 20, 64, cu_count=256)
+    assert p["tier"] == "splitk" and p["slices"] == 256 and p["grid"] == 256
+    assert p["workspace_bytes"] == 256 * 64 * 8 and p["tile_cols"] == 4096
+    p = rr.plan_axis(1, 1000, 64, cu_count=256)
+    assert p["tier"] == "splitk" and p["slices"] == 8                  # ceil(1000 / 128)
+    assert rr.plan_axis(1, 100, 64)["tier"] == "tiled"                 # axis too short
+    assert rr.plan_axis(3, 100, 7)["lanes_per_row"] == 1               # inner % 4 != 0
+    assert rr.plan_axis(3, 100, 8, tier="serial")["lanes_per_row"] == 1
+    for tier, status in (("block", 4), ("wave", 4)):
+        with pytest.raises(rr.RRError) as e:
+            rr.plan_axis(3, 100, 8, tier=tier)
+        assert e.value.status == status
+    with pytest.raises(rr.RRError) as e:
+        rr.plan_axis(1 << 40, 1 << 20, 1 << 10)                        # size overflows
+    assert e.value.status == 2
+
+
+def test_axis_entry_point_validates_before_touching_the_device():
+    lib = ctypes.CDLL(rr.lib_path())
+    vp, i64, it = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.rr_reduce_axis.argtypes = [vp, vp, i64, i64, i64, it, it, it, vp, ctypes.c_size_t, vp]
+    assert lib.rr_reduce_axis(None, None, -1, 4, 4, 0, 0, 0, None, 0, None) == 2
+    assert lib.rr_reduce_axis(None, None, 4, 4, 4, 2, 0, 0, None, 0, None) == 3
+    assert lib.rr_reduce_axis(None, None, 4, 4, 4, 0, 5, 0, None, 0, None) == 7
+    assert lib.rr_reduce_axis(None, None, 4, 4, 4, 0, 0, 2, None, 0, None) == 4
+    assert lib.rr_reduce_axis(None, None, 0, 4, 4, 0, 0, 0, None, 0, None) == 0
+    assert lib.rr_reduce_axis(None, None, 4, 4, 0, 0, 0, 0, None, 0, None) == 0
+    assert lib.rr_reduce_axis(None, None, 4, 4, 4, 0, 0, 0, None, 0, None) == 1
+
+
 def test_splitk_forced_on_short_rows_has_one_slice():
     p = rr.plan_reduce(64, 1000, tier="splitk", cu_count=256)
     assert p["slices"] == 1 and p["grid"] == 64
