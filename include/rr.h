@@ -210,12 +210,15 @@ rr_status rr_reduce_rows_multi(const void* x, void* y_sum, void* y_max, void* y_
 /*
  * rr_plan_axis -- tier selection and geometry for rr_reduce_axis (host only).
  * Legal tiers: AUTO, TILED, SERIAL, SPLITK (others: RR_ERR_TIER).  With g the
- * output groups (outer * inner / 4 when inner % 4 == 0, else outer * inner)
- * and B = ceil(g / 256): AUTO picks SPLITK when B < 2 * cu_count and
- * axis >= 512, else TILED.  SPLITK: G = clamp(ceil(4 * cu_count / B), 1,
- * min(256, ceil(axis / 128))) slices of ceil(axis / G) steps (tile_cols);
- * workspace G * outer * inner * 8 bytes.  lanes_per_row holds the outputs
- * per thread (4 or 1).  The planner assumes 16-byte aligned pointers.
+ * output groups (outer * inner / 4 when inner % 4 == 0, else outer * inner),
+ * per outer index gpo = g / outer and B = ceil(g / 256): AUTO picks SPLITK
+ * when axis >= 512 and (B < cu_count or gpo < 64), else TILED.  SPLITK
+ * workgroups are tiles of GW = min(256, gpo rounded up to a power of two)
+ * output groups by AL = 256 / GW axis lanes; with T tiles, G =
+ * clamp(ceil(4 * cu_count / T), 1, min(1024, ceil(axis / (32 * AL)))) slices
+ * of ceil(axis / G) steps (tile_cols); workspace G * outer * inner * 8
+ * bytes.  lanes_per_row holds the outputs per thread (4 or 1).  The planner
+ * assumes 16-byte aligned pointers.
  */
 rr_status rr_plan_axis(int64_t outer, int64_t axis, int64_t inner, rr_dtype dtype, rr_op op,
                        rr_tier tier, int32_t cu_count, rr_plan* plan_out);
@@ -233,7 +236,8 @@ rr_status rr_plan_axis(int64_t outer, int64_t axis, int64_t inner, rr_dtype dtyp
  *   tier    AUTO, TILED (a thread owns 4 adjacent outputs -- 1 when inner is
  *           not a multiple of 4 or a pointer is not 16-byte aligned -- and
  *           walks the whole axis in order), SERIAL (a thread per output), or
- *           SPLITK (G axis slices: partials, then a fold in ascending slice
+ *           SPLITK (G axis slices, AL axis lanes per output group in each:
+ *           partials folded in lane order, then a fold in ascending slice
  *           order, two launches)
  *   workspace, workspace_bytes
  *           device scratch for SPLITK, 8-byte aligned, size from

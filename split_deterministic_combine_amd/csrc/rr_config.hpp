@@ -52,9 +52,32 @@ constexpr int kSoftmaxSplitKUnroll = 4;
 // workgroups of outputs per CU and the axis has at least kAxisSplitKMinAxis
 // steps, with slices of at least kAxisMinSlice steps.
 constexpr int kAxisUnroll = 8;
-constexpr int kAxisSplitKMaxBlocksPerCU = 2;
+constexpr int kAxisSplitKMaxBlocksPerCU = 1;
 constexpr int64_t kAxisSplitKMinAxis = 512;
-constexpr int64_t kAxisMinSlice = 128;
+constexpr int64_t kAxisNarrowGroups = 64;   // fewer output groups per outer: split-K tiles
+constexpr int64_t kAxisMinStepsPerLane = 32;
+constexpr int64_t kAxisMaxSlices = 1024;  // the fold pass reads G partials per output
+
+// Axis fold pass: log2 of the slice lanes per output, the largest power of
+// two that leaves every lane at least 4 partials (at most 256).
+constexpr int axis_fold_lanes_log2(int64_t slices)
+{
+    int l = 0;
+    while (l < 8 && ((int64_t)4 << (l + 1)) <= slices)
+        ++l;
+    return l;
+}
+
+// Split-K axis tile: log2 of the output groups per workgroup (the rest of the
+// 256 threads are axis lanes): the groups of one outer index rounded up to a
+// power of two, at most 256.
+constexpr int axis_tile_log2(int64_t groups_per_outer)
+{
+    int l = 0;
+    while (l < 8 && ((int64_t)1 << l) < groups_per_outer)
+        ++l;
+    return l;
+}
 
 // Layernorm.  Rows of whole aligned 16-byte chunks, up to kLnPfMaxChunks of
 // them, stay in registers on persistent workgroups whose size follows the

@@ -203,8 +203,8 @@ rr_status plan_layernorm(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype 
 
 // Reduction over the middle axis of [outer][axis][inner].  TILED: a thread
 // per 4 adjacent outputs (1 on the scalar path); SERIAL: a thread per output;
-// SPLITK: the axis cut into G slices (partials, then a fold).  Block and
-// wave have no meaning here.
+// SPLITK: workgroup tiles of output groups x axis lanes over G axis slices
+// (partials, then a fold).  Block and wave have no meaning here.
 rr_status plan_axis(int64_t outer, int64_t axis, int64_t inner, rr_dtype dtype, rr_op op,
                     rr_tier tier, int32_t cu_count, bool vec, rr_plan* out)
 {
@@ -221,11 +221,12 @@ rr_status plan_axis(int64_t outer, int64_t axis, int64_t inner, rr_dtype dtype, 
         return RR_ERR_TIER;
     memset(out, 0, sizeof *out);
     const int64_t v = (vec && inner % 4 == 0 && tier != RR_TIER_SERIAL) ? 4 : 1;
-    const int64_t groups = outer * (inner / v);
-    const int64_t nblk = ceil_div(groups, (int64_t)kBlockThreads);
+    const int64_t gpo = inner / v;  // output groups per outer index
+    const int64_t nblk = ceil_div(outer * gpo, (int64_t)kBlockThreads);
     rr_tier t = tier;
     if (t == RR_TIER_AUTO)
-        t = (nblk < (int64_t)kAxisSplitKMaxBlocksPerCU * cu_count && axis >= kAxisSplitKMinAxis)
+        t = axis >= kAxisSplitKMinAxis &&
+                    (nblk < (int64_t)kAxisSplitKMaxBlocksPerCU * cu_count || gpo < kAxisNarrowGroups)
                 ? RR_TIER_SPLITK
                 : RR_TIER_TILED;
     out->tier = t;
@@ -234,14 +235,18 @@ rr_status plan_axis(int64_t outer, int64_t axis, int64_t inner, rr_dtype dtype, 
     out->slices = 1;
     out->grid = nblk;
     if (t == RR_TIER_SPLITK) {
-        int64_t g = ceil_div((int64_t)kSplitKBlocksPerCU * cu_count, nblk > 0 ? nblk : 1);
-        int64_t cap = ceil_div(axis, kAxisMinSlice);
-        if (cap > kSplitKMaxSlices) cap = kSplitKMaxSlices;
+        // workgroup tiles of GW output groups x AL axis lanes, per outer index
+        const int gwl = axis_tile_log2(gpo);
+        const int64_t lanes = kBlockThreads >> gwl;
+        const int64_t tiles = outer * ceil_div(gpo, (int64_t)1 << gwl);
+        int64_t g = ceil_div((int64_t)kSplitKBlocksPerCU * cu_count, tiles > 0 ? tiles : 1);
+        int64_t cap = ceil_div(axis, lanes * kAxisMinStepsPerLane);
+        if (cap > kAxisMaxSlices) cap = kAxisMaxSlices;
         if (g > cap) g = cap;
         if (g < 1) g = 1;
         out->slices = (int32_t)g;
         out->tile_cols = ceil_div(axis > 0 ? axis : 1, g);
-        out->grid = nblk * g;
+        out->grid = tiles * g;
         out->workspace_bytes = (uint64_t)(g * outer * inner * 8);
     }
     if (out->grid > kMaxGrid) out->grid = kMaxGrid;

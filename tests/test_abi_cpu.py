@@ -114,10 +114,16 @@ def test_axis_plan():
     assert p["tier"] == "tiled" and p["lanes_per_row"] == 4 and p["grid"] == (1 << 20) // 4 // 256
     # few outputs, long axis: split-K over the axis
     p = rr.plan_axis(1, 1 << 20, 64, cu_count=256)
-    assert p["tier"] == "splitk" and p["slices"] == 256 and p["grid"] == 256
-    assert p["workspace_bytes"] == 256 * 64 * 8 and p["tile_cols"] == 4096
+    # 16 output groups: one tile of 16 groups x 16 axis lanes, 1024 slices
+    assert p["tier"] == "splitk" and p["slices"] == 1024 and p["grid"] == 1024
+    assert p["workspace_bytes"] == 1024 * 64 * 8 and p["tile_cols"] == 1024
     p = rr.plan_axis(1, 1000, 64, cu_count=256)
-    assert p["tier"] == "splitk" and p["slices"] == 8                  # ceil(1000 / 128)
+    # 16 groups: tiles of 16 groups x 16 axis lanes; slices of >= 32 steps per lane
+    assert p["tier"] == "splitk" and p["slices"] == 2 and p["grid"] == 2
+    p = rr.plan_axis(1024, 4096, 16, cu_count=256)                      # narrow inner
+    assert p["tier"] == "splitk" and p["slices"] == 1 and p["grid"] == 1024
+    p = rr.plan_axis(1, 1 << 16, 1024, cu_count=256)                    # one full tile
+    assert p["slices"] == 1024 and p["grid"] == 1024
     assert rr.plan_axis(1, 100, 64)["tier"] == "tiled"                 # axis too short
     assert rr.plan_axis(3, 100, 7)["lanes_per_row"] == 1               # inner % 4 != 0
     assert rr.plan_axis(3, 100, 8, tier="serial")["lanes_per_row"] == 1
