@@ -12,6 +12,7 @@ timed on their own workloads and reported under "next_rows":
   layernorm     bf16 layernorm over [16384, 4096], float32 gamma/beta,
                 float32 mean/rstd written                      (block tier)
   multi_long    f32 sum, max and min over [16, 2^24] from one read (split-K)
+  axis_cols     f32 column sums of [16384, 16384] (non-last axis, split-K)
 
 Inputs are resident in HBM before timing.  Buffer sets rotate from one step
 to the next so that the data touched by consecutive launches exceeds the
@@ -62,6 +63,8 @@ KERNEL_OF_OP = {
     "softmax_long_map": "k_softmax_splitk_map<unsigned short, unsigned short, true>",
     "layernorm": "k_layernorm_rows_pf<unsigned short, unsigned short, 4, 128, true, true>",
     "multi_long": "k_reduce_splitk<rr::MultiF32, 4>",
+    "axis_cols_partial": "k_reduce_axis_partial<rr::SumF32, 4>",
+    "axis_cols_fold": "k_reduce_axis_fold<rr::SumF32>",
 }
 LAYERNORM = (16384, 4096)
 SOFTMAX_LONG = (16, 1 << 22)
@@ -79,9 +82,14 @@ ALGO_BYTES = {
     # x read and y written once (bf16), gamma/beta read once, mean/rstd written
     "layernorm": 16384 * 4096 * 2 * 2 + 2 * 4096 * 4 + 2 * 16384 * 4,
     "multi_long": 16 * (1 << 24) * 4 + 3 * 16 * 4,
+    # column sums of [16384, 16384]: the partial pass reads x, writes G = 64
+    # partials per column; the fold pass reads them and writes y
+    "axis_cols_partial": 16384 * 16384 * 4 + 64 * 16384 * 8,
+    "axis_cols_fold": 64 * 16384 * 8 + 16384 * 4,
 }
 # next-row operations as a whole: x read once and y written once
 NEXT_BYTES = {"multi_long": 16 * (1 << 24) * 4 + 3 * 16 * 4,
+              "axis_cols": 16384 * 16384 * 4 + 16384 * 4,
               "softmax_long": 16 * (1 << 22) * 2 * 2,
               "layernorm": 16384 * 4096 * 2 * 2 + 2 * 4096 * 4 + 2 * 16384 * 4}
 STEP_OPS = ("short_sum", "short_max", "softmax", "long_sum", "long_max", "merge")
@@ -309,8 +317,11 @@ def main():
                                                out=dx["merge_out"][i % 8]),
     }
     y_multi = {k: torch.empty(16, dtype=torch.float32, device=dev) for k in ("sum", "max", "min")}
+    y_cols = torch.empty(16384, dtype=torch.float32, device=dev)
     next_ops = {
         "multi_long": lambda i: rr.reduce_rows_multi(dx["long_f"][0], out=y_multi),
+        "axis_cols": lambda i: rr.reduce_axis(dx["long_f"][0].view(16384, 16384), 0, "sum",
+                                              out=y_cols),
         "softmax_long": lambda i: rr.softmax_rows(dx["softmax_long"][i % 3],
                                                   out=dx["softmax_long_out"][i % 3]),
         "layernorm": lambda i: rr.layernorm_rows(dx["layernorm"][i % 4], *dx["layernorm_w"], 1e-5,
@@ -339,6 +350,10 @@ def main():
             y = dx["softmax_long_out"][0][pick].cpu().view(torch.int16).numpy().view(np.uint16)
             r = oracle.softmax_rows(np.ascontiguousarray(host["softmax_long"][pick]), "bf16")
             ok &= bool(bf16_ulp_diff(y, r).max() <= 1)
+        if "axis_cols" in next_names:
+            r = oracle.reduce_axis(host["long_f"].reshape(1, 16384, 16384), "sum")[0]
+            y = y_cols.cpu().numpy()
+            ok &= bool(np.all(np.abs(y - r) <= 1e-6 + 1e-5 * np.abs(r)))
         if "multi_long" in next_names:
             for k in ("sum", "max", "min"):
                 y = y_multi[k][:2].cpu().numpy()
@@ -469,6 +484,11 @@ def main():
             next_rows[n] = {"ms_mean": round(mean, 5), "ms_median": round(ts[len(ts) // 2], 5),
                             "ms_min": round(ts[0], 5), "bytes": NEXT_BYTES[n],
                             "GBps": round(gbs, 1), "pct_peak": round(100 * gbs / PEAK_HBM_GBS, 1)}
+        if "axis_cols" in next_rows:
+            next_rows["axis_cols"].update({
+                "config": "f32 column sums of [16384, 16384] (reduce over a non-last axis), "
+                          "split-K: 64 slices, tiles of 256 output groups",
+                "kernels": [KERNEL_OF_OP["axis_cols_partial"], KERNEL_OF_OP["axis_cols_fold"]]})
         if "multi_long" in next_rows:
             next_rows["multi_long"].update({
                 "config": "f32 sum, max and min over [16, 16777216] from one read, split-K "
