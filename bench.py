@@ -335,6 +335,7 @@ def main():
 
     # ------------------------------------------------------------ parity
     parity = "skipped"
+    bit_identical = None
     if not args.no_parity:
         import oracle
 
@@ -398,8 +399,22 @@ def main():
                                         np.ascontiguousarray(mh.reshape(8, -1)[:, :256]),
                                         np.ascontiguousarray(lh.reshape(8, -1)[:, :256]), 1.0, "bf16")
             ok &= bool(bf16_ulp_diff(y, r).max() <= 1)
+        # run-to-run bit identity: each step op again into the same outputs
+        outs = {"short_sum": lambda: y_short_sum, "short_max": lambda: y_short_max,
+                "softmax": lambda: dx["softmax_out"][0], "long_sum": lambda: y_long_f,
+                "long_max": lambda: y_long_i, "merge": lambda: dx["merge_out"][0]}
+        first = {n: outs[n]().clone() for n in names}
+        for n in names:
+            ops[n](0)
+        torch.cuda.synchronize()
+        same = all(torch.equal(first[n].view(torch.int16) if first[n].element_size() == 2
+                               else first[n].view(torch.int32),
+                               outs[n]().view(torch.int16) if first[n].element_size() == 2
+                               else outs[n]().view(torch.int32)) for n in names)
+        ok &= same
+        bit_identical = same
         parity = "ok" if ok else "FAILED"
-        log("parity %s" % parity)
+        log("parity %s (repeat bit-identical: %s)" % (parity, same))
         if not ok:
             sys.exit(1)
 
@@ -456,7 +471,8 @@ def main():
         ts = sorted(dom_ms if n == dom else brk[n])
         mean = sum(ts) / len(ts)
         per_op[n] = {"ms_mean": round(mean, 5), "ms_median": round(ts[len(ts) // 2], 5),
-                     "ms_min": round(ts[0], 5), "bytes": B[n],
+                     "ms_min": round(ts[0], 5),
+                     "ms_p90": round(ts[min(len(ts) - 1, (9 * len(ts)) // 10)], 5), "bytes": B[n],
                      "GBps": round(B[n] / (mean * 1e-3) / 1e9, 1),
                      "pct_peak": round(100 * B[n] / (mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 1),
                      "timed_in": "timed region" if n == dom else "instrumented pass"}
@@ -572,7 +588,8 @@ def main():
                                "[8192,8192] block tier; f32 sum + i32 max [16,2^24] split-K; "
                                "LSE merge P=8 O[8,32,128,128] -> bf16",
                    "ops": names, "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBS, 1),
-                   "step_bytes": step_bytes, "parity": parity},
+                   "step_bytes": step_bytes, "parity": parity,
+                   "repeat_bit_identical": bit_identical},
         "per_op": per_op,
         "next_rows": next_rows,
         "roofline": roofline,

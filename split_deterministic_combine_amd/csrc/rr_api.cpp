@@ -164,7 +164,7 @@ extern "C" rr_status rr_softmax_rows(const void* x, void* y, int64_t rows, int64
         if (!workspace || workspace_bytes < p.workspace_bytes || !aligned(workspace, 8))
             return RR_ERR_WORKSPACE;
     }
-    rr::SoftmaxLaunch a{x, y, rows, cols, ld_x, ld_y, x_dtype, y_dtype, vec, workspace,
+    rr::SoftmaxLaunch a{x, y, rows, cols, ld_x, ld_y, x_dtype, y_dtype, vec, workspace, cu,
                         as_stream(stream)};
     return rr::launch_softmax(p, a);
 }

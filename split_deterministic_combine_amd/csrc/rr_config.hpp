@@ -29,19 +29,14 @@ constexpr int kSplitKBlocksPerCU = 4;  // G aims at this many workgroups per CU 
 constexpr int kBlockUnroll = 4;
 constexpr int kSplitKUnroll = 8;
 
-// Softmax block tier: 16-byte chunks per thread held in registers.  Rows
-// needing more than kSoftmaxMaxChunks chunks per thread use the streaming
-// variant that reads x twice.
+// Softmax block tier.  Whole-chunk, 16-byte aligned rows run the persistent
+// kernel (row_pf_shape below).  Other rows keep up to kSoftmaxMaxChunks
+// 16-byte chunks per thread in registers, one row per workgroup; rows too
+// long for kBlockThreads threads (more than kSoftmaxWideMinChunks chunks) run
+// on workgroups of kSoftmaxWideThreads, and beyond that the streaming variant
+// reads x twice.
 constexpr int kSoftmaxMaxChunks = 8;
-// Rows too long to stay in the registers of kBlockThreads threads (more
-// than kBlockThreads * kSoftmaxMaxChunks 16-byte chunks) run on workgroups of
-// kSoftmaxWideThreads threads, which keeps rows up to twice as long resident
-// instead of reading them twice.
 constexpr int kSoftmaxWideThreads = 512;
-// Block-tier softmax on whole-chunk, 16-byte aligned rows runs persistent
-// workgroups (each walks rows b, b + grid, ... with a one-row prefetch):
-// this many per CU.
-constexpr int kSoftmaxRowBlocksPerCU = 2;
 constexpr int64_t kSoftmaxWideMinChunks = (int64_t)kBlockThreads * kSoftmaxMaxChunks;
 
 // Split-K softmax: 16-byte chunks per thread per tile (a tile is one load
@@ -79,40 +74,43 @@ constexpr int axis_tile_log2(int64_t groups_per_outer)
     return l;
 }
 
-// Layernorm.  Rows of whole aligned 16-byte chunks, up to kLnPfMaxChunks of
-// them, stay in registers on persistent workgroups whose size follows the
-// row (ln_pf_shape).  A CU gets kLnPfLoadsPerCU / (wavefronts per workgroup *
-// chunks per thread) of them (at least one): that many 16-byte loads per
-// lane in flight per CU, the measured optimum (fewer starve HBM, more
-// contend).  Other rows of up to kLnMaxChunks chunks per thread of 256 stay
-// in registers one row per workgroup; longer rows stream twice.  Split-K
-// tiles are kLnSplitKUnroll chunks per thread.
-constexpr int kLnMaxChunks = 8;
-constexpr int64_t kLnPfMaxChunks = 2048;
-constexpr int kLnPfLoadsPerCU = 32;
-constexpr int kLnSplitKUnroll = 4;
+// Persistent rows (softmax and layernorm block tiers).  Rows of whole
+// aligned 16-byte chunks, up to kPfMaxChunks of them, stay in registers on
+// persistent workgroups whose size follows the row (row_pf_shape).  A CU gets
+// kPfLoadsPerCU / (wavefronts per workgroup * chunks per thread) of them (at
+// least one): that many 16-byte loads per lane in flight per CU, the measured
+// optimum (fewer starve HBM, more contend).  The launch lowers the grid to
+// what the kernel's occupancy allows, so a persistent grid never queues.
+constexpr int64_t kPfMaxChunks = 2048;
+constexpr int kPfLoadsPerCU = 32;
 
-// Threads per row (nt) and chunks per thread (nch) of the persistent
-// layernorm for a row of `chunks` chunks; nt == 0 when the row is too long.
-struct LnPfShape {
+// Threads per row (nt) and chunks per thread (nch) of a persistent row of
+// `chunks` chunks; nt == 0 when the row is too long for registers.
+struct RowPfShape {
     int nt;
     int nch;
 };
-constexpr LnPfShape ln_pf_shape(int64_t chunks)
+constexpr RowPfShape row_pf_shape(int64_t chunks)
 {
-    return chunks <= 64     ? LnPfShape{64, 1}
-           : chunks <= 128  ? LnPfShape{64, 2}
-           : chunks <= 256  ? LnPfShape{64, 4}
-           : chunks <= 512  ? LnPfShape{128, 4}
-           : chunks <= 1024 ? LnPfShape{256, 4}
-           : chunks <= kLnPfMaxChunks ? LnPfShape{512, 4}
-                                      : LnPfShape{0, 0};
+    return chunks <= 64     ? RowPfShape{64, 1}
+           : chunks <= 128  ? RowPfShape{64, 2}
+           : chunks <= 256  ? RowPfShape{64, 4}
+           : chunks <= 512  ? RowPfShape{128, 4}
+           : chunks <= 1024 ? RowPfShape{256, 4}
+           : chunks <= kPfMaxChunks ? RowPfShape{512, 4}
+                                    : RowPfShape{0, 0};
 }
-constexpr int ln_pf_blocks_per_cu(LnPfShape sh)
+constexpr int row_pf_blocks_per_cu(RowPfShape sh)
 {
-    return kLnPfLoadsPerCU / (sh.nt / 64 * sh.nch) > 0 ? kLnPfLoadsPerCU / (sh.nt / 64 * sh.nch)
-                                                       : 1;
+    return kPfLoadsPerCU / (sh.nt / 64 * sh.nch) > 0 ? kPfLoadsPerCU / (sh.nt / 64 * sh.nch) : 1;
 }
+
+// Layernorm: rows that are not persistent-eligible but have up to
+// kLnMaxChunks chunks per thread of 256 stay in registers one row per
+// workgroup; longer rows stream twice.  Split-K tiles are kLnSplitKUnroll
+// chunks per thread.
+constexpr int kLnMaxChunks = 8;
+constexpr int kLnSplitKUnroll = 4;
 
 // LSE merge: partitions staged per batch of loads, and workgroup size.
 constexpr int kMergeBatch = 8;

@@ -29,6 +29,7 @@ struct SoftmaxLaunch {
     rr_dtype x_dtype, y_dtype;
     bool vec;
     void* workspace;      // split-K only
+    int32_t cu;           // compute units of the current device
     hipStream_t stream;
 };
 

@@ -622,7 +622,7 @@ static rr_status launch_block(const rr_plan& p, const XT* x, YT* y, const Weight
     if constexpr (VEC) {
         if (a.cols % E == 0) {
             // persistent rows; the plan chose the shape and sized the grid
-            const LnPfShape sh = ln_pf_shape(a.cols / E);
+            const RowPfShape sh = row_pf_shape(a.cols / E);
             if (sh.nt > 0 && sh.nt != p.block)
                 return RR_ERR_TIER;  // plan and launch disagree: refuse, launch nothing
             switch (sh.nt * 16 + sh.nch) {

@@ -146,21 +146,23 @@ rr_status plan_softmax(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype y_
     fill_rowwise_geometry(t, rows, cols, vec_elems, out);
     if (t == RR_TIER_BLOCK) {
         const int64_t chunks = ceil_div(cols, vec_elems);
-        if (chunks > kSoftmaxWideMinChunks)
-            out->block = kSoftmaxWideThreads;
-        // Rows of whole 16-byte chunks that stay in registers: persistent
-        // workgroups with a one-row prefetch.
-        if (vec && cols % vec_elems == 0 && ceil_div(chunks, out->block) <= kSoftmaxMaxChunks) {
-            const int64_t g = (int64_t)cu_count * kSoftmaxRowBlocksPerCU;
+        const RowPfShape sh = row_pf_shape(chunks);
+        if (vec && cols % vec_elems == 0 && sh.nt > 0) {
+            // rows of whole 16-byte chunks that stay in registers: persistent
+            // workgroups sized to the row, with a one-row prefetch
+            out->block = sh.nt;
+            const int64_t g = (int64_t)cu_count * row_pf_blocks_per_cu(sh);
             out->grid = rows < g ? rows : g;
+        } else if (chunks > kSoftmaxWideMinChunks) {
+            out->block = kSoftmaxWideThreads;
         }
     }
     return RR_OK;
 }
 
 // Layernorm: the softmax's tier rule.  The block tier keeps rows of whole
-// aligned chunks in registers on persistent workgroups sized by ln_pf_shape,
-// ln_pf_blocks_per_cu of them per CU (the launch lowers that to what the
+// aligned chunks in registers on persistent workgroups sized by row_pf_shape,
+// row_pf_blocks_per_cu of them per CU (the launch lowers that to what the
 // kernel's occupancy allows, so a persistent grid never queues).
 rr_status plan_layernorm(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype y_dtype,
                          rr_dtype w_dtype, rr_tier tier, int32_t cu_count, bool vec,
@@ -191,10 +193,10 @@ rr_status plan_layernorm(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype 
     }
     fill_rowwise_geometry(t, rows, cols, vec_elems, out);
     if (t == RR_TIER_BLOCK && vec && cols % vec_elems == 0) {
-        const LnPfShape sh = ln_pf_shape(cols / vec_elems);
+        const RowPfShape sh = row_pf_shape(cols / vec_elems);
         if (sh.nt > 0) {
             out->block = sh.nt;
-            const int64_t g = (int64_t)cu_count * ln_pf_blocks_per_cu(sh);
+            const int64_t g = (int64_t)cu_count * row_pf_blocks_per_cu(sh);
             out->grid = rows < g ? rows : g;
         }
     }

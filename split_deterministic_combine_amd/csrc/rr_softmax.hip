@@ -654,19 +654,28 @@ static rr_status launch_splitk(const rr_plan& p, const SoftmaxLaunch& a)
 }
 
 // ---------------------------------------------------------------- launch
+// Persistent rows: the plan's grid, lowered to the workgroups that can be
+// resident at once (occupancy times CUs), so no workgroup of the persistent
+// grid waits for another to finish before it starts.
 template <class XT, class YT, int NCH, int NT>
-static rr_status launch_pf(dim3 grid, hipStream_t s, const XT* x, YT* y, const SoftmaxLaunch& a)
+static rr_status launch_pf(const XT* x, YT* y, const rr_plan& p, const SoftmaxLaunch& a)
 {
     constexpr int64_t kExactCols = (int64_t)NT * NCH * XIn<XT>::kChunk;
-    if (a.cols == kExactCols)
-        return launch_kernel(k_softmax_rows_pf<XT, YT, NCH, NT, true>, grid, dim3(NT), 0, s, x, y,
-                             a.rows, a.cols, a.ld_x, a.ld_y);
-    return launch_kernel(k_softmax_rows_pf<XT, YT, NCH, NT, false>, grid, dim3(NT), 0, s, x, y,
-                         a.rows, a.cols, a.ld_x, a.ld_y);
+    auto kernel = a.cols == kExactCols ? k_softmax_rows_pf<XT, YT, NCH, NT, true>
+                                       : k_softmax_rows_pf<XT, YT, NCH, NT, false>;
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, NT, 0) != hipSuccess ||
+        per_cu < 1)
+        return RR_ERR_HIP;
+    const int64_t cap = (int64_t)per_cu * a.cu;
+    const dim3 grid((unsigned)(p.grid < cap ? p.grid : cap));
+    return launch_kernel(kernel, grid, dim3(NT), 0, a.stream, x, y, a.rows, a.cols, a.ld_x,
+                         a.ld_y);
 }
 
-// Block tier: the row stays in registers when each of the NT threads holds
-// at most kSoftmaxMaxChunks chunks; longer rows stream twice.
+// Block tier, one row per workgroup: the row stays in registers when each of
+// the NT threads holds at most kSoftmaxMaxChunks chunks; longer rows stream
+// twice.
 template <class XT, class YT, bool VEC, int NT>
 static rr_status launch_block(const rr_plan& p, const SoftmaxLaunch& a)
 {
@@ -676,19 +685,6 @@ static rr_status launch_block(const rr_plan& p, const SoftmaxLaunch& a)
     const hipStream_t s = a.stream;
     constexpr int E = VEC ? XIn<XT>::kChunk : 1;
     const int64_t nch = ceil_div(ceil_div(a.cols, E), NT);
-    if constexpr (VEC) {
-        if (a.cols % E == 0 && nch <= kSoftmaxMaxChunks) {
-            // persistent rows with prefetch; the plan sized the grid
-            const dim3 pg((unsigned)p.grid);
-            if (nch <= 1)
-                return launch_pf<XT, YT, 1, NT>(pg, s, x, y, a);
-            if (nch <= 2)
-                return launch_pf<XT, YT, 2, NT>(pg, s, x, y, a);
-            if (nch <= 4)
-                return launch_pf<XT, YT, 4, NT>(pg, s, x, y, a);
-            return launch_pf<XT, YT, kSoftmaxMaxChunks, NT>(pg, s, x, y, a);
-        }
-    }
     if (nch <= 1)
         return launch_kernel(k_softmax_block<XT, YT, 1, VEC, NT>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
     if (nch <= 2)
@@ -700,6 +696,36 @@ static rr_status launch_block(const rr_plan& p, const SoftmaxLaunch& a)
     return launch_kernel(k_softmax_stream<XT, YT, VEC, NT>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
 }
 
+// Block tier: persistent rows when the plan chose them, else one row per
+// workgroup.
+template <class XT, class YT, bool VEC>
+static rr_status launch_block_tier(const rr_plan& p, const SoftmaxLaunch& a)
+{
+    if constexpr (VEC) {
+        constexpr int E = XIn<XT>::kChunk;
+        if (a.cols % E == 0) {
+            const RowPfShape sh = row_pf_shape(a.cols / E);
+            if (sh.nt > 0) {
+                if (sh.nt != p.block)
+                    return RR_ERR_TIER;  // plan and launch disagree: refuse, launch nothing
+                const XT* x = static_cast<const XT*>(a.x);
+                YT* y = static_cast<YT*>(a.y);
+                switch (sh.nt * 16 + sh.nch) {
+                case 64 * 16 + 1: return launch_pf<XT, YT, 1, 64>(x, y, p, a);
+                case 64 * 16 + 2: return launch_pf<XT, YT, 2, 64>(x, y, p, a);
+                case 64 * 16 + 4: return launch_pf<XT, YT, 4, 64>(x, y, p, a);
+                case 128 * 16 + 4: return launch_pf<XT, YT, 4, 128>(x, y, p, a);
+                case 256 * 16 + 4: return launch_pf<XT, YT, 4, 256>(x, y, p, a);
+                case 512 * 16 + 4: return launch_pf<XT, YT, 4, 512>(x, y, p, a);
+                default: return RR_ERR_TIER;
+                }
+            }
+        }
+    }
+    return p.block == kSoftmaxWideThreads ? launch_block<XT, YT, VEC, kSoftmaxWideThreads>(p, a)
+                                          : launch_block<XT, YT, VEC, kBlockThreads>(p, a);
+}
+
 template <class XT, class YT, bool VEC>
 static rr_status launch_typed(const rr_plan& p, const SoftmaxLaunch& a)
 {
@@ -709,8 +735,7 @@ static rr_status launch_typed(const rr_plan& p, const SoftmaxLaunch& a)
     const hipStream_t s = a.stream;
     switch (p.tier) {
     case RR_TIER_BLOCK:
-        return p.block == kSoftmaxWideThreads ? launch_block<XT, YT, VEC, kSoftmaxWideThreads>(p, a)
-                                              : launch_block<XT, YT, VEC, kBlockThreads>(p, a);
+        return launch_block_tier<XT, YT, VEC>(p, a);
     case RR_TIER_WAVE:
         switch (p.lanes_per_row) {
         case 4: return launch_kernel(k_softmax_wave<XT, YT, VEC, 4>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);

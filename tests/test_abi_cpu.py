@@ -167,8 +167,12 @@ def test_softmax_tier_rule():
     assert rr.plan_softmax(8192, 8192)["block"] == 256
     assert rr.plan_softmax(8192, 8192)["grid"] == 512        # persistent rows: 2 per CU
     assert rr.plan_softmax(8192, 8191)["grid"] == 8192       # ragged rows: one per workgroup
-    assert rr.plan_softmax(64, 16384)["block"] == 256        # 256 threads x 8 chunks x 8 bf16
-    assert rr.plan_softmax(64, 16385)["block"] == 512        # longer rows: wider workgroups
+    assert rr.plan_softmax(64, 16384)["block"] == 512        # 2048 chunks: 512 threads x 4
+    assert rr.plan_softmax(65536, 1024)["block"] == 64       # 128 chunks: one wavefront x 2
+    assert rr.plan_softmax(65536, 1024)["grid"] == 256 * 16  # 32 loads per lane per CU
+    assert rr.plan_softmax(64, 16385)["block"] == 512        # ragged, long: wider workgroups
+    assert rr.plan_softmax(64, 8201)["block"] == 256         # ragged: one row per workgroup
+    assert rr.plan_softmax(64, 8200)["block"] == 512         # 1025 whole chunks: persistent
     assert rr.plan_softmax(100, 40)["tier"] == "wave"
     assert rr.plan_softmax(100, 4)["tier"] == "tiled"
     assert rr.plan_softmax(16, 1 << 20)["tier"] == "splitk"    # rows < CU and long rows

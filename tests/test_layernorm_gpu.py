@@ -196,6 +196,30 @@ def test_layernorm_rows_config_full_size():
     assert_close_f32(to_host(rstd)[sample], rrstd, "layernorm_rows rstd")
 
 
+PERSISTENT_SHAPES = [(40000, 512), (20000, 1000), (20000, 1024), (6000, 2048), (4000, 4096),
+                     (2000, 8192), (700, 16384), (3000, 4000)]
+
+
+@pytest.mark.parametrize("rows,cols", PERSISTENT_SHAPES)
+def test_layernorm_persistent_rows_walk_several_rows(rows, cols):
+    # every persistent (threads, chunks) shape with several rows per workgroup
+    x = _x("bf16", rows, cols, 3200 + cols)
+    g, b = _weights("f32", cols, 3300 + cols)
+    plan = rr.plan_layernorm(rows, cols, cu_count=rr.device_cu_count())
+    assert plan["tier"] == "block" and plan["grid"] < rows
+    mean = torch.empty(rows, device="cuda")
+    rstd = torch.empty(rows, device="cuda")
+    y = rr.layernorm_rows(to_gpu(x), to_gpu(g), to_gpu(b), 1e-5, mean_out=mean, rstd_out=rstd)
+    torch.cuda.synchronize()
+    sample = np.unique(np.concatenate([np.linspace(0, rows - 1, 40).astype(np.int64),
+                                       np.arange(rows - 5, rows)]))
+    ref, rm, rs = oracle.layernorm_rows(np.ascontiguousarray(x[sample]), g, b, 1e-5, "bf16")
+    what = "persistent %dx%d" % (rows, cols)
+    assert_bf16_within_1ulp_or_abs(to_host(y)[sample], ref, what)
+    assert_close_f32(to_host(mean)[sample], rm, what + " mean")
+    assert_close_f32(to_host(rstd)[sample], rs, what + " rstd")
+
+
 def test_layernorm_block_tier_bit_identical_across_runs():
     g = to_gpu(synth.normal_bf16(52, (2048, 8192)))
     first = rr.layernorm_rows(g).clone()

@@ -264,6 +264,28 @@ def test_softmax_strided_and_misaligned_rows(pad, offset, cols):
         _check_softmax(to_host(yv), ref, "bf16", "cols %d pad %d off %d %s" % (cols, pad, offset, tier))
 
 
+# Persistent block tier: every (threads, chunks) shape, with enough rows that
+# each workgroup walks several rows through its prefetch loop.
+PERSISTENT_SHAPES = [(40000, 512), (20000, 1000), (20000, 1024), (6000, 2048), (4000, 4096),
+                     (2000, 8192), (700, 16384), (3000, 4000)]
+
+
+@pytest.mark.parametrize("rows,cols", PERSISTENT_SHAPES)
+def test_softmax_persistent_rows_walk_several_rows(rows, cols):
+    x = synth.normal_bf16(3100 + cols, (rows, cols))
+    plan = rr.plan_softmax(rows, cols, cu_count=rr.device_cu_count())
+    assert plan["tier"] == "block" and plan["grid"] < rows
+    y = rr.softmax_rows(to_gpu(x))
+    torch.cuda.synchronize()
+    # sampled rows against the oracle, including the last rows of the walk
+    sample = np.unique(np.concatenate([np.linspace(0, rows - 1, 40).astype(np.int64),
+                                       np.arange(rows - 5, rows)]))
+    ref = oracle.softmax_rows(np.ascontiguousarray(x[sample]), "bf16")
+    assert_bf16_within_1ulp(to_host(y)[sample], ref, "persistent %dx%d" % (rows, cols))
+    s = y.float().sum(dim=1)
+    assert float((s - 1).abs().max()) <= 2.0 ** -8
+
+
 def test_softmax_uniform_row_is_exactly_2_pow_minus_13():
     x = torch.full((4, 8192), 3.0, dtype=torch.bfloat16, device="cuda")
     y = to_host(rr.softmax_rows(x))
