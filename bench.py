@@ -508,7 +508,7 @@ def main():
         if "multi_long" in next_rows:
             next_rows["multi_long"].update({
                 "config": "f32 sum, max and min over [16, 16777216] from one read, split-K "
-                          "(G = 64, 16-byte partials)",
+                          "(G = 32, 16-byte partials)",
                 "kernels": [KERNEL_OF_OP["multi_long"]]})
         if "layernorm" in next_rows:
             next_rows["layernorm"].update({

@@ -121,7 +121,7 @@ typedef struct {
  *   WAVE    if cols <= 64
  *   BLOCK   otherwise
  * SERIAL is used only when forced.  WAVE is legal for cols <= 64 only.
- * SPLITK: G = clamp(ceil(4*cu_count/rows), 1, min(256, ceil(cols/16384), tiles))
+ * SPLITK: G = clamp(ceil(2*cu_count/rows), 1, min(256, ceil(cols/16384), tiles))
  * with tiles = ceil(cols / tile_cols), tile_cols = 8192 (2048 on the scalar path).
  * Workspace: rows * 4 ticket bytes padded to 256, then rows * G partials of 8
  * bytes (16 for RR_SUM_MAX_MIN).
@@ -135,7 +135,8 @@ rr_status rr_plan_reduce(int64_t rows, int64_t cols, int64_t ld, rr_dtype dtype,
  * rr_plan_softmax -- tier selection for rr_softmax_rows: the reduce rule
  * (SPLITK when rows < cu_count and cols >= 65536, then TILED / WAVE /
  * BLOCK).  SPLITK uses tiles of 4 * 256 * 16-byte chunks (4 * 256 elements
- * on the scalar path), G as for rr_plan_reduce with that tile, and needs the
+ * on the scalar path), G as for rr_plan_reduce with that tile but 4 * cu_count
+ * workgroups in all, and needs the
  * workspace reported in workspace_bytes (rows * G * 8).
  */
 rr_status rr_plan_softmax(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype y_dtype,

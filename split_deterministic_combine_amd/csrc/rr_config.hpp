@@ -23,7 +23,12 @@ constexpr int kTiledRows = 4;
 constexpr int64_t kSplitKMinCols = 65536;
 constexpr int64_t kSplitKMinColsPerGroup = 16384;
 constexpr int kSplitKMaxSlices = 256;
-constexpr int kSplitKBlocksPerCU = 4;  // G aims at this many workgroups per CU in total
+// G aims at this many workgroups per CU in total: the row reduction streams
+// best at 2 (4 or 8 measured slower: more concurrent streams per CU contend);
+// the softmax and layernorm split-K passes and the axis split-K, which do
+// more work per element, keep 4.
+constexpr int kSplitKBlocksPerCU = 2;
+constexpr int kSplitKHeavyBlocksPerCU = 4;
 
 // Block-tier loads in flight per thread (128-bit each).
 constexpr int kBlockUnroll = 4;

@@ -28,10 +28,10 @@ uint64_t softmax_splitk_workspace_bytes(int64_t rows, int32_t slices)
 // row; the row is cut into tiles of one load round of a workgroup, dealt to
 // the G workgroups in turn.
 static void fill_splitk_geometry(int64_t rows, int64_t cols, int64_t tile, int32_t cu_count,
-                                 rr_plan* out)
+                                 int blocks_per_cu, rr_plan* out)
 {
     const int64_t ntiles = ceil_div(cols > 0 ? cols : 1, tile);
-    int64_t g = ceil_div((int64_t)kSplitKBlocksPerCU * cu_count, rows > 0 ? rows : 1);
+    int64_t g = ceil_div((int64_t)blocks_per_cu * cu_count, rows > 0 ? rows : 1);
     int64_t g_cap = ceil_div(cols, kSplitKMinColsPerGroup);
     if (g_cap > kSplitKMaxSlices) g_cap = kSplitKMaxSlices;
     if (g_cap > ntiles) g_cap = ntiles;  // every workgroup gets at least one tile
@@ -103,7 +103,7 @@ rr_status plan_reduce(int64_t rows, int64_t cols, int64_t ld, rr_dtype dtype, rr
         return RR_OK;
     }
     fill_splitk_geometry(rows, cols, (int64_t)kSplitKUnroll * kBlockThreads * vec_elems, cu_count,
-                         out);
+                         kSplitKBlocksPerCU, out);
     out->workspace_bytes = splitk_workspace_bytes(rows, out->slices, op == RR_SUM_MAX_MIN ? 16 : 8);
     return RR_OK;
 }
@@ -139,7 +139,7 @@ rr_status plan_softmax(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype y_
     const int vec_elems = vec ? (x_dtype == RR_BF16 ? 8 : 4) : 1;
     if (t == RR_TIER_SPLITK) {
         fill_splitk_geometry(rows, cols, (int64_t)kSoftmaxSplitKUnroll * kBlockThreads * vec_elems,
-                             cu_count, out);
+                             cu_count, kSplitKHeavyBlocksPerCU, out);
         out->workspace_bytes = softmax_splitk_workspace_bytes(rows, out->slices);
         return RR_OK;
     }
@@ -187,7 +187,7 @@ rr_status plan_layernorm(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype 
     const int vec_elems = vec ? (x_dtype == RR_BF16 ? 8 : 4) : 1;
     if (t == RR_TIER_SPLITK) {
         fill_splitk_geometry(rows, cols, (int64_t)kLnSplitKUnroll * kBlockThreads * vec_elems,
-                             cu_count, out);
+                             cu_count, kSplitKHeavyBlocksPerCU, out);
         out->workspace_bytes = (uint64_t)(rows * (int64_t)out->slices * 16);
         return RR_OK;
     }
@@ -241,7 +241,7 @@ rr_status plan_axis(int64_t outer, int64_t axis, int64_t inner, rr_dtype dtype, 
         const int gwl = axis_tile_log2(gpo);
         const int64_t lanes = kBlockThreads >> gwl;
         const int64_t tiles = outer * ceil_div(gpo, (int64_t)1 << gwl);
-        int64_t g = ceil_div((int64_t)kSplitKBlocksPerCU * cu_count, tiles > 0 ? tiles : 1);
+        int64_t g = ceil_div((int64_t)kSplitKHeavyBlocksPerCU * cu_count, tiles > 0 ? tiles : 1);
         int64_t cap = ceil_div(axis, lanes * kAxisMinStepsPerLane);
         if (cap > kAxisMaxSlices) cap = kAxisMaxSlices;
         if (g > cap) g = cap;

@@ -69,8 +69,8 @@ def test_auto_tier_rule(rows, cols, tier):
 
 def test_splitk_geometry_for_the_long_row_workload():
     p = rr.plan_reduce(16, 1 << 24, cu_count=256)
-    assert p["slices"] == 64 and p["grid"] == 1024 and p["tile_cols"] == 8192
-    assert p["workspace_bytes"] == 256 + 16 * 64 * 8
+    assert p["slices"] == 32 and p["grid"] == 512 and p["tile_cols"] == 8192
+    assert p["workspace_bytes"] == 256 + 16 * 32 * 8
 
 
 @pytest.mark.parametrize("rows,cols", [(1, 65536), (7, 100003), (200, 1 << 20), (3, 70001),
@@ -85,8 +85,8 @@ def test_splitk_every_workgroup_gets_a_tile(rows, cols):
 
 def test_multi_stat_plan_uses_16_byte_partials():
     p = rr.plan_reduce(16, 1 << 24, op="sum_max_min", cu_count=256)
-    assert p["tier"] == "splitk" and p["slices"] == 64
-    assert p["workspace_bytes"] == 256 + 16 * 64 * 16
+    assert p["tier"] == "splitk" and p["slices"] == 32
+    assert p["workspace_bytes"] == 256 + 16 * 32 * 16
     assert rr.plan_reduce(1000, 48, op="sum_max_min")["tier"] == "wave"
 
 
