@@ -116,6 +116,7 @@ constexpr int row_pf_blocks_per_cu(RowPfShape sh)
 // chunks per thread.
 constexpr int kLnMaxChunks = 8;
 constexpr int kLnSplitKUnroll = 4;
+constexpr int kLnMapMinRows = 4;  // split-K map: rows sharing one load of a tile's gamma / beta
 
 // LSE merge: partitions staged per batch of loads, and workgroup size.
 constexpr int kMergeBatch = 8;

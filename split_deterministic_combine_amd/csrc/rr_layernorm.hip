@@ -466,13 +466,30 @@ __global__ __launch_bounds__(kBlockThreads) void k_layernorm_tiled(
 }
 
 // ----------------------------------------------------------- split-K tier
-// G workgroups per row, tiles g, g + G, ... (kLnSplitKUnroll 16-byte chunks
-// per thread).  Statistics pass: workgroup (r, g) stores its shifted sums
-// (s1, s2) to part[(r * G + g) * 2 + {0, 1}].  Map pass: every workgroup of
-// row r reads the row's G pairs, sums each state over a fixed tree whose
-// leaves are the ranks in order (so every workgroup of the row gets the same
-// bits: "cluster_allreduce", description, the all-gather variant), and maps
-// its tiles.  Workgroup 0 of the row writes mean / rstd.
+// G workgroups per row own tiles g, g + G, ... (kLnSplitKUnroll 16-byte
+// chunks per thread).  Statistics pass: workgroup (r, g) stores its shifted
+// sums (s1, s2) to part[(r * G + g) * 2 + {0, 1}].  Map pass, tile-major: a
+// work item is one column tile of a chunk of rows; its workgroup sums each
+// of the chunk's rows' G pairs over a fixed tree (the same in every
+// workgroup: "cluster_allreduce", description, the all-gather variant),
+// loads the tile's gamma / beta once and maps that tile of every row of the
+// chunk, the next row's tile in flight.
+
+// Shifted sums of one tile's N values in double, into 4 interleaved
+// accumulator pairs (element i goes to pair i % 4; fixed order).
+template <int N, class R>
+__device__ __forceinline__ void ln_fold_raw(const R& raw, double K, double* s1, double* s2)
+{
+    float v[N];
+    raw.unpack(v);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const double d = (double)v[i] - K;
+        s1[i & 3] += d;
+        s2[i & 3] = __builtin_fma(d, d, s2[i & 3]);
+    }
+}
+
 template <class XT, bool VEC>
 __global__ __launch_bounds__(kBlockThreads) void k_layernorm_splitk_stats(
     const XT* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, int32_t G,
@@ -480,33 +497,59 @@ __global__ __launch_bounds__(kBlockThreads) void k_layernorm_splitk_stats(
 {
     constexpr int E = VEC ? XIn<XT>::kChunk : 1;
     constexpr int U = kLnSplitKUnroll;
-    constexpr int64_t kTile = (int64_t)U * kBlockThreads * E;
+    constexpr int N = U * E;
+    constexpr int64_t kTile = (int64_t)N * kBlockThreads;
     __shared__ double slot[2][kWavesPerBlock];
     const int64_t total = rows * G;
     const int64_t ntiles = ceil_div(cols, kTile);
+    const int64_t nfull = cols / kTile;
     for (int64_t blk = blockIdx.x; blk < total; blk += gridDim.x) {
         const int64_t r = blk / G;
         const int32_t gi = (int32_t)(blk - r * G);
         const XT* xr = x + r * ldx;
         const float kf = XIn<XT>::one(xr);
         const double K = (double)kf;
-        double s1 = 0.0, s2 = 0.0;
-        for (int64_t t = gi; t < ntiles; t += G) {
-            float v[U * E];
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                load_padded<XT, E, VEC>(
-                    xr, t * kTile + ((int64_t)u * kBlockThreads + threadIdx.x) * E, cols,
-                    v + u * E, kf);
-#pragma unroll
-            for (int i = 0; i < U * E; ++i) {
-                const double d = (double)v[i] - K;
-                s1 += d;
-                s2 = __builtin_fma(d, d, s2);
+        double s1[4] = {0.0, 0.0, 0.0, 0.0}, s2[4] = {0.0, 0.0, 0.0, 0.0};
+        // whole tiles, double-buffered (next tile's loads issued before the
+        // current one is folded; trip counts uniform over the workgroup)
+        const int64_t n = gi < nfull ? (nfull - 1 - gi) / G + 1 : 0;
+        if (n > 0) {
+            const int64_t step = (int64_t)G * kTile;
+            const XT* tp = xr + (int64_t)gi * kTile;
+            RawTile<XT, VEC, U> A, B;
+            A.load(tp);
+            int64_t k = 0;
+            for (; k + 2 < n; k += 2) {
+                B.load(tp + (k + 1) * step);
+                __builtin_amdgcn_sched_barrier(0);
+                ln_fold_raw<N>(A, K, s1, s2);
+                A.load(tp + (k + 2) * step);
+                __builtin_amdgcn_sched_barrier(0);
+                ln_fold_raw<N>(B, K, s1, s2);
+            }
+            if (k + 1 < n) {
+                B.load(tp + (k + 1) * step);
+                __builtin_amdgcn_sched_barrier(0);
+                ln_fold_raw<N>(A, K, s1, s2);
+                ln_fold_raw<N>(B, K, s1, s2);
+            } else {
+                ln_fold_raw<N>(A, K, s1, s2);
             }
         }
-        const double S1 = block_reduce<SumF32, kBlockThreads>(s1, slot[0]);
-        const double S2 = block_reduce<SumF32, kBlockThreads>(s2, slot[1]);
+        for (int64_t t = gi + n * G; t < ntiles; t += G) {  // ragged tile, padded with K
+            float v[N];
+            load_tile_padded<XT, E, VEC, U>(xr, t * kTile, cols, v, kf);
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                const double d = (double)v[i] - K;
+                s1[i & 3] += d;
+                s2[i & 3] = __builtin_fma(d, d, s2[i & 3]);
+            }
+        }
+        const double t1 = (s1[0] + s1[1]) + (s1[2] + s1[3]);
+        const double t2 = (s2[0] + s2[1]) + (s2[2] + s2[3]);
+        const double S1 = block_reduce<SumF32, kBlockThreads>(t1, slot[0]);
+        const double S2 = block_reduce<SumF32, kBlockThreads>(t2, slot[1]);
         if (threadIdx.x == 0) {
             part[(r * G + gi) * 2] = S1;
             part[(r * G + gi) * 2 + 1] = S2;
@@ -515,54 +558,124 @@ __global__ __launch_bounds__(kBlockThreads) void k_layernorm_splitk_stats(
     }
 }
 
-template <class XT, class YT, bool VEC>
+// Row statistics of rows r0 .. r0+nr-1 (nr <= kBlockThreads) from their G
+// pairs, into LDS.  TPR = threads per row (a power of two, at most 64):
+// lane l of a row sums the pairs g = l, l + TPR, ... in order, then the TPR
+// lane sums are added over the fixed DPP tree.
+template <class XT>
+__device__ __forceinline__ void ln_row_stats_lds(const XT* x, int64_t ldx, int64_t r0, int nr,
+                                                 int64_t cols, float eps, int32_t G,
+                                                 const double* part, double* smean, float* srstd)
+{
+    int tpr = 1;
+    while (tpr < 64 && tpr * 2 * nr <= kBlockThreads)
+        tpr *= 2;
+    const int row = (int)threadIdx.x / tpr;
+    const int lane = (int)threadIdx.x % tpr;
+    double s1 = 0.0, s2 = 0.0;
+    if (row < nr) {
+        const double* pr = part + (r0 + row) * (int64_t)G * 2;
+        for (int32_t g = lane; g < G; g += tpr) {
+            s1 += pr[g * 2];
+            s2 += pr[g * 2 + 1];
+        }
+    }
+    double S1 = s1, S2 = s2;
+    switch (tpr) {
+    case 2: S1 = segment_reduce<SumF32, 2>(s1); S2 = segment_reduce<SumF32, 2>(s2); break;
+    case 4: S1 = segment_reduce<SumF32, 4>(s1); S2 = segment_reduce<SumF32, 4>(s2); break;
+    case 8: S1 = segment_reduce<SumF32, 8>(s1); S2 = segment_reduce<SumF32, 8>(s2); break;
+    case 16: S1 = segment_reduce<SumF32, 16>(s1); S2 = segment_reduce<SumF32, 16>(s2); break;
+    case 32: S1 = segment_reduce<SumF32, 32>(s1); S2 = segment_reduce<SumF32, 32>(s2); break;
+    case 64: S1 = segment_reduce<SumF32, 64>(s1); S2 = segment_reduce<SumF32, 64>(s2); break;
+    default: break;
+    }
+    if (row < nr && lane == 0) {
+        const double K = (double)XIn<XT>::one(x + (r0 + row) * ldx);
+        const LnRow st = row_from_shifted(K, S1, S2, cols, eps);
+        smean[row] = st.mean;
+        srstd[row] = st.rstd;
+    }
+}
+
+// Work item b of the map pass: column tile t = b % ntiles of the row chunk
+// b / ntiles (rows chunk * rc .. + rc - 1, rc <= kBlockThreads).  The
+// workgroup of tile 0 of a chunk writes that chunk's mean / rstd.
+template <class XT, class YT, bool VEC, bool AFF>
 __global__ __launch_bounds__(kBlockThreads) void k_layernorm_splitk_map(
     const XT* __restrict__ x, YT* __restrict__ y, Weights g, Weights b, float* mean_out,
     float* rstd_out, int64_t rows, int64_t cols, int64_t ldx, int64_t ldy, float eps, int32_t G,
-    const double* __restrict__ part)
+    const double* __restrict__ part, int32_t rc)
 {
     constexpr int E = VEC ? XIn<XT>::kChunk : 1;
     constexpr int U = kLnSplitKUnroll;
-    constexpr int64_t kTile = (int64_t)U * kBlockThreads * E;
-    static_assert(kSplitKMaxSlices <= kBlockThreads, "one pair per thread in the row fold");
-    __shared__ double slot[2][kWavesPerBlock];
-    const int64_t total = rows * G;
+    constexpr int N = U * E;
+    constexpr int64_t kTile = (int64_t)N * kBlockThreads;
+    __shared__ double smean[kBlockThreads];
+    __shared__ float srstd[kBlockThreads];
     const int64_t ntiles = ceil_div(cols, kTile);
-    for (int64_t blk = blockIdx.x; blk < total; blk += gridDim.x) {
-        const int64_t r = blk / G;
-        const int32_t gi = (int32_t)(blk - r * G);
-        const XT* xr = x + r * ldx;
-        YT* yr = y + r * ldy;
-        double p1 = 0.0, p2 = 0.0;
-        if ((int32_t)threadIdx.x < G) {
-            p1 = part[(r * G + threadIdx.x) * 2];
-            p2 = part[(r * G + threadIdx.x) * 2 + 1];
+    const int64_t nfull = cols / kTile;
+    const int64_t nchunk = ceil_div(rows, (int64_t)rc);
+    int64_t have = -1;  // row chunk whose statistics are in LDS
+    for (int64_t item = blockIdx.x; item < ntiles * nchunk; item += gridDim.x) {
+        const int64_t chunk = item / ntiles;
+        const int64_t t = item - chunk * ntiles;
+        const int64_t r0 = chunk * rc;
+        const int nr = (int)(rows - r0 < rc ? rows - r0 : rc);
+        if (chunk != have) {  // uniform over the workgroup
+            __syncthreads();  // the previous chunk is done with the LDS statistics
+            ln_row_stats_lds<XT>(x, ldx, r0, nr, cols, eps, G, part, smean, srstd);
+            __syncthreads();
+            have = chunk;
         }
-        const double K = (double)XIn<XT>::one(xr);
-        const double S1 = block_reduce<SumF32, kBlockThreads>(p1, slot[0]);
-        const double S2 = block_reduce<SumF32, kBlockThreads>(p2, slot[1]);
-        const LnRow st = row_from_shifted(K, S1, S2, cols, eps);
-        if (gi == 0 && threadIdx.x == 0)
-            write_stats(mean_out, rstd_out, r, st);
-        const Centre centre(st.mean);
-        for (int64_t t = gi; t < ntiles; t += G) {
-            float v[U * E];
+        if (t == 0 && (int)threadIdx.x < nr)
+            write_stats(mean_out, rstd_out, r0 + threadIdx.x,
+                        LnRow{smean[threadIdx.x], srstd[threadIdx.x]});
+        {
+            float gw[AFF ? N : 1], bw[AFF ? N : 1];
+            if constexpr (AFF) {
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-                load_padded<XT, E, VEC>(
-                    xr, t * kTile + ((int64_t)u * kBlockThreads + threadIdx.x) * E, cols,
-                    v + u * E, 0.0f);
+                for (int u = 0; u < U; ++u) {
+                    const int64_t j0 = t * kTile + ((int64_t)u * kBlockThreads + threadIdx.x) * E;
+                    load_weights<E, VEC>(g, j0, cols, gw + u * E);
+                    load_weights<E, VEC>(b, j0, cols, bw + u * E);
+                }
+            }
+            if (t < nfull) {
+                // whole tiles: row r's tile in A while row r+1's loads fly
+                RawTile<XT, VEC, U> A, B;
+                A.load(x + r0 * ldx + t * kTile);
+                for (int i = 0; i < nr; ++i) {
+                    const int ip = i + 1 < nr ? i + 1 : i;
+                    B.load(x + (r0 + ip) * ldx + t * kTile);
+                    __builtin_amdgcn_sched_barrier(0);
+                    float v[N];
+                    A.unpack(v);
+                    const Centre centre(smean[i]);
+                    const float rs = srstd[i];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int64_t j0 = t * kTile + ((int64_t)u * kBlockThreads + threadIdx.x) * E;
+                    for (int k = 0; k < N; ++k) {
+                        const float q = centre(v[k]) * rs;
+                        v[k] = AFF ? __builtin_fmaf(q, gw[k], bw[k]) : q;
+                    }
+                    store_tile_full<YT, E, VEC, U>(y + (r0 + i) * ldy + t * kTile, v);
+                    A = B;
+                }
+            } else {
+                for (int i = 0; i < nr; ++i) {
+                    float v[N];
+                    load_tile_padded<XT, E, VEC, U>(x + (r0 + i) * ldx, t * kTile, cols, v, 0.0f);
+                    const Centre centre(smean[i]);
+                    const float rs = srstd[i];
 #pragma unroll
-                for (int i = 0; i < E; ++i)
-                    v[u * E + i] = centre(v[u * E + i]);
-                affine<E, VEC>(v + u * E, st.rstd, g, b, j0, cols);
-                store_masked<YT, E, VEC>(yr, j0, cols, v + u * E);
+                    for (int k = 0; k < N; ++k) {
+                        const float q = centre(v[k]) * rs;
+                        v[k] = AFF ? __builtin_fmaf(q, gw[k], bw[k]) : q;
+                    }
+                    store_tile_masked<YT, E, VEC, U>(y + (r0 + i) * ldy, t * kTile, cols, v);
+                }
             }
         }
-        __syncthreads();  // slot reuse by the next (row, slice)
     }
 }
 
@@ -677,8 +790,25 @@ static rr_status launch_typed(const rr_plan& p, const LayernormLaunch& a)
                                      a.rows, a.cols, a.ld_x, p.slices, part);
         if (st != RR_OK)
             return st;
-        return launch_kernel(k_layernorm_splitk_map<XT, YT, VEC>, grid, block, 0, s, RR_LN_ARGS,
-                             p.slices, (const double*)part);
+        // map: work items of one column tile x a chunk of rows; chunks of at
+        // least kLnMapMinRows rows (gamma / beta reuse), enough of them to give
+        // 2 work items per CU, at most kSplitKHeavyBlocksPerCU workgroups per CU
+        constexpr int E = VEC ? XIn<XT>::kChunk : 1;
+        const int64_t ntiles = ceil_div(a.cols, (int64_t)kLnSplitKUnroll * kBlockThreads * E);
+        int64_t nchunk = ceil_div((int64_t)2 * a.cu, ntiles);
+        const int64_t max_chunks = ceil_div(a.rows, (int64_t)kLnMapMinRows);
+        if (nchunk > max_chunks) nchunk = max_chunks;
+        if (nchunk < 1) nchunk = 1;
+        int64_t rc = ceil_div(a.rows, nchunk);
+        if (rc > kBlockThreads) rc = kBlockThreads;
+        const int64_t items = ntiles * ceil_div(a.rows, rc);
+        const int64_t cap = (int64_t)kSplitKHeavyBlocksPerCU * a.cu;
+        const dim3 mgrid((unsigned)(items < cap ? items : cap));
+        if (g.p || b.p)
+            return launch_kernel(k_layernorm_splitk_map<XT, YT, VEC, true>, mgrid, block, 0, s,
+                                 RR_LN_ARGS, p.slices, (const double*)part, (int32_t)rc);
+        return launch_kernel(k_layernorm_splitk_map<XT, YT, VEC, false>, mgrid, block, 0, s,
+                             RR_LN_ARGS, p.slices, (const double*)part, (int32_t)rc);
     }
     default:
         return RR_ERR_TIER;

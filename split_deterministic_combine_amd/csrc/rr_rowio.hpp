@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "rr_config.hpp"
 #include "rr_device.hpp"
 
 namespace rr {
@@ -121,5 +122,104 @@ __device__ __forceinline__ void unpack_chunk(uint4 u, float* v)
         v[2] = __uint_as_float(u.z); v[3] = __uint_as_float(u.w);
     }
 }
+
+// ------------------------------------------------ split-K tiles of a row
+// One split-K tile of a thread: U chunks of E elements, chunk u at element
+// offset (u * kBlockThreads + threadIdx.x) * E of the tile.
+template <class XT, int E, bool VEC, int U>
+__device__ __forceinline__ void load_tile_full(const XT* tile, float* v)
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const XT* p = tile + ((int64_t)u * kBlockThreads + threadIdx.x) * E;
+        if constexpr (VEC)
+            XIn<XT>::chunk(p, v + u * E);
+        else
+            v[u] = XIn<XT>::one(p);
+    }
+}
+
+template <class XT, int E, bool VEC, int U>
+__device__ __forceinline__ void load_tile_padded(const XT* row, int64_t begin, int64_t cols, float* v,
+                                                 float pad = -__builtin_inff())
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        load_padded<XT, E, VEC>(row, begin + ((int64_t)u * kBlockThreads + threadIdx.x) * E, cols,
+                                v + u * E, pad);
+}
+
+template <class YT, int E, bool VEC, int U>
+__device__ __forceinline__ void store_tile_full(YT* tile, const float* v)
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        YT* p = tile + ((int64_t)u * kBlockThreads + threadIdx.x) * E;
+        if constexpr (VEC)
+            YOut<YT>::template chunk<E>(p, v + u * E);
+        else
+            YOut<YT>::one(p, v[u]);
+    }
+}
+
+template <class YT, int E, bool VEC, int U>
+__device__ __forceinline__ void store_tile_masked(YT* row, int64_t begin, int64_t cols, const float* v)
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        store_masked<YT, E, VEC>(row, begin + ((int64_t)u * kBlockThreads + threadIdx.x) * E, cols,
+                                 v + u * E);
+}
+
+// A thread's share of one whole tile as loaded, before conversion to float,
+// so that the next tile's loads can be in flight while this one is folded.
+// Plain (cached) loads: split-K statistics passes are followed by a map pass
+// that re-reads the same rows soon after.
+template <class XT, bool VEC, int U>
+struct RawTile;
+template <class XT, int U>
+struct RawTile<XT, true, U> {
+    uint4 c[U];
+    __device__ void load(const XT* tile)
+    {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            c[u] = *reinterpret_cast<const uint4*>(
+                tile + ((int64_t)u * kBlockThreads + threadIdx.x) * XIn<XT>::kChunk);
+    }
+    __device__ void unpack(float* v) const
+    {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if constexpr (sizeof(XT) == 2) {
+                float* o = v + u * 8;
+                o[0] = bf16_lo(c[u].x); o[1] = bf16_hi(c[u].x);
+                o[2] = bf16_lo(c[u].y); o[3] = bf16_hi(c[u].y);
+                o[4] = bf16_lo(c[u].z); o[5] = bf16_hi(c[u].z);
+                o[6] = bf16_lo(c[u].w); o[7] = bf16_hi(c[u].w);
+            } else {
+                float* o = v + u * 4;
+                o[0] = __uint_as_float(c[u].x); o[1] = __uint_as_float(c[u].y);
+                o[2] = __uint_as_float(c[u].z); o[3] = __uint_as_float(c[u].w);
+            }
+        }
+    }
+};
+template <class XT, int U>
+struct RawTile<XT, false, U> {
+    float c[U];
+    __device__ void load(const XT* tile)
+    {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            c[u] = XIn<XT>::one(tile + (int64_t)u * kBlockThreads + threadIdx.x);
+    }
+    __device__ void unpack(float* v) const
+    {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            v[u] = c[u];
+    }
+};
 
 }  // namespace rr
