@@ -134,20 +134,27 @@ rr_status rr_plan_reduce(int64_t rows, int64_t cols, int64_t ld, rr_dtype dtype,
 /*
  * rr_plan_softmax -- tier selection for rr_softmax_rows: the reduce rule
  * (SPLITK when rows < cu_count and cols >= 65536, then TILED / WAVE /
- * BLOCK).  SPLITK uses tiles of 4 * 256 * 16-byte chunks (4 * 256 elements
- * on the scalar path), G as for rr_plan_reduce with that tile but 4 * cu_count
- * workgroups in all, and needs the
- * workspace reported in workspace_bytes (rows * G * 8).
+ * BLOCK).  BLOCK: rows of whole 16-byte chunks (c chunks, c <= 2048, aligned)
+ * run persistent workgroups sized to the row -- (threads, chunks per thread)
+ * = (64, 1) for c <= 64, (64, 2) <= 128, (64, 4) <= 256, (128, 4) <= 512,
+ * (256, 4) <= 1024, (512, 4) <= 2048 -- with 32 / (wavefronts x chunks per
+ * thread) workgroups per CU (at least 1), lowered at launch to what the
+ * kernel's occupancy allows; other rows take one workgroup of 256 threads
+ * per row (512 beyond 2048 chunks), reading x twice beyond 8 chunks per
+ * thread.  SPLITK uses tiles of 4 * 256 * 16-byte chunks (4 * 256 elements
+ * on the scalar path), G as for rr_plan_reduce with that tile but
+ * 4 * cu_count workgroups in all, and needs the workspace reported in
+ * workspace_bytes (rows * G * 8).
  */
 rr_status rr_plan_softmax(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype y_dtype,
                           rr_tier tier, int32_t cu_count, rr_plan* plan_out);
 
 /*
- * rr_plan_layernorm -- tier selection for rr_layernorm_rows: the softmax rule.
- * BLOCK keeps rows of whole 16-byte chunks, up to 8 chunks per thread of 256,
- * in registers on persistent workgroups (2 per CU); longer or unaligned rows
- * are read twice.  SPLITK tiles are 4 * 256 16-byte chunks; its workspace is
- * rows * G * 16 bytes (workspace_bytes).
+ * rr_plan_layernorm -- tier selection for rr_layernorm_rows: the softmax rule,
+ * with the same persistent BLOCK shapes; unaligned or ragged rows of up to 8
+ * chunks per thread of 256 stay in registers one row per workgroup, longer
+ * rows are read twice.  SPLITK tiles are 4 * 256 16-byte chunks, G as for the
+ * softmax; its workspace is rows * G * 16 bytes (workspace_bytes).
  */
 rr_status rr_plan_layernorm(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype y_dtype,
                             rr_dtype w_dtype, rr_tier tier, int32_t cu_count, rr_plan* plan_out);
