@@ -3,6 +3,7 @@ headers declare, plans tiers by the documented rule and rejects bad
 arguments before it touches the device."""
 import ctypes
 import os
+import subprocess
 import re
 
 import pytest
@@ -38,6 +39,24 @@ def test_every_declared_symbol_is_exported():
     assert {"rr_reduce_rows", "rr_softmax_rows", "rr_splitk_lse_merge"} <= set(declared)
     missing = [n for n in declared if not hasattr(lib, n)]
     assert not missing, missing
+
+
+def test_plain_c_consumer_compiles_links_and_runs(tmp_path):
+    # rr.h is a C header: a C11 program includes it, links librr.so and calls
+    # the host-only entry points
+    exe = str(tmp_path / "abi_consumer")
+    libdir = os.path.dirname(rr.lib_path())
+    cmd = ["gcc", "-std=c11", "-Wall", "-Wextra", "-Werror", "-pedantic",
+           "-I", os.path.join(ROOT, "include"), os.path.join(ROOT, "tests", "abi_consumer.c"),
+           "-o", exe, "-L", libdir, "-l:librr.so", "-Wl,-rpath," + libdir]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    out = subprocess.run([exe], check=True, capture_output=True, text=True).stdout
+    assert "reduce tier=5 slices=32 grid=512 ws=4352" in out
+    assert "softmax tier=2 block=256 grid=512" in out
+    assert "layernorm tier=2 block=128 grid=1024" in out
+    assert "axis tier=5 slices=16" in out
+    assert "bad ld -> 2 (invalid shape" in out
+    assert "empty softmax -> 0" in out and "P=0 merge -> 2" in out
 
 
 def test_status_strings_are_distinct():
