@@ -24,6 +24,8 @@
 // (wave DPP tree, then waves in order), so every run gives the same bits.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "rr_config.hpp"
 #include "rr_device.hpp"
 #include "rr_launch.hpp"
@@ -151,6 +153,58 @@ __device__ __forceinline__ void write_stats(float* mean_out, float* rstd_out, in
         rstd_out[r] = st.rstd;
 }
 
+// The weights of a thread's NCH chunks of E columns as raw pieces of 2E bytes
+// (a bf16 chunk; a float chunk is two pieces, a bf16 one reads its piece
+// twice).  Chunks past the row end load chunk 0 and are never stored.  No
+// branch depends on a loaded value, so all the loads go out together and the
+// unpack, later, waits for nothing else.
+template <int NCH, int NT, int E>
+struct RawWeights {
+    using Piece = typename std::conditional<E == 8, uint4, uint2>::type;
+    Piece lo[NCH], hi[NCH];
+    __device__ void load(const Weights& w, int64_t cols)
+    {
+        if (!w.p)
+            return;
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) {
+            int64_t j0 = ((int64_t)threadIdx.x + (int64_t)k * NT) * E;
+            j0 = j0 < cols ? j0 : 0;
+            const Piece* q = reinterpret_cast<const Piece*>(static_cast<const char*>(w.p) +
+                                                            j0 * (w.bf16 ? 2 : 4));
+            lo[k] = q[0];
+            hi[k] = q[w.bf16 ? 0 : 1];
+        }
+    }
+    __device__ void unpack(const Weights& w, float* o) const
+    {
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) {
+            float* ok = o + k * E;
+            if (!w.p) {
+#pragma unroll
+                for (int i = 0; i < E; ++i)
+                    ok[i] = w.dflt;
+            } else if (w.bf16) {
+                const uint32_t* u = reinterpret_cast<const uint32_t*>(&lo[k]);
+#pragma unroll
+                for (int i = 0; i < E / 2; ++i) {
+                    ok[2 * i] = bf16_lo(u[i]);
+                    ok[2 * i + 1] = bf16_hi(u[i]);
+                }
+            } else {
+                const uint32_t* u0 = reinterpret_cast<const uint32_t*>(&lo[k]);
+                const uint32_t* u1 = reinterpret_cast<const uint32_t*>(&hi[k]);
+#pragma unroll
+                for (int i = 0; i < E / 2; ++i) {
+                    ok[i] = __uint_as_float(u0[i]);
+                    ok[E / 2 + i] = __uint_as_float(u1[i]);
+                }
+            }
+        }
+    }
+};
+
 // ------------------------------------------------ block tier, row in registers
 // One row at a time per workgroup; the thread's chunks are k = 0 .. NCH-1 at
 // columns (threadIdx.x + k * NT) * E.  `valid(k, i)` says whether element i
@@ -227,25 +281,11 @@ __device__ __forceinline__ void ln_row_from_chunks(const uint4* raw, YT* yr, int
     }
 }
 
-template <class XT, int NCH, int NT, bool EXACT>
-__device__ __forceinline__ void ln_load_row_chunks(const XT* xr, int64_t cols, uint4* raw)
-{
-    constexpr int E = XIn<XT>::kChunk;
-#pragma unroll
-    for (int k = 0; k < NCH; ++k) {
-        int64_t j0 = ((int64_t)threadIdx.x + (int64_t)k * NT) * E;
-        if (!EXACT)
-            j0 = j0 < cols ? j0 : 0;  // chunks past the row end read chunk 0 (ignored)
-        raw[k] = load16_nt(xr + j0);
-    }
-}
-
-// Persistent rows with a one-row prefetch: workgroup b takes rows b, b + grid,
-// ... and loads the next row's chunks while it computes the current one (two
-// register buffers; with no next row the prefetch re-reads the current one,
-// an L2 hit, and is dropped, so no load sits behind a branch).  Rows are
-// whole 16-byte chunks, 16-byte aligned.  A thread's columns are the same in
-// every row, so its gamma / beta are loaded into registers once.
+// Persistent rows (persistent_rows: one-row prefetch, two register buffers).
+// A thread's columns are the same in every row, so its gamma / beta are loaded
+// into registers once: issued before the first row's loads, unpacked after
+// the first two rows' loads are out.  Rows are whole 16-byte chunks, 16-byte
+// aligned.
 template <class XT, class YT, int NCH, int NT, bool EXACT, bool AFF>
 __global__ __launch_bounds__(NT) void k_layernorm_rows_pf(
     const XT* __restrict__ x, YT* __restrict__ y, Weights g, Weights b, float* mean_out,
@@ -253,37 +293,30 @@ __global__ __launch_bounds__(NT) void k_layernorm_rows_pf(
 {
     constexpr int E = XIn<XT>::kChunk;
     __shared__ double slot[2][NT / kWave];
-    int64_t r = blockIdx.x;
-    if (r >= rows)
+    if ((int64_t)blockIdx.x >= rows)
         return;
-    const int64_t step = gridDim.x;
-    uint4 a[NCH], c[NCH];
-    ln_load_row_chunks<XT, NCH, NT, EXACT>(x + r * ldx, cols, a);
     float gw[AFF ? NCH * E : 1], bw[AFF ? NCH * E : 1];
+    RawWeights<AFF ? NCH : 1, NT, E> graw, braw;
     if constexpr (AFF) {
-#pragma unroll
-        for (int k = 0; k < NCH; ++k) {
-            const int64_t j0 = ((int64_t)threadIdx.x + (int64_t)k * NT) * E;
-            load_weights<E, true>(g, j0, cols, gw + k * E);
-            load_weights<E, true>(b, j0, cols, bw + k * E);
-        }
+        graw.load(g, cols);
+        braw.load(b, cols);
     }
-    for (;;) {
-        const bool more = r + step < rows;
-        ln_load_row_chunks<XT, NCH, NT, EXACT>(x + (more ? r + step : r) * ldx, cols, c);
-        ln_row_from_chunks<XT, YT, NCH, NT, EXACT, AFF>(a, y + r * ldy, r, cols, eps, gw, bw,
-                                                        mean_out, rstd_out, slot[0], slot[1]);
-        if (!more)
-            break;
-        r += step;
-        const bool more2 = r + step < rows;
-        ln_load_row_chunks<XT, NCH, NT, EXACT>(x + (more2 ? r + step : r) * ldx, cols, a);
-        ln_row_from_chunks<XT, YT, NCH, NT, EXACT, AFF>(c, y + r * ldy, r, cols, eps, gw, bw,
-                                                        mean_out, rstd_out, slot[0], slot[1]);
-        if (!more2)
-            break;
-        r += step;
-    }
+    persistent_rows<NCH>(
+        blockIdx.x, gridDim.x, rows,
+        [&](int64_t r, bool live, uint4* raw) {
+            load_row_raw<NCH, NT>(x + r * ldx, live ? cols * (int64_t)sizeof(XT) : 0, raw);
+        },
+        [&] {
+            if constexpr (AFF) {
+                graw.unpack(g, gw);
+                braw.unpack(b, bw);
+            }
+        },
+        [&](const uint4* raw, int64_t r, int) {
+            ln_row_from_chunks<XT, YT, NCH, NT, EXACT, AFF>(raw, y + r * ldy, r, cols, eps, gw,
+                                                            bw, mean_out, rstd_out, slot[0],
+                                                            slot[1]);
+        });
 }
 
 // Any alignment and any column count (masked chunks), one row per workgroup

@@ -222,4 +222,81 @@ struct RawTile<XT, false, U> {
     }
 };
 
+// The 16-byte chunks k = 0 .. NCH-1 of a row held in registers by NT threads,
+// at byte offsets (threadIdx.x + k * NT) * 16 from the row's start, as
+// non-temporal buffer loads.  The row's start and length go into a buffer
+// descriptor (scalar registers) and each chunk's offset is a loop-invariant
+// 32-bit VGPR, so issuing a row takes no vector instruction.  The descriptor
+// covers row_bytes: a chunk past the row end reads as zero (never stored).
+// Word 3 sets the 32-bit data format, which untyped buffer loads on this
+// architecture family expect to be non-zero.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kBufferNonTemporal = 2;  // cache-policy bit of the buffer builtins
+
+template <int NCH, int NT>
+__device__ __forceinline__ void load_row_raw(const void* row, int64_t row_bytes, uint4* raw)
+{
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(row), 0, (int)row_bytes, kBufferWord3);
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+        const int off = ((int)threadIdx.x + k * NT) * 16;
+        const rr_u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kBufferNonTemporal);
+        raw[k] = make_uint4(v.x, v.y, v.z, v.w);
+    }
+}
+
+// Persistent rows with a one-row prefetch.  Workgroup b takes rows b, b + step,
+// ... < rows; the loads of the next row go out before the current row is
+// computed, into the other of two register buffers.  On gfx9 one in-order
+// counter (vmcnt) covers loads and stores, and the compiler places each wait
+// before the first use of a row's data, so two things keep that wait from
+// retiring the next row's loads too:
+//   * a scheduling barrier after each prefetch keeps the first uses of the
+//     current row below those loads;
+//   * the first row is peeled, so the loop is entered with the same memory
+//     operations in flight as on its back edge (the next row's loads, then
+//     the current row's stores).  Otherwise the wait at the loop head is the
+//     stricter of the two paths, and on the back edge it also waits for the
+//     previous row's stores.
+// Loads the caller issues before this (a row's weights) retire with the first
+// row.  With no next row the prefetch still goes out, with no bytes to read
+// (load_row_raw then reads zeros and touches no memory), so no load sits
+// behind a branch.  load(r, live, buf) issues row r's loads (none of its bytes
+// when live is false); start() runs once, after the first two rows' loads are
+// out (to unpack what the caller loaded before); row(buf, r, parity) computes
+// and stores row r (parity alternates, for double-buffered shared memory).
+template <int NCH, class Load, class Start, class Row>
+__device__ __forceinline__ void persistent_rows(int64_t r, int64_t step, int64_t rows, Load load,
+                                                Start start, Row row)
+{
+    // Rows after the current one; the loop tests it against zero only (a
+    // 64-bit less-than has no scalar form and would put a VGPR write, and
+    // with it a wait, ahead of the prefetch).
+    int64_t left = (rows - 1 - r) / step;
+    uint4 a[NCH], c[NCH];
+    load(r, true, a);
+    __builtin_amdgcn_sched_barrier(0);  // the first row's loads go out first
+    load(r + step, left != 0, c);
+    __builtin_amdgcn_sched_barrier(0);
+    start();
+    row(a, r, 0);
+    for (;;) {
+        if (left == 0)
+            return;
+        r += step;
+        --left;
+        load(r + step, left != 0, a);
+        __builtin_amdgcn_sched_barrier(0);
+        row(c, r, 1);
+        if (left == 0)
+            return;
+        r += step;
+        --left;
+        load(r + step, left != 0, c);
+        __builtin_amdgcn_sched_barrier(0);
+        row(a, r, 0);
+    }
+}
+
 }  // namespace rr

@@ -166,45 +166,23 @@ __device__ __forceinline__ void softmax_row_from_chunks(const uint4* raw, YT* yr
     }
 }
 
-template <class XT, int NCH, int NT, bool EXACT>
-__device__ __forceinline__ void load_row_chunks(const XT* xr, int64_t cols, uint4* raw)
-{
-    constexpr int E = XIn<XT>::kChunk;
-#pragma unroll
-    for (int k = 0; k < NCH; ++k) {
-        int64_t j0 = ((int64_t)threadIdx.x + (int64_t)k * NT) * E;
-        if (!EXACT)
-            j0 = j0 < cols ? j0 : 0;  // chunks past the row end read chunk 0 (ignored)
-        raw[k] = load16_nt(xr + j0);
-    }
-}
-
 template <class XT, class YT, int NCH, int NT, bool EXACT>
 __global__ __launch_bounds__(NT) void k_softmax_rows_pf(const XT* __restrict__ x,
                                                         YT* __restrict__ y, int64_t rows,
                                                         int64_t cols, int64_t ldx, int64_t ldy)
 {
     __shared__ MS slot[2][NT / kWave];
-    int64_t r = blockIdx.x;
-    if (r >= rows)
+    if ((int64_t)blockIdx.x >= rows)
         return;
-    const int64_t step = gridDim.x;
-    uint4 a[NCH], b[NCH];
-    load_row_chunks<XT, NCH, NT, EXACT>(x + r * ldx, cols, a);
-    for (;;) {
-        const bool more = r + step < rows;
-        load_row_chunks<XT, NCH, NT, EXACT>(x + (more ? r + step : r) * ldx, cols, b);
-        softmax_row_from_chunks<XT, YT, NCH, NT, EXACT>(a, y + r * ldy, cols, slot[0]);
-        if (!more)
-            break;
-        r += step;
-        const bool more2 = r + step < rows;
-        load_row_chunks<XT, NCH, NT, EXACT>(x + (more2 ? r + step : r) * ldx, cols, a);
-        softmax_row_from_chunks<XT, YT, NCH, NT, EXACT>(b, y + r * ldy, cols, slot[1]);
-        if (!more2)
-            break;
-        r += step;
-    }
+    persistent_rows<NCH>(
+        blockIdx.x, gridDim.x, rows,
+        [&](int64_t r, bool live, uint4* raw) {
+            load_row_raw<NCH, NT>(x + r * ldx, live ? cols * (int64_t)sizeof(XT) : 0, raw);
+        },
+        [] {},
+        [&](const uint4* raw, int64_t r, int par) {
+            softmax_row_from_chunks<XT, YT, NCH, NT, EXACT>(raw, y + r * ldy, cols, slot[par]);
+        });
 }
 
 // ---------------------------------------- block tier, streaming long rows
