@@ -44,6 +44,10 @@
  *   - Results are bit-identical from run to run for the same device, shape,
  *     strides, alignment, tier and library build.
  *   - No C++ exception crosses this interface.
+ *   - The library prints nothing, unless the environment variable RR_LOG is
+ *     "1" when a call is made: then every call that launches writes one line
+ *     to stderr with its dimensions, vector path and plan (tier, workgroup
+ *     size, grid, lanes per row, slices, tile columns, workspace bytes).
  */
 #ifndef RR_H
 #define RR_H

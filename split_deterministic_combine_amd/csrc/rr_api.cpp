@@ -7,6 +7,8 @@
 
 #include <atomic>
 #include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
 
 #include "../../include/rr.h"
 #include "../../include/rr_test.h"
@@ -37,6 +39,43 @@ rr_status current_cu(int32_t* cu)
     if (dev >= 0 && dev < kMaxDevices) g_cu_count[dev].store(v, std::memory_order_relaxed);
     *cu = v;
     return RR_OK;
+}
+
+// RR_LOG=1 in the environment (read at every call): every call that
+// launches prints its plan to stderr, one line.  Otherwise nothing is printed.
+bool log_enabled()
+{
+    const char* e = getenv("RR_LOG");
+    return e && e[0] == '1' && e[1] == '\0';
+}
+
+const char* tier_name(int32_t t)
+{
+    switch (t) {
+    case RR_TIER_WAVE: return "wave";
+    case RR_TIER_BLOCK: return "block";
+    case RR_TIER_TILED: return "tiled";
+    case RR_TIER_SERIAL: return "serial";
+    case RR_TIER_SPLITK: return "splitk";
+    default: return "auto";
+    }
+}
+
+// dims: "rows=R cols=C", or "outer=O axis=A inner=I" for rr_reduce_axis.
+void log_plan(const char* call, const char* d0, int64_t v0, const char* d1, int64_t v1,
+              const char* d2, int64_t v2, bool vec, const rr_plan& p)
+{
+    if (!log_enabled())
+        return;
+    char extra[48] = "";
+    if (d2)
+        snprintf(extra, sizeof extra, " %s=%lld", d2, (long long)v2);
+    fprintf(stderr,
+            "rr: %s %s=%lld %s=%lld%s vec=%d tier=%s block=%d grid=%lld lanes_per_row=%d "
+            "slices=%d tile_cols=%lld workspace=%llu\n",
+            call, d0, (long long)v0, d1, (long long)v1, extra, (int)vec, tier_name(p.tier),
+            p.block, (long long)p.grid, p.lanes_per_row, p.slices, (long long)p.tile_cols,
+            (unsigned long long)p.workspace_bytes);
 }
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
@@ -84,6 +123,7 @@ extern "C" rr_status rr_reduce_rows(const void* x, void* y, int64_t rows, int64_
         if (!workspace || workspace_bytes < p.workspace_bytes || !aligned(workspace, 8))
             return RR_ERR_WORKSPACE;
     }
+    log_plan("rr_reduce_rows", "rows", rows, "cols", cols, nullptr, 0, vec, p);
     return rr::launch_reduce(p, a);
 }
 
@@ -111,6 +151,7 @@ extern "C" rr_status rr_reduce_rows_multi(const void* x, void* y_sum, void* y_ma
         if (!workspace || workspace_bytes < p.workspace_bytes || !aligned(workspace, 8))
             return RR_ERR_WORKSPACE;
     }
+    log_plan("rr_reduce_rows_multi", "rows", rows, "cols", cols, nullptr, 0, vec, p);
     return rr::launch_reduce(p, a);
 }
 
@@ -139,6 +180,7 @@ extern "C" rr_status rr_reduce_axis(const void* x, void* y, int64_t outer, int64
     }
     rr::AxisLaunch a{x, y, outer, axis, inner, dtype, op, p.lanes_per_row == 4, workspace,
                      as_stream(stream)};
+    log_plan("rr_reduce_axis", "outer", outer, "axis", axis, "inner", inner, vec, p);
     return rr::launch_reduce_axis(p, a);
 }
 
@@ -166,6 +208,7 @@ extern "C" rr_status rr_softmax_rows(const void* x, void* y, int64_t rows, int64
     }
     rr::SoftmaxLaunch a{x, y, rows, cols, ld_x, ld_y, x_dtype, y_dtype, vec, workspace, cu,
                         as_stream(stream)};
+    log_plan("rr_softmax_rows", "rows", rows, "cols", cols, nullptr, 0, vec, p);
     return rr::launch_softmax(p, a);
 }
 
@@ -198,6 +241,7 @@ extern "C" rr_status rr_layernorm_rows(const void* x, void* y, const void* gamma
     }
     rr::LayernormLaunch a{x, y, gamma, beta, mean_out, rstd_out, rows, cols, ld_x, ld_y,
                           x_dtype, y_dtype, w_dtype, eps, vec, workspace, cu, as_stream(stream)};
+    log_plan("rr_layernorm_rows", "rows", rows, "cols", cols, nullptr, 0, vec, p);
     return rr::launch_layernorm(p, a);
 }
 
@@ -214,6 +258,9 @@ extern "C" rr_status rr_splitk_lse_merge(const float* o_part, const float* m_par
                      aligned(out, out_dtype == RR_F32 ? 16 : 8);
     rr::MergeLaunch a{o_part, m_part, l_part, out, P, rows, depth, scale, out_dtype, vec,
                       as_stream(stream)};
+    if (log_enabled())
+        fprintf(stderr, "rr: rr_splitk_lse_merge P=%d rows=%lld depth=%d vec=%d\n", P,
+                (long long)rows, depth, (int)vec);
     return rr::launch_merge(a);
 }
 

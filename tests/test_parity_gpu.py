@@ -509,3 +509,24 @@ def test_reduce_beyond_32bit_element_offsets():
             assert_exact(to_host(rr.reduce_rows(g, op, tier)), ref, "large %s %s" % (op, tier))
     del g
     torch.cuda.empty_cache()
+
+
+@pytest.mark.gpu
+def test_rr_log_prints_plan(capfd, monkeypatch):
+    """RR_LOG=1: each launching call writes its plan to stderr; unset, nothing."""
+    x = torch.randn(64, 1024, device="cuda")
+    monkeypatch.delenv("RR_LOG", raising=False)
+    rr.reduce_rows(x, "sum")
+    torch.cuda.synchronize()
+    assert "rr:" not in capfd.readouterr().err
+    monkeypatch.setenv("RR_LOG", "1")
+    rr.reduce_rows(x, "sum")
+    rr.softmax_rows(x.bfloat16())
+    rr.reduce_axis(x.view(64, 8, 128), 1, "max")
+    torch.cuda.synchronize()
+    err = capfd.readouterr().err
+    plan = rr.plan_reduce(64, 1024, torch.float32, "sum", cu_count=rr.device_cu_count())
+    assert ("rr: rr_reduce_rows rows=64 cols=1024 vec=1 tier=block block=%d grid=%d"
+            % (plan["block"], plan["grid"])) in err, err
+    assert "rr: rr_softmax_rows rows=64 cols=1024" in err, err
+    assert "rr: rr_reduce_axis outer=64 axis=8 inner=128" in err, err
