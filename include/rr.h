@@ -136,16 +136,18 @@ rr_status rr_plan_reduce(int64_t rows, int64_t cols, int64_t ld, rr_dtype dtype,
                          rr_tier tier, int32_t cu_count, rr_plan* plan_out);
 
 /*
- * rr_plan_softmax -- tier selection for rr_softmax_rows: the reduce rule
- * (SPLITK when rows < cu_count and cols >= 65536, then TILED / WAVE /
- * BLOCK).  BLOCK: rows of whole 16-byte chunks (c chunks, c <= 2048, aligned)
+ * rr_plan_softmax -- tier selection for rr_softmax_rows: SPLITK when
+ * rows < cu_count and cols >= 65536, or when a row spans more than 2048
+ * 16-byte chunks (cols > 16384 for bf16 input, > 8192 for float32) at any
+ * row count -- too long to stay in registers; else TILED (cols <= 8), WAVE
+ * (cols <= 64), BLOCK.  BLOCK: rows of whole 16-byte chunks (c chunks, c <= 2048, aligned)
  * run persistent workgroups sized to the row -- (threads, chunks per thread)
  * = (64, 1) for c <= 64, (64, 2) <= 128, (64, 4) <= 256, (128, 4) <= 512,
  * (256, 4) <= 1024, (512, 4) <= 2048 -- with 32 / (wavefronts x chunks per
  * thread) workgroups per CU (at least 1), lowered at launch to what the
  * kernel's occupancy allows; other rows take one workgroup of 256 threads
- * per row (512 beyond 2048 chunks), reading x twice beyond 8 chunks per
- * thread.  SPLITK uses tiles of 4 * 256 * 16-byte chunks (4 * 256 elements
+ * per row (512 beyond 2048 chunks, reached when BLOCK is forced), reading x
+ * twice beyond 8 chunks per thread.  SPLITK uses tiles of 4 * 256 * 16-byte chunks (4 * 256 elements
  * on the scalar path), G as for rr_plan_reduce with that tile but
  * 4 * cu_count workgroups in all, and needs the workspace reported in
  * workspace_bytes (rows * G * 8).
@@ -328,7 +330,8 @@ rr_status rr_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols, in
  * x - x[r][0] and its square, whose cancellation Samuelson's inequality
  * bounds by log2(cols) bits), each combined over a fixed-shape tree so the
  * result does not change from run to run.  The map runs in float; bf16
- * results are rounded to nearest even.  Split-K (rows < CU and long rows):
+ * results are rounded to nearest even.  Split-K (rows < CU and long rows, or
+ * rows too long for registers):
  * G workgroups per row store their two sums, then every workgroup of the map
  * pass sums its row's G pairs over a fixed tree ("cluster_allreduce",
  * description: the all-gather variant) and maps its tiles.  rows == 0 or

@@ -189,14 +189,25 @@ def test_softmax_tier_rule():
     assert rr.plan_softmax(64, 16384)["block"] == 512        # 2048 chunks: 512 threads x 4
     assert rr.plan_softmax(65536, 1024)["block"] == 64       # 128 chunks: one wavefront x 2
     assert rr.plan_softmax(65536, 1024)["grid"] == 256 * 16  # 32 loads per lane per CU
-    assert rr.plan_softmax(64, 16385)["block"] == 512        # ragged, long: wider workgroups
+    assert rr.plan_softmax(64, 16385, tier="block")["block"] == 512  # ragged, long: wider
     assert rr.plan_softmax(64, 8201)["block"] == 256         # ragged: one row per workgroup
     assert rr.plan_softmax(64, 8200)["block"] == 512         # 1025 whole chunks: persistent
     assert rr.plan_softmax(100, 40)["tier"] == "wave"
     assert rr.plan_softmax(100, 4)["tier"] == "tiled"
     assert rr.plan_softmax(16, 1 << 20)["tier"] == "splitk"    # rows < CU and long rows
-    assert rr.plan_softmax(256, 1 << 20)["tier"] == "block"
-    assert rr.plan_softmax(16, 65535)["tier"] == "block"
+    assert rr.plan_softmax(16, 16384)["tier"] == "block"       # 2048 chunks stay in registers
+    # rows too long for registers (more than 2048 16-byte chunks) go split-K at
+    # any row count
+    assert rr.plan_softmax(64, 16385)["tier"] == "splitk"
+    assert rr.plan_softmax(256, 1 << 20)["tier"] == "splitk"
+    assert rr.plan_softmax(8192, 16392)["tier"] == "splitk"
+    assert rr.plan_softmax(8192, 8193, x_dtype=torch.float32)["tier"] == "splitk"
+    assert rr.plan_softmax(8192, 8192, x_dtype=torch.float32)["tier"] == "block"
+    assert rr.plan_softmax(16, 65535)["tier"] == "splitk"
+    assert rr.plan_layernorm(4096, 32768)["tier"] == "splitk"
+    assert rr.plan_layernorm(4096, 16384)["tier"] == "block"
+    p = rr.plan_softmax(4096, 32768, cu_count=256)           # G = 1: a workgroup per row
+    assert p["slices"] == 1 and p["grid"] == 4096
 
 
 def test_softmax_splitk_geometry():
