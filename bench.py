@@ -500,15 +500,18 @@ def main():
             next_rows[n] = {"ms_mean": round(mean, 5), "ms_median": round(ts[len(ts) // 2], 5),
                             "ms_min": round(ts[0], 5), "bytes": NEXT_BYTES[n],
                             "GBps": round(gbs, 1), "pct_peak": round(100 * gbs / PEAK_HBM_GBS, 1)}
+        cu = rr.device_cu_count()
         if "axis_cols" in next_rows:
+            pa = rr.plan_axis(1, 16384, 16384, torch.float32, "sum", cu_count=cu)
             next_rows["axis_cols"].update({
                 "config": "f32 column sums of [16384, 16384] (reduce over a non-last axis), "
-                          "split-K: 64 slices, tiles of 256 output groups",
+                          "split-K: %d slices, %d workgroups" % (pa["slices"], pa["grid"]),
                 "kernels": [KERNEL_OF_OP["axis_cols_partial"], KERNEL_OF_OP["axis_cols_fold"]]})
         if "multi_long" in next_rows:
+            pm = rr.plan_reduce(16, 1 << 24, torch.float32, "sum_max_min", cu_count=cu)
             next_rows["multi_long"].update({
                 "config": "f32 sum, max and min over [16, 16777216] from one read, split-K "
-                          "(G = 32, 16-byte partials)",
+                          "(G = %d, 16-byte partials)" % pm["slices"],
                 "kernels": [KERNEL_OF_OP["multi_long"]]})
         if "layernorm" in next_rows:
             next_rows["layernorm"].update({

@@ -227,9 +227,9 @@ rr_status rr_reduce_rows_multi(const void* x, void* y_sum, void* y_max, void* y_
  * output groups (outer * inner / 4 when inner % 4 == 0, else outer * inner),
  * per outer index gpo = g / outer and B = ceil(g / 256): AUTO picks SPLITK
  * when axis >= 512 and (B < cu_count or gpo < 64), else TILED.  SPLITK
- * workgroups are tiles of GW = min(256, gpo rounded up to a power of two)
+ * workgroups are tiles of GW = min(64, gpo rounded up to a power of two)
  * output groups by AL = 256 / GW axis lanes; with T tiles, G =
- * clamp(ceil(4 * cu_count / T), 1, min(1024, ceil(axis / (32 * AL)))) slices
+ * clamp(ceil(2 * cu_count / T), 1, min(1024, ceil(axis / (32 * AL)))) slices
  * of ceil(axis / G) steps (tile_cols); workspace G * outer * inner * 8
  * bytes.  lanes_per_row holds the outputs per thread (4 or 1).  The planner
  * assumes 16-byte aligned pointers.

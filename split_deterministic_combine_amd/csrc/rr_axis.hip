@@ -105,7 +105,7 @@ __device__ __forceinline__ void fold_axis_lanes(const typename M::in_t* p, int64
                                                 typename M::acc_t* acc)
 {
     using T = typename M::in_t;
-    constexpr int U = kAxisUnroll;
+    constexpr int U = kAxisSplitKUnroll;
     int64_t a = start;
     for (; a + (U - 1) * AL < a1; a += U * AL) {
         Vec<T, VEC> v[U];

@@ -48,10 +48,16 @@ constexpr int64_t kSoftmaxWideMinChunks = (int64_t)kBlockThreads * kSoftmaxMaxCh
 // round of the workgroup).
 constexpr int kSoftmaxSplitKUnroll = 4;
 // Reduction over a non-last axis: 16-byte loads in flight per thread (one
-// per axis step), split-K when there are fewer than kAxisSplitKMaxBlocksPerCU
-// workgroups of outputs per CU and the axis has at least kAxisSplitKMinAxis
-// steps, with slices of at least kAxisMinSlice steps.
+// per axis step; kAxisSplitKUnroll in the split-K partial pass), split-K when
+// there are fewer than kAxisSplitKMaxBlocksPerCU workgroups of outputs per CU
+// and the axis has at least kAxisSplitKMinAxis steps, with slices of at least
+// kAxisMinStepsPerLane steps per axis lane.  The split-K pass aims at
+// kAxisSplitKBlocksPerCU workgroups per CU (swept on [16384, 16384],
+// [4096, 65536] and [65536, 1024] f32: 2 beat 3, 4 and 8; unroll 4 beat 8
+// and 16; tiles of 64 groups beat 32, 128 and 256).
 constexpr int kAxisUnroll = 8;
+constexpr int kAxisSplitKUnroll = 4;
+constexpr int kAxisSplitKBlocksPerCU = 2;
 constexpr int kAxisSplitKMaxBlocksPerCU = 1;
 constexpr int64_t kAxisSplitKMinAxis = 512;
 constexpr int64_t kAxisNarrowGroups = 64;   // fewer output groups per outer: split-K tiles
@@ -70,11 +76,11 @@ constexpr int axis_fold_lanes_log2(int64_t slices)
 
 // Split-K axis tile: log2 of the output groups per workgroup (the rest of the
 // 256 threads are axis lanes): the groups of one outer index rounded up to a
-// power of two, at most 256.
+// power of two, at most 64 (so at least 4 axis lanes).
 constexpr int axis_tile_log2(int64_t groups_per_outer)
 {
     int l = 0;
-    while (l < 8 && ((int64_t)1 << l) < groups_per_outer)
+    while (l < 6 && ((int64_t)1 << l) < groups_per_outer)
         ++l;
     return l;
 }

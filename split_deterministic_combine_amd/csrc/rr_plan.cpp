@@ -248,7 +248,7 @@ rr_status plan_axis(int64_t outer, int64_t axis, int64_t inner, rr_dtype dtype, 
         const int gwl = axis_tile_log2(gpo);
         const int64_t lanes = kBlockThreads >> gwl;
         const int64_t tiles = outer * ceil_div(gpo, (int64_t)1 << gwl);
-        int64_t g = ceil_div((int64_t)kSplitKHeavyBlocksPerCU * cu_count, tiles > 0 ? tiles : 1);
+        int64_t g = ceil_div((int64_t)kAxisSplitKBlocksPerCU * cu_count, tiles > 0 ? tiles : 1);
         int64_t cap = ceil_div(axis, lanes * kAxisMinStepsPerLane);
         if (cap > kAxisMaxSlices) cap = kAxisMaxSlices;
         if (g > cap) g = cap;

@@ -54,7 +54,7 @@ def test_plain_c_consumer_compiles_links_and_runs(tmp_path):
     assert "reduce tier=5 slices=32 grid=512 ws=4352" in out
     assert "softmax tier=2 block=256 grid=512" in out
     assert "layernorm tier=2 block=128 grid=1024" in out
-    assert "axis tier=5 slices=16" in out
+    assert "axis tier=5 slices=2" in out
     assert "bad ld -> 2 (invalid shape" in out
     assert "empty softmax -> 0" in out and "P=0 merge -> 2" in out
 
@@ -133,16 +133,17 @@ def test_axis_plan():
     assert p["tier"] == "tiled" and p["lanes_per_row"] == 4 and p["grid"] == (1 << 20) // 4 // 256
     # few outputs, long axis: split-K over the axis
     p = rr.plan_axis(1, 1 << 20, 64, cu_count=256)
-    # 16 output groups: one tile of 16 groups x 16 axis lanes, 1024 slices
-    assert p["tier"] == "splitk" and p["slices"] == 1024 and p["grid"] == 1024
-    assert p["workspace_bytes"] == 1024 * 64 * 8 and p["tile_cols"] == 1024
+    # 16 output groups: one tile of 16 groups x 16 axis lanes; 2 workgroups
+    # per CU, so 512 slices
+    assert p["tier"] == "splitk" and p["slices"] == 512 and p["grid"] == 512
+    assert p["workspace_bytes"] == 512 * 64 * 8 and p["tile_cols"] == 2048
     p = rr.plan_axis(1, 1000, 64, cu_count=256)
     # 16 groups: tiles of 16 groups x 16 axis lanes; slices of >= 32 steps per lane
     assert p["tier"] == "splitk" and p["slices"] == 2 and p["grid"] == 2
     p = rr.plan_axis(1024, 4096, 16, cu_count=256)                      # narrow inner
     assert p["tier"] == "splitk" and p["slices"] == 1 and p["grid"] == 1024
-    p = rr.plan_axis(1, 1 << 16, 1024, cu_count=256)                    # one full tile
-    assert p["slices"] == 1024 and p["grid"] == 1024
+    p = rr.plan_axis(1, 1 << 16, 1024, cu_count=256)    # 256 groups: 4 tiles of 64 x 4 lanes
+    assert p["slices"] == 128 and p["grid"] == 512
     assert rr.plan_axis(1, 100, 64)["tier"] == "tiled"                 # axis too short
     assert rr.plan_axis(3, 100, 7)["lanes_per_row"] == 1               # inner % 4 != 0
     assert rr.plan_axis(3, 100, 8, tier="serial")["lanes_per_row"] == 1
