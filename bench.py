@@ -68,28 +68,45 @@ KERNEL_OF_OP = {
 }
 LAYERNORM = (16384, 4096)
 SOFTMAX_LONG = (16, 1 << 22)
-ALGO_BYTES = {
-    "short_sum": 1048576 * 48 * 4 + 1048576 * 4,
-    "short_max": 1048576 * 48 * 4 + 1048576 * 4,
-    "softmax": 8192 * 8192 * 2 * 2,
-    "long_sum": 16 * (1 << 24) * 4 + 16 * 4,
-    "long_max": 16 * (1 << 24) * 4 + 16 * 4,
-    "merge": 8 * 32768 * 128 * 4 + 2 * 8 * 32768 * 4 + 32768 * 128 * 2,
-    # split-K softmax, per kernel: the statistics pass reads x and stores
-    # 16 x 64 (max, sum) pairs; the map pass reads the pairs and x, writes y
-    "softmax_long_stats": 16 * (1 << 22) * 2 + 16 * 64 * 8,
-    "softmax_long_map": 16 * (1 << 22) * 2 * 2 + 16 * 64 * 64 * 8,
-    # x read and y written once (bf16), gamma/beta read once, mean/rstd written
-    "layernorm": 16384 * 4096 * 2 * 2 + 2 * 4096 * 4 + 2 * 16384 * 4,
-    "multi_long": 16 * (1 << 24) * 4 + 3 * 16 * 4,
-    # column sums of [16384, 16384]: the partial pass reads x, writes G = 64
-    # partials per column; the fold pass reads them and writes y
-    "axis_cols_partial": 16384 * 16384 * 4 + 64 * 16384 * 8,
-    "axis_cols_fold": 64 * 16384 * 8 + 16384 * 4,
-}
+AXIS_COLS = (16384, 16384)
+CU_MI355X = 256
+
+
+def _algo_bytes():
+    """Algorithmic bytes per launch of each timed kernel.  The split-K
+    workspace terms depend on the slice count G, taken from the library's
+    host planner for a 256-CU MI355X (the same plan the launches use)."""
+    import split_deterministic_combine_amd as rr_host
+
+    g_sm = rr_host.plan_softmax(*SOFTMAX_LONG, cu_count=CU_MI355X)["slices"]
+    g_ax = rr_host.plan_axis(1, AXIS_COLS[0], AXIS_COLS[1], cu_count=CU_MI355X)["slices"]
+    sr, sc = SOFTMAX_LONG
+    ar, ac = AXIS_COLS
+    return {
+        "short_sum": 1048576 * 48 * 4 + 1048576 * 4,
+        "short_max": 1048576 * 48 * 4 + 1048576 * 4,
+        "softmax": 8192 * 8192 * 2 * 2,
+        "long_sum": 16 * (1 << 24) * 4 + 16 * 4,
+        "long_max": 16 * (1 << 24) * 4 + 16 * 4,
+        "merge": 8 * 32768 * 128 * 4 + 2 * 8 * 32768 * 4 + 32768 * 128 * 2,
+        # split-K softmax, per kernel: the statistics pass reads x and stores
+        # rows x G (max, sum) pairs; the map pass reads x and, in each of the
+        # G workgroups of a row, the row's G pairs, and writes y
+        "softmax_long_stats": sr * sc * 2 + sr * g_sm * 8,
+        "softmax_long_map": sr * sc * 2 * 2 + sr * g_sm * g_sm * 8,
+        # x read and y written once (bf16), gamma/beta read once, mean/rstd written
+        "layernorm": 16384 * 4096 * 2 * 2 + 2 * 4096 * 4 + 2 * 16384 * 4,
+        "multi_long": 16 * (1 << 24) * 4 + 3 * 16 * 4,
+        # column sums: the partial pass reads x and writes G partials (8 B)
+        # per column; the fold pass reads them and writes y
+        "axis_cols_partial": ar * ac * 4 + g_ax * ac * 8,
+        "axis_cols_fold": g_ax * ac * 8 + ac * 4,
+    }
+
+
 # next-row operations as a whole: x read once and y written once
 NEXT_BYTES = {"multi_long": 16 * (1 << 24) * 4 + 3 * 16 * 4,
-              "axis_cols": 16384 * 16384 * 4 + 16384 * 4,
+              "axis_cols": AXIS_COLS[0] * AXIS_COLS[1] * 4 + AXIS_COLS[1] * 4,
               "softmax_long": 16 * (1 << 22) * 2 * 2,
               "layernorm": 16384 * 4096 * 2 * 2 + 2 * 4096 * 4 + 2 * 16384 * 4}
 STEP_OPS = ("short_sum", "short_max", "softmax", "long_sum", "long_max", "merge")
@@ -109,6 +126,7 @@ def _csv_rows(directory, suffix):
 
 def ingest_counters(trace_dir, fetch_dir, write_dir):
     """Turn rocprofv3 CSVs into profiles/traffic.json and markdown summaries."""
+    ALGO_BYTES = _algo_bytes()
     stats = _csv_rows(trace_dir, "kernel_stats.csv")
     per_counter = {}
     for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
@@ -306,7 +324,7 @@ def main():
     torch.cuda.synchronize()
 
     # algorithmic bytes per launch (inputs read once, outputs written once)
-    B = dict(ALGO_BYTES)
+    B = _algo_bytes()
     ops = {
         "short_sum": lambda i: rr.reduce_rows(dx["short"][i % 5], "sum", out=y_short_sum),
         "short_max": lambda i: rr.reduce_rows(dx["short"][i % 5], "max", out=y_short_max),
@@ -521,11 +539,12 @@ def main():
         if "softmax_long" in next_rows:
             r, c = SOFTMAX_LONG
             next_rows["softmax_long"].update({
-                "config": "bf16 softmax [%d, %d] -> bf16, split-K tier (G = 64)" % (r, c),
+                "config": "bf16 softmax [%d, %d] -> bf16, split-K tier (G = %d)" % (
+                    r, c, rr.plan_softmax(r, c, cu_count=cu)["slices"]),
                 "kernels": [KERNEL_OF_OP["softmax_long_stats"], KERNEL_OF_OP["softmax_long_map"]],
                 "bytes_note": "bytes = x read once + y written once; the two-launch design reads "
-                              "x twice (%d bytes moved)" % (ALGO_BYTES["softmax_long_stats"]
-                                                            + ALGO_BYTES["softmax_long_map"])})
+                              "x twice (%d bytes moved)" % (B["softmax_long_stats"]
+                                                            + B["softmax_long_map"])})
 
     step_bytes = sum(B[n] for n in names)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9

@@ -286,6 +286,22 @@ def test_softmax_persistent_rows_walk_several_rows(rows, cols):
     assert float((s - 1).abs().max()) <= 2.0 ** -8
 
 
+def test_softmax_rows_config_full_size():
+    # bf16 [8192, 8192], logits normal(0, 3): every row against the oracle,
+    # in the launch the planner picks for this shape, then ten runs bit-identical.
+    x = synth.softmax_rows()
+    rows, cols = x.shape
+    plan = rr.plan_softmax(rows, cols, cu_count=rr.device_cu_count())
+    assert plan["tier"] == "block"
+    g = to_gpu(x)
+    y = rr.softmax_rows(g)
+    torch.cuda.synchronize()
+    assert_bf16_within_1ulp(to_host(y), oracle.softmax_rows(x, "bf16"), "softmax config")
+    first = y.clone()
+    for _ in range(9):
+        assert torch.equal(rr.softmax_rows(g).view(torch.int16), first.view(torch.int16))
+
+
 def test_softmax_uniform_row_is_exactly_2_pow_minus_13():
     x = torch.full((4, 8192), 3.0, dtype=torch.bfloat16, device="cuda")
     y = to_host(rr.softmax_rows(x))
