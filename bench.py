@@ -65,6 +65,9 @@ KERNEL_OF_OP = {
     "multi_long": "k_reduce_splitk<rr::MultiF32, 4>",
     "axis_cols_partial": "k_reduce_axis_partial<rr::SumF32, 4>",
     "axis_cols_fold": "k_reduce_axis_fold<rr::SumF32>",
+    # reference streams of known size (not ops of the step): rr_test_stream
+    "stream_read": "k_stream<0>",
+    "stream_write": "k_stream<1>",
 }
 LAYERNORM = (16384, 4096)
 SOFTMAX_LONG = (16, 1 << 22)
@@ -101,6 +104,8 @@ def _algo_bytes():
         # per column; the fold pass reads them and writes y
         "axis_cols_partial": ar * ac * 4 + g_ax * ac * 8,
         "axis_cols_fold": g_ax * ac * 8 + ac * 4,
+        "stream_read": 1 << 30,
+        "stream_write": 1 << 30,
     }
 
 
@@ -225,6 +230,8 @@ def parse():
     ap.add_argument("--no-next", action="store_true",
                     help="skip the operations outside the step (next_rows)")
     ap.add_argument("--only", default=None, help="comma list of ops to run (profiling)")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the reference streams (plain read / write / copy of known size)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 512 MiB elementwise copy (negation) three times: "
                          "the known-size reference for scaling FETCH_SIZE / WRITE_SIZE")
@@ -452,12 +459,15 @@ def main():
         torch.cuda.synchronize()
         return {n: [a.elapsed_time(b) for a, b in evs[n]] for n in names}
 
-    # Warmup with every launch instrumented: it also picks the dominant op.
+    # Warmup with every launch instrumented.  The dominant op is the one that
+    # moves the most algorithmic bytes (every op is HBM-bound, so it is also
+    # the longest); the first in step order on a tie (the f32 and i32 long-row
+    # reductions move the same bytes), so the choice does not flip between runs.
     log("warmup %d steps" % args.warmup)
     if not names:
         sys.exit("bench.py: --only selected no operation of the step")
-    warm = instrumented(max(args.warmup, 1), 0)
-    dom = max(names, key=lambda n: sum(warm[n]) / len(warm[n]))
+    instrumented(max(args.warmup, 1), 0)
+    dom = max(names, key=lambda n: (B[n], -names.index(n)))
 
     # Timed region: exactly K steps; HIP events only around the dominant op
     # (an event pair costs a few microseconds of GPU time, so instrumenting
@@ -546,6 +556,45 @@ def main():
                               "x twice (%d bytes moved)" % (B["softmax_long_stats"]
                                                             + B["softmax_long_map"])})
 
+    # ------------------------------------------- achievable-bandwidth reference
+    # Plain 128-bit non-temporal streams with no arithmetic (rr_test_stream):
+    # what HBM delivers to a kernel that does nothing but move bytes, beside
+    # the published 8 TB/s.  Read: the two 1 GiB long-row inputs alternated;
+    # copy: softmax-shaped 128 MiB -> 128 MiB over the four softmax buffer sets,
+    # and 512 MiB -> 512 MiB; write: 1 GiB.
+    ceilings = None
+    if not args.no_ceilings:
+        log("timing the reference streams")
+        big = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        src_big = dx["long_f"][0].view(-1).view(torch.uint8)
+        runs = {
+            "read_1GiB": (1 << 30, lambda i: rr._test_stream(
+                "read", (dx["long_f"][0] if i % 2 == 0 else dx["long_i"][0]))),
+            "write_1GiB": (1 << 30, lambda i: rr._test_stream("write", None, big)),
+            "copy_512MiB_each_way": (1 << 30, lambda i: rr._test_stream(
+                "copy", src_big[:1 << 29], big[(i % 2) << 29:((i % 2) + 1) << 29])),
+            "copy_128MiB_each_way": (1 << 28, lambda i: rr._test_stream(
+                "copy", dx["softmax"][i % 4], dx["softmax_out"][i % 4])),
+        }
+        ceilings = {}
+        for name, (nbytes, fn) in runs.items():
+            evs = []
+            for i in range(23):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                fn(i)
+                b.record(stream)
+                if i >= 3:
+                    evs.append((a, b))
+            torch.cuda.synchronize()
+            ts = sorted(a.elapsed_time(b) for a, b in evs)
+            med = ts[len(ts) // 2]
+            gbs = nbytes / (med * 1e-3) / 1e9
+            ceilings[name] = {"ms_median": round(med, 5), "bytes": nbytes, "GBps": round(gbs, 1),
+                              "pct_peak": round(100 * gbs / PEAK_HBM_GBS, 1)}
+        del big
+        torch.cuda.empty_cache()
+
     step_bytes = sum(B[n] for n in names)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
@@ -562,6 +611,12 @@ def main():
                 "achieved": achieved, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                 "algorithmic_bytes": B[dom]}
+    if ceilings:
+        # the reference stream with the dominant kernel's mix of reads and writes
+        ref = "copy_128MiB_each_way" if dom == "softmax" else "read_1GiB"
+        roofline["reference_stream"] = ref
+        roofline["reference_GBps"] = ceilings[ref]["GBps"]
+        roofline["frac_of_reference"] = round(achieved / ceilings[ref]["GBps"], 4)
 
     # ------------------------------------------------------------ CPU baseline
     cpu = None
@@ -654,6 +709,7 @@ def main():
         "per_op": per_op,
         "next_rows": next_rows,
         "roofline": roofline,
+        "reference_streams": ceilings,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

@@ -106,8 +106,10 @@ typedef struct {
     int64_t grid;            /* workgroups launched */
     int32_t lanes_per_row;   /* wave tier: lanes that share one row; else 0 */
     int32_t slices;          /* split-K: workgroups per row (G); else 1 */
-    int64_t tile_cols;       /* split-K: columns per tile; workgroup g of a row folds
-                                tiles g, g+G, g+2G, ... (the last tile may be shorter);
+    int64_t tile_cols;       /* split-K: columns per tile (the last tile of a row may be
+                                shorter); of a row's T tiles, workgroup g folds the
+                                contiguous run [g*T/G, (g+1)*T/G) in the row reduction,
+                                and tiles g, g+G, g+2G, ... in softmax and layernorm;
                                 else 0 */
     uint64_t workspace_bytes;/* bytes of workspace the call needs (0 if none) */
 } rr_plan;

@@ -4,7 +4,10 @@
 #ifndef RR_TEST_H
 #define RR_TEST_H
 
+#include <stddef.h>
 #include <stdint.h>
+
+#include "rr.h"
 
 #ifdef __cplusplus
 extern "C" {
@@ -20,6 +23,25 @@ extern "C" {
  * values count as 0.  Process-wide; affects launches made after the call.
  */
 void rr_test_set_splitk_skew(int32_t sleeps_per_rank);
+
+/*
+ * Reference streams of known size, the achievable HBM bandwidth against which
+ * the row kernels' rooflines are read (the published peak is not reachable):
+ *   RR_TEST_STREAM_READ   reads `bytes` of x (y is not used and may be NULL);
+ *   RR_TEST_STREAM_WRITE  writes `bytes` of y with a fixed pattern (x may be NULL);
+ *   RR_TEST_STREAM_COPY   copies `bytes` from x to y (the ranges must not overlap).
+ * Device pointers, 16-byte aligned; `bytes` a multiple of 16.  128-bit
+ * non-temporal loads and stores, no arithmetic on the data; each workgroup
+ * streams one contiguous run.  blocks_per_cu workgroups of 256 threads per
+ * compute unit (1..16; 0 picks 2).  Asynchronous on `stream` (a hipStream_t,
+ * NULL for the default stream); nothing is allocated.
+ * Errors (nothing launched): RR_ERR_SHAPE for an unknown mode, misaligned
+ * pointers or size, or blocks_per_cu out of range; RR_ERR_NULL for a missing
+ * pointer the mode uses; RR_ERR_HIP if the launch fails.
+ */
+enum { RR_TEST_STREAM_READ = 0, RR_TEST_STREAM_WRITE = 1, RR_TEST_STREAM_COPY = 2 };
+rr_status rr_test_stream(int32_t mode, const void* x, void* y, size_t bytes,
+                         int32_t blocks_per_cu, void* stream);
 
 #ifdef __cplusplus
 }

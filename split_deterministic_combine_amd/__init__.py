@@ -98,11 +98,12 @@ def _load():
         lib.rr_version.restype = ctypes.c_int
         lib.rr_test_set_splitk_skew.argtypes = [i32]
         lib.rr_test_set_splitk_skew.restype = None
+        lib.rr_test_stream.argtypes = [i32, vp, vp, ctypes.c_size_t, i32, vp]
         for name in ("rr_reduce_rows", "rr_reduce_rows_multi", "rr_reduce_axis", "rr_plan_axis",
                      "rr_softmax_rows", "rr_splitk_lse_merge", "rr_plan_reduce",
                      "rr_plan_softmax", "rr_layernorm_rows", "rr_plan_layernorm",
                      "rr_workspace_bytes", "rr_select_tier",
-                     "rr_workspace_reset", "rr_device_cu_count"):
+                     "rr_workspace_reset", "rr_device_cu_count", "rr_test_stream"):
             getattr(lib, name).restype = st
         _lib = lib
     return _lib
@@ -531,3 +532,24 @@ def device_cu_count():
 def _set_splitk_skew(sleeps_per_rank):
     """Test hook: arrival-order skew for the split-K tier (0 turns it off)."""
     _load().rr_test_set_splitk_skew(int(sleeps_per_rank))
+
+
+_STREAM_MODES = {"read": 0, "write": 1, "copy": 2}
+
+
+def _test_stream(mode, x=None, y=None, blocks_per_cu=0):
+    """Test hook: a reference stream of known size ("read" x, "write" y, or
+    "copy" x to y), the achievable-bandwidth reference for the rooflines.
+    Asynchronous on the current stream."""
+    t = x if x is not None else y
+    if t is None or not t.is_cuda:
+        raise RuntimeError("rr._test_stream needs CUDA tensors")
+    for a in (x, y):
+        if a is not None and not a.is_contiguous():
+            raise RuntimeError("rr._test_stream needs contiguous tensors")
+    nbytes = (x if mode != "write" else y).numel() * (x if mode != "write" else y).element_size()
+    if mode == "copy" and y.numel() * y.element_size() < nbytes:
+        raise RuntimeError("rr._test_stream: y is smaller than x")
+    _check(_load().rr_test_stream(_STREAM_MODES[mode], None if x is None else x.data_ptr(),
+                                  None if y is None else y.data_ptr(), nbytes, int(blocks_per_cu),
+                                  _stream_ptr(t.device)))

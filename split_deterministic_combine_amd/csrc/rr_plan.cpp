@@ -24,9 +24,10 @@ uint64_t softmax_splitk_workspace_bytes(int64_t rows, int32_t slices)
     return (uint64_t)(rows * (int64_t)slices * 8);
 }
 
-// Split-K geometry shared by the reduce and softmax tiers: G workgroups per
-// row; the row is cut into tiles of one load round of a workgroup, dealt to
-// the G workgroups in turn.
+// Split-K geometry shared by the reduce, softmax and layernorm tiers: G
+// workgroups per row; the row is cut into tiles of one load round of a
+// workgroup (the kernels give each workgroup its own tiles: a contiguous run
+// in the row reduction, every G-th tile in softmax and layernorm).
 static void fill_splitk_geometry(int64_t rows, int64_t cols, int64_t tile, int32_t cu_count,
                                  int blocks_per_cu, rr_plan* out)
 {

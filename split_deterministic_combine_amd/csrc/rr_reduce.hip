@@ -240,9 +240,12 @@ __device__ __forceinline__ typename M::acc_t fold_tile(typename M::acc_t acc,
 
 // ----------------------------------------------------------- split-K tier
 // A row is cut into tiles of kSplitKUnroll * kBlockThreads * VEC columns
-// (one unrolled load round of the workgroup); workgroup (r, g) folds tiles
-// g, g + G, g + 2G, ... of row r, so at any moment the G workgroups of a row
-// stream adjacent memory.  It then publishes its partial to part[r * G + g]
+// (one unrolled load round of the workgroup); workgroup (r, g) folds the
+// contiguous run of tiles [g * T / G, (g + 1) * T / G) of row r (T tiles in
+// the row, the ragged last one included), in ascending order.  One long
+// sequential stream per workgroup reads faster on MI355X than tiles dealt
+// round-robin (measured on a 1 GiB read at 2 workgroups per CU: 88% against
+// 84% of peak).  It then publishes its partial to part[r * G + g]
 // and takes a ticket on row r.  The workgroup that draws ticket G - 1 is the
 // last to arrive: it folds part[r * G + 0 .. G - 1] in ascending g, writes
 // y[r] and resets the ticket and the row's partial slots to zero for the
@@ -274,18 +277,20 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce_splitk(
         // one tile, then folds them.  Tile indices are uniform across the
         // workgroup, so the loop branch is scalar.
         const int64_t nfull = cols / kTile;
-        int64_t t = g;
+        const int64_t t_end = (int64_t)(g + 1) * ntiles / G;
+        const int64_t t_full = t_end < nfull ? t_end : nfull;
+        int64_t t = (int64_t)g * ntiles / G;
         {
             using T = typename M::in_t;
             const T* p = row + (int64_t)threadIdx.x * VEC;
-            for (; t < nfull; t += G) {
+            for (; t < t_full; ++t) {
                 Vec<T, VEC> v[kSplitKUnroll];
                 load_tile<VEC, kBlockThreads, kSplitKUnroll>(p + t * kTile, v);
                 acc = fold_tile<M, VEC, kSplitKUnroll>(acc, v);
             }
         }
         // The partial last tile, if this workgroup owns it.
-        for (; t < ntiles; t += G) {
+        for (; t < t_end; ++t) {
             const int64_t begin = t * kTile;
             const int64_t end = begin + kTile < cols ? begin + kTile : cols;
             acc = thread_fold<M, VEC, kBlockThreads, kSplitKUnroll>(row, begin, end, threadIdx.x, acc);

@@ -98,7 +98,7 @@ def test_splitk_every_workgroup_gets_a_tile(rows, cols):
     p = rr.plan_reduce(rows, cols, tier="splitk", cu_count=256)
     g, t = p["slices"], p["tile_cols"]
     assert 1 <= g <= 256 and t % 4 == 0
-    assert g <= -(-cols // t)          # tiles g, g+G, ... : workgroup G-1 has tile G-1
+    assert g <= -(-cols // t)          # T >= G tiles: every run [g*T/G, (g+1)*T/G) is non-empty
     assert p["grid"] == rows * g
 
 
@@ -327,6 +327,20 @@ def test_entry_points_validate_before_touching_the_device():
     assert lib.rr_splitk_lse_merge(None, None, None, None, 8, 4, 8, 1.0, 1, None) == 3
     assert lib.rr_splitk_lse_merge(None, None, None, None, 8, 0, 8, 1.0, 2, None) == 0
     assert lib.rr_splitk_lse_merge(None, None, None, None, 8, 4, 8, 1.0, 2, None) == 1
+
+
+def test_stream_reference_validates_before_touching_the_device():
+    lib = ctypes.CDLL(rr.lib_path())
+    vp = ctypes.c_void_p
+    lib.rr_test_stream.argtypes = [ctypes.c_int32, vp, vp, ctypes.c_size_t, ctypes.c_int32, vp]
+    assert lib.rr_test_stream(3, 16, 16, 64, 0, None) == 2      # unknown mode
+    assert lib.rr_test_stream(0, None, None, 64, 0, None) == 1  # read without x
+    assert lib.rr_test_stream(1, None, None, 64, 0, None) == 1  # write without y
+    assert lib.rr_test_stream(2, 16, None, 64, 0, None) == 1    # copy without y
+    assert lib.rr_test_stream(2, 16, 32, 40, 0, None) == 2      # size not a multiple of 16
+    assert lib.rr_test_stream(2, 8, 32, 64, 0, None) == 2       # misaligned x
+    assert lib.rr_test_stream(0, 16, None, 64, 17, None) == 2   # blocks per CU out of range
+    assert lib.rr_test_stream(2, 16, 32, 0, 0, None) == 0       # nothing to move
 
 
 def test_product_path_has_no_cpu_fallback():
