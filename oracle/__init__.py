@@ -12,7 +12,9 @@ Sources: the Modular API pages "cluster_allreduce" (associative add/max/min
 over 32-bit values, folded in ascending rank order), "reduce" from
 algorithm.gpu.rowwise (the monoid fold along the last axis and the two-pass
 softmax and layernorm) and "fa4_splitk_reduce_scatter_write" (the split-K (max, sum)
-reweighting of partial outputs into bf16 rows).  See rro.c for the readings.
+reweighting of partial outputs into bf16 rows, and the per-partition partial
+outputs with their row max and row sum that it takes).  See rro.c for the
+readings.
 """
 import ctypes
 import os
@@ -47,6 +49,8 @@ def _load():
                                            ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                            ctypes.c_double]
         lib.rro_layernorm_rows.restype = ctypes.c_int
+        lib.rro_attention_partials.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                               i32, i32, ctypes.c_float]
         lib.rro_bf16_from_double.argtypes = [ctypes.c_double]
         lib.rro_bf16_from_double.restype = ctypes.c_uint16
         lib.rro_bf16_to_double.argtypes = [ctypes.c_uint16]
@@ -204,6 +208,34 @@ def splitk_lse_merge(o, m, l, scale=1.0, out_dtype="bf16"):
     if rc:
         raise ValueError("rro_splitk_lse_merge rejected its arguments")
     return out
+
+
+def attention_partials(q, k, v, P, scale, kv_heads=None):
+    """Split-K attention partials (m_p, l_p, normalised O_p) of every query row.
+
+    q: bf16 bits (uint16) [batch, heads, q_rows, depth]; k, v: bf16 bits
+    [batch, kv_heads, kv_len, depth].  Returns (o [P, batch*heads*q_rows, depth],
+    m [P, rows], l [P, rows]) as float32 -- the layout the LSE merge takes.
+    """
+    lib = _load()
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    v = np.ascontiguousarray(v, dtype=np.uint16)
+    batch, heads, q_rows, depth = q.shape
+    kb, kvh, kv_len, kd = k.shape
+    if kb != batch or kd != depth or v.shape != k.shape:
+        raise ValueError("k and v must be [batch, kv_heads, kv_len, depth]")
+    if kv_heads is not None and kv_heads != kvh:
+        raise ValueError("kv_heads does not match k")
+    rows = batch * heads * q_rows
+    o = np.empty((P, rows, depth), dtype=np.float32)
+    m = np.empty((P, rows), dtype=np.float32)
+    l = np.empty((P, rows), dtype=np.float32)
+    rc = lib.rro_attention_partials(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(m), _ptr(l), batch,
+                                    heads, kvh, q_rows, kv_len, depth, P, float(scale))
+    if rc:
+        raise ValueError("rro_attention_partials rejected its arguments")
+    return o, m, l
 
 
 def bf16_from_double(values):

@@ -38,6 +38,11 @@
  *     sum_p (w_p / W) O_p with W = sum_p w_p; a row with no non-empty
  *     partition is zero; empty partitions are skipped, so their O_p is never
  *     read into the sum.
+ *   - the split-K attention partials that the merge takes are, per query row
+ *     and partition of the keys (P contiguous ranges p*n/P .. (p+1)*n/P), the
+ *     scores s_j = scale * q.k_j, m_p = max s_j, l_p = sum exp(s_j - m_p) and
+ *     O_p = sum exp(s_j - m_p) v_j / l_p; grouped query heads share key/value
+ *     head h / (heads / kv_heads); a partition with no key is (-inf, 0, 0).
  */
 #include <math.h>
 #include <stdint.h>
@@ -437,5 +442,93 @@ int rro_splitk_lse_merge(const float* o, const float* m, const float* l, void* o
     }
     free(w);
     free(live);
+    return RRO_OK;
+}
+
+/*
+ * Split-K attention partials, the producer side of the LSE merge
+ * ("fa4_splitk_reduce_scatter_write", per-band steps: the partial output of
+ * each partition carries its own row max and row sum).
+ *
+ *   q [batch*heads][q_rows][depth]      bf16 bits
+ *   k, v [batch*kv_heads][kv_len][depth] bf16 bits
+ * Query head h of batch b reads key/value head h / (heads / kv_heads) of
+ * batch b (grouped heads; kv_heads == heads is plain multi-head attention).
+ * The keys are cut into P contiguous partitions: partition p holds keys
+ * j with p*kv_len/P <= j < (p+1)*kv_len/P (integer division).  For query
+ * row i and partition p, with s_j = scale * sum_d q[i][d] * k[j][d]:
+ *   m_p    = max over the partition's keys of s_j
+ *   l_p    = sum over the partition's keys of exp(s_j - m_p)
+ *   O_p[d] = sum over the partition's keys of exp(s_j - m_p) * v[j][d] / l_p
+ * (normalised partials, as the merge takes them).  A partition with no key
+ * gives m_p = -inf, l_p = 0 and O_p = 0.
+ *   o [P][batch*heads*q_rows][depth], m, l [P][batch*heads*q_rows]: float,
+ *   each rounded once from double.
+ */
+int rro_attention_partials(const uint16_t* q, const uint16_t* k, const uint16_t* v, float* o,
+                           float* m, float* l, int64_t batch, int64_t heads, int64_t kv_heads,
+                           int64_t q_rows, int64_t kv_len, int32_t depth, int32_t P, float scale)
+{
+    if (batch < 0 || heads < 1 || kv_heads < 1 || heads % kv_heads != 0 || q_rows < 0 ||
+        kv_len < 0 || depth < 1 || P < 1)
+        return RRO_BAD;
+    const int64_t group = heads / kv_heads;
+    const int64_t rows = batch * heads * q_rows;
+    double* s = (double*)malloc(sizeof(double) * (size_t)(kv_len > 0 ? kv_len : 1));
+    double* acc = (double*)malloc(sizeof(double) * (size_t)depth);
+    if (!s || !acc) {
+        free(s);
+        free(acc);
+        return RRO_BAD;
+    }
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t h = 0; h < heads; ++h) {
+            const int64_t kvh = b * kv_heads + h / group;
+            const uint16_t* kh = k + kvh * kv_len * depth;
+            const uint16_t* vh = v + kvh * kv_len * depth;
+            for (int64_t i = 0; i < q_rows; ++i) {
+                const int64_t row = (b * heads + h) * q_rows + i;
+                const uint16_t* qi = q + row * depth;
+                /* scores of every key */
+                for (int64_t j = 0; j < kv_len; ++j) {
+                    double dot = 0.0;
+                    for (int32_t d = 0; d < depth; ++d)
+                        dot += rro_bf16_to_double(qi[d]) * rro_bf16_to_double(kh[j * depth + d]);
+                    s[j] = (double)scale * dot;
+                }
+                for (int32_t p = 0; p < P; ++p) {
+                    const int64_t j0 = (int64_t)p * kv_len / P;
+                    const int64_t j1 = ((int64_t)p + 1) * kv_len / P;
+                    float* op = o + ((int64_t)p * rows + row) * depth;
+                    if (j1 <= j0) {
+                        m[(int64_t)p * rows + row] = -INFINITY;
+                        l[(int64_t)p * rows + row] = 0.0f;
+                        for (int32_t d = 0; d < depth; ++d)
+                            op[d] = 0.0f;
+                        continue;
+                    }
+                    double mp = s[j0];
+                    for (int64_t j = j0 + 1; j < j1; ++j)
+                        if (s[j] > mp)
+                            mp = s[j];
+                    double lp = 0.0;
+                    for (int32_t d = 0; d < depth; ++d)
+                        acc[d] = 0.0;
+                    for (int64_t j = j0; j < j1; ++j) {
+                        const double e = exp(s[j] - mp);
+                        lp += e;
+                        for (int32_t d = 0; d < depth; ++d)
+                            acc[d] += e * rro_bf16_to_double(vh[j * depth + d]);
+                    }
+                    m[(int64_t)p * rows + row] = (float)mp;
+                    l[(int64_t)p * rows + row] = (float)lp;
+                    for (int32_t d = 0; d < depth; ++d)
+                        op[d] = (float)(acc[d] / lp);
+                }
+            }
+        }
+    }
+    free(s);
+    free(acc);
     return RRO_OK;
 }

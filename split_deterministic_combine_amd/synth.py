@@ -20,6 +20,8 @@ Workloads (sizes are the defaults; smaller sizes keep the distributions):
   layernorm_rows     bf16 of 0.5 + 2 * standard normal, [16384, 4096], with
                      float32 gamma = 1 + 0.1 * standard normal and
                      beta = 0.1 * standard normal over the columns
+  attention    bf16 of standard normal q [8, 32, 128, 128], k and v
+               [8, 32, 8192, 128] (the producer of the LSE merge's partials)
 """
 import numpy as np
 
@@ -30,6 +32,7 @@ SEED_LONG_ROWS = 4
 SEED_LSE_MERGE = 5
 SEED_SOFTMAX_LONG_ROWS = 6
 SEED_LAYERNORM_ROWS = 7
+SEED_ATTENTION = 8
 
 
 def _bf16_bits(x_f32):
@@ -119,3 +122,14 @@ def ints_i32(seed, shape, lo, hi):
 
 def normal_bf16(seed, shape, std=3.0):
     return _bf16_bits(normal_f32(seed, shape, std))
+
+
+def attention(seed=SEED_ATTENTION, batch=8, heads=32, kv_heads=32, q_rows=128, kv_len=8192,
+              depth=128):
+    """bf16 bits of standard normal q [batch, heads, q_rows, depth], then k and
+    v [batch, kv_heads, kv_len, depth]."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((batch, heads, q_rows, depth), dtype=np.float32)
+    k = rng.standard_normal((batch, kv_heads, kv_len, depth), dtype=np.float32)
+    v = rng.standard_normal((batch, kv_heads, kv_len, depth), dtype=np.float32)
+    return _bf16_bits(q), _bf16_bits(k), _bf16_bits(v)

@@ -561,3 +561,133 @@ def test_merge_config_shape_smoke():
     out = oracle.splitk_lse_merge(o.reshape(8, 4, 128), m.reshape(8, 4), l.reshape(8, 4), 1.0,
                                   "bf16")
     assert out.shape == (4, 128) and out.dtype == np.uint16
+
+
+# ------------------------------------------------- split-K attention partials
+# Pins of oracle.attention_partials ("fa4_splitk_reduce_scatter_write": each
+# partition's partial output carries its own row max and row sum).
+
+def _bf16_array(bits):
+    """Values of an array of bf16 bit patterns (the top half of a binary32), as double."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _attn_reference(q, k, v, scale):
+    """softmax(scale * q k^T) v in double through torch's own routines, per head."""
+    qd = torch.from_numpy(_bf16_array(q))
+    kd = torch.from_numpy(_bf16_array(k))
+    vd = torch.from_numpy(_bf16_array(v))
+    group = qd.shape[1] // kd.shape[1]
+    kd = kd.repeat_interleave(group, dim=1)
+    vd = vd.repeat_interleave(group, dim=1)
+    s = scale * torch.matmul(qd, kd.transpose(-1, -2))
+    return s, torch.matmul(torch.softmax(s, dim=-1), vd)
+
+
+def test_attention_partials_single_partition_is_softmax_attention():
+    q, k, v = synth.attention(801, batch=2, heads=3, kv_heads=3, q_rows=5, kv_len=70, depth=16)
+    scale = 0.25
+    o, m, l = oracle.attention_partials(q, k, v, 1, scale)
+    s, full = _attn_reference(q, k, v, scale)
+    rows = 2 * 3 * 5
+    assert np.max(np.abs(o[0] - full.reshape(rows, 16).numpy())) <= 2e-7 * max(1.0, float(full.abs().max()))
+    smax = s.amax(-1).reshape(rows).numpy()
+    assert np.array_equal(m[0], smax.astype(np.float32))
+    lsum = torch.exp(s - s.amax(-1, keepdim=True)).sum(-1).reshape(rows).numpy()
+    assert np.max(np.abs(l[0] - lsum) / lsum) <= 2 ** -23
+
+
+def test_attention_partials_merge_to_full_attention():
+    # The closed form of split-K attention: merging the partials of any
+    # partition count gives softmax attention over all keys.
+    q, k, v = synth.attention(802, batch=1, heads=4, kv_heads=2, q_rows=6, kv_len=131, depth=32)
+    scale = 1.0 / math.sqrt(32)
+    _, full = _attn_reference(q, k, v, scale)
+    full = full.reshape(-1, 32).numpy()
+    for P in (1, 2, 3, 8, 131):
+        o, m, l = oracle.attention_partials(q, k, v, P, scale)
+        got = oracle.splitk_lse_merge(o, m, l, 1.0, "f32")
+        assert np.max(np.abs(got - full)) <= 2e-6 * max(1.0, np.abs(full).max()), P
+
+
+def test_attention_partials_grouped_heads_equal_repeated_kv():
+    q, k, v = synth.attention(803, batch=2, heads=6, kv_heads=2, q_rows=3, kv_len=40, depth=8)
+    a = oracle.attention_partials(q, k, v, 4, 0.5)
+    kr = np.repeat(k, 3, axis=1)
+    vr = np.repeat(v, 3, axis=1)
+    b = oracle.attention_partials(q, kr, vr, 4, 0.5)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    # and not what a wrong head mapping (h % kv_heads) would give
+    kw = np.tile(k, (1, 3, 1, 1))
+    vw = np.tile(v, (1, 3, 1, 1))
+    w = oracle.attention_partials(q, kw, vw, 4, 0.5)
+    assert not np.array_equal(a[0], w[0])
+
+
+def test_attention_partials_partition_boundaries():
+    # partition p holds keys [p*n/P, (p+1)*n/P): each equals one partition
+    # over exactly that slice of the keys
+    q, k, v = synth.attention(804, batch=1, heads=2, kv_heads=2, q_rows=4, kv_len=23, depth=8)
+    P = 5
+    o, m, l = oracle.attention_partials(q, k, v, P, 0.7)
+    for p in range(P):
+        j0, j1 = p * 23 // P, (p + 1) * 23 // P
+        op, mp, lp = oracle.attention_partials(q, k[:, :, j0:j1].copy(), v[:, :, j0:j1].copy(), 1,
+                                               0.7)
+        assert np.array_equal(o[p], op[0]) and np.array_equal(m[p], mp[0])
+        assert np.array_equal(l[p], lp[0])
+
+
+def test_attention_partials_invariants_and_empty_partitions():
+    q, k, v = synth.attention(805, batch=1, heads=2, kv_heads=1, q_rows=7, kv_len=5, depth=16)
+    P = 8                                      # more partitions than keys: some are empty
+    o, m, l = oracle.attention_partials(q, k, v, P, 0.3)
+    vv = _bf16_array(v)[0, 0]                  # [keys, depth]
+    nonempty = 0
+    for p in range(P):
+        j0, j1 = p * 5 // P, (p + 1) * 5 // P
+        if j1 == j0:
+            assert np.all(m[p] == -np.inf) and np.all(l[p] == 0) and np.all(o[p] == 0)
+            continue
+        nonempty += 1
+        assert np.all(l[p] >= 1.0) and np.all(l[p] <= j1 - j0)
+        lo, hi = vv[j0:j1].min(0), vv[j0:j1].max(0)   # a convex combination of the rows of V
+        assert np.all(o[p] >= lo - 1e-6) and np.all(o[p] <= hi + 1e-6)
+        if j1 - j0 == 1:                       # one key: weight 1, O is that row of V
+            assert np.array_equal(o[p], np.broadcast_to(vv[j0].astype(np.float32), o[p].shape))
+            assert np.all(l[p] == 1.0)
+    assert nonempty == 5
+
+
+def test_attention_partials_reject_bad_shapes():
+    q, k, v = synth.attention(806, batch=1, heads=3, kv_heads=2, q_rows=2, kv_len=4, depth=8)
+    with pytest.raises(ValueError):
+        oracle.attention_partials(q, k, v, 2, 1.0)     # 3 heads over 2 kv heads
+    q, k, v = synth.attention(806, batch=1, heads=2, kv_heads=2, q_rows=2, kv_len=4, depth=8)
+    with pytest.raises(ValueError):
+        oracle.attention_partials(q, k, v, 0, 1.0)
+
+
+def test_attention_partials_max_at_the_first_or_last_key_of_a_partition():
+    # Positive queries and one key of all 4.0 per partition (its first or last
+    # key): that key's score sum_d 4 q_d is the partition's maximum, and m_p
+    # must be exactly that score.
+    q, k, v = synth.attention(807, batch=1, heads=1, kv_heads=1, q_rows=6, kv_len=40, depth=16)
+    q = q & np.uint16(0x7FFF)                  # clear the sign bits: q > 0
+    four = np.uint16(0x4080)                   # bf16 4.0
+    P = 4
+    for pick_last in (True, False):
+        kk = k.copy()
+        for p in range(P):
+            j0, j1 = p * 40 // P, (p + 1) * 40 // P
+            kk[0, 0, j1 - 1 if pick_last else j0, :] = four
+        o, m, l = oracle.attention_partials(q, kk, v, P, 0.5)
+        s, _ = _attn_reference(q, kk, v, 0.5)
+        s = s.reshape(6, 40).numpy()
+        for p in range(P):
+            j0, j1 = p * 40 // P, (p + 1) * 40 // P
+            j = j1 - 1 if pick_last else j0
+            assert np.all(s[:, j] == s[:, j0:j1].max(1))
+            assert np.array_equal(m[p], s[:, j].astype(np.float32))
+            assert np.all(l[p] >= 1.0)
