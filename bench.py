@@ -13,6 +13,8 @@ timed on their own workloads and reported under "next_rows":
                 float32 mean/rstd written                      (block tier)
   multi_long    f32 sum, max and min over [16, 2^24] from one read (split-K)
   axis_cols     f32 column sums of [16384, 16384] (non-last axis, split-K)
+  attention     split-K attention partials: bf16 q [8, 32, 128, 128] over 8192
+                keys in 8 partitions -> float32 O, m, l (matrix cores)
 
 Inputs are resident in HBM before timing.  Buffer sets rotate from one step
 to the next so that the data touched by consecutive launches exceeds the
@@ -28,6 +30,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -66,13 +69,28 @@ KERNEL_OF_OP = {
     "axis_cols_partial": "k_reduce_axis_partial<rr::SumF32, 4>",
     "axis_cols_fold": "k_reduce_axis_fold<rr::SumF32>",
     # reference streams of known size (not ops of the step): rr_test_stream
+    "attention": "k_attn_staged<128, 32, 4>",
     "stream_read": "k_stream<0>",
     "stream_write": "k_stream<1>",
 }
 LAYERNORM = (16384, 4096)
 SOFTMAX_LONG = (16, 1 << 22)
 AXIS_COLS = (16384, 16384)
+# split-K attention partials: batch, heads, query rows, depth, keys, partitions
+ATTN = (8, 32, 128, 128, 8192, 8)
 CU_MI355X = 256
+
+
+def _attn_bytes():
+    """q, k, v read once (bf16); O (float32), m and l written once."""
+    b, h, sq, d, n, p = ATTN
+    return b * h * sq * d * 2 + 2 * b * h * n * d * 2 + p * b * h * sq * d * 4 + 2 * p * b * h * sq * 4
+
+
+def _attn_flops():
+    """q k^T and P v: 2 flops per multiply-add, 4 * batch*heads*q_rows*keys*depth."""
+    b, h, sq, d, n, _ = ATTN
+    return 4 * b * h * sq * n * d
 
 
 def _algo_bytes():
@@ -104,6 +122,7 @@ def _algo_bytes():
         # per column; the fold pass reads them and writes y
         "axis_cols_partial": ar * ac * 4 + g_ax * ac * 8,
         "axis_cols_fold": g_ax * ac * 8 + ac * 4,
+        "attention": _attn_bytes(),
         "stream_read": 1 << 30,
         "stream_write": 1 << 30,
     }
@@ -113,7 +132,8 @@ def _algo_bytes():
 NEXT_BYTES = {"multi_long": 16 * (1 << 24) * 4 + 3 * 16 * 4,
               "axis_cols": AXIS_COLS[0] * AXIS_COLS[1] * 4 + AXIS_COLS[1] * 4,
               "softmax_long": 16 * (1 << 22) * 2 * 2,
-              "layernorm": 16384 * 4096 * 2 * 2 + 2 * 4096 * 4 + 2 * 16384 * 4}
+              "layernorm": 16384 * 4096 * 2 * 2 + 2 * 4096 * 4 + 2 * 16384 * 4,
+              "attention": _attn_bytes()}
 STEP_OPS = ("short_sum", "short_max", "softmax", "long_sum", "long_max", "merge")
 COPY_BYTES = 512 << 20
 
@@ -324,6 +344,17 @@ def main():
         dx["layernorm_w"] = (gpu(gl), gpu(bl))
         dx["layernorm_stats"] = [(torch.empty(LAYERNORM[0], device=dev),
                                   torch.empty(LAYERNORM[0], device=dev)) for _ in range(4)]
+    if not args.no_next:
+        # attention inputs drawn on the device (1 GiB of keys and values):
+        # standard normal from a seeded generator, rounded to bf16
+        ab, ah, asq, ad, an, ap = ATTN
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(synth.SEED_ATTENTION)
+        dx["attn_qkv"] = tuple(torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16)
+                               for shape in ((ab, ah, asq, ad), (ab, ah, an, ad), (ab, ah, an, ad)))
+        arows = ab * ah * asq
+        dx["attn_out"] = (torch.empty((ap, arows, ad), device=dev), torch.empty((ap, arows), device=dev),
+                          torch.empty((ap, arows), device=dev))
     y_short_sum = torch.empty(1048576, dtype=torch.float32, device=dev)
     y_short_max = torch.empty(1048576, dtype=torch.float32, device=dev)
     y_long_f = torch.empty(16, dtype=torch.float32, device=dev)
@@ -353,6 +384,8 @@ def main():
                                                  out=dx["layernorm_out"][i % 4],
                                                  mean_out=dx["layernorm_stats"][i % 4][0],
                                                  rstd_out=dx["layernorm_stats"][i % 4][1]),
+        "attention": lambda i: rr.splitk_attention_partials(*dx["attn_qkv"], ATTN[5],
+                                                            out=dx["attn_out"]),
     }
     only = args.only.split(",") if args.only else None
     names = [n for n in ops if only is None or n in only]
@@ -399,6 +432,22 @@ def main():
             gs = dx["layernorm_stats"][0][1][pick].cpu().numpy()
             ok &= bool(np.all(np.abs(gm - rm) <= 1e-6 + 1e-5 * np.abs(rm)))
             ok &= bool(np.all(np.abs(gs - rs) <= 1e-6 + 1e-5 * np.abs(rs)))
+        if "attention" in next_names:
+            # one head against the oracle; bound from the kernel's arithmetic
+            # (bf16 probabilities: 2^-8 of the weighted |v|, plus float32 terms)
+            ab, ah, asq, ad, an, ap = ATTN
+            bh = (ab - 1, ah - 1)
+            bits = [t[bh[0]:bh[0] + 1, bh[1]:bh[1] + 1].contiguous().cpu().view(torch.int16)
+                    .numpy().view(np.uint16) for t in dx["attn_qkv"]]
+            sc = 1.0 / math.sqrt(ad)
+            o_r, m_r, l_r = oracle.attention_partials(*bits, ap, sc)
+            o_a, _, _ = oracle.attention_partials(bits[0], bits[1], bits[2] & np.uint16(0x7FFF),
+                                                  ap, sc)
+            rows = slice((bh[0] * ah + bh[1]) * asq, (bh[0] * ah + bh[1] + 1) * asq)
+            og = dx["attn_out"][0][:, rows].cpu().numpy()
+            mg = dx["attn_out"][1][:, rows].cpu().numpy()
+            ok &= bool(np.all(np.abs(og - o_r) <= (2.0 ** -8 + 2.0 ** -12) * o_a + 1e-6))
+            ok &= bool(np.all(np.abs(mg - m_r) <= 1e-5 * (1 + np.abs(m_r))))
         # sampled rows of the full-size outputs of the pass above (no extra launches)
         xs = host["short"][:4096]
         if "short_sum" in names:
@@ -546,6 +595,17 @@ def main():
                 "config": "bf16 layernorm [%d, %d] -> bf16, float32 gamma/beta, float32 "
                           "mean/rstd, block tier (persistent)" % LAYERNORM,
                 "kernels": [KERNEL_OF_OP["layernorm"]]})
+        if "attention" in next_rows:
+            ab, ah, asq, ad, an, ap = ATTN
+            t_s = next_rows["attention"]["ms_mean"] * 1e-3
+            next_rows["attention"].update({
+                "config": "split-K attention partials: bf16 q [%d, %d, %d, %d], k and v over %d "
+                          "keys in %d partitions -> float32 O, m, l (matrix cores, "
+                          "v_mfma_f32_32x32x16_bf16)" % (ab, ah, asq, ad, an, ap),
+                "kernels": [KERNEL_OF_OP["attention"]],
+                "flops": _attn_flops(),
+                "TFLOPs": round(_attn_flops() / t_s / 1e12, 1),
+                "pct_peak_bf16_mfma": round(100 * _attn_flops() / t_s / 2.5e15, 1)})
         if "softmax_long" in next_rows:
             r, c = SOFTMAX_LONG
             next_rows["softmax_long"].update({

@@ -1,7 +1,7 @@
 /*
  * rr.h -- deterministic row reductions on AMD Instinct MI355X (gfx950).
  *
- * A C ABI over hand-written HIP kernels.  Six operations:
+ * A C ABI over hand-written HIP kernels.  Seven operations:
  *
  *   rr_reduce_rows       sum / max / min of every row over its last axis, on
  *                        float32 or int32 values, through one of five tiers
@@ -15,6 +15,10 @@
  *                        mean and variance; pass 2: a map that writes y).
  *   rr_splitk_lse_merge  combine P split-K partial attention outputs by their
  *                        per-row (max, sum) statistics into bf16 or f32 rows.
+ *   rr_splitk_attention_partials
+ *                        the producer of those partials: attention of every
+ *                        query row over each of P partitions of the keys, with
+ *                        the partition's row max and row sum (matrix cores).
  *
  * Sources (Modular API pages, cited by title and section):
  *   "reduce" (algorithm.gpu.rowwise): the tier semantics list and the
@@ -370,6 +374,40 @@ rr_status rr_layernorm_rows(const void* x, void* y, const void* gamma, const voi
 rr_status rr_splitk_lse_merge(const float* o_part, const float* m_part, const float* l_part,
                               void* out, int32_t P, int64_t rows, int32_t depth, float scale,
                               rr_dtype out_dtype, void* stream);
+
+/*
+ * rr_splitk_attention_partials -- split-K attention partials, the inputs of
+ * rr_splitk_lse_merge.  "fa4_splitk_reduce_scatter_write", per-band steps:
+ * each partition's partial output carries its own row max and row sum, which
+ * the merge uses to reweight it.
+ *
+ *   q       device, bf16 [batch][heads][q_rows][depth]
+ *   k, v    device, bf16 [batch][kv_heads][kv_len][depth]; query head h of a
+ *           batch reads key/value head h / (heads / kv_heads) (grouped heads;
+ *           kv_heads == heads is plain multi-head attention)
+ *   o_part  device, float32 [P][batch*heads*q_rows][depth] (written)
+ *   m_part, l_part  device, float32 [P][batch*heads*q_rows] (written)
+ *   depth   64 or 128;  P 1 .. RR_MERGE_MAX_P;  heads % kv_heads == 0;
+ *           batch, q_rows, kv_len >= 0;  q_rows * depth * 2 < 2^31
+ *   scale   finite; multiplies q . k (1/sqrt(depth) for standard attention)
+ * The keys are cut into P contiguous partitions: partition p holds keys
+ * p*kv_len/P .. (p+1)*kv_len/P - 1 (integer division).  For query row i and
+ * partition p, with s_j = scale * q_i . k_j over the partition's keys:
+ *   m_part[p][i] = max_j s_j,   l_part[p][i] = sum_j exp(s_j - m_part[p][i]),
+ *   o_part[p][i][d] = sum_j exp(s_j - m_part[p][i]) * v_j[d] / l_part[p][i]
+ * (normalised partials in natural-log units, so rr_splitk_lse_merge takes
+ * them with scale 1.0).  A partition with no key is written as m = -inf,
+ * l = 0, O = 0, which the merge skips.  Rows are ordered (batch, head, query
+ * row).  q . k and P v accumulate in float32 on the matrix cores with the
+ * probabilities rounded to bf16 as the second product's operand; the row
+ * statistics are float32.  q, k, v and o_part must be 16-byte aligned.
+ * Errors (nothing launched): RR_ERR_SHAPE (sizes, depth, P, alignment,
+ * scale), RR_ERR_NULL; batch*heads*q_rows == 0 is a no-op.
+ */
+rr_status rr_splitk_attention_partials(const void* q, const void* k, const void* v, float* o_part,
+                                       float* m_part, float* l_part, int64_t batch, int64_t heads,
+                                       int64_t kv_heads, int64_t q_rows, int64_t kv_len,
+                                       int32_t depth, int32_t P, float scale, void* stream);
 
 /* Bytes of workspace rr_reduce_rows (RR_KIND_REDUCE), rr_softmax_rows
  * (RR_KIND_SOFTMAX, dtype = x_dtype) or rr_layernorm_rows (RR_KIND_LAYERNORM,

@@ -14,8 +14,12 @@ Operations (names as in the C ABI):
   layernorm_rows     two-pass layer normalisation over the last axis
   splitk_lse_merge   merge of P split-K partial attention outputs by their
                      per-row (max, sum) statistics
+  splitk_attention_partials
+                     the producer of those partials (attention over each of P
+                     partitions of the keys, on the matrix cores)
 """
 import ctypes
+import math
 import os
 import threading
 
@@ -23,6 +27,7 @@ import torch
 
 __all__ = [
     "RRError", "reduce_rows", "reduce_rows_multi", "reduce_axis", "plan_axis", "softmax_rows", "layernorm_rows", "splitk_lse_merge",
+    "splitk_attention_partials",
     "plan_reduce", "plan_softmax", "plan_layernorm", "select_tier", "workspace_bytes", "workspace_reset", "device_cu_count",
     "version", "lib_path", "TIERS", "OPS",
 ]
@@ -82,6 +87,8 @@ def _load():
         lib.rr_softmax_rows.argtypes = [vp, vp, i64, i64, i64, i64, st, st, st, vp,
                                         ctypes.c_size_t, vp]
         lib.rr_splitk_lse_merge.argtypes = [vp, vp, vp, vp, i32, i64, i32, ctypes.c_float, st, vp]
+        lib.rr_splitk_attention_partials.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                                     i64, i32, i32, ctypes.c_float, vp]
         lib.rr_reduce_axis.argtypes = [vp, vp, i64, i64, i64, st, st, st, vp, ctypes.c_size_t, vp]
         lib.rr_plan_axis.argtypes = [i64, i64, i64, st, st, st, i32, ctypes.POINTER(_Plan)]
         lib.rr_layernorm_rows.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, st, st, st,
@@ -103,7 +110,8 @@ def _load():
                      "rr_softmax_rows", "rr_splitk_lse_merge", "rr_plan_reduce",
                      "rr_plan_softmax", "rr_layernorm_rows", "rr_plan_layernorm",
                      "rr_workspace_bytes", "rr_select_tier",
-                     "rr_workspace_reset", "rr_device_cu_count", "rr_test_stream"):
+                     "rr_workspace_reset", "rr_device_cu_count", "rr_test_stream",
+                     "rr_splitk_attention_partials"):
             getattr(lib, name).restype = st
         _lib = lib
     return _lib
@@ -448,6 +456,45 @@ def splitk_lse_merge(o_part, m_part, l_part, scale=1.0, out_dtype=torch.bfloat16
                                        float(scale), _dtype_code(out_dtype),
                                        _stream_ptr(o_part.device)))
     return out
+
+
+def splitk_attention_partials(q, k, v, P, scale=None, out=None):
+    """Split-K attention partials: q bf16 [batch, heads, q_rows, depth], k and v
+    bf16 [batch, kv_heads, kv_len, depth] (depth 64 or 128).
+
+    Returns (o_part [P, batch*heads*q_rows, depth], m_part [P, rows],
+    l_part [P, rows]) in float32 -- the inputs of splitk_lse_merge (scale 1.0).
+    ``scale`` defaults to 1/sqrt(depth); ``out`` may give the three tensors.
+    """
+    lib = _load()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.bfloat16:
+            raise ValueError("%s must be a bfloat16 GPU tensor" % n)
+        if not t.is_contiguous() or t.dim() != 4:
+            raise ValueError("%s must be a contiguous 4-d tensor" % n)
+    batch, heads, q_rows, depth = q.shape
+    kb, kv_heads, kv_len, kd = k.shape
+    if kb != batch or kd != depth or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [batch, kv_heads, kv_len, depth] matching q")
+    rows = batch * heads * q_rows
+    if scale is None:
+        scale = 1.0 / math.sqrt(depth)
+    if out is None:
+        out = (torch.empty((P, rows, depth), dtype=torch.float32, device=q.device),
+               torch.empty((P, rows), dtype=torch.float32, device=q.device),
+               torch.empty((P, rows), dtype=torch.float32, device=q.device))
+    o, m, l = out
+    for t, shape in ((o, (P, rows, depth)), (m, (P, rows)), (l, (P, rows))):
+        if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != shape:
+            raise ValueError("outputs must be contiguous float32 %s, %s, %s"
+                             % ((P, rows, depth), (P, rows), (P, rows)))
+    with _OnDevice(q.device):
+        _check(lib.rr_splitk_attention_partials(
+            ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+            ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(o.data_ptr()),
+            ctypes.c_void_p(m.data_ptr()), ctypes.c_void_p(l.data_ptr()), batch, heads, kv_heads,
+            q_rows, kv_len, depth, int(P), float(scale), _stream_ptr(q.device)))
+    return o, m, l
 
 
 def _plan_dict(plan):

@@ -25,7 +25,8 @@ LIB = os.path.join(PKG, "librr.so")
 ARCH = "gfx950"
 
 SOURCES = ["rr_plan.cpp", "rr_api.cpp", "rr_reduce.hip", "rr_softmax.hip", "rr_merge.hip",
-           "rr_layernorm.hip", "rr_axis.hip", "rr_stream.hip"]
+           "rr_layernorm.hip", "rr_axis.hip", "rr_stream.hip",
+           "rr_attention.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall", "-Wno-unused-result",
           "-I", os.path.join(ROOT, "include")]

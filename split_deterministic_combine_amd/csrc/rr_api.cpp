@@ -264,6 +264,35 @@ extern "C" rr_status rr_splitk_lse_merge(const float* o_part, const float* m_par
     return rr::launch_merge(a);
 }
 
+extern "C" rr_status rr_splitk_attention_partials(const void* q, const void* k, const void* v,
+                                                  float* o_part, float* m_part, float* l_part,
+                                                  int64_t batch, int64_t heads, int64_t kv_heads,
+                                                  int64_t q_rows, int64_t kv_len, int32_t depth,
+                                                  int32_t P, float scale, void* stream)
+{
+    if (batch < 0 || heads < 1 || kv_heads < 1 || heads % kv_heads != 0 || q_rows < 0 ||
+        kv_len < 0 || P < 1 || P > RR_MERGE_MAX_P || (depth != 64 && depth != 128) ||
+        !isfinite(scale))
+        return RR_ERR_SHAPE;
+    if (q_rows * (int64_t)depth * 2 > (int64_t)INT32_MAX) return RR_ERR_SHAPE;
+    const int64_t q_tiles = (q_rows + rr::kAttnRows - 1) / rr::kAttnRows;
+    if (q_tiles * P * batch * heads > (int64_t)INT32_MAX) return RR_ERR_SHAPE;
+    if (batch * heads * q_rows == 0) return RR_OK;
+    if (!q || !o_part || !m_part || !l_part || (kv_len > 0 && (!k || !v))) return RR_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o_part, 16))
+        return RR_ERR_SHAPE;
+    rr::AttentionLaunch a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                          static_cast<const uint16_t*>(v), o_part, m_part, l_part, batch, heads,
+                          kv_heads, q_rows, kv_len, depth, P, scale, as_stream(stream)};
+    if (log_enabled())
+        fprintf(stderr,
+                "rr: rr_splitk_attention_partials batch=%lld heads=%lld kv_heads=%lld "
+                "q_rows=%lld kv_len=%lld depth=%d P=%d workgroups=%lld\n",
+                (long long)batch, (long long)heads, (long long)kv_heads, (long long)q_rows,
+                (long long)kv_len, depth, P, (long long)(q_tiles * P * batch * heads));
+    return rr::launch_attention(a);
+}
+
 extern "C" rr_status rr_workspace_bytes(rr_kind kind, int64_t rows, int64_t cols, rr_dtype dtype,
                                         rr_op op, rr_tier tier, size_t* bytes_out)
 {

@@ -1,0 +1,459 @@
+// rr_attention.hip -- split-K attention partials on MFMA, gfx950.
+//
+// The producer side of the LSE merge ("fa4_splitk_reduce_scatter_write",
+// per-band steps: the partial output of each partition carries its row max
+// and row sum).  The keys of a head are cut into P contiguous partitions
+// (partition p holds keys p*n/P .. (p+1)*n/P - 1); for every query row and
+// partition the kernel writes
+//   m_p = max_j s_j,  l_p = sum_j exp(s_j - m_p),
+//   O_p = sum_j exp(s_j - m_p) v_j / l_p,       s_j = scale * q . k_j,
+// in the merge's layout: O [P][rows][depth], m and l [P][rows] (float),
+// rows = batch * heads * q_rows.  A partition with no key gets (-inf, 0, 0).
+//
+// This is a dense contraction, so it runs on the matrix cores
+// (v_mfma_f32_32x32x16_bf16).  A workgroup of four wavefronts takes 128
+// query rows (32 per wavefront) of one head and one partition and walks the
+// partition's keys in stages of kAttnStageKeys, kAttnStages of them in
+// flight: each stage's K and V tiles go from HBM straight into LDS (buffer
+// loads with the lds modifier, non-temporal), so no registers hold data in
+// transit.  Per stage a wavefront forms S^T = K Q^T (keys x its 32 queries)
+// and, after the online max / sum update, O^T += V^T P^T; in both products a
+// lane owns one query column of the accumulator, so the rescale of O and the
+// row statistics stay inside the lane.  Q stays in registers as the B
+// operand for the whole walk.  At the end O goes out through LDS as whole
+// 128-byte lines.
+//
+// Precision: q.k and P V accumulate in float32 inside the MFMA; P is rounded
+// to bf16 as the MFMA operand (the usual flash-attention practice); the
+// running max and sum are float32.  Everything is in a fixed order, so the
+// bits do not change from run to run.
+#include <hip/hip_runtime.h>
+
+#include "rr_config.hpp"
+#include "rr_device.hpp"
+#include "rr_launch.hpp"
+#include "rr_launch_util.hpp"
+#include "rr_rowio.hpp"
+
+namespace rr {
+
+typedef __bf16 rr_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float rr_f32x16 __attribute__((ext_vector_type(16)));
+
+// Accumulator layout of the 32x32 MFMA (checked on MI355X against a host
+// product): register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4 and
+// column l%32; an A operand lane holds row l%32, a B operand lane column
+// l%32, both at k = 8*(l/32) + 0..7 of the 16-deep step.
+
+__device__ __forceinline__ rr_bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(rr_bf16x8, u); }
+
+// Pack eight floats to bf16 (round to nearest even).
+__device__ __forceinline__ rr_bf16x8 pack8(const float* f)
+{
+    uint4 u;
+    u.x = pack_bf16x2(f[0], f[1]);
+    u.y = pack_bf16x2(f[2], f[3]);
+    u.z = pack_bf16x2(f[4], f[5]);
+    u.w = pack_bf16x2(f[6], f[7]);
+    return as_bf16x8(u);
+}
+
+// ------------------------------------------------ staged through LDS by DMA
+// Keys stream in stages of kAttnStageKeys; each stage's K and V tiles go from
+// HBM straight into LDS (buffer loads with the lds modifier: no registers),
+// NS stages in flight.  Tiles are unpadded and XOR-swizzled by 16-byte chunk
+// (each lane picks the global chunk that belongs at its LDS slot):
+//   K: chunk c of row r at slot c ^ (r mod chunks-per-row): the S operand
+//      reads (16 lanes = 16 rows, one chunk) hit 16 distinct bank groups;
+//   V: chunk c of row r at slot c ^ 2 (r mod 4): the transposed reads below
+//      (4 rows x 4 half-chunks per 16 lanes) hit 16 distinct bank pairs.
+// V stays row-major (keys x depth); the A operand of O^T += V^T P^T comes from
+// ds_read_b64_tr_b16, which hands lane i of a 16-lane group element i%4 of
+// the 8 bytes addressed by lane 4j + i/4, j = 0..3 (checked on MI355X): with
+// lane 4j + q pointing at V[k0 + j][d0 + 4q], lane i receives
+// V[k0 .. k0+3][d0 + i] -- four consecutive keys at one depth.
+template <int D, int KB>
+struct AttnStage {
+    uint16_t k[KB * D];
+    uint16_t v[KB * D];
+};
+
+template <int D>
+__device__ __forceinline__ int k_slot_byte(int row, int chunk)
+{
+    return row * D * 2 + 16 * (chunk ^ (row & (D / 8 - 1)));
+}
+template <int D>
+__device__ __forceinline__ int v_slot_byte(int row, int chunk)
+{
+    return row * D * 2 + 16 * (chunk ^ ((row & 3) << 1));
+}
+
+// s_waitcnt on the vector-memory counter only (N < 16): expcnt and lgkmcnt
+// fields at their maxima.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 16, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt(N | 0x70 | 0xF00);
+}
+
+// Wait until at most `after` stages of OPS DMA operations each are still
+// outstanding (every stage issued before them has landed); at most NS - 2
+// stages are ever outstanding after the one about to be read.
+template <int OPS, int NS>
+__device__ __forceinline__ void wait_stages(int64_t after)
+{
+    if constexpr (NS - 2 >= 3) {
+        if (after >= 3) { wait_vmcnt<OPS * 3>(); return; }
+    }
+    if constexpr (NS - 2 >= 2) {
+        if (after >= 2) { wait_vmcnt<OPS * 2>(); return; }
+    }
+    if constexpr (NS - 2 >= 1) {
+        if (after >= 1) { wait_vmcnt<OPS>(); return; }
+    }
+    wait_vmcnt<0>();
+}
+
+// DMA of one stage: keys [js, js + nvalid) of a head into stage buffer st.
+// Rows past nvalid repeat row nvalid - 1 (finite values; their scores are
+// masked), so every load stays inside the head's keys.
+template <int D, int KB>
+__device__ __forceinline__ void attn_dma_stage(const uint16_t* kh, const uint16_t* vh, int64_t js,
+                                               int nvalid, AttnStage<D, KB>* st)
+{
+    constexpr int CH = D / 8;                       // 16-byte chunks per row
+    constexpr int OPS = KB * CH / kBlockThreads;    // per tensor per thread
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(kh + js * D), 0, nvalid * D * 2, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(vh + js * D), 0, nvalid * D * 2, kBufferWord3);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lane = lane_id();
+#pragma unroll
+    for (int i = 0; i < OPS; ++i) {
+        const int base = i * kBlockThreads + wave * kWave;   // first slot of this wave's op
+        const int slot = base + lane;
+        const int row = slot / CH, pos = slot % CH;
+        const int rr_ = row < nvalid ? row : nvalid - 1;
+        const int kc = pos ^ (row & (CH - 1));
+        const int vc = pos ^ ((row & 3) << 1);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rk, (__attribute__((address_space(3))) void*)((char*)st->k + 16 * base), 16,
+            rr_ * D * 2 + 16 * kc, 0, 0, kBufferNonTemporal);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rv, (__attribute__((address_space(3))) void*)((char*)st->v + 16 * base), 16,
+            rr_ * D * 2 + 16 * vc, 0, 0, kBufferNonTemporal);
+    }
+}
+
+typedef short rr_i16x4 __attribute__((ext_vector_type(4)));
+
+// Workgroup barrier between stages.  __syncthreads() carries a workgroup
+// release fence, which on this target waits for every outstanding LDS DMA
+// (vmcnt(0)) and would drain the stages in flight.  Here each wave has
+// already waited for its own DMA of the stage it is about to read
+// (wait_vmcnt), so a bare s_barrier suffices; before it, lgkmcnt(0) retires
+// the wave's LDS reads of the previous stage, whose buffer the next DMA
+// overwrites.  The signal fences keep the compiler from moving LDS accesses
+// across the barrier.
+__device__ __forceinline__ void stage_barrier()
+{
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt at their maxima
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+template <int D, int KB, int NS>
+__global__ __launch_bounds__(kBlockThreads, 2) void k_attn_staged(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    float* __restrict__ o, float* __restrict__ m_out, float* __restrict__ l_out, int64_t heads,
+    int64_t kv_heads, int64_t q_rows, int64_t kv_len, int32_t P, float scale, int32_t q_tiles,
+    int64_t rows)
+{
+    constexpr int NC = D / 16;
+    constexpr int NT = D / 32;
+    constexpr int CH = D / 8;
+    constexpr int OPS = 2 * (KB * CH / kBlockThreads);  // DMA ops per stage per thread
+    constexpr int NST = KB / 32;                         // 32-key tiles per stage
+    static_assert(OPS * (NS - 2) < 16, "vmcnt immediate");
+    static_assert(NS >= 2 && NS <= 5, "stage count");
+    static_assert(KB % 32 == 0 && (KB * CH) % kBlockThreads == 0, "stage shape");
+    // One LDS object per stage: the compiler's wait insertion then knows that
+    // a DMA into one stage cannot alias reads of another, and does not drain
+    // the DMA queue before every read.  The stage loop below is unrolled by
+    // NS, so every stage reference is to a named object.
+    __shared__ AttnStage<D, KB> S0;
+    __shared__ AttnStage<D, KB> S1;
+    __shared__ AttnStage<D, KB> S2;
+    __shared__ AttnStage<D, KB> S3;
+    __shared__ AttnStage<D, KB> S4;
+#define RR_ATTN_STAGE(u) ((u) == 0 ? &S0 : (u) == 1 ? &S1 : (u) == 2 ? &S2 : (u) == 3 ? &S3 : &S4)
+
+    const int64_t nb = gridDim.x;
+    const int64_t per = nb / kXcds, rem = nb % kXcds;
+    const int64_t xcd = blockIdx.x % kXcds, idx = blockIdx.x / kXcds;
+    int64_t w = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+    const int64_t group = heads / kv_heads;
+    const int32_t qt = (int32_t)(w % q_tiles);
+    w /= q_tiles;
+    const int64_t g = w % group;
+    w /= group;
+    const int32_t p = (int32_t)(w % P);
+    w /= P;
+    const int64_t kvl = w % kv_heads;
+    const int64_t b = w / kv_heads;
+    const int64_t bh = b * heads + kvl * group + g;
+    const int64_t kvh = b * kv_heads + kvl;
+
+    const int lane = lane_id();
+    const int hf = lane / 32;
+    const int wave = threadIdx.x / kWave;
+    const int64_t qrow = (int64_t)qt * kAttnRows + wave * 32 + lane % 32;
+    const bool row_ok = qrow < q_rows;
+    const int64_t row = bh * q_rows + qrow;
+    const int64_t j0 = (int64_t)p * kv_len / P, j1 = ((int64_t)p + 1) * kv_len / P;
+    float* orow = o + ((int64_t)p * rows + row) * D;
+
+    if (j1 <= j0) {
+        if (row_ok) {
+#pragma unroll
+            for (int d = 0; d < D / 2; d += 4)
+                *reinterpret_cast<float4*>(orow + hf * (D / 2) + d) = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (hf == 0) {
+                m_out[(int64_t)p * rows + row] = -__builtin_inff();
+                l_out[(int64_t)p * rows + row] = 0.0f;
+            }
+        }
+        return;
+    }
+
+    rr_bf16x8 qb[NC];
+    {
+        const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(q + bh * q_rows * D), 0, (int)(q_rows * D * 2), kBufferWord3);
+        const int qoff = (int)(qrow < q_rows ? qrow : q_rows) * D * 2;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const rr_u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + (16 * c + 8 * hf) * 2, 0, 0);
+            qb[c] = as_bf16x8(make_uint4(u.x, u.y, u.z, u.w));
+        }
+    }
+
+    const uint16_t* kh = k + kvh * kv_len * D;
+    const uint16_t* vh = v + kvh * kv_len * D;
+    const int64_t nstg = ceil_div(j1 - j0, KB);
+    auto nvalid_of = [&](int64_t s_) {
+        const int64_t left = j1 - j0 - s_ * KB;
+        return (int)(left < KB ? left : KB);
+    };
+#pragma unroll
+    for (int s_ = 0; s_ < NS - 1; ++s_)
+        if (s_ < nstg)
+            attn_dma_stage<D, KB>(kh, vh, j0 + (int64_t)s_ * KB, nvalid_of(s_), RR_ATTN_STAGE(s_));
+
+    rr_f32x16 acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            acc[t][r] = 0.0f;
+    // Scores stay raw (q . k, float32 out of the MFMA); with c2 = |scale| *
+    // log2(e) the probability is exp2(raw * c2 - m_ref * c2), one FMA per
+    // score.  A negative scale is carried by negating q (exact in bf16), and
+    // because rounding is monotonic, |scale| * max(raw) is the largest of the
+    // rounded scaled scores, which is the m written out.
+    // Online (max, sum) with a lazy reference: the exponentials are taken
+    // relative to m_ref, which moves (rescaling O and l) only when a block's
+    // maximum exceeds it by more than 2^kAttnLazyLog2 in the exponential, so
+    // after the first stage the rescale is skipped; m_true is the exact
+    // running maximum, and l is brought to it at the end.  O / l does not
+    // depend on the reference.
+    if (scale < 0.0f) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            uint4 u = __builtin_bit_cast(uint4, qb[c]);
+            u.x ^= 0x80008000u; u.y ^= 0x80008000u; u.z ^= 0x80008000u; u.w ^= 0x80008000u;
+            qb[c] = as_bf16x8(u);
+        }
+    }
+    const float ascale = fabsf(scale);
+    const float c2 = ascale * kLog2e;
+    float m_ref = -__builtin_inff();
+    float m_true = -__builtin_inff();
+    float l_run = 0.0f;
+    const int G = (lane / 16) & 1, a16 = lane % 16, jj = a16 / 4, qq = a16 % 4;
+
+    auto stage = [&](int64_t st, AttnStage<D, KB>* T, AttnStage<D, KB>* F) {
+        const int64_t issued = nstg < st + NS - 1 ? nstg : st + NS - 1;
+        const int64_t after = issued - st - 1;
+        wait_stages<OPS, NS>(after);
+        stage_barrier();
+        if (st + NS - 1 < nstg)
+            attn_dma_stage<D, KB>(kh, vh, j0 + (st + NS - 1) * KB, nvalid_of(st + NS - 1), F);
+        const int nvalid = nvalid_of(st);
+        const char* kb = reinterpret_cast<const char*>(T->k);
+        const char* vb = reinterpret_cast<const char*>(T->v);
+
+        rr_f32x16 s[NST];
+#pragma unroll
+        for (int t = 0; t < NST; ++t) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                s[t][r] = 0.0f;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const uint4 a = *reinterpret_cast<const uint4*>(
+                    kb + k_slot_byte<D>(32 * t + lane % 32, 2 * c + hf));
+                s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qb[c], s[t], 0, 0, 0);
+            }
+        }
+        const bool full = nvalid == KB;                 // all keys of the stage are in the partition
+        float bm = -__builtin_inff();
+        if (full) {
+#pragma unroll
+            for (int t = 0; t < NST; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    bm = fmaxf(bm, s[t][r]);
+        } else {
+#pragma unroll
+            for (int t = 0; t < NST; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (32 * t + 8 * (r / 4) + 4 * hf + (r % 4) < nvalid)
+                        bm = fmaxf(bm, s[t][r]);
+        }
+        bm = fmaxf(bm, __shfl_xor(bm, 32));            // finite: every stage has a key
+        m_true = fmaxf(m_true, bm);
+        const bool move = st == 0 || (bm - m_ref) * c2 > kAttnLazyLog2;
+        if (__any(move)) {                              // wavefront-uniform branch
+            const float m_new = move ? fmaxf(m_ref, bm) : m_ref;
+            const float alpha = m_ref == -__builtin_inff() ? 0.0f : exp2_hw((m_ref - m_new) * c2);
+            m_ref = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    acc[t][r] *= alpha;
+        }
+        const float mb = -m_ref * c2;
+        float ls = 0.0f;
+#pragma unroll
+        for (int t = 0; t < NST; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float pv = exp2_hw(__builtin_fmaf(s[t][r], c2, mb));
+                if (!full && 32 * t + 8 * (r / 4) + 4 * hf + (r % 4) >= nvalid)
+                    pv = 0.0f;
+                s[t][r] = pv;
+                ls += pv;
+            }
+        l_run += ls;
+        rr_bf16x8 pb[NST][2];
+#pragma unroll
+        for (int t = 0; t < NST; ++t)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                float f[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    f[j] = s[t][8 * c + j];
+                pb[t][c] = pack8(f);
+            }
+#pragma unroll
+        for (int dt = 0; dt < NT; ++dt)
+#pragma unroll
+            for (int t = 0; t < NST; ++t)
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const int r1 = 32 * t + 16 * c + 4 * hf + jj;
+                    const int chunk = 4 * dt + 2 * G + (qq >> 1);
+                    const int off = 8 * (qq & 1);
+                    const rr_i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (rr_i16x4 __attribute__((address_space(3)))*)(vb + v_slot_byte<D>(r1, chunk) + off));
+                    const rr_i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (rr_i16x4 __attribute__((address_space(3)))*)(vb + v_slot_byte<D>(r1 + 8, chunk) + off));
+                    const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+                    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y)), pb[t][c], acc[dt], 0, 0, 0);
+                }
+    };
+    for (int64_t st0 = 0; st0 < nstg; st0 += NS) {
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+            if (st0 + u >= nstg)
+                break;
+            stage(st0 + u, RR_ATTN_STAGE(u), RR_ATTN_STAGE((u + NS - 1) % NS));
+        }
+    }
+#undef RR_ATTN_STAGE
+
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float inv = 1.0f / l_tot;
+    if (row_ok && hf == 0) {
+        m_out[(int64_t)p * rows + row] = ascale * m_true;
+        l_out[(int64_t)p * rows + row] = l_tot * exp2_hw((m_ref - m_true) * c2);
+    }
+    // O through LDS, one 32-column depth tile at a time: a lane holds one
+    // query column of the tile, so stores straight from the accumulator put
+    // 32 bytes in each of 32 rows per instruction.  Each wavefront writes its
+    // 32 x 32 floats row-major into a region of a stage buffer (rows padded
+    // to 36 floats: 16-byte aligned, the b128 writes of 16 lanes on distinct
+    // banks), then stores whole 128-byte lines, 8 rows per instruction.
+    stage_barrier();                                   // every wavefront is done with the stages
+    constexpr int kOStride = 36;                       // floats per staged row
+    constexpr int kOWaveBytes = 32 * kOStride * 4;
+    constexpr int kWavesPerStage = (kWavesPerBlock + NS - 1) / NS;
+    static_assert(kWavesPerStage * kOWaveBytes <= (int)sizeof(AttnStage<D, KB>), "O staging fits");
+    const int wst = wave / kWavesPerStage;
+    char* sb = reinterpret_cast<char*>(&S0);
+    if (NS > 1 && wst == 1) sb = reinterpret_cast<char*>(&S1);
+    if (NS > 2 && wst == 2) sb = reinterpret_cast<char*>(&S2);
+    if (NS > 3 && wst == 3) sb = reinterpret_cast<char*>(&S3);
+    char* obase = sb + (wave % kWavesPerStage) * kOWaveBytes;
+    float* ow = reinterpret_cast<float*>(obase);
+    const int64_t qrow0 = (int64_t)qt * kAttnRows + wave * 32;
+#pragma unroll
+    for (int dt = 0; dt < NT; ++dt) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+            *reinterpret_cast<float4*>(ow + (lane % 32) * kOStride + 8 * g4 + 4 * hf) =
+                make_float4(acc[dt][4 * g4] * inv, acc[dt][4 * g4 + 1] * inv,
+                            acc[dt][4 * g4 + 2] * inv, acc[dt][4 * g4 + 3] * inv);
+        __builtin_amdgcn_s_waitcnt(0xC07F);            // lgkmcnt(0): the wavefront's writes are in
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = lane / 8 + 8 * i;
+            const float4 val = *reinterpret_cast<const float4*>(ow + r * kOStride + 4 * (lane % 8));
+            if (qrow0 + r < q_rows) {
+                float* dst = o + ((int64_t)p * rows + bh * q_rows + qrow0 + r) * D + 32 * dt + 4 * (lane % 8);
+                store16_nt(dst, make_uint4(__float_as_uint(val.x), __float_as_uint(val.y),
+                                           __float_as_uint(val.z), __float_as_uint(val.w)));
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);            // reads done before the next tile overwrites
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+rr_status launch_attention(const AttentionLaunch& a)
+{
+    const int32_t q_tiles = (int32_t)ceil_div(a.q_rows, kAttnRows);
+    const int64_t nwork = (int64_t)q_tiles * a.P * a.batch * a.heads;
+    const int64_t rows = a.batch * a.heads * a.q_rows;
+    const dim3 grid((unsigned)nwork), block(kBlockThreads);
+    if (a.depth == 128)
+        return launch_kernel(k_attn_staged<128, kAttnStageKeys, kAttnStages>, grid, block, 0,
+                             a.stream, a.q, a.k, a.v, a.o, a.m, a.l, a.heads, a.kv_heads, a.q_rows,
+                             a.kv_len, a.P, a.scale, q_tiles, rows);
+    return launch_kernel(k_attn_staged<64, kAttnStageKeys, kAttnStages>, grid, block, 0, a.stream,
+                         a.q, a.k, a.v, a.o, a.m, a.l, a.heads, a.kv_heads, a.q_rows, a.kv_len,
+                         a.P, a.scale, q_tiles, rows);
+}
+
+}  // namespace rr

@@ -132,6 +132,18 @@ constexpr int kMergeMaxP = 256;
 constexpr int kMergePOuterRowsPerLane = 4;
 constexpr int kMergePOuterMaxP = 32;
 
+// Split-K attention partials: query rows per workgroup (4 wavefronts of 32),
+// keys per LDS stage and stages in flight (32 x 4 measured fastest on
+// [8, 32, 128, 128] over 8192 keys, beside 32 x 2, 32 x 3 and 64 x 2).
+constexpr int kAttnRows = 128;
+constexpr int kAttnStages = 4;
+constexpr int kAttnMaxP = 256;
+constexpr int kAttnStageKeys = 32;
+constexpr float kAttnLazyLog2 = 8.0f; // lazy rescale: the reference max moves past 2^8
+
+// XCDs of MI355X: consecutive workgroups are dealt to them in turn.
+constexpr int kXcds = 8;
+
 // Largest grid.x the launchers use; kernels loop over the remainder.
 constexpr int64_t kMaxGrid = 1 << 30;
 

@@ -74,10 +74,24 @@ struct MergeLaunch {
     hipStream_t stream;
 };
 
+struct AttentionLaunch {
+    const uint16_t* q;    // [batch*heads][q_rows][depth] bf16
+    const uint16_t* k;    // [batch*kv_heads][kv_len][depth] bf16
+    const uint16_t* v;
+    float* o;             // [P][rows][depth]
+    float* m;             // [P][rows]
+    float* l;             // [P][rows]
+    int64_t batch, heads, kv_heads, q_rows, kv_len;
+    int32_t depth, P;
+    float scale;
+    hipStream_t stream;
+};
+
 rr_status launch_reduce(const rr_plan& plan, const ReduceLaunch& a);
 rr_status launch_reduce_identity(const ReduceLaunch& a);  // cols == 0
 rr_status launch_softmax(const rr_plan& plan, const SoftmaxLaunch& a);
 rr_status launch_merge(const MergeLaunch& a);
+rr_status launch_attention(const AttentionLaunch& a);
 rr_status launch_layernorm(const rr_plan& plan, const LayernormLaunch& a);
 rr_status launch_reduce_axis(const rr_plan& plan, const AxisLaunch& a);
 rr_status launch_fill_zero(void* p, size_t bytes, hipStream_t stream);

@@ -329,6 +329,31 @@ def test_entry_points_validate_before_touching_the_device():
     assert lib.rr_splitk_lse_merge(None, None, None, None, 8, 4, 8, 1.0, 2, None) == 1
 
 
+def test_attention_partials_validate_before_touching_the_device():
+    lib = ctypes.CDLL(rr.lib_path())
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.rr_splitk_attention_partials.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                                 i32, i32, ctypes.c_float, vp]
+    f = lib.rr_splitk_attention_partials
+    ok = dict(batch=1, heads=4, kv_heads=2, q_rows=8, kv_len=16, depth=128, P=2, scale=0.1)
+
+    def call(ptr=16, **kw):
+        a = dict(ok, **kw)
+        return f(ptr, ptr, ptr, ptr, ptr, ptr, a["batch"], a["heads"], a["kv_heads"], a["q_rows"],
+                 a["kv_len"], a["depth"], a["P"], a["scale"], None)
+
+    assert call(depth=96) == 2                     # depth 64 or 128 only
+    assert call(heads=3) == 2                      # heads % kv_heads
+    assert call(kv_heads=0) == 2
+    assert call(P=0) == 2 and call(P=257) == 2
+    assert call(scale=float("nan")) == 2 and call(scale=float("inf")) == 2
+    assert call(q_rows=-1) == 2 and call(kv_len=-1) == 2
+    assert call(q_rows=1 << 23) == 2               # q_rows * depth * 2 >= 2^31
+    assert call(ptr=None) == 1                     # NULL
+    assert call(ptr=8) == 2                        # misaligned
+    assert call(ptr=None, q_rows=0) == 0           # nothing to do
+
+
 def test_stream_reference_validates_before_touching_the_device():
     lib = ctypes.CDLL(rr.lib_path())
     vp = ctypes.c_void_p
