@@ -152,3 +152,30 @@ def test_partials_config_full_size_sampled_heads():
         assert np.all(np.abs(lg - l_r) / l_r <= 2 * bs + 1024 * 2.0 ** -24 + 2.0 ** -22), (b, h)
         tol = (2.0 ** -8 + 2.0 ** -13 + 2 * bs)[:, :, None] * o_a + 1e-6
         assert np.all(np.abs(og - o_r) <= tol), (b, h)
+
+
+def _random_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        kv_heads = int(rng.choice([1, 2]))
+        heads = kv_heads * int(rng.choice([1, 2, 3]))
+        cases.append((i, int(rng.integers(1, 3)), heads, kv_heads, int(rng.integers(1, 300)),
+                      int(rng.integers(0, 2000)), int(rng.choice([64, 128])),
+                      int(rng.integers(1, 13)), float(rng.uniform(-0.3, 0.3))))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(12, 958),
+                         ids=lambda c: "t%d_b%dh%dk%dq%dn%dd%dP%d" % c[:8])
+def test_partials_random_shapes(case):
+    i, batch, heads, kv_heads, q_rows, kv_len, depth, P, scale = case
+    q, k, v = synth.attention(960 + i, batch=batch, heads=heads, kv_heads=kv_heads, q_rows=q_rows,
+                              kv_len=kv_len, depth=depth)
+    if kv_len == 0:
+        o, m, l = rr.splitk_attention_partials(_bf16_tensor(q), _bf16_tensor(k), _bf16_tensor(v), P,
+                                               scale)
+        torch.cuda.synchronize()
+        assert torch.all(m == -math.inf) and torch.all(l == 0) and torch.all(o == 0)
+        return
+    _check_partials(q, k, v, P, scale, "random %r" % (case,))

@@ -35,6 +35,8 @@ def test_graph_replays_match_eager_bit_for_bit():
     x_ax = to_gpu(synth.normal_f32(48, (1, 1 << 16, 64)))             # axis split-K
     o, m, l = synth.lse_merge(49, P=8, batch=1, heads=4, q_rows=64, depth=128)
     o, m, l = to_gpu(o), to_gpu(m), to_gpu(l)
+    aq, ak, av = (to_gpu(a) for a in synth.attention(50, batch=1, heads=4, kv_heads=2, q_rows=130,
+                                                     kv_len=777, depth=128))
 
     outs = {
         "long_sum": torch.empty(16, device=dev),
@@ -48,6 +50,8 @@ def test_graph_replays_match_eager_bit_for_bit():
         "ln_splitk": torch.empty_like(x_lnk),
         "axis": torch.empty((1, 64), device=dev),
         "merge": torch.empty((1, 4, 64, 128), dtype=torch.bfloat16, device=dev),
+        "attn": {"o": torch.empty((4, 520, 128), device=dev), "m": torch.empty((4, 520), device=dev),
+                 "l": torch.empty((4, 520), device=dev)},
     }
 
     def run_all():
@@ -61,6 +65,8 @@ def test_graph_replays_match_eager_bit_for_bit():
         rr.layernorm_rows(x_lnk, eps=1e-5, out=outs["ln_splitk"])
         rr.reduce_axis(x_ax, 1, "sum", out=outs["axis"])
         rr.splitk_lse_merge(o, m, l, 1.0, torch.bfloat16, out=outs["merge"])
+        rr.splitk_attention_partials(aq, ak, av, 4, out=(outs["attn"]["o"], outs["attn"]["m"],
+                                                         outs["attn"]["l"]))
 
     def snapshot():
         flat = {}
