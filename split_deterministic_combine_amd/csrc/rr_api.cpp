@@ -274,10 +274,15 @@ extern "C" rr_status rr_splitk_attention_partials(const void* q, const void* k, 
         kv_len < 0 || P < 1 || P > RR_MERGE_MAX_P || (depth != 64 && depth != 128) ||
         !isfinite(scale))
         return RR_ERR_SHAPE;
-    if (q_rows * (int64_t)depth * 2 > (int64_t)INT32_MAX) return RR_ERR_SHAPE;
+    if (q_rows > (int64_t)INT32_MAX / (2 * depth)) return RR_ERR_SHAPE;  // q_rows*depth*2 < 2^31
+    // one workgroup per (128 query rows, partition, head): the grid must fit
+    // in 31 bits; checked factor by factor so no product can overflow
     const int64_t q_tiles = (q_rows + rr::kAttnRows - 1) / rr::kAttnRows;
-    if (q_tiles * P * batch * heads > (int64_t)INT32_MAX) return RR_ERR_SHAPE;
-    if (batch * heads * q_rows == 0) return RR_OK;
+    if (q_rows == 0 || batch == 0) return RR_OK;
+    int64_t work = q_tiles * P;                      // <= 2^24 * 256
+    if (batch > (int64_t)INT32_MAX / work) return RR_ERR_SHAPE;
+    work *= batch;
+    if (heads > (int64_t)INT32_MAX / work) return RR_ERR_SHAPE;
     if (!q || !o_part || !m_part || !l_part || (kv_len > 0 && (!k || !v))) return RR_ERR_NULL;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o_part, 16))
         return RR_ERR_SHAPE;

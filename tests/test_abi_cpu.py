@@ -349,6 +349,8 @@ def test_attention_partials_validate_before_touching_the_device():
     assert call(scale=float("nan")) == 2 and call(scale=float("inf")) == 2
     assert call(q_rows=-1) == 2 and call(kv_len=-1) == 2
     assert call(q_rows=1 << 23) == 2               # q_rows * depth * 2 >= 2^31
+    assert call(batch=1 << 40, heads=1 << 40, kv_heads=1) == 2   # grid beyond 31 bits, no overflow
+    assert call(batch=1 << 62, P=256) == 2
     assert call(ptr=None) == 1                     # NULL
     assert call(ptr=8) == 2                        # misaligned
     assert call(ptr=None, q_rows=0) == 0           # nothing to do
