@@ -15,6 +15,7 @@ timed on their own workloads and reported under "next_rows":
   axis_cols     f32 column sums of [16384, 16384] (non-last axis, split-K)
   attention     split-K attention partials: bf16 q [8, 32, 128, 128] over 8192
                 keys in 8 partitions -> float32 O, m, l (matrix cores)
+  attention_merged  the same, then the LSE merge of the partials -> bf16
 
 Inputs are resident in HBM before timing.  Buffer sets rotate from one step
 to the next so that the data touched by consecutive launches exceeds the
@@ -133,7 +134,11 @@ NEXT_BYTES = {"multi_long": 16 * (1 << 24) * 4 + 3 * 16 * 4,
               "axis_cols": AXIS_COLS[0] * AXIS_COLS[1] * 4 + AXIS_COLS[1] * 4,
               "softmax_long": 16 * (1 << 22) * 2 * 2,
               "layernorm": 16384 * 4096 * 2 * 2 + 2 * 4096 * 4 + 2 * 16384 * 4,
-              "attention": _attn_bytes()}
+              "attention": _attn_bytes(),
+              # q, k, v read and bf16 attention written once (the partials are internal)
+              "attention_merged": ATTN[0] * ATTN[1] * ATTN[2] * ATTN[3] * 2
+                                  + 2 * ATTN[0] * ATTN[1] * ATTN[4] * ATTN[3] * 2
+                                  + ATTN[0] * ATTN[1] * ATTN[2] * ATTN[3] * 2}
 STEP_OPS = ("short_sum", "short_max", "softmax", "long_sum", "long_max", "merge")
 COPY_BYTES = 512 << 20
 
@@ -355,6 +360,7 @@ def main():
         arows = ab * ah * asq
         dx["attn_out"] = (torch.empty((ap, arows, ad), device=dev), torch.empty((ap, arows), device=dev),
                           torch.empty((ap, arows), device=dev))
+        dx["attn_merged"] = torch.empty((arows, ad), dtype=torch.bfloat16, device=dev)
     y_short_sum = torch.empty(1048576, dtype=torch.float32, device=dev)
     y_short_max = torch.empty(1048576, dtype=torch.float32, device=dev)
     y_long_f = torch.empty(16, dtype=torch.float32, device=dev)
@@ -386,6 +392,10 @@ def main():
                                                  rstd_out=dx["layernorm_stats"][i % 4][1]),
         "attention": lambda i: rr.splitk_attention_partials(*dx["attn_qkv"], ATTN[5],
                                                             out=dx["attn_out"]),
+        # the whole split-K attention: the partials above, then their LSE merge
+        "attention_merged": lambda i: rr.splitk_lse_merge(
+            *rr.splitk_attention_partials(*dx["attn_qkv"], ATTN[5], out=dx["attn_out"]), 1.0,
+            torch.bfloat16, out=dx["attn_merged"]),
     }
     only = args.only.split(",") if args.only else None
     names = [n for n in ops if only is None or n in only]
@@ -606,6 +616,17 @@ def main():
                 "flops": _attn_flops(),
                 "TFLOPs": round(_attn_flops() / t_s / 1e12, 1),
                 "pct_peak_bf16_mfma": round(100 * _attn_flops() / t_s / 2.5e15, 1)})
+        if "attention_merged" in next_rows:
+            ab, ah, asq, ad, an, ap = ATTN
+            t_s = next_rows["attention_merged"]["ms_mean"] * 1e-3
+            next_rows["attention_merged"].update({
+                "config": "split-K attention end to end: the partials above, then their LSE merge "
+                          "into bf16 [%d, %d, %d, %d] (two launches)" % (ab, ah, asq, ad),
+                "kernels": [KERNEL_OF_OP["attention"], KERNEL_OF_OP["merge"]],
+                "flops": _attn_flops(),
+                "TFLOPs": round(_attn_flops() / t_s / 1e12, 1),
+                "bytes_note": "bytes = q, k, v read once and the bf16 output written once; the "
+                              "partials (130 MiB) go through HBM between the launches"})
         if "softmax_long" in next_rows:
             r, c = SOFTMAX_LONG
             next_rows["softmax_long"].update({
