@@ -16,6 +16,9 @@ timed on their own workloads and reported under "next_rows":
   attention     split-K attention partials: bf16 q [8, 32, 128, 128] over 8192
                 keys in 8 partitions -> float32 O, m, l (matrix cores)
   attention_merged  the same, then the LSE merge of the partials -> bf16
+  attention_fused   the same in one launch: the last workgroup of each query
+                tile folds the partials in partition order -> bf16 (the
+                same bits as attention_merged)
 
 Inputs are resident in HBM before timing.  Buffer sets rotate from one step
 to the next so that the data touched by consecutive launches exceeds the
@@ -70,7 +73,8 @@ KERNEL_OF_OP = {
     "axis_cols_partial": "k_reduce_axis_partial<rr::SumF32, 4>",
     "axis_cols_fold": "k_reduce_axis_fold<rr::SumF32>",
     # reference streams of known size (not ops of the step): rr_test_stream
-    "attention": "k_attn_staged<128, 32, 4>",
+    "attention": "k_attn_staged<128, 32, 4, false, float>",
+    "attention_fused": "k_attn_staged<128, 32, 4, true, unsigned short>",
     "stream_read": "k_stream<0>",
     "stream_write": "k_stream<1>",
 }
@@ -86,6 +90,12 @@ def _attn_bytes():
     """q, k, v read once (bf16); O (float32), m and l written once."""
     b, h, sq, d, n, p = ATTN
     return b * h * sq * d * 2 + 2 * b * h * n * d * 2 + p * b * h * sq * d * 4 + 2 * p * b * h * sq * 4
+
+
+def _attn_fused_bytes():
+    """q, k, v read once and the bf16 attention output written once."""
+    b, h, sq, d, n, _ = ATTN
+    return b * h * sq * d * 2 + 2 * b * h * n * d * 2 + b * h * sq * d * 2
 
 
 def _attn_flops():
@@ -124,6 +134,9 @@ def _algo_bytes():
         "axis_cols_partial": ar * ac * 4 + g_ax * ac * 8,
         "axis_cols_fold": g_ax * ac * 8 + ac * 4,
         "attention": _attn_bytes(),
+        # one launch: q, k, v read once and the bf16 output written once (the
+        # partials pass through the device-coherent level, not counted)
+        "attention_fused": _attn_fused_bytes(),
         "stream_read": 1 << 30,
         "stream_write": 1 << 30,
     }
@@ -136,9 +149,8 @@ NEXT_BYTES = {"multi_long": 16 * (1 << 24) * 4 + 3 * 16 * 4,
               "layernorm": 16384 * 4096 * 2 * 2 + 2 * 4096 * 4 + 2 * 16384 * 4,
               "attention": _attn_bytes(),
               # q, k, v read and bf16 attention written once (the partials are internal)
-              "attention_merged": ATTN[0] * ATTN[1] * ATTN[2] * ATTN[3] * 2
-                                  + 2 * ATTN[0] * ATTN[1] * ATTN[4] * ATTN[3] * 2
-                                  + ATTN[0] * ATTN[1] * ATTN[2] * ATTN[3] * 2}
+              "attention_merged": _attn_fused_bytes(),
+              "attention_fused": _attn_fused_bytes()}
 STEP_OPS = ("short_sum", "short_max", "softmax", "long_sum", "long_max", "merge")
 COPY_BYTES = 512 << 20
 
@@ -361,6 +373,9 @@ def main():
         dx["attn_out"] = (torch.empty((ap, arows, ad), device=dev), torch.empty((ap, arows), device=dev),
                           torch.empty((ap, arows), device=dev))
         dx["attn_merged"] = torch.empty((arows, ad), dtype=torch.bfloat16, device=dev)
+        dx["attn_fused"] = torch.empty((ab, ah, asq, ad), dtype=torch.bfloat16, device=dev)
+        dx["attn_ws"] = torch.zeros(rr.splitk_attention_workspace_bytes(ab, ah, ah, asq, an, ad, ap),
+                                    dtype=torch.uint8, device=dev)
     y_short_sum = torch.empty(1048576, dtype=torch.float32, device=dev)
     y_short_max = torch.empty(1048576, dtype=torch.float32, device=dev)
     y_long_f = torch.empty(16, dtype=torch.float32, device=dev)
@@ -396,6 +411,10 @@ def main():
         "attention_merged": lambda i: rr.splitk_lse_merge(
             *rr.splitk_attention_partials(*dx["attn_qkv"], ATTN[5], out=dx["attn_out"]), 1.0,
             torch.bfloat16, out=dx["attn_merged"]),
+        # both in one launch, the partials combined by the last workgroup of each tile
+        "attention_fused": lambda i: rr.splitk_attention(*dx["attn_qkv"], ATTN[5],
+                                                         out=dx["attn_fused"],
+                                                         workspace=dx["attn_ws"]),
     }
     only = args.only.split(",") if args.only else None
     names = [n for n in ops if only is None or n in only]
@@ -458,6 +477,10 @@ def main():
             mg = dx["attn_out"][1][:, rows].cpu().numpy()
             ok &= bool(np.all(np.abs(og - o_r) <= (2.0 ** -8 + 2.0 ** -12) * o_a + 1e-6))
             ok &= bool(np.all(np.abs(mg - m_r) <= 1e-5 * (1 + np.abs(m_r))))
+        if "attention_fused" in next_names and "attention_merged" in next_names:
+            # the one-launch attention gives the bits of partials + merge
+            ok &= bool(torch.equal(dx["attn_fused"].view(-1).view(torch.int16),
+                                   dx["attn_merged"].view(-1).view(torch.int16)))
         # sampled rows of the full-size outputs of the pass above (no extra launches)
         xs = host["short"][:4096]
         if "short_sum" in names:
@@ -627,6 +650,18 @@ def main():
                 "TFLOPs": round(_attn_flops() / t_s / 1e12, 1),
                 "bytes_note": "bytes = q, k, v read once and the bf16 output written once; the "
                               "partials (130 MiB) go through HBM between the launches"})
+        if "attention_fused" in next_rows:
+            ab, ah, asq, ad, an, ap = ATTN
+            t_s = next_rows["attention_fused"]["ms_mean"] * 1e-3
+            next_rows["attention_fused"].update({
+                "config": "split-K attention in one launch: the partials of every (head, 128 "
+                          "query rows) folded in partition order by the last of its %d "
+                          "workgroups into bf16 [%d, %d, %d, %d]" % (ap, ab, ah, asq, ad),
+                "kernels": [KERNEL_OF_OP["attention_fused"]],
+                "flops": _attn_flops(),
+                "TFLOPs": round(_attn_flops() / t_s / 1e12, 1),
+                "bytes_note": "bytes = q, k, v read once and the bf16 output written once; the "
+                              "partials go through the device-coherent level once each way"})
         if "softmax_long" in next_rows:
             r, c = SOFTMAX_LONG
             next_rows["softmax_long"].update({

@@ -1,7 +1,7 @@
 /*
  * rr.h -- deterministic row reductions on AMD Instinct MI355X (gfx950).
  *
- * A C ABI over hand-written HIP kernels.  Seven operations:
+ * A C ABI over hand-written HIP kernels.  Eight operations:
  *
  *   rr_reduce_rows       sum / max / min of every row over its last axis, on
  *                        float32 or int32 values, through one of five tiers
@@ -19,6 +19,9 @@
  *                        the producer of those partials: attention of every
  *                        query row over each of P partitions of the keys, with
  *                        the partition's row max and row sum (matrix cores).
+ *   rr_splitk_attention  both in one launch: the last workgroup of each
+ *                        query tile to finish folds its P partials in
+ *                        partition order into the output rows.
  *
  * Sources (Modular API pages, cited by title and section):
  *   "reduce" (algorithm.gpu.rowwise): the tier semantics list and the
@@ -408,6 +411,49 @@ rr_status rr_splitk_attention_partials(const void* q, const void* k, const void*
                                        float* m_part, float* l_part, int64_t batch, int64_t heads,
                                        int64_t kv_heads, int64_t q_rows, int64_t kv_len,
                                        int32_t depth, int32_t P, float scale, void* stream);
+
+/*
+ * rr_splitk_attention -- the whole split-K attention in one launch: the
+ * partials of rr_splitk_attention_partials, combined as rr_splitk_lse_merge
+ * combines them (scale 1.0), into one output row per query row.
+ * "fa4_splitk_reduce_scatter_write" (the partials and their LSE weights) with
+ * the rank-ordered fold of "cluster_allreduce": every (head, 128 query rows,
+ * partition) workgroup writes its partial into the workspace and takes a
+ * ticket for its (head, query rows) group; the workgroup that draws the last
+ * ticket folds the group's P partials in ascending partition order.  The
+ * result is bit-identical to rr_splitk_attention_partials followed by
+ * rr_splitk_lse_merge(..., scale 1.0, out_dtype) on the same inputs, whatever
+ * order the workgroups run in.
+ *
+ *   q, k, v     as rr_splitk_attention_partials
+ *   out         device, out_dtype [batch][heads][q_rows][depth] (written),
+ *               16-byte aligned
+ *   out_dtype   RR_BF16 (rounded to nearest even) or RR_F32
+ *   P           1 .. depth / 8 (the fold keeps P (m, l, weight) cells per row
+ *               in LDS)
+ *   workspace, workspace_bytes
+ *               device, 16-byte aligned, at least
+ *               rr_splitk_attention_workspace_bytes; owned by the caller.  Its
+ *               first bytes are the tickets, which must be zero before the
+ *               first call (rr_workspace_reset over the whole workspace) and
+ *               which every completed call leaves zero; the rest holds the
+ *               partials and is overwritten by every call, so a workspace
+ *               that then serves rr_reduce_rows must be reset first.  One
+ *               workspace must not serve two calls in flight.
+ * Errors (nothing launched): RR_ERR_SHAPE (as rr_splitk_attention_partials,
+ * and P > depth / 8), RR_ERR_DTYPE, RR_ERR_NULL, RR_ERR_WORKSPACE;
+ * batch*heads*q_rows == 0 is a no-op.
+ */
+rr_status rr_splitk_attention(const void* q, const void* k, const void* v, void* out,
+                              rr_dtype out_dtype, int64_t batch, int64_t heads, int64_t kv_heads,
+                              int64_t q_rows, int64_t kv_len, int32_t depth, int32_t P,
+                              float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace rr_splitk_attention needs for this shape (0 for a no-op
+ * shape); the same shape errors as rr_splitk_attention.  Host only. */
+rr_status rr_splitk_attention_workspace_bytes(int64_t batch, int64_t heads, int64_t kv_heads,
+                                              int64_t q_rows, int64_t kv_len, int32_t depth,
+                                              int32_t P, size_t* bytes_out);
 
 /* Bytes of workspace rr_reduce_rows (RR_KIND_REDUCE), rr_softmax_rows
  * (RR_KIND_SOFTMAX, dtype = x_dtype) or rr_layernorm_rows (RR_KIND_LAYERNORM,

@@ -17,6 +17,8 @@ Operations (names as in the C ABI):
   splitk_attention_partials
                      the producer of those partials (attention over each of P
                      partitions of the keys, on the matrix cores)
+  splitk_attention   both in one launch, the partials folded in partition
+                     order by the last workgroup of each query tile
 """
 import ctypes
 import math
@@ -27,7 +29,7 @@ import torch
 
 __all__ = [
     "RRError", "reduce_rows", "reduce_rows_multi", "reduce_axis", "plan_axis", "softmax_rows", "layernorm_rows", "splitk_lse_merge",
-    "splitk_attention_partials",
+    "splitk_attention_partials", "splitk_attention", "splitk_attention_workspace_bytes",
     "plan_reduce", "plan_softmax", "plan_layernorm", "select_tier", "workspace_bytes", "workspace_reset", "device_cu_count",
     "version", "lib_path", "TIERS", "OPS",
 ]
@@ -89,6 +91,10 @@ def _load():
         lib.rr_splitk_lse_merge.argtypes = [vp, vp, vp, vp, i32, i64, i32, ctypes.c_float, st, vp]
         lib.rr_splitk_attention_partials.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                                      i64, i32, i32, ctypes.c_float, vp]
+        lib.rr_splitk_attention.argtypes = [vp, vp, vp, vp, st, i64, i64, i64, i64, i64, i32, i32,
+                                            ctypes.c_float, vp, ctypes.c_size_t, vp]
+        lib.rr_splitk_attention_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32, i32,
+                                                            ctypes.POINTER(ctypes.c_size_t)]
         lib.rr_reduce_axis.argtypes = [vp, vp, i64, i64, i64, st, st, st, vp, ctypes.c_size_t, vp]
         lib.rr_plan_axis.argtypes = [i64, i64, i64, st, st, st, i32, ctypes.POINTER(_Plan)]
         lib.rr_layernorm_rows.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, st, st, st,
@@ -111,7 +117,8 @@ def _load():
                      "rr_plan_softmax", "rr_layernorm_rows", "rr_plan_layernorm",
                      "rr_workspace_bytes", "rr_select_tier",
                      "rr_workspace_reset", "rr_device_cu_count", "rr_test_stream",
-                     "rr_splitk_attention_partials"):
+                     "rr_splitk_attention_partials", "rr_splitk_attention",
+                     "rr_splitk_attention_workspace_bytes"):
             getattr(lib, name).restype = st
         _lib = lib
     return _lib
@@ -215,7 +222,9 @@ def _softmax_workspace_need(rows, cols, xdt, ydt, tier, cu):
 
 # split-K workspaces, one per (kind, device, stream).  A reduction's tickets
 # reset themselves, so its workspace stays zero between calls on its stream;
-# the softmax workspace holds only pairs that each call writes before reading.
+# the softmax workspace holds only pairs that each call writes before reading;
+# the fused attention's tickets reset themselves and its partials are
+# rewritten by every call.
 _workspaces = {}
 
 
@@ -467,15 +476,7 @@ def splitk_attention_partials(q, k, v, P, scale=None, out=None):
     ``scale`` defaults to 1/sqrt(depth); ``out`` may give the three tensors.
     """
     lib = _load()
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.bfloat16:
-            raise ValueError("%s must be a bfloat16 GPU tensor" % n)
-        if not t.is_contiguous() or t.dim() != 4:
-            raise ValueError("%s must be a contiguous 4-d tensor" % n)
-    batch, heads, q_rows, depth = q.shape
-    kb, kv_heads, kv_len, kd = k.shape
-    if kb != batch or kd != depth or tuple(v.shape) != tuple(k.shape):
-        raise ValueError("k and v must be [batch, kv_heads, kv_len, depth] matching q")
+    batch, heads, kv_heads, q_rows, kv_len, depth = _attention_shapes(q, k, v)
     rows = batch * heads * q_rows
     if scale is None:
         scale = 1.0 / math.sqrt(depth)
@@ -495,6 +496,63 @@ def splitk_attention_partials(q, k, v, P, scale=None, out=None):
             ctypes.c_void_p(m.data_ptr()), ctypes.c_void_p(l.data_ptr()), batch, heads, kv_heads,
             q_rows, kv_len, depth, int(P), float(scale), _stream_ptr(q.device)))
     return o, m, l
+
+
+def _attention_shapes(q, k, v):
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.bfloat16:
+            raise ValueError("%s must be a bfloat16 GPU tensor" % n)
+        if not t.is_contiguous() or t.dim() != 4:
+            raise ValueError("%s must be a contiguous 4-d tensor" % n)
+    batch, heads, q_rows, depth = q.shape
+    kb, kv_heads, kv_len, kd = k.shape
+    if kb != batch or kd != depth or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [batch, kv_heads, kv_len, depth] matching q")
+    return batch, heads, kv_heads, q_rows, kv_len, depth
+
+
+def splitk_attention_workspace_bytes(batch, heads, kv_heads, q_rows, kv_len, depth, P):
+    """Bytes of workspace splitk_attention needs (host only)."""
+    n = ctypes.c_size_t(0)
+    _check(_load().rr_splitk_attention_workspace_bytes(batch, heads, kv_heads, q_rows, kv_len,
+                                                       depth, int(P), ctypes.byref(n)))
+    return n.value
+
+
+def splitk_attention(q, k, v, P, scale=None, out_dtype=torch.bfloat16, out=None, workspace=None):
+    """Split-K attention in one launch: softmax(scale q k^T) v computed over P
+    partitions of the keys and combined in partition order (1 <= P <= depth/8).
+
+    Shapes as splitk_attention_partials; returns [batch, heads, q_rows, depth]
+    in ``out_dtype`` (bfloat16 or float32), bit-identical to
+    ``splitk_lse_merge(*splitk_attention_partials(q, k, v, P, scale), 1.0,
+    out_dtype)``.  ``workspace`` (uint8, zeroed before its first use) defaults
+    to one cached per device and stream.
+    """
+    lib = _load()
+    batch, heads, kv_heads, q_rows, kv_len, depth = _attention_shapes(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(depth)
+    if out is None:
+        out = torch.empty((batch, heads, q_rows, depth), dtype=out_dtype, device=q.device)
+    if out.dtype != out_dtype or not out.is_contiguous() or out.numel() != batch * heads * q_rows * depth:
+        raise ValueError("out must be a contiguous %s tensor of %d elements"
+                         % (out_dtype, batch * heads * q_rows * depth))
+    need = splitk_attention_workspace_bytes(batch, heads, kv_heads, q_rows, kv_len, depth, P)
+    with _OnDevice(q.device):
+        stream = _stream_ptr(q.device)
+        if workspace is None:
+            ws = _workspace("attention", q.device, stream.value, need) if need else None
+        else:
+            ws = workspace
+        ws_ptr = ctypes.c_void_p(ws.data_ptr()) if ws is not None else None
+        ws_len = ws.numel() * ws.element_size() if ws is not None else 0
+        _check(lib.rr_splitk_attention(
+            ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+            ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+            _dtype_code(out_dtype), batch, heads, kv_heads, q_rows, kv_len, depth, int(P),
+            float(scale), ws_ptr, ws_len, stream))
+    return out
 
 
 def _plan_dict(plan):

@@ -264,37 +264,123 @@ extern "C" rr_status rr_splitk_lse_merge(const float* o_part, const float* m_par
     return rr::launch_merge(a);
 }
 
-extern "C" rr_status rr_splitk_attention_partials(const void* q, const void* k, const void* v,
-                                                  float* o_part, float* m_part, float* l_part,
-                                                  int64_t batch, int64_t heads, int64_t kv_heads,
-                                                  int64_t q_rows, int64_t kv_len, int32_t depth,
-                                                  int32_t P, float scale, void* stream)
+// Shape checks common to the attention calls; *work_out is the grid size
+// (one workgroup per 128 query rows, partition and head), 0 for a no-op.
+static rr_status check_attention(int64_t batch, int64_t heads, int64_t kv_heads, int64_t q_rows,
+                                 int64_t kv_len, int32_t depth, int32_t P, float scale,
+                                 int64_t* work_out)
 {
+    *work_out = 0;
     if (batch < 0 || heads < 1 || kv_heads < 1 || heads % kv_heads != 0 || q_rows < 0 ||
         kv_len < 0 || P < 1 || P > RR_MERGE_MAX_P || (depth != 64 && depth != 128) ||
         !isfinite(scale))
         return RR_ERR_SHAPE;
     if (q_rows > (int64_t)INT32_MAX / (2 * depth)) return RR_ERR_SHAPE;  // q_rows*depth*2 < 2^31
-    // one workgroup per (128 query rows, partition, head): the grid must fit
-    // in 31 bits; checked factor by factor so no product can overflow
+    // the grid must fit in 31 bits; checked factor by factor so no product
+    // can overflow
     const int64_t q_tiles = (q_rows + rr::kAttnRows - 1) / rr::kAttnRows;
     if (q_rows == 0 || batch == 0) return RR_OK;
     int64_t work = q_tiles * P;                      // <= 2^24 * 256
     if (batch > (int64_t)INT32_MAX / work) return RR_ERR_SHAPE;
     work *= batch;
     if (heads > (int64_t)INT32_MAX / work) return RR_ERR_SHAPE;
+    *work_out = work * heads;
+    return RR_OK;
+}
+
+extern "C" rr_status rr_splitk_attention_partials(const void* q, const void* k, const void* v,
+                                                  float* o_part, float* m_part, float* l_part,
+                                                  int64_t batch, int64_t heads, int64_t kv_heads,
+                                                  int64_t q_rows, int64_t kv_len, int32_t depth,
+                                                  int32_t P, float scale, void* stream)
+{
+    int64_t work = 0;
+    rr_status st = check_attention(batch, heads, kv_heads, q_rows, kv_len, depth, P, scale, &work);
+    if (st != RR_OK || work == 0) return st;
     if (!q || !o_part || !m_part || !l_part || (kv_len > 0 && (!k || !v))) return RR_ERR_NULL;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o_part, 16))
         return RR_ERR_SHAPE;
     rr::AttentionLaunch a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                           static_cast<const uint16_t*>(v), o_part, m_part, l_part, batch, heads,
-                          kv_heads, q_rows, kv_len, depth, P, scale, as_stream(stream)};
+                          kv_heads, q_rows, kv_len, depth, P, scale, nullptr, RR_F32, nullptr,
+                          as_stream(stream)};
     if (log_enabled())
         fprintf(stderr,
                 "rr: rr_splitk_attention_partials batch=%lld heads=%lld kv_heads=%lld "
                 "q_rows=%lld kv_len=%lld depth=%d P=%d workgroups=%lld\n",
                 (long long)batch, (long long)heads, (long long)kv_heads, (long long)q_rows,
-                (long long)kv_len, depth, P, (long long)(q_tiles * P * batch * heads));
+                (long long)kv_len, depth, P, (long long)work);
+    return rr::launch_attention(a);
+}
+
+// Workspace of the fused call: the tickets (one per group = head and 128
+// query rows), padded to 256 bytes, then O_p, m_p and l_p group-major,
+// [group][P][128 rows] (the kernel's fold reads a group's partials from one
+// range).
+namespace {
+struct AttnWorkspace {
+    uint64_t tickets, o, m, l, total;
+};
+AttnWorkspace attn_workspace(int64_t batch, int64_t heads, int64_t q_rows, int32_t depth, int32_t P)
+{
+    const uint64_t groups = (uint64_t)batch * (uint64_t)heads *
+                            (uint64_t)((q_rows + rr::kAttnRows - 1) / rr::kAttnRows);
+    const uint64_t cells = groups * (uint64_t)P * rr::kAttnRows;
+    AttnWorkspace w;
+    w.tickets = 0;
+    w.o = (groups * 4 + 255) / 256 * 256;
+    w.m = w.o + cells * (uint64_t)depth * 4;
+    w.l = w.m + cells * 4;
+    w.total = w.l + cells * 4;
+    return w;
+}
+}  // namespace
+
+extern "C" rr_status rr_splitk_attention_workspace_bytes(int64_t batch, int64_t heads,
+                                                         int64_t kv_heads, int64_t q_rows,
+                                                         int64_t kv_len, int32_t depth, int32_t P,
+                                                         size_t* bytes_out)
+{
+    if (!bytes_out) return RR_ERR_NULL;
+    int64_t work = 0;
+    rr_status st = check_attention(batch, heads, kv_heads, q_rows, kv_len, depth, P, 1.0f, &work);
+    if (st != RR_OK) return st;
+    if (P > depth / 8) return RR_ERR_SHAPE;
+    *bytes_out = work == 0 ? 0 : (size_t)attn_workspace(batch, heads, q_rows, depth, P).total;
+    return RR_OK;
+}
+
+extern "C" rr_status rr_splitk_attention(const void* q, const void* k, const void* v, void* out,
+                                         rr_dtype out_dtype, int64_t batch, int64_t heads,
+                                         int64_t kv_heads, int64_t q_rows, int64_t kv_len,
+                                         int32_t depth, int32_t P, float scale, void* workspace,
+                                         size_t workspace_bytes, void* stream)
+{
+    int64_t work = 0;
+    rr_status st = check_attention(batch, heads, kv_heads, q_rows, kv_len, depth, P, scale, &work);
+    if (st != RR_OK) return st;
+    if (P > depth / 8) return RR_ERR_SHAPE;          // the fold's (row, partition) cells fit in LDS
+    if (out_dtype != RR_BF16 && out_dtype != RR_F32) return RR_ERR_DTYPE;
+    if (work == 0) return RR_OK;
+    if (!q || !out || (kv_len > 0 && (!k || !v))) return RR_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+        return RR_ERR_SHAPE;
+    const AttnWorkspace w = attn_workspace(batch, heads, q_rows, depth, P);
+    if (!workspace || workspace_bytes < w.total || !aligned(workspace, 16))
+        return RR_ERR_WORKSPACE;
+    char* ws = static_cast<char*>(workspace);
+    rr::AttentionLaunch a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                          static_cast<const uint16_t*>(v), reinterpret_cast<float*>(ws + w.o),
+                          reinterpret_cast<float*>(ws + w.m), reinterpret_cast<float*>(ws + w.l),
+                          batch, heads, kv_heads, q_rows, kv_len, depth, P, scale, out, out_dtype,
+                          reinterpret_cast<uint32_t*>(ws + w.tickets), as_stream(stream)};
+    if (log_enabled())
+        fprintf(stderr,
+                "rr: rr_splitk_attention batch=%lld heads=%lld kv_heads=%lld q_rows=%lld "
+                "kv_len=%lld depth=%d P=%d out=%s workgroups=%lld\n",
+                (long long)batch, (long long)heads, (long long)kv_heads, (long long)q_rows,
+                (long long)kv_len, depth, P, out_dtype == RR_BF16 ? "bf16" : "f32",
+                (long long)work);
     return rr::launch_attention(a);
 }
 

@@ -33,6 +33,7 @@
 #include "rr_device.hpp"
 #include "rr_launch.hpp"
 #include "rr_launch_util.hpp"
+#include "rr_merge_math.hpp"
 #include "rr_rowio.hpp"
 
 namespace rr {
@@ -166,12 +167,68 @@ __device__ __forceinline__ void stage_barrier()
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <int D, int KB, int NS>
+// The fold of a fused group's O partials: out_rows[r][d] = sum over p of
+// cell[r][p] * O_p[r][d] in ascending p (merge_accumulate), for r < nr.  A
+// thread owns 4 columns of rows r0, r0 + RPP, ...; it issues the loads of RB
+// whole rows (RB * PC cells, PC >= P a compile-time bound) before folding any
+// of them, so that a round trip to the device-coherent level is paid once
+// per RB rows.  Loads of cells p >= P are not issued.
+template <int D, int PC, class YT>
+__device__ __forceinline__ void fold_group_rows(const __amdgpu_buffer_rsrc_t rg,
+                                                const double* cell, YT* out_rows, int32_t P,
+                                                int nr)
+{
+    constexpr int LPR = D / 4;                          // lanes per row, 4 columns each
+    constexpr int RPP = kBlockThreads / LPR;            // rows per pass
+    constexpr int kCells = 32;                          // 16-byte loads in flight per thread
+    constexpr int RB = kCells / PC < kAttnRows / RPP ? kCells / PC : kAttnRows / RPP;
+    const int li = threadIdx.x % LPR;
+    const int r0 = threadIdx.x / LPR;
+    const int lane_off = (r0 * D + 4 * li) * 4;
+    for (int kb = 0; r0 + kb * RPP < nr; kb += RB) {
+        rr_u32x4 u[RB][PC];
+#pragma unroll
+        for (int kk = 0; kk < RB; ++kk)
+#pragma unroll
+            for (int pp = 0; pp < PC; ++pp) {
+                u[kk][pp] = rr_u32x4{0u, 0u, 0u, 0u};   // one register per value on both paths
+                if (pp < P && r0 + (kb + kk) * RPP < nr)
+                    u[kk][pp] = __builtin_amdgcn_raw_buffer_load_b128(
+                        rg, lane_off, ((pp * kAttnRows + (kb + kk) * RPP) * D) * 4,
+                        kBufferDeviceScope);
+            }
+#pragma unroll
+        for (int kk = 0; kk < RB; ++kk) {
+            const int r = r0 + (kb + kk) * RPP;
+            if (r < nr) {
+                double a4[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+                for (int pp = 0; pp < PC; ++pp)
+                    if (pp < P) {
+                        const float vf[4] = {__uint_as_float(u[kk][pp].x), __uint_as_float(u[kk][pp].y),
+                                             __uint_as_float(u[kk][pp].z), __uint_as_float(u[kk][pp].w)};
+                        merge_accumulate<4>(a4, cell[r * P + pp], vf);
+                    }
+                MergeOut<YT>::four(out_rows + r * D + 4 * li, a4);
+            }
+        }
+    }
+}
+
+// FUSED: the partitions of a (head, query tile) combine themselves.  Each
+// workgroup publishes its partial (O_p, m_p, l_p) with device-scope
+// write-through stores, waits for their acknowledgement and takes the
+// group's ticket; the workgroup that draws ticket P - 1 arrives last and
+// folds the P partials in ascending partition order with the arithmetic of
+// rr_splitk_lse_merge (rr_merge_math.hpp) into `out`, then resets the ticket
+// ("cluster_allreduce", description: the fold visits ranks in order whatever
+// the arrival order).  Without FUSED the partials are the output.
+template <int D, int KB, int NS, bool FUSED, class YT>
 __global__ __launch_bounds__(kBlockThreads, 2) void k_attn_staged(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     float* __restrict__ o, float* __restrict__ m_out, float* __restrict__ l_out, int64_t heads,
     int64_t kv_heads, int64_t q_rows, int64_t kv_len, int32_t P, float scale, int32_t q_tiles,
-    int64_t rows)
+    int64_t rows, YT* __restrict__ out, uint32_t* __restrict__ tickets)
 {
     constexpr int NC = D / 16;
     constexpr int NT = D / 32;
@@ -217,7 +274,8 @@ __global__ __launch_bounds__(kBlockThreads, 2) void k_attn_staged(
     const int64_t j0 = (int64_t)p * kv_len / P, j1 = ((int64_t)p + 1) * kv_len / P;
     float* orow = o + ((int64_t)p * rows + row) * D;
 
-    if (j1 <= j0) {
+    const bool empty = j1 <= j0;   // a partition with no key: (O, m, l) = (0, -inf, 0)
+    if (!FUSED && empty) {
         if (row_ok) {
 #pragma unroll
             for (int d = 0; d < D / 2; d += 4)
@@ -392,11 +450,27 @@ __global__ __launch_bounds__(kBlockThreads, 2) void k_attn_staged(
     }
 #undef RR_ATTN_STAGE
 
+    // Where the partial of (partition p, row) lives.  Unfused: [P][rows]
+    // (the layout rr_splitk_lse_merge reads).  Fused: group-major,
+    // [group][P][kAttnRows] with group = (head, query tile), so that the
+    // fold finds a group's P partials in one range of at most 1 MiB.
+    const int64_t grp = bh * q_tiles + qt;
+    const int64_t slot0 = FUSED ? (grp * P + p) * kAttnRows : (int64_t)p * rows + bh * q_rows
+                                                                  + (int64_t)qt * kAttnRows;
     const float l_tot = l_run + __shfl_xor(l_run, 32);
-    const float inv = 1.0f / l_tot;
+    const float inv = empty ? 0.0f : 1.0f / l_tot;
     if (row_ok && hf == 0) {
-        m_out[(int64_t)p * rows + row] = ascale * m_true;
-        l_out[(int64_t)p * rows + row] = l_tot * exp2_hw((m_ref - m_true) * c2);
+        const float mv = empty ? -__builtin_inff() : ascale * m_true;
+        const float lv = empty ? 0.0f : l_tot * exp2_hw((m_ref - m_true) * c2);
+        float* mp = m_out + slot0 + (qrow - (int64_t)qt * kAttnRows);
+        float* lp = l_out + slot0 + (qrow - (int64_t)qt * kAttnRows);
+        if constexpr (FUSED) {
+            __hip_atomic_store(mp, mv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(lp, lv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            *mp = mv;
+            *lp = lv;
+        }
     }
     // O through LDS, one 32-column depth tile at a time: a lane holds one
     // query column of the tile, so stores straight from the accumulator put
@@ -417,6 +491,11 @@ __global__ __launch_bounds__(kBlockThreads, 2) void k_attn_staged(
     char* obase = sb + (wave % kWavesPerStage) * kOWaveBytes;
     float* ow = reinterpret_cast<float*>(obase);
     const int64_t qrow0 = (int64_t)qt * kAttnRows + wave * 32;
+    // the wavefront's 32 rows of O_p; rows past q_rows fall outside the range
+    // and are not written
+    const int64_t wrows = q_rows - qrow0 < 32 ? (q_rows - qrow0 > 0 ? q_rows - qrow0 : 0) : 32;
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+        o + (slot0 + wave * 32) * D, 0, (int)(wrows * D * 4), kBufferWord3);
 #pragma unroll
     for (int dt = 0; dt < NT; ++dt) {
 #pragma unroll
@@ -430,30 +509,117 @@ __global__ __launch_bounds__(kBlockThreads, 2) void k_attn_staged(
         for (int i = 0; i < 4; ++i) {
             const int r = lane / 8 + 8 * i;
             const float4 val = *reinterpret_cast<const float4*>(ow + r * kOStride + 4 * (lane % 8));
-            if (qrow0 + r < q_rows) {
-                float* dst = o + ((int64_t)p * rows + bh * q_rows + qrow0 + r) * D + 32 * dt + 4 * (lane % 8);
-                store16_nt(dst, make_uint4(__float_as_uint(val.x), __float_as_uint(val.y),
-                                           __float_as_uint(val.z), __float_as_uint(val.w)));
-            }
+            const rr_u32x4 u = {__float_as_uint(val.x), __float_as_uint(val.y),
+                                __float_as_uint(val.z), __float_as_uint(val.w)};
+            // FUSED: device-scope write-through (another workgroup reads it);
+            // otherwise a streaming store
+            __builtin_amdgcn_raw_buffer_store_b128(u, ro, (r * D + 32 * dt + 4 * (lane % 8)) * 4, 0,
+                                                   FUSED ? kBufferDeviceScope : kBufferNonTemporal);
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);            // reads done before the next tile overwrites
         __builtin_amdgcn_wave_barrier();
     }
+    if constexpr (FUSED) {
+        static_assert(NS >= 3 && kAttnRows * (D / 8) * 8 <= (int)sizeof(AttnStage<D, KB>),
+                      "three stage buffers hold the fold's (row, partition) cells for P <= D / 8");
+        __shared__ uint32_t last;
+        // the agent-scope release of publish_partial (rr_device.hpp): the
+        // stores above went through to the device-coherent level, and the
+        // wait holds each wavefront until they are acknowledged
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        stage_barrier();                               // every wavefront's partial is in
+        if (threadIdx.x == 0) {
+            const uint32_t t = __hip_atomic_fetch_add(&tickets[grp], 1u, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+            last = t == (uint32_t)P - 1;
+        }
+        __syncthreads();
+        if (!last)
+            return;
+        // The last arriver: the fold of rr_splitk_lse_merge over the group's
+        // rows, the partials read with device-scope loads.  LDS: the (m, l)
+        // pairs, the weights and the coefficients of nr x P (row, partition)
+        // cells in three stage buffers (P <= D / 8 keeps each within one).
+        const int64_t row_base = bh * q_rows + (int64_t)qt * kAttnRows;
+        const int nr = (int)(q_rows - (int64_t)qt * kAttnRows < kAttnRows
+                                 ? q_rows - (int64_t)qt * kAttnRows : kAttnRows);
+        const int npairs = nr * P;
+        constexpr int kMaxP = D / 8;                   // the largest P of the fused call
+        constexpr int kCellPasses = kAttnRows * kMaxP / kBlockThreads;
+        float2* stat = reinterpret_cast<float2*>(&S0);
+        double* wd = reinterpret_cast<double*>(&S1);
+        double* cell = reinterpret_cast<double*>(&S2);
+        // every load of a phase is issued before the first is used: they are
+        // device-scope, served beyond the XCD's L2, and a wait per load would
+        // leave the fold latency-bound
+        {
+            float2 st[kCellPasses];
+#pragma unroll
+            for (int u = 0; u < kCellPasses; ++u) {
+                const int i = threadIdx.x + u * kBlockThreads;
+                if (i < npairs) {
+                    const int r = i / P, pp = i - r * P;
+                    const int64_t at = (grp * P + pp) * kAttnRows + r;
+                    st[u] = make_float2(
+                        __hip_atomic_load(m_out + at, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                        __hip_atomic_load(l_out + at, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kCellPasses; ++u)
+                if (threadIdx.x + u * kBlockThreads < npairs)
+                    stat[threadIdx.x + u * kBlockThreads] = st[u];
+        }
+        __syncthreads();
+        for (int i = threadIdx.x; i < npairs; i += kBlockThreads)
+            wd[i] = merge_weight(stat[i], merge_row_max(stat + (i / P) * P, P), 1.0f);
+        __syncthreads();
+        for (int i = threadIdx.x; i < npairs; i += kBlockThreads)
+            cell[i] = merge_coef(stat[i], wd[i], merge_total(wd + (i / P) * P, P));
+        __syncthreads();
+        // the group's P partials, [P][kAttnRows][D] floats; every partition,
+        // empty ones included, wrote its rows
+        const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+            o + grp * P * kAttnRows * D, 0, P * kAttnRows * D * 4, kBufferWord3);
+        YT* out_rows = out + row_base * D;
+        if (P <= 2)
+            fold_group_rows<D, 2>(rg, cell, out_rows, P, nr);
+        else if (P <= 4)
+            fold_group_rows<D, 4>(rg, cell, out_rows, P, nr);
+        else if (P <= 8 || kMaxP < 16)
+            fold_group_rows<D, (kMaxP < 8 ? kMaxP : 8)>(rg, cell, out_rows, P, nr);
+        else
+            fold_group_rows<D, (kMaxP < 16 ? kMaxP : 16)>(rg, cell, out_rows, P, nr);
+        if (threadIdx.x == 0)
+            __hip_atomic_store(&tickets[grp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
-rr_status launch_attention(const AttentionLaunch& a)
+template <bool FUSED, class YT>
+static rr_status launch_attn(const AttentionLaunch& a, YT* out)
 {
     const int32_t q_tiles = (int32_t)ceil_div(a.q_rows, kAttnRows);
     const int64_t nwork = (int64_t)q_tiles * a.P * a.batch * a.heads;
     const int64_t rows = a.batch * a.heads * a.q_rows;
     const dim3 grid((unsigned)nwork), block(kBlockThreads);
     if (a.depth == 128)
-        return launch_kernel(k_attn_staged<128, kAttnStageKeys, kAttnStages>, grid, block, 0,
-                             a.stream, a.q, a.k, a.v, a.o, a.m, a.l, a.heads, a.kv_heads, a.q_rows,
-                             a.kv_len, a.P, a.scale, q_tiles, rows);
-    return launch_kernel(k_attn_staged<64, kAttnStageKeys, kAttnStages>, grid, block, 0, a.stream,
-                         a.q, a.k, a.v, a.o, a.m, a.l, a.heads, a.kv_heads, a.q_rows, a.kv_len,
-                         a.P, a.scale, q_tiles, rows);
+        return launch_kernel(k_attn_staged<128, kAttnStageKeys, kAttnStages, FUSED, YT>, grid, block,
+                             0, a.stream, a.q, a.k, a.v, a.o, a.m, a.l, a.heads, a.kv_heads,
+                             a.q_rows, a.kv_len, a.P, a.scale, q_tiles, rows, out, a.tickets);
+    return launch_kernel(k_attn_staged<64, kAttnStageKeys, kAttnStages, FUSED, YT>, grid, block, 0,
+                         a.stream, a.q, a.k, a.v, a.o, a.m, a.l, a.heads, a.kv_heads, a.q_rows,
+                         a.kv_len, a.P, a.scale, q_tiles, rows, out, a.tickets);
+}
+
+rr_status launch_attention(const AttentionLaunch& a)
+{
+    if (!a.out)
+        return launch_attn<false, float>(a, nullptr);
+    if (a.out_dtype == RR_BF16)
+        return launch_attn<true, uint16_t>(a, static_cast<uint16_t*>(a.out));
+    return launch_attn<true, float>(a, static_cast<float*>(a.out));
 }
 
 }  // namespace rr

@@ -84,6 +84,9 @@ struct AttentionLaunch {
     int64_t batch, heads, kv_heads, q_rows, kv_len;
     int32_t depth, P;
     float scale;
+    void* out;            // fused: [rows][depth] of out_dtype; NULL: the partials are the output
+    rr_dtype out_dtype;
+    uint32_t* tickets;    // fused: one per (head, query tile), zero on entry and on exit
     hipStream_t stream;
 };
 

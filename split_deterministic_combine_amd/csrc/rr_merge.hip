@@ -9,7 +9,8 @@
 // Per row: partition p is empty when l_p <= 0 or m_p == -inf; M is the
 // largest m_p of the non-empty ones; w_p = exp(scale * (m_p - M)) * l_p;
 // W = sum w_p; out = sum over non-empty p (ascending) of (w_p / W) * O_p.
-// Weights and the accumulation are double precision with fused multiply-add.
+// Weights and the accumulation are double precision with fused multiply-add
+// (rr_merge_math.hpp, shared with the fused split-K attention).
 //
 // One workgroup takes `rw` rows.  Phase 1 stages (m_p, l_p) of those rows in
 // LDS, phase 2 forms w_p, phase 3 the coefficients c_p = w_p / W (or -1 for
@@ -23,31 +24,9 @@
 #include "rr_device.hpp"
 #include "rr_launch.hpp"
 #include "rr_launch_util.hpp"
+#include "rr_merge_math.hpp"
 
 namespace rr {
-
-template <class YT>
-struct MergeOut;
-template <>
-struct MergeOut<uint16_t> {
-    __device__ static void four(uint16_t* p, const double* a)
-    {
-        uint2 u;
-        u.x = pack_bf16x2((float)a[0], (float)a[1]);
-        u.y = pack_bf16x2((float)a[2], (float)a[3]);
-        store8_nt(p, u);
-    }
-    __device__ static void one(uint16_t* p, double a) { *p = f32_to_bf16_bits((float)a); }
-};
-template <>
-struct MergeOut<float> {
-    __device__ static void four(float* p, const double* a)
-    {
-        store16_nt(p, make_uint4(__float_as_uint((float)a[0]), __float_as_uint((float)a[1]),
-                                 __float_as_uint((float)a[2]), __float_as_uint((float)a[3])));
-    }
-    __device__ static void one(float* p, double a) { *p = (float)a; }
-};
 
 template <int VE>
 struct OChunk {
@@ -133,32 +112,15 @@ __global__ __launch_bounds__(kBlockThreads) void k_lse_merge(const float* __rest
         // Phase 2: M over the non-empty partitions of the row, then w_p.
         for (int32_t i = threadIdx.x; i < npairs; i += kBlockThreads) {
             const int32_t qq = i / P;
-            const float2* rs = stat + (int64_t)qq * P;
-            bool any = false;
-            double M = 0.0;
-            for (int32_t pp = 0; pp < P; ++pp) {
-                const float2 s = rs[pp];
-                if (s.y > 0.0f && s.x > -__builtin_inff()) {
-                    if (!any || (double)s.x > M)
-                        M = (double)s.x;
-                    any = true;
-                }
-            }
-            const float2 s = stat[i];
-            const bool live = s.y > 0.0f && s.x > -__builtin_inff();
-            wd[i] = live ? exp((double)scale * ((double)s.x - M)) * (double)s.y : 0.0;
+            const double M = merge_row_max(stat + (int64_t)qq * P, P);
+            wd[i] = merge_weight(stat[i], M, scale);
         }
         __syncthreads();
         // Phase 3: W in ascending partition order, then c_p (or -1 if empty).
         for (int32_t i = threadIdx.x; i < npairs; i += kBlockThreads) {
             const int32_t qq = i / P;
-            const double* wrow = wd + (int64_t)qq * P;
-            double W = 0.0;
-            for (int32_t pp = 0; pp < P; ++pp)
-                W += wrow[pp];
-            const float2 s = stat[i];
-            const bool live = s.y > 0.0f && s.x > -__builtin_inff();
-            cell[i] = live ? wd[i] / W : -1.0;
+            const double W = merge_total(wd + (int64_t)qq * P, P);
+            cell[i] = merge_coef(stat[i], wd[i], W);
         }
         __syncthreads();
 
@@ -177,16 +139,9 @@ __global__ __launch_bounds__(kBlockThreads) void k_lse_merge(const float* __rest
                             ch[b] = load_o<VE>(o + ((int64_t)(p0 + b < P ? p0 + b : P - 1) * rows + r) * depth + d0);
                     }
 #pragma unroll
-                    for (int b = 0; b < B; ++b) {
-                        if (p0 + b < P) {
-                            const double cp = c[p0 + b];
-                            if (cp >= 0.0) {
-#pragma unroll
-                                for (int e = 0; e < VE; ++e)
-                                    acc[e] = fma(cp, (double)ch[b].v[e], acc[e]);
-                            }
-                        }
-                    }
+                    for (int b = 0; b < B; ++b)
+                        if (p0 + b < P)
+                            merge_accumulate<VE>(acc, c[p0 + b], ch[b].v);
                 }
                 YT* orow = out + r * depth + d0;
                 if (VE == 4 && d0 + 4 <= depth) {
@@ -233,12 +188,7 @@ __device__ __forceinline__ void po_fold(double (*acc)[4], const Chunks<K>& ch, c
 {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        const double cp = cell[qk[k] * P + p];
-        if (cp >= 0.0) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                acc[k][e] = fma(cp, (double)ch.c[k].v[e], acc[k][e]);
-        }
+        merge_accumulate<4>(acc[k], cell[qk[k] * P + p], ch.c[k].v);
     }
 }
 
@@ -295,32 +245,15 @@ __global__ __launch_bounds__(kBlockThreads) void k_lse_merge_po(const float* __r
         // Phase 2: M over the non-empty partitions of the row, then w_p.
         for (int32_t i = threadIdx.x; i < npairs; i += kBlockThreads) {
             const int32_t qq = i / P;
-            const float2* rs = stat + (int64_t)qq * P;
-            bool any = false;
-            double M = 0.0;
-            for (int32_t pp = 0; pp < P; ++pp) {
-                const float2 st = rs[pp];
-                if (st.y > 0.0f && st.x > -__builtin_inff()) {
-                    if (!any || (double)st.x > M)
-                        M = (double)st.x;
-                    any = true;
-                }
-            }
-            const float2 st = stat[i];
-            const bool live = st.y > 0.0f && st.x > -__builtin_inff();
-            wd[i] = live ? exp((double)scale * ((double)st.x - M)) * (double)st.y : 0.0;
+            const double M = merge_row_max(stat + (int64_t)qq * P, P);
+            wd[i] = merge_weight(stat[i], M, scale);
         }
         __syncthreads();
         // Phase 3: W in ascending partition order, then c_p (or -1 if empty).
         for (int32_t i = threadIdx.x; i < npairs; i += kBlockThreads) {
             const int32_t qq = i / P;
-            const double* wrow = wd + (int64_t)qq * P;
-            double W = 0.0;
-            for (int32_t pp = 0; pp < P; ++pp)
-                W += wrow[pp];
-            const float2 st = stat[i];
-            const bool live = st.y > 0.0f && st.x > -__builtin_inff();
-            cell[i] = live ? wd[i] / W : -1.0;
+            const double W = merge_total(wd + (int64_t)qq * P, P);
+            cell[i] = merge_coef(stat[i], wd[i], W);
         }
         __syncthreads();
 

@@ -231,7 +231,8 @@ struct RawTile<XT, false, U> {
 // Word 3 sets the 32-bit data format, which untyped buffer loads on this
 // architecture family expect to be non-zero.
 constexpr int kBufferWord3 = 0x00020000;
-constexpr int kBufferNonTemporal = 2;  // cache-policy bit of the buffer builtins
+constexpr int kBufferNonTemporal = 2;  // cache-policy bits of the buffer builtins: nt
+constexpr int kBufferDeviceScope = 16;  // sc1: device-coherent (write-through / L2-bypassing)
 
 template <int NCH, int NT>
 __device__ __forceinline__ void load_row_raw(const void* row, int64_t row_bytes, uint4* raw)

@@ -356,6 +356,50 @@ def test_attention_partials_validate_before_touching_the_device():
     assert call(ptr=None, q_rows=0) == 0           # nothing to do
 
 
+def test_fused_attention_validates_before_touching_the_device():
+    lib = ctypes.CDLL(rr.lib_path())
+    vp, i64, i32, st = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int
+    lib.rr_splitk_attention.argtypes = [vp, vp, vp, vp, st, i64, i64, i64, i64, i64, i32, i32,
+                                        ctypes.c_float, vp, ctypes.c_size_t, vp]
+    lib.rr_splitk_attention_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32, i32,
+                                                        ctypes.POINTER(ctypes.c_size_t)]
+    f = lib.rr_splitk_attention
+    ok = dict(batch=2, heads=4, kv_heads=2, q_rows=200, kv_len=16, depth=128, P=8, scale=0.1,
+              dtype=2)
+
+    def need(**kw):
+        a = dict(ok, **kw)
+        n = ctypes.c_size_t(7)
+        s = lib.rr_splitk_attention_workspace_bytes(a["batch"], a["heads"], a["kv_heads"],
+                                                    a["q_rows"], a["kv_len"], a["depth"], a["P"],
+                                                    ctypes.byref(n))
+        return s, n.value
+
+    # tickets for 2*4*2 (head, query tile) groups padded to 256 bytes, then
+    # O_p, m_p and l_p for P whole 128-row tiles of every group
+    cells = 2 * 4 * 2 * 8 * 128
+    assert need() == (0, 256 + cells * 128 * 4 + 2 * cells * 4)
+    assert need(P=17)[0] == 2 and need(depth=64, P=9)[0] == 2   # P <= depth / 8
+    assert need(depth=64, P=8)[0] == 0
+    assert need(q_rows=0) == (0, 0)
+    assert lib.rr_splitk_attention_workspace_bytes(1, 1, 1, 1, 1, 128, 1, None) == 1
+    ws_len = need()[1]
+
+    def call(ptr=256, ws=4096, ws_len=ws_len, **kw):
+        a = dict(ok, **kw)
+        return f(ptr, ptr, ptr, ptr, a["dtype"], a["batch"], a["heads"], a["kv_heads"], a["q_rows"],
+                 a["kv_len"], a["depth"], a["P"], a["scale"], ws, ws_len, None)
+
+    assert call(depth=96) == 2 and call(heads=3) == 2 and call(P=0) == 2
+    assert call(P=17) == 2 and call(depth=64, P=9) == 2
+    assert call(scale=float("nan")) == 2
+    assert call(dtype=1) == 3                      # int32 output
+    assert call(ptr=None) == 1
+    assert call(ptr=8) == 2                        # misaligned
+    assert call(ws=None) == 5 and call(ws_len=ws_len - 1) == 5 and call(ws=4100) == 5
+    assert call(ptr=None, ws=None, q_rows=0) == 0  # nothing to do
+
+
 def test_stream_reference_validates_before_touching_the_device():
     lib = ctypes.CDLL(rr.lib_path())
     vp = ctypes.c_void_p

@@ -179,3 +179,79 @@ def test_partials_random_shapes(case):
         assert torch.all(m == -math.inf) and torch.all(l == 0) and torch.all(o == 0)
         return
     _check_partials(q, k, v, P, scale, "random %r" % (case,))
+
+
+# ------------------------------------------------ fused split-K attention
+def _fused_vs_two_launch(q, k, v, P, scale, out_dtype, what, workspace=None):
+    """rr_splitk_attention against rr_splitk_attention_partials followed by
+    rr_splitk_lse_merge: the same bits, and the tickets left zero."""
+    tq, tk, tv = _bf16_tensor(q), _bf16_tensor(k), _bf16_tensor(v)
+    ref = rr.splitk_lse_merge(*rr.splitk_attention_partials(tq, tk, tv, P, scale), 1.0, out_dtype)
+    got = rr.splitk_attention(tq, tk, tv, P, scale, out_dtype, workspace=workspace)
+    torch.cuda.synchronize()
+    a = got.reshape(-1).view(torch.int16 if out_dtype == torch.bfloat16 else torch.int32)
+    b = ref.reshape(-1).view(a.dtype)
+    bad = torch.nonzero(a != b)
+    assert bad.numel() == 0, (what, "first differing element", int(bad[0]), bad.numel())
+    return got
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("depth", [64, 128])
+@pytest.mark.parametrize("q_rows,kv_len,P", [(130, 300, 3), (32, 64, 1), (7, 1000, 8),
+                                             (256, 129, 2), (9, 5, 8)])
+def test_fused_equals_partials_then_merge(out_dtype, depth, q_rows, kv_len, P):
+    q, k, v = synth.attention(1000 + q_rows + kv_len, batch=2, heads=4, kv_heads=2, q_rows=q_rows,
+                              kv_len=kv_len, depth=depth)
+    _fused_vs_two_launch(q, k, v, P, 1.0 / math.sqrt(depth), out_dtype,
+                         "%d rows %d keys P=%d d=%d" % (q_rows, kv_len, P, depth))
+
+
+def test_fused_largest_p_negative_scale_and_no_keys():
+    q, k, v = synth.attention(1010, batch=1, heads=2, kv_heads=1, q_rows=77, kv_len=2000, depth=128)
+    _fused_vs_two_launch(q, k, v, 16, -0.2, torch.float32, "P=16, negative scale")
+    q, k, v = synth.attention(1011, batch=1, heads=2, kv_heads=2, q_rows=3, kv_len=0, depth=64)
+    got = _fused_vs_two_launch(q, k, v, 8, 0.125, torch.bfloat16, "no keys")
+    assert torch.all(got.float() == 0)
+
+
+def test_fused_is_attention_and_leaves_tickets_zero():
+    q, k, v = synth.attention(1012, batch=1, heads=4, kv_heads=2, q_rows=64, kv_len=1500, depth=128)
+    scale = 1.0 / math.sqrt(128)
+    need = rr.splitk_attention_workspace_bytes(1, 4, 2, 64, 1500, 128, 8)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for _ in range(3):                             # the tickets must be reusable
+        got = to_host(_fused_vs_two_launch(q, k, v, 8, scale, torch.float32, "fused", ws))
+        assert torch.all(ws[:256] == 0)
+    ref_o, _, _ = oracle.attention_partials(q, k, v, 1, scale)
+    abs_o, _, _ = oracle.attention_partials(q, k, v & np.uint16(0x7FFF), 1, scale)
+    bs = _score_bound(q, k, scale)
+    tol = (2.0 ** -8 + 2.0 ** -13 + 4 * bs)[:, None] * abs_o[0] + 1e-6
+    assert np.all(np.abs(got.reshape(ref_o[0].shape) - ref_o[0]) <= tol)
+
+
+def test_fused_bit_identical_across_runs_and_shapes_sharing_a_workspace():
+    q, k, v = synth.attention(1013, batch=2, heads=4, kv_heads=4, q_rows=128, kv_len=1024, depth=128)
+    tq, tk, tv = _bf16_tensor(q), _bf16_tensor(k), _bf16_tensor(v)
+    first = rr.splitk_attention(tq, tk, tv, 8).clone()
+    q2, k2, v2 = synth.attention(1014, batch=1, heads=2, kv_heads=1, q_rows=300, kv_len=99, depth=64)
+    for _ in range(4):
+        again = rr.splitk_attention(tq, tk, tv, 8)
+        assert torch.equal(again.view(torch.int16), first.view(torch.int16))
+        # another shape on the same cached workspace between the runs
+        _fused_vs_two_launch(q2, k2, v2, 5, 0.125, torch.bfloat16, "interleaved shape")
+
+
+def test_fused_config_full_size_matches_two_launch():
+    # [8, 32, 128, 128] queries over 8192 keys in 8 partitions, as the
+    # benchmark runs it: the fused launch against partials + merge, every element
+    B, H, S, D, N, P = 8, 32, 128, 128, 8192, 8
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1015)
+    q = torch.randn((B, H, S, D), generator=gen, device="cuda").to(torch.bfloat16)
+    k = torch.randn((B, H, N, D), generator=gen, device="cuda").to(torch.bfloat16)
+    v = torch.randn((B, H, N, D), generator=gen, device="cuda").to(torch.bfloat16)
+    ref = rr.splitk_lse_merge(*rr.splitk_attention_partials(q, k, v, P), 1.0, torch.bfloat16)
+    for _ in range(2):
+        got = rr.splitk_attention(q, k, v, P)
+        assert torch.equal(got.reshape(-1).view(torch.int16), ref.reshape(-1).view(torch.int16))

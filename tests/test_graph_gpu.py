@@ -52,6 +52,7 @@ def test_graph_replays_match_eager_bit_for_bit():
         "merge": torch.empty((1, 4, 64, 128), dtype=torch.bfloat16, device=dev),
         "attn": {"o": torch.empty((4, 520, 128), device=dev), "m": torch.empty((4, 520), device=dev),
                  "l": torch.empty((4, 520), device=dev)},
+        "attn_fused": torch.empty((1, 4, 130, 128), dtype=torch.bfloat16, device=dev),
     }
 
     def run_all():
@@ -67,6 +68,7 @@ def test_graph_replays_match_eager_bit_for_bit():
         rr.splitk_lse_merge(o, m, l, 1.0, torch.bfloat16, out=outs["merge"])
         rr.splitk_attention_partials(aq, ak, av, 4, out=(outs["attn"]["o"], outs["attn"]["m"],
                                                          outs["attn"]["l"]))
+        rr.splitk_attention(aq, ak, av, 4, out=outs["attn_fused"])
 
     def snapshot():
         flat = {}
