@@ -66,8 +66,14 @@ __device__ __forceinline__ rr_bf16x8 pack8(const float* f)
 // (each lane picks the global chunk that belongs at its LDS slot):
 //   K: chunk c of row r at slot c ^ (r mod chunks-per-row): the S operand
 //      reads (16 lanes = 16 rows, one chunk) hit 16 distinct bank groups;
-//   V: chunk c of row r at slot c ^ 2 (r mod 4): the transposed reads below
-//      (4 rows x 4 half-chunks per 16 lanes) hit 16 distinct bank pairs.
+//   V: chunk c of row r at slot c ^ v_swz(r): the transposed reads below
+//      (4 rows x 4 half-chunks per 16 lanes, two such groups per 32 lanes)
+//      hit 32 distinct 8-byte bank pairs.  The LDS serves 256 bytes per
+//      cycle (64 banks; an 8-byte read takes 32 lanes at once, measured on
+//      MI355X), so with 256-byte rows (depth 128) the row does not change
+//      the bank and the XOR must separate all 32 lanes: 4 (r mod 4) moves
+//      the two high chunk bits.  With 128-byte rows the row's parity picks
+//      the bank half, and 2 (r mod 4) suffices.
 // V stays row-major (keys x depth); the A operand of O^T += V^T P^T comes from
 // ds_read_b64_tr_b16, which hands lane i of a 16-lane group element i%4 of
 // the 8 bytes addressed by lane 4j + i/4, j = 0..3 (checked on MI355X): with
@@ -85,9 +91,14 @@ __device__ __forceinline__ int k_slot_byte(int row, int chunk)
     return row * D * 2 + 16 * (chunk ^ (row & (D / 8 - 1)));
 }
 template <int D>
+__device__ __forceinline__ int v_swz(int row)
+{
+    return D == 128 ? (row & 3) << 2 : (row & 3) << 1;
+}
+template <int D>
 __device__ __forceinline__ int v_slot_byte(int row, int chunk)
 {
-    return row * D * 2 + 16 * (chunk ^ ((row & 3) << 1));
+    return row * D * 2 + 16 * (chunk ^ v_swz<D>(row));
 }
 
 // s_waitcnt on the vector-memory counter only (N < 16): expcnt and lgkmcnt
@@ -139,7 +150,7 @@ __device__ __forceinline__ void attn_dma_stage(const uint16_t* kh, const uint16_
         const int row = slot / CH, pos = slot % CH;
         const int rr_ = row < nvalid ? row : nvalid - 1;
         const int kc = pos ^ (row & (CH - 1));
-        const int vc = pos ^ ((row & 3) << 1);
+        const int vc = pos ^ v_swz<D>(row);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rk, (__attribute__((address_space(3))) void*)((char*)st->k + 16 * base), 16,
             rr_ * D * 2 + 16 * kc, 0, 0, kBufferNonTemporal);
@@ -150,6 +161,16 @@ __device__ __forceinline__ void attn_dma_stage(const uint16_t* kh, const uint16_
 }
 
 typedef short rr_i16x4 __attribute__((ext_vector_type(4)));
+
+// The larger of a lane's value and that of lane i ^ 32 (the other half of
+// the wavefront), in every lane: v_permlane32_swap hands each half the
+// other half's values without going through LDS.
+__device__ __forceinline__ float max_halves(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
 // Workgroup barrier between stages.  __syncthreads() carries a workgroup
 // release fence, which on this target waits for every outstanding LDS DMA
@@ -368,7 +389,12 @@ __global__ __launch_bounds__(kBlockThreads, 2) void k_attn_staged(
                 s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qb[c], s[t], 0, 0, 0);
             }
         }
+        // Score (t, r) of a lane is key 32 t + 8 (r / 4) + 4 hf + r % 4 of the
+        // stage; only the partition's last stage can be partial, and there
+        // key (t, r) is in when its offset 32 t + 8 (r / 4) + r % 4 is below
+        // lim = nvalid - 4 hf (one register, compared against constants).
         const bool full = nvalid == KB;                 // all keys of the stage are in the partition
+        const int lim = nvalid - 4 * hf;
         float bm = -__builtin_inff();
         if (full) {
 #pragma unroll
@@ -381,10 +407,10 @@ __global__ __launch_bounds__(kBlockThreads, 2) void k_attn_staged(
             for (int t = 0; t < NST; ++t)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    if (32 * t + 8 * (r / 4) + 4 * hf + (r % 4) < nvalid)
+                    if (32 * t + 8 * (r / 4) + (r % 4) < lim)
                         bm = fmaxf(bm, s[t][r]);
         }
-        bm = fmaxf(bm, __shfl_xor(bm, 32));            // finite: every stage has a key
+        bm = max_halves(bm);                            // finite: every stage has a key
         m_true = fmaxf(m_true, bm);
         const bool move = st == 0 || (bm - m_ref) * c2 > kAttnLazyLog2;
         if (__any(move)) {                              // wavefront-uniform branch
@@ -400,16 +426,26 @@ __global__ __launch_bounds__(kBlockThreads, 2) void k_attn_staged(
         }
         const float mb = -m_ref * c2;
         float ls = 0.0f;
+        if (full) {
 #pragma unroll
-        for (int t = 0; t < NST; ++t)
+            for (int t = 0; t < NST; ++t)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float pv = exp2_hw(__builtin_fmaf(s[t][r], c2, mb));
-                if (!full && 32 * t + 8 * (r / 4) + 4 * hf + (r % 4) >= nvalid)
-                    pv = 0.0f;
-                s[t][r] = pv;
-                ls += pv;
-            }
+                for (int r = 0; r < 16; ++r) {
+                    const float pv = exp2_hw(__builtin_fmaf(s[t][r], c2, mb));
+                    s[t][r] = pv;
+                    ls += pv;
+                }
+        } else {
+#pragma unroll
+            for (int t = 0; t < NST; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float pv = 32 * t + 8 * (r / 4) + (r % 4) < lim
+                                         ? exp2_hw(__builtin_fmaf(s[t][r], c2, mb)) : 0.0f;
+                    s[t][r] = pv;
+                    ls += pv;
+                }
+        }
         l_run += ls;
         rr_bf16x8 pb[NST][2];
 #pragma unroll
