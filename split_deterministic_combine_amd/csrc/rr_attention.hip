@@ -128,35 +128,58 @@ __device__ __forceinline__ void wait_stages(int64_t after)
     wait_vmcnt<0>();
 }
 
+// A thread's share of one stage's DMA: OPS 16-byte chunks of K and of V.
+// Slot i * kBlockThreads + threadIdx.x of a stage holds chunk `pos` of key
+// row `row`; the byte offsets into the stage's keys (with the K and V
+// swizzles) do not depend on the stage, so they are formed once.
+template <int D, int KB>
+struct AttnDmaLane {
+    static constexpr int CH = D / 8;                       // 16-byte chunks per row
+    static constexpr int OPS = KB * CH / kBlockThreads;    // per tensor per thread
+    int koff[OPS], voff[OPS];
+    __device__ AttnDmaLane()
+    {
+#pragma unroll
+        for (int i = 0; i < OPS; ++i) {
+            const int slot = i * kBlockThreads + (int)threadIdx.x;
+            const int row = slot / CH, pos = slot % CH;
+            koff[i] = row * D * 2 + 16 * (pos ^ (row & (CH - 1)));
+            voff[i] = row * D * 2 + 16 * (pos ^ v_swz<D>(row));
+        }
+    }
+};
+
 // DMA of one stage: keys [js, js + nvalid) of a head into stage buffer st.
-// Rows past nvalid repeat row nvalid - 1 (finite values; their scores are
-// masked), so every load stays inside the head's keys.
+// In a partial stage (nvalid < KB) rows past nvalid repeat row nvalid - 1
+// (finite values; their scores are masked), so every load stays inside the
+// head's keys.
 template <int D, int KB>
 __device__ __forceinline__ void attn_dma_stage(const uint16_t* kh, const uint16_t* vh, int64_t js,
-                                               int nvalid, AttnStage<D, KB>* st)
+                                               int nvalid, AttnStage<D, KB>* st,
+                                               const AttnDmaLane<D, KB>& dl)
 {
-    constexpr int CH = D / 8;                       // 16-byte chunks per row
-    constexpr int OPS = KB * CH / kBlockThreads;    // per tensor per thread
+    using L = AttnDmaLane<D, KB>;
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(kh + js * D), 0, nvalid * D * 2, kBufferWord3);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(vh + js * D), 0, nvalid * D * 2, kBufferWord3);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int lane = lane_id();
 #pragma unroll
-    for (int i = 0; i < OPS; ++i) {
+    for (int i = 0; i < L::OPS; ++i) {
         const int base = i * kBlockThreads + wave * kWave;   // first slot of this wave's op
-        const int slot = base + lane;
-        const int row = slot / CH, pos = slot % CH;
-        const int rr_ = row < nvalid ? row : nvalid - 1;
-        const int kc = pos ^ (row & (CH - 1));
-        const int vc = pos ^ v_swz<D>(row);
+        int ko = dl.koff[i], vo = dl.voff[i];
+        if (nvalid < KB) {                                   // uniform: the partial stage only
+            const int row = (base + lane_id()) / L::CH;
+            const int shift = ((row < nvalid ? row : nvalid - 1) - row) * D * 2;
+            ko += shift;
+            vo += shift;
+        }
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rk, (__attribute__((address_space(3))) void*)((char*)st->k + 16 * base), 16,
-            rr_ * D * 2 + 16 * kc, 0, 0, kBufferNonTemporal);
+            rk, (__attribute__((address_space(3))) void*)((char*)st->k + 16 * base), 16, ko, 0, 0,
+            kBufferNonTemporal);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rv, (__attribute__((address_space(3))) void*)((char*)st->v + 16 * base), 16,
-            rr_ * D * 2 + 16 * vc, 0, 0, kBufferNonTemporal);
+            rv, (__attribute__((address_space(3))) void*)((char*)st->v + 16 * base), 16, vo, 0, 0,
+            kBufferNonTemporal);
     }
 }
 
@@ -324,6 +347,7 @@ __global__ __launch_bounds__(kBlockThreads, 2) void k_attn_staged(
     const uint16_t* kh = k + kvh * kv_len * D;
     const uint16_t* vh = v + kvh * kv_len * D;
     const int64_t nstg = ceil_div(j1 - j0, KB);
+    const AttnDmaLane<D, KB> dl;
     auto nvalid_of = [&](int64_t s_) {
         const int64_t left = j1 - j0 - s_ * KB;
         return (int)(left < KB ? left : KB);
@@ -331,7 +355,7 @@ __global__ __launch_bounds__(kBlockThreads, 2) void k_attn_staged(
 #pragma unroll
     for (int s_ = 0; s_ < NS - 1; ++s_)
         if (s_ < nstg)
-            attn_dma_stage<D, KB>(kh, vh, j0 + (int64_t)s_ * KB, nvalid_of(s_), RR_ATTN_STAGE(s_));
+            attn_dma_stage<D, KB>(kh, vh, j0 + (int64_t)s_ * KB, nvalid_of(s_), RR_ATTN_STAGE(s_), dl);
 
     rr_f32x16 acc[NT];
 #pragma unroll
@@ -371,7 +395,7 @@ __global__ __launch_bounds__(kBlockThreads, 2) void k_attn_staged(
         wait_stages<OPS, NS>(after);
         stage_barrier();
         if (st + NS - 1 < nstg)
-            attn_dma_stage<D, KB>(kh, vh, j0 + (st + NS - 1) * KB, nvalid_of(st + NS - 1), F);
+            attn_dma_stage<D, KB>(kh, vh, j0 + (st + NS - 1) * KB, nvalid_of(st + NS - 1), F, dl);
         const int nvalid = nvalid_of(st);
         const char* kb = reinterpret_cast<const char*>(T->k);
         const char* vb = reinterpret_cast<const char*>(T->v);
@@ -558,7 +582,10 @@ __global__ __launch_bounds__(kBlockThreads, 2) void k_attn_staged(
     if constexpr (FUSED) {
         static_assert(NS >= 3 && kAttnRows * (D / 8) * 8 <= (int)sizeof(AttnStage<D, KB>),
                       "three stage buffers hold the fold's (row, partition) cells for P <= D / 8");
-        __shared__ uint32_t last;
+        // the ticket's verdict, in the last stage buffer: free once every
+        // wavefront's O has left the staging, and not used by the fold below
+        uint32_t* last = reinterpret_cast<uint32_t*>(NS == 5 ? (void*)&S4 : NS == 4 ? (void*)&S3
+                                                                                   : (void*)&S2);
         // the agent-scope release of publish_partial (rr_device.hpp): the
         // stores above went through to the device-coherent level, and the
         // wait holds each wavefront until they are acknowledged
@@ -569,10 +596,10 @@ __global__ __launch_bounds__(kBlockThreads, 2) void k_attn_staged(
         if (threadIdx.x == 0) {
             const uint32_t t = __hip_atomic_fetch_add(&tickets[grp], 1u, __ATOMIC_RELAXED,
                                                       __HIP_MEMORY_SCOPE_AGENT);
-            last = t == (uint32_t)P - 1;
+            *last = t == (uint32_t)P - 1;
         }
         __syncthreads();
-        if (!last)
+        if (!*last)
             return;
         // The last arriver: the fold of rr_splitk_lse_merge over the group's
         // rows, the partials read with device-scope loads.  LDS: the (m, l)
