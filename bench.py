@@ -257,6 +257,44 @@ def ingest_counters(trace_dir, fetch_dir, write_dir):
     return out, table
 
 
+# SQ counter passes behind profiles/counters_<op>.md (at most 8 SQ counters
+# per rocprofv3 run)
+SQ_PASSES = (
+    ("SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES",
+     "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_LDS", "SQ_WAIT_ANY"),
+    ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_ADDR_CONFLICT", "SQ_INSTS_LDS",
+     "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY"),
+)
+
+
+def sq_summary(op, dirs):
+    """profiles/counters_<op>.md: the mean of every SQ counter over the
+    dispatches of op's kernel in the rocprofv3 --pmc output directories."""
+    pat = KERNEL_OF_OP[op]
+    vals = {}
+    for d in dirs:
+        for r in _csv_rows(d, "counter_collection.csv"):
+            if pat in r["Kernel_Name"]:
+                vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    cmds = "\n".join(
+        "    cd /tmp && export TMPDIR=/tmp && timeout -s KILL 90 rocprofv3 --pmc %s -f csv "
+        "-d $R/gpurun_out/sq_%s_%d -o sq -- python3 $R/bench.py --only %s --steps 3 --warmup 0 "
+        "--no-parity --no-cpu-baseline" % (" ".join(c), op, i, op) for i, c in enumerate(SQ_PASSES))
+    rows = ["| counter | mean per dispatch | dispatches |", "|---|---|---|"]
+    for k in sorted(vals):
+        rows.append("| %s | %.4g | %d |" % (k, sum(vals[k]) / len(vals[k]), len(vals[k])))
+    path = os.path.join(os.path.dirname(TRAFFIC_FILE), "counters_%s.md" % op)
+    with open(path, "w") as f:
+        f.write("# SQ counters, `%s` (%s, one MI355X)\n\nTwo counter passes from the repository "
+                "root `R`:\n\n%s\n\nsummarised by `python bench.py --sq-summary %s DIR DIR`. "
+                "Values as rocprofv3 reports them per dispatch (accumulated over the chip); "
+                "read them as ratios of one another (bank-conflict cycles against LDS-active "
+                "cycles, waiting against wave cycles, instructions per dispatch)."
+                "\n\n%s\n\nKernel sources hash: `%s`.\n" % (pat, op, cmds, op, "\n".join(rows),
+                                                             kernel_source_hash()))
+    return path
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -272,6 +310,9 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 512 MiB elementwise copy (negation) three times: "
                          "the known-size reference for scaling FETCH_SIZE / WRITE_SIZE")
+    ap.add_argument("--sq-summary", nargs="+", metavar="OP_OR_DIR",
+                    help="host only: OP then the rocprofv3 --pmc output directories of the "
+                         "SQ counter passes; writes profiles/counters_OP.md")
     ap.add_argument("--ingest-counters", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="host only: read rocprofv3 CSV output (kernel stats, FETCH_SIZE run, "
                          "WRITE_SIZE run) and write profiles/traffic.json and summaries")
@@ -293,6 +334,9 @@ def log(msg):
 
 def main():
     args = parse()
+    if args.sq_summary:
+        print(sq_summary(args.sq_summary[0], args.sq_summary[1:]))
+        return
     if args.ingest_counters:
         out, table = ingest_counters(*args.ingest_counters)
         print(json.dumps(out, indent=1))
@@ -545,6 +589,15 @@ def main():
     # moves the most algorithmic bytes (every op is HBM-bound, so it is also
     # the longest); the first in step order on a tie (the f32 and i32 long-row
     # reductions move the same bytes), so the choice does not flip between runs.
+    if not names and next_names:
+        # a profiling run of operations outside the step (under rocprofv3):
+        # each selected one launched warmup + steps times; nothing is timed
+        for i in range(args.warmup + args.steps):
+            for n in next_names:
+                next_ops[n](i)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_run": next_names, "launches_each": args.warmup + args.steps}))
+        return
     log("warmup %d steps" % args.warmup)
     if not names:
         sys.exit("bench.py: --only selected no operation of the step")
