@@ -255,3 +255,26 @@ def test_fused_config_full_size_matches_two_launch():
     for _ in range(2):
         got = rr.splitk_attention(q, k, v, P)
         assert torch.equal(got.reshape(-1).view(torch.int16), ref.reshape(-1).view(torch.int16))
+
+
+def _fused_random_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        kv_heads = int(rng.choice([1, 2]))
+        depth = int(rng.choice([64, 128]))
+        cases.append((i, int(rng.integers(1, 3)), kv_heads * int(rng.choice([1, 2, 3])), kv_heads,
+                      int(rng.integers(1, 300)), int(rng.integers(0, 2000)), depth,
+                      int(rng.integers(1, depth // 8 + 1)), float(rng.uniform(-0.3, 0.3)),
+                      bool(rng.integers(0, 2))))
+    return cases
+
+
+@pytest.mark.parametrize("case", _fused_random_cases(12, 1016),
+                         ids=lambda c: "t%d_b%dh%dk%dq%dn%dd%dP%d" % c[:8])
+def test_fused_random_shapes(case):
+    i, batch, heads, kv_heads, q_rows, kv_len, depth, P, scale, bf16 = case
+    q, k, v = synth.attention(1020 + i, batch=batch, heads=heads, kv_heads=kv_heads, q_rows=q_rows,
+                              kv_len=kv_len, depth=depth)
+    _fused_vs_two_launch(q, k, v, P, scale, torch.bfloat16 if bf16 else torch.float32,
+                         "random %r" % (case,))
