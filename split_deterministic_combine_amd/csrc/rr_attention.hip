@@ -267,8 +267,19 @@ __device__ __forceinline__ void fold_group_rows(const __amdgpu_buffer_rsrc_t rg,
 // rr_splitk_lse_merge (rr_merge_math.hpp) into `out`, then resets the ticket
 // ("cluster_allreduce", description: the fold visits ranks in order whatever
 // the arrival order).  Without FUSED the partials are the output.
+template <int D, bool FUSED>
+constexpr int attn_stages()
+{
+    return D == 128 && !FUSED ? kAttnStages : kAttnStagesOther;
+}
+template <int D, bool FUSED>
+constexpr int attn_workgroups_per_cu()
+{
+    return D == 128 && !FUSED ? kAttnWorkgroupsPerCU : kAttnWorkgroupsPerCUOther;
+}
+
 template <int D, int KB, int NS, bool FUSED, class YT>
-__global__ __launch_bounds__(kBlockThreads, 2) void k_attn_staged(
+__global__ __launch_bounds__(kBlockThreads, (attn_workgroups_per_cu<D, FUSED>())) void k_attn_staged(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     float* __restrict__ o, float* __restrict__ m_out, float* __restrict__ l_out, int64_t heads,
     int64_t kv_heads, int64_t q_rows, int64_t kv_len, int32_t P, float scale, int32_t q_tiles,
@@ -399,6 +410,21 @@ __global__ __launch_bounds__(kBlockThreads, 2) void k_attn_staged(
         const int nvalid = nvalid_of(st);
         const char* kb = reinterpret_cast<const char*>(T->k);
         const char* vb = reinterpret_cast<const char*>(T->v);
+        // LDS read addresses, formed again in every stage from the lane's
+        // coordinates (the empty asm hides them from loop-invariant code
+        // motion): holding the 16 per-lane addresses across the loop would
+        // cost 16 registers, forming them costs a dozen instructions that
+        // issue while the matrix cores work.
+        int lrow = lane % 32, lhf = hf, ljj = jj, lg = G, lqq = qq;
+        asm volatile("" : "+v"(lrow), "+v"(lhf), "+v"(ljj), "+v"(lg), "+v"(lqq));
+        // K: chunk 2c + hf of row lrow at slot (2c + hf) ^ (lrow mod D/8),
+        // i.e. byte kbase + ((32 c) ^ kx)
+        const int kbase = lrow * D * 2 + 16 * ((lhf ^ lrow) & 1);
+        const int kx = 16 * (lrow & (D / 8 - 2));
+        // V: rows 32 t + 16 c + 4 hf + jj (+ 8), chunk 4 dt + 2 G + (qq >> 1),
+        // swizzled by v_swz(jj): byte vbase + ((64 dt + 32 G) ^ vx) + rows
+        const int vbase = (4 * lhf + ljj) * D * 2 + 16 * (lqq >> 1) + 8 * (lqq & 1);
+        const int vx = 16 * v_swz<D>(ljj);
 
         rr_f32x16 s[NST];
 #pragma unroll
@@ -409,7 +435,7 @@ __global__ __launch_bounds__(kBlockThreads, 2) void k_attn_staged(
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
                 const uint4 a = *reinterpret_cast<const uint4*>(
-                    kb + k_slot_byte<D>(32 * t + lane % 32, 2 * c + hf));
+                    kb + 32 * t * D * 2 + kbase + ((32 * c) ^ kx));
                 s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qb[c], s[t], 0, 0, 0);
             }
         }
@@ -488,13 +514,11 @@ __global__ __launch_bounds__(kBlockThreads, 2) void k_attn_staged(
             for (int t = 0; t < NST; ++t)
 #pragma unroll
                 for (int c = 0; c < 2; ++c) {
-                    const int r1 = 32 * t + 16 * c + 4 * hf + jj;
-                    const int chunk = 4 * dt + 2 * G + (qq >> 1);
-                    const int off = 8 * (qq & 1);
+                    const int va = vbase + ((64 * dt + 32 * lg) ^ vx) + (32 * t + 16 * c) * D * 2;
                     const rr_i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (rr_i16x4 __attribute__((address_space(3)))*)(vb + v_slot_byte<D>(r1, chunk) + off));
+                        (rr_i16x4 __attribute__((address_space(3)))*)(vb + va));
                     const rr_i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (rr_i16x4 __attribute__((address_space(3)))*)(vb + v_slot_byte<D>(r1 + 8, chunk) + off));
+                        (rr_i16x4 __attribute__((address_space(3)))*)(vb + va + 8 * D * 2));
                     const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
                     acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y)), pb[t][c], acc[dt], 0, 0, 0);
@@ -668,12 +692,14 @@ static rr_status launch_attn(const AttentionLaunch& a, YT* out)
     const int64_t rows = a.batch * a.heads * a.q_rows;
     const dim3 grid((unsigned)nwork), block(kBlockThreads);
     if (a.depth == 128)
-        return launch_kernel(k_attn_staged<128, kAttnStageKeys, kAttnStages, FUSED, YT>, grid, block,
-                             0, a.stream, a.q, a.k, a.v, a.o, a.m, a.l, a.heads, a.kv_heads,
-                             a.q_rows, a.kv_len, a.P, a.scale, q_tiles, rows, out, a.tickets);
-    return launch_kernel(k_attn_staged<64, kAttnStageKeys, kAttnStages, FUSED, YT>, grid, block, 0,
-                         a.stream, a.q, a.k, a.v, a.o, a.m, a.l, a.heads, a.kv_heads, a.q_rows,
-                         a.kv_len, a.P, a.scale, q_tiles, rows, out, a.tickets);
+        return launch_kernel(
+            k_attn_staged<128, kAttnStageKeys, attn_stages<128, FUSED>(), FUSED, YT>, grid, block, 0,
+            a.stream, a.q, a.k, a.v, a.o, a.m, a.l, a.heads, a.kv_heads, a.q_rows, a.kv_len, a.P,
+            a.scale, q_tiles, rows, out, a.tickets);
+    return launch_kernel(k_attn_staged<64, kAttnStageKeys, attn_stages<64, FUSED>(), FUSED, YT>,
+                         grid, block, 0, a.stream, a.q, a.k, a.v, a.o, a.m, a.l, a.heads,
+                         a.kv_heads, a.q_rows, a.kv_len, a.P, a.scale, q_tiles, rows, out,
+                         a.tickets);
 }
 
 rr_status launch_attention(const AttentionLaunch& a)
