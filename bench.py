@@ -74,7 +74,7 @@ KERNEL_OF_OP = {
     "axis_cols_fold": "k_reduce_axis_fold<rr::SumF32>",
     # reference streams of known size (not ops of the step): rr_test_stream
     "attention": "k_attn_staged<128, 32, 3, false, float>",
-    "attention_fused": "k_attn_staged<128, 32, 4, true, unsigned short>",
+    "attention_fused": "k_attn_staged<128, 32, 3, true, unsigned short>",
     "stream_read": "k_stream<0>",
     "stream_write": "k_stream<1>",
 }

@@ -224,7 +224,7 @@ __device__ __forceinline__ void fold_group_rows(const __amdgpu_buffer_rsrc_t rg,
 {
     constexpr int LPR = D / 4;                          // lanes per row, 4 columns each
     constexpr int RPP = kBlockThreads / LPR;            // rows per pass
-    constexpr int kCells = 32;                          // 16-byte loads in flight per thread
+    constexpr int kCells = 16;                          // 16-byte loads in flight per thread
     constexpr int RB = kCells / PC < kAttnRows / RPP ? kCells / PC : kAttnRows / RPP;
     const int li = threadIdx.x % LPR;
     const int r0 = threadIdx.x / LPR;
@@ -270,12 +270,12 @@ __device__ __forceinline__ void fold_group_rows(const __amdgpu_buffer_rsrc_t rg,
 template <int D, bool FUSED>
 constexpr int attn_stages()
 {
-    return D == 128 && !FUSED ? kAttnStages : kAttnStagesOther;
+    return D == 128 ? kAttnStages : kAttnStagesOther;
 }
 template <int D, bool FUSED>
 constexpr int attn_workgroups_per_cu()
 {
-    return D == 128 && !FUSED ? kAttnWorkgroupsPerCU : kAttnWorkgroupsPerCUOther;
+    return D == 128 ? kAttnWorkgroupsPerCU : kAttnWorkgroupsPerCUOther;
 }
 
 template <int D, int KB, int NS, bool FUSED, class YT>

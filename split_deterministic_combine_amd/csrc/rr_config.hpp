@@ -133,16 +133,15 @@ constexpr int kMergePOuterRowsPerLane = 4;
 constexpr int kMergePOuterMaxP = 32;
 
 // Split-K attention partials: query rows per workgroup (4 wavefronts of 32)
-// and keys per LDS stage.  Depth 128 (unfused): 3 stages in flight at 3
-// workgroups per CU (48 KiB of LDS and at most 168 registers each) measured
-// fastest on [8, 32, 128, 128] over 8192 keys, beside 4 and 5 stages at 2 per
-// CU; depth 64 and the one-launch variant keep 4 stages at (at least) 2 per
-// CU -- 3 stages are too small for depth 64's O staging, and the one-launch
-// kernel's fold spills at 3 per CU.
+// and keys per LDS stage.  Depth 128: 3 stages in flight at 3 workgroups per
+// CU (48 KiB of LDS and at most 168 registers each) measured fastest on
+// [8, 32, 128, 128] over 8192 keys, beside 4 and 5 stages at 2 per CU; depth
+// 64 keeps 4 stages at (at least) 2 per CU -- 3 stages are too small for its
+// O staging.
 constexpr int kAttnRows = 128;
 constexpr int kAttnStageKeys = 32;
-constexpr int kAttnStages = 3;            // depth 128, unfused
-constexpr int kAttnWorkgroupsPerCU = 3;   // depth 128, unfused
+constexpr int kAttnStages = 3;            // depth 128
+constexpr int kAttnWorkgroupsPerCU = 3;   // depth 128
 constexpr int kAttnStagesOther = 4;
 constexpr int kAttnWorkgroupsPerCUOther = 2;
 constexpr int kAttnMaxP = 256;
