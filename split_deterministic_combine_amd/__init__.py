@@ -176,6 +176,13 @@ def _as_rows(x, name="x"):
     return x2, rows, cols, max(ld, cols)
 
 
+def _same_gpu(t, device, name):
+    """Refuse a tensor the kernels cannot address: not on the GPU, or on
+    another GPU than the call's inputs."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != device:
+        raise ValueError("%s must be a GPU tensor on %s" % (name, device))
+
+
 def _dtype_code(t):
     try:
         return _DTYPES[t]
@@ -453,8 +460,11 @@ def splitk_lse_merge(o_part, m_part, l_part, scale=1.0, out_dtype=torch.bfloat16
         rows *= s
     if tuple(m_part.shape) != (P, *rows_shape) or tuple(l_part.shape) != (P, *rows_shape):
         raise ValueError("m_part and l_part must have shape %s" % ((P, *rows_shape),))
+    for t, n in ((m_part, "m_part"), (l_part, "l_part")):
+        _same_gpu(t, o_part.device, n)
     if out is None:
         out = torch.empty((*rows_shape, depth), dtype=out_dtype, device=o_part.device)
+    _same_gpu(out, o_part.device, "out")
     if out.dtype != out_dtype or not out.is_contiguous() or out.numel() != rows * depth:
         raise ValueError("out must be a contiguous %s tensor of %d elements" % (out_dtype, rows * depth))
     with _OnDevice(o_part.device):
@@ -486,6 +496,7 @@ def splitk_attention_partials(q, k, v, P, scale=None, out=None):
                torch.empty((P, rows), dtype=torch.float32, device=q.device))
     o, m, l = out
     for t, shape in ((o, (P, rows, depth)), (m, (P, rows)), (l, (P, rows))):
+        _same_gpu(t, q.device, "out")
         if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != shape:
             raise ValueError("outputs must be contiguous float32 %s, %s, %s"
                              % ((P, rows, depth), (P, rows), (P, rows)))
@@ -504,6 +515,8 @@ def _attention_shapes(q, k, v):
             raise ValueError("%s must be a bfloat16 GPU tensor" % n)
         if not t.is_contiguous() or t.dim() != 4:
             raise ValueError("%s must be a contiguous 4-d tensor" % n)
+    for t, n in ((k, "k"), (v, "v")):
+        _same_gpu(t, q.device, n)
     batch, heads, q_rows, depth = q.shape
     kb, kv_heads, kv_len, kd = k.shape
     if kb != batch or kd != depth or tuple(v.shape) != tuple(k.shape):
@@ -535,6 +548,7 @@ def splitk_attention(q, k, v, P, scale=None, out_dtype=torch.bfloat16, out=None,
         scale = 1.0 / math.sqrt(depth)
     if out is None:
         out = torch.empty((batch, heads, q_rows, depth), dtype=out_dtype, device=q.device)
+    _same_gpu(out, q.device, "out")
     if out.dtype != out_dtype or not out.is_contiguous() or out.numel() != batch * heads * q_rows * depth:
         raise ValueError("out must be a contiguous %s tensor of %d elements"
                          % (out_dtype, batch * heads * q_rows * depth))
@@ -544,6 +558,9 @@ def splitk_attention(q, k, v, P, scale=None, out_dtype=torch.bfloat16, out=None,
         if workspace is None:
             ws = _workspace("attention", q.device, stream.value, need) if need else None
         else:
+            _same_gpu(workspace, q.device, "workspace")
+            if not workspace.is_contiguous():
+                raise ValueError("workspace must be contiguous")
             ws = workspace
         ws_ptr = ctypes.c_void_p(ws.data_ptr()) if ws is not None else None
         ws_len = ws.numel() * ws.element_size() if ws is not None else 0

@@ -278,3 +278,22 @@ def test_fused_random_shapes(case):
                               kv_len=kv_len, depth=depth)
     _fused_vs_two_launch(q, k, v, P, scale, torch.bfloat16 if bf16 else torch.float32,
                          "random %r" % (case,))
+
+
+def test_host_tensors_are_refused_before_any_launch():
+    q, k, v = synth.attention(1030, batch=1, heads=2, kv_heads=2, q_rows=16, kv_len=64, depth=64)
+    tq, tk, tv = _bf16_tensor(q), _bf16_tensor(k), _bf16_tensor(v)
+    with pytest.raises(ValueError):
+        rr.splitk_attention(tq, tk, tv, 2, out=torch.empty((1, 2, 16, 64), dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        rr.splitk_attention(tq, tk, tv, 2, workspace=torch.zeros(1 << 20, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        rr.splitk_attention(tq, tk.cpu(), tv, 2)
+    with pytest.raises(ValueError):
+        rr.splitk_attention_partials(tq, tk, tv, 2, out=(torch.empty((2, 32, 64)),
+                                                         torch.empty((2, 32)), torch.empty((2, 32))))
+    o, m, l = rr.splitk_attention_partials(tq, tk, tv, 2)
+    with pytest.raises(ValueError):
+        rr.splitk_lse_merge(o, m.cpu(), l, 1.0)
+    with pytest.raises(ValueError):
+        rr.splitk_lse_merge(o, m, l, 1.0, torch.bfloat16, out=torch.empty((32, 64), dtype=torch.bfloat16))
