@@ -255,6 +255,7 @@ def reduce_rows(x, op="sum", tier="auto", out=None):
     dt = _dtype_code(x.dtype)
     if out is None:
         out = torch.empty(x.shape[:-1], dtype=x.dtype, device=x.device)
+    _same_gpu(out, x.device, "out")
     if out.dtype != x.dtype or out.numel() != rows or not out.is_contiguous():
         raise ValueError("out must be a contiguous %s tensor of %d elements" % (x.dtype, rows))
     o, t = OPS[op], TIERS[tier]
@@ -293,6 +294,7 @@ def reduce_rows_multi(x, stats=("sum", "max", "min"), tier="auto", out=None):
         t = out.get(k)
         if t is None:
             t = out[k] = torch.empty(x.shape[:-1], dtype=x.dtype, device=x.device)
+        _same_gpu(t, x.device, "out[%r]" % k)
         if t.dtype != x.dtype or t.numel() != rows or not t.is_contiguous():
             raise ValueError("out[%r] must be a contiguous %s tensor of %d elements" % (
                 k, x.dtype, rows))
@@ -335,6 +337,7 @@ def reduce_axis(x, dim, op="sum", tier="auto", out=None):
     dt = _dtype_code(x.dtype)
     if out is None:
         out = torch.empty(oshape, dtype=x.dtype, device=x.device)
+    _same_gpu(out, x.device, "out")
     if out.dtype != x.dtype or tuple(out.shape) != oshape or not out.is_contiguous():
         raise ValueError("out must be a contiguous %s tensor of shape %s" % (x.dtype, oshape))
     o, t = OPS[op], TIERS[tier]
@@ -362,6 +365,7 @@ def softmax_rows(x, out_dtype=None, tier="auto", out=None):
     out_dtype = x.dtype if out_dtype is None else out_dtype
     if out is None:
         out = torch.empty(x.shape, dtype=out_dtype, device=x.device)
+    _same_gpu(out, x.device, "out")
     if out.dtype != out_dtype or out.shape != x.shape:
         raise ValueError("out must be a %s tensor of shape %s" % (out_dtype, tuple(x.shape)))
     y2, _, _, ld_y = _as_rows(out, "out")
@@ -389,12 +393,11 @@ def _layernorm_workspace_need(rows, cols, xdt, ydt, wdt, tier, cu):
     return n
 
 
-def _vector_arg(t, n, dtypes, name):
+def _vector_arg(t, n, dtypes, name, device):
     """Device pointer of an optional contiguous [n] tensor (None -> NULL)."""
     if t is None:
         return None
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
-        raise ValueError("%s must be a GPU tensor" % name)
+    _same_gpu(t, device, name)
     if t.dtype not in dtypes or t.numel() != n or not t.is_contiguous():
         raise ValueError("%s must be a contiguous tensor of %d elements of %s" % (
             name, n, " or ".join(str(d) for d in dtypes)))
@@ -416,6 +419,7 @@ def layernorm_rows(x, gamma=None, beta=None, eps=1e-5, out_dtype=None, tier="aut
     out_dtype = x.dtype if out_dtype is None else out_dtype
     if out is None:
         out = torch.empty(x.shape, dtype=out_dtype, device=x.device)
+    _same_gpu(out, x.device, "out")
     if out.dtype != out_dtype or out.shape != x.shape:
         raise ValueError("out must be a %s tensor of shape %s" % (out_dtype, tuple(x.shape)))
     y2, _, _, ld_y = _as_rows(out, "out")
@@ -424,10 +428,10 @@ def layernorm_rows(x, gamma=None, beta=None, eps=1e-5, out_dtype=None, tier="aut
     if any(w.dtype != w_dtype for w in wts):
         raise ValueError("gamma and beta must have the same dtype")
     wdt = _dtype_code(w_dtype)
-    g_ptr = _vector_arg(gamma, cols, (torch.float32, torch.bfloat16), "gamma")
-    b_ptr = _vector_arg(beta, cols, (torch.float32, torch.bfloat16), "beta")
-    m_ptr = _vector_arg(mean_out, rows, (torch.float32,), "mean_out")
-    r_ptr = _vector_arg(rstd_out, rows, (torch.float32,), "rstd_out")
+    g_ptr = _vector_arg(gamma, cols, (torch.float32, torch.bfloat16), "gamma", x.device)
+    b_ptr = _vector_arg(beta, cols, (torch.float32, torch.bfloat16), "beta", x.device)
+    m_ptr = _vector_arg(mean_out, rows, (torch.float32,), "mean_out", x.device)
+    r_ptr = _vector_arg(rstd_out, rows, (torch.float32,), "rstd_out", x.device)
     xdt, ydt, t = _dtype_code(x.dtype), _dtype_code(out_dtype), TIERS[tier]
     with _OnDevice(x.device):
         stream = _stream_ptr(x.device)

@@ -546,3 +546,22 @@ def test_rr_log_prints_plan(capfd, monkeypatch):
             % (plan["block"], plan["grid"])) in err, err
     assert "rr: rr_softmax_rows rows=64 cols=1024" in err, err
     assert "rr: rr_reduce_axis outer=64 axis=8 inner=128" in err, err
+
+
+def test_host_outputs_are_refused_before_any_launch():
+    x = torch.randn(64, 256, device="cuda")
+    with pytest.raises(ValueError):
+        rr.reduce_rows(x, "sum", out=torch.empty(64))
+    with pytest.raises(ValueError):
+        rr.reduce_rows_multi(x, out={"sum": torch.empty(64)})
+    with pytest.raises(ValueError):
+        rr.reduce_axis(x, 0, "sum", out=torch.empty(256))
+    with pytest.raises(ValueError):
+        rr.softmax_rows(x, out=torch.empty(64, 256))
+    with pytest.raises(ValueError):
+        rr.layernorm_rows(x, out=torch.empty(64, 256))
+    with pytest.raises(ValueError):
+        rr.layernorm_rows(x, torch.ones(256), torch.zeros(256, device="cuda"))
+    with pytest.raises(ValueError):
+        rr.layernorm_rows(x, mean_out=torch.empty(64))
+    torch.cuda.synchronize()
