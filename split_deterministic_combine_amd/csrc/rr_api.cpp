@@ -302,7 +302,7 @@ extern "C" rr_status rr_splitk_attention_partials(const void* q, const void* k, 
         return RR_ERR_SHAPE;
     rr::AttentionLaunch a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                           static_cast<const uint16_t*>(v), o_part, m_part, l_part, batch, heads,
-                          kv_heads, q_rows, kv_len, depth, P, scale, nullptr, RR_F32, nullptr,
+                          kv_heads, q_rows, kv_len, depth, P, scale, nullptr, RR_F32, nullptr, 0,
                           as_stream(stream)};
     if (log_enabled())
         fprintf(stderr,
@@ -373,7 +373,8 @@ extern "C" rr_status rr_splitk_attention(const void* q, const void* k, const voi
                           static_cast<const uint16_t*>(v), reinterpret_cast<float*>(ws + w.o),
                           reinterpret_cast<float*>(ws + w.m), reinterpret_cast<float*>(ws + w.l),
                           batch, heads, kv_heads, q_rows, kv_len, depth, P, scale, out, out_dtype,
-                          reinterpret_cast<uint32_t*>(ws + w.tickets), as_stream(stream)};
+                          reinterpret_cast<uint32_t*>(ws + w.tickets),
+                          g_splitk_skew.load(std::memory_order_relaxed), as_stream(stream)};
     if (log_enabled())
         fprintf(stderr,
                 "rr: rr_splitk_attention batch=%lld heads=%lld kv_heads=%lld q_rows=%lld "

@@ -283,7 +283,7 @@ __global__ __launch_bounds__(kBlockThreads, (attn_workgroups_per_cu<D, FUSED>())
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     float* __restrict__ o, float* __restrict__ m_out, float* __restrict__ l_out, int64_t heads,
     int64_t kv_heads, int64_t q_rows, int64_t kv_len, int32_t P, float scale, int32_t q_tiles,
-    int64_t rows, YT* __restrict__ out, uint32_t* __restrict__ tickets)
+    int64_t rows, YT* __restrict__ out, uint32_t* __restrict__ tickets, int32_t skew)
 {
     constexpr int NC = D / 16;
     constexpr int NT = D / 32;
@@ -618,6 +618,11 @@ __global__ __launch_bounds__(kBlockThreads, (attn_workgroups_per_cu<D, FUSED>())
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         stage_barrier();                               // every wavefront's partial is in
         if (threadIdx.x == 0) {
+            // test hook (normally 0): partition p waits about (P - 1 - p) *
+            // skew sleep periods, so the partitions tend to arrive in
+            // descending order; the fold below does not depend on it
+            for (int i = 0; i < (P - 1 - p) * skew; ++i)
+                __builtin_amdgcn_s_sleep(8);
             const uint32_t t = __hip_atomic_fetch_add(&tickets[grp], 1u, __ATOMIC_RELAXED,
                                                       __HIP_MEMORY_SCOPE_AGENT);
             *last = t == (uint32_t)P - 1;
@@ -695,11 +700,11 @@ static rr_status launch_attn(const AttentionLaunch& a, YT* out)
         return launch_kernel(
             k_attn_staged<128, kAttnStageKeys, attn_stages<128, FUSED>(), FUSED, YT>, grid, block, 0,
             a.stream, a.q, a.k, a.v, a.o, a.m, a.l, a.heads, a.kv_heads, a.q_rows, a.kv_len, a.P,
-            a.scale, q_tiles, rows, out, a.tickets);
+            a.scale, q_tiles, rows, out, a.tickets, a.skew);
     return launch_kernel(k_attn_staged<64, kAttnStageKeys, attn_stages<64, FUSED>(), FUSED, YT>,
                          grid, block, 0, a.stream, a.q, a.k, a.v, a.o, a.m, a.l, a.heads,
                          a.kv_heads, a.q_rows, a.kv_len, a.P, a.scale, q_tiles, rows, out,
-                         a.tickets);
+                         a.tickets, a.skew);
 }
 
 rr_status launch_attention(const AttentionLaunch& a)

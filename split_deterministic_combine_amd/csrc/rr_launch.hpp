@@ -87,6 +87,7 @@ struct AttentionLaunch {
     void* out;            // fused: [rows][depth] of out_dtype; NULL: the partials are the output
     rr_dtype out_dtype;
     uint32_t* tickets;    // fused: one per (head, query tile), zero on entry and on exit
+    int skew;             // fused, test hook: partition arrival skew (0 = off)
     hipStream_t stream;
 };
 

@@ -297,3 +297,20 @@ def test_host_tensors_are_refused_before_any_launch():
         rr.splitk_lse_merge(o, m.cpu(), l, 1.0)
     with pytest.raises(ValueError):
         rr.splitk_lse_merge(o, m, l, 1.0, torch.bfloat16, out=torch.empty((32, 64), dtype=torch.bfloat16))
+
+
+def test_fused_bits_do_not_depend_on_arrival_order():
+    # Under the skew hook the partitions of a query tile take their ticket in
+    # (roughly) descending order, so another workgroup does the fold; it
+    # still visits the partitions in ascending order.
+    q, k, v = synth.attention(1040, batch=2, heads=4, kv_heads=2, q_rows=200, kv_len=3000, depth=128)
+    tq, tk, tv = _bf16_tensor(q), _bf16_tensor(k), _bf16_tensor(v)
+    plain = rr.splitk_attention(tq, tk, tv, 8, None, torch.float32).clone()
+    try:
+        rr._set_splitk_skew(16)
+        skewed = rr.splitk_attention(tq, tk, tv, 8, None, torch.float32).clone()
+        torch.cuda.synchronize()
+    finally:
+        rr._set_splitk_skew(0)
+    assert torch.equal(skewed.view(torch.int32), plain.view(torch.int32))
+    _fused_vs_two_launch(q, k, v, 8, 1.0 / math.sqrt(128), torch.float32, "after the skewed run")
