@@ -21,7 +21,15 @@
 // lane owns one query column of the accumulator, so the rescale of O and the
 // row statistics stay inside the lane.  Q stays in registers as the B
 // operand for the whole walk.  At the end O goes out through LDS as whole
-// 128-byte lines.
+// 128-byte lines.  Depth 128 runs 3 stages in flight at 3 workgroups per CU
+// (the LDS read addresses are formed in every stage rather than held in
+// registers, which keeps the kernel under the 168 registers that allows);
+// depth 64 runs 4 stages.
+//
+// The one-launch variant (FUSED) adds the merge: the last of a query tile's
+// P workgroups to take the tile's ticket folds the P partials, which the
+// workgroups wrote to a workspace through the device-coherent level, with
+// the merge's own per-row functions.
 //
 // Precision: q.k and P V accumulate in float32 inside the MFMA; P is rounded
 // to bf16 as the MFMA operand (the usual flash-attention practice); the
