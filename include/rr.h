@@ -432,14 +432,17 @@ rr_status rr_splitk_attention_partials(const void* q, const void* k, const void*
  *   P           1 .. depth / 8 (the fold keeps P (m, l, weight) cells per row
  *               in LDS)
  *   workspace, workspace_bytes
- *               device, 16-byte aligned, at least
- *               rr_splitk_attention_workspace_bytes; owned by the caller.  Its
- *               first bytes are the tickets, which must be zero before the
- *               first call (rr_workspace_reset over the whole workspace) and
- *               which every completed call leaves zero; the rest holds the
- *               partials and is overwritten by every call, so a workspace
- *               that then serves rr_reduce_rows must be reset first.  One
- *               workspace must not serve two calls in flight.
+ *               device, 16-byte aligned, at least the bytes_out of
+ *               rr_splitk_attention_workspace_bytes; owned by the caller.
+ *               Its first ticket_bytes_out bytes (same query) are the
+ *               tickets and must be zero when the call starts; a completed
+ *               call leaves them zero and overwrites the bytes after them
+ *               with partials.  So a workspace that served a call with a
+ *               smaller ticket region must have the bytes between the two
+ *               ticket sizes cleared (rr_workspace_reset) before a call with
+ *               a larger one, and one that then serves rr_reduce_rows must be
+ *               reset first.  One workspace must not serve two calls in
+ *               flight.
  * Errors (nothing launched): RR_ERR_SHAPE (as rr_splitk_attention_partials,
  * and P > depth / 8), RR_ERR_DTYPE, RR_ERR_NULL, RR_ERR_WORKSPACE;
  * batch*heads*q_rows == 0 is a no-op.
@@ -449,11 +452,15 @@ rr_status rr_splitk_attention(const void* q, const void* k, const void* v, void*
                               int64_t q_rows, int64_t kv_len, int32_t depth, int32_t P,
                               float scale, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace rr_splitk_attention needs for this shape (0 for a no-op
- * shape); the same shape errors as rr_splitk_attention.  Host only. */
+/* Bytes of workspace rr_splitk_attention needs for this shape (bytes_out)
+ * and how many of its first bytes are tickets that must be zero when a call
+ * starts (ticket_bytes_out, may be NULL): 4 per (head, 128 query rows),
+ * rounded up to 256.  0 and 0 for a no-op shape; the same shape errors as
+ * rr_splitk_attention.  Host only. */
 rr_status rr_splitk_attention_workspace_bytes(int64_t batch, int64_t heads, int64_t kv_heads,
                                               int64_t q_rows, int64_t kv_len, int32_t depth,
-                                              int32_t P, size_t* bytes_out);
+                                              int32_t P, size_t* bytes_out,
+                                              size_t* ticket_bytes_out);
 
 /* Bytes of workspace rr_reduce_rows (RR_KIND_REDUCE), rr_softmax_rows
  * (RR_KIND_SOFTMAX, dtype = x_dtype) or rr_layernorm_rows (RR_KIND_LAYERNORM,

@@ -94,6 +94,7 @@ def _load():
         lib.rr_splitk_attention.argtypes = [vp, vp, vp, vp, st, i64, i64, i64, i64, i64, i32, i32,
                                             ctypes.c_float, vp, ctypes.c_size_t, vp]
         lib.rr_splitk_attention_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32, i32,
+                                                            ctypes.POINTER(ctypes.c_size_t),
                                                             ctypes.POINTER(ctypes.c_size_t)]
         lib.rr_reduce_axis.argtypes = [vp, vp, i64, i64, i64, st, st, st, vp, ctypes.c_size_t, vp]
         lib.rr_plan_axis.argtypes = [i64, i64, i64, st, st, st, i32, ctypes.POINTER(_Plan)]
@@ -528,12 +529,37 @@ def _attention_shapes(q, k, v):
     return batch, heads, kv_heads, q_rows, kv_len, depth
 
 
-def splitk_attention_workspace_bytes(batch, heads, kv_heads, q_rows, kv_len, depth, P):
-    """Bytes of workspace splitk_attention needs (host only)."""
-    n = ctypes.c_size_t(0)
+def splitk_attention_workspace_bytes(batch, heads, kv_heads, q_rows, kv_len, depth, P,
+                                     with_tickets=False):
+    """Bytes of workspace splitk_attention needs (host only); with
+    ``with_tickets``, also how many of its first bytes must be zero when a
+    call starts (the tickets)."""
+    n, t = ctypes.c_size_t(0), ctypes.c_size_t(0)
     _check(_load().rr_splitk_attention_workspace_bytes(batch, heads, kv_heads, q_rows, kv_len,
-                                                       depth, int(P), ctypes.byref(n)))
-    return n.value
+                                                       depth, int(P), ctypes.byref(n),
+                                                       ctypes.byref(t)))
+    return (n.value, t.value) if with_tickets else n.value
+
+
+# The cached one-launch attention workspaces, per (device, stream): the
+# tensor and how many of its first bytes are known to be zero.  A completed
+# call leaves its ticket bytes zero and its partials after them, so before a
+# call whose ticket region is larger, the bytes in between are cleared.
+_attn_ws = {}
+
+
+def _attention_workspace(device, stream, need, tickets):
+    key = (device.index, stream.value)
+    ent = _attn_ws.get(key)
+    if ent is None or ent[0].numel() < need:
+        ws = torch.zeros(max(need, 4096), dtype=torch.uint8, device=device)
+        ent = _attn_ws[key] = [ws, ws.numel()]
+    ws, zero = ent
+    if tickets > zero:
+        _check(_load().rr_workspace_reset(ctypes.c_void_p(ws.data_ptr() + zero), tickets - zero,
+                                          stream))
+    ent[1] = tickets        # after this call: tickets zero, partials after them
+    return ws
 
 
 def splitk_attention(q, k, v, P, scale=None, out_dtype=torch.bfloat16, out=None, workspace=None):
@@ -543,8 +569,10 @@ def splitk_attention(q, k, v, P, scale=None, out_dtype=torch.bfloat16, out=None,
     Shapes as splitk_attention_partials; returns [batch, heads, q_rows, depth]
     in ``out_dtype`` (bfloat16 or float32), bit-identical to
     ``splitk_lse_merge(*splitk_attention_partials(q, k, v, P, scale), 1.0,
-    out_dtype)``.  ``workspace`` (uint8, zeroed before its first use) defaults
-    to one cached per device and stream.
+    out_dtype)``.  ``workspace`` (uint8) defaults to one cached per device and
+    stream; a caller's own must hold zeros in its first ticket bytes
+    (``splitk_attention_workspace_bytes(..., with_tickets=True)``) when the
+    call starts, which every completed call leaves so.
     """
     lib = _load()
     batch, heads, kv_heads, q_rows, kv_len, depth = _attention_shapes(q, k, v)
@@ -556,11 +584,12 @@ def splitk_attention(q, k, v, P, scale=None, out_dtype=torch.bfloat16, out=None,
     if out.dtype != out_dtype or not out.is_contiguous() or out.numel() != batch * heads * q_rows * depth:
         raise ValueError("out must be a contiguous %s tensor of %d elements"
                          % (out_dtype, batch * heads * q_rows * depth))
-    need = splitk_attention_workspace_bytes(batch, heads, kv_heads, q_rows, kv_len, depth, P)
+    need, tickets = splitk_attention_workspace_bytes(batch, heads, kv_heads, q_rows, kv_len,
+                                                     depth, P, with_tickets=True)
     with _OnDevice(q.device):
         stream = _stream_ptr(q.device)
         if workspace is None:
-            ws = _workspace("attention", q.device, stream.value, need) if need else None
+            ws = _attention_workspace(q.device, stream, need, tickets) if need else None
         else:
             _same_gpu(workspace, q.device, "workspace")
             if not workspace.is_contiguous():

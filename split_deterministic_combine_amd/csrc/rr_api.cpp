@@ -339,14 +339,17 @@ AttnWorkspace attn_workspace(int64_t batch, int64_t heads, int64_t q_rows, int32
 extern "C" rr_status rr_splitk_attention_workspace_bytes(int64_t batch, int64_t heads,
                                                          int64_t kv_heads, int64_t q_rows,
                                                          int64_t kv_len, int32_t depth, int32_t P,
-                                                         size_t* bytes_out)
+                                                         size_t* bytes_out,
+                                                         size_t* ticket_bytes_out)
 {
     if (!bytes_out) return RR_ERR_NULL;
     int64_t work = 0;
     rr_status st = check_attention(batch, heads, kv_heads, q_rows, kv_len, depth, P, 1.0f, &work);
     if (st != RR_OK) return st;
     if (P > depth / 8) return RR_ERR_SHAPE;
-    *bytes_out = work == 0 ? 0 : (size_t)attn_workspace(batch, heads, q_rows, depth, P).total;
+    const AttnWorkspace w = attn_workspace(batch, heads, q_rows, depth, P);
+    *bytes_out = work == 0 ? 0 : (size_t)w.total;
+    if (ticket_bytes_out) *ticket_bytes_out = work == 0 ? 0 : (size_t)w.o;
     return RR_OK;
 }
 

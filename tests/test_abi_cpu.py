@@ -362,6 +362,7 @@ def test_fused_attention_validates_before_touching_the_device():
     lib.rr_splitk_attention.argtypes = [vp, vp, vp, vp, st, i64, i64, i64, i64, i64, i32, i32,
                                         ctypes.c_float, vp, ctypes.c_size_t, vp]
     lib.rr_splitk_attention_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32, i32,
+                                                        ctypes.POINTER(ctypes.c_size_t),
                                                         ctypes.POINTER(ctypes.c_size_t)]
     f = lib.rr_splitk_attention
     ok = dict(batch=2, heads=4, kv_heads=2, q_rows=200, kv_len=16, depth=128, P=8, scale=0.1,
@@ -369,20 +370,25 @@ def test_fused_attention_validates_before_touching_the_device():
 
     def need(**kw):
         a = dict(ok, **kw)
-        n = ctypes.c_size_t(7)
+        n, t = ctypes.c_size_t(7), ctypes.c_size_t(7)
         s = lib.rr_splitk_attention_workspace_bytes(a["batch"], a["heads"], a["kv_heads"],
                                                     a["q_rows"], a["kv_len"], a["depth"], a["P"],
-                                                    ctypes.byref(n))
+                                                    ctypes.byref(n), ctypes.byref(t))
+        need.tickets = t.value
         return s, n.value
 
     # tickets for 2*4*2 (head, query tile) groups padded to 256 bytes, then
     # O_p, m_p and l_p for P whole 128-row tiles of every group
     cells = 2 * 4 * 2 * 8 * 128
-    assert need() == (0, 256 + cells * 128 * 4 + 2 * cells * 4)
+    assert need() == (0, 256 + cells * 128 * 4 + 2 * cells * 4) and need.tickets == 256
+    assert need(batch=40, q_rows=1)[0] == 0 and need.tickets == 768   # 160 tickets, 640 B
     assert need(P=17)[0] == 2 and need(depth=64, P=9)[0] == 2   # P <= depth / 8
     assert need(depth=64, P=8)[0] == 0
     assert need(q_rows=0) == (0, 0)
-    assert lib.rr_splitk_attention_workspace_bytes(1, 1, 1, 1, 1, 128, 1, None) == 1
+    assert lib.rr_splitk_attention_workspace_bytes(1, 1, 1, 1, 1, 128, 1, None, None) == 1
+    n = ctypes.c_size_t(0)
+    assert lib.rr_splitk_attention_workspace_bytes(1, 1, 1, 1, 1, 128, 1, ctypes.byref(n),
+                                                   None) == 0 and n.value > 0
     ws_len = need()[1]
 
     def call(ptr=256, ws=4096, ws_len=ws_len, **kw):

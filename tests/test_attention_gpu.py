@@ -314,3 +314,21 @@ def test_fused_bits_do_not_depend_on_arrival_order():
         rr._set_splitk_skew(0)
     assert torch.equal(skewed.view(torch.int32), plain.view(torch.int32))
     _fused_vs_two_launch(q, k, v, 8, 1.0 / math.sqrt(128), torch.float32, "after the skewed run")
+
+
+def test_fused_cached_workspace_grows_its_ticket_region():
+    # A call with few query tiles but large partials, then one with more
+    # tiles (a ticket region past the first 256 bytes) and smaller partials:
+    # the cached workspace is reused, and the second call's tickets lie where
+    # the first call left partials, so the binding clears them first.
+    qa, ka, va = synth.attention(1050, batch=1, heads=1, kv_heads=1, q_rows=1024, kv_len=64,
+                                 depth=128)
+    _fused_vs_two_launch(qa, ka, va, 16, 0.1, torch.float32, "few tiles, large partials")
+    qb, kb, vb = synth.attention(1051, batch=4, heads=32, kv_heads=32, q_rows=16, kv_len=50,
+                                 depth=64)
+    need_a = rr.splitk_attention_workspace_bytes(1, 1, 1, 1024, 64, 128, 16)
+    need_b, tick_b = rr.splitk_attention_workspace_bytes(4, 32, 32, 16, 50, 64, 1,
+                                                         with_tickets=True)
+    assert need_b < need_a and tick_b > 256
+    for _ in range(2):
+        _fused_vs_two_launch(qb, kb, vb, 1, 0.125, torch.bfloat16, "more tiles, reused workspace")
