@@ -277,7 +277,7 @@ def sq_summary(op, dirs):
             if pat in r["Kernel_Name"]:
                 vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
     cmds = "\n".join(
-        "    cd /tmp && export TMPDIR=/tmp && timeout -s KILL 90 rocprofv3 --pmc %s -f csv "
+        "    cd /tmp && export TMPDIR=/tmp && timeout -s KILL 120 rocprofv3 --pmc %s -f csv "
         "-d $R/gpurun_out/sq_%s_%d -o sq -- python3 $R/bench.py --only %s --steps 3 --warmup 0 "
         "--no-parity --no-cpu-baseline" % (" ".join(c), op, i, op) for i, c in enumerate(SQ_PASSES))
     rows = ["| counter | mean per dispatch | dispatches |", "|---|---|---|"]
