@@ -429,3 +429,26 @@ def test_product_path_has_no_cpu_fallback():
         rr.softmax_rows(x.bfloat16())
     src = open(os.path.join(ROOT, "split_deterministic_combine_amd", "__init__.py")).read()
     assert "oracle" not in src
+
+
+def test_binding_argtypes_match_the_header_prototypes():
+    # every prototype in rr.h / rr_test.h against the ctypes argtypes the
+    # binding sets for it: a drifted signature would pass garbage silently
+    import re
+    lib = rr._load()
+    protos = {}
+    for h in ("rr.h", "rr_test.h"):
+        text = open(os.path.join(ROOT, "include", h)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"\b(?:rr_status|void|int|const char\*)\s+(rr_\w+)\s*\(([^)]*)\)\s*;", text):
+            params = m.group(2).strip()
+            protos[m.group(1)] = 0 if params in ("", "void") else params.count(",") + 1
+    assert len(protos) >= 20
+    checked = 0
+    for name, n in protos.items():
+        fn = getattr(lib, name)
+        if fn.argtypes is None:
+            continue
+        assert len(fn.argtypes) == n, (name, len(fn.argtypes), n)
+        checked += 1
+    assert checked >= 15
