@@ -395,6 +395,36 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float a)
     return __builtin_bit_cast(uint16_t, (__bf16)a);
 }
 
+// double -> float rounded to odd: truncate toward zero and, if anything was
+// dropped, set the last fraction bit.  Boldo and Melquiond ("Emulation of FMA
+// and correctly rounded sums: proved algorithms using rounding to odd", IEEE
+// Trans. Computers 57(4), 2008) show that a rounding to odd into a format
+// with at least two more bits, followed by a rounding to nearest even into
+// the narrower format, equals one rounding to nearest even.  float carries 16
+// more fraction bits than bf16, so the pair below rounds a double to bf16
+// once, where (float)a followed by the bf16 conversion can round twice (a
+// value just above a bf16 tie becomes the tie in float and then rounds to
+// even, one bf16 ulp low).  NaN stays NaN.
+__device__ __forceinline__ float f32_round_odd(double a)
+{
+    float f = (float)a;  // nearest even
+    if ((double)f != a) {
+        uint32_t u = __float_as_uint(f);
+        if (fabs((double)f) > fabs(a))
+            u -= 1u;     // rounded away from zero (incl. overflow to inf): one step back
+        f = __uint_as_float(u | 1u);
+    }
+    return f;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2_from_double(double a, double b)
+{
+    return pack_bf16x2(f32_round_odd(a), f32_round_odd(b));
+}
+__device__ __forceinline__ uint16_t bf16_bits_from_double(double a)
+{
+    return f32_to_bf16_bits(f32_round_odd(a));
+}
+
 // ------------------------------------------ cross-workgroup publishing
 // Publishing a partial across workgroups (and across the eight XCDs, whose
 // L2 caches are not coherent with each other).  The partial is written with a

@@ -71,7 +71,9 @@ __device__ __forceinline__ void merge_accumulate(double* acc, double cp, const f
 }
 
 // Four accumulated values of an output row, rounded once to YT (bf16 bits
-// or float) and stored together.
+// or float) and stored together.  bf16: the double goes to float rounded to
+// odd, then to bf16 rounded to nearest even -- one correct rounding of the
+// double (f32_round_odd).
 template <class YT>
 struct MergeOut;
 template <>
@@ -79,11 +81,11 @@ struct MergeOut<uint16_t> {
     __device__ static void four(uint16_t* p, const double* a)
     {
         uint2 u;
-        u.x = pack_bf16x2((float)a[0], (float)a[1]);
-        u.y = pack_bf16x2((float)a[2], (float)a[3]);
+        u.x = pack_bf16x2_from_double(a[0], a[1]);
+        u.y = pack_bf16x2_from_double(a[2], a[3]);
         store8_nt(p, u);
     }
-    __device__ static void one(uint16_t* p, double a) { *p = f32_to_bf16_bits((float)a); }
+    __device__ static void one(uint16_t* p, double a) { *p = bf16_bits_from_double(a); }
 };
 template <>
 struct MergeOut<float> {

@@ -25,8 +25,11 @@ constexpr float kNegInf = -__builtin_inff();
 
 // Pass 1 on values held by one thread: m = max, v <- exp(v - m), s = sum v.
 // With m == -inf (nothing but -inf / padding) every p is 0.
-// The exponent argument is x*log2(e) - m*log2(e) in one fused multiply-add.
-// The hardware exponential is exact for normal results; when any argument
+// The exponent argument is (x - m) * log2(e): the difference first, so its
+// error is relative to the (small) argument whatever the size of m.  A
+// fused x*log2(e) - m*log2(e) would carry the rounding of m*log2(e), half an
+// ulp of |m|*1.44, into every exponent (a relative error of 4e-5 at m = 1000,
+// different in every thread).  The hardware exponential is exact for normal results; when any argument
 // falls below -126 (a subnormal or vanishing result, or a -inf entry) the
 // thread recomputes its values with exp2f, which scales the range itself.
 template <int N>
@@ -38,11 +41,10 @@ __device__ __forceinline__ MS local_exp_sum(float* v)
         m = fmaxf(m, v[i]);
     float s = 0.0f;
     if (m != kNegInf) {
-        const float mb = -m * kLog2e;
         float tmin = 0.0f;
 #pragma unroll
         for (int i = 0; i < N; ++i) {
-            v[i] = __builtin_fmaf(v[i], kLog2e, mb);
+            v[i] = (v[i] - m) * kLog2e;
             tmin = fminf(tmin, v[i]);
         }
         if (tmin >= -126.0f) {
@@ -364,10 +366,9 @@ __device__ __forceinline__ void stats_fold_tile(float* v, float& tm, double& ts)
     const float M = fmaxf(tm, cm);
     if (M == kNegInf)
         return;
-    const float mb = -M * kLog2e;
 #pragma unroll
     for (int i = 0; i < N; ++i)
-        v[i] = exp2_hw(__builtin_fmaf(v[i], kLog2e, mb));
+        v[i] = exp2_hw((v[i] - M) * kLog2e);
 #pragma unroll
     for (int w = N / 2; w >= 1; w /= 2)
 #pragma unroll
@@ -449,11 +450,11 @@ __global__ __launch_bounds__(kBlockThreads) void k_softmax_splitk_stats(
 
 // y = exp(x - M) / S on the tile's values, in place.
 template <int N>
-__device__ __forceinline__ void map_tile(float* v, float mb, float inv)
+__device__ __forceinline__ void map_tile(float* v, float M, float inv)
 {
 #pragma unroll
     for (int i = 0; i < N; ++i)
-        v[i] = __builtin_fmaf(v[i], kLog2e, mb);
+        v[i] = (v[i] - M) * kLog2e;
     exp2_values<N>(v);
 #pragma unroll
     for (int i = 0; i < N; ++i)
@@ -503,17 +504,16 @@ __global__ __launch_bounds__(kBlockThreads) void k_softmax_splitk_map(
         if (t < nfull)
             load_tile_full<XT, E, VEC, U>(xr + t * kTile, v);
         const MS st = fold_row_partials(p, fslot, dslot);
-        const float mb = -st.m * kLog2e;
         const float inv = 1.0f / st.s;
         for (; t < nfull; t += G) {
-            map_tile<U * E>(v, mb, inv);
+            map_tile<U * E>(v, st.m, inv);
             store_tile_full<YT, E, VEC, U>(yr + t * kTile, v);
             if (t + G < nfull)
                 load_tile_full<XT, E, VEC, U>(xr + (t + G) * kTile, v);
         }
         for (; t < ntiles; t += G) {
             load_tile_padded<XT, E, VEC, U>(xr, t * kTile, cols, v);
-            map_tile<U * E>(v, mb, inv);
+            map_tile<U * E>(v, st.m, inv);
             store_tile_masked<YT, E, VEC, U>(yr, t * kTile, cols, v);
         }
         __syncthreads();  // the fold's LDS slots are reused by the next row

@@ -333,6 +333,37 @@ def test_softmax_wide_logit_range():
         _check_softmax(y, ref, yt, "wide range " + yt)
 
 
+def _spiked_rows(seed, rows, cols, offset, spikes=8):
+    """Rows at a large common offset: `spikes` entries spread over the row at
+    offset + N(0, 1), the rest 40 below (their exponentials ~1e-17), so the
+    outputs that matter are ~1/spikes and the relative 1e-5 term of the f32
+    bar decides pass or fail, wherever the tier puts its per-thread maxima."""
+    rng = np.random.default_rng(seed)
+    x = (offset - 40.0 + rng.standard_normal((rows, cols))).astype(np.float32)
+    for r in range(rows):
+        at = rng.choice(cols, size=min(spikes, cols), replace=False)
+        x[r, at] = (offset + rng.standard_normal(at.size)).astype(np.float32)
+    return x
+
+
+@pytest.mark.parametrize("offset", [-3000.0, -1000.0, 1000.0, 3000.0, 1.0e6])
+def test_softmax_large_row_maxima_keep_the_relative_bar(offset):
+    # The exponent argument must be formed from x - m: a rounded m*log2(e)
+    # would put an error of half an ulp of |m|*1.44 into every exponent (a
+    # relative error of 4e-5 at |m| = 1000), different in every thread.
+    for cols, tiers in ((10, ("auto", "wave", "block", "tiled", "serial")),
+                        (3000, ("auto", "block", "tiled")),
+                        (8192, ("auto", "block")),
+                        (70001, ("auto", "splitk"))):
+        rows = 7 if cols > 5000 else 24
+        x = _spiked_rows(int(abs(offset)) + cols, rows, cols, offset)
+        ref = oracle.softmax_rows(x, "f32")
+        assert ref.max() > 0.05  # the relative term decides
+        for tier in tiers:
+            y = to_host(rr.softmax_rows(to_gpu(x), torch.float32, tier))
+            assert_close_f32(y, ref, "offset %g cols %d %s" % (offset, cols, tier))
+
+
 def test_softmax_in_place():
     x = _softmax_input("bf16", 9, 3000, 41)
     ref = oracle.softmax_rows(x, "bf16")
@@ -490,6 +521,46 @@ def test_merge_large_spread_of_maxima():
     o, m, l = _merge_case(4, 40, 64, 23)
     m[1] += 900.0   # exp(scale * (m_p - M)) underflows for every other partition
     _check_merge(o, m, l, 1.0, "spread")
+
+
+def _bf16_ties(rng, n):
+    """Float bit patterns of bf16 ties: a random normal bf16 value plus half a
+    bf16 ulp (fraction bit 15 set, bits 0..14 clear), both signs."""
+    h = rng.integers(0x3800, 0x4800, size=n).astype(np.uint32)  # |v| in [2^-15, 2^17)
+    sign = rng.integers(0, 2, size=n).astype(np.uint32) << 31
+    return sign | (h << 16) | 0x8000
+
+
+def test_merge_bf16_rounds_once_near_ties():
+    # P = 2 with equal statistics: c_0 = c_1 = 1/2 exactly, so the double sum
+    # is (O_0 + O_1) / 2 with no error.  O_0 is a bf16 tie and O_1 the float
+    # one step above or below it, so the sum lies half a float ulp off the
+    # tie: rounded to float first it becomes the tie (float's nearest even)
+    # and then rounds to the even bf16, the wrong way in half of the cases.
+    # One rounding of the double, as the oracle does, must give the oracle's
+    # bits exactly.
+    rng = np.random.default_rng(404)
+    rows, depth = 64, 128
+    tie = _bf16_ties(rng, rows * depth)
+    step = np.where(rng.random(rows * depth) < 0.5, 1, -1).astype(np.int64)
+    o = np.empty((2, rows, depth), dtype=np.float32)
+    o[0] = tie.view(np.float32).reshape(rows, depth)
+    o[1] = (tie.astype(np.int64) + step).astype(np.uint32).view(np.float32).reshape(rows, depth)
+    m = np.full((2, rows), 0.75, dtype=np.float32)
+    l = np.full((2, rows), 3.0, dtype=np.float32)
+    ref = oracle.splitk_lse_merge(o, m, l, 1.0, "bf16")
+    # the case is live: rounding the exact mean to float first, then to bf16,
+    # differs from the oracle's one rounding on many elements
+    mean_f = ((o[0].astype(np.float64) + o[1]) / 2).astype(np.float32)
+    twice = torch.from_numpy(mean_f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert (twice != ref).sum() > rows * depth // 8
+    assert_exact(_run_merge(o, m, l, 1.0, "bf16"), ref, "bf16 near ties")
+    assert_exact(_run_merge(o, m, l, 1.0, "f32"), oracle.splitk_lse_merge(o, m, l, 1.0, "f32"),
+                 "f32 near ties")
+    # the same rows through the row-outer kernel (depth not one 128-bit chunk per lane)
+    o3 = np.ascontiguousarray(o[:, :, :100])
+    assert_exact(_run_merge(o3, m, l, 1.0, "bf16"), oracle.splitk_lse_merge(o3, m, l, 1.0, "bf16"),
+                 "bf16 near ties, depth 100")
 
 
 def test_merge_config_full_size():
