@@ -76,7 +76,9 @@ typedef enum {
     RR_ERR_TIER = 4,      /* forced tier is not legal for this shape / kind */
     RR_ERR_WORKSPACE = 5, /* split-K workspace missing or too small */
     RR_ERR_HIP = 6,       /* a HIP runtime call or launch failed */
-    RR_ERR_OP = 7         /* unknown reduction op */
+    RR_ERR_OP = 7,        /* unknown reduction op */
+    RR_ERR_SCRATCH = 8    /* rr_reduce_rows_noalloc: the plan's split-K workspace is
+                             larger than RR_NOALLOC_SCRATCH_BYTES */
 } rr_status;
 
 typedef enum { RR_F32 = 0, RR_I32 = 1, RR_BF16 = 2 } rr_dtype;
@@ -100,6 +102,9 @@ typedef enum { RR_KIND_REDUCE = 0, RR_KIND_SOFTMAX = 1, RR_KIND_LAYERNORM = 2 } 
 
 /* Rows owned by one thread in the tiled tier (the page's emit_tile_width). */
 #define RR_TILED_ROWS 4
+/* Bytes of device memory per GPU that rr_reduce_rows_noalloc uses as its
+ * split-K workspace (a scratch array inside the library). */
+#define RR_NOALLOC_SCRATCH_BYTES (1 << 20)
 /* Largest partition count accepted by rr_splitk_lse_merge. */
 #define RR_MERGE_MAX_P 256
 
@@ -205,6 +210,34 @@ rr_status rr_plan_layernorm(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dty
 rr_status rr_reduce_rows(const void* x, void* y, int64_t rows, int64_t cols, int64_t ld,
                          rr_dtype dtype, rr_op op, rr_tier tier, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/*
+ * rr_reduce_rows_noalloc -- rr_reduce_rows for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc.  Arguments, results and errors as
+ * rr_reduce_rows, without the workspace: the split-K tier uses a scratch
+ * array inside the library instead, RR_NOALLOC_SCRATCH_BYTES (1 MiB) of
+ * device memory per GPU, which each GPU the call runs on holds from the
+ * first call there until the process ends.  The call allocates nothing
+ * (no hipMalloc, no allocating library routine).  The same plan and kernels
+ * as rr_reduce_rows run, so the results are bit-identical to it.
+ *
+ *   x, y, rows, cols, ld, dtype, op, tier, stream   as rr_reduce_rows
+ *
+ * Split-K: the first call on a device looks up the device address of that
+ * GPU's copy of the array (RR_ERR_HIP if that fails); every split-K call
+ * then clears the bytes it uses with a fill kernel on `stream` (tickets must
+ * start at zero; the array keeps what the previous call left) before its
+ * reduction launch.  Every call on one GPU shares that GPU's array: calls
+ * that overlap in time on one GPU (two streams, or two host threads) race
+ * and give wrong results.  Returns RR_ERR_SCRATCH, launching nothing, when
+ * the plan's workspace (rr_workspace_bytes) exceeds RR_NOALLOC_SCRATCH_BYTES
+ * (a forced split-K over very many rows; an automatic split-K plan has
+ * rows < CU count and needs at most a few KiB).  Tiers other than split-K
+ * use no workspace and behave exactly as rr_reduce_rows.
+ */
+rr_status rr_reduce_rows_noalloc(const void* x, void* y, int64_t rows, int64_t cols, int64_t ld,
+                                 rr_dtype dtype, rr_op op, rr_tier tier, void* stream);
 
 /*
  * rr_reduce_rows_multi -- the sum, the maximum and the minimum of every row

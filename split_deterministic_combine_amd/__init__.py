@@ -8,6 +8,9 @@ the first call raises.
 
 Operations (names as in the C ABI):
   reduce_rows        sum / max / min over the last axis (float32, int32)
+  reduce_rows_noalloc
+                     the same with the library's own split-K scratch (for
+                     callers that cannot allocate; the output is passed in)
   reduce_rows_multi  sum, max and min over the last axis from one read
   reduce_axis        sum / max / min over a non-last axis
   softmax_rows       two-pass softmax over the last axis (bf16 / float32)
@@ -28,7 +31,7 @@ import threading
 import torch
 
 __all__ = [
-    "RRError", "reduce_rows", "reduce_rows_multi", "reduce_axis", "plan_axis", "softmax_rows", "layernorm_rows", "splitk_lse_merge",
+    "RRError", "reduce_rows", "reduce_rows_noalloc", "reduce_rows_multi", "reduce_axis", "plan_axis", "softmax_rows", "layernorm_rows", "splitk_lse_merge",
     "splitk_attention_partials", "splitk_attention", "splitk_attention_workspace_bytes",
     "plan_reduce", "plan_softmax", "plan_layernorm", "select_tier", "workspace_bytes", "workspace_reset", "device_cu_count",
     "version", "lib_path", "TIERS", "OPS",
@@ -84,6 +87,7 @@ def _load():
         lib = ctypes.CDLL(_LIB_PATH)
         vp, i64, i32, st = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int
         lib.rr_reduce_rows.argtypes = [vp, vp, i64, i64, i64, st, st, st, vp, ctypes.c_size_t, vp]
+        lib.rr_reduce_rows_noalloc.argtypes = [vp, vp, i64, i64, i64, st, st, st, vp]
         lib.rr_reduce_rows_multi.argtypes = [vp, vp, vp, vp, i64, i64, i64, st, st, vp,
                                              ctypes.c_size_t, vp]
         lib.rr_softmax_rows.argtypes = [vp, vp, i64, i64, i64, i64, st, st, st, vp,
@@ -113,7 +117,7 @@ def _load():
         lib.rr_test_set_splitk_skew.argtypes = [i32]
         lib.rr_test_set_splitk_skew.restype = None
         lib.rr_test_stream.argtypes = [i32, vp, vp, ctypes.c_size_t, i32, vp]
-        for name in ("rr_reduce_rows", "rr_reduce_rows_multi", "rr_reduce_axis", "rr_plan_axis",
+        for name in ("rr_reduce_rows", "rr_reduce_rows_noalloc", "rr_reduce_rows_multi", "rr_reduce_axis", "rr_plan_axis",
                      "rr_softmax_rows", "rr_splitk_lse_merge", "rr_plan_reduce",
                      "rr_plan_softmax", "rr_layernorm_rows", "rr_plan_layernorm",
                      "rr_workspace_bytes", "rr_select_tier",
@@ -269,6 +273,28 @@ def reduce_rows(x, op="sum", tier="auto", out=None):
             ws_ptr, ws_len = ctypes.c_void_p(ws.data_ptr()), ws.numel()
         _check(lib.rr_reduce_rows(ctypes.c_void_p(x2.data_ptr()), ctypes.c_void_p(out.data_ptr()),
                                   rows, cols, ld, dt, o, t, ws_ptr, ws_len, stream))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 1 << 20  # RR_NOALLOC_SCRATCH_BYTES
+
+
+def reduce_rows_noalloc(x, out, op="sum", tier="auto"):
+    """``reduce_rows`` through ``rr_reduce_rows_noalloc``: no workspace and no
+    allocation -- ``out`` (contiguous, ``rows`` elements of x's dtype, on x's
+    GPU) must be passed in; the split-K tier uses the library's scratch array
+    (RR_NOALLOC_SCRATCH_BYTES per GPU).  Calls that overlap in time on one GPU
+    share that array and must not be made."""
+    lib = _lib or _load()
+    x2, rows, cols, ld = _as_rows(x)
+    dt = _dtype_code(x.dtype)
+    _same_gpu(out, x.device, "out")
+    if out.dtype != x.dtype or out.numel() != rows or not out.is_contiguous():
+        raise ValueError("out must be a contiguous %s tensor of %d elements" % (x.dtype, rows))
+    with _OnDevice(x.device):
+        _check(lib.rr_reduce_rows_noalloc(ctypes.c_void_p(x2.data_ptr()),
+                                          ctypes.c_void_p(out.data_ptr()), rows, cols, ld, dt,
+                                          OPS[op], TIERS[tier], _stream_ptr(x.device)))
     return out
 
 

@@ -99,9 +99,13 @@ extern "C" rr_status rr_device_cu_count(int32_t* cu_out)
     return current_cu(cu_out);
 }
 
-extern "C" rr_status rr_reduce_rows(const void* x, void* y, int64_t rows, int64_t cols,
+// rr_reduce_rows and rr_reduce_rows_noalloc: the same plan and kernels; the
+// split-K workspace is the caller's (noalloc false) or the library's own
+// per-device scratch array (noalloc true).
+static rr_status reduce_rows_common(const void* x, void* y, int64_t rows, int64_t cols,
                                     int64_t ld, rr_dtype dtype, rr_op op, rr_tier tier,
-                                    void* workspace, size_t workspace_bytes, void* stream)
+                                    bool noalloc, void* workspace, size_t workspace_bytes,
+                                    void* stream)
 {
     if (op == RR_SUM_MAX_MIN) return RR_ERR_OP;  // that is rr_reduce_rows_multi
     // Shape / type / tier checks that need no device.
@@ -120,11 +124,38 @@ extern "C" rr_status rr_reduce_rows(const void* x, void* y, int64_t rows, int64_
                        as_stream(stream)};
     if (cols == 0) return rr::launch_reduce_identity(a);
     if (p.tier == RR_TIER_SPLITK) {
-        if (!workspace || workspace_bytes < p.workspace_bytes || !aligned(workspace, 8))
+        if (noalloc) {
+            if (p.workspace_bytes > RR_NOALLOC_SCRATCH_BYTES) return RR_ERR_SCRATCH;
+            void* ws = nullptr;
+            if ((st = rr::noalloc_scratch(&ws)) != RR_OK) return st;
+            // The array keeps what the last call on this GPU left there; the
+            // tickets must start at zero, so the bytes this call uses are
+            // cleared first (a fill kernel: no memset node, no allocation).
+            if ((st = rr::launch_fill_zero(ws, (size_t)p.workspace_bytes, a.stream)) != RR_OK)
+                return st;
+            a.workspace = ws;
+        } else if (!workspace || workspace_bytes < p.workspace_bytes || !aligned(workspace, 8)) {
             return RR_ERR_WORKSPACE;
+        }
     }
-    log_plan("rr_reduce_rows", "rows", rows, "cols", cols, nullptr, 0, vec, p);
+    log_plan(noalloc ? "rr_reduce_rows_noalloc" : "rr_reduce_rows", "rows", rows, "cols", cols,
+             nullptr, 0, vec, p);
     return rr::launch_reduce(p, a);
+}
+
+extern "C" rr_status rr_reduce_rows(const void* x, void* y, int64_t rows, int64_t cols,
+                                    int64_t ld, rr_dtype dtype, rr_op op, rr_tier tier,
+                                    void* workspace, size_t workspace_bytes, void* stream)
+{
+    return reduce_rows_common(x, y, rows, cols, ld, dtype, op, tier, false, workspace,
+                              workspace_bytes, stream);
+}
+
+extern "C" rr_status rr_reduce_rows_noalloc(const void* x, void* y, int64_t rows, int64_t cols,
+                                            int64_t ld, rr_dtype dtype, rr_op op, rr_tier tier,
+                                            void* stream)
+{
+    return reduce_rows_common(x, y, rows, cols, ld, dtype, op, tier, true, nullptr, 0, stream);
 }
 
 extern "C" rr_status rr_reduce_rows_multi(const void* x, void* y_sum, void* y_max, void* y_min,

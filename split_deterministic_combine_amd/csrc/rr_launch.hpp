@@ -99,5 +99,8 @@ rr_status launch_attention(const AttentionLaunch& a);
 rr_status launch_layernorm(const rr_plan& plan, const LayernormLaunch& a);
 rr_status launch_reduce_axis(const rr_plan& plan, const AxisLaunch& a);
 rr_status launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
+// Device address of this GPU's copy of the library's scratch array
+// (RR_NOALLOC_SCRATCH_BYTES, rr_reduce.hip), looked up once per device.
+rr_status noalloc_scratch(void** out);
 
 }  // namespace rr

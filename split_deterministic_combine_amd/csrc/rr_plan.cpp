@@ -303,6 +303,9 @@ extern "C" const char* rr_status_string(rr_status s)
     case RR_ERR_WORKSPACE: return "split-K workspace missing or too small";
     case RR_ERR_HIP: return "HIP runtime error";
     case RR_ERR_OP: return "unknown reduction op";
+    case RR_ERR_SCRATCH: return "the shape needs more split-K workspace than the library's "
+                                "scratch array holds (RR_NOALLOC_SCRATCH_BYTES); pass a "
+                                "workspace to rr_reduce_rows instead";
     }
     return "unknown status";
 }

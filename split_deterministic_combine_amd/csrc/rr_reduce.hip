@@ -12,6 +12,7 @@
 // The monoids (sum / max / min on 32-bit values) are the page's combine_fn.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "rr_config.hpp"
@@ -362,6 +363,36 @@ rr_status launch_fill_zero(void* p, size_t bytes, hipStream_t stream)
     if (bytes == 0) return RR_OK;
     return launch_kernel(k_fill_zero_bytes, dim3(grid_for((int64_t)bytes)), dim3(kBlockThreads),
                          0, stream, (uint8_t*)p, (int64_t)bytes);
+}
+
+// ------------------------------------------------ library-owned scratch
+// The split-K workspace of rr_reduce_rows_noalloc, for callers that cannot
+// allocate: a file-scope device array, one copy per GPU, held until the
+// process ends.  On the host the name `scratch` only stands for the symbol;
+// the device address of the current GPU's copy comes from
+// hipGetSymbolAddress, looked up once per device with that device current and
+// kept per device, and only that address is ever passed to a kernel or a
+// fill.
+static __device__ __align__(256) uint8_t scratch[RR_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::atomic<void*> g_scratch[kScratchDevices];
+}  // namespace
+
+rr_status noalloc_scratch(void** out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices)
+        return RR_ERR_HIP;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return RR_ERR_HIP;
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return RR_OK;
 }
 
 // ---------------------------------------------------------------- launch

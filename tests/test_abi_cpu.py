@@ -62,8 +62,8 @@ def test_plain_c_consumer_compiles_links_and_runs(tmp_path):
 def test_status_strings_are_distinct():
     lib = ctypes.CDLL(rr.lib_path())
     lib.rr_status_string.restype = ctypes.c_char_p
-    texts = {lib.rr_status_string(s) for s in range(8)}
-    assert len(texts) == 8 and all(texts)
+    texts = {lib.rr_status_string(s) for s in range(9)}
+    assert len(texts) == 9 and all(texts)
 
 
 # ------------------------------------------------------------- tier rules
@@ -327,6 +327,37 @@ def test_entry_points_validate_before_touching_the_device():
     assert lib.rr_splitk_lse_merge(None, None, None, None, 8, 4, 8, 1.0, 1, None) == 3
     assert lib.rr_splitk_lse_merge(None, None, None, None, 8, 0, 8, 1.0, 2, None) == 0
     assert lib.rr_splitk_lse_merge(None, None, None, None, 8, 4, 8, 1.0, 2, None) == 1
+
+
+def test_noalloc_entry_point_validates_before_touching_the_device():
+    lib = ctypes.CDLL(rr.lib_path())
+    vp, i64, it = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.rr_reduce_rows_noalloc.argtypes = [vp, vp, i64, i64, i64, it, it, it, vp]
+    f = lib.rr_reduce_rows_noalloc
+    assert f(None, None, -1, 4, 4, 0, 0, 0, None) == 2        # negative rows
+    assert f(None, None, 4, 8, 4, 0, 0, 0, None) == 2         # ld < cols
+    assert f(None, None, 4, 8, 8, 2, 0, 0, None) == 3         # bf16 reduce
+    assert f(None, None, 4, 8, 8, 0, 3, 0, None) == 7         # the multi-statistic op
+    assert f(None, None, 4, 100, 100, 0, 0, 1, None) == 4     # wave tier, cols > 64
+    assert f(None, None, 0, 8, 8, 0, 0, 0, None) == 0         # no-op
+    assert f(None, None, 4, 8, 8, 0, 0, 0, None) == 1         # NULL
+    lib.rr_status_string.restype = ctypes.c_char_p
+    assert b"scratch" in lib.rr_status_string(8)
+    assert rr.NOALLOC_SCRATCH_BYTES == 1 << 20
+    hdr = open(os.path.join(ROOT, "include", "rr.h")).read()
+    assert "#define RR_NOALLOC_SCRATCH_BYTES (1 << 20)" in hdr
+
+
+def test_noalloc_scratch_bound_matches_the_plans():
+    # an automatic split-K plan (rows < CU) fits the library's scratch with
+    # room to spare; a forced split-K over many rows does not, and the entry
+    # point refuses it (RR_ERR_SCRATCH) rather than overrun the array
+    for rows in (1, 16, 37, 255):
+        for op in ("sum", "max"):
+            need = rr.plan_reduce(rows, 1 << 20, torch.float32, op, cu_count=256)["workspace_bytes"]
+            assert 0 < need <= 16384, (rows, need)
+    big = rr.plan_reduce(200000, 64, torch.float32, "sum", "splitk", cu_count=256)
+    assert big["workspace_bytes"] > rr.NOALLOC_SCRATCH_BYTES
 
 
 def test_attention_partials_validate_before_touching_the_device():
