@@ -150,7 +150,16 @@ NEXT_BYTES = {"multi_long": 16 * (1 << 24) * 4 + 3 * 16 * 4,
               "attention": _attn_bytes(),
               # q, k, v read and bf16 attention written once (the partials are internal)
               "attention_merged": _attn_fused_bytes(),
-              "attention_fused": _attn_fused_bytes()}
+              "attention_fused": _attn_fused_bytes(),
+              # rows that do not all start 16-byte aligned (odd row strides),
+              # beside their aligned neighbours: each row's body from its
+              # first 16-byte boundary in 128-bit loads, head and tail scalar
+              "sum_47": 1048576 * 47 * 4 + 1048576 * 4,
+              "sum_1001": 65536 * 1001 * 4 + 65536 * 4,
+              "sum_1000": 65536 * 1000 * 4 + 65536 * 4,
+              "softmax_8191": 8192 * 8191 * 2 * 2}
+# each odd-stride row's aligned neighbour: a step op or another next row
+NEIGHBOUR = {"sum_47": "short_sum", "sum_1001": "sum_1000", "softmax_8191": "softmax"}
 STEP_OPS = ("short_sum", "short_max", "softmax", "long_sum", "long_max", "merge")
 COPY_BYTES = 512 << 20
 
@@ -420,6 +429,20 @@ def main():
         dx["attn_fused"] = torch.empty((ab, ah, asq, ad), dtype=torch.bfloat16, device=dev)
         dx["attn_ws"] = torch.zeros(rr.splitk_attention_workspace_bytes(ab, ah, ah, asq, an, ad, ap),
                                     dtype=torch.uint8, device=dev)
+    if not args.no_next:
+        # odd-stride rows and their aligned neighbours, drawn on the device
+        # (standard normal, seeded); two sets each so consecutive launches
+        # touch more than the 256 MB of last-level cache
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(9)
+        for key, shape, dt in (("sum_47", (1048576, 47), torch.float32),
+                               ("sum_1001", (65536, 1001), torch.float32),
+                               ("sum_1000", (65536, 1000), torch.float32),
+                               ("softmax_8191", (8192, 8191), torch.bfloat16)):
+            dx[key] = [torch.randn(shape, generator=gen, device=dev).to(dt) for _ in range(2)]
+        dx["softmax_8191_out"] = [torch.empty_like(dx["softmax_8191"][0]) for _ in range(2)]
+        dx["sum_47_out"] = torch.empty(1048576, device=dev)
+        dx["sum_1001_out"] = torch.empty(65536, device=dev)
     y_short_sum = torch.empty(1048576, dtype=torch.float32, device=dev)
     y_short_max = torch.empty(1048576, dtype=torch.float32, device=dev)
     y_long_f = torch.empty(16, dtype=torch.float32, device=dev)
@@ -459,6 +482,11 @@ def main():
         "attention_fused": lambda i: rr.splitk_attention(*dx["attn_qkv"], ATTN[5],
                                                          out=dx["attn_fused"],
                                                          workspace=dx["attn_ws"]),
+        "sum_47": lambda i: rr.reduce_rows(dx["sum_47"][i % 2], "sum", out=dx["sum_47_out"]),
+        "sum_1001": lambda i: rr.reduce_rows(dx["sum_1001"][i % 2], "sum", out=dx["sum_1001_out"]),
+        "sum_1000": lambda i: rr.reduce_rows(dx["sum_1000"][i % 2], "sum", out=dx["sum_1001_out"]),
+        "softmax_8191": lambda i: rr.softmax_rows(dx["softmax_8191"][i % 2],
+                                                  out=dx["softmax_8191_out"][i % 2]),
     }
     only = args.only.split(",") if args.only else None
     names = [n for n in ops if only is None or n in only]
@@ -715,6 +743,20 @@ def main():
                 "TFLOPs": round(_attn_flops() / t_s / 1e12, 1),
                 "bytes_note": "bytes = q, k, v read once and the bf16 output written once; the "
                               "partials go through the device-coherent level once each way"})
+        for n, nb in NEIGHBOUR.items():
+            if n in next_rows:
+                ref = next_rows.get(nb) or per_op.get(nb)
+                next_rows[n]["aligned_neighbour"] = nb
+                if ref:
+                    next_rows[n]["frac_of_neighbour"] = round(next_rows[n]["GBps"] / ref["GBps"], 4)
+        for n, cfg in (("sum_47", "f32 row sum [1048576, 47] (row stride 47: rows at every "
+                                  "offset from a 16-byte boundary), wave tier"),
+                       ("sum_1001", "f32 row sum [65536, 1001] (odd row stride), block tier"),
+                       ("sum_1000", "f32 row sum [65536, 1000] (aligned rows), block tier"),
+                       ("softmax_8191", "bf16 softmax [8192, 8191] -> bf16 (odd row stride), "
+                                        "block tier, persistent rows")):
+            if n in next_rows:
+                next_rows[n]["config"] = cfg
         if "softmax_long" in next_rows:
             r, c = SOFTMAX_LONG
             next_rows["softmax_long"].update({
@@ -728,9 +770,9 @@ def main():
     # ------------------------------------------- achievable-bandwidth reference
     # Plain 128-bit non-temporal streams with no arithmetic (rr_test_stream):
     # what HBM delivers to a kernel that does nothing but move bytes, beside
-    # the published 8 TB/s.  Read: the two 1 GiB long-row inputs alternated;
-    # copy: softmax-shaped 128 MiB -> 128 MiB over the four softmax buffer sets,
-    # and 512 MiB -> 512 MiB; write: 1 GiB.
+    # the published 8 TB/s.  Read: the two 1 GiB long-row inputs alternated,
+    # and the merge's 128 MiB inputs; copy: softmax-shaped 128 MiB -> 128 MiB
+    # over the four softmax buffer sets, and 512 MiB -> 512 MiB; write: 1 GiB.
     ceilings = None
     if not args.no_ceilings:
         log("timing the reference streams")
@@ -744,6 +786,11 @@ def main():
                 "copy", src_big[:1 << 29], big[(i % 2) << 29:((i % 2) + 1) << 29])),
             "copy_128MiB_each_way": (1 << 28, lambda i: rr._test_stream(
                 "copy", dx["softmax"][i % 4], dx["softmax_out"][i % 4])),
+            # the LSE merge's partial outputs (128 MiB, the merge's eight sets
+            # in turn): a kernel of the merge's size has a larger fixed share
+            # (launch, ramp, drain) than a 1 GiB pass
+            "read_128MiB": (1 << 27, lambda i: rr._test_stream(
+                "read", dx["merge"][i % 8][0])),
         }
         ceilings = {}
         for name, (nbytes, fn) in runs.items():
@@ -776,6 +823,13 @@ def main():
         ent = tr.get("kernels", {}).get(dom)
         if ent and tr.get("source_hash") == kernel_source_hash():
             traffic = ent.get("bytes_per_launch")
+    if ceilings:
+        # each step op beside the reference stream closest to its size and mix
+        for n, ref in (("softmax", "copy_128MiB_each_way"), ("long_sum", "read_1GiB"),
+                       ("long_max", "read_1GiB"), ("merge", "read_128MiB")):
+            if n in per_op and ref in ceilings:
+                per_op[n]["reference_stream"] = ref
+                per_op[n]["frac_of_reference"] = round(per_op[n]["GBps"] / ceilings[ref]["GBps"], 4)
     roofline = {"bound": "hbm", "kernel": dom, "kernel_symbol": KERNEL_OF_OP[dom],
                 "achieved": achieved, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,

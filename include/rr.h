@@ -45,9 +45,18 @@
  *     has been launched and no output byte has been written.  After a launch
  *     the HIP launch status is checked and reported as RR_ERR_HIP.
  *   - Rows are laid out with a stride `ld` (in elements) between row starts;
- *     the last axis is contiguous (stride 1).  128-bit vector loads are used
- *     when the base pointer is 16-byte aligned and ld * element size is a
- *     multiple of 16; otherwise the same kernels run with scalar loads.
+ *     the last axis is contiguous (stride 1).  Rows may start at any element
+ *     offset: the block, wave and split-K tiers load each row's body from its
+ *     first 16-byte boundary with 128-bit loads and its head and tail (the
+ *     elements before that boundary and after the last whole 16 bytes) one
+ *     element at a time ("reduce", algorithm.gpu.rowwise, tier semantics:
+ *     the full-width tile function on aligned chunks, the one-element one on
+ *     the rest); outputs are stored 128 bits at a time where they are aligned
+ *     for it.  Only bytes of the rows' elements are read or written.  The
+ *     tiled and serial tiers, the softmax and layernorm wave tiers and the
+ *     layernorm's persistent rows take 128-bit loads only when every row is
+ *     16-byte aligned; pointers not aligned to their element size run every
+ *     tier element by element.
  *   - Results are bit-identical from run to run for the same device, shape,
  *     strides, alignment, tier and library build.
  *   - No C++ exception crosses this interface.

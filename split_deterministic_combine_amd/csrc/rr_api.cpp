@@ -116,12 +116,12 @@ static rr_status reduce_rows_common(const void* x, void* y, int64_t rows, int64_
     if (!y || (!x && cols > 0)) return RR_ERR_NULL;
     int32_t cu = 0;
     if ((st = current_cu(&cu)) != RR_OK) return st;
-    const bool vec = rows_aligned16(x, ld, rows, 4);
+    const bool vec = aligned(x, 4);
     if ((st = rr::plan_reduce(rows, cols, ld, dtype, op, tier, cu, vec, &p)) != RR_OK) return st;
 
     rr::ReduceLaunch a{x, y, rows, cols, ld, dtype, op, false, {nullptr, nullptr, nullptr}, vec,
-                       workspace, g_splitk_skew.load(std::memory_order_relaxed),
-                       as_stream(stream)};
+                       rows_aligned16(x, ld, rows, 4), workspace,
+                       g_splitk_skew.load(std::memory_order_relaxed), as_stream(stream)};
     if (cols == 0) return rr::launch_reduce_identity(a);
     if (p.tier == RR_TIER_SPLITK) {
         if (noalloc) {
@@ -171,12 +171,12 @@ extern "C" rr_status rr_reduce_rows_multi(const void* x, void* y_sum, void* y_ma
     if (!x && cols > 0) return RR_ERR_NULL;
     int32_t cu = 0;
     if ((st = current_cu(&cu)) != RR_OK) return st;
-    const bool vec = rows_aligned16(x, ld, rows, 4);
+    const bool vec = aligned(x, 4);
     if ((st = rr::plan_reduce(rows, cols, ld, dtype, RR_SUM_MAX_MIN, tier, cu, vec, &p)) != RR_OK)
         return st;
     rr::ReduceLaunch a{x, nullptr, rows, cols, ld, dtype, RR_SUM, true, {y_sum, y_max, y_min},
-                       vec, workspace, g_splitk_skew.load(std::memory_order_relaxed),
-                       as_stream(stream)};
+                       vec, rows_aligned16(x, ld, rows, 4), workspace,
+                       g_splitk_skew.load(std::memory_order_relaxed), as_stream(stream)};
     if (cols == 0) return rr::launch_reduce_identity(a);
     if (p.tier == RR_TIER_SPLITK) {
         if (!workspace || workspace_bytes < p.workspace_bytes || !aligned(workspace, 8))
@@ -197,7 +197,8 @@ extern "C" rr_status rr_reduce_axis(const void* x, void* y, int64_t outer, int64
     if (!y || (!x && axis > 0)) return RR_ERR_NULL;
     if (axis == 0) {  // every output is the identity
         rr::ReduceLaunch a{x, y, outer * inner, 0, 0, dtype, op, false,
-                           {nullptr, nullptr, nullptr}, false, nullptr, 0, as_stream(stream)};
+                           {nullptr, nullptr, nullptr}, false, false, nullptr, 0,
+                           as_stream(stream)};
         return rr::launch_reduce_identity(a);
     }
     int32_t cu = 0;
@@ -221,7 +222,7 @@ extern "C" rr_status rr_softmax_rows(const void* x, void* y, int64_t rows, int64
                                      size_t workspace_bytes, void* stream)
 {
     rr_plan p;
-    rr_status st = rr::plan_softmax(rows, cols, x_dtype, y_dtype, tier, 1, true, &p);
+    rr_status st = rr::plan_softmax(rows, cols, x_dtype, y_dtype, tier, 1, true, true, &p);
     if (st != RR_OK) return st;
     if (ld_x < cols || ld_y < cols) return RR_ERR_SHAPE;
     if (rows == 0 || cols == 0) return RR_OK;
@@ -229,15 +230,18 @@ extern "C" rr_status rr_softmax_rows(const void* x, void* y, int64_t rows, int64
     if (x == y && (ld_x != ld_y || x_dtype != y_dtype)) return RR_ERR_SHAPE;
     int32_t cu = 0;
     if ((st = current_cu(&cu)) != RR_OK) return st;
-    const bool vec = rows_aligned16(x, ld_x, rows, elem_size(x_dtype)) &&
-                     rows_aligned16(y, ld_y, rows, elem_size(y_dtype));
-    if ((st = rr::plan_softmax(rows, cols, x_dtype, y_dtype, tier, cu, vec, &p)) != RR_OK)
+    // element-aligned rows take 128-bit chunks from each row's first 16-byte
+    // boundary (block and split-K tiers); the wave tier needs aligned rows
+    const bool vec = aligned(x, elem_size(x_dtype)) && aligned(y, elem_size(y_dtype));
+    const bool rows16 = rows_aligned16(x, ld_x, rows, elem_size(x_dtype)) &&
+                        rows_aligned16(y, ld_y, rows, elem_size(y_dtype));
+    if ((st = rr::plan_softmax(rows, cols, x_dtype, y_dtype, tier, cu, vec, rows16, &p)) != RR_OK)
         return st;
     if (p.tier == RR_TIER_SPLITK) {
         if (!workspace || workspace_bytes < p.workspace_bytes || !aligned(workspace, 8))
             return RR_ERR_WORKSPACE;
     }
-    rr::SoftmaxLaunch a{x, y, rows, cols, ld_x, ld_y, x_dtype, y_dtype, vec, workspace, cu,
+    rr::SoftmaxLaunch a{x, y, rows, cols, ld_x, ld_y, x_dtype, y_dtype, vec, rows16, workspace, cu,
                         as_stream(stream)};
     log_plan("rr_softmax_rows", "rows", rows, "cols", cols, nullptr, 0, vec, p);
     return rr::launch_softmax(p, a);
@@ -251,7 +255,7 @@ extern "C" rr_status rr_layernorm_rows(const void* x, void* y, const void* gamma
                                        size_t workspace_bytes, void* stream)
 {
     rr_plan p;
-    rr_status st = rr::plan_layernorm(rows, cols, x_dtype, y_dtype, w_dtype, tier, 1, true, &p);
+    rr_status st = rr::plan_layernorm(rows, cols, x_dtype, y_dtype, w_dtype, tier, 1, true, true, &p);
     if (st != RR_OK) return st;
     if (ld_x < cols || ld_y < cols) return RR_ERR_SHAPE;
     if (!(eps >= 0.0f) || isinf(eps)) return RR_ERR_SHAPE;
@@ -260,18 +264,23 @@ extern "C" rr_status rr_layernorm_rows(const void* x, void* y, const void* gamma
     if (x == y && (ld_x != ld_y || x_dtype != y_dtype)) return RR_ERR_SHAPE;
     int32_t cu = 0;
     if ((st = current_cu(&cu)) != RR_OK) return st;
-    const bool vec = rows_aligned16(x, ld_x, rows, elem_size(x_dtype)) &&
-                     rows_aligned16(y, ld_y, rows, elem_size(y_dtype)) &&
-                     (!gamma || aligned(gamma, 16)) && (!beta || aligned(beta, 16));
-    if ((st = rr::plan_layernorm(rows, cols, x_dtype, y_dtype, w_dtype, tier, cu, vec, &p)) !=
-        RR_OK)
+    const int ew = elem_size(w_dtype);
+    const bool vec = aligned(x, elem_size(x_dtype)) && aligned(y, elem_size(y_dtype)) &&
+                     (!gamma || aligned(gamma, ew)) && (!beta || aligned(beta, ew));
+    const bool rows16 = rows_aligned16(x, ld_x, rows, elem_size(x_dtype)) &&
+                        rows_aligned16(y, ld_y, rows, elem_size(y_dtype)) &&
+                        (!gamma || aligned(gamma, 16)) && (!beta || aligned(beta, 16));
+    const bool same_phase = rows <= 1 || (ld_x * elem_size(x_dtype)) % 16 == 0;
+    if ((st = rr::plan_layernorm(rows, cols, x_dtype, y_dtype, w_dtype, tier, cu, vec, rows16,
+                                 &p)) != RR_OK)
         return st;
     if (p.tier == RR_TIER_SPLITK) {
         if (!workspace || workspace_bytes < p.workspace_bytes || !aligned(workspace, 8))
             return RR_ERR_WORKSPACE;
     }
     rr::LayernormLaunch a{x, y, gamma, beta, mean_out, rstd_out, rows, cols, ld_x, ld_y,
-                          x_dtype, y_dtype, w_dtype, eps, vec, workspace, cu, as_stream(stream)};
+                          x_dtype, y_dtype, w_dtype, eps, vec, rows16, same_phase, workspace, cu,
+                          as_stream(stream)};
     log_plan("rr_layernorm_rows", "rows", rows, "cols", cols, nullptr, 0, vec, p);
     return rr::launch_layernorm(p, a);
 }
@@ -432,9 +441,9 @@ extern "C" rr_status rr_workspace_bytes(rr_kind kind, int64_t rows, int64_t cols
     if (kind == RR_KIND_REDUCE)
         st = rr::plan_reduce(rows, cols, cols, dtype, op, tier, cu, true, &p);
     else if (kind == RR_KIND_SOFTMAX)
-        st = rr::plan_softmax(rows, cols, dtype, dtype, tier, cu, true, &p);
+        st = rr::plan_softmax(rows, cols, dtype, dtype, tier, cu, true, true, &p);
     else
-        st = rr::plan_layernorm(rows, cols, dtype, dtype, RR_F32, tier, cu, true, &p);
+        st = rr::plan_layernorm(rows, cols, dtype, dtype, RR_F32, tier, cu, true, true, &p);
     if (st != RR_OK) return st;
     *bytes_out = (size_t)p.workspace_bytes;
     return RR_OK;
@@ -451,9 +460,9 @@ extern "C" rr_status rr_select_tier(rr_kind kind, int64_t rows, int64_t cols, rr
     if (kind == RR_KIND_REDUCE)
         st = rr::plan_reduce(rows, cols, cols, dtype, op, RR_TIER_AUTO, cu, true, &p);
     else if (kind == RR_KIND_SOFTMAX)
-        st = rr::plan_softmax(rows, cols, dtype, dtype, RR_TIER_AUTO, cu, true, &p);
+        st = rr::plan_softmax(rows, cols, dtype, dtype, RR_TIER_AUTO, cu, true, true, &p);
     else if (kind == RR_KIND_LAYERNORM)
-        st = rr::plan_layernorm(rows, cols, dtype, dtype, RR_F32, RR_TIER_AUTO, cu, true, &p);
+        st = rr::plan_layernorm(rows, cols, dtype, dtype, RR_F32, RR_TIER_AUTO, cu, true, true, &p);
     else
         return RR_ERR_TIER;
     if (st != RR_OK) return st;

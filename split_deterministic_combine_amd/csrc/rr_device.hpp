@@ -32,10 +32,12 @@ enum : int {
     kDppMirror = 0x140,
 };
 
+// Every lane reads a lane of its own row (all row and bank masks on), so no
+// lane keeps an old value: mov_dpp, with no old operand to materialise.
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
 {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
 }
 
 // A trivially copyable value as 32-bit words (for cross-lane moves).
@@ -225,6 +227,14 @@ __device__ __forceinline__ float exp2_f32(float t) { return exp2f(t); }
 // a result cannot change anything, or behind a check for that range.
 __device__ __forceinline__ float exp2_hw(float t) { return __builtin_amdgcn_exp2f(t); }
 
+// exp2 over the whole range from the hardware instruction: below -126 the
+// argument is raised by 64 (a normal result, exact as above) and the result
+// scaled by 2^-64, which rounds it once onto the subnormal grid.
+__device__ __forceinline__ float exp2_sub(float t)
+{
+    return t < -126.0f ? exp2_hw(t + 64.0f) * 0x1p-64f : exp2_hw(t);
+}
+
 struct SoftmaxMS {
     using acc_t = MS;
     __device__ static acc_t identity() { return MS{-__builtin_inff(), 0.0f}; }
@@ -360,6 +370,18 @@ __device__ __forceinline__ void store8_nt(void* p, uint2 u)
 {
     rr_u32x2 v = {u.x, u.y};
     __builtin_nontemporal_store(v, reinterpret_cast<rr_u32x2*>(p));
+}
+
+// Elements of a row before its first 16-byte boundary (its head), at most
+// cols: the row's 128-bit body starts at p + head_elems(p, cols).  p must be
+// aligned to its element size.  "reduce" (algorithm.gpu.rowwise), tier
+// semantics: the full-width tile function runs on the aligned chunks and the
+// one-element tile function on the rest.
+template <class T>
+__device__ __forceinline__ int64_t head_elems(const T* p, int64_t cols)
+{
+    const int64_t h = (int64_t)((0u - (uint32_t)(uintptr_t)p) & 15u) / (int64_t)sizeof(T);
+    return h < cols ? h : cols;
 }
 
 // One 128-bit load of 4 elements of 4 bytes (NT: non-temporal).

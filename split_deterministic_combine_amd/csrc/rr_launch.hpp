@@ -16,7 +16,10 @@ struct ReduceLaunch {
     rr_op op;
     bool multi;           // sum, max and min over one read into ys (NULL: not written)
     void* ys[3];
-    bool vec;             // 128-bit loads allowed (alignment checked by the caller)
+    bool vec;             // element-aligned x: block, wave and split-K tiers load each
+                          // row's body from its first 16-byte boundary in 128 bits
+    bool rows16;          // every row starts 16-byte aligned: tiled and serial tiers
+                          // load 128 bits per step
     void* workspace;      // split-K only
     int skew;             // test hook: split-K arrival skew (0 = off)
     hipStream_t stream;
@@ -27,7 +30,10 @@ struct SoftmaxLaunch {
     void* y;
     int64_t rows, cols, ld_x, ld_y;
     rr_dtype x_dtype, y_dtype;
-    bool vec;
+    bool vec;             // x and y element-aligned: block and split-K tiers take each
+                          // row's body from its first 16-byte boundary in 128 bits
+    bool rows16;          // every row of x and y 16-byte aligned (wave tier, and the
+                          // persistent rows without a head or tail)
     void* workspace;      // split-K only
     int32_t cu;           // compute units of the current device
     hipStream_t stream;
@@ -54,7 +60,12 @@ struct LayernormLaunch {
     int64_t rows, cols, ld_x, ld_y;
     rr_dtype x_dtype, y_dtype, w_dtype;
     float eps;
-    bool vec;
+    bool vec;             // x, y, gamma, beta element-aligned: block tier chunks from each
+                          // row's first 16-byte boundary
+    bool rows16;          // every row of x and y 16-byte aligned, gamma / beta too
+                          // (persistent rows, wave tier)
+    bool same_phase;      // every row of x at one offset from a 16-byte boundary
+                          // (split-K tier with chunks)
     void* workspace;      // split-K only
     int32_t cu;           // compute units of the current device
     hipStream_t stream;

@@ -57,11 +57,30 @@ __device__ __forceinline__ float weight_one(const Weights& w, int64_t j)
                   : static_cast<const float*>(w.p)[j];
 }
 
-// E weights of columns j0 .. j0+E-1 (past `cols`: the default).  With VEC the
-// base is 16-byte aligned and a whole chunk inside the row is loaded with
-// vector loads (cached: every row reads the same weights).
+// The weights of a row's body that starts h columns in: the same vector,
+// offset by h elements (a NULL vector stays NULL).
+__device__ __forceinline__ Weights shifted(const Weights& w, int64_t h)
+{
+    return Weights{w.p ? static_cast<const char*>(w.p) + h * (w.bf16 ? 2 : 4) : nullptr, w.bf16,
+                   w.dflt};
+}
+
+// Whether a vector's chunks of E columns load whole: 16-byte aligned base
+// (8 bytes for a bf16 chunk of 4), or no vector at all.
+template <int E>
+__device__ __forceinline__ bool weights_aligned(const Weights& w)
+{
+    const uint32_t a = (w.bf16 && E == 4) ? 7u : 15u;
+    return !w.p || ((uint32_t)(uintptr_t)w.p & a) == 0;
+}
+
+// E weights of columns j0 .. j0+E-1 (past `cols`: the default).  With VEC
+// and wvec (the base aligned for chunk loads: weights_aligned) a whole chunk
+// inside the row is loaded with vector loads (cached: every row reads the
+// same weights); else element by element.
 template <int E, bool VEC>
-__device__ __forceinline__ void load_weights(const Weights& w, int64_t j0, int64_t cols, float* o)
+__device__ __forceinline__ void load_weights(const Weights& w, int64_t j0, int64_t cols, float* o,
+                                             bool wvec = true)
 {
     if (!w.p) {
 #pragma unroll
@@ -70,7 +89,7 @@ __device__ __forceinline__ void load_weights(const Weights& w, int64_t j0, int64
         return;
     }
     if constexpr (VEC) {
-        if (j0 + E <= cols) {
+        if (wvec && j0 + E <= cols) {
             if (w.bf16) {
                 const uint16_t* p = static_cast<const uint16_t*>(w.p) + j0;
                 if constexpr (E == 8) {
@@ -105,7 +124,7 @@ __device__ __forceinline__ void load_weights(const Weights& w, int64_t j0, int64
 // y = d * rstd * gamma + beta on E values of columns j0.. (in place).
 template <int E, bool VEC>
 __device__ __forceinline__ void affine(float* d, float rstd, const Weights& g, const Weights& b,
-                                       int64_t j0, int64_t cols)
+                                       int64_t j0, int64_t cols, bool wvec = true)
 {
     if (!g.p && !b.p) {
 #pragma unroll
@@ -114,8 +133,8 @@ __device__ __forceinline__ void affine(float* d, float rstd, const Weights& g, c
         return;
     }
     float gw[E], bw[E];
-    load_weights<E, VEC>(g, j0, cols, gw);
-    load_weights<E, VEC>(b, j0, cols, bw);
+    load_weights<E, VEC>(g, j0, cols, gw, wvec);
+    load_weights<E, VEC>(b, j0, cols, bw, wvec);
 #pragma unroll
     for (int i = 0; i < E; ++i)
         d[i] = __builtin_fmaf(d[i] * rstd, gw[i], bw[i]);
@@ -209,15 +228,20 @@ struct RawWeights {
 // One row at a time per workgroup; the thread's chunks are k = 0 .. NCH-1 at
 // columns (threadIdx.x + k * NT) * E.  `valid(k, i)` says whether element i
 // of chunk k lies in the row; invalid elements hold 0 and are left out.
+// *e: one more element of the row held by this thread (a misaligned row's
+// head element) when has_e, centred in place like the others; else unused.
 template <int NCH, int E, int NT, class Valid>
 __device__ __forceinline__ LnRow row_stats_in_registers(float* v, int64_t cols, float eps,
                                                         double* slot_a, double* slot_b,
-                                                        Valid valid)
+                                                        Valid valid, float* e = nullptr,
+                                                        bool has_e = false)
 {
     double s = 0.0;  // invalid elements hold 0
 #pragma unroll
     for (int i = 0; i < NCH * E; ++i)
         s += (double)v[i];
+    if (has_e)
+        s += (double)*e;
     const double S = block_reduce<SumF32, NT>(s, slot_a);
     const double mean = S / (double)cols;
     const Centre centre(mean);
@@ -232,6 +256,11 @@ __device__ __forceinline__ LnRow row_stats_in_registers(float* v, int64_t cols, 
             cq = __builtin_fmaf(d, d, cq);
         }
         q += (double)cq;
+    }
+    if (has_e) {
+        const float d = centre(*e);
+        *e = d;
+        q += (double)(d * d);
     }
     const double Q = block_reduce<SumF32, NT>(q, slot_b);
     return LnRow{mean, rstd_of(Q, cols, eps)};
@@ -301,10 +330,10 @@ __global__ __launch_bounds__(NT) void k_layernorm_rows_pf(
         graw.load(g, cols);
         braw.load(b, cols);
     }
-    persistent_rows<NCH>(
+    persistent_rows<RowBuf<NCH>>(
         blockIdx.x, gridDim.x, rows,
-        [&](int64_t r, bool live, uint4* raw) {
-            load_row_raw<NCH, NT>(x + r * ldx, live ? cols * (int64_t)sizeof(XT) : 0, raw);
+        [&](int64_t r, bool live, RowBuf<NCH>& buf) {
+            load_row_raw<NCH, NT>(x + r * ldx, live ? cols * (int64_t)sizeof(XT) : 0, buf.c);
         },
         [&] {
             if constexpr (AFF) {
@@ -312,15 +341,19 @@ __global__ __launch_bounds__(NT) void k_layernorm_rows_pf(
                 braw.unpack(b, bw);
             }
         },
-        [&](const uint4* raw, int64_t r, int) {
-            ln_row_from_chunks<XT, YT, NCH, NT, EXACT, AFF>(raw, y + r * ldy, r, cols, eps, gw,
+        [&](const RowBuf<NCH>& buf, int64_t r, int) {
+            ln_row_from_chunks<XT, YT, NCH, NT, EXACT, AFF>(buf.c, y + r * ldy, r, cols, eps, gw,
                                                             bw, mean_out, rstd_out, slot[0],
                                                             slot[1]);
         });
 }
 
 // Any alignment and any column count (masked chunks), one row per workgroup
-// at a time, the row in registers.
+// at a time, the row in registers.  VEC (element-aligned x and y): each row's
+// body from its first 16-byte boundary in chunks (the tail chunk element by
+// element), the head (h < E elements) one element to each of the first
+// threads; y's chunks are stored whole, and gamma / beta loaded whole, where
+// they are aligned at the body's first column.
 template <class XT, class YT, int NCH, bool VEC, int NT>
 __global__ __launch_bounds__(NT) void k_layernorm_block(
     const XT* __restrict__ x, YT* __restrict__ y, Weights g, Weights b, float* mean_out,
@@ -329,25 +362,38 @@ __global__ __launch_bounds__(NT) void k_layernorm_block(
     constexpr int E = VEC ? XIn<XT>::kChunk : 1;
     __shared__ double slot[2][NT / kWave];
     for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
-        const XT* xr = x + r * ldx;
-        YT* yr = y + r * ldy;
+        const XT* xr0 = x + r * ldx;
+        YT* yr0 = y + r * ldy;
+        const int64_t h = VEC ? head_elems(xr0, cols) : 0;
+        const XT* xr = xr0 + h;
+        YT* yr = yr0 + h;
+        const int64_t cb = cols - h;
+        const Weights gh = shifted(g, h), bh = shifted(b, h);
+        const bool yvec = VEC && chunk_aligned<YT, E>(yr);
+        const bool wvec = VEC && weights_aligned<E>(gh) && weights_aligned<E>(bh);
         float v[NCH * E];
 #pragma unroll
         for (int k = 0; k < NCH; ++k)
-            load_padded<XT, E, VEC>(xr, ((int64_t)threadIdx.x + (int64_t)k * NT) * E, cols,
+            load_padded<XT, E, VEC>(xr, ((int64_t)threadIdx.x + (int64_t)k * NT) * E, cb,
                                     v + k * E, 0.0f);
+        const bool has_e = (int64_t)threadIdx.x < h;
+        float e = has_e ? XIn<XT>::one(xr0 + threadIdx.x) : 0.0f;
         const LnRow st = row_stats_in_registers<NCH, E, NT>(
-            v, cols, eps, slot[0], slot[1], [&](int k, int i) {
-                return ((int64_t)threadIdx.x + (int64_t)k * NT) * E + i < cols;
-            });
+            v, cols, eps, slot[0], slot[1],
+            [&](int k, int i) { return ((int64_t)threadIdx.x + (int64_t)k * NT) * E + i < cb; },
+            &e, has_e);
         if (threadIdx.x == 0)
             write_stats(mean_out, rstd_out, r, st);
 #pragma unroll
         for (int k = 0; k < NCH; ++k) {
             const int64_t j0 = ((int64_t)threadIdx.x + (int64_t)k * NT) * E;
-            affine<E, VEC>(v + k * E, st.rstd, g, b, j0, cols);
-            store_masked<YT, E, VEC>(yr, j0, cols, v + k * E);
+            affine<E, VEC>(v + k * E, st.rstd, gh, bh, j0, cb, wvec);
+            store_masked_rt<YT, E>(yr, j0, cb, v + k * E, yvec);
         }
+        if (has_e)
+            YOut<YT>::one(yr0 + threadIdx.x,
+                          __builtin_fmaf(e * st.rstd, weight_one(g, threadIdx.x),
+                                         weight_one(b, threadIdx.x)));
     }
 }
 
@@ -362,14 +408,29 @@ __global__ __launch_bounds__(NT) void k_layernorm_stream(
     constexpr int E = VEC ? XIn<XT>::kChunk : 1;
     __shared__ double slot[2][NT / kWave];
     for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
-        const XT* xr = x + r * ldx;
-        YT* yr = y + r * ldy;
-        const float kf = XIn<XT>::one(xr);
+        // VEC: the body from the row's first 16-byte boundary in chunks, the
+        // head (h < E elements) one element to each of the first threads
+        const XT* xr0 = x + r * ldx;
+        YT* yr0 = y + r * ldy;
+        const int64_t h = VEC ? head_elems(xr0, cols) : 0;
+        const XT* xr = xr0 + h;
+        YT* yr = yr0 + h;
+        const int64_t cb = cols - h;
+        const Weights gh = shifted(g, h), bh = shifted(b, h);
+        const bool yvec = VEC && chunk_aligned<YT, E>(yr);
+        const bool wvec = VEC && weights_aligned<E>(gh) && weights_aligned<E>(bh);
+        const bool has_e = (int64_t)threadIdx.x < h;
+        const float kf = XIn<XT>::one(xr0);
         const double K = (double)kf;
         double s1 = 0.0, s2 = 0.0;
-        for (int64_t j0 = (int64_t)threadIdx.x * E; j0 < cols; j0 += (int64_t)NT * E) {
+        if (has_e) {
+            const double d = (double)XIn<XT>::one(xr0 + threadIdx.x) - K;
+            s1 = d;
+            s2 = d * d;
+        }
+        for (int64_t j0 = (int64_t)threadIdx.x * E; j0 < cb; j0 += (int64_t)NT * E) {
             float v[E];
-            load_padded<XT, E, VEC>(xr, j0, cols, v, kf);
+            load_padded<XT, E, VEC>(xr, j0, cb, v, kf);
 #pragma unroll
             for (int i = 0; i < E; ++i) {
                 const double d = (double)v[i] - K;
@@ -383,14 +444,18 @@ __global__ __launch_bounds__(NT) void k_layernorm_stream(
         if (threadIdx.x == 0)
             write_stats(mean_out, rstd_out, r, st);
         const Centre centre(st.mean);
-        for (int64_t j0 = (int64_t)threadIdx.x * E; j0 < cols; j0 += (int64_t)NT * E) {
+        if (has_e)
+            YOut<YT>::one(yr0 + threadIdx.x,
+                          __builtin_fmaf(centre(XIn<XT>::one(xr0 + threadIdx.x)) * st.rstd,
+                                         weight_one(g, threadIdx.x), weight_one(b, threadIdx.x)));
+        for (int64_t j0 = (int64_t)threadIdx.x * E; j0 < cb; j0 += (int64_t)NT * E) {
             float v[E];
-            load_padded<XT, E, VEC>(xr, j0, cols, v, 0.0f);
+            load_padded<XT, E, VEC>(xr, j0, cb, v, 0.0f);
 #pragma unroll
             for (int i = 0; i < E; ++i)
                 v[i] = centre(v[i]);
-            affine<E, VEC>(v, st.rstd, g, b, j0, cols);
-            store_masked<YT, E, VEC>(yr, j0, cols, v);
+            affine<E, VEC>(v, st.rstd, gh, bh, j0, cb, wvec);
+            store_masked_rt<YT, E>(yr, j0, cb, v, yvec);
         }
         __syncthreads();  // slot reuse by the next row
     }
@@ -534,15 +599,26 @@ __global__ __launch_bounds__(kBlockThreads) void k_layernorm_splitk_stats(
     constexpr int64_t kTile = (int64_t)N * kBlockThreads;
     __shared__ double slot[2][kWavesPerBlock];
     const int64_t total = rows * G;
-    const int64_t ntiles = ceil_div(cols, kTile);
-    const int64_t nfull = cols / kTile;
     for (int64_t blk = blockIdx.x; blk < total; blk += gridDim.x) {
         const int64_t r = blk / G;
         const int32_t gi = (int32_t)(blk - r * G);
-        const XT* xr = x + r * ldx;
-        const float kf = XIn<XT>::one(xr);
+        // Tiles cover the row's body from its first 16-byte boundary (VEC);
+        // workgroup 0 also takes the head, h < E elements, one element to
+        // each of its first threads.
+        const XT* xr0 = x + r * ldx;
+        const int64_t h = VEC ? head_elems(xr0, cols) : 0;
+        const XT* xr = xr0 + h;
+        const int64_t cb = cols - h;
+        const int64_t ntiles = ceil_div(cb, kTile);
+        const int64_t nfull = cb / kTile;
+        const float kf = XIn<XT>::one(xr0);
         const double K = (double)kf;
         double s1[4] = {0.0, 0.0, 0.0, 0.0}, s2[4] = {0.0, 0.0, 0.0, 0.0};
+        if (VEC && gi == 0 && (int64_t)threadIdx.x < h) {
+            const double d = (double)XIn<XT>::one(xr0 + threadIdx.x) - K;
+            s1[0] = d;
+            s2[0] = d * d;
+        }
         // whole tiles, double-buffered (next tile's loads issued before the
         // current one is folded; trip counts uniform over the workgroup)
         const int64_t n = gi < nfull ? (nfull - 1 - gi) / G + 1 : 0;
@@ -571,7 +647,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_layernorm_splitk_stats(
         }
         for (int64_t t = gi + n * G; t < ntiles; t += G) {  // ragged tile, padded with K
             float v[N];
-            load_tile_padded<XT, E, VEC, U>(xr, t * kTile, cols, v, kf);
+            load_tile_padded<XT, E, VEC, U>(xr, t * kTile, cb, v, kf);
 #pragma unroll
             for (int i = 0; i < N; ++i) {
                 const double d = (double)v[i] - K;
@@ -633,7 +709,11 @@ __device__ __forceinline__ void ln_row_stats_lds(const XT* x, int64_t ldx, int64
 
 // Work item b of the map pass: column tile t = b % ntiles of the row chunk
 // b / ntiles (rows chunk * rc .. + rc - 1, rc <= kBlockThreads).  The
-// workgroup of tile 0 of a chunk writes that chunk's mean / rstd.
+// workgroup of tile 0 of a chunk writes that chunk's mean / rstd.  VEC: every
+// row of x starts at the same offset from a 16-byte boundary (the host checks
+// the row stride), so the tiles of all rows cover the same columns from the
+// first row's head h on, and share one load of their gamma / beta; the
+// workgroup of tile 0 also maps the head columns of its rows.
 template <class XT, class YT, bool VEC, bool AFF>
 __global__ __launch_bounds__(kBlockThreads) void k_layernorm_splitk_map(
     const XT* __restrict__ x, YT* __restrict__ y, Weights g, Weights b, float* mean_out,
@@ -646,8 +726,15 @@ __global__ __launch_bounds__(kBlockThreads) void k_layernorm_splitk_map(
     constexpr int64_t kTile = (int64_t)N * kBlockThreads;
     __shared__ double smean[kBlockThreads];
     __shared__ float srstd[kBlockThreads];
-    const int64_t ntiles = ceil_div(cols, kTile);
-    const int64_t nfull = cols / kTile;
+    const int64_t h = VEC ? head_elems(x, cols) : 0;
+    const int64_t cb = cols - h;
+    const Weights gh = shifted(g, h), bh = shifted(b, h);
+    const bool wvec = VEC && weights_aligned<E>(gh) && weights_aligned<E>(bh);
+    // at least one tile, so that the work items of tile 0 also map the head
+    // when it is the whole row (a row shorter than its offset to the next
+    // 16-byte boundary: the tile itself is then empty)
+    const int64_t ntiles = cb > 0 ? ceil_div(cb, kTile) : 1;
+    const int64_t nfull = cb / kTile;
     const int64_t nchunk = ceil_div(rows, (int64_t)rc);
     int64_t have = -1;  // row chunk whose statistics are in LDS
     for (int64_t item = blockIdx.x; item < ntiles * nchunk; item += gridDim.x) {
@@ -664,23 +751,31 @@ __global__ __launch_bounds__(kBlockThreads) void k_layernorm_splitk_map(
         if (t == 0 && (int)threadIdx.x < nr)
             write_stats(mean_out, rstd_out, r0 + threadIdx.x,
                         LnRow{smean[threadIdx.x], srstd[threadIdx.x]});
+        if (VEC && t == 0 && (int64_t)threadIdx.x < h) {  // head columns of the chunk's rows
+            const float gj = weight_one(g, threadIdx.x), bj = weight_one(b, threadIdx.x);
+            for (int i = 0; i < nr; ++i) {
+                const float q = Centre(smean[i])(XIn<XT>::one(x + (r0 + i) * ldx + threadIdx.x)) *
+                                srstd[i];
+                YOut<YT>::one(y + (r0 + i) * ldy + threadIdx.x, __builtin_fmaf(q, gj, bj));
+            }
+        }
         {
             float gw[AFF ? N : 1], bw[AFF ? N : 1];
             if constexpr (AFF) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const int64_t j0 = t * kTile + ((int64_t)u * kBlockThreads + threadIdx.x) * E;
-                    load_weights<E, VEC>(g, j0, cols, gw + u * E);
-                    load_weights<E, VEC>(b, j0, cols, bw + u * E);
+                    load_weights<E, VEC>(gh, j0, cb, gw + u * E, wvec);
+                    load_weights<E, VEC>(bh, j0, cb, bw + u * E, wvec);
                 }
             }
             if (t < nfull) {
                 // whole tiles: row r's tile in A while row r+1's loads fly
                 RawTile<XT, VEC, U> A, B;
-                A.load(x + r0 * ldx + t * kTile);
+                A.load(x + r0 * ldx + h + t * kTile);
                 for (int i = 0; i < nr; ++i) {
                     const int ip = i + 1 < nr ? i + 1 : i;
-                    B.load(x + (r0 + ip) * ldx + t * kTile);
+                    B.load(x + (r0 + ip) * ldx + h + t * kTile);
                     __builtin_amdgcn_sched_barrier(0);
                     float v[N];
                     A.unpack(v);
@@ -691,13 +786,17 @@ __global__ __launch_bounds__(kBlockThreads) void k_layernorm_splitk_map(
                         const float q = centre(v[k]) * rs;
                         v[k] = AFF ? __builtin_fmaf(q, gw[k], bw[k]) : q;
                     }
-                    store_tile_full<YT, E, VEC, U>(y + (r0 + i) * ldy + t * kTile, v);
+                    YT* yt = y + (r0 + i) * ldy + h + t * kTile;
+                    if (!VEC || chunk_aligned<YT, E>(yt))
+                        store_tile_full<YT, E, VEC, U>(yt, v);
+                    else
+                        store_tile_full_rt<YT, E, U>(yt, v, false);
                     A = B;
                 }
             } else {
                 for (int i = 0; i < nr; ++i) {
                     float v[N];
-                    load_tile_padded<XT, E, VEC, U>(x + (r0 + i) * ldx, t * kTile, cols, v, 0.0f);
+                    load_tile_padded<XT, E, VEC, U>(x + (r0 + i) * ldx + h, t * kTile, cb, v, 0.0f);
                     const Centre centre(smean[i]);
                     const float rs = srstd[i];
 #pragma unroll
@@ -705,7 +804,9 @@ __global__ __launch_bounds__(kBlockThreads) void k_layernorm_splitk_map(
                         const float q = centre(v[k]) * rs;
                         v[k] = AFF ? __builtin_fmaf(q, gw[k], bw[k]) : q;
                     }
-                    store_tile_masked<YT, E, VEC, U>(y + (r0 + i) * ldy, t * kTile, cols, v);
+                    YT* yb = y + (r0 + i) * ldy + h;
+                    store_tile_masked_rt<YT, E, U>(yb, t * kTile, cb, v,
+                                                   VEC && chunk_aligned<YT, E>(yb));
                 }
             }
         }
@@ -766,7 +867,7 @@ static rr_status launch_block(const rr_plan& p, const XT* x, YT* y, const Weight
     const hipStream_t s = a.stream;
     const int64_t nch = ceil_div(ceil_div(a.cols, E), NT);
     if constexpr (VEC) {
-        if (a.cols % E == 0) {
+        if (a.rows16 && a.cols % E == 0) {
             // persistent rows; the plan chose the shape and sized the grid
             const RowPfShape sh = row_pf_shape(a.cols / E);
             if (sh.nt > 0 && sh.nt != p.block)
@@ -795,6 +896,17 @@ static rr_status launch_block(const rr_plan& p, const XT* x, YT* y, const Weight
 }
 
 template <class XT, class YT, bool VEC>
+static rr_status launch_wave(const rr_plan& p, const XT* x, YT* y, const Weights& g,
+                             const Weights& b, const LayernormLaunch& a);
+template <class XT, class YT, bool VEC>
+static rr_status launch_splitk(const rr_plan& p, const XT* x, YT* y, const Weights& g,
+                               const Weights& b, const LayernormLaunch& a);
+
+// VEC (x, y, gamma and beta aligned to their element sizes): the block tier
+// takes each row's body from its first 16-byte boundary in chunks (persistent
+// rows only when every row starts aligned and ends on a chunk, rows16); the
+// wave tier needs rows16 too, split-K rows at one offset (same_phase).
+template <class XT, class YT, bool VEC>
 static rr_status launch_typed(const rr_plan& p, const LayernormLaunch& a)
 {
     const XT* x = static_cast<const XT*>(a.x);
@@ -807,17 +919,43 @@ static rr_status launch_typed(const rr_plan& p, const LayernormLaunch& a)
     case RR_TIER_BLOCK:
         return launch_block<XT, YT, VEC>(p, x, y, g, b, a);
     case RR_TIER_WAVE:
-        switch (p.lanes_per_row) {
-        case 4: return launch_kernel(k_layernorm_wave<XT, YT, VEC, 4>, grid, block, 0, s, RR_LN_ARGS);
-        case 16: return launch_kernel(k_layernorm_wave<XT, YT, VEC, 16>, grid, block, 0, s, RR_LN_ARGS);
-        case 64: return launch_kernel(k_layernorm_wave<XT, YT, VEC, 64>, grid, block, 0, s, RR_LN_ARGS);
-        default: return RR_ERR_TIER;
-        }
+        return VEC && a.rows16 ? launch_wave<XT, YT, true>(p, x, y, g, b, a)
+                               : launch_wave<XT, YT, false>(p, x, y, g, b, a);
     case RR_TIER_TILED:
         return launch_kernel(k_layernorm_tiled<XT, YT, kTiledRows>, grid, block, 0, s, RR_LN_ARGS);
     case RR_TIER_SERIAL:
         return launch_kernel(k_layernorm_tiled<XT, YT, 1>, grid, block, 0, s, RR_LN_ARGS);
-    case RR_TIER_SPLITK: {
+    case RR_TIER_SPLITK:
+        return VEC && a.same_phase ? launch_splitk<XT, YT, true>(p, x, y, g, b, a)
+                                   : launch_splitk<XT, YT, false>(p, x, y, g, b, a);
+    default:
+        return RR_ERR_TIER;
+    }
+}
+
+template <class XT, class YT, bool VEC>
+static rr_status launch_wave(const rr_plan& p, const XT* x, YT* y, const Weights& g,
+                             const Weights& b, const LayernormLaunch& a)
+{
+    const dim3 grid((unsigned)(p.grid > kMaxGrid ? kMaxGrid : p.grid)), block(kBlockThreads);
+    const hipStream_t s = a.stream;
+    switch (p.lanes_per_row) {
+    case 4: return launch_kernel(k_layernorm_wave<XT, YT, VEC, 4>, grid, block, 0, s, RR_LN_ARGS);
+    case 16: return launch_kernel(k_layernorm_wave<XT, YT, VEC, 16>, grid, block, 0, s, RR_LN_ARGS);
+    case 64: return launch_kernel(k_layernorm_wave<XT, YT, VEC, 64>, grid, block, 0, s, RR_LN_ARGS);
+    default: return RR_ERR_TIER;
+    }
+}
+
+// Split-K: VEC needs every row of x at the same offset from a 16-byte
+// boundary (the map pass shares one tile of gamma / beta between rows).
+template <class XT, class YT, bool VEC>
+static rr_status launch_splitk(const rr_plan& p, const XT* x, YT* y, const Weights& g,
+                               const Weights& b, const LayernormLaunch& a)
+{
+    const dim3 grid((unsigned)(p.grid > kMaxGrid ? kMaxGrid : p.grid)), block(kBlockThreads);
+    const hipStream_t s = a.stream;
+    {
         double* part = static_cast<double*>(a.workspace);
         rr_status st = launch_kernel(k_layernorm_splitk_stats<XT, VEC>, grid, block, 0, s, x,
                                      a.rows, a.cols, a.ld_x, p.slices, part);
@@ -842,9 +980,6 @@ static rr_status launch_typed(const rr_plan& p, const LayernormLaunch& a)
                                  RR_LN_ARGS, p.slices, (const double*)part, (int32_t)rc);
         return launch_kernel(k_layernorm_splitk_map<XT, YT, VEC, false>, mgrid, block, 0, s,
                              RR_LN_ARGS, p.slices, (const double*)part, (int32_t)rc);
-    }
-    default:
-        return RR_ERR_TIER;
     }
 }
 

@@ -100,7 +100,9 @@ rr_status plan_reduce(int64_t rows, int64_t cols, int64_t ld, rr_dtype dtype, rr
     memset(out, 0, sizeof *out);
     const int vec_elems = vec ? 4 : 1;
     if (t != RR_TIER_SPLITK) {
-        fill_rowwise_geometry(t, rows, cols, vec_elems, out);
+        // the wave tier takes 128-bit chunks for rows of at least 7 elements
+        // (every row then has a whole chunk after its head)
+        fill_rowwise_geometry(t, rows, cols, t == RR_TIER_WAVE && cols < 7 ? 1 : vec_elems, out);
         return RR_OK;
     }
     fill_splitk_geometry(rows, cols, (int64_t)kSplitKUnroll * kBlockThreads * vec_elems, cu_count,
@@ -135,7 +137,7 @@ rr_tier auto_two_pass_tier(int64_t rows, int64_t cols, rr_dtype x_dtype, int32_t
 }
 
 rr_status plan_softmax(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype y_dtype,
-                       rr_tier tier, int32_t cu_count, bool vec, rr_plan* out)
+                       rr_tier tier, int32_t cu_count, bool vec, bool rows16, rr_plan* out)
 {
     if (!out) return RR_ERR_NULL;
     if (rows < 0 || cols < 0) return RR_ERR_SHAPE;
@@ -148,20 +150,22 @@ rr_status plan_softmax(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype y_
         t = auto_two_pass_tier(rows, cols, x_dtype, cu_count);
     if (t == RR_TIER_WAVE && cols > 64) return RR_ERR_TIER;
     memset(out, 0, sizeof *out);
-    const int vec_elems = vec ? (x_dtype == RR_BF16 ? 8 : 4) : 1;
+    const int chunk = x_dtype == RR_BF16 ? 8 : 4;
+    const int vec_elems = vec ? chunk : 1;
     if (t == RR_TIER_SPLITK) {
         fill_splitk_geometry(rows, cols, (int64_t)kSoftmaxSplitKUnroll * kBlockThreads * vec_elems,
                              cu_count, kSplitKHeavyBlocksPerCU, out);
         out->workspace_bytes = softmax_splitk_workspace_bytes(rows, out->slices);
         return RR_OK;
     }
-    fill_rowwise_geometry(t, rows, cols, vec_elems, out);
+    fill_rowwise_geometry(t, rows, cols, t == RR_TIER_WAVE ? (rows16 ? chunk : 1) : vec_elems, out);
     if (t == RR_TIER_BLOCK) {
         const int64_t chunks = ceil_div(cols, vec_elems);
         const RowPfShape sh = row_pf_shape(chunks);
-        if (vec && cols % vec_elems == 0 && sh.nt > 0) {
-            // rows of whole 16-byte chunks that stay in registers: persistent
-            // workgroups sized to the row, with a one-row prefetch
+        if (vec && sh.nt > 0) {
+            // rows that stay in registers: persistent workgroups sized to the
+            // row, with a one-row prefetch (each row's body of whole chunks
+            // from its first 16-byte boundary, the rest element by element)
             out->block = sh.nt;
             const int64_t g = (int64_t)cu_count * row_pf_blocks_per_cu(sh);
             out->grid = rows < g ? rows : g;
@@ -178,7 +182,7 @@ rr_status plan_softmax(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype y_
 // kernel's occupancy allows, so a persistent grid never queues).
 rr_status plan_layernorm(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype y_dtype,
                          rr_dtype w_dtype, rr_tier tier, int32_t cu_count, bool vec,
-                         rr_plan* out)
+                         bool rows16, rr_plan* out)
 {
     if (!out) return RR_ERR_NULL;
     if (rows < 0 || cols < 0) return RR_ERR_SHAPE;
@@ -192,16 +196,19 @@ rr_status plan_layernorm(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype 
         t = auto_two_pass_tier(rows, cols, x_dtype, cu_count);
     if (t == RR_TIER_WAVE && cols > 64) return RR_ERR_TIER;
     memset(out, 0, sizeof *out);
-    const int vec_elems = vec ? (x_dtype == RR_BF16 ? 8 : 4) : 1;
+    const int chunk = x_dtype == RR_BF16 ? 8 : 4;
+    const int vec_elems = vec ? chunk : 1;
     if (t == RR_TIER_SPLITK) {
         fill_splitk_geometry(rows, cols, (int64_t)kLnSplitKUnroll * kBlockThreads * vec_elems,
                              cu_count, kSplitKHeavyBlocksPerCU, out);
         out->workspace_bytes = (uint64_t)(rows * (int64_t)out->slices * 16);
         return RR_OK;
     }
-    fill_rowwise_geometry(t, rows, cols, vec_elems, out);
-    if (t == RR_TIER_BLOCK && vec && cols % vec_elems == 0) {
-        const RowPfShape sh = row_pf_shape(cols / vec_elems);
+    fill_rowwise_geometry(t, rows, cols, t == RR_TIER_WAVE ? (rows16 ? chunk : 1) : vec_elems, out);
+    // persistent rows keep each thread's gamma / beta in registers, so they
+    // need every row to start 16-byte aligned and to be whole chunks
+    if (t == RR_TIER_BLOCK && vec && rows16 && cols % chunk == 0) {
+        const RowPfShape sh = row_pf_shape(cols / chunk);
         if (sh.nt > 0) {
             out->block = sh.nt;
             const int64_t g = (int64_t)cu_count * row_pf_blocks_per_cu(sh);
@@ -275,7 +282,7 @@ extern "C" rr_status rr_plan_layernorm(int64_t rows, int64_t cols, rr_dtype x_dt
                                        rr_dtype y_dtype, rr_dtype w_dtype, rr_tier tier,
                                        int32_t cu_count, rr_plan* plan_out)
 {
-    return rr::plan_layernorm(rows, cols, x_dtype, y_dtype, w_dtype, tier, cu_count, true,
+    return rr::plan_layernorm(rows, cols, x_dtype, y_dtype, w_dtype, tier, cu_count, true, true,
                               plan_out);
 }
 
@@ -289,7 +296,7 @@ extern "C" rr_status rr_plan_softmax(int64_t rows, int64_t cols, rr_dtype x_dtyp
                                      rr_dtype y_dtype, rr_tier tier, int32_t cu_count,
                                      rr_plan* plan_out)
 {
-    return rr::plan_softmax(rows, cols, x_dtype, y_dtype, tier, cu_count, true, plan_out);
+    return rr::plan_softmax(rows, cols, x_dtype, y_dtype, tier, cu_count, true, true, plan_out);
 }
 
 extern "C" const char* rr_status_string(rr_status s)

@@ -75,7 +75,14 @@ __device__ __forceinline__ typename M::acc_t thread_fold(const typename M::in_t*
 }
 
 // ------------------------------------------------------------ block tier
-template <class M, int VEC>
+// VEC == 4: each row's body from its first 16-byte boundary goes in 128-bit
+// loads; its head (h <= 3 elements before that boundary) and its tail (at
+// most 3 elements after the last whole chunk) one element to each of the
+// first h + tl threads, loaded before the body so that every load of the row
+// is in flight at once.
+// VEC == 4 and not PEEL: every row starts 16-byte aligned (only the tail
+// chunk of a row goes element by element, after the body).
+template <class M, int VEC, bool PEEL>
 __global__ __launch_bounds__(kBlockThreads) void k_reduce_block(
     const typename M::in_t* __restrict__ x, typename M::out_t y, int64_t rows,
     int64_t cols, int64_t ld)
@@ -84,8 +91,25 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce_block(
     __shared__ A slot[2][kWavesPerBlock];
     int par = 0;
     for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
-        A acc = thread_fold<M, VEC, kBlockThreads, kBlockUnroll>(x + r * ld, 0, cols,
-                                                                  threadIdx.x, M::identity());
+        const typename M::in_t* row = x + r * ld;
+        A acc;
+        if constexpr (VEC == 4 && !PEEL) {
+            acc = thread_fold<M, 4, kBlockThreads, kBlockUnroll>(row, 0, cols, threadIdx.x,
+                                                                  M::identity());
+        } else if constexpr (VEC == 4) {
+            const int64_t h = head_elems(row, cols);
+            const int64_t nbe = (cols - h) & ~(int64_t)3;
+            const int64_t t = threadIdx.x;
+            const int64_t e = t < h ? t : t < cols - nbe ? nbe + t : -1;  // extra's column
+            const typename M::in_t xe = row[e >= 0 ? e : 0];
+            acc = thread_fold<M, 4, kBlockThreads, kBlockUnroll>(row + h, 0, nbe, threadIdx.x,
+                                                                  M::identity());
+            if (e >= 0)
+                acc = M::combine(acc, M::lift(xe));
+        } else {
+            acc = thread_fold<M, 1, kBlockThreads, kBlockUnroll>(row, 0, cols, threadIdx.x,
+                                                                 M::identity());
+        }
         acc = block_reduce<M, kBlockThreads>(acc, slot[par]);
         par ^= 1;
         if (threadIdx.x == 0)
@@ -95,12 +119,21 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce_block(
 
 // ------------------------------------------------------------- wave tier
 // S lanes per row (S >= ceil(cols / VEC)); 64 / S rows per group and
-// kWaveRowGroups groups per wavefront task.  Lane l of a row owns columns
-// [(l % S) * VEC, (l % S) * VEC + VEC).  All loads of a task are issued
+// kWaveRowGroups groups per wavefront task.  VEC == 4 (rows of at least 7
+// elements, so every row has a whole chunk): a row's body starts at its
+// first 16-byte boundary, h = 0..3 elements in; lane l < nb (nb = whole body
+// chunks) owns columns [h + 4l, h + 4l + 4), and the head and the tail
+// (h + tl <= 6 elements) go one element to lanes 0, 1, ... (NX per lane).
+// VEC == 1: lane l owns column l.  (Fewer lanes per row with several chunks
+// each -- a shorter cross-lane combine -- measured slower: 38.5 against
+// 32.5 us for f32 sums of [1048576, 48].)  All loads of a task are issued
 // before any is folded, at clamped addresses that stay inside the row (rows
-// past the end read the last row; the values are then masked off), so the
-// wavefront has kWaveRowGroups loads in flight without branches between.
-template <class M, int VEC, int S>
+// past the end read the last row, lanes without a chunk or an element the
+// first ones; those values are masked off), so the wavefront has all of them
+// in flight without branches between.
+// PEEL false: every row starts 16-byte aligned and is whole chunks (no head
+// or tail elements).
+template <class M, int VEC, int S, bool PEEL>
 __global__ __launch_bounds__(kBlockThreads) void k_reduce_wave(
     const typename M::in_t* __restrict__ x, typename M::out_t y, int64_t rows,
     int64_t cols, int64_t ld)
@@ -109,54 +142,65 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce_wave(
     using A = typename M::acc_t;
     constexpr int RPG = kWave / S;
     constexpr int U = kWaveRowGroups;
+    constexpr int NX = VEC == 4 && PEEL ? (6 + S - 1) / S : 0;  // head / tail elements per lane
     const int lane = lane_id();
     const int seg = lane / S;
-    const int64_t c0 = (int64_t)(lane % S) * VEC;
-    const bool full = c0 + VEC <= cols;               // lane owns a whole chunk
-    const int64_t ntail = cols - c0;                  // 1 .. VEC-1 on the partial-chunk lane
-    const bool tail = VEC > 1 && !full && ntail > 0;
+    const int li = lane % S;
     const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
     for (int64_t w = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
          w * RPG * U < rows; w += nwaves) {
         const int64_t row0 = w * RPG * U;
         Vec<T, VEC> v[U];
+        T xe[U][NX > 0 ? NX : 1];
+        bool full[U], has[U][NX > 0 ? NX : 1];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             int64_t r = row0 + (int64_t)u * RPG + seg;
             r = r < rows ? r : rows - 1;
-            const T* p = x + r * ld + (full ? c0 : 0);
+            const T* rp = x + r * ld;
             if constexpr (VEC == 4) {
-                if (cols >= 4)
-                    v[u] = load4<T, true>(p);
+                // 32-bit column arithmetic: a wave-tier row has at most 64 columns
+                const int c = (int)cols;
+                const int h = PEEL ? (int)head_elems(rp, cols) : 0;
+                const int nbe = (c - h) & ~3;
+                full[u] = li * 4 < nbe;
+                v[u] = load4<T, true>(rp + h + (full[u] ? li * 4 : 0));
+#pragma unroll
+                for (int k = 0; k < NX; ++k) {
+                    // head or tail element ex of h + tl = cols - nbe: column ex
+                    // of the head, or nbe + ex (= h + nbe + (ex - h)) of the tail
+                    const int ex = li + k * S;
+                    has[u][k] = ex < c - nbe;
+                    xe[u][k] = rp[has[u][k] ? (ex < h ? ex : nbe + ex) : 0];
+                }
             } else {
-                v[u].v[0] = *p;
+                full[u] = li < cols;
+                v[u].v[0] = rp[full[u] ? li : 0];
             }
         }
+        __builtin_amdgcn_sched_barrier(0);  // every load of the task goes out before any fold
         A acc[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             acc[u] = M::identity();
 #pragma unroll
             for (int i = 0; i < VEC; ++i)
-                acc[u] = full ? M::combine(acc[u], M::lift(v[u].v[i])) : acc[u];
-        }
-        if (VEC > 1 && (cols % VEC) != 0) {
-            // the lane holding the partial last chunk folds it element by element
+                acc[u] = full[u] ? M::combine(acc[u], M::lift(v[u].v[i])) : acc[u];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                int64_t r = row0 + (int64_t)u * RPG + seg;
-                r = r < rows ? r : rows - 1;
-                if (tail)
-                    for (int64_t i = 0; i < ntail; ++i)
-                        acc[u] = M::combine(acc[u], M::lift(x[r * ld + c0 + i]));
-            }
+            for (int k = 0; k < NX; ++k)
+                acc[u] = has[u][k] ? M::combine(acc[u], M::lift(xe[u][k])) : acc[u];
         }
+        // Every lane of a segment holds the row's result after the combine,
+        // so all of them store it (the same bits to one address), and rows
+        // past the end store their clamped row's result -- the last row's,
+        // computed the same way -- to that row.  No store is predicated: a
+        // predicated store between two groups makes the memory-counter wait
+        // before the next group's fold also hold for a load it does not need.
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             A t = segment_reduce<M, S>(acc[u]);
             const int64_t r = row0 + (int64_t)u * RPG + seg;
-            if ((lane % S) == 0 && r < rows)
-                M::store(y, r, t);
+            M::store(y, r < rows ? r : rows - 1, t);
         }
     }
 }
@@ -268,16 +312,24 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce_splitk(
     if (threadIdx.x == 0)
         last = false;
     const int64_t total = rows * G;
-    const int64_t ntiles = ceil_div(cols, kTile);
     for (int64_t b = blockIdx.x; b < total; b += gridDim.x) {
         const int64_t r = b / G;
         const int32_t g = (int32_t)(b - r * G);
-        const typename M::in_t* row = x + r * ld;
+        // Tiles cover the row's body from its first 16-byte boundary (h
+        // elements in, VEC == 4); workgroup 0 also folds the head [0, h),
+        // one element to each of its first threads.
+        const typename M::in_t* row0 = x + r * ld;
+        const int64_t h = VEC == 4 ? head_elems(row0, cols) : 0;
+        const typename M::in_t* row = row0 + h;
+        const int64_t body = cols - h;
+        const int64_t ntiles = ceil_div(body, kTile);
         A acc = M::identity();
+        if (VEC == 4 && g == 0 && (int64_t)threadIdx.x < h)
+            acc = M::lift(row0[threadIdx.x]);
         // Whole tiles: each round issues the thread's kSplitKUnroll loads of
         // one tile, then folds them.  Tile indices are uniform across the
         // workgroup, so the loop branch is scalar.
-        const int64_t nfull = cols / kTile;
+        const int64_t nfull = body / kTile;
         const int64_t t_end = (int64_t)(g + 1) * ntiles / G;
         const int64_t t_full = t_end < nfull ? t_end : nfull;
         int64_t t = (int64_t)g * ntiles / G;
@@ -293,7 +345,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce_splitk(
         // The partial last tile, if this workgroup owns it.
         for (; t < t_end; ++t) {
             const int64_t begin = t * kTile;
-            const int64_t end = begin + kTile < cols ? begin + kTile : cols;
+            const int64_t end = begin + kTile < body ? begin + kTile : body;
             acc = thread_fold<M, VEC, kBlockThreads, kSplitKUnroll>(row, begin, end, threadIdx.x, acc);
         }
         acc = block_reduce<M, kBlockThreads>(acc, slot[par]);
@@ -420,28 +472,37 @@ static rr_status launch_monoid(const rr_plan& p, const ReduceLaunch& a)
     const hipStream_t s = a.stream;
     switch (p.tier) {
     case RR_TIER_BLOCK:
-        return a.vec ? launch_kernel(k_reduce_block<M, 4>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld)
-                     : launch_kernel(k_reduce_block<M, 1>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld);
-    case RR_TIER_WAVE:
+        return !a.vec ? launch_kernel(k_reduce_block<M, 1, false>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld)
+               : a.rows16 ? launch_kernel(k_reduce_block<M, 4, false>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld)
+                          : launch_kernel(k_reduce_block<M, 4, true>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld);
+    case RR_TIER_WAVE: {
+        // 128-bit chunks for rows of at least 7 elements (as the plan's
+        // lanes); head and tail elements unless every row is aligned whole chunks
+        const bool v4 = a.vec && a.cols >= 7;
+        const bool peel = !(a.rows16 && a.cols % 4 == 0);
         switch (p.lanes_per_row) {
         case 4:
-            return a.vec ? launch_kernel(k_reduce_wave<M, 4, 4>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld)
-                         : launch_kernel(k_reduce_wave<M, 1, 4>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld);
+            return !v4 ? launch_kernel(k_reduce_wave<M, 1, 4, false>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld)
+                   : peel ? launch_kernel(k_reduce_wave<M, 4, 4, true>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld)
+                          : launch_kernel(k_reduce_wave<M, 4, 4, false>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld);
         case 16:
-            return a.vec ? launch_kernel(k_reduce_wave<M, 4, 16>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld)
-                         : launch_kernel(k_reduce_wave<M, 1, 16>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld);
+            return !v4 ? launch_kernel(k_reduce_wave<M, 1, 16, false>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld)
+                   : peel ? launch_kernel(k_reduce_wave<M, 4, 16, true>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld)
+                          : launch_kernel(k_reduce_wave<M, 4, 16, false>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld);
         case 64:
-            return a.vec ? launch_kernel(k_reduce_wave<M, 4, 64>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld)
-                         : launch_kernel(k_reduce_wave<M, 1, 64>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld);
+            return !v4 ? launch_kernel(k_reduce_wave<M, 1, 64, false>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld)
+                   : peel ? launch_kernel(k_reduce_wave<M, 4, 64, true>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld)
+                          : launch_kernel(k_reduce_wave<M, 4, 64, false>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld);
         default:
             return RR_ERR_TIER;
         }
+    }
     case RR_TIER_TILED:
-        return a.vec ? launch_kernel(k_reduce_tiled<M, 4, kTiledRows>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld)
-                     : launch_kernel(k_reduce_tiled<M, 1, kTiledRows>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld);
+        return a.rows16 ? launch_kernel(k_reduce_tiled<M, 4, kTiledRows>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld)
+                        : launch_kernel(k_reduce_tiled<M, 1, kTiledRows>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld);
     case RR_TIER_SERIAL:
-        return a.vec ? launch_kernel(k_reduce_tiled<M, 4, 1>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld)
-                     : launch_kernel(k_reduce_tiled<M, 1, 1>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld);
+        return a.rows16 ? launch_kernel(k_reduce_tiled<M, 4, 1>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld)
+                        : launch_kernel(k_reduce_tiled<M, 1, 1>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld);
     case RR_TIER_SPLITK: {
         uint32_t* ticket = static_cast<uint32_t*>(a.workspace);
         A* part = reinterpret_cast<A*>(static_cast<char*>(a.workspace) +

@@ -92,6 +92,33 @@ __device__ __forceinline__ void load_padded(const XT* row, int64_t j0, int64_t c
     }
 }
 
+// Whether a chunk of E output elements can be stored at p with one (or two)
+// vector stores: 16-byte alignment, 8 bytes for a bf16 chunk of 4.
+template <class YT, int E>
+__device__ __forceinline__ bool chunk_aligned(const YT* p)
+{
+    constexpr int kAlign = E * (int)sizeof(YT) < 16 ? E * (int)sizeof(YT) : 16;
+    return ((uint32_t)(uintptr_t)p & (uint32_t)(kAlign - 1)) == 0;
+}
+
+// store_masked with the vector form chosen at run time (yvec: the row's
+// chunks are chunk_aligned).
+template <class YT, int E>
+__device__ __forceinline__ void store_masked_rt(YT* row, int64_t j0, int64_t cols, const float* v,
+                                                bool yvec)
+{
+    if constexpr (E > 1) {
+        if (yvec && j0 + E <= cols) {
+            YOut<YT>::template chunk<E>(row + j0, v);
+            return;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < E; ++i)
+        if (j0 + i < cols)
+            YOut<YT>::one(row + j0 + i, v[i]);
+}
+
 template <class YT, int E, bool VEC>
 __device__ __forceinline__ void store_masked(YT* row, int64_t j0, int64_t cols, const float* v)
 {
@@ -171,6 +198,35 @@ __device__ __forceinline__ void store_tile_masked(YT* row, int64_t begin, int64_
                                  v + u * E);
 }
 
+// Tile stores with the vector form chosen at run time (yvec: the row's chunks
+// are chunk_aligned; else element by element).
+template <class YT, int E, int U>
+__device__ __forceinline__ void store_tile_full_rt(YT* tile, const float* v, bool yvec)
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        YT* p = tile + ((int64_t)u * kBlockThreads + threadIdx.x) * E;
+        if (E > 1 && yvec) {
+            if constexpr (E > 1)
+                YOut<YT>::template chunk<E>(p, v + u * E);
+        } else {
+#pragma unroll
+            for (int i = 0; i < E; ++i)
+                YOut<YT>::one(p + i, v[u * E + i]);
+        }
+    }
+}
+
+template <class YT, int E, int U>
+__device__ __forceinline__ void store_tile_masked_rt(YT* row, int64_t begin, int64_t cols,
+                                                     const float* v, bool yvec)
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        store_masked_rt<YT, E>(row, begin + ((int64_t)u * kBlockThreads + threadIdx.x) * E, cols,
+                               v + u * E, yvec);
+}
+
 // A thread's share of one whole tile as loaded, before conversion to float,
 // so that the next tile's loads can be in flight while this one is folded.
 // Plain (cached) loads: split-K statistics passes are followed by a map pass
@@ -247,6 +303,67 @@ __device__ __forceinline__ void load_row_raw(const void* row, int64_t row_bytes,
     }
 }
 
+// A persistent row as loaded: the thread's NCH 16-byte chunks of the row's
+// body and, for rows that do not start 16-byte aligned or do not end on a
+// chunk, one element of the head or the tail (PeelGeom).
+template <int NCH>
+struct RowBuf {
+    uint4 c[NCH];
+    float e;
+};
+
+// Where a row's elements go when its body is whole 16-byte chunks from its
+// first 16-byte boundary ("reduce", algorithm.gpu.rowwise, tier semantics:
+// full-width tiles on the aligned chunks, one-element tiles on the rest): h
+// head elements, nbe body elements (a multiple of E), tl tail elements.
+// Thread t < h holds head element t; thread h <= t < h + tl holds tail
+// element h + nbe + (t - h) (h + tl <= 2E - 2, fewer than any workgroup's
+// threads); `idx` is that element's column, or -1.
+template <class XT>
+struct PeelGeom {
+    int64_t h, nbe, idx;
+    __device__ PeelGeom(const XT* xr, int64_t cols)
+    {
+        constexpr int E = XIn<XT>::kChunk;
+        h = head_elems(xr, cols);
+        nbe = (cols - h) / E * E;
+        const int64_t tl = cols - h - nbe;
+        const int64_t t = threadIdx.x;
+        idx = t < h ? t : t < h + tl ? nbe + t : -1;
+    }
+};
+
+// Load a row's body chunks and the thread's head or tail element through one
+// buffer descriptor over the row (bytes 0 when the row is not live: nothing
+// is read, every value comes back as zero; the element is then -inf).
+template <class XT, int NCH, int NT>
+__device__ __forceinline__ void load_row_peeled(const XT* xr, int64_t cols, bool live,
+                                                RowBuf<NCH>& buf)
+{
+    const PeelGeom<XT> pg(xr, cols);
+    const int64_t row_bytes = live ? cols * (int64_t)sizeof(XT) : 0;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<XT*>(xr), 0, (int)row_bytes, kBufferWord3);
+    const int body = (int)(pg.h * (int64_t)sizeof(XT));
+    const int body_end = live ? (int)((pg.h + pg.nbe) * (int64_t)sizeof(XT)) : 0;
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+        const int off = ((int)threadIdx.x + k * NT) * 16;
+        // chunks past the body read as zero (never used): clamp them to an
+        // offset past the descriptor's range
+        const int o = off + 16 <= body_end - body ? body + off : row_bytes + 16;
+        const rr_u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, o, 0, kBufferNonTemporal);
+        buf.c[k] = make_uint4(v.x, v.y, v.z, v.w);
+    }
+    const int eo = pg.idx >= 0 ? (int)(pg.idx * (int64_t)sizeof(XT)) : row_bytes + 16;
+    float e;
+    if constexpr (sizeof(XT) == 2)
+        e = bf16_bits_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rs, eo, 0, kBufferNonTemporal));
+    else
+        e = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, eo, 0, kBufferNonTemporal));
+    buf.e = (live && pg.idx >= 0) ? e : -__builtin_inff();
+}
+
 // Persistent rows with a one-row prefetch.  Workgroup b takes rows b, b + step,
 // ... < rows; the loads of the next row go out before the current row is
 // computed, into the other of two register buffers.  On gfx9 one in-order
@@ -262,12 +379,13 @@ __device__ __forceinline__ void load_row_raw(const void* row, int64_t row_bytes,
 //     previous row's stores.
 // Loads the caller issues before this (a row's weights) retire with the first
 // row.  With no next row the prefetch still goes out, with no bytes to read
-// (load_row_raw then reads zeros and touches no memory), so no load sits
-// behind a branch.  load(r, live, buf) issues row r's loads (none of its bytes
-// when live is false); start() runs once, after the first two rows' loads are
-// out (to unpack what the caller loaded before); row(buf, r, parity) computes
-// and stores row r (parity alternates, for double-buffered shared memory).
-template <int NCH, class Load, class Start, class Row>
+// (the buffer loads then read zeros and touch no memory), so no load sits
+// behind a branch.  load(r, live, buf) issues row r's loads (none of its
+// bytes when live is false); start() runs once, after the first two rows'
+// loads are out (to unpack what the caller loaded before); row(buf, r,
+// parity) computes and stores row r (parity alternates, for double-buffered
+// shared memory).
+template <class Buf, class Load, class Start, class Row>
 __device__ __forceinline__ void persistent_rows(int64_t r, int64_t step, int64_t rows, Load load,
                                                 Start start, Row row)
 {
@@ -275,7 +393,7 @@ __device__ __forceinline__ void persistent_rows(int64_t r, int64_t step, int64_t
     // 64-bit less-than has no scalar form and would put a VGPR write, and
     // with it a wait, ahead of the prefetch).
     int64_t left = (rows - 1 - r) / step;
-    uint4 a[NCH], c[NCH];
+    Buf a, c;
     load(r, true, a);
     __builtin_amdgcn_sched_barrier(0);  // the first row's loads go out first
     load(r + step, left != 0, c);

@@ -29,16 +29,13 @@ constexpr float kNegInf = -__builtin_inff();
 // error is relative to the (small) argument whatever the size of m.  A
 // fused x*log2(e) - m*log2(e) would carry the rounding of m*log2(e), half an
 // ulp of |m|*1.44, into every exponent (a relative error of 4e-5 at m = 1000,
-// different in every thread).  The hardware exponential is exact for normal results; when any argument
-// falls below -126 (a subnormal or vanishing result, or a -inf entry) the
-// thread recomputes its values with exp2f, which scales the range itself.
+// different in every thread).  The hardware exponential is exact for normal
+// results; when any argument falls below -126 (a subnormal or vanishing
+// result, or a -inf entry) the thread takes exp2_sub, which scales such
+// arguments into the normal range.  m is the thread's maximum.
 template <int N>
-__device__ __forceinline__ MS local_exp_sum(float* v)
+__device__ __forceinline__ MS exp_sum_from(float* v, float m)
 {
-    float m = kNegInf;
-#pragma unroll
-    for (int i = 0; i < N; ++i)
-        m = fmaxf(m, v[i]);
     float s = 0.0f;
     if (m != kNegInf) {
         float tmin = 0.0f;
@@ -54,7 +51,7 @@ __device__ __forceinline__ MS local_exp_sum(float* v)
         } else {
 #pragma unroll
             for (int i = 0; i < N; ++i)
-                v[i] = exp2_f32(v[i]);
+                v[i] = exp2_sub(v[i]);
         }
 #pragma unroll
         for (int i = 0; i < N; ++i)
@@ -65,6 +62,34 @@ __device__ __forceinline__ MS local_exp_sum(float* v)
             v[i] = 0.0f;
     }
     return MS{m, s};
+}
+
+template <int N>
+__device__ __forceinline__ MS local_exp_sum(float* v)
+{
+    float m = kNegInf;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        m = fmaxf(m, v[i]);
+    return exp_sum_from<N>(v, m);
+}
+
+// Pass 1 on a thread's N values plus one more element e (a misaligned row's
+// head or tail element, or -inf for none): the maximum covers both; e's
+// exponential (exp2_sub, any range) is added after the others' sum and
+// returned in *pe for pass 2.
+template <int N>
+__device__ __forceinline__ MS local_exp_sum_plus(float* v, float e, float* pe)
+{
+    float m = e;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        m = fmaxf(m, v[i]);
+    MS own = exp_sum_from<N>(v, m);
+    const float p = e == kNegInf ? 0.0f : exp2_sub((e - m) * kLog2e);
+    own.s += p;
+    *pe = p;
+    return own;
 }
 
 // Row statistics (M, S) over the workgroup from each thread's (m_t, s_t),
@@ -96,6 +121,10 @@ __device__ __forceinline__ MS block_softmax_stats(MS own, MS* slot, float* e_t)
 }
 
 // ------------------------------------------- block tier, row in registers
+// VEC: each row's body from its first 16-byte boundary goes in chunks (the
+// tail chunk element by element); the head, h < E elements before that
+// boundary, one element to each of the first threads.  y's chunks are stored
+// whole when y + h is aligned for them, else element by element.
 template <class XT, class YT, int NCH, bool VEC, int NT>
 __global__ __launch_bounds__(NT) void k_softmax_block(const XT* __restrict__ x,
                                                       YT* __restrict__ y, int64_t rows,
@@ -107,12 +136,18 @@ __global__ __launch_bounds__(NT) void k_softmax_block(const XT* __restrict__ x,
     for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
         const XT* xr = x + r * ldx;
         YT* yr = y + r * ldy;
+        const int64_t h = VEC ? head_elems(xr, cols) : 0;
+        const int64_t cb = cols - h;
+        const bool yvec = VEC && chunk_aligned<YT, E>(yr + h);
         float v[NCH * E];
 #pragma unroll
         for (int k = 0; k < NCH; ++k)
-            load_padded<XT, E, VEC>(xr, ((int64_t)threadIdx.x + (int64_t)k * NT) * E, cols,
+            load_padded<XT, E, VEC>(xr + h, ((int64_t)threadIdx.x + (int64_t)k * NT) * E, cb,
                                     v + k * E);
-        const MS own = local_exp_sum<NCH * E>(v);
+        const bool has_e = (int64_t)threadIdx.x < h;
+        const float e = has_e ? XIn<XT>::one(xr + threadIdx.x) : kNegInf;
+        float pe;
+        const MS own = local_exp_sum_plus<NCH * E>(v, e, &pe);
         float e_t;
         const MS tot = block_softmax_stats<NT>(own, slot[par], &e_t);
         par ^= 1;
@@ -122,53 +157,76 @@ __global__ __launch_bounds__(NT) void k_softmax_block(const XT* __restrict__ x,
             v[i] *= sc;
 #pragma unroll
         for (int k = 0; k < NCH; ++k)
-            store_masked<YT, E, VEC>(yr, ((int64_t)threadIdx.x + (int64_t)k * NT) * E, cols,
-                                     v + k * E);
+            store_masked_rt<YT, E>(yr + h, ((int64_t)threadIdx.x + (int64_t)k * NT) * E, cb,
+                                   v + k * E, yvec);
+        if (has_e)
+            YOut<YT>::one(yr + threadIdx.x, pe * sc);
     }
 }
 
 // ------------------------- block tier, persistent rows with prefetch
-// Whole-chunk rows (cols a multiple of the chunk, 16-byte aligned rows):
-// workgroup b takes rows b, b + grid, b + 2*grid, ... and loads the next
+// Workgroup b takes rows b, b + grid, b + 2*grid, ... and loads the next
 // row's chunks while it computes the current one, so each workgroup keeps a
 // row's worth of loads in flight through its compute phase.  Two register
-// buffers alternate; when there is no next row the prefetch re-reads the
-// current one (an L2 hit) and is dropped, so no load sits behind a branch.
-// EXACT: cols == NT * NCH * chunk, so every chunk of every thread is in the
-// row and no per-chunk bound check is emitted.
-template <class XT, class YT, int NCH, int NT, bool EXACT>
-__device__ __forceinline__ void softmax_row_from_chunks(const uint4* raw, YT* yr, int64_t cols,
-                                                        MS* slot)
+// buffers alternate; when there is no next row the prefetch goes out with no
+// bytes to read and is dropped, so no load sits behind a branch.
+// EXACT: cols == NT * NCH * chunk and every row 16-byte aligned, so every
+// chunk of every thread is in the row and no per-chunk bound check is
+// emitted.  PEEL: rows at any element offset or length -- each row's body
+// of whole chunks from its first 16-byte boundary, and one head or tail
+// element per thread (PeelGeom); y's chunks are stored whole when y + h is
+// aligned for them.  Neither: 16-byte aligned rows of whole chunks.
+template <class XT, class YT, int NCH, int NT, bool EXACT, bool PEEL>
+__device__ __forceinline__ void softmax_row_from_chunks(const RowBuf<NCH>& buf, const XT* xr,
+                                                        YT* yr, int64_t cols, MS* slot)
 {
     constexpr int E = XIn<XT>::kChunk;
+    int64_t h = 0, nbe = cols, idx = -1;
+    if constexpr (PEEL) {
+        const PeelGeom<XT> pg(xr, cols);
+        h = pg.h;
+        nbe = pg.nbe;
+        idx = pg.idx;
+    }
     float v[NCH * E];
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
         const int64_t j0 = ((int64_t)threadIdx.x + (int64_t)k * NT) * E;
-        if (EXACT || j0 < cols) {
-            unpack_chunk<XT>(raw[k], v + k * E);
+        if (EXACT || j0 < nbe) {
+            unpack_chunk<XT>(buf.c[k], v + k * E);
         } else {
 #pragma unroll
             for (int i = 0; i < E; ++i)
                 v[k * E + i] = kNegInf;
         }
     }
-    const MS own = local_exp_sum<NCH * E>(v);
+    float pe = 0.0f;
+    const MS own = PEEL ? local_exp_sum_plus<NCH * E>(v, buf.e, &pe) : local_exp_sum<NCH * E>(v);
     float e_t;
     const MS tot = block_softmax_stats<NT>(own, slot, &e_t);
     const float sc = e_t / tot.s;
 #pragma unroll
     for (int i = 0; i < NCH * E; ++i)
         v[i] *= sc;
+    const bool yvec = !PEEL || chunk_aligned<YT, E>(yr + h);
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
         const int64_t j0 = ((int64_t)threadIdx.x + (int64_t)k * NT) * E;
-        if (EXACT || j0 < cols)
-            YOut<YT>::template chunk<E>(yr + j0, v + k * E);
+        if (EXACT || j0 < nbe) {
+            if (!PEEL || yvec) {
+                YOut<YT>::template chunk<E>(yr + h + j0, v + k * E);
+            } else {
+#pragma unroll
+                for (int i = 0; i < E; ++i)
+                    YOut<YT>::one(yr + h + j0 + i, v[k * E + i]);
+            }
+        }
     }
+    if (PEEL && idx >= 0)
+        YOut<YT>::one(yr + idx, pe * sc);
 }
 
-template <class XT, class YT, int NCH, int NT, bool EXACT>
+template <class XT, class YT, int NCH, int NT, bool EXACT, bool PEEL>
 __global__ __launch_bounds__(NT) void k_softmax_rows_pf(const XT* __restrict__ x,
                                                         YT* __restrict__ y, int64_t rows,
                                                         int64_t cols, int64_t ldx, int64_t ldy)
@@ -176,19 +234,25 @@ __global__ __launch_bounds__(NT) void k_softmax_rows_pf(const XT* __restrict__ x
     __shared__ MS slot[2][NT / kWave];
     if ((int64_t)blockIdx.x >= rows)
         return;
-    persistent_rows<NCH>(
+    persistent_rows<RowBuf<NCH>>(
         blockIdx.x, gridDim.x, rows,
-        [&](int64_t r, bool live, uint4* raw) {
-            load_row_raw<NCH, NT>(x + r * ldx, live ? cols * (int64_t)sizeof(XT) : 0, raw);
+        [&](int64_t r, bool live, RowBuf<NCH>& buf) {
+            if constexpr (PEEL)
+                load_row_peeled<XT, NCH, NT>(x + r * ldx, cols, live, buf);
+            else
+                load_row_raw<NCH, NT>(x + r * ldx, live ? cols * (int64_t)sizeof(XT) : 0, buf.c);
         },
         [] {},
-        [&](const uint4* raw, int64_t r, int par) {
-            softmax_row_from_chunks<XT, YT, NCH, NT, EXACT>(raw, y + r * ldy, cols, slot[par]);
+        [&](const RowBuf<NCH>& buf, int64_t r, int par) {
+            softmax_row_from_chunks<XT, YT, NCH, NT, EXACT, PEEL>(buf, x + r * ldx, y + r * ldy,
+                                                                  cols, slot[par]);
         });
 }
 
 // ---------------------------------------- block tier, streaming long rows
-// Pass 1 folds (m, s) chunk by chunk; pass 2 reads x again.
+// Pass 1 folds (m, s) chunk by chunk; pass 2 reads x again.  VEC: the row's
+// body from its first 16-byte boundary in chunks, the head (h < E elements)
+// first, one element to each of the first threads.
 template <class XT, class YT, bool VEC, int NT>
 __global__ __launch_bounds__(NT) void k_softmax_stream(const XT* __restrict__ x,
                                                        YT* __restrict__ y, int64_t rows,
@@ -198,15 +262,25 @@ __global__ __launch_bounds__(NT) void k_softmax_stream(const XT* __restrict__ x,
     __shared__ MS slot[2][NT / kWave];
     int par = 0;
     for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
-        const XT* xr = x + r * ldx;
-        YT* yr = y + r * ldy;
+        const XT* xr0 = x + r * ldx;
+        YT* yr0 = y + r * ldy;
+        const int64_t h = VEC ? head_elems(xr0, cols) : 0;
+        const bool has_e = (int64_t)threadIdx.x < h;
+        const XT* xr = xr0 + h;
+        YT* yr = yr0 + h;
+        const int64_t cb = cols - h;
+        const bool yvec = VEC && chunk_aligned<YT, E>(yr);
         // per-thread running (m, s); s is kept in double because a thread
         // adds many terms in sequence on long rows
         float tm = kNegInf;
         double ts = 0.0;
-        for (int64_t j0 = (int64_t)threadIdx.x * E; j0 < cols; j0 += (int64_t)NT * E) {
+        if (has_e) {
+            tm = XIn<XT>::one(xr0 + threadIdx.x);
+            ts = tm == kNegInf ? 0.0 : 1.0;
+        }
+        for (int64_t j0 = (int64_t)threadIdx.x * E; j0 < cb; j0 += (int64_t)NT * E) {
             float v[E];
-            load_padded<XT, E, VEC>(xr, j0, cols, v);
+            load_padded<XT, E, VEC>(xr, j0, cb, v);
             float cm = kNegInf;
 #pragma unroll
             for (int i = 0; i < E; ++i)
@@ -224,13 +298,16 @@ __global__ __launch_bounds__(NT) void k_softmax_stream(const XT* __restrict__ x,
         const MS tot = block_reduce<SoftmaxMS, NT>(MS{tm, (float)ts}, slot[par]);
         par ^= 1;
         const float inv = 1.0f / tot.s;
-        for (int64_t j0 = (int64_t)threadIdx.x * E; j0 < cols; j0 += (int64_t)NT * E) {
+        if (has_e)
+            YOut<YT>::one(yr0 + threadIdx.x,
+                          exp2_f32((XIn<XT>::one(xr0 + threadIdx.x) - tot.m) * kLog2e) * inv);
+        for (int64_t j0 = (int64_t)threadIdx.x * E; j0 < cb; j0 += (int64_t)NT * E) {
             float v[E];
-            load_padded<XT, E, VEC>(xr, j0, cols, v);
+            load_padded<XT, E, VEC>(xr, j0, cb, v);
 #pragma unroll
             for (int i = 0; i < E; ++i)
                 v[i] = exp2_f32((v[i] - tot.m) * kLog2e) * inv;
-            store_masked<YT, E, VEC>(yr, j0, cols, v);
+            store_masked_rt<YT, E>(yr, j0, cb, v, yvec);
         }
     }
 }
@@ -330,7 +407,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_softmax_tiled(const XT* __res
 // kSoftmaxSplitKUnroll 16-byte chunks per thread.
 
 // Exponentials of a thread's map arguments t: the hardware instruction when
-// every t >= -126 (exact there), else exp2f (subnormal results).
+// every t >= -126 (exact there), else exp2_sub (subnormal results).
 template <int N>
 __device__ __forceinline__ void exp2_values(float* t)
 {
@@ -345,7 +422,7 @@ __device__ __forceinline__ void exp2_values(float* t)
     } else {
 #pragma unroll
         for (int i = 0; i < N; ++i)
-            t[i] = exp2_f32(t[i]);
+            t[i] = exp2_sub(t[i]);
     }
 }
 
@@ -398,14 +475,24 @@ __global__ __launch_bounds__(kBlockThreads) void k_softmax_splitk_stats(
     __shared__ MS slot[2][kWavesPerBlock];
     int par = 0;
     const int64_t total = rows * G;
-    const int64_t ntiles = ceil_div(cols, kTile);
-    const int64_t nfull = cols / kTile;
     for (int64_t b = blockIdx.x; b < total; b += gridDim.x) {
         const int64_t r = b / G;
         const int32_t g = (int32_t)(b - r * G);
-        const XT* xr = x + r * ldx;
+        // Tiles cover the row's body from its first 16-byte boundary (VEC);
+        // workgroup 0 also takes the head, h < E elements, one element to
+        // each of its first threads.
+        const XT* xr0 = x + r * ldx;
+        const int64_t h = VEC ? head_elems(xr0, cols) : 0;
+        const XT* xr = xr0 + h;
+        const int64_t cb = cols - h;
+        const int64_t ntiles = ceil_div(cb, kTile);
+        const int64_t nfull = cb / kTile;
         float tm = kNegInf;
         double ts = 0.0;
+        if (VEC && g == 0 && (int64_t)threadIdx.x < h) {
+            tm = XIn<XT>::one(xr0 + threadIdx.x);
+            ts = tm == kNegInf ? 0.0 : 1.0;
+        }
         // Whole tiles g, g + G, ...: n of them.  Two register buffers; the
         // next tile's loads are issued before the current one is folded.
         // Trip counts are uniform over the workgroup (scalar branches).
@@ -437,7 +524,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_softmax_splitk_stats(
         }
         for (int64_t t = g + n * G; t < ntiles; t += G) {  // ragged last tile, -inf padded
             float v[N];
-            load_tile_padded<XT, E, VEC, U>(xr, t * kTile, cols, v);
+            load_tile_padded<XT, E, VEC, U>(xr, t * kTile, cb, v);
             stats_fold_tile<N>(v, tm, ts);
         }
         float e_t;
@@ -487,13 +574,20 @@ __global__ __launch_bounds__(kBlockThreads) void k_softmax_splitk_map(
     __shared__ float fslot[kWavesPerBlock];
     __shared__ double dslot[kWavesPerBlock];
     const int64_t total = rows * G;
-    const int64_t ntiles = ceil_div(cols, kTile);
-    const int64_t nfull = cols / kTile;
     for (int64_t b = blockIdx.x; b < total; b += gridDim.x) {
         const int64_t r = b / G;
         const int32_t g = (int32_t)(b - r * G);
-        const XT* xr = x + r * ldx;
-        YT* yr = y + r * ldy;
+        // the statistics pass's tiles (from the row's first 16-byte
+        // boundary); y's chunks are stored whole when y + h is aligned
+        const XT* xr0 = x + r * ldx;
+        YT* yr0 = y + r * ldy;
+        const int64_t h = VEC ? head_elems(xr0, cols) : 0;
+        const XT* xr = xr0 + h;
+        YT* yr = yr0 + h;
+        const int64_t cb = cols - h;
+        const int64_t ntiles = ceil_div(cb, kTile);
+        const int64_t nfull = cb / kTile;
+        const bool yvec = VEC && chunk_aligned<YT, E>(yr);
         // the row's pairs first, then the first tile: the fold waits only
         // for the pairs while the tile is in flight
         MS p = MS{kNegInf, 0.0f};
@@ -505,16 +599,25 @@ __global__ __launch_bounds__(kBlockThreads) void k_softmax_splitk_map(
             load_tile_full<XT, E, VEC, U>(xr + t * kTile, v);
         const MS st = fold_row_partials(p, fslot, dslot);
         const float inv = 1.0f / st.s;
+        if (VEC && g == 0 && (int64_t)threadIdx.x < h)
+            YOut<YT>::one(yr0 + threadIdx.x,
+                          exp2_f32((XIn<XT>::one(xr0 + threadIdx.x) - st.m) * kLog2e) * inv);
         for (; t < nfull; t += G) {
             map_tile<U * E>(v, st.m, inv);
-            store_tile_full<YT, E, VEC, U>(yr + t * kTile, v);
+            if (!VEC || yvec)
+                store_tile_full<YT, E, VEC, U>(yr + t * kTile, v);
+            else
+                store_tile_full_rt<YT, E, U>(yr + t * kTile, v, false);
             if (t + G < nfull)
                 load_tile_full<XT, E, VEC, U>(xr + (t + G) * kTile, v);
         }
         for (; t < ntiles; t += G) {
-            load_tile_padded<XT, E, VEC, U>(xr, t * kTile, cols, v);
+            load_tile_padded<XT, E, VEC, U>(xr, t * kTile, cb, v);
             map_tile<U * E>(v, st.m, inv);
-            store_tile_masked<YT, E, VEC, U>(yr, t * kTile, cols, v);
+            if (!VEC)
+                store_tile_masked<YT, E, VEC, U>(yr, t * kTile, cb, v);
+            else
+                store_tile_masked_rt<YT, E, U>(yr, t * kTile, cb, v, yvec);
         }
         __syncthreads();  // the fold's LDS slots are reused by the next row
     }
@@ -542,9 +645,13 @@ static rr_status launch_splitk(const rr_plan& p, const SoftmaxLaunch& a)
 template <class XT, class YT, int NCH, int NT>
 static rr_status launch_pf(const XT* x, YT* y, const rr_plan& p, const SoftmaxLaunch& a)
 {
-    constexpr int64_t kExactCols = (int64_t)NT * NCH * XIn<XT>::kChunk;
-    auto kernel = a.cols == kExactCols ? k_softmax_rows_pf<XT, YT, NCH, NT, true>
-                                       : k_softmax_rows_pf<XT, YT, NCH, NT, false>;
+    constexpr int E = XIn<XT>::kChunk;
+    constexpr int64_t kExactCols = (int64_t)NT * NCH * E;
+    // rows that start 16-byte aligned and end on a chunk need no head or tail
+    const bool whole = a.rows16 && a.cols % E == 0;
+    auto kernel = !whole ? k_softmax_rows_pf<XT, YT, NCH, NT, false, true>
+                  : a.cols == kExactCols ? k_softmax_rows_pf<XT, YT, NCH, NT, true, false>
+                                         : k_softmax_rows_pf<XT, YT, NCH, NT, false, false>;
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, NT, 0) != hipSuccess ||
         per_cu < 1)
@@ -585,8 +692,8 @@ static rr_status launch_block_tier(const rr_plan& p, const SoftmaxLaunch& a)
 {
     if constexpr (VEC) {
         constexpr int E = XIn<XT>::kChunk;
-        if (a.cols % E == 0) {
-            const RowPfShape sh = row_pf_shape(a.cols / E);
+        {
+            const RowPfShape sh = row_pf_shape(ceil_div(a.cols, E));
             if (sh.nt > 0) {
                 if (sh.nt != p.block)
                     return RR_ERR_TIER;  // plan and launch disagree: refuse, launch nothing
@@ -609,6 +716,23 @@ static rr_status launch_block_tier(const rr_plan& p, const SoftmaxLaunch& a)
 }
 
 template <class XT, class YT, bool VEC>
+static rr_status launch_wave(const rr_plan& p, const SoftmaxLaunch& a)
+{
+    const XT* x = static_cast<const XT*>(a.x);
+    YT* y = static_cast<YT*>(a.y);
+    const dim3 grid((unsigned)p.grid), block(kBlockThreads);
+    const hipStream_t s = a.stream;
+    switch (p.lanes_per_row) {
+    case 4: return launch_kernel(k_softmax_wave<XT, YT, VEC, 4>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
+    case 16: return launch_kernel(k_softmax_wave<XT, YT, VEC, 16>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
+    case 64: return launch_kernel(k_softmax_wave<XT, YT, VEC, 64>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
+    default: return RR_ERR_TIER;
+    }
+}
+
+// VEC (element-aligned x and y): the block and split-K tiers; the wave tier
+// takes 128-bit chunks only when every row is 16-byte aligned (rows16).
+template <class XT, class YT, bool VEC>
 static rr_status launch_typed(const rr_plan& p, const SoftmaxLaunch& a)
 {
     const XT* x = static_cast<const XT*>(a.x);
@@ -619,12 +743,7 @@ static rr_status launch_typed(const rr_plan& p, const SoftmaxLaunch& a)
     case RR_TIER_BLOCK:
         return launch_block_tier<XT, YT, VEC>(p, a);
     case RR_TIER_WAVE:
-        switch (p.lanes_per_row) {
-        case 4: return launch_kernel(k_softmax_wave<XT, YT, VEC, 4>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
-        case 16: return launch_kernel(k_softmax_wave<XT, YT, VEC, 16>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
-        case 64: return launch_kernel(k_softmax_wave<XT, YT, VEC, 64>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld_x, a.ld_y);
-        default: return RR_ERR_TIER;
-        }
+        return VEC && a.rows16 ? launch_wave<XT, YT, true>(p, a) : launch_wave<XT, YT, false>(p, a);
     case RR_TIER_SPLITK:
         return launch_splitk<XT, YT, VEC>(p, a);
     case RR_TIER_TILED:

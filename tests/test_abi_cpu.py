@@ -186,12 +186,12 @@ def test_softmax_tier_rule():
     assert rr.plan_softmax(8192, 8192)["tier"] == "block"
     assert rr.plan_softmax(8192, 8192)["block"] == 256
     assert rr.plan_softmax(8192, 8192)["grid"] == 512        # persistent rows: 2 per CU
-    assert rr.plan_softmax(8192, 8191)["grid"] == 8192       # ragged rows: one per workgroup
+    assert rr.plan_softmax(8192, 8191)["grid"] == 512        # ragged rows: persistent too
     assert rr.plan_softmax(64, 16384)["block"] == 512        # 2048 chunks: 512 threads x 4
     assert rr.plan_softmax(65536, 1024)["block"] == 64       # 128 chunks: one wavefront x 2
     assert rr.plan_softmax(65536, 1024)["grid"] == 256 * 16  # 32 loads per lane per CU
     assert rr.plan_softmax(64, 16385, tier="block")["block"] == 512  # ragged, long: wider
-    assert rr.plan_softmax(64, 8201)["block"] == 256         # ragged: one row per workgroup
+    assert rr.plan_softmax(64, 8201)["block"] == 512         # 1026 chunks: 512 threads x 4
     assert rr.plan_softmax(64, 8200)["block"] == 512         # 1025 whole chunks: persistent
     assert rr.plan_softmax(100, 40)["tier"] == "wave"
     assert rr.plan_softmax(100, 4)["tier"] == "tiled"
