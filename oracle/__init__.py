@@ -51,6 +51,9 @@ def _load():
         lib.rro_layernorm_rows.restype = ctypes.c_int
         lib.rro_attention_partials.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                                i32, i32, ctypes.c_float]
+        lib.rro_attention_partials_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64,
+                                                      i64, i64, i64, i32, i32, ctypes.c_float]
+        lib.rro_attention_partials_varlen.restype = ctypes.c_int
         lib.rro_bf16_from_double.argtypes = [ctypes.c_double]
         lib.rro_bf16_from_double.restype = ctypes.c_uint16
         lib.rro_bf16_to_double.argtypes = [ctypes.c_uint16]
@@ -235,6 +238,39 @@ def attention_partials(q, k, v, P, scale, kv_heads=None):
                                     heads, kvh, q_rows, kv_len, depth, P, float(scale))
     if rc:
         raise ValueError("rro_attention_partials rejected its arguments")
+    return o, m, l
+
+
+def attention_partials_varlen(q, k, v, cu_q, cu_k, P, scale):
+    """Split-K attention partials of packed variable-length sequences.
+
+    q: bf16 bits [total_q, heads, depth]; k, v: bf16 bits [total_k, kv_heads,
+    depth]; cu_q, cu_k: int32 [batch + 1] token offsets of each sequence.
+    Returns (o [P, total_q * heads, depth], m [P, total_q * heads],
+    l [P, total_q * heads]) float32, partial row t * heads + h for token t and
+    head h; rows of tokens that belong to no sequence are NaN (not written).
+    """
+    lib = _load()
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    v = np.ascontiguousarray(v, dtype=np.uint16)
+    cu_q = np.ascontiguousarray(cu_q, dtype=np.int32)
+    cu_k = np.ascontiguousarray(cu_k, dtype=np.int32)
+    total_q, heads, depth = q.shape
+    total_k, kvh, kd = k.shape
+    if kd != depth or v.shape != k.shape or cu_q.shape != cu_k.shape or cu_q.ndim != 1:
+        raise ValueError("q [total_q, heads, depth], k and v [total_k, kv_heads, depth], "
+                         "cu_q and cu_k [batch + 1]")
+    batch = cu_q.size - 1
+    rows = total_q * heads
+    o = np.full((P, rows, depth), np.nan, dtype=np.float32)
+    m = np.full((P, rows), np.nan, dtype=np.float32)
+    l = np.full((P, rows), np.nan, dtype=np.float32)
+    rc = lib.rro_attention_partials_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_q), _ptr(cu_k),
+                                           _ptr(o), _ptr(m), _ptr(l), batch, heads, kvh, total_q,
+                                           total_k, depth, P, float(scale))
+    if rc:
+        raise ValueError("rro_attention_partials_varlen rejected its arguments")
     return o, m, l
 
 

@@ -532,3 +532,97 @@ int rro_attention_partials(const uint16_t* q, const uint16_t* k, const uint16_t*
     free(acc);
     return RRO_OK;
 }
+
+/*
+ * Split-K attention partials of packed variable-length sequences ([FA4], the
+ * ragged placement of the combine's output: its Signature places each output
+ * tile by a head index and a row index into a ragged [tokens][heads][depth]
+ * tensor, with the tile's row count -- num_output_rows -- cut to the
+ * sequence).  Sequences are packed along the token axis:
+ *   q [total_q][heads][depth], k, v [total_k][kv_heads][depth]  (bf16 bits);
+ *   sequence b has queries cu_q[b] .. cu_q[b+1]-1 and keys
+ *   cu_k[b] .. cu_k[b+1]-1 (cu_q, cu_k: batch + 1 non-decreasing offsets,
+ *   cu[0] >= 0, cu[batch] <= total).
+ * Outputs, one partial row per (token t, head h) at t * heads + h:
+ *   o [P][total_q][heads][depth], m, l [P][total_q][heads].
+ * For each sequence this is rro_attention_partials of that sequence alone: the
+ * keys of sequence b are cut into P contiguous partitions of its own keys
+ * (p*n_b/P .. (p+1)*n_b/P - 1), with the same arithmetic in the same order;
+ * a sequence without keys gives (-inf, 0, 0) in every partition.  Rows of
+ * tokens that belong to no sequence are not written.
+ */
+int rro_attention_partials_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                  const int32_t* cu_q, const int32_t* cu_k, float* o, float* m,
+                                  float* l, int64_t batch, int64_t heads, int64_t kv_heads,
+                                  int64_t total_q, int64_t total_k, int32_t depth, int32_t P,
+                                  float scale)
+{
+    if (batch < 0 || heads < 1 || kv_heads < 1 || heads % kv_heads != 0 || total_q < 0 ||
+        total_k < 0 || depth < 1 || P < 1)
+        return RRO_BAD;
+    if (cu_q[0] < 0 || cu_k[0] < 0 || cu_q[batch] > total_q || cu_k[batch] > total_k)
+        return RRO_BAD;
+    for (int64_t b = 0; b < batch; ++b)
+        if (cu_q[b + 1] < cu_q[b] || cu_k[b + 1] < cu_k[b])
+            return RRO_BAD;
+    const int64_t group = heads / kv_heads;
+    const int64_t rows = total_q * heads;
+    double* s = (double*)malloc(sizeof(double) * (size_t)(total_k > 0 ? total_k : 1));
+    double* acc = (double*)malloc(sizeof(double) * (size_t)depth);
+    if (!s || !acc) {
+        free(s);
+        free(acc);
+        return RRO_BAD;
+    }
+    for (int64_t b = 0; b < batch; ++b) {
+        const int64_t n_k = cu_k[b + 1] - cu_k[b];
+        for (int64_t h = 0; h < heads; ++h) {
+            const int64_t kvh = h / group;
+            for (int64_t t = cu_q[b]; t < cu_q[b + 1]; ++t) {
+                const int64_t row = t * heads + h;
+                const uint16_t* qi = q + row * depth;
+                /* scores of every key of the sequence */
+                for (int64_t j = 0; j < n_k; ++j) {
+                    const uint16_t* kj = k + ((cu_k[b] + j) * kv_heads + kvh) * depth;
+                    double dot = 0.0;
+                    for (int32_t d = 0; d < depth; ++d)
+                        dot += rro_bf16_to_double(qi[d]) * rro_bf16_to_double(kj[d]);
+                    s[j] = (double)scale * dot;
+                }
+                for (int32_t p = 0; p < P; ++p) {
+                    const int64_t j0 = (int64_t)p * n_k / P;
+                    const int64_t j1 = ((int64_t)p + 1) * n_k / P;
+                    float* op = o + ((int64_t)p * rows + row) * depth;
+                    if (j1 <= j0) {
+                        m[(int64_t)p * rows + row] = -INFINITY;
+                        l[(int64_t)p * rows + row] = 0.0f;
+                        for (int32_t d = 0; d < depth; ++d)
+                            op[d] = 0.0f;
+                        continue;
+                    }
+                    double mp = s[j0];
+                    for (int64_t j = j0 + 1; j < j1; ++j)
+                        if (s[j] > mp)
+                            mp = s[j];
+                    double lp = 0.0;
+                    for (int32_t d = 0; d < depth; ++d)
+                        acc[d] = 0.0;
+                    for (int64_t j = j0; j < j1; ++j) {
+                        const double e = exp(s[j] - mp);
+                        const uint16_t* vj = v + ((cu_k[b] + j) * kv_heads + kvh) * depth;
+                        lp += e;
+                        for (int32_t d = 0; d < depth; ++d)
+                            acc[d] += e * rro_bf16_to_double(vj[d]);
+                    }
+                    m[(int64_t)p * rows + row] = (float)mp;
+                    l[(int64_t)p * rows + row] = (float)lp;
+                    for (int32_t d = 0; d < depth; ++d)
+                        op[d] = (float)(acc[d] / lp);
+                }
+            }
+        }
+    }
+    free(s);
+    free(acc);
+    return RRO_OK;
+}

@@ -133,3 +133,20 @@ def attention(seed=SEED_ATTENTION, batch=8, heads=32, kv_heads=32, q_rows=128, k
     k = rng.standard_normal((batch, kv_heads, kv_len, depth), dtype=np.float32)
     v = rng.standard_normal((batch, kv_heads, kv_len, depth), dtype=np.float32)
     return _bf16_bits(q), _bf16_bits(k), _bf16_bits(v)
+
+
+def attention_varlen(seed, q_lens, k_lens, heads, kv_heads, depth, q_lead=0, k_lead=0):
+    """Packed variable-length sequences: bf16 bits of standard normal
+    q [total_q, heads, depth], then k and v [total_k, kv_heads, depth], and the
+    int32 token offsets cu_q, cu_k [batch + 1] of sequences of q_lens[b]
+    queries and k_lens[b] keys, laid out one after another from token q_lead
+    (k_lead) on; the lead tokens belong to no sequence."""
+    q_lens = np.asarray(q_lens, dtype=np.int64)
+    k_lens = np.asarray(k_lens, dtype=np.int64)
+    cu_q = (q_lead + np.concatenate([[0], np.cumsum(q_lens)])).astype(np.int32)
+    cu_k = (k_lead + np.concatenate([[0], np.cumsum(k_lens)])).astype(np.int32)
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((int(cu_q[-1]), heads, depth), dtype=np.float32)
+    k = rng.standard_normal((int(cu_k[-1]), kv_heads, depth), dtype=np.float32)
+    v = rng.standard_normal((int(cu_k[-1]), kv_heads, depth), dtype=np.float32)
+    return _bf16_bits(q), _bf16_bits(k), _bf16_bits(v), cu_q, cu_k

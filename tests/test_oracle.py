@@ -691,3 +691,87 @@ def test_attention_partials_max_at_the_first_or_last_key_of_a_partition():
             assert np.all(s[:, j] == s[:, j0:j1].max(1))
             assert np.array_equal(m[p], s[:, j].astype(np.float32))
             assert np.all(l[p] >= 1.0)
+
+
+# ------------------------------------------------ ragged (varlen) attention
+
+def _dense_of_sequence(q, k, v, cu_q, cu_k, b):
+    """Sequence b of packed [tokens, heads, depth] tensors as the dense
+    [1, heads, rows, depth] layout of rro_attention_partials."""
+    qs = np.ascontiguousarray(q[cu_q[b]:cu_q[b + 1]].transpose(1, 0, 2)[None])
+    ks = np.ascontiguousarray(k[cu_k[b]:cu_k[b + 1]].transpose(1, 0, 2)[None])
+    vs = np.ascontiguousarray(v[cu_k[b]:cu_k[b + 1]].transpose(1, 0, 2)[None])
+    return qs, ks, vs
+
+
+def test_attention_varlen_equals_the_dense_oracle_per_sequence():
+    # ragged placement: every sequence's partial rows, at (token, head), are
+    # bit for bit what the dense oracle gives for that sequence alone; lead
+    # tokens of no sequence are left alone; zero-length sequences of queries
+    # or keys included
+    q_lens, k_lens = [5, 0, 17, 1, 9, 4], [33, 12, 0, 7, 1, 64]
+    heads, kvh, depth, P = 4, 2, 16, 3
+    q, k, v, cu_q, cu_k = synth.attention_varlen(811, q_lens, k_lens, heads, kvh, depth,
+                                                 q_lead=2, k_lead=3)
+    o, m, l = oracle.attention_partials_varlen(q, k, v, cu_q, cu_k, P, 0.3)
+    total_q = q.shape[0]
+    o4 = o.reshape(P, total_q, heads, depth)
+    m3, l3 = m.reshape(P, total_q, heads), l.reshape(P, total_q, heads)
+    for b in range(len(q_lens)):
+        t0, t1 = cu_q[b], cu_q[b + 1]
+        if t1 == t0:
+            continue
+        qs, ks, vs = _dense_of_sequence(q, k, v, cu_q, cu_k, b)
+        od, md, ld = oracle.attention_partials(qs, ks, vs, P, 0.3)
+        n = t1 - t0
+        assert np.array_equal(o4[:, t0:t1].transpose(0, 2, 1, 3).reshape(P, heads * n, depth), od)
+        assert np.array_equal(m3[:, t0:t1].transpose(0, 2, 1).reshape(P, heads * n), md)
+        assert np.array_equal(l3[:, t0:t1].transpose(0, 2, 1).reshape(P, heads * n), ld)
+        if k_lens[b] == 0:                 # no keys: every partition empty
+            assert np.all(m3[:, t0:t1] == -np.inf) and np.all(l3[:, t0:t1] == 0)
+            assert np.all(o4[:, t0:t1] == 0)
+    assert np.all(np.isnan(o4[:, :2])) and np.all(np.isnan(m3[:, :2]))
+
+
+def test_attention_varlen_sequences_do_not_see_each_other():
+    # changing one sequence's keys and values changes that sequence's rows only
+    q_lens, k_lens = [6, 3, 8], [20, 9, 30]
+    q, k, v, cu_q, cu_k = synth.attention_varlen(812, q_lens, k_lens, 2, 2, 8)
+    a = oracle.attention_partials_varlen(q, k, v, cu_q, cu_k, 2, 1.0)
+    k2, v2 = k.copy(), v.copy()
+    k2[cu_k[1]:cu_k[2]] ^= np.uint16(0x0040)
+    v2[cu_k[1]:cu_k[2]] ^= np.uint16(0x0040)
+    bb = oracle.attention_partials_varlen(q, k2, v2, cu_q, cu_k, 2, 1.0)
+    rows_b = np.zeros(q.shape[0] * 2, dtype=bool)
+    rows_b[cu_q[1] * 2:cu_q[2] * 2] = True
+    for x, y in zip(a, bb):
+        assert np.array_equal(x[:, ~rows_b], y[:, ~rows_b])
+        assert not np.array_equal(x[:, rows_b], y[:, rows_b])
+
+
+def test_attention_varlen_merge_is_attention_per_sequence():
+    # closed form per sequence: the merge of the ragged partials (rows
+    # t * heads + h) is softmax attention over that sequence's keys
+    q_lens, k_lens = [7, 2, 11], [40, 3, 90]
+    heads, kvh, depth = 4, 1, 32
+    q, k, v, cu_q, cu_k = synth.attention_varlen(813, q_lens, k_lens, heads, kvh, depth)
+    scale = 1.0 / math.sqrt(depth)
+    for P in (1, 4, 7):
+        o, m, l = oracle.attention_partials_varlen(q, k, v, cu_q, cu_k, P, scale)
+        got = oracle.splitk_lse_merge(o, m, l, 1.0, "f32").reshape(-1, heads, depth)
+        for b in range(3):
+            qs, ks, vs = _dense_of_sequence(q, k, v, cu_q, cu_k, b)
+            _, full = _attn_reference(qs, ks, vs, scale)
+            want = full[0].numpy().transpose(1, 0, 2)     # [tokens, heads, depth]
+            have = got[cu_q[b]:cu_q[b + 1]]
+            assert np.max(np.abs(have - want)) <= 2e-6 * max(1.0, np.abs(want).max()), (P, b)
+
+
+def test_attention_varlen_rejects_bad_offsets():
+    q, k, v, cu_q, cu_k = synth.attention_varlen(814, [3, 2], [4, 4], 2, 2, 8)
+    with pytest.raises(ValueError):
+        oracle.attention_partials_varlen(q, k, v, cu_q[::-1].copy(), cu_k, 2, 1.0)
+    bad = cu_k.copy()
+    bad[-1] = k.shape[0] + 1
+    with pytest.raises(ValueError):
+        oracle.attention_partials_varlen(q, k, v, cu_q, bad, 2, 1.0)
