@@ -182,13 +182,14 @@ __device__ __forceinline__ void po_load(const float* __restrict__ o, int64_t row
         dst.c[k] = load_o<4>(o + ((int64_t)p * rows + rk[k]) * depth + d);
 }
 
-template <int K>
+// The coefficient of (row q, partition p) is cell[p * RW + q].
+template <int K, int RW>
 __device__ __forceinline__ void po_fold(double (*acc)[4], const Chunks<K>& ch, const double* cell,
-                                        const int* qk, int32_t P, int32_t p)
+                                        const int* qk, int32_t p)
 {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        merge_accumulate<4>(acc[k], cell[qk[k] * P + p], ch.c[k].v);
+        merge_accumulate<4>(acc[k], cell[p * RW + qk[k]], ch.c[k].v);
     }
 }
 
@@ -220,9 +221,12 @@ __global__ __launch_bounds__(kBlockThreads) void k_lse_merge_po(const float* __r
             const int64_t r = row_base + qk[k];
             rk[k] = r < rows ? r : rows - 1;
         }
-        // statistics of this thread's first pair, then partition 0's chunks
+        // Statistics of this thread's first pair, then partition 0's chunks.
+        // Pairs are partition-major, cell i = p * RW + q (row fastest): a
+        // wavefront reads whole 128-byte lines of m and l (32 rows of one
+        // partition), and consecutive lanes touch consecutive LDS cells.
         const int32_t i0 = (int32_t)threadIdx.x < npairs ? (int32_t)threadIdx.x : npairs - 1;
-        const int32_t q0 = i0 / P, p0i = i0 - q0 * P;
+        const int32_t p0i = i0 / RW, q0 = i0 - p0i * RW;
         const int64_t r0 = row_base + q0 < rows ? row_base + q0 : rows - 1;
         const float m0 = m[(int64_t)p0i * rows + r0];
         const float l0 = l[(int64_t)p0i * rows + r0];
@@ -234,7 +238,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_lse_merge_po(const float* __r
         // Phase 1: stage (m_p, l_p) (cells past npairs are never read).
         stat[threadIdx.x] = make_float2(st0_ok ? m0 : -__builtin_inff(), st0_ok ? l0 : 0.0f);
         for (int32_t i = threadIdx.x + kBlockThreads; i < npairs; i += kBlockThreads) {
-            const int32_t qq = i / P, p = i - qq * P;
+            const int32_t p = i / RW, qq = i - p * RW;
             float2 st = make_float2(-__builtin_inff(), 0.0f);
             if (row_base + qq < rows)
                 st = make_float2(m[(int64_t)p * rows + row_base + qq],
@@ -244,15 +248,15 @@ __global__ __launch_bounds__(kBlockThreads) void k_lse_merge_po(const float* __r
         __syncthreads();
         // Phase 2: M over the non-empty partitions of the row, then w_p.
         for (int32_t i = threadIdx.x; i < npairs; i += kBlockThreads) {
-            const int32_t qq = i / P;
-            const double M = merge_row_max(stat + (int64_t)qq * P, P);
+            const int32_t qq = i % RW;
+            const double M = merge_row_max(stat + qq, P, RW);
             wd[i] = merge_weight(stat[i], M, scale);
         }
         __syncthreads();
         // Phase 3: W in ascending partition order, then c_p (or -1 if empty).
         for (int32_t i = threadIdx.x; i < npairs; i += kBlockThreads) {
-            const int32_t qq = i / P;
-            const double W = merge_total(wd + (int64_t)qq * P, P);
+            const int32_t qq = i % RW;
+            const double W = merge_total(wd + qq, P, RW);
             cell[i] = merge_coef(stat[i], wd[i], W);
         }
         __syncthreads();
@@ -267,12 +271,12 @@ __global__ __launch_bounds__(kBlockThreads) void k_lse_merge_po(const float* __r
         for (int32_t p = 0;;) {
             const int32_t pn = p + 1 < P ? p + 1 : p;
             po_load<LPR, K>(o, rows, depth, pn, rk, B);
-            po_fold<K>(acc, A, cell, qk, P, p);
+            po_fold<K, RW>(acc, A, cell, qk, p);
             if (++p >= P)
                 break;
             const int32_t pn2 = p + 1 < P ? p + 1 : p;
             po_load<LPR, K>(o, rows, depth, pn2, rk, A);
-            po_fold<K>(acc, B, cell, qk, P, p);
+            po_fold<K, RW>(acc, B, cell, qk, p);
             if (++p >= P)
                 break;
         }

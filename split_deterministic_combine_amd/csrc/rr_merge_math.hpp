@@ -23,14 +23,14 @@ __device__ __forceinline__ bool merge_live(float2 st)
     return st.y > 0.0f && st.x > -__builtin_inff();
 }
 
-// M over a row's P statistics (m_p, l_p); 0 when no partition is live (then
-// no weight uses it).
-__device__ __forceinline__ double merge_row_max(const float2* rs, int32_t P)
+// M over a row's P statistics (m_p, l_p), `stride` cells apart; 0 when no
+// partition is live (then no weight uses it).
+__device__ __forceinline__ double merge_row_max(const float2* rs, int32_t P, int32_t stride = 1)
 {
     bool any = false;
     double M = 0.0;
     for (int32_t p = 0; p < P; ++p) {
-        const float2 s = rs[p];
+        const float2 s = rs[(int64_t)p * stride];
         if (merge_live(s)) {
             if (!any || (double)s.x > M)
                 M = (double)s.x;
@@ -45,12 +45,13 @@ __device__ __forceinline__ double merge_weight(float2 st, double M, float scale)
     return merge_live(st) ? exp((double)scale * ((double)st.x - M)) * (double)st.y : 0.0;
 }
 
-// W: the row's P weights added in ascending partition order.
-__device__ __forceinline__ double merge_total(const double* wrow, int32_t P)
+// W: the row's P weights (`stride` cells apart) added in ascending partition
+// order.
+__device__ __forceinline__ double merge_total(const double* wrow, int32_t P, int32_t stride = 1)
 {
     double W = 0.0;
     for (int32_t p = 0; p < P; ++p)
-        W += wrow[p];
+        W += wrow[(int64_t)p * stride];
     return W;
 }
 
