@@ -455,6 +455,50 @@ rr_status rr_splitk_attention_partials(const void* q, const void* k, const void*
                                        int32_t depth, int32_t P, float scale, void* stream);
 
 /*
+ * rr_splitk_attention_partials_varlen -- the partials of
+ * rr_splitk_attention_partials for a batch of sequences of different lengths
+ * packed token after token, each attending only to its own keys.
+ * "fa4_splitk_reduce_scatter_write", signature and semantics: each output
+ * tile is placed by a head index and a row index into a ragged [tokens]
+ * [heads][depth] tensor, its row count cut to the sequence's length.
+ *
+ *   q             device, bf16 [total_q][heads][depth]
+ *   k, v          device, bf16 [total_k][kv_heads][depth] (grouped heads as
+ *                 rr_splitk_attention_partials)
+ *   cu_seqlens_q  device, int32 [batch + 1], non-decreasing: sequence b owns
+ *                 query tokens cu_seqlens_q[b] .. cu_seqlens_q[b+1] - 1
+ *   cu_seqlens_k  device, int32 [batch + 1]: its keys cu_seqlens_k[b] ..
+ *                 cu_seqlens_k[b+1] - 1.  Offsets are clamped into
+ *                 [0, total_q] and [0, total_k] (a decreasing pair gives an
+ *                 empty sequence); a sequence may have no query or no key.
+ *   o_part        device, float32 [P][total_q][heads][depth] (written)
+ *   m_part, l_part  device, float32 [P][total_q][heads] (written)
+ *   max_q_rows    at least the longest sequence's query count: query rows
+ *                 of a sequence past max_q_rows are not computed
+ *   depth, P, scale  as rr_splitk_attention_partials;
+ *                 heads * depth * 512 < 2^31;  total_q, total_k < 2^31
+ * For sequence b its keys are cut into P contiguous partitions as
+ * rr_splitk_attention_partials cuts kv_len keys (partition p holds keys
+ * p*n_b/P .. (p+1)*n_b/P - 1 of the sequence's n_b keys), and every
+ * (token, head, partition) of the sequence gets m, l and O as there; a
+ * partition with no key is written as m = -inf, l = 0, O = 0.  Tokens that
+ * belong to no sequence are not written.  The rows of o_part, m_part and
+ * l_part, (token, head) in token order, are the rows of rr_splitk_lse_merge
+ * with rows = total_q * heads, which then writes the output as [total_q]
+ * [heads][depth].  The cu_seqlens arrays are read on the device only.
+ * q, k, v and o_part must be 16-byte aligned.
+ * Errors (nothing launched): RR_ERR_SHAPE, RR_ERR_NULL; batch, total_q or
+ * max_q_rows == 0 is a no-op.
+ */
+rr_status rr_splitk_attention_partials_varlen(const void* q, const void* k, const void* v,
+                                              const int32_t* cu_seqlens_q,
+                                              const int32_t* cu_seqlens_k, float* o_part,
+                                              float* m_part, float* l_part, int64_t batch,
+                                              int64_t heads, int64_t kv_heads, int64_t total_q,
+                                              int64_t total_k, int64_t max_q_rows, int32_t depth,
+                                              int32_t P, float scale, void* stream);
+
+/*
  * rr_splitk_attention -- the whole split-K attention in one launch: the
  * partials of rr_splitk_attention_partials, combined as rr_splitk_lse_merge
  * combines them (scale 1.0), into one output row per query row.

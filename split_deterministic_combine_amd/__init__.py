@@ -20,6 +20,9 @@ Operations (names as in the C ABI):
   splitk_attention_partials
                      the producer of those partials (attention over each of P
                      partitions of the keys, on the matrix cores)
+  splitk_attention_partials_varlen
+                     the same for sequences of different lengths packed token
+                     after token, partials placed by (token, head)
   splitk_attention   both in one launch, the partials folded in partition
                      order by the last workgroup of each query tile
 """
@@ -32,7 +35,8 @@ import torch
 
 __all__ = [
     "RRError", "reduce_rows", "reduce_rows_noalloc", "reduce_rows_multi", "reduce_axis", "plan_axis", "softmax_rows", "layernorm_rows", "splitk_lse_merge",
-    "splitk_attention_partials", "splitk_attention", "splitk_attention_workspace_bytes",
+    "splitk_attention_partials", "splitk_attention_partials_varlen", "splitk_attention",
+    "splitk_attention_workspace_bytes",
     "plan_reduce", "plan_softmax", "plan_layernorm", "select_tier", "workspace_bytes", "workspace_reset", "device_cu_count",
     "version", "lib_path", "TIERS", "OPS",
 ]
@@ -95,6 +99,9 @@ def _load():
         lib.rr_splitk_lse_merge.argtypes = [vp, vp, vp, vp, i32, i64, i32, ctypes.c_float, st, vp]
         lib.rr_splitk_attention_partials.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                                      i64, i32, i32, ctypes.c_float, vp]
+        lib.rr_splitk_attention_partials_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64,
+                                                            i64, i64, i64, i64, i64, i32, i32,
+                                                            ctypes.c_float, vp]
         lib.rr_splitk_attention.argtypes = [vp, vp, vp, vp, st, i64, i64, i64, i64, i64, i32, i32,
                                             ctypes.c_float, vp, ctypes.c_size_t, vp]
         lib.rr_splitk_attention_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32, i32,
@@ -122,7 +129,8 @@ def _load():
                      "rr_plan_softmax", "rr_layernorm_rows", "rr_plan_layernorm",
                      "rr_workspace_bytes", "rr_select_tier",
                      "rr_workspace_reset", "rr_device_cu_count", "rr_test_stream",
-                     "rr_splitk_attention_partials", "rr_splitk_attention",
+                     "rr_splitk_attention_partials", "rr_splitk_attention_partials_varlen",
+                     "rr_splitk_attention",
                      "rr_splitk_attention_workspace_bytes"):
             getattr(lib, name).restype = st
         _lib = lib
@@ -537,6 +545,59 @@ def splitk_attention_partials(q, k, v, P, scale=None, out=None):
             ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(o.data_ptr()),
             ctypes.c_void_p(m.data_ptr()), ctypes.c_void_p(l.data_ptr()), batch, heads, kv_heads,
             q_rows, kv_len, depth, int(P), float(scale), _stream_ptr(q.device)))
+    return o, m, l
+
+
+def splitk_attention_partials_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_q_rows, P,
+                                     scale=None, out=None):
+    """Split-K attention partials of sequences packed token after token: q bf16
+    [total_q, heads, depth], k and v bf16 [total_k, kv_heads, depth], and int32
+    GPU offsets cu_seqlens_q, cu_seqlens_k [batch + 1] (sequence b owns tokens
+    cu[b] .. cu[b+1] - 1 of each).  ``max_q_rows`` is at least the longest
+    sequence's query count (read by the host as given; the offsets stay on
+    the device).
+
+    Returns (o_part [P, total_q, heads, depth], m_part [P, total_q, heads],
+    l_part [P, total_q, heads]) in float32; tokens outside every sequence are
+    not written.  splitk_lse_merge takes them as rows = total_q * heads.
+    """
+    lib = _load()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.bfloat16:
+            raise ValueError("%s must be a bfloat16 GPU tensor" % n)
+        if not t.is_contiguous() or t.dim() != 3:
+            raise ValueError("%s must be a contiguous 3-d tensor" % n)
+    for t, n in ((k, "k"), (v, "v"), (cu_seqlens_q, "cu_seqlens_q"),
+                 (cu_seqlens_k, "cu_seqlens_k")):
+        _same_gpu(t, q.device, n)
+    total_q, heads, depth = q.shape
+    total_k, kv_heads, kd = k.shape
+    if kd != depth or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [total_k, kv_heads, depth] matching q")
+    for t, n in ((cu_seqlens_q, "cu_seqlens_q"), (cu_seqlens_k, "cu_seqlens_k")):
+        if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous() or t.numel() < 1:
+            raise ValueError("%s must be a contiguous 1-d int32 tensor of batch + 1 offsets" % n)
+    batch = cu_seqlens_q.numel() - 1
+    if cu_seqlens_k.numel() != batch + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    if scale is None:
+        scale = 1.0 / math.sqrt(depth)
+    shapes = ((P, total_q, heads, depth), (P, total_q, heads), (P, total_q, heads))
+    if out is None:
+        out = tuple(torch.empty(sh, dtype=torch.float32, device=q.device) for sh in shapes)
+    for t, shape in zip(out, shapes):
+        _same_gpu(t, q.device, "out")
+        if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != shape:
+            raise ValueError("outputs must be contiguous float32 %s, %s, %s" % shapes)
+    o, m, l = out
+    with _OnDevice(q.device):
+        _check(lib.rr_splitk_attention_partials_varlen(
+            ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+            ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(cu_seqlens_q.data_ptr()),
+            ctypes.c_void_p(cu_seqlens_k.data_ptr()), ctypes.c_void_p(o.data_ptr()),
+            ctypes.c_void_p(m.data_ptr()), ctypes.c_void_p(l.data_ptr()), batch, heads, kv_heads,
+            total_q, total_k, int(max_q_rows), depth, int(P), float(scale),
+            _stream_ptr(q.device)))
     return o, m, l
 
 

@@ -353,6 +353,41 @@ extern "C" rr_status rr_splitk_attention_partials(const void* q, const void* k, 
     return rr::launch_attention(a);
 }
 
+extern "C" rr_status rr_splitk_attention_partials_varlen(
+    const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+    const int32_t* cu_seqlens_k, float* o_part, float* m_part, float* l_part, int64_t batch,
+    int64_t heads, int64_t kv_heads, int64_t total_q, int64_t total_k, int64_t max_q_rows,
+    int32_t depth, int32_t P, float scale, void* stream)
+{
+    int64_t work = 0;
+    if (total_q < 0 || total_k < 0 || total_q > INT32_MAX || total_k > INT32_MAX)
+        return RR_ERR_SHAPE;
+    rr_status st = check_attention(batch, heads, kv_heads, max_q_rows, total_k, depth, P, scale,
+                                   &work);
+    if (st != RR_OK) return st;
+    // byte ranges of one tile's rows inside the kernel stay below 2^31: the
+    // 128 query rows (heads * depth * 2 bytes apart) and the 32 output rows
+    // of a wavefront (heads * depth * 4 bytes apart)
+    if (heads > (int64_t)INT32_MAX / ((int64_t)depth * 4 * rr::kAttnRows)) return RR_ERR_SHAPE;
+    if (work == 0 || total_q == 0) return RR_OK;
+    if (!q || !o_part || !m_part || !l_part || !cu_seqlens_q || !cu_seqlens_k ||
+        (total_k > 0 && (!k || !v)))
+        return RR_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o_part, 16))
+        return RR_ERR_SHAPE;
+    rr::AttentionLaunch a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                          static_cast<const uint16_t*>(v), o_part, m_part, l_part, batch, heads,
+                          kv_heads, max_q_rows, total_k, depth, P, scale, nullptr, RR_F32, nullptr,
+                          0, as_stream(stream), cu_seqlens_q, cu_seqlens_k, total_q};
+    if (log_enabled())
+        fprintf(stderr,
+                "rr: rr_splitk_attention_partials_varlen batch=%lld heads=%lld kv_heads=%lld "
+                "total_q=%lld total_k=%lld max_q_rows=%lld depth=%d P=%d workgroups=%lld\n",
+                (long long)batch, (long long)heads, (long long)kv_heads, (long long)total_q,
+                (long long)total_k, (long long)max_q_rows, depth, P, (long long)work);
+    return rr::launch_attention(a);
+}
+
 // Workspace of the fused call: the tickets (one per group = head and 128
 // query rows), padded to 256 bytes, then O_p, m_p and l_p group-major,
 // [group][P][128 rows] (the kernel's fold reads a group's partials from one

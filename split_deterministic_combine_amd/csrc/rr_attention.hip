@@ -140,37 +140,40 @@ __device__ __forceinline__ void wait_stages(int64_t after)
 // Slot i * kBlockThreads + threadIdx.x of a stage holds chunk `pos` of key
 // row `row`; the byte offsets into the stage's keys (with the K and V
 // swizzles) do not depend on the stage, so they are formed once.
+// row_bytes: bytes between consecutive keys of one head in K and V (D * 2
+// for the dense layout, kv_heads * D * 2 for tokens packed with their heads).
 template <int D, int KB>
 struct AttnDmaLane {
     static constexpr int CH = D / 8;                       // 16-byte chunks per row
     static constexpr int OPS = KB * CH / kBlockThreads;    // per tensor per thread
     int koff[OPS], voff[OPS];
-    __device__ AttnDmaLane()
+    __device__ explicit AttnDmaLane(int row_bytes)
     {
 #pragma unroll
         for (int i = 0; i < OPS; ++i) {
             const int slot = i * kBlockThreads + (int)threadIdx.x;
             const int row = slot / CH, pos = slot % CH;
-            koff[i] = row * D * 2 + 16 * (pos ^ (row & (CH - 1)));
-            voff[i] = row * D * 2 + 16 * (pos ^ v_swz<D>(row));
+            koff[i] = row * row_bytes + 16 * (pos ^ (row & (CH - 1)));
+            voff[i] = row * row_bytes + 16 * (pos ^ v_swz<D>(row));
         }
     }
 };
 
-// DMA of one stage: keys [js, js + nvalid) of a head into stage buffer st.
-// In a partial stage (nvalid < KB) rows past nvalid repeat row nvalid - 1
-// (finite values; their scores are masked), so every load stays inside the
-// head's keys.
+// DMA of one stage: keys [js, js + nvalid) of a head into stage buffer st;
+// key j of the head starts kstride elements after key j - 1.  In a partial
+// stage (nvalid < KB) rows past nvalid repeat row nvalid - 1 (finite values;
+// their scores are masked), so every load stays inside the head's keys.
 template <int D, int KB>
 __device__ __forceinline__ void attn_dma_stage(const uint16_t* kh, const uint16_t* vh, int64_t js,
                                                int nvalid, AttnStage<D, KB>* st,
-                                               const AttnDmaLane<D, KB>& dl)
+                                               const AttnDmaLane<D, KB>& dl, int kstride)
 {
     using L = AttnDmaLane<D, KB>;
+    const int span = (nvalid - 1) * kstride * 2 + D * 2;  // bytes from the first key to the end of the last
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(kh + js * D), 0, nvalid * D * 2, kBufferWord3);
+        const_cast<uint16_t*>(kh + js * kstride), 0, span, kBufferWord3);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(vh + js * D), 0, nvalid * D * 2, kBufferWord3);
+        const_cast<uint16_t*>(vh + js * kstride), 0, span, kBufferWord3);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
 #pragma unroll
     for (int i = 0; i < L::OPS; ++i) {
@@ -178,7 +181,7 @@ __device__ __forceinline__ void attn_dma_stage(const uint16_t* kh, const uint16_
         int ko = dl.koff[i], vo = dl.voff[i];
         if (nvalid < KB) {                                   // uniform: the partial stage only
             const int row = (base + lane_id()) / L::CH;
-            const int shift = ((row < nvalid ? row : nvalid - 1) - row) * D * 2;
+            const int shift = ((row < nvalid ? row : nvalid - 1) - row) * kstride * 2;
             ko += shift;
             vo += shift;
         }
@@ -286,13 +289,25 @@ constexpr int attn_workgroups_per_cu()
     return D == 128 ? kAttnWorkgroupsPerCU : kAttnWorkgroupsPerCUOther;
 }
 
-template <int D, int KB, int NS, bool FUSED, class YT>
+// RAGGED: packed variable-length sequences ("fa4_splitk_reduce_scatter_write",
+// signature: the output tile is placed by a head index and a row index into
+// a ragged [tokens][heads][depth] tensor, its row count cut to the
+// sequence).  q is [total_q][heads][D] and k, v [total_k][kv_heads][D];
+// sequence b has tokens cu_q[b] .. cu_q[b+1] - 1 and keys cu_k[b] ..
+// cu_k[b+1] - 1 (offsets clamped into the tensors); q_rows is the longest
+// sequence's query count (q_tiles tiles of it), kv_len the total key count;
+// the partial of (token t, head h) is row t * heads + h of the rows
+// (= total_q * heads) of each partition.  Tiles past a sequence's end exit.
+template <int D, int KB, int NS, bool FUSED, class YT, bool RAGGED = false>
 __global__ __launch_bounds__(kBlockThreads, (attn_workgroups_per_cu<D, FUSED>())) void k_attn_staged(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     float* __restrict__ o, float* __restrict__ m_out, float* __restrict__ l_out, int64_t heads,
     int64_t kv_heads, int64_t q_rows, int64_t kv_len, int32_t P, float scale, int32_t q_tiles,
-    int64_t rows, YT* __restrict__ out, uint32_t* __restrict__ tickets, int32_t skew)
+    int64_t rows, YT* __restrict__ out, uint32_t* __restrict__ tickets, int32_t skew,
+    const int32_t* __restrict__ cu_q = nullptr, const int32_t* __restrict__ cu_k = nullptr,
+    int64_t total_q = 0)
 {
+    static_assert(!(RAGGED && FUSED), "the one-launch fold takes dense query tiles");
     constexpr int NC = D / 16;
     constexpr int NT = D / 32;
     constexpr int CH = D / 8;
@@ -328,13 +343,37 @@ __global__ __launch_bounds__(kBlockThreads, (attn_workgroups_per_cu<D, FUSED>())
     const int64_t bh = b * heads + kvl * group + g;
     const int64_t kvh = b * kv_heads + kvl;
 
+    // The head's query rows: nq of them, row i at partial row prow0 + i * rs
+    // (also its row of q), consecutive rows qs elements apart in q; its keys:
+    // nk of them from kh / vh, kstride elements apart.
+    int64_t nq = q_rows, nk = kv_len, prow0 = bh * q_rows, rs = 1;
+    int qs = D, kstride = D;
+    const uint16_t* kh = k + kvh * kv_len * D;
+    const uint16_t* vh = v + kvh * kv_len * D;
+    if constexpr (RAGGED) {
+        const int64_t hq = kvl * group + g;            // query head within the token
+        const int64_t a0 = min(max((int64_t)cu_q[b], (int64_t)0), total_q);
+        const int64_t a1 = min(max((int64_t)cu_q[b + 1], a0), total_q);
+        const int64_t c0 = min(max((int64_t)cu_k[b], (int64_t)0), kv_len);
+        const int64_t c1 = min(max((int64_t)cu_k[b + 1], c0), kv_len);
+        nq = a1 - a0;
+        nk = c1 - c0;
+        prow0 = a0 * heads + hq;
+        rs = heads;
+        qs = (int)(heads * D);
+        kstride = (int)(kv_heads * D);
+        kh = k + (c0 * kv_heads + kvl) * D;
+        vh = v + (c0 * kv_heads + kvl) * D;
+        if ((int64_t)qt * kAttnRows >= nq)
+            return;                                    // the tile is past the sequence's end
+    }
     const int lane = lane_id();
     const int hf = lane / 32;
     const int wave = threadIdx.x / kWave;
     const int64_t qrow = (int64_t)qt * kAttnRows + wave * 32 + lane % 32;
-    const bool row_ok = qrow < q_rows;
-    const int64_t row = bh * q_rows + qrow;
-    const int64_t j0 = (int64_t)p * kv_len / P, j1 = ((int64_t)p + 1) * kv_len / P;
+    const bool row_ok = qrow < nq;
+    const int64_t row = prow0 + qrow * rs;
+    const int64_t j0 = (int64_t)p * nk / P, j1 = ((int64_t)p + 1) * nk / P;
     float* orow = o + ((int64_t)p * rows + row) * D;
 
     const bool empty = j1 <= j0;   // a partition with no key: (O, m, l) = (0, -inf, 0)
@@ -352,7 +391,7 @@ __global__ __launch_bounds__(kBlockThreads, (attn_workgroups_per_cu<D, FUSED>())
     }
 
     rr_bf16x8 qb[NC];
-    {
+    if constexpr (!RAGGED) {
         const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t*>(q + bh * q_rows * D), 0, (int)(q_rows * D * 2), kBufferWord3);
         const int qoff = (int)(qrow < q_rows ? qrow : q_rows) * D * 2;
@@ -361,12 +400,25 @@ __global__ __launch_bounds__(kBlockThreads, (attn_workgroups_per_cu<D, FUSED>())
             const rr_u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + (16 * c + 8 * hf) * 2, 0, 0);
             qb[c] = as_bf16x8(make_uint4(u.x, u.y, u.z, u.w));
         }
+    } else {
+        // the tile's rows from its first one, qs elements apart; rows past
+        // the sequence read as zero (their results are not stored)
+        const int64_t tr = nq - (int64_t)qt * kAttnRows;     // rows of the tile in the sequence
+        const int tv = (int)(tr < kAttnRows ? tr : kAttnRows);
+        const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(q + (prow0 + (int64_t)qt * kAttnRows * rs) * D), 0,
+            (tv - 1) * qs * 2 + D * 2, kBufferWord3);
+        const int ri = wave * 32 + lane % 32;
+        const int qoff = (ri < tv ? ri : tv) * qs * 2;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const rr_u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + (16 * c + 8 * hf) * 2, 0, 0);
+            qb[c] = as_bf16x8(make_uint4(u.x, u.y, u.z, u.w));
+        }
     }
 
-    const uint16_t* kh = k + kvh * kv_len * D;
-    const uint16_t* vh = v + kvh * kv_len * D;
     const int64_t nstg = ceil_div(j1 - j0, KB);
-    const AttnDmaLane<D, KB> dl;
+    const AttnDmaLane<D, KB> dl(kstride * 2);
     auto nvalid_of = [&](int64_t s_) {
         const int64_t left = j1 - j0 - s_ * KB;
         return (int)(left < KB ? left : KB);
@@ -374,7 +426,8 @@ __global__ __launch_bounds__(kBlockThreads, (attn_workgroups_per_cu<D, FUSED>())
 #pragma unroll
     for (int s_ = 0; s_ < NS - 1; ++s_)
         if (s_ < nstg)
-            attn_dma_stage<D, KB>(kh, vh, j0 + (int64_t)s_ * KB, nvalid_of(s_), RR_ATTN_STAGE(s_), dl);
+            attn_dma_stage<D, KB>(kh, vh, j0 + (int64_t)s_ * KB, nvalid_of(s_), RR_ATTN_STAGE(s_), dl,
+                                  kstride);
 
     rr_f32x16 acc[NT];
 #pragma unroll
@@ -414,7 +467,8 @@ __global__ __launch_bounds__(kBlockThreads, (attn_workgroups_per_cu<D, FUSED>())
         wait_stages<OPS, NS>(after);
         stage_barrier();
         if (st + NS - 1 < nstg)
-            attn_dma_stage<D, KB>(kh, vh, j0 + (st + NS - 1) * KB, nvalid_of(st + NS - 1), F, dl);
+            attn_dma_stage<D, KB>(kh, vh, j0 + (st + NS - 1) * KB, nvalid_of(st + NS - 1), F, dl,
+                                  kstride);
         const int nvalid = nvalid_of(st);
         const char* kb = reinterpret_cast<const char*>(T->k);
         const char* vb = reinterpret_cast<const char*>(T->v);
@@ -547,15 +601,15 @@ __global__ __launch_bounds__(kBlockThreads, (attn_workgroups_per_cu<D, FUSED>())
     // [group][P][kAttnRows] with group = (head, query tile), so that the
     // fold finds a group's P partials in one range of at most 1 MiB.
     const int64_t grp = bh * q_tiles + qt;
-    const int64_t slot0 = FUSED ? (grp * P + p) * kAttnRows : (int64_t)p * rows + bh * q_rows
-                                                                  + (int64_t)qt * kAttnRows;
+    const int64_t slot0 = FUSED ? (grp * P + p) * kAttnRows
+                                : (int64_t)p * rows + prow0 + (int64_t)qt * kAttnRows * rs;
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const float inv = empty ? 0.0f : 1.0f / l_tot;
     if (row_ok && hf == 0) {
         const float mv = empty ? -__builtin_inff() : ascale * m_true;
         const float lv = empty ? 0.0f : l_tot * exp2_hw((m_ref - m_true) * c2);
-        float* mp = m_out + slot0 + (qrow - (int64_t)qt * kAttnRows);
-        float* lp = l_out + slot0 + (qrow - (int64_t)qt * kAttnRows);
+        float* mp = m_out + slot0 + (qrow - (int64_t)qt * kAttnRows) * rs;
+        float* lp = l_out + slot0 + (qrow - (int64_t)qt * kAttnRows) * rs;
         if constexpr (FUSED) {
             __hip_atomic_store(mp, mv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(lp, lv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -583,11 +637,13 @@ __global__ __launch_bounds__(kBlockThreads, (attn_workgroups_per_cu<D, FUSED>())
     char* obase = sb + (wave % kWavesPerStage) * kOWaveBytes;
     float* ow = reinterpret_cast<float*>(obase);
     const int64_t qrow0 = (int64_t)qt * kAttnRows + wave * 32;
-    // the wavefront's 32 rows of O_p; rows past q_rows fall outside the range
-    // and are not written
-    const int64_t wrows = q_rows - qrow0 < 32 ? (q_rows - qrow0 > 0 ? q_rows - qrow0 : 0) : 32;
+    // the wavefront's 32 rows of O_p, rs * D floats apart; rows past the
+    // head's query rows fall outside the range and are not written
+    const int64_t wrows = nq - qrow0 < 32 ? (nq - qrow0 > 0 ? nq - qrow0 : 0) : 32;
+    const int orow_bytes = (int)(rs * D * 4);
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
-        o + (slot0 + wave * 32) * D, 0, (int)(wrows * D * 4), kBufferWord3);
+        o + (slot0 + wave * 32 * rs) * D, 0,
+        wrows > 0 ? (int)((wrows - 1) * orow_bytes + D * 4) : 0, kBufferWord3);
 #pragma unroll
     for (int dt = 0; dt < NT; ++dt) {
 #pragma unroll
@@ -605,8 +661,8 @@ __global__ __launch_bounds__(kBlockThreads, (attn_workgroups_per_cu<D, FUSED>())
                                 __float_as_uint(val.z), __float_as_uint(val.w)};
             // FUSED: device-scope write-through (another workgroup reads it);
             // otherwise a streaming store
-            __builtin_amdgcn_raw_buffer_store_b128(u, ro, (r * D + 32 * dt + 4 * (lane % 8)) * 4, 0,
-                                                   FUSED ? kBufferDeviceScope : kBufferNonTemporal);
+            __builtin_amdgcn_raw_buffer_store_b128(u, ro, r * orow_bytes + (32 * dt + 4 * (lane % 8)) * 4,
+                                                   0, FUSED ? kBufferDeviceScope : kBufferNonTemporal);
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);            // reads done before the next tile overwrites
         __builtin_amdgcn_wave_barrier();
@@ -697,6 +753,26 @@ __global__ __launch_bounds__(kBlockThreads, (attn_workgroups_per_cu<D, FUSED>())
     }
 }
 
+// Packed variable-length sequences: q_tiles tiles of the longest sequence
+// for every (sequence, head, partition); a.kv_len is the total key count.
+static rr_status launch_attn_varlen(const AttentionLaunch& a)
+{
+    const int32_t q_tiles = (int32_t)ceil_div(a.q_rows, kAttnRows);
+    const int64_t nwork = (int64_t)q_tiles * a.P * a.batch * a.heads;
+    const int64_t rows = a.total_q * a.heads;
+    const dim3 grid((unsigned)nwork), block(kBlockThreads);
+    float* none = nullptr;
+    if (a.depth == 128)
+        return launch_kernel(
+            k_attn_staged<128, kAttnStageKeys, attn_stages<128, false>(), false, float, true>, grid,
+            block, 0, a.stream, a.q, a.k, a.v, a.o, a.m, a.l, a.heads, a.kv_heads, a.q_rows,
+            a.kv_len, a.P, a.scale, q_tiles, rows, none, a.tickets, 0, a.cu_q, a.cu_k, a.total_q);
+    return launch_kernel(
+        k_attn_staged<64, kAttnStageKeys, attn_stages<64, false>(), false, float, true>, grid,
+        block, 0, a.stream, a.q, a.k, a.v, a.o, a.m, a.l, a.heads, a.kv_heads, a.q_rows, a.kv_len,
+        a.P, a.scale, q_tiles, rows, none, a.tickets, 0, a.cu_q, a.cu_k, a.total_q);
+}
+
 template <bool FUSED, class YT>
 static rr_status launch_attn(const AttentionLaunch& a, YT* out)
 {
@@ -708,15 +784,17 @@ static rr_status launch_attn(const AttentionLaunch& a, YT* out)
         return launch_kernel(
             k_attn_staged<128, kAttnStageKeys, attn_stages<128, FUSED>(), FUSED, YT>, grid, block, 0,
             a.stream, a.q, a.k, a.v, a.o, a.m, a.l, a.heads, a.kv_heads, a.q_rows, a.kv_len, a.P,
-            a.scale, q_tiles, rows, out, a.tickets, a.skew);
+            a.scale, q_tiles, rows, out, a.tickets, a.skew, nullptr, nullptr, 0);
     return launch_kernel(k_attn_staged<64, kAttnStageKeys, attn_stages<64, FUSED>(), FUSED, YT>,
                          grid, block, 0, a.stream, a.q, a.k, a.v, a.o, a.m, a.l, a.heads,
                          a.kv_heads, a.q_rows, a.kv_len, a.P, a.scale, q_tiles, rows, out,
-                         a.tickets, a.skew);
+                         a.tickets, a.skew, nullptr, nullptr, 0);
 }
 
 rr_status launch_attention(const AttentionLaunch& a)
 {
+    if (a.cu_q)
+        return launch_attn_varlen(a);
     if (!a.out)
         return launch_attn<false, float>(a, nullptr);
     if (a.out_dtype == RR_BF16)

@@ -100,6 +100,12 @@ struct AttentionLaunch {
     uint32_t* tickets;    // fused: one per (head, query tile), zero on entry and on exit
     int skew;             // fused, test hook: partition arrival skew (0 = off)
     hipStream_t stream;
+    // packed variable-length sequences (NULL: the dense layout): q [total_q]
+    // [heads][depth], k, v [kv_len][kv_heads][depth], token offsets of batch
+    // sequences; q_rows is then the longest sequence's query count
+    const int32_t* cu_q = nullptr;
+    const int32_t* cu_k = nullptr;
+    int64_t total_q = 0;
 };
 
 rr_status launch_reduce(const rr_plan& plan, const ReduceLaunch& a);

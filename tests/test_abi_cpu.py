@@ -387,6 +387,35 @@ def test_attention_partials_validate_before_touching_the_device():
     assert call(ptr=None, q_rows=0) == 0           # nothing to do
 
 
+def test_varlen_attention_partials_validate_before_touching_the_device():
+    lib = ctypes.CDLL(rr.lib_path())
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.rr_splitk_attention_partials_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64,
+                                                        i64, i64, i64, i64, i32, i32,
+                                                        ctypes.c_float, vp]
+    f = lib.rr_splitk_attention_partials_varlen
+    ok = dict(batch=3, heads=4, kv_heads=2, total_q=40, total_k=90, max_q=20, depth=128, P=2,
+              scale=0.1)
+
+    def call(ptr=16, cu=16, **kw):
+        a = dict(ok, **kw)
+        return f(ptr, ptr, ptr, cu, cu, ptr, ptr, ptr, a["batch"], a["heads"], a["kv_heads"],
+                 a["total_q"], a["total_k"], a["max_q"], a["depth"], a["P"], a["scale"], None)
+
+    assert call(depth=96) == 2 and call(heads=3) == 2 and call(P=0) == 2
+    assert call(scale=float("nan")) == 2
+    assert call(total_q=-1) == 2 and call(total_k=-1) == 2 and call(max_q=-1) == 2
+    assert call(total_q=1 << 31) == 2 and call(total_k=1 << 31) == 2   # int32 offsets
+    assert call(heads=1 << 15, kv_heads=1) == 2    # 128 query rows' bytes beyond 2^31
+    assert call(heads=1 << 14, kv_heads=1, ptr=None) == 1
+    assert call(batch=1 << 40, heads=1 << 12, kv_heads=1) == 2   # grid beyond 31 bits
+    assert call(ptr=None) == 1 and call(cu=None) == 1
+    assert call(ptr=8) == 2                        # misaligned
+    assert call(ptr=None, cu=None, total_q=0) == 0 # nothing to do
+    assert call(ptr=None, cu=None, batch=0) == 0
+    assert call(ptr=None, cu=None, max_q=0) == 0
+
+
 def test_fused_attention_validates_before_touching_the_device():
     lib = ctypes.CDLL(rr.lib_path())
     vp, i64, i32, st = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int
