@@ -84,13 +84,18 @@ __device__ __forceinline__ float f32_from_order_key(int32_t k)
 }
 
 // Every monoid writes its result with store(out, r, acc); out_t is the
-// output pointer (a tuple of pointers for the tuple monoids below).
+// output pointer (a tuple of pointers for the tuple monoids below).  A
+// single-statistic monoid also names an input whose lift leaves every state
+// as it is (neutral_in), which masked lanes fold instead of selecting their
+// state; the tuple monoids have none.
 // float SUM: double accumulator, one rounding at the end.
 struct SumF32 {
     using in_t = float;
     using acc_t = double;
     using out_t = float*;
     __device__ static acc_t identity() { return 0.0; }
+    // -0 adds nothing to any sum (also to -0)
+    __device__ static float neutral_in() { return -0.0f; }
     __device__ static acc_t lift(float x) { return (double)x; }
     __device__ static acc_t combine(acc_t a, acc_t b) { return a + b; }
     __device__ static float finish(acc_t a) { return (float)a; }
@@ -102,6 +107,8 @@ struct MaxF32 {
     using acc_t = int32_t;
     using out_t = float*;
     __device__ static acc_t identity() { return INT32_MIN; }
+    // the negative NaN of largest payload has the smallest key
+    __device__ static float neutral_in() { return __int_as_float(-1); }
     __device__ static acc_t lift(float x) { return f32_order_key(x); }
     __device__ static acc_t combine(acc_t a, acc_t b) { return a > b ? a : b; }
     __device__ static float finish(acc_t a) { return f32_from_order_key(a); }
@@ -112,6 +119,8 @@ struct MinF32 {
     using acc_t = int32_t;
     using out_t = float*;
     __device__ static acc_t identity() { return INT32_MAX; }
+    // the positive NaN of largest payload has the largest key
+    __device__ static float neutral_in() { return __int_as_float(INT32_MAX); }
     __device__ static acc_t lift(float x) { return f32_order_key(x); }
     __device__ static acc_t combine(acc_t a, acc_t b) { return a < b ? a : b; }
     __device__ static float finish(acc_t a) { return f32_from_order_key(a); }
@@ -123,6 +132,7 @@ struct SumI32 {
     using acc_t = uint32_t;
     using out_t = int32_t*;
     __device__ static acc_t identity() { return 0u; }
+    __device__ static int32_t neutral_in() { return 0; }
     __device__ static acc_t lift(int32_t x) { return (uint32_t)x; }
     __device__ static acc_t combine(acc_t a, acc_t b) { return a + b; }
     __device__ static int32_t finish(acc_t a) { return (int32_t)a; }
@@ -133,6 +143,7 @@ struct MaxI32 {
     using acc_t = int32_t;
     using out_t = int32_t*;
     __device__ static acc_t identity() { return INT32_MIN; }
+    __device__ static int32_t neutral_in() { return INT32_MIN; }
     __device__ static acc_t lift(int32_t x) { return x; }
     __device__ static acc_t combine(acc_t a, acc_t b) { return a > b ? a : b; }
     __device__ static int32_t finish(acc_t a) { return a; }
@@ -143,6 +154,7 @@ struct MinI32 {
     using acc_t = int32_t;
     using out_t = int32_t*;
     __device__ static acc_t identity() { return INT32_MAX; }
+    __device__ static int32_t neutral_in() { return INT32_MAX; }
     __device__ static acc_t lift(int32_t x) { return x; }
     __device__ static acc_t combine(acc_t a, acc_t b) { return a < b ? a : b; }
     __device__ static int32_t finish(acc_t a) { return a; }
@@ -317,6 +329,80 @@ __device__ __forceinline__ typename M::acc_t segment_reduce(typename M::acc_t v)
         return group_reduce_wide<M, S>(v);
 }
 
+// segment_reduce of N independent values, one combine step at a time over
+// all of them, so that the DPP moves of one value fill the wait states of
+// another.  Each value gets exactly the combines segment_reduce gives it.
+template <class M, int S, int N>
+__device__ __forceinline__ void segment_reduce_n(typename M::acc_t (&v)[N])
+{
+    using A = typename M::acc_t;
+    if constexpr (S >= 2) {
+        A t[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) t[i] = dpp<kDppQuadSwap1>(v[i]);
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] = M::combine(v[i], t[i]);
+    }
+    if constexpr (S >= 4) {
+        A t[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) t[i] = dpp<kDppQuadSwap2>(v[i]);
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] = M::combine(v[i], t[i]);
+    }
+    if constexpr (S >= 8) {
+        A t[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) t[i] = dpp<kDppHalfMirror>(v[i]);
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] = M::combine(v[i], t[i]);
+    }
+    if constexpr (S >= 16) {
+        A t[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) t[i] = dpp<kDppMirror>(v[i]);
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] = M::combine(v[i], t[i]);
+    }
+    if constexpr (S > 16) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            // the 16-lane rows folded in ascending order, as group_reduce_wide
+            const A r0 = readlane(v[i], 0), r1 = readlane(v[i], 16);
+            const A r2 = readlane(v[i], 32), r3 = readlane(v[i], 48);
+            if constexpr (S == 64) {
+                v[i] = M::combine(M::combine(M::combine(r0, r1), r2), r3);
+            } else {
+                const A lo = M::combine(r0, r1), hi = M::combine(r2, r3);
+                v[i] = lane_id() < 32 ? lo : hi;
+            }
+        }
+    }
+}
+
+// Whether M names a neutral input (see the monoids above).
+template <class M, class = void>
+struct HasNeutralIn {
+    static constexpr bool value = false;
+};
+template <class M>
+struct HasNeutralIn<M, decltype((void)M::neutral_in())> {
+    static constexpr bool value = true;
+};
+
+// acc combined with x when `on`, else left as it is: through the neutral
+// input where M has one (a 32-bit select before the lift), else by
+// selecting the state.
+template <class M>
+__device__ __forceinline__ typename M::acc_t fold_if(typename M::acc_t acc, typename M::in_t x,
+                                                     bool on)
+{
+    if constexpr (HasNeutralIn<M>::value)
+        return M::combine(acc, M::lift(on ? x : M::neutral_in()));
+    else
+        return on ? M::combine(acc, M::lift(x)) : acc;
+}
+
 // Workgroup combine of NT threads: wave combine, then each wave's lane 0
 // writes its result to an LDS slot and every thread folds the slots in wave
 // order after one barrier, so all threads return identical bits.  The caller
@@ -382,6 +468,27 @@ __device__ __forceinline__ int64_t head_elems(const T* p, int64_t cols)
 {
     const int64_t h = (int64_t)((0u - (uint32_t)(uintptr_t)p) & 15u) / (int64_t)sizeof(T);
     return h < cols ? h : cols;
+}
+
+// One 128-bit load of 4 elements of 4 bytes at any 4-byte aligned address
+// (the chip serves unaligned vector loads; NT: non-temporal).
+typedef uint32_t rr_u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+template <class T, bool NT = false>
+__device__ __forceinline__ Vec<T, 4> load4_unaligned(const T* p)
+{
+    static_assert(sizeof(T) == 4, "4-byte elements");
+    const rr_u32x4_a4* q = reinterpret_cast<const rr_u32x4_a4*>(p);
+    const rr_u32x4_a4 u = NT ? __builtin_nontemporal_load(q) : *q;
+    // the words as plain values first: this compiler reads every element of
+    // an under-aligned vector as element 0 when __builtin_bit_cast takes it
+    // directly
+    const uint32_t w0 = u.x, w1 = u.y, w2 = u.z, w3 = u.w;
+    Vec<T, 4> r;
+    r.v[0] = __builtin_bit_cast(T, w0);
+    r.v[1] = __builtin_bit_cast(T, w1);
+    r.v[2] = __builtin_bit_cast(T, w2);
+    r.v[3] = __builtin_bit_cast(T, w3);
+    return r;
 }
 
 // One 128-bit load of 4 elements of 4 bytes (NT: non-temporal).

@@ -131,51 +131,133 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce_block(
 // past the end read the last row, lanes without a chunk or an element the
 // first ones; those values are masked off), so the wavefront has all of them
 // in flight without branches between.
-// PEEL false: every row starts 16-byte aligned and is whole chunks (no head
-// or tail elements).
-template <class M, int VEC, int S, bool PEEL>
+// PEEL (kPeelNone): every row starts 16-byte aligned and is whole chunks (no
+// head or tail elements).  kPeelQuads, when a segment has two lanes past the
+// body (nb + 2 <= S): lane nb reads the row's first four elements and lane
+// nb + 1 its last four, each in one 128-bit load of the same instruction
+// as the body, and folds the head's h (the tail's tl) of them; with no
+// separate instruction for the head and tail, no memory line of the row is
+// asked for twice.  kPeelElements: the head and tail one element per lane
+// as above, in their own loads.
+//
+// Tasks start at multiples of 4 * 64 / S rows, so with 4-byte elements the
+// row a lane reads in group u of any task sits at the same offset from a
+// 16-byte boundary as row u * 64 / S + (its segment): the lane's column
+// split is worked out once per group before the first task (once in all
+// when 64 / S is a multiple of 4) and reused by every task that has all
+// its rows.  Only the last task of a ragged row count works it out per row.
+enum WavePeel { kPeelNone = 0, kPeelElements = 1, kPeelQuads = 2 };
+
+template <class M, int VEC, int S, int PEEL>
 __global__ __launch_bounds__(kBlockThreads) void k_reduce_wave(
     const typename M::in_t* __restrict__ x, typename M::out_t y, int64_t rows,
     int64_t cols, int64_t ld)
 {
     using T = typename M::in_t;
     using A = typename M::acc_t;
+    static_assert(sizeof(T) == 4, "the wave tier reads 4-byte elements");
     constexpr int RPG = kWave / S;
     constexpr int U = kWaveRowGroups;
-    constexpr int NX = VEC == 4 && PEEL ? (6 + S - 1) / S : 0;  // head / tail elements per lane
+    constexpr int NX = VEC == 4 && PEEL == kPeelElements ? (6 + S - 1) / S : 0;  // per lane
+    constexpr int NXA = NX > 0 ? NX : 1;
+    constexpr int NG = VEC == 4 && PEEL != kPeelNone && RPG % 4 != 0 ? U : 1;  // distinct splits
     const int lane = lane_id();
     const int seg = lane / S;
     const int li = lane % S;
-    const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
-    for (int64_t w = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
-         w * RPG * U < rows; w += nwaves) {
-        const int64_t row0 = w * RPG * U;
+    const int c = (int)cols;  // a wave-tier row has at most 64 * VEC columns
+
+    // The column split of a row starting at p: the lane's body chunk (or
+    // element) offset and which of its VEC values are in the row (all or
+    // none, except for the quads), its head / tail element offsets (0 when
+    // it has none) and whether each is in the row.
+    struct Split {
+        int body;
+        uint32_t on;  // bit i: value i of the lane's chunk is folded
+        int xo[NXA];
+        bool has[NXA];
+    };
+    auto split_of = [&](const T* p) {
+        Split g;
+        if constexpr (VEC == 4) {
+            const int h = PEEL != kPeelNone ? (int)head_elems(p, cols) : 0;
+            const int nbe = (c - h) & ~3;
+            const int nb = nbe / 4;
+            const bool full = li < nb;
+            g.on = full ? 0xFu : 0u;
+            g.body = h + (full ? li * 4 : 0);
+            if constexpr (PEEL == kPeelQuads) {
+                const int tl = c - h - nbe;                  // 0..3 tail elements
+                if (li == nb) {                              // the first four: h of them
+                    g.body = 0;
+                    g.on = (1u << h) - 1u;
+                } else if (li == nb + 1) {                   // the last four: tl of them
+                    g.body = c - 4;
+                    g.on = (0xFu << (4 - tl)) & 0xFu;
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < NXA; ++k) {
+                // head or tail element ex of h + tl = cols - nbe: column ex
+                // of the head, or nbe + ex (= h + nbe + (ex - h)) of the tail
+                const int ex = li + k * S;
+                g.has[k] = NX > 0 && ex < c - nbe;
+                g.xo[k] = g.has[k] ? (ex < h ? ex : nbe + ex) : 0;
+            }
+        } else {
+            g.on = li < c ? 1u : 0u;
+            g.body = li < c ? li : 0;
+#pragma unroll
+            for (int k = 0; k < NXA; ++k) {
+                g.has[k] = false;
+                g.xo[k] = 0;
+            }
+        }
+        return g;
+    };
+    Split pre[NG];
+#pragma unroll
+    for (int u = 0; u < NG; ++u) {
+        // row u * RPG + seg's offset from a 16-byte boundary, from integers
+        // (the row need not exist)
+        const uintptr_t a = (uintptr_t)x + (uintptr_t)(((int64_t)u * RPG + seg) * ld) * sizeof(T);
+        pre[u] = split_of(reinterpret_cast<const T*>(a));
+    }
+    // one task: loads of all U groups, then the folds, the combines and the
+    // stores.  WHOLE: every row of the task exists, group u's row is RPG * ld
+    // elements after group u - 1's and its split is pre[u]; otherwise rows
+    // are clamped and each split is worked out from its row.
+    auto task = [&](int64_t row0, auto whole) {
+        constexpr bool WHOLE = decltype(whole)::value;
         Vec<T, VEC> v[U];
-        T xe[U][NX > 0 ? NX : 1];
-        bool full[U], has[U][NX > 0 ? NX : 1];
+        T xe[U][NXA];
+        uint32_t on[U];
+        bool has[U][NXA];
+        const T* base = x + (row0 + seg) * ld;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            int64_t r = row0 + (int64_t)u * RPG + seg;
-            r = r < rows ? r : rows - 1;
-            const T* rp = x + r * ld;
-            if constexpr (VEC == 4) {
-                // 32-bit column arithmetic: a wave-tier row has at most 64 columns
-                const int c = (int)cols;
-                const int h = PEEL ? (int)head_elems(rp, cols) : 0;
-                const int nbe = (c - h) & ~3;
-                full[u] = li * 4 < nbe;
-                v[u] = load4<T, true>(rp + h + (full[u] ? li * 4 : 0));
-#pragma unroll
-                for (int k = 0; k < NX; ++k) {
-                    // head or tail element ex of h + tl = cols - nbe: column ex
-                    // of the head, or nbe + ex (= h + nbe + (ex - h)) of the tail
-                    const int ex = li + k * S;
-                    has[u][k] = ex < c - nbe;
-                    xe[u][k] = rp[has[u][k] ? (ex < h ? ex : nbe + ex) : 0];
-                }
+            const T* rp;
+            Split g;
+            if constexpr (WHOLE) {
+                rp = base + (int64_t)u * RPG * ld;
+                g = pre[NG == 1 ? 0 : u];
             } else {
-                full[u] = li < cols;
-                v[u].v[0] = rp[full[u] ? li : 0];
+                int64_t r = row0 + (int64_t)u * RPG + seg;
+                r = r < rows ? r : rows - 1;
+                rp = x + r * ld;
+                g = split_of(rp);
+            }
+            on[u] = g.on;
+            if constexpr (VEC == 4)
+                v[u] = PEEL == kPeelQuads ? load4_unaligned<T, true>(rp + g.body)
+                                          : load4<T, true>(rp + g.body);
+            else
+                v[u].v[0] = rp[g.body];
+#pragma unroll
+            for (int k = 0; k < NX; ++k) {
+                // non-temporal like the body: a plain load of a line that a
+                // streaming load of the body also asks for costs a refetch
+                has[u][k] = g.has[k];
+                xe[u][k] = __builtin_nontemporal_load(rp + g.xo[k]);
             }
         }
         __builtin_amdgcn_sched_barrier(0);  // every load of the task goes out before any fold
@@ -185,11 +267,12 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce_wave(
             acc[u] = M::identity();
 #pragma unroll
             for (int i = 0; i < VEC; ++i)
-                acc[u] = full[u] ? M::combine(acc[u], M::lift(v[u].v[i])) : acc[u];
+                acc[u] = fold_if<M>(acc[u], v[u].v[i], (on[u] >> i) & 1u);
 #pragma unroll
             for (int k = 0; k < NX; ++k)
-                acc[u] = has[u][k] ? M::combine(acc[u], M::lift(xe[u][k])) : acc[u];
+                acc[u] = fold_if<M>(acc[u], xe[u][k], has[u][k]);
         }
+        segment_reduce_n<M, S, U>(acc);
         // Every lane of a segment holds the row's result after the combine,
         // so all of them store it (the same bits to one address), and rows
         // past the end store their clamped row's result -- the last row's,
@@ -198,10 +281,19 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce_wave(
         // before the next group's fold also hold for a load it does not need.
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            A t = segment_reduce<M, S>(acc[u]);
             const int64_t r = row0 + (int64_t)u * RPG + seg;
-            M::store(y, r < rows ? r : rows - 1, t);
+            M::store(y, WHOLE || r < rows ? r : rows - 1, acc[u]);
         }
+    };
+
+    const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
+    for (int64_t w = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+         w * RPG * U < rows; w += nwaves) {
+        const int64_t row0 = w * RPG * U;
+        if (row0 + RPG * U <= rows)  // wave-uniform: every row of the task exists
+            task(row0, std::true_type{});
+        else
+            task(row0, std::false_type{});
     }
 }
 
@@ -461,6 +553,23 @@ static typename M::out_t outputs_of(const ReduceLaunch& a)
     }
 }
 
+// The wave tier with S lanes per row: 128-bit chunks for rows of at least
+// 7 elements (as the plan's lanes); head and tail elements unless every row
+// is aligned whole chunks, as quads when two lanes of every segment are
+// past the body (a body has at most cols / 4 chunks).
+template <class M, int S>
+static rr_status launch_wave(dim3 grid, dim3 block, hipStream_t s, const typename M::in_t* x,
+                             typename M::out_t y, const ReduceLaunch& a)
+{
+    if (!(a.vec && a.cols >= 7))
+        return launch_kernel(k_reduce_wave<M, 1, S, kPeelNone>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld);
+    if (a.rows16 && a.cols % 4 == 0)
+        return launch_kernel(k_reduce_wave<M, 4, S, kPeelNone>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld);
+    if (a.cols / 4 + 2 <= S)
+        return launch_kernel(k_reduce_wave<M, 4, S, kPeelQuads>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld);
+    return launch_kernel(k_reduce_wave<M, 4, S, kPeelElements>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld);
+}
+
 template <class M>
 static rr_status launch_monoid(const rr_plan& p, const ReduceLaunch& a)
 {
@@ -475,28 +584,13 @@ static rr_status launch_monoid(const rr_plan& p, const ReduceLaunch& a)
         return !a.vec ? launch_kernel(k_reduce_block<M, 1, false>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld)
                : a.rows16 ? launch_kernel(k_reduce_block<M, 4, false>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld)
                           : launch_kernel(k_reduce_block<M, 4, true>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld);
-    case RR_TIER_WAVE: {
-        // 128-bit chunks for rows of at least 7 elements (as the plan's
-        // lanes); head and tail elements unless every row is aligned whole chunks
-        const bool v4 = a.vec && a.cols >= 7;
-        const bool peel = !(a.rows16 && a.cols % 4 == 0);
+    case RR_TIER_WAVE:
         switch (p.lanes_per_row) {
-        case 4:
-            return !v4 ? launch_kernel(k_reduce_wave<M, 1, 4, false>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld)
-                   : peel ? launch_kernel(k_reduce_wave<M, 4, 4, true>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld)
-                          : launch_kernel(k_reduce_wave<M, 4, 4, false>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld);
-        case 16:
-            return !v4 ? launch_kernel(k_reduce_wave<M, 1, 16, false>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld)
-                   : peel ? launch_kernel(k_reduce_wave<M, 4, 16, true>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld)
-                          : launch_kernel(k_reduce_wave<M, 4, 16, false>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld);
-        case 64:
-            return !v4 ? launch_kernel(k_reduce_wave<M, 1, 64, false>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld)
-                   : peel ? launch_kernel(k_reduce_wave<M, 4, 64, true>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld)
-                          : launch_kernel(k_reduce_wave<M, 4, 64, false>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld);
-        default:
-            return RR_ERR_TIER;
+        case 4: return launch_wave<M, 4>(grid, block, s, x, y, a);
+        case 16: return launch_wave<M, 16>(grid, block, s, x, y, a);
+        case 64: return launch_wave<M, 64>(grid, block, s, x, y, a);
+        default: return RR_ERR_TIER;
         }
-    }
     case RR_TIER_TILED:
         return a.rows16 ? launch_kernel(k_reduce_tiled<M, 4, kTiledRows>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld)
                         : launch_kernel(k_reduce_tiled<M, 1, kTiledRows>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld);

@@ -42,6 +42,12 @@ def _out(rows, cols, dtype, offset, pad):
     (999, 61, ("wave", "block")),
     (777, 5, ("wave", "block", "tiled")),
     (300, 3, ("wave",)),
+    (500, 9, ("wave",)),               # 4 lanes per row, head and tail as quads
+    (400, 11, ("wave",)),
+    (333, 14, ("wave",)),              # 4 lanes: no two lanes past the body
+    (300, 55, ("wave",)),              # 16 lanes per row, quads
+    (200, 59, ("wave",)),
+    (200, 60, ("wave",)),              # 16 lanes: element by element when misaligned
     (64, 1001, ("auto", "block", "splitk")),
     (33, 4099, ("block", "splitk")),
     (5, 70001, ("auto", "block")),
