@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <tuple>
 #include <utility>
 
@@ -28,6 +29,38 @@ rr_status launch_kernel(void (*k)(KArgs...), dim3 grid, dim3 block, size_t lds_b
             return e == hipSuccess ? RR_OK : RR_ERR_HIP;
         },
         held);
+}
+
+// Workgroups of kernel k resident per CU at nt threads (no dynamic LDS).
+// The runtime's answer depends only on the kernel's resources, and asking
+// costs microseconds of host time in front of every launch, so each
+// (kernel, nt) is asked once per process; the table holds a few dozen pairs.
+template <class K>
+rr_status blocks_per_cu(K k, int nt, int* out)
+{
+    struct Entry {
+        const void* fn;
+        int nt, blocks;
+    };
+    static std::mutex mu;
+    static Entry table[64];
+    static int used = 0;
+    const void* fn = reinterpret_cast<const void*>(k);
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        for (int i = 0; i < used; ++i)
+            if (table[i].fn == fn && table[i].nt == nt) {
+                *out = table[i].blocks;
+                return RR_OK;
+            }
+    }
+    int v = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k, nt, 0) != hipSuccess || v < 1)
+        return RR_ERR_HIP;
+    std::lock_guard<std::mutex> lock(mu);
+    if (used < 64) table[used++] = Entry{fn, nt, v};
+    *out = v;
+    return RR_OK;
 }
 
 }  // namespace rr

@@ -822,8 +822,7 @@ static rr_status persistent_grid(K kernel, int nt, const rr_plan& p, const Layer
                                  dim3* grid)
 {
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, nt, 0) != hipSuccess ||
-        per_cu < 1)
+    if (blocks_per_cu(kernel, nt, &per_cu) != RR_OK)
         return RR_ERR_HIP;
     const int64_t cap = (int64_t)per_cu * a.cu;
     *grid = dim3((unsigned)(p.grid < cap ? p.grid : cap));

@@ -290,14 +290,37 @@ constexpr int kBufferWord3 = 0x00020000;
 constexpr int kBufferNonTemporal = 2;  // cache-policy bits of the buffer builtins: nt
 constexpr int kBufferDeviceScope = 16;  // sc1: device-coherent (write-through / L2-bypassing)
 
-template <int NCH, int NT>
+// Which chunk of a row's body slot k of a thread holds.  Unrotated, slot k
+// of thread t holds chunk t + k * NT, so a wavefront's 64 slots of one k are
+// 1 KiB of consecutive chunks.  Rotated by q (the body start's 16-byte index
+// within its 128-byte memory line), slot s holds chunk (s - q) mod NS (NS =
+// NCH * NT slots, a power of two): every wavefront's load or store of one k
+// then covers whole lines from a line boundary, instead of touching nine
+// lines, two of them partly, when rows do not start on a line (16 KiB bf16
+// rows at a 16-byte row phase: 51 against 47 us for the whole softmax).
+// Which chunks a row's sum folds in which thread changes with q; the result
+// is still a function of the row's bytes and address.
+template <int NCH, int NT, bool ROT>
+__device__ __forceinline__ int slot_chunk(int k, int q)
+{
+    constexpr int NS = NCH * NT;
+    static_assert((NS & (NS - 1)) == 0, "a power-of-two slot count");
+    return ROT ? (((int)threadIdx.x + k * NT - q) & (NS - 1)) : (int)threadIdx.x + k * NT;
+}
+__device__ __forceinline__ int line_phase(const void* p)
+{
+    return (int)(((uintptr_t)p >> 4) & 7);
+}
+
+template <int NCH, int NT, bool ROT = false>
 __device__ __forceinline__ void load_row_raw(const void* row, int64_t row_bytes, uint4* raw)
 {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<void*>(row), 0, (int)row_bytes, kBufferWord3);
+    const int q = ROT ? line_phase(row) : 0;
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
-        const int off = ((int)threadIdx.x + k * NT) * 16;
+        const int off = slot_chunk<NCH, NT, ROT>(k, q) * 16;
         const rr_u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kBufferNonTemporal);
         raw[k] = make_uint4(v.x, v.y, v.z, v.w);
     }
@@ -346,9 +369,10 @@ __device__ __forceinline__ void load_row_peeled(const XT* xr, int64_t cols, bool
         const_cast<XT*>(xr), 0, (int)row_bytes, kBufferWord3);
     const int body = (int)(pg.h * (int64_t)sizeof(XT));
     const int body_end = live ? (int)((pg.h + pg.nbe) * (int64_t)sizeof(XT)) : 0;
+    const int q = line_phase(xr + pg.h);
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
-        const int off = ((int)threadIdx.x + k * NT) * 16;
+        const int off = slot_chunk<NCH, NT, true>(k, q) * 16;
         // chunks past the body read as zero (never used): clamp them to an
         // offset past the descriptor's range
         const int o = off + 16 <= body_end - body ? body + off : row_bytes + 16;
@@ -362,6 +386,56 @@ __device__ __forceinline__ void load_row_peeled(const XT* xr, int64_t cols, bool
     else
         e = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, eo, 0, kBufferNonTemporal));
     buf.e = (live && pg.idx >= 0) ? e : -__builtin_inff();
+}
+
+// The stores of one row held as NCH chunks of E values per thread (slot k
+// of thread t: row elements h + slot_chunk(k, q) * E onwards, the layout
+// load_row_peeled reads) plus one head or tail value (element idx, or none
+// when idx < 0), as non-temporal buffer stores: a chunk's E outputs in one
+// 8-, 16- or 32-byte store at whatever 2-byte offset the output row gives
+// them, the extra value in a 16- or 32-bit one.  Chunks past the body
+// (element h + nbe on) and threads without an extra value store at an
+// offset past the descriptor's range, which the hardware drops, so every
+// thread issues the same stores with no branch between them: the waits of
+// persistent_rows then count a fixed number of stores.
+template <class YT, int E, int NCH, int NT, bool ROT>
+__device__ __forceinline__ void store_row_peeled(YT* yr, int64_t cols, int64_t h, int64_t nbe,
+                                                 int64_t idx, const float* v, float ev, int q)
+{
+    constexpr int S = (int)sizeof(YT);
+    const int row_bytes = (int)(cols * S);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(yr, 0, row_bytes, kBufferWord3);
+    const int past = row_bytes + 32;
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+        const int j0 = slot_chunk<NCH, NT, ROT>(k, q) * E;
+        const int o = j0 + E <= nbe ? (int)(h + j0) * S : past;
+        const float* c = v + k * E;
+        if constexpr (S == 2) {
+            if constexpr (E == 8) {
+                const rr_u32x4 u = {pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3]),
+                                    pack_bf16x2(c[4], c[5]), pack_bf16x2(c[6], c[7])};
+                __builtin_amdgcn_raw_buffer_store_b128(u, rs, o, 0, kBufferNonTemporal);
+            } else {
+                static_assert(E == 4, "chunks of 4 or 8 elements");
+                const rr_u32x2 u = {pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3])};
+                __builtin_amdgcn_raw_buffer_store_b64(u, rs, o, 0, kBufferNonTemporal);
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < E; q += 4) {
+                const rr_u32x4 u = {__float_as_uint(c[q]), __float_as_uint(c[q + 1]),
+                                    __float_as_uint(c[q + 2]), __float_as_uint(c[q + 3])};
+                __builtin_amdgcn_raw_buffer_store_b128(u, rs, o + q * 4, 0, kBufferNonTemporal);
+            }
+        }
+    }
+    const int eo = idx >= 0 ? (int)idx * S : past;
+    if constexpr (S == 2)
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f32_to_bf16_bits(ev), rs, eo, 0,
+                                              kBufferNonTemporal);
+    else
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ev), rs, eo, 0, kBufferNonTemporal);
 }
 
 // Persistent rows with a one-row prefetch.  Workgroup b takes rows b, b + step,

@@ -176,7 +176,7 @@ __global__ __launch_bounds__(NT) void k_softmax_block(const XT* __restrict__ x,
 // of whole chunks from its first 16-byte boundary, and one head or tail
 // element per thread (PeelGeom); y's chunks are stored whole when y + h is
 // aligned for them.  Neither: 16-byte aligned rows of whole chunks.
-template <class XT, class YT, int NCH, int NT, bool EXACT, bool PEEL>
+template <class XT, class YT, int NCH, int NT, bool EXACT, bool PEEL, bool ROT>
 __device__ __forceinline__ void softmax_row_from_chunks(const RowBuf<NCH>& buf, const XT* xr,
                                                         YT* yr, int64_t cols, MS* slot)
 {
@@ -188,10 +188,11 @@ __device__ __forceinline__ void softmax_row_from_chunks(const RowBuf<NCH>& buf, 
         nbe = pg.nbe;
         idx = pg.idx;
     }
+    const int q = ROT ? line_phase(xr + h) : 0;  // as the row's loads
     float v[NCH * E];
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
-        const int64_t j0 = ((int64_t)threadIdx.x + (int64_t)k * NT) * E;
+        const int64_t j0 = (int64_t)slot_chunk<NCH, NT, ROT>(k, q) * E;
         if (EXACT || j0 < nbe) {
             unpack_chunk<XT>(buf.c[k], v + k * E);
         } else {
@@ -208,25 +209,18 @@ __device__ __forceinline__ void softmax_row_from_chunks(const RowBuf<NCH>& buf, 
 #pragma unroll
     for (int i = 0; i < NCH * E; ++i)
         v[i] *= sc;
-    const bool yvec = !PEEL || chunk_aligned<YT, E>(yr + h);
+    if constexpr (EXACT) {
 #pragma unroll
-    for (int k = 0; k < NCH; ++k) {
-        const int64_t j0 = ((int64_t)threadIdx.x + (int64_t)k * NT) * E;
-        if (EXACT || j0 < nbe) {
-            if (!PEEL || yvec) {
-                YOut<YT>::template chunk<E>(yr + h + j0, v + k * E);
-            } else {
-#pragma unroll
-                for (int i = 0; i < E; ++i)
-                    YOut<YT>::one(yr + h + j0 + i, v[k * E + i]);
-            }
-        }
+        for (int k = 0; k < NCH; ++k)
+            YOut<YT>::template chunk<E>(yr + (int64_t)slot_chunk<NCH, NT, ROT>(k, q) * E, v + k * E);
+    } else {
+        store_row_peeled<YT, E, NCH, NT, ROT>(yr, cols, h, nbe, idx, v, pe * sc, q);
     }
-    if (PEEL && idx >= 0)
-        YOut<YT>::one(yr + idx, pe * sc);
 }
 
-template <class XT, class YT, int NCH, int NT, bool EXACT, bool PEEL>
+// PEEL rows are always rotated; ROT rotates whole-chunk rows that do not all
+// start on a 128-byte line.
+template <class XT, class YT, int NCH, int NT, bool EXACT, bool PEEL, bool ROT>
 __global__ __launch_bounds__(NT) void k_softmax_rows_pf(const XT* __restrict__ x,
                                                         YT* __restrict__ y, int64_t rows,
                                                         int64_t cols, int64_t ldx, int64_t ldy)
@@ -240,11 +234,13 @@ __global__ __launch_bounds__(NT) void k_softmax_rows_pf(const XT* __restrict__ x
             if constexpr (PEEL)
                 load_row_peeled<XT, NCH, NT>(x + r * ldx, cols, live, buf);
             else
-                load_row_raw<NCH, NT>(x + r * ldx, live ? cols * (int64_t)sizeof(XT) : 0, buf.c);
+                load_row_raw<NCH, NT, ROT>(x + r * ldx, live ? cols * (int64_t)sizeof(XT) : 0,
+                                           buf.c);
         },
         [] {},
         [&](const RowBuf<NCH>& buf, int64_t r, int par) {
-            softmax_row_from_chunks<XT, YT, NCH, NT, EXACT, PEEL>(buf, x + r * ldx, y + r * ldy,
+            softmax_row_from_chunks<XT, YT, NCH, NT, EXACT, PEEL, PEEL || ROT>(buf, x + r * ldx,
+                                                                               y + r * ldy,
                                                                   cols, slot[par]);
         });
 }
@@ -647,14 +643,18 @@ static rr_status launch_pf(const XT* x, YT* y, const rr_plan& p, const SoftmaxLa
 {
     constexpr int E = XIn<XT>::kChunk;
     constexpr int64_t kExactCols = (int64_t)NT * NCH * E;
-    // rows that start 16-byte aligned and end on a chunk need no head or tail
+    // rows that start 16-byte aligned and end on a chunk need no head or tail;
+    // those that also all start on a 128-byte line need no rotation
     const bool whole = a.rows16 && a.cols % E == 0;
-    auto kernel = !whole ? k_softmax_rows_pf<XT, YT, NCH, NT, false, true>
-                  : a.cols == kExactCols ? k_softmax_rows_pf<XT, YT, NCH, NT, true, false>
-                                         : k_softmax_rows_pf<XT, YT, NCH, NT, false, false>;
+    const bool lines = (uintptr_t)a.x % 128 == 0 && (a.ld_x * (int64_t)sizeof(XT)) % 128 == 0;
+    const bool exact = a.cols == kExactCols;
+    auto kernel = !whole ? k_softmax_rows_pf<XT, YT, NCH, NT, false, true, true>
+                  : lines ? (exact ? k_softmax_rows_pf<XT, YT, NCH, NT, true, false, false>
+                                   : k_softmax_rows_pf<XT, YT, NCH, NT, false, false, false>)
+                          : (exact ? k_softmax_rows_pf<XT, YT, NCH, NT, true, false, true>
+                                   : k_softmax_rows_pf<XT, YT, NCH, NT, false, false, true>);
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, NT, 0) != hipSuccess ||
-        per_cu < 1)
+    if (blocks_per_cu(kernel, NT, &per_cu) != RR_OK)
         return RR_ERR_HIP;
     const int64_t cap = (int64_t)per_cu * a.cu;
     const dim3 grid((unsigned)(p.grid < cap ? p.grid : cap));

@@ -108,6 +108,33 @@ def test_softmax_rows_at_any_offset(rows, cols, tiers, xt, yt, xo, yo, pad):
             assert_close_f32(to_host(y), ref, what)
 
 
+@pytest.mark.parametrize("rows,cols,ld,xt", [
+    (300, 8192, 8200, "bf16"),   # whole rows of 1024 chunks, row phase steps by 16 bytes
+    (300, 8184, 8184, "bf16"),   # 1023 chunks a row
+    (257, 2048, 2056, "bf16"),   # 64 threads x 4 chunks
+    (200, 4096, 4100, "f32"),    # f32 chunks of 4
+    (150, 1000, 1000, "f32"),
+])
+@pytest.mark.parametrize("yt", ["bf16", "f32"])
+def test_softmax_whole_chunk_rows_off_line(rows, cols, ld, xt, yt):
+    # rows that start 16-byte aligned but not on a 128-byte line: the
+    # persistent kernel rotates its chunk slots to the lines
+    x = (synth.normal_bf16(rows + ld, (rows, cols)) if xt == "bf16"
+         else synth.normal_f32(rows + ld, (rows, cols), 3.0))
+    g = _placed(x, 0, ld - cols)
+    y = _out(rows, cols, TORCH[yt], 0, ld - cols)
+    rr.softmax_rows(g, TORCH[yt], out=y)
+    ref = oracle.softmax_rows(x, yt)
+    what = "%s->%s %dx%d ld %d" % (xt, yt, rows, cols, ld)
+    if yt == "bf16":
+        assert_bf16_within_1ulp(to_host(y), ref, what)
+    else:
+        assert_close_f32(to_host(y), ref, what)
+    # the padding between rows is never written
+    big = y.as_strided((rows, ld - cols), (ld, 1), cols)
+    assert torch.all(torch.isnan(big.float())), what
+
+
 def test_softmax_odd_stride_rows_persistent_plan_and_repeats():
     x = synth.normal_bf16(92, (2000, 8191))
     g = to_gpu(x)
