@@ -491,6 +491,24 @@ __device__ __forceinline__ Vec<T, 4> load4_unaligned(const T* p)
     return r;
 }
 
+// 16 and 8 bytes from any address with the alignment of the elements they
+// hold (2 or 4 bytes), through the cache: one vector load each.  The words go
+// through plain values first, as in load4_unaligned.
+typedef uint32_t rr_u32x4_a2 __attribute__((ext_vector_type(4), aligned(2)));
+typedef uint32_t rr_u32x2_a2 __attribute__((ext_vector_type(2), aligned(2)));
+__device__ __forceinline__ uint4 load16_any(const void* p)
+{
+    const rr_u32x4_a2 u = *reinterpret_cast<const rr_u32x4_a2*>(p);
+    const uint32_t w0 = u.x, w1 = u.y, w2 = u.z, w3 = u.w;
+    return make_uint4(w0, w1, w2, w3);
+}
+__device__ __forceinline__ uint2 load8_any(const void* p)
+{
+    const rr_u32x2_a2 u = *reinterpret_cast<const rr_u32x2_a2*>(p);
+    const uint32_t w0 = u.x, w1 = u.y;
+    return make_uint2(w0, w1);
+}
+
 // One 128-bit load of 4 elements of 4 bytes (NT: non-temporal).
 template <class T, bool NT = false>
 __device__ __forceinline__ Vec<T, 4> load4(const T* p)

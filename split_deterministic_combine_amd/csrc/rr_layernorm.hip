@@ -65,22 +65,12 @@ __device__ __forceinline__ Weights shifted(const Weights& w, int64_t h)
                    w.dflt};
 }
 
-// Whether a vector's chunks of E columns load whole: 16-byte aligned base
-// (8 bytes for a bf16 chunk of 4), or no vector at all.
-template <int E>
-__device__ __forceinline__ bool weights_aligned(const Weights& w)
-{
-    const uint32_t a = (w.bf16 && E == 4) ? 7u : 15u;
-    return !w.p || ((uint32_t)(uintptr_t)w.p & a) == 0;
-}
-
-// E weights of columns j0 .. j0+E-1 (past `cols`: the default).  With VEC
-// and wvec (the base aligned for chunk loads: weights_aligned) a whole chunk
-// inside the row is loaded with vector loads (cached: every row reads the
-// same weights); else element by element.
+// E weights of columns j0 .. j0+E-1 (past `cols`: the default).  With VEC a
+// whole chunk inside the row is one vector load at whatever element
+// alignment the vector gives it (cached: every row reads the same weights);
+// the rest element by element.
 template <int E, bool VEC>
-__device__ __forceinline__ void load_weights(const Weights& w, int64_t j0, int64_t cols, float* o,
-                                             bool wvec = true)
+__device__ __forceinline__ void load_weights(const Weights& w, int64_t j0, int64_t cols, float* o)
 {
     if (!w.p) {
 #pragma unroll
@@ -89,18 +79,18 @@ __device__ __forceinline__ void load_weights(const Weights& w, int64_t j0, int64
         return;
     }
     if constexpr (VEC) {
-        if (wvec && j0 + E <= cols) {
+        if (j0 + E <= cols) {
             if (w.bf16) {
                 const uint16_t* p = static_cast<const uint16_t*>(w.p) + j0;
                 if constexpr (E == 8) {
-                    const uint4 u = *reinterpret_cast<const uint4*>(p);
+                    const uint4 u = load16_any(p);
                     o[0] = bf16_lo(u.x); o[1] = bf16_hi(u.x);
                     o[2] = bf16_lo(u.y); o[3] = bf16_hi(u.y);
                     o[4] = bf16_lo(u.z); o[5] = bf16_hi(u.z);
                     o[6] = bf16_lo(u.w); o[7] = bf16_hi(u.w);
                 } else {
                     static_assert(E == 4, "chunks of 4 or 8 elements");
-                    const uint2 u = *reinterpret_cast<const uint2*>(p);
+                    const uint2 u = load8_any(p);
                     o[0] = bf16_lo(u.x); o[1] = bf16_hi(u.x);
                     o[2] = bf16_lo(u.y); o[3] = bf16_hi(u.y);
                 }
@@ -108,7 +98,7 @@ __device__ __forceinline__ void load_weights(const Weights& w, int64_t j0, int64
                 const float* p = static_cast<const float*>(w.p) + j0;
 #pragma unroll
                 for (int k = 0; k < E; k += 4) {
-                    const uint4 u = *reinterpret_cast<const uint4*>(p + k);
+                    const uint4 u = load16_any(p + k);
                     o[k] = __uint_as_float(u.x); o[k + 1] = __uint_as_float(u.y);
                     o[k + 2] = __uint_as_float(u.z); o[k + 3] = __uint_as_float(u.w);
                 }
@@ -124,7 +114,7 @@ __device__ __forceinline__ void load_weights(const Weights& w, int64_t j0, int64
 // y = d * rstd * gamma + beta on E values of columns j0.. (in place).
 template <int E, bool VEC>
 __device__ __forceinline__ void affine(float* d, float rstd, const Weights& g, const Weights& b,
-                                       int64_t j0, int64_t cols, bool wvec = true)
+                                       int64_t j0, int64_t cols)
 {
     if (!g.p && !b.p) {
 #pragma unroll
@@ -133,8 +123,8 @@ __device__ __forceinline__ void affine(float* d, float rstd, const Weights& g, c
         return;
     }
     float gw[E], bw[E];
-    load_weights<E, VEC>(g, j0, cols, gw, wvec);
-    load_weights<E, VEC>(b, j0, cols, bw, wvec);
+    load_weights<E, VEC>(g, j0, cols, gw);
+    load_weights<E, VEC>(b, j0, cols, bw);
 #pragma unroll
     for (int i = 0; i < E; ++i)
         d[i] = __builtin_fmaf(d[i] * rstd, gw[i], bw[i]);
@@ -370,7 +360,6 @@ __global__ __launch_bounds__(NT) void k_layernorm_block(
         const int64_t cb = cols - h;
         const Weights gh = shifted(g, h), bh = shifted(b, h);
         const bool yvec = VEC && chunk_aligned<YT, E>(yr);
-        const bool wvec = VEC && weights_aligned<E>(gh) && weights_aligned<E>(bh);
         float v[NCH * E];
 #pragma unroll
         for (int k = 0; k < NCH; ++k)
@@ -387,7 +376,7 @@ __global__ __launch_bounds__(NT) void k_layernorm_block(
 #pragma unroll
         for (int k = 0; k < NCH; ++k) {
             const int64_t j0 = ((int64_t)threadIdx.x + (int64_t)k * NT) * E;
-            affine<E, VEC>(v + k * E, st.rstd, gh, bh, j0, cb, wvec);
+            affine<E, VEC>(v + k * E, st.rstd, gh, bh, j0, cb);
             store_masked_rt<YT, E>(yr, j0, cb, v + k * E, yvec);
         }
         if (has_e)
@@ -418,7 +407,6 @@ __global__ __launch_bounds__(NT) void k_layernorm_stream(
         const int64_t cb = cols - h;
         const Weights gh = shifted(g, h), bh = shifted(b, h);
         const bool yvec = VEC && chunk_aligned<YT, E>(yr);
-        const bool wvec = VEC && weights_aligned<E>(gh) && weights_aligned<E>(bh);
         const bool has_e = (int64_t)threadIdx.x < h;
         const float kf = XIn<XT>::one(xr0);
         const double K = (double)kf;
@@ -454,7 +442,7 @@ __global__ __launch_bounds__(NT) void k_layernorm_stream(
 #pragma unroll
             for (int i = 0; i < E; ++i)
                 v[i] = centre(v[i]);
-            affine<E, VEC>(v, st.rstd, gh, bh, j0, cb, wvec);
+            affine<E, VEC>(v, st.rstd, gh, bh, j0, cb);
             store_masked_rt<YT, E>(yr, j0, cb, v, yvec);
         }
         __syncthreads();  // slot reuse by the next row
@@ -729,7 +717,6 @@ __global__ __launch_bounds__(kBlockThreads) void k_layernorm_splitk_map(
     const int64_t h = VEC ? head_elems(x, cols) : 0;
     const int64_t cb = cols - h;
     const Weights gh = shifted(g, h), bh = shifted(b, h);
-    const bool wvec = VEC && weights_aligned<E>(gh) && weights_aligned<E>(bh);
     // at least one tile, so that the work items of tile 0 also map the head
     // when it is the whole row (a row shorter than its offset to the next
     // 16-byte boundary: the tile itself is then empty)
@@ -765,8 +752,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_layernorm_splitk_map(
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const int64_t j0 = t * kTile + ((int64_t)u * kBlockThreads + threadIdx.x) * E;
-                    load_weights<E, VEC>(gh, j0, cb, gw + u * E, wvec);
-                    load_weights<E, VEC>(bh, j0, cb, bw + u * E, wvec);
+                    load_weights<E, VEC>(gh, j0, cb, gw + u * E);
+                    load_weights<E, VEC>(bh, j0, cb, bw + u * E);
                 }
             }
             if (t < nfull) {
