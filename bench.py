@@ -60,22 +60,29 @@ def kernel_source_hash():
 
 # op name -> substring of the kernel symbol that runs it at the benchmark shapes
 KERNEL_OF_OP = {
-    "short_sum": "k_reduce_wave<rr::SumF32, 4, 16>",
-    "short_max": "k_reduce_wave<rr::MaxF32, 4, 16>",
-    "softmax": "k_softmax_rows_pf<unsigned short, unsigned short, 4, 256, true>",
+    "short_sum": "k_reduce_wave<rr::SumF32, 4, 16, 0>",
+    "short_max": "k_reduce_wave<rr::MaxF32, 4, 16, 0>",
+    "softmax": "k_softmax_rows_pf<unsigned short, unsigned short, 4, 256, true, false, false>",
     "long_sum": "k_reduce_splitk<rr::SumF32, 4>",
     "long_max": "k_reduce_splitk<rr::MaxI32, 4>",
-    "merge": "k_lse_merge_po<unsigned short, 32, 4>",
+    "merge": "k_lse_merge_po<unsigned short, 32, 4, true>",
     "softmax_long_stats": "k_softmax_splitk_stats<unsigned short, true>",
     "softmax_long_map": "k_softmax_splitk_map<unsigned short, unsigned short, true>",
     "layernorm": "k_layernorm_rows_pf<unsigned short, unsigned short, 4, 128, true, true>",
     "multi_long": "k_reduce_splitk<rr::MultiF32, 4>",
     "axis_cols_partial": "k_reduce_axis_partial<rr::SumF32, 4>",
     "axis_cols_fold": "k_reduce_axis_fold<rr::SumF32>",
-    # reference streams of known size (not ops of the step): rr_test_stream
-    "attention": "k_attn_staged<128, 32, 3, false, float>",
-    "attention_fused": "k_attn_staged<128, 32, 3, true, unsigned short>",
+    "attention": "k_attn_staged<128, 32, 3, false, float, false>",
+    "attention_fused": "k_attn_staged<128, 32, 3, true, unsigned short, false>",
+    # rows at every offset from a 16-byte boundary and their aligned neighbour
+    "sum_47": "k_reduce_wave<rr::SumF32, 4, 16, 2>",
+    "sum_1001": "k_reduce_block<rr::SumF32, 4, true>",
+    "sum_1000": "k_reduce_block<rr::SumF32, 4, false>",
+    "softmax_8191": "k_softmax_rows_pf<unsigned short, unsigned short, 4, 256, false, true, true>",
+    # reference streams of known size (not ops of the step): rr_test_stream;
+    # launches of one kernel at two sizes are told apart by their bytes
     "stream_read": "k_stream<0>",
+    "stream_read_128MiB": "k_stream<0>",
     "stream_write": "k_stream<1>",
 }
 LAYERNORM = (16384, 4096)
@@ -137,7 +144,12 @@ def _algo_bytes():
         # one launch: q, k, v read once and the bf16 output written once (the
         # partials pass through the device-coherent level, not counted)
         "attention_fused": _attn_fused_bytes(),
+        "sum_47": 1048576 * 47 * 4 + 1048576 * 4,
+        "sum_1001": 65536 * 1001 * 4 + 65536 * 4,
+        "sum_1000": 65536 * 1000 * 4 + 65536 * 4,
+        "softmax_8191": 8192 * 8191 * 2 * 2,
         "stream_read": 1 << 30,
+        "stream_read_128MiB": 128 << 20,
         "stream_write": 1 << 30,
     }
 
@@ -178,7 +190,6 @@ def _csv_rows(directory, suffix):
 def ingest_counters(trace_dir, fetch_dir, write_dir):
     """Turn rocprofv3 CSVs into profiles/traffic.json and markdown summaries."""
     ALGO_BYTES = _algo_bytes()
-    stats = _csv_rows(trace_dir, "kernel_stats.csv")
     per_counter = {}
     for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         vals = {}
@@ -188,8 +199,11 @@ def ingest_counters(trace_dir, fetch_dir, write_dir):
             vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
         per_counter[name] = vals
 
-    def mean_for(vals, pattern):
-        hits = [v for k, vs in vals.items() if pattern in k for v in vs]
+    def mean_for(vals, pattern, kib_expected=None):
+        # dispatches of the pattern; where one kernel runs at several sizes,
+        # only those within a factor of 2.5 of the op's expected KiB
+        hits = [v for k, vs in vals.items() if pattern in k for v in vs
+                if kib_expected is None or v == 0 or 0.4 * kib_expected <= v <= 2.5 * kib_expected]
         return sum(hits) / len(hits) if hits else None
 
     copy_pat = "neg"  # torch's elementwise negation kernel run by --calibrate-copy
@@ -200,7 +214,10 @@ def ingest_counters(trace_dir, fetch_dir, write_dir):
     write_scale = COPY_BYTES / (1024.0 * max(copy_write)) if copy_write else None
     kernels = {}
     for op, pat in KERNEL_OF_OP.items():
-        f = mean_for(per_counter["FETCH_SIZE"], pat)
+        shared = sum(1 for q in KERNEL_OF_OP.values() if q == pat) > 1
+        exp_kib = ALGO_BYTES[op] / 1024.0 if shared else None
+        f = mean_for(per_counter["FETCH_SIZE"], pat,
+                     exp_kib / fetch_scale if exp_kib and fetch_scale else None)
         w = mean_for(per_counter["WRITE_SIZE"], pat)
         if f is None or w is None or fetch_scale is None or write_scale is None:
             continue
@@ -219,16 +236,26 @@ def ingest_counters(trace_dir, fetch_dir, write_dir):
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
-    lines = ["| kernel (op) | calls | avg us | min us | max us | algorithmic GB/s | % of 8 TB/s |",
-             "|---|---|---|---|---|---|---|"]
+    # durations per dispatch (the trace), so that launches of one kernel at
+    # two sizes are told apart: an op whose kernel also runs another op keeps
+    # the dispatches whose algorithmic rate would lie between 2 and 9 TB/s
+    durs = {}
+    for r in _csv_rows(trace_dir, "kernel_trace.csv"):
+        durs.setdefault(r["Kernel_Name"], []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = ["| kernel (op) | launches | avg us | median us | min us | max us | algorithmic GB/s "
+             "| % of 8 TB/s |", "|---|---|---|---|---|---|---|---|"]
     for op, pat in KERNEL_OF_OP.items():
-        for r in stats:
-            if pat in r.get("Name", ""):
-                avg = float(r["AverageNs"]) / 1e3
-                gbs = ALGO_BYTES[op] / (avg * 1e-6) / 1e9
-                lines.append("| `%s` (%s) | %s | %.1f | %.1f | %.1f | %.0f | %.1f |" % (
-                    pat, op, r["Calls"], avg, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, gbs,
-                    100 * gbs / PEAK_HBM_GBS))
+        shared = sum(1 for q in KERNEL_OF_OP.values() if q == pat) > 1
+        ds = sorted(d for k, v in durs.items() if pat in k for d in v
+                    if d > 0 and (not shared or 2e12 <= ALGO_BYTES[op] / (d * 1e-6) <= 9e12))
+        if not ds:
+            continue
+        avg = sum(ds) / len(ds)
+        gbs = ALGO_BYTES[op] / (avg * 1e-6) / 1e9
+        lines.append("| `%s` (%s) | %d | %.1f | %.1f | %.1f | %.1f | %.0f | %.1f |" % (
+            pat, op, len(ds), avg, ds[len(ds) // 2], ds[0], ds[-1], gbs,
+            100 * gbs / PEAK_HBM_GBS))
     table = "\n".join(lines)
     prof = os.path.dirname(TRAFFIC_FILE)
     with open(os.path.join(prof, "kernels_rowwise_suite.md"), "w") as f:
@@ -238,7 +265,8 @@ def ingest_counters(trace_dir, fetch_dir, write_dir):
                 "-d $R/gpurun_out/prof_trace -o trace -- python3 $R/bench.py\n\n"
                 "with `R` the repository root; summarised by `python bench.py --ingest-counters "
                 "gpurun_out/prof_trace gpurun_out/prof_fetch gpurun_out/prof_write`.\n"
-                "GB/s = algorithmic bytes per launch / average kernel duration.\n\n" + table + "\n")
+                "GB/s = algorithmic bytes per launch / average kernel duration (the "
+                "trace's per-dispatch times).\n\n" + table + "\n")
     tl = ["| op | kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (scaled) | algorithmic bytes | ratio |",
           "|---|---|---|---|---|---|---|"]
     for op, k in kernels.items():

@@ -25,6 +25,7 @@
 #include "rr_launch.hpp"
 #include "rr_launch_util.hpp"
 #include "rr_merge_math.hpp"
+#include "rr_rowio.hpp"
 
 namespace rr {
 
@@ -172,14 +173,35 @@ struct Chunks {
     OChunk<4> c[K];
 };
 
-template <int LPR, int K>
+// Partition p's chunks of the K rows rk.  BUF (a partition of at most 2^31
+// bytes): buffer loads over partition p's range, which is empty when live
+// is false, so a look-ahead past the last partition reads zeros and no
+// memory (a clamped one would read the last partition again); else plain
+// non-temporal loads, the look-ahead clamped by the caller.
+template <int LPR, int K, bool BUF>
 __device__ __forceinline__ void po_load(const float* __restrict__ o, int64_t rows, int32_t depth,
-                                        int32_t p, const int64_t* rk, Chunks<K>& dst)
+                                        int32_t p, const int64_t* rk, Chunks<K>& dst,
+                                        bool live = true)
 {
     const int64_t d = (int64_t)(threadIdx.x % LPR) * 4;
+    if constexpr (BUF) {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(o + (int64_t)p * rows * depth), 0,
+            live ? (int)(rows * depth * 4) : 0, kBufferWord3);
 #pragma unroll
-    for (int k = 0; k < K; ++k)
-        dst.c[k] = load_o<4>(o + ((int64_t)p * rows + rk[k]) * depth + d);
+        for (int k = 0; k < K; ++k) {
+            const rr_u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(
+                rs, (int)((rk[k] * depth + d) * 4), 0, kBufferNonTemporal);
+            dst.c[k].v[0] = __uint_as_float(u.x);
+            dst.c[k].v[1] = __uint_as_float(u.y);
+            dst.c[k].v[2] = __uint_as_float(u.z);
+            dst.c[k].v[3] = __uint_as_float(u.w);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            dst.c[k] = load_o<4>(o + ((int64_t)p * rows + rk[k]) * depth + d);
+    }
 }
 
 // The coefficient of (row q, partition p) is cell[p * RW + q].
@@ -193,7 +215,7 @@ __device__ __forceinline__ void po_fold(double (*acc)[4], const Chunks<K>& ch, c
     }
 }
 
-template <class YT, int LPR, int K>
+template <class YT, int LPR, int K, bool BUF>
 __global__ __launch_bounds__(kBlockThreads) void k_lse_merge_po(const float* __restrict__ o,
                                                                 const float* __restrict__ m,
                                                                 const float* __restrict__ l,
@@ -232,7 +254,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_lse_merge_po(const float* __r
         const float l0 = l[(int64_t)p0i * rows + r0];
         __builtin_amdgcn_sched_barrier(0);
         Chunks<K> A, B;
-        po_load<LPR, K>(o, rows, depth, 0, rk, A);
+        po_load<LPR, K, BUF>(o, rows, depth, 0, rk, A);
         const bool st0_ok = (int32_t)threadIdx.x < npairs && row_base + q0 < rows;
 
         // Phase 1: stage (m_p, l_p) (cells past npairs are never read).
@@ -270,12 +292,12 @@ __global__ __launch_bounds__(kBlockThreads) void k_lse_merge_po(const float* __r
                 acc[k][e] = 0.0;
         for (int32_t p = 0;;) {
             const int32_t pn = p + 1 < P ? p + 1 : p;
-            po_load<LPR, K>(o, rows, depth, pn, rk, B);
+            po_load<LPR, K, BUF>(o, rows, depth, pn, rk, B, p + 1 < P);
             po_fold<K, RW>(acc, A, cell, qk, p);
             if (++p >= P)
                 break;
             const int32_t pn2 = p + 1 < P ? p + 1 : p;
-            po_load<LPR, K>(o, rows, depth, pn2, rk, A);
+            po_load<LPR, K, BUF>(o, rows, depth, pn2, rk, A, p + 1 < P);
             po_fold<K, RW>(acc, B, cell, qk, p);
             if (++p >= P)
                 break;
@@ -307,9 +329,11 @@ static rr_status launch_po(const MergeLaunch& a)
     if (grid > kMaxGrid) grid = kMaxGrid;
     const int64_t npairs = (int64_t)RW * a.P;
     const size_t lds = (size_t)8 * npairs + (size_t)8 * (npairs > kBlockThreads ? npairs : kBlockThreads);
-    return launch_kernel(k_lse_merge_po<YT, LPR, K>, dim3((unsigned)grid), dim3(kBlockThreads), lds,
-                         a.stream, a.o, a.m, a.l, static_cast<YT*>(a.out), a.P, a.rows, a.depth,
-                         a.scale);
+    // buffer loads when one partition's bytes fit a 31-bit offset
+    auto kernel = a.rows * (int64_t)a.depth * 4 <= (int64_t)INT32_MAX ? k_lse_merge_po<YT, LPR, K, true>
+                                                                      : k_lse_merge_po<YT, LPR, K, false>;
+    return launch_kernel(kernel, dim3((unsigned)grid), dim3(kBlockThreads), lds, a.stream, a.o,
+                         a.m, a.l, static_cast<YT*>(a.out), a.P, a.rows, a.depth, a.scale);
 }
 
 static int lanes_per_row(int32_t depth, int ve)

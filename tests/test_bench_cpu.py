@@ -44,9 +44,14 @@ def test_counter_ingest_scales_by_the_calibration_copy(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "prof" / "traffic.json"))
     sym = bench.KERNEL_OF_OP["long_sum"]
     copy = "void at::native::neg_kernel_impl(float)"
-    _write_csv(str(tmp_path / "trace" / "x" / "t_kernel_stats.csv"),
-               [{"Name": "void rr::%s(float const*)" % sym, "Calls": "3", "AverageNs": "152000",
-                 "MinNs": "150000", "MaxNs": "155000"}])
+    # three dispatches of 150, 151 and 155 us, and the reference read at its
+    # two sizes: 1 GiB in 150 us and 128 MiB in 21 us
+    disp = [("void rr::%s(float const*)" % sym, 150000), ("void rr::%s(float const*)" % sym, 151000),
+            ("void rr::%s(float const*)" % sym, 155000), ("void rr::k_stream<0>(x)", 150000),
+            ("void rr::k_stream<0>(x)", 21000)]
+    _write_csv(str(tmp_path / "trace" / "x" / "t_kernel_trace.csv"),
+               [{"Kernel_Name": n, "Start_Timestamp": str(1000 * i),
+                 "End_Timestamp": str(1000 * i + d)} for i, (n, d) in enumerate(disp)])
     half = bench.COPY_BYTES / 1024.0 / 2   # FETCH_SIZE reads half the bytes on this part
     for d, name, k_val, c_val in (("fetch", "FETCH_SIZE", 524288.0, half),
                                   ("write", "WRITE_SIZE", 0.0625, bench.COPY_BYTES / 1024.0)):
@@ -62,7 +67,10 @@ def test_counter_ingest_scales_by_the_calibration_copy(tmp_path, monkeypatch):
     assert k["fetch_bytes"] == 1 << 30 and k["write_bytes"] == 64
     assert k["traffic_over_algorithmic"] == pytest.approx(1.0, abs=1e-3)
     assert out["source_hash"] == bench.kernel_source_hash()
-    assert "152.0" in table
+    assert "| 3 | 152.0 | 151.0 | 150.0 | 155.0 |" in table
+    # one kernel at two sizes: each op keeps its own dispatch
+    assert "(stream_read) | 1 | 150.0 |" in table
+    assert "(stream_read_128MiB) | 1 | 21.0 |" in table
     assert json.load(open(bench.TRAFFIC_FILE))["kernels"]["long_sum"]["bytes_per_launch"] == (1 << 30) + 64
 
 
