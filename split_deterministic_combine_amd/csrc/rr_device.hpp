@@ -563,6 +563,22 @@ __device__ __forceinline__ float f32_round_odd(double a)
     }
     return f;
 }
+// The same bf16 through the plain float rounding, cheaper where most values
+// are not near a bf16 halfway point: the double rounded to the nearest
+// float, which the bf16 store's round to nearest even then takes to the
+// double's correct bf16 -- except where that float lands exactly on a bf16
+// halfway point (low 16 bits 0x8000) without being the double.  The double
+// then lies to one side of the halfway point, and one float ulp toward it
+// makes the store round that way.
+__device__ __forceinline__ float f32_for_bf16(double a)
+{
+    const float f = (float)a;
+    const uint32_t u = __float_as_uint(f);
+    const double fd = (double)f;
+    const uint32_t toward = fabs(a) > fabs(fd) ? u + 1u : u - 1u;
+    return __uint_as_float((u & 0xFFFFu) == 0x8000u && fd != a ? toward : u);
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2_from_double(double a, double b)
 {
     return pack_bf16x2(f32_round_odd(a), f32_round_odd(b));

@@ -44,7 +44,7 @@ struct Weights {
 // Row statistics from the two reduced states.
 struct LnRow {
     double mean;
-    float rstd;
+    double rstd;
 };
 
 namespace {
@@ -111,29 +111,71 @@ __device__ __forceinline__ void load_weights(const Weights& w, int64_t j0, int64
         o[i] = j0 + i < cols ? weight_one(w, j0 + i) : w.dflt;
 }
 
-// y = d * rstd * gamma + beta on E values of columns j0.. (in place).
-template <int E, bool VEC>
-__device__ __forceinline__ void affine(float* d, float rstd, const Weights& g, const Weights& b,
-                                       int64_t j0, int64_t cols)
-{
-    if (!g.p && !b.p) {
+// One output, y = (x - mean) * rstd * gamma + beta, formed in double (x -
+// mean is exact there) and rounded once to the output type: a float output
+// directly; a bf16 one through the float that the bf16 store then rounds to
+// the double's correct bf16 (f32_for_bf16).  Without weights gamma is 1 and
+// beta 0, which leave the product as it is.
+template <class YT>
+struct LnMap {
+    double mean, rstd;
+    __device__ double exact(float x, float g, float b) const
+    {
+        return __builtin_fma(((double)x - mean) * rstd, (double)g, (double)b);
+    }
+    __device__ float operator()(float x, float g, float b) const
+    {
+        const double y = exact(x, g, b);
+        if constexpr (sizeof(YT) == 2)
+            return f32_for_bf16(y);
+        else
+            return (float)y;
+    }
+    // E values in place: for bf16, the plain float roundings first and the
+    // halfway-point check of f32_for_bf16 only for a chunk that has a float
+    // on a bf16 halfway point (one branch per chunk, rarely taken).
+    template <int E>
+    __device__ void chunk(float* v, const float* g, const float* b) const
+    {
+        double y[E];
 #pragma unroll
         for (int i = 0; i < E; ++i)
-            d[i] *= rstd;
-        return;
+            y[i] = exact(v[i], g[i], b[i]);
+        if constexpr (sizeof(YT) == 2) {
+            bool half = false;
+#pragma unroll
+            for (int i = 0; i < E; ++i) {
+                v[i] = (float)y[i];
+                half |= (__float_as_uint(v[i]) & 0xFFFFu) == 0x8000u;
+            }
+            if (half) {
+#pragma unroll
+                for (int i = 0; i < E; ++i)
+                    v[i] = f32_for_bf16(y[i]);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < E; ++i)
+                v[i] = (float)y[i];
+        }
     }
+};
+
+// The map on E values x of columns j0.. (in place), with their weights.
+template <class YT, int E, bool VEC>
+__device__ __forceinline__ void ln_affine(float* v, const LnMap<YT>& map, const Weights& g,
+                                          const Weights& b, int64_t j0, int64_t cols)
+{
     float gw[E], bw[E];
     load_weights<E, VEC>(g, j0, cols, gw);
     load_weights<E, VEC>(b, j0, cols, bw);
-#pragma unroll
-    for (int i = 0; i < E; ++i)
-        d[i] = __builtin_fmaf(d[i] * rstd, gw[i], bw[i]);
+    map.template chunk<E>(v, gw, bw);
 }
 
-__device__ __forceinline__ float rstd_of(double m2, int64_t n, float eps)
+__device__ __forceinline__ double rstd_of(double m2, int64_t n, float eps)
 {
     const double var = (m2 > 0.0 ? m2 : 0.0) / (double)n;
-    return (float)(1.0 / sqrt(var + (double)eps));
+    return 1.0 / sqrt(var + (double)eps);
 }
 
 // Shifted sums (s1 = sum (x - K), s2 = sum (x - K)^2) to (mean, rstd).
@@ -144,22 +186,13 @@ __device__ __forceinline__ LnRow row_from_shifted(double K, double s1, double s2
     return LnRow{K + s1 / dn, rstd_of(s2 - s1 * (s1 / dn), n, eps)};
 }
 
-// The centred value of x: (x - mean_f) - c with mean_f = (float)mean and
-// c = (float)(mean - mean_f).
-struct Centre {
-    float mf, c;
-    __device__ explicit Centre(double mean)
-        : mf((float)mean), c((float)(mean - (double)(float)mean)) {}
-    __device__ float operator()(float x) const { return (x - mf) - c; }
-};
-
 __device__ __forceinline__ void write_stats(float* mean_out, float* rstd_out, int64_t r,
                                             const LnRow& st)
 {
     if (mean_out)
         mean_out[r] = (float)st.mean;
     if (rstd_out)
-        rstd_out[r] = st.rstd;
+        rstd_out[r] = (float)st.rstd;
 }
 
 // The weights of a thread's NCH chunks of E columns as raw pieces of 2E bytes
@@ -219,11 +252,12 @@ struct RawWeights {
 // columns (threadIdx.x + k * NT) * E.  `valid(k, i)` says whether element i
 // of chunk k lies in the row; invalid elements hold 0 and are left out.
 // *e: one more element of the row held by this thread (a misaligned row's
-// head element) when has_e, centred in place like the others; else unused.
+// head element) when has_e; else unused.  The values stay as they are: the
+// sum of squared deviations takes x - mean in double, element by element.
 template <int NCH, int E, int NT, class Valid>
-__device__ __forceinline__ LnRow row_stats_in_registers(float* v, int64_t cols, float eps,
+__device__ __forceinline__ LnRow row_stats_in_registers(const float* v, int64_t cols, float eps,
                                                         double* slot_a, double* slot_b,
-                                                        Valid valid, float* e = nullptr,
+                                                        Valid valid, const float* e = nullptr,
                                                         bool has_e = false)
 {
     double s = 0.0;  // invalid elements hold 0
@@ -232,25 +266,18 @@ __device__ __forceinline__ LnRow row_stats_in_registers(float* v, int64_t cols, 
         s += (double)v[i];
     if (has_e)
         s += (double)*e;
-    const double S = block_reduce<SumF32, NT>(s, slot_a);
-    const double mean = S / (double)cols;
-    const Centre centre(mean);
+    const double mean = block_reduce<SumF32, NT>(s, slot_a) / (double)cols;
     double q = 0.0;
 #pragma unroll
-    for (int k = 0; k < NCH; ++k) {
-        float cq = 0.0f;
+    for (int k = 0; k < NCH; ++k)
 #pragma unroll
         for (int i = 0; i < E; ++i) {
-            const float d = valid(k, i) ? centre(v[k * E + i]) : 0.0f;
-            v[k * E + i] = d;
-            cq = __builtin_fmaf(d, d, cq);
+            const double d = (double)v[k * E + i] - mean;
+            q = valid(k, i) ? __builtin_fma(d, d, q) : q;
         }
-        q += (double)cq;
-    }
     if (has_e) {
-        const float d = centre(*e);
-        *e = d;
-        q += (double)(d * d);
+        const double d = (double)*e - mean;
+        q = __builtin_fma(d, d, q);
     }
     const double Q = block_reduce<SumF32, NT>(q, slot_b);
     return LnRow{mean, rstd_of(Q, cols, eps)};
@@ -286,14 +313,21 @@ __device__ __forceinline__ void ln_row_from_chunks(const uint4* raw, YT* yr, int
         });
     if (threadIdx.x == 0)
         write_stats(mean_out, rstd_out, r, st);
+    const LnMap<YT> map{st.mean, st.rstd};
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
         const int64_t j0 = ((int64_t)threadIdx.x + (int64_t)k * NT) * E;
         if (EXACT || j0 < cols) {
+            if constexpr (AFF) {
+                map.template chunk<E>(v + k * E, gw + k * E, bw + k * E);
+            } else {
+                float ones[E], zeros[E];
 #pragma unroll
-            for (int i = 0; i < E; ++i) {
-                const float t = v[k * E + i] * st.rstd;
-                v[k * E + i] = AFF ? __builtin_fmaf(t, gw[k * E + i], bw[k * E + i]) : t;
+                for (int i = 0; i < E; ++i) {
+                    ones[i] = 1.0f;
+                    zeros[i] = 0.0f;
+                }
+                map.template chunk<E>(v + k * E, ones, zeros);
             }
             YOut<YT>::template chunk<E>(yr + j0, v + k * E);
         }
@@ -373,16 +407,16 @@ __global__ __launch_bounds__(NT) void k_layernorm_block(
             &e, has_e);
         if (threadIdx.x == 0)
             write_stats(mean_out, rstd_out, r, st);
+        const LnMap<YT> map{st.mean, st.rstd};
 #pragma unroll
         for (int k = 0; k < NCH; ++k) {
             const int64_t j0 = ((int64_t)threadIdx.x + (int64_t)k * NT) * E;
-            affine<E, VEC>(v + k * E, st.rstd, gh, bh, j0, cb);
+            ln_affine<YT, E, VEC>(v + k * E, map, gh, bh, j0, cb);
             store_masked_rt<YT, E>(yr, j0, cb, v + k * E, yvec);
         }
         if (has_e)
             YOut<YT>::one(yr0 + threadIdx.x,
-                          __builtin_fmaf(e * st.rstd, weight_one(g, threadIdx.x),
-                                         weight_one(b, threadIdx.x)));
+                          map(e, weight_one(g, threadIdx.x), weight_one(b, threadIdx.x)));
     }
 }
 
@@ -431,18 +465,15 @@ __global__ __launch_bounds__(NT) void k_layernorm_stream(
         const LnRow st = row_from_shifted(K, S1, S2, cols, eps);
         if (threadIdx.x == 0)
             write_stats(mean_out, rstd_out, r, st);
-        const Centre centre(st.mean);
+        const LnMap<YT> map{st.mean, st.rstd};
         if (has_e)
-            YOut<YT>::one(yr0 + threadIdx.x,
-                          __builtin_fmaf(centre(XIn<XT>::one(xr0 + threadIdx.x)) * st.rstd,
-                                         weight_one(g, threadIdx.x), weight_one(b, threadIdx.x)));
+            YOut<YT>::one(yr0 + threadIdx.x, map(XIn<XT>::one(xr0 + threadIdx.x),
+                                                 weight_one(g, threadIdx.x),
+                                                 weight_one(b, threadIdx.x)));
         for (int64_t j0 = (int64_t)threadIdx.x * E; j0 < cb; j0 += (int64_t)NT * E) {
             float v[E];
             load_padded<XT, E, VEC>(xr, j0, cb, v, 0.0f);
-#pragma unroll
-            for (int i = 0; i < E; ++i)
-                v[i] = centre(v[i]);
-            affine<E, VEC>(v, st.rstd, gh, bh, j0, cb);
+            ln_affine<YT, E, VEC>(v, map, gh, bh, j0, cb);
             store_masked_rt<YT, E>(yr, j0, cb, v, yvec);
         }
         __syncthreads();  // slot reuse by the next row
@@ -490,23 +521,20 @@ __global__ __launch_bounds__(kBlockThreads) void k_layernorm_wave(
             for (int i = 0; i < E; ++i)
                 s += (double)v[u][i];
             const double mean = segment_reduce<SumF32, S>(s) / (double)cols;
-            const Centre centre(mean);
-            float cq = 0.0f;
+            double q = 0.0;
 #pragma unroll
             for (int i = 0; i < E; ++i) {
-                const float d = j0 + i < cols ? centre(v[u][i]) : 0.0f;
-                v[u][i] = d;
-                cq = __builtin_fmaf(d, d, cq);
+                const double d = (double)v[u][i] - mean;
+                q = j0 + i < cols ? __builtin_fma(d, d, q) : q;
             }
-            const double Q = segment_reduce<SumF32, S>((double)cq);
+            const double Q = segment_reduce<SumF32, S>(q);
             const LnRow st{mean, rstd_of(Q, cols, eps)};
+            const LnMap<YT> map{st.mean, st.rstd};
             const int64_t r = row0 + (int64_t)u * RPG + seg;
             if (r < rows) {
                 if (lane % S == 0)
                     write_stats(mean_out, rstd_out, r, st);
-#pragma unroll
-                for (int i = 0; i < E; ++i)
-                    v[u][i] = __builtin_fmaf(v[u][i] * st.rstd, gw[i], bw[i]);
+                map.template chunk<E>(v[u], gw, bw);
                 store_masked<YT, E, VEC>(y + r * ldy, j0, cols, v[u]);
             }
         }
@@ -541,12 +569,9 @@ __global__ __launch_bounds__(kBlockThreads) void k_layernorm_tiled(
             }
             const LnRow st{mean, rstd_of(q, cols, eps)};
             write_stats(mean_out, rstd_out, r, st);
-            const Centre centre(mean);
-            for (int64_t j = 0; j < cols; ++j) {
-                const float d = centre(XIn<XT>::one(xr + j));
-                YOut<YT>::one(yr + j, __builtin_fmaf(d * st.rstd, weight_one(g, j),
-                                                     weight_one(b, j)));
-            }
+            const LnMap<YT> map{st.mean, st.rstd};
+            for (int64_t j = 0; j < cols; ++j)
+                YOut<YT>::one(yr + j, map(XIn<XT>::one(xr + j), weight_one(g, j), weight_one(b, j)));
         }
     }
 }
@@ -662,7 +687,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_layernorm_splitk_stats(
 template <class XT>
 __device__ __forceinline__ void ln_row_stats_lds(const XT* x, int64_t ldx, int64_t r0, int nr,
                                                  int64_t cols, float eps, int32_t G,
-                                                 const double* part, double* smean, float* srstd)
+                                                 const double* part, double* smean, double* srstd)
 {
     int tpr = 1;
     while (tpr < 64 && tpr * 2 * nr <= kBlockThreads)
@@ -713,7 +738,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_layernorm_splitk_map(
     constexpr int N = U * E;
     constexpr int64_t kTile = (int64_t)N * kBlockThreads;
     __shared__ double smean[kBlockThreads];
-    __shared__ float srstd[kBlockThreads];
+    __shared__ double srstd[kBlockThreads];
     const int64_t h = VEC ? head_elems(x, cols) : 0;
     const int64_t cb = cols - h;
     const Weights gh = shifted(g, h), bh = shifted(b, h);
@@ -741,9 +766,9 @@ __global__ __launch_bounds__(kBlockThreads) void k_layernorm_splitk_map(
         if (VEC && t == 0 && (int64_t)threadIdx.x < h) {  // head columns of the chunk's rows
             const float gj = weight_one(g, threadIdx.x), bj = weight_one(b, threadIdx.x);
             for (int i = 0; i < nr; ++i) {
-                const float q = Centre(smean[i])(XIn<XT>::one(x + (r0 + i) * ldx + threadIdx.x)) *
-                                srstd[i];
-                YOut<YT>::one(y + (r0 + i) * ldy + threadIdx.x, __builtin_fmaf(q, gj, bj));
+                const LnMap<YT> map{smean[i], srstd[i]};
+                YOut<YT>::one(y + (r0 + i) * ldy + threadIdx.x,
+                              map(XIn<XT>::one(x + (r0 + i) * ldx + threadIdx.x), gj, bj));
             }
         }
         {
@@ -766,12 +791,17 @@ __global__ __launch_bounds__(kBlockThreads) void k_layernorm_splitk_map(
                     __builtin_amdgcn_sched_barrier(0);
                     float v[N];
                     A.unpack(v);
-                    const Centre centre(smean[i]);
-                    const float rs = srstd[i];
+                    const LnMap<YT> map{smean[i], srstd[i]};
+                    if constexpr (AFF) {
+                        map.template chunk<N>(v, gw, bw);
+                    } else {
+                        float ones[N], zeros[N];
 #pragma unroll
-                    for (int k = 0; k < N; ++k) {
-                        const float q = centre(v[k]) * rs;
-                        v[k] = AFF ? __builtin_fmaf(q, gw[k], bw[k]) : q;
+                        for (int k = 0; k < N; ++k) {
+                            ones[k] = 1.0f;
+                            zeros[k] = 0.0f;
+                        }
+                        map.template chunk<N>(v, ones, zeros);
                     }
                     YT* yt = y + (r0 + i) * ldy + h + t * kTile;
                     if (!VEC || chunk_aligned<YT, E>(yt))
@@ -784,12 +814,17 @@ __global__ __launch_bounds__(kBlockThreads) void k_layernorm_splitk_map(
                 for (int i = 0; i < nr; ++i) {
                     float v[N];
                     load_tile_padded<XT, E, VEC, U>(x + (r0 + i) * ldx + h, t * kTile, cb, v, 0.0f);
-                    const Centre centre(smean[i]);
-                    const float rs = srstd[i];
+                    const LnMap<YT> map{smean[i], srstd[i]};
+                    if constexpr (AFF) {
+                        map.template chunk<N>(v, gw, bw);
+                    } else {
+                        float ones[N], zeros[N];
 #pragma unroll
-                    for (int k = 0; k < N; ++k) {
-                        const float q = centre(v[k]) * rs;
-                        v[k] = AFF ? __builtin_fmaf(q, gw[k], bw[k]) : q;
+                        for (int k = 0; k < N; ++k) {
+                            ones[k] = 1.0f;
+                            zeros[k] = 0.0f;
+                        }
+                        map.template chunk<N>(v, ones, zeros);
                     }
                     YT* yb = y + (r0 + i) * ldy + h;
                     store_tile_masked_rt<YT, E, U>(yb, t * kTile, cb, v,

@@ -64,26 +64,3 @@ def assert_bf16_within_1ulp(gpu, ref, what=""):
             [hex(v) for v in r.ravel()[i]]))
     return int((d > 0).sum())
 
-
-def assert_bf16_within_1ulp_or_abs(gpu, ref, what="", abs_=ABS):
-    """bf16 results within 1 ulp of the oracle, or within `abs_` of it in value.
-
-    For outputs formed by cancellation in float arithmetic (a layernorm's
-    gamma * d * rstd + beta near zero), float's error is absolute, about
-    1e-7 of the terms, and can be several bf16 ulps of a tiny result; the
-    absolute floor is the float32 bar's.
-    """
-    g, r = np.asarray(gpu, dtype=np.uint16), np.asarray(ref, dtype=np.uint16)
-    assert g.shape == r.shape, (what, g.shape, r.shape)
-    gn, rn = _bf16_nan(g), _bf16_nan(r)
-    d = bf16_ulp_diff(g, r)
-    gv = (g.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    rv = (r.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    with np.errstate(invalid="ignore"):
-        near = np.abs(gv - rv) <= abs_
-    ok = ((d <= 1) | near) & ~gn & ~rn | (gn & rn)
-    if not ok.all():
-        i = np.flatnonzero(~ok.ravel())[:5]
-        raise AssertionError("%s: %d of %d beyond 1 bf16 ulp and abs %g; first at %s: gpu %s oracle %s" % (
-            what, (~ok).sum(), ok.size, abs_, i, [hex(v) for v in g.ravel()[i]],
-            [hex(v) for v in r.ravel()[i]]))

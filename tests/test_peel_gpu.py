@@ -14,7 +14,7 @@ import torch
 import oracle
 import split_deterministic_combine_amd as rr
 from split_deterministic_combine_amd import synth
-from tests.gpu_util import (assert_bf16_within_1ulp, assert_bf16_within_1ulp_or_abs,
+from tests.gpu_util import (assert_bf16_within_1ulp,
                             assert_close_f32, assert_exact, to_gpu, to_host)
 
 pytestmark = pytest.mark.gpu
@@ -182,7 +182,7 @@ def test_layernorm_rows_at_any_offset(rows, cols, tiers, xt, yt, xo, yo, pad):
             what = "%s->%s %dx%d x off %d y off %d pad %d w %s %s" % (
                 xt, yt, rows, cols, xo, yo, pad, wmode, tier)
             if yt == "bf16":
-                assert_bf16_within_1ulp_or_abs(to_host(y), ref, what)
+                assert_bf16_within_1ulp(to_host(y), ref, what)
             else:
                 assert_close_f32(to_host(y), ref, what)
             assert_close_f32(to_host(mean), rmean, what + " mean")

@@ -8,7 +8,7 @@ import torch
 import oracle
 import split_deterministic_combine_amd as rr
 from split_deterministic_combine_amd import synth
-from tests.gpu_util import (assert_bf16_within_1ulp, assert_bf16_within_1ulp_or_abs,
+from tests.gpu_util import (assert_bf16_within_1ulp,
                             assert_close_f32, assert_exact, to_gpu, to_host)
 
 pytestmark = pytest.mark.gpu
@@ -91,7 +91,7 @@ def test_random_softmax_and_layernorm(case):
         got = to_host(rr.layernorm_rows(g, eps=1e-5, out_dtype=ydt, tier=tier))
         what = "layernorm %s->%s %dx%d pad %d off %d %s" % (xt, yt, rows, cols, pad, offset, tier)
         if yt == "bf16":
-            assert_bf16_within_1ulp_or_abs(got, ref, what)
+            assert_bf16_within_1ulp(got, ref, what)
         else:
             assert_close_f32(got, ref, what)
 
