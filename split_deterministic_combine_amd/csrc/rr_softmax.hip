@@ -32,9 +32,15 @@ constexpr float kNegInf = -__builtin_inff();
 // different in every thread).  The hardware exponential is exact for normal
 // results; when any argument falls below -126 (a subnormal or vanishing
 // result, or a -inf entry) the thread takes exp2_sub, which scales such
-// arguments into the normal range.  m is the thread's maximum.
-template <int N>
-__device__ __forceinline__ MS exp_sum_from(float* v, float m)
+// arguments into the normal range.  m is the thread's maximum.  live(i):
+// whether value i is a row element; the others (-inf padding, whose
+// exponential the hardware gives as 0 exactly) leave the range check alone,
+// so padding alone does not send a thread to the slow path.
+struct AllLive {
+    __device__ bool operator()(int) const { return true; }
+};
+template <int N, class Live = AllLive>
+__device__ __forceinline__ MS exp_sum_from(float* v, float m, Live live = Live())
 {
     float s = 0.0f;
     if (m != kNegInf) {
@@ -42,7 +48,7 @@ __device__ __forceinline__ MS exp_sum_from(float* v, float m)
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             v[i] = (v[i] - m) * kLog2e;
-            tmin = fminf(tmin, v[i]);
+            tmin = fminf(tmin, live(i) ? v[i] : 0.0f);
         }
         if (tmin >= -126.0f) {
 #pragma unroll
@@ -64,28 +70,29 @@ __device__ __forceinline__ MS exp_sum_from(float* v, float m)
     return MS{m, s};
 }
 
-template <int N>
-__device__ __forceinline__ MS local_exp_sum(float* v)
+template <int N, class Live = AllLive>
+__device__ __forceinline__ MS local_exp_sum(float* v, Live live = Live())
 {
     float m = kNegInf;
 #pragma unroll
     for (int i = 0; i < N; ++i)
         m = fmaxf(m, v[i]);
-    return exp_sum_from<N>(v, m);
+    return exp_sum_from<N>(v, m, live);
 }
 
 // Pass 1 on a thread's N values plus one more element e (a misaligned row's
 // head or tail element, or -inf for none): the maximum covers both; e's
 // exponential (exp2_sub, any range) is added after the others' sum and
 // returned in *pe for pass 2.
-template <int N>
-__device__ __forceinline__ MS local_exp_sum_plus(float* v, float e, float* pe)
+template <int N, class Live = AllLive>
+__device__ __forceinline__ MS local_exp_sum_plus(float* v, float e, float* pe,
+                                                 Live live = Live())
 {
     float m = e;
 #pragma unroll
     for (int i = 0; i < N; ++i)
         m = fmaxf(m, v[i]);
-    MS own = exp_sum_from<N>(v, m);
+    MS own = exp_sum_from<N>(v, m, live);
     const float p = e == kNegInf ? 0.0f : exp2_sub((e - m) * kLog2e);
     own.s += p;
     *pe = p;
@@ -147,7 +154,9 @@ __global__ __launch_bounds__(NT) void k_softmax_block(const XT* __restrict__ x,
         const bool has_e = (int64_t)threadIdx.x < h;
         const float e = has_e ? XIn<XT>::one(xr + threadIdx.x) : kNegInf;
         float pe;
-        const MS own = local_exp_sum_plus<NCH * E>(v, e, &pe);
+        const MS own = local_exp_sum_plus<NCH * E>(v, e, &pe, [&](int i) {
+            return ((int64_t)threadIdx.x + (int64_t)(i / E) * NT) * E + i % E < cb;
+        });
         float e_t;
         const MS tot = block_softmax_stats<NT>(own, slot[par], &e_t);
         par ^= 1;
@@ -190,10 +199,12 @@ __device__ __forceinline__ void softmax_row_from_chunks(const RowBuf<NCH>& buf, 
     }
     const int q = ROT ? line_phase(xr + h) : 0;  // as the row's loads
     float v[NCH * E];
+    bool ok[NCH];  // the slot holds a chunk of the row's body
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
         const int64_t j0 = (int64_t)slot_chunk<NCH, NT, ROT>(k, q) * E;
-        if (EXACT || j0 < nbe) {
+        ok[k] = EXACT || j0 < nbe;
+        if (ok[k]) {
             unpack_chunk<XT>(buf.c[k], v + k * E);
         } else {
 #pragma unroll
@@ -202,7 +213,9 @@ __device__ __forceinline__ void softmax_row_from_chunks(const RowBuf<NCH>& buf, 
         }
     }
     float pe = 0.0f;
-    const MS own = PEEL ? local_exp_sum_plus<NCH * E>(v, buf.e, &pe) : local_exp_sum<NCH * E>(v);
+    const auto live = [&](int i) { return ok[i / E]; };
+    const MS own = PEEL ? local_exp_sum_plus<NCH * E>(v, buf.e, &pe, live)
+                        : local_exp_sum<NCH * E>(v, live);
     float e_t;
     const MS tot = block_softmax_stats<NT>(own, slot, &e_t);
     const float sc = e_t / tot.s;
@@ -340,7 +353,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_softmax_wave(const XT* __rest
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const MS own = local_exp_sum<E>(v[u]);
+            const MS own = local_exp_sum<E>(v[u], [&](int i) { return j0 + i < cols; });
             const MS tot = segment_reduce<SoftmaxMS, S>(own);
             const float sc = exp2_f32((own.m - tot.m) * kLog2e) / tot.s;
 #pragma unroll
