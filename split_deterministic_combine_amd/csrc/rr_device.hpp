@@ -244,8 +244,15 @@ __device__ __forceinline__ float exp2_hw(float t) { return __builtin_amdgcn_exp2
 // scaled by 2^-64, which rounds it once onto the subnormal grid.
 __device__ __forceinline__ float exp2_sub(float t)
 {
-    return t < -126.0f ? exp2_hw(t + 64.0f) * 0x1p-64f : exp2_hw(t);
+    const bool low = t < -126.0f;  // one exponential either way
+    return exp2_hw(low ? t + 64.0f : t) * (low ? 0x1p-64f : 1.0f);
 }
+
+// Marks the rarely taken side of a branch between a fast and a
+// subnormal-safe computation: an empty statement the compiler must keep, so
+// that it does not turn the branch into both computations and a select
+// (which ran every element through both).
+__device__ __forceinline__ void keep_branch() { __asm__ volatile(""); }
 
 struct SoftmaxMS {
     using acc_t = MS;

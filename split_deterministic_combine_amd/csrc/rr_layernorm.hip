@@ -186,6 +186,26 @@ __device__ __forceinline__ LnRow row_from_shifted(double K, double s1, double s2
     return LnRow{K + s1 / dn, rstd_of(s2 - s1 * (s1 / dn), n, eps)};
 }
 
+// Per-row statistics written by every thread of a persistent row loop (the
+// same bits to one address): buffer stores whose range is empty for a NULL
+// output, so no store of the loop sits behind a branch and the prefetch's
+// memory-counter waits count a fixed number of them.
+struct StatsOut {
+    __amdgpu_buffer_rsrc_t m, s;
+    __device__ StatsOut(float* mean_out, float* rstd_out, int64_t rows)
+        : m(__builtin_amdgcn_make_buffer_rsrc(mean_out, 0, mean_out ? (int)(rows * 4) : 0,
+                                              kBufferWord3)),
+          s(__builtin_amdgcn_make_buffer_rsrc(rstd_out, 0, rstd_out ? (int)(rows * 4) : 0,
+                                              kBufferWord3))
+    {
+    }
+    __device__ void write(int64_t r, const LnRow& st) const
+    {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((float)st.mean), m, (int)(r * 4), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((float)st.rstd), s, (int)(r * 4), 0, 0);
+    }
+};
+
 __device__ __forceinline__ void write_stats(float* mean_out, float* rstd_out, int64_t r,
                                             const LnRow& st)
 {
@@ -290,9 +310,8 @@ __device__ __forceinline__ LnRow row_stats_in_registers(const float* v, int64_t 
 template <class XT, class YT, int NCH, int NT, bool EXACT, bool AFF>
 __device__ __forceinline__ void ln_row_from_chunks(const uint4* raw, YT* yr, int64_t r,
                                                    int64_t cols, float eps, const float* gw,
-                                                   const float* bw, float* mean_out,
-                                                   float* rstd_out, double* slot_a,
-                                                   double* slot_b)
+                                                   const float* bw, const StatsOut& so,
+                                                   double* slot_a, double* slot_b)
 {
     constexpr int E = XIn<XT>::kChunk;
     float v[NCH * E];
@@ -311,27 +330,26 @@ __device__ __forceinline__ void ln_row_from_chunks(const uint4* raw, YT* yr, int
         v, cols, eps, slot_a, slot_b, [&](int k, int) {
             return EXACT || ((int64_t)threadIdx.x + (int64_t)k * NT) * E < cols;
         });
-    if (threadIdx.x == 0)
-        write_stats(mean_out, rstd_out, r, st);
+    so.write(r, st);
     const LnMap<YT> map{st.mean, st.rstd};
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
-        const int64_t j0 = ((int64_t)threadIdx.x + (int64_t)k * NT) * E;
-        if (EXACT || j0 < cols) {
-            if constexpr (AFF) {
-                map.template chunk<E>(v + k * E, gw + k * E, bw + k * E);
-            } else {
-                float ones[E], zeros[E];
+        if constexpr (AFF) {
+            map.template chunk<E>(v + k * E, gw + k * E, bw + k * E);
+        } else {
+            float ones[E], zeros[E];
 #pragma unroll
-                for (int i = 0; i < E; ++i) {
-                    ones[i] = 1.0f;
-                    zeros[i] = 0.0f;
-                }
-                map.template chunk<E>(v + k * E, ones, zeros);
+            for (int i = 0; i < E; ++i) {
+                ones[i] = 1.0f;
+                zeros[i] = 0.0f;
             }
-            YOut<YT>::template chunk<E>(yr + j0, v + k * E);
+            map.template chunk<E>(v + k * E, ones, zeros);
         }
+        if constexpr (EXACT)
+            YOut<YT>::template chunk<E>(yr + ((int64_t)threadIdx.x + (int64_t)k * NT) * E, v + k * E);
     }
+    if constexpr (!EXACT)  // chunks past the row go past the buffer range: dropped
+        store_row_peeled<YT, E, NCH, NT, false>(yr, cols, 0, cols, -1, v, 0.0f, 0);
 }
 
 // Persistent rows (persistent_rows: one-row prefetch, two register buffers).
@@ -348,6 +366,7 @@ __global__ __launch_bounds__(NT) void k_layernorm_rows_pf(
     __shared__ double slot[2][NT / kWave];
     if ((int64_t)blockIdx.x >= rows)
         return;
+    const StatsOut so(mean_out, rstd_out, rows);
     float gw[AFF ? NCH * E : 1], bw[AFF ? NCH * E : 1];
     RawWeights<AFF ? NCH : 1, NT, E> graw, braw;
     if constexpr (AFF) {
@@ -367,8 +386,76 @@ __global__ __launch_bounds__(NT) void k_layernorm_rows_pf(
         },
         [&](const RowBuf<NCH>& buf, int64_t r, int) {
             ln_row_from_chunks<XT, YT, NCH, NT, EXACT, AFF>(buf.c, y + r * ldy, r, cols, eps, gw,
-                                                            bw, mean_out, rstd_out, slot[0],
-                                                            slot[1]);
+                                                            bw, so, slot[0], slot[1]);
+        });
+}
+
+// Persistent rows at any alignment and any column count (rows that do not
+// all start 16-byte aligned or do not end on a chunk): the softmax's row
+// layout (load_row_peeled: each row's body from its first 16-byte boundary
+// in chunk slots rotated onto 128-byte lines, one head or tail element per
+// thread).  A thread's columns then move with the row's phase, so gamma and
+// beta are read per row at the body's columns (whole 16-byte words at any
+// element alignment; every row reads the same vectors, which stay in the
+// caches).
+template <class XT, class YT, int NCH, int NT>
+__global__ __launch_bounds__(NT) void k_layernorm_rows_peel(
+    const XT* __restrict__ x, YT* __restrict__ y, Weights g, Weights b, float* mean_out,
+    float* rstd_out, int64_t rows, int64_t cols, int64_t ldx, int64_t ldy, float eps)
+{
+    constexpr int E = XIn<XT>::kChunk;
+    __shared__ double slot[2][NT / kWave];
+    if ((int64_t)blockIdx.x >= rows)
+        return;
+    const StatsOut so(mean_out, rstd_out, rows);
+    persistent_rows<RowBuf<NCH>>(
+        blockIdx.x, gridDim.x, rows,
+        [&](int64_t r, bool live, RowBuf<NCH>& buf) {
+            load_row_peeled<XT, NCH, NT>(x + r * ldx, cols, live, buf);
+        },
+        [] {},
+        [&](const RowBuf<NCH>& buf, int64_t r, int) {
+            const XT* xr = x + r * ldx;
+            const PeelGeom<XT> pg(xr, cols);
+            const int q = line_phase(xr + pg.h);  // as the row's loads
+            // the row's weights first, so that their loads are in flight
+            // while the statistics are formed
+            const Weights gh = shifted(g, pg.h), bh = shifted(b, pg.h);
+            bool ok[NCH];  // the slot holds a chunk of the row's body
+            float gw[NCH * E], bw[NCH * E];
+#pragma unroll
+            for (int k = 0; k < NCH; ++k) {
+                ok[k] = (int64_t)slot_chunk<NCH, NT, true>(k, q) * E < pg.nbe;
+                // slots past the body take chunk 0's weights (never stored)
+                const int64_t j0 = ok[k] ? (int64_t)slot_chunk<NCH, NT, true>(k, q) * E : 0;
+                load_weights<E, true>(gh, j0, pg.nbe, gw + k * E);
+                load_weights<E, true>(bh, j0, pg.nbe, bw + k * E);
+            }
+            const int64_t we = pg.idx >= 0 ? pg.idx : 0;
+            const float ge = weight_one(g, we), be = weight_one(b, we);
+            float v[NCH * E];
+#pragma unroll
+            for (int k = 0; k < NCH; ++k) {
+                if (ok[k]) {
+                    unpack_chunk<XT>(buf.c[k], v + k * E);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < E; ++i)
+                        v[k * E + i] = 0.0f;
+                }
+            }
+            const bool has_e = pg.idx >= 0;
+            float e = has_e ? buf.e : 0.0f;
+            const LnRow st = row_stats_in_registers<NCH, E, NT>(
+                v, cols, eps, slot[0], slot[1], [&](int k, int) { return ok[k]; }, &e, has_e);
+            so.write(r, st);
+            const LnMap<YT> map{st.mean, st.rstd};
+#pragma unroll
+            for (int k = 0; k < NCH; ++k)
+                map.template chunk<E>(v + k * E, gw + k * E, bw + k * E);
+            const float ev = map(e, ge, be);
+            store_row_peeled<YT, E, NCH, NT, true>(y + r * ldy, cols, pg.h, pg.nbe,
+                                                   has_e ? pg.idx : -1, v, ev, q);
         });
 }
 
@@ -871,6 +958,15 @@ template <class XT, class YT, int NCH, int NT>
 static rr_status launch_pf(const XT* x, YT* y, const Weights& g, const Weights& b,
                            const rr_plan& p, const LayernormLaunch& a)
 {
+    if (!(a.rows16 && a.cols % XIn<XT>::kChunk == 0)) {
+        dim3 grid;
+        const rr_status st = persistent_grid(k_layernorm_rows_peel<XT, YT, NCH, NT>, NT, p, a, &grid);
+        if (st != RR_OK)
+            return st;
+        return launch_kernel(k_layernorm_rows_peel<XT, YT, NCH, NT>, grid, dim3(NT), 0, a.stream,
+                             x, y, g, b, a.mean_out, a.rstd_out, a.rows, a.cols, a.ld_x, a.ld_y,
+                             a.eps);
+    }
     if (g.p || b.p)
         return launch_pf_aff<XT, YT, NCH, NT, true>(x, y, g, b, p, a);
     return launch_pf_aff<XT, YT, NCH, NT, false>(x, y, g, b, p, a);
@@ -888,9 +984,10 @@ static rr_status launch_block(const rr_plan& p, const XT* x, YT* y, const Weight
     const hipStream_t s = a.stream;
     const int64_t nch = ceil_div(ceil_div(a.cols, E), NT);
     if constexpr (VEC) {
-        if (a.rows16 && a.cols % E == 0) {
-            // persistent rows; the plan chose the shape and sized the grid
-            const RowPfShape sh = row_pf_shape(a.cols / E);
+        {
+            // persistent rows (any alignment); the plan chose the shape and
+            // sized the grid
+            const RowPfShape sh = row_pf_shape(ceil_div(a.cols, E));
             if (sh.nt > 0 && sh.nt != p.block)
                 return RR_ERR_TIER;  // plan and launch disagree: refuse, launch nothing
             switch (sh.nt * 16 + sh.nch) {

@@ -205,10 +205,12 @@ rr_status plan_layernorm(int64_t rows, int64_t cols, rr_dtype x_dtype, rr_dtype 
         return RR_OK;
     }
     fill_rowwise_geometry(t, rows, cols, t == RR_TIER_WAVE ? (rows16 ? chunk : 1) : vec_elems, out);
-    // persistent rows keep each thread's gamma / beta in registers, so they
-    // need every row to start 16-byte aligned and to be whole chunks
-    if (t == RR_TIER_BLOCK && vec && rows16 && cols % chunk == 0) {
-        const RowPfShape sh = row_pf_shape(cols / chunk);
+    // persistent rows: rows that all start 16-byte aligned and are whole
+    // chunks keep each thread's gamma / beta in registers; the others read
+    // them per row (k_layernorm_rows_peel)
+    (void)rows16;
+    if (t == RR_TIER_BLOCK && vec && cols > 0) {
+        const RowPfShape sh = row_pf_shape(ceil_div(cols, (int64_t)chunk));
         if (sh.nt > 0) {
             out->block = sh.nt;
             const int64_t g = (int64_t)cu_count * row_pf_blocks_per_cu(sh);

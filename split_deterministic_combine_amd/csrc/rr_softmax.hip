@@ -55,6 +55,7 @@ __device__ __forceinline__ MS exp_sum_from(float* v, float m, Live live = Live()
             for (int i = 0; i < N; ++i)
                 v[i] = exp2_hw(v[i]);
         } else {
+            keep_branch();
 #pragma unroll
             for (int i = 0; i < N; ++i)
                 v[i] = exp2_sub(v[i]);
@@ -429,6 +430,7 @@ __device__ __forceinline__ void exp2_values(float* t)
         for (int i = 0; i < N; ++i)
             t[i] = exp2_hw(t[i]);
     } else {
+        keep_branch();
 #pragma unroll
         for (int i = 0; i < N; ++i)
             t[i] = exp2_sub(t[i]);

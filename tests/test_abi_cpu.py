@@ -239,7 +239,9 @@ def test_layernorm_tier_rule_and_geometry():
     p = rr.plan_layernorm(4096, 16384)
     assert p["block"] == 512 and p["grid"] == 256                # 2048 chunks: 4 per lane
     assert rr.plan_layernorm(4096, 16392)["grid"] == 4096        # too long: one row per workgroup
-    assert rr.plan_layernorm(16384, 4095)["grid"] == 16384     # ragged rows: one per workgroup
+    # rows at any alignment are persistent too (per-row weights)
+    assert rr.plan_layernorm(16384, 4095)["grid"] == 1024
+    assert rr.plan_layernorm(16384, 4095)["block"] == 128
     assert rr.plan_layernorm(100, 40)["tier"] == "wave"
     assert rr.plan_layernorm(100, 8)["tier"] == "tiled"
     assert rr.plan_layernorm(16, 1 << 20)["tier"] == "splitk"
