@@ -74,6 +74,7 @@ KERNEL_OF_OP = {
     "axis_cols_fold": "k_reduce_axis_fold<rr::SumF32>",
     "attention": "k_attn_staged<128, 32, 3, false, float, false>",
     "attention_fused": "k_attn_staged<128, 32, 3, true, unsigned short, false>",
+    "attention_varlen": "k_attn_staged<128, 32, 3, false, float, true>",
     # rows at every offset from a 16-byte boundary and their aligned neighbour
     "sum_47": "k_reduce_wave<rr::SumF32, 4, 16, 2>",
     "sum_1001": "k_reduce_block<rr::SumF32, 4, true>",
@@ -90,6 +91,11 @@ SOFTMAX_LONG = (16, 1 << 22)
 AXIS_COLS = (16384, 16384)
 # split-K attention partials: batch, heads, query rows, depth, keys, partitions
 ATTN = (8, 32, 128, 128, 8192, 8)
+# the same attention over packed sequences of mixed key lengths (ragged
+# placement): ATTN's batch of 128-query sequences, key lengths summing to
+# batch * keys, so the bytes and flops equal the dense row's
+ATTN_VARLEN_K = (2048, 4096, 6144, 8192, 8192, 10240, 12288, 14336)
+assert sum(ATTN_VARLEN_K) == ATTN[0] * ATTN[4] and len(ATTN_VARLEN_K) == ATTN[0]
 CU_MI355X = 256
 
 
@@ -144,6 +150,7 @@ def _algo_bytes():
         # one launch: q, k, v read once and the bf16 output written once (the
         # partials pass through the device-coherent level, not counted)
         "attention_fused": _attn_fused_bytes(),
+        "attention_varlen": _attn_bytes(),
         "sum_47": 1048576 * 47 * 4 + 1048576 * 4,
         "sum_1001": 65536 * 1001 * 4 + 65536 * 4,
         "sum_1000": 65536 * 1000 * 4 + 65536 * 4,
@@ -163,6 +170,8 @@ NEXT_BYTES = {"multi_long": 16 * (1 << 24) * 4 + 3 * 16 * 4,
               # q, k, v read and bf16 attention written once (the partials are internal)
               "attention_merged": _attn_fused_bytes(),
               "attention_fused": _attn_fused_bytes(),
+              # packed sequences: the dense row's q, k, v and partial bytes
+              "attention_varlen": _attn_bytes(),
               # rows that do not all start 16-byte aligned (odd row strides),
               # beside their aligned neighbours: each row's body from its
               # first 16-byte boundary in 128-bit loads, head and tail scalar
@@ -457,6 +466,17 @@ def main():
         dx["attn_fused"] = torch.empty((ab, ah, asq, ad), dtype=torch.bfloat16, device=dev)
         dx["attn_ws"] = torch.zeros(rr.splitk_attention_workspace_bytes(ab, ah, ah, asq, an, ad, ap),
                                     dtype=torch.uint8, device=dev)
+        # packed sequences: q [tokens, heads, depth], k / v [key tokens, heads,
+        # depth], standard normal rounded to bf16, int32 token offsets
+        gen.manual_seed(synth.SEED_ATTENTION + 1)
+        tq, tk = ab * asq, sum(ATTN_VARLEN_K)
+        dx["varlen_qkv"] = tuple(torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16)
+                                 for shape in ((tq, ah, ad), (tk, ah, ad), (tk, ah, ad)))
+        dx["varlen_cu"] = tuple(
+            torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=dev)
+            for lens in ([asq] * ab, list(ATTN_VARLEN_K)))
+        dx["varlen_out"] = (torch.empty((ap, tq, ah, ad), device=dev),
+                            torch.empty((ap, tq, ah), device=dev), torch.empty((ap, tq, ah), device=dev))
     if not args.no_next:
         # odd-stride rows and their aligned neighbours, drawn on the device
         # (standard normal, seeded); two sets each so consecutive launches
@@ -510,6 +530,9 @@ def main():
         "attention_fused": lambda i: rr.splitk_attention(*dx["attn_qkv"], ATTN[5],
                                                          out=dx["attn_fused"],
                                                          workspace=dx["attn_ws"]),
+        # the partials of packed sequences of mixed key lengths
+        "attention_varlen": lambda i: rr.splitk_attention_partials_varlen(
+            *dx["varlen_qkv"], *dx["varlen_cu"], ATTN[2], ATTN[5], out=dx["varlen_out"]),
         "sum_47": lambda i: rr.reduce_rows(dx["sum_47"][i % 2], "sum", out=dx["sum_47_out"]),
         "sum_1001": lambda i: rr.reduce_rows(dx["sum_1001"][i % 2], "sum", out=dx["sum_1001_out"]),
         "sum_1000": lambda i: rr.reduce_rows(dx["sum_1000"][i % 2], "sum", out=dx["sum_1001_out"]),
@@ -575,6 +598,25 @@ def main():
             rows = slice((bh[0] * ah + bh[1]) * asq, (bh[0] * ah + bh[1] + 1) * asq)
             og = dx["attn_out"][0][:, rows].cpu().numpy()
             mg = dx["attn_out"][1][:, rows].cpu().numpy()
+            ok &= bool(np.all(np.abs(og - o_r) <= (2.0 ** -8 + 2.0 ** -12) * o_a + 1e-6))
+            ok &= bool(np.all(np.abs(mg - m_r) <= 1e-5 * (1 + np.abs(m_r))))
+        if "attention_varlen" in next_names:
+            # the last sequence (the most keys) at its last head against the
+            # oracle, with the dense row's bound
+            ab, ah, asq, ad, an, ap = ATTN
+            sb, hh = ab - 1, ah - 1
+            q0, k0 = sb * asq, sum(ATTN_VARLEN_K[:sb])
+            nk = ATTN_VARLEN_K[sb]
+            qv, kv, vv = dx["varlen_qkv"]
+            bits = [t[a:a + n, hh:hh + 1].contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+                    for t, a, n in ((qv, q0, asq), (kv, k0, nk), (vv, k0, nk))]
+            cq, ck = np.array([0, asq], np.int32), np.array([0, nk], np.int32)
+            sc = 1.0 / math.sqrt(ad)
+            o_r, m_r, _ = oracle.attention_partials_varlen(*bits, cq, ck, ap, sc)
+            o_a, _, _ = oracle.attention_partials_varlen(bits[0], bits[1], bits[2] & np.uint16(0x7FFF),
+                                                         cq, ck, ap, sc)
+            og = dx["varlen_out"][0][:, q0:q0 + asq, hh].cpu().numpy()
+            mg = dx["varlen_out"][1][:, q0:q0 + asq, hh].cpu().numpy()
             ok &= bool(np.all(np.abs(og - o_r) <= (2.0 ** -8 + 2.0 ** -12) * o_a + 1e-6))
             ok &= bool(np.all(np.abs(mg - m_r) <= 1e-5 * (1 + np.abs(m_r))))
         if "attention_fused" in next_names and "attention_merged" in next_names:
@@ -748,6 +790,20 @@ def main():
                 "flops": _attn_flops(),
                 "TFLOPs": round(_attn_flops() / t_s / 1e12, 1),
                 "pct_peak_bf16_mfma": round(100 * _attn_flops() / t_s / 2.5e15, 1)})
+        if "attention_varlen" in next_rows:
+            ab, ah, asq, ad, an, ap = ATTN
+            t_s = next_rows["attention_varlen"]["ms_mean"] * 1e-3
+            next_rows["attention_varlen"].update({
+                "config": "split-K attention partials of %d packed sequences of %d queries, key "
+                          "lengths %s, %d heads of depth %d, %d partitions per sequence -> float32 "
+                          "O, m, l placed by (token, head)" % (ab, asq, list(ATTN_VARLEN_K), ah,
+                                                               ad, ap),
+                "kernels": [KERNEL_OF_OP["attention_varlen"]],
+                "flops": _attn_flops(),
+                "TFLOPs": round(_attn_flops() / t_s / 1e12, 1)})
+            if "attention" in next_rows:
+                next_rows["attention_varlen"]["frac_of_dense"] = round(
+                    next_rows["attention"]["ms_mean"] / next_rows["attention_varlen"]["ms_mean"], 4)
         if "attention_merged" in next_rows:
             ab, ah, asq, ad, an, ap = ATTN
             t_s = next_rows["attention_merged"]["ms_mean"] * 1e-3

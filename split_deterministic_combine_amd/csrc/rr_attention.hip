@@ -297,7 +297,36 @@ constexpr int attn_workgroups_per_cu()
 // cu_k[b+1] - 1 (offsets clamped into the tensors); q_rows is the longest
 // sequence's query count (q_tiles tiles of it), kv_len the total key count;
 // the partial of (token t, head h) is row t * heads + h of the rows
-// (= total_q * heads) of each partition.  Tiles past a sequence's end exit.
+// (= total_q * heads) of each partition.  Tiles past a sequence's end exit;
+// a sequence's query rows past q_rows are left unwritten.
+// The sequence of rank pos when a batch's sequences are ordered by key count,
+// most first, ties by index: thread t < batch counts the sequences ahead of
+// sequence t, and the one with pos ahead of it is the answer (the order is
+// total, so exactly one thread finds it).  Key counts as the work items take
+// them, from cu_k clamped into [0, kv_len].  Every thread of the workgroup
+// calls it (one barrier).
+__device__ int64_t attn_sequence_of_rank(int64_t pos, const int32_t* __restrict__ cu_k,
+                                         int64_t batch, int64_t kv_len, int32_t* slot)
+{
+    auto keys = [&](int64_t s) {
+        const int64_t c0 = min(max((int64_t)cu_k[s], (int64_t)0), kv_len);
+        return min(max((int64_t)cu_k[s + 1], c0), kv_len) - c0;
+    };
+    if ((int64_t)threadIdx.x < batch) {
+        const int64_t t = threadIdx.x, kt = keys(t);
+        int64_t ahead = 0;
+        for (int64_t u = 0; u < batch; ++u) {
+            const int64_t ku = keys(u);
+            ahead += (ku > kt || (ku == kt && u < t)) ? 1 : 0;
+        }
+        if (ahead == pos)
+            *slot = (int32_t)t;
+    }
+    __syncthreads();
+    const int64_t s = *slot;
+    return s < 0 ? 0 : s >= batch ? batch - 1 : s;
+}
+
 template <int D, int KB, int NS, bool FUSED, class YT, bool RAGGED = false>
 __global__ __launch_bounds__(kBlockThreads, (attn_workgroups_per_cu<D, FUSED>())) void k_attn_staged(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -332,14 +361,47 @@ __global__ __launch_bounds__(kBlockThreads, (attn_workgroups_per_cu<D, FUSED>())
     const int64_t xcd = blockIdx.x % kXcds, idx = blockIdx.x / kXcds;
     int64_t w = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
     const int64_t group = heads / kv_heads;
-    const int32_t qt = (int32_t)(w % q_tiles);
-    w /= q_tiles;
-    const int64_t g = w % group;
-    w /= group;
-    const int32_t p = (int32_t)(w % P);
-    w /= P;
-    const int64_t kvl = w % kv_heads;
-    const int64_t b = w / kv_heads;
+    int32_t qt, p;
+    int64_t g, kvl, b;
+    if constexpr (RAGGED) {
+        // Sequences of different lengths.  A unit of work is (sequence, kv
+        // head, partition); its q_tiles * group items share the unit's keys
+        // and run one after another on one XCD.  When a sequence's units
+        // divide evenly over the XCDs (and the batch fits the workgroup),
+        // XCD x takes units x, x + 8, ... of every sequence, the sequences
+        // in order of key count, most first (longest-processing-time
+        // order); else the sequence index varies fastest, so that every
+        // XCD's range of work still takes its share of each sequence.
+        __shared__ int32_t seq_slot;
+        const int64_t inner = (int64_t)q_tiles * group;
+        const int64_t per_seq = (int64_t)P * kv_heads;
+        const int64_t batch = nb / (inner * per_seq);
+        int64_t i, unit;
+        if (per_seq % kXcds == 0 && batch <= kBlockThreads) {
+            const int64_t span = per_seq / kXcds * inner;  // a sequence's items on one XCD
+            i = idx % inner;
+            unit = (idx % span) / inner * kXcds + xcd;
+            b = attn_sequence_of_rank(idx / span, cu_k, batch, kv_len, &seq_slot);
+        } else {
+            i = w % inner;
+            w /= inner;
+            b = w % batch;
+            unit = w / batch;
+        }
+        qt = (int32_t)(i % q_tiles);
+        g = i / q_tiles;
+        p = (int32_t)(unit % P);
+        kvl = unit / P;
+    } else {
+        qt = (int32_t)(w % q_tiles);
+        w /= q_tiles;
+        g = w % group;
+        w /= group;
+        p = (int32_t)(w % P);
+        w /= P;
+        kvl = w % kv_heads;
+        b = w / kv_heads;
+    }
     const int64_t bh = b * heads + kvl * group + g;
     const int64_t kvh = b * kv_heads + kvl;
 
@@ -356,7 +418,7 @@ __global__ __launch_bounds__(kBlockThreads, (attn_workgroups_per_cu<D, FUSED>())
         const int64_t a1 = min(max((int64_t)cu_q[b + 1], a0), total_q);
         const int64_t c0 = min(max((int64_t)cu_k[b], (int64_t)0), kv_len);
         const int64_t c1 = min(max((int64_t)cu_k[b + 1], c0), kv_len);
-        nq = a1 - a0;
+        nq = min(a1 - a0, (int64_t)q_rows);            // rows past q_rows are not computed
         nk = c1 - c0;
         prow0 = a0 * heads + hq;
         rs = heads;

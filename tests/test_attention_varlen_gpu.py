@@ -48,13 +48,15 @@ def _score_bound(q, k, cu_q, cu_k, scale):
     return bs.reshape(-1)
 
 
-def _varlen(q, k, v, cu_q, cu_k, P, scale):
-    """The GPU partials, written into NaN-filled outputs, copied back."""
+def _varlen(q, k, v, cu_q, cu_k, P, scale, max_q=None):
+    """The GPU partials, written into NaN-filled outputs (max_q: the longest
+    sequence unless given)."""
     total_q, heads, depth = q.shape
     out = (torch.full((P, total_q, heads, depth), float("nan"), device="cuda"),
            torch.full((P, total_q, heads), float("nan"), device="cuda"),
            torch.full((P, total_q, heads), float("nan"), device="cuda"))
-    max_q = int(np.max(np.diff(cu_q))) if cu_q.size > 1 else 0
+    if max_q is None:
+        max_q = int(np.max(np.diff(cu_q))) if cu_q.size > 1 else 0
     rr.splitk_attention_partials_varlen(
         _bf16_tensor(q), _bf16_tensor(k), _bf16_tensor(v),
         torch.from_numpy(cu_q).cuda(), torch.from_numpy(cu_k).cuda(), max_q, P, scale, out=out)
@@ -101,6 +103,10 @@ CASES = [
     ([128, 129, 1], [64, 64, 8], 2, 2, 64, 8, 0, 0),
     ([0, 0, 33], [5, 0, 40], 3, 1, 128, 4, 2, 1),
     ([200, 17, 64, 300], [17, 1024, 200, 1], 8, 2, 128, 8, 0, 11),
+    # many short sequences: the longest-first order over a batch of 256 (one
+    # per thread of the ranking) and, past 256, the sequence-fastest order
+    ([(i * 7) % 4 for i in range(256)], [(i * 13) % 21 for i in range(256)], 1, 1, 64, 8, 1, 0),
+    ([(i * 5) % 3 for i in range(260)], [(i * 11) % 17 for i in range(260)], 2, 1, 64, 8, 0, 2),
 ]
 
 
@@ -165,6 +171,24 @@ def test_varlen_partials_then_merge_is_ragged_attention():
     assert np.all(np.abs(got[live] - ref_o[0][live]) <= tol[live])
     # rows with no key or of no sequence merge to zeros
     assert np.all(got[~live] == 0)
+
+
+def test_varlen_rows_past_max_q_rows_are_not_written():
+    # max_q_rows below the longest sequence: each sequence's first max_q_rows
+    # query rows carry the bits of the call with the full bound, and the rest
+    # keep what the outputs held
+    q_lens, k_lens, heads, kvh, depth, P, max_q = [130, 40, 97, 0], [300, 17, 90, 5], 2, 1, 64, 4, 64
+    q, k, v, cu_q, cu_k = synth.attention_varlen(764, q_lens, k_lens, heads, kvh, depth, 2, 0)
+    full = _varlen(q, k, v, cu_q, cu_k, P, 0.125)
+    part = _varlen(q, k, v, cu_q, cu_k, P, 0.125, max_q=max_q)
+    local = np.full(q.shape[0], -1)
+    for b in range(len(q_lens)):
+        local[cu_q[b]:cu_q[b + 1]] = np.arange(cu_q[b + 1] - cu_q[b])
+    done = torch.from_numpy((local >= 0) & (local < max_q)).cuda()
+    assert int(done.sum()) == sum(min(n, max_q) for n in q_lens)
+    for f, g in zip(full, part):
+        assert torch.equal(f[:, done].view(torch.int32), g[:, done].view(torch.int32))
+        assert torch.all(torch.isnan(g[:, ~done]))
 
 
 def test_varlen_rejects_bad_arguments():
