@@ -123,6 +123,11 @@ constexpr int row_pf_blocks_per_cu(RowPfShape sh)
 constexpr int kLnMaxChunks = 8;
 constexpr int kLnSplitKUnroll = 4;
 constexpr int kLnMapMinRows = 4;  // split-K map: rows sharing one load of a tile's gamma / beta
+// Persistent layernorm rows at any alignment: gamma and beta as float in LDS
+// (the row's phase moves its columns across the threads, so every row reads
+// them at new offsets) when both, padded one word per chunk, fit in
+// kLnLdsWeightBytes (bf16 rows up to 4096 columns).
+constexpr int64_t kLnLdsWeightBytes = 36880;
 
 // LSE merge: partitions staged per batch of loads, and workgroup size.
 constexpr int kMergeBatch = 8;

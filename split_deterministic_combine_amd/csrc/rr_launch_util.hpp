@@ -31,16 +31,19 @@ rr_status launch_kernel(void (*k)(KArgs...), dim3 grid, dim3 block, size_t lds_b
         held);
 }
 
-// Workgroups of kernel k resident per CU at nt threads (no dynamic LDS).
-// The runtime's answer depends only on the kernel's resources, and asking
-// costs microseconds of host time in front of every launch, so each
-// (kernel, nt) is asked once per process; the table holds a few dozen pairs.
+// Workgroups of kernel k resident per CU at nt threads and `lds` bytes of
+// dynamic LDS.  The runtime's answer depends only on the kernel's resources,
+// and asking costs microseconds of host time in front of every launch, so
+// each (kernel, nt, lds) is asked once per process; the table holds a few
+// dozen of them.
 template <class K>
-rr_status blocks_per_cu(K k, int nt, int* out)
+rr_status blocks_per_cu(K k, int nt, int* out, size_t lds = 0)
 {
     struct Entry {
         const void* fn;
-        int nt, blocks;
+        int nt;
+        size_t lds;
+        int blocks;
     };
     static std::mutex mu;
     static Entry table[64];
@@ -49,16 +52,16 @@ rr_status blocks_per_cu(K k, int nt, int* out)
     {
         std::lock_guard<std::mutex> lock(mu);
         for (int i = 0; i < used; ++i)
-            if (table[i].fn == fn && table[i].nt == nt) {
+            if (table[i].fn == fn && table[i].nt == nt && table[i].lds == lds) {
                 *out = table[i].blocks;
                 return RR_OK;
             }
     }
     int v = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k, nt, 0) != hipSuccess || v < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k, nt, lds) != hipSuccess || v < 1)
         return RR_ERR_HIP;
     std::lock_guard<std::mutex> lock(mu);
-    if (used < 64) table[used++] = Entry{fn, nt, v};
+    if (used < 64) table[used++] = Entry{fn, nt, lds, v};
     *out = v;
     return RR_OK;
 }

@@ -395,19 +395,32 @@ __global__ __launch_bounds__(NT) void k_layernorm_rows_pf(
 // layout (load_row_peeled: each row's body from its first 16-byte boundary
 // in chunk slots rotated onto 128-byte lines, one head or tail element per
 // thread).  A thread's columns then move with the row's phase, so gamma and
-// beta are read per row at the body's columns (whole 16-byte words at any
-// element alignment; every row reads the same vectors, which stay in the
-// caches).
-template <class XT, class YT, int NCH, int NT>
+// beta are read per row at the body's columns.  LDSW: the workgroup first
+// copies them, as float, into LDS, column c of gamma at word c + c / E and
+// of beta as many words further on -- one pad word after every E columns,
+// so that the lanes of a chunk read (E columns apart) fall in distinct
+// banks -- and each row reads its columns there; else from global memory
+// (whole 16-byte words at any element alignment; every row reads the same
+// vectors, which stay in the caches).
+template <class XT, class YT, int NCH, int NT, bool LDSW>
 __global__ __launch_bounds__(NT) void k_layernorm_rows_peel(
     const XT* __restrict__ x, YT* __restrict__ y, Weights g, Weights b, float* mean_out,
     float* rstd_out, int64_t rows, int64_t cols, int64_t ldx, int64_t ldy, float eps)
 {
     constexpr int E = XIn<XT>::kChunk;
     __shared__ double slot[2][NT / kWave];
+    extern __shared__ float ldsw[];
     if ((int64_t)blockIdx.x >= rows)
         return;
     const StatsOut so(mean_out, rstd_out, rows);
+    const uint32_t bw0 = (uint32_t)(cols + cols / E);  // beta's first word
+    if constexpr (LDSW) {
+        for (uint32_t j = threadIdx.x; j < (uint32_t)cols; j += NT) {
+            ldsw[j + j / E] = weight_one(g, j);
+            ldsw[bw0 + j + j / E] = weight_one(b, j);
+        }
+        __syncthreads();
+    }
     persistent_rows<RowBuf<NCH>>(
         blockIdx.x, gridDim.x, rows,
         [&](int64_t r, bool live, RowBuf<NCH>& buf) {
@@ -418,21 +431,27 @@ __global__ __launch_bounds__(NT) void k_layernorm_rows_peel(
             const XT* xr = x + r * ldx;
             const PeelGeom<XT> pg(xr, cols);
             const int q = line_phase(xr + pg.h);  // as the row's loads
-            // the row's weights first, so that their loads are in flight
-            // while the statistics are formed
-            const Weights gh = shifted(g, pg.h), bh = shifted(b, pg.h);
             bool ok[NCH];  // the slot holds a chunk of the row's body
             float gw[NCH * E], bw[NCH * E];
-#pragma unroll
-            for (int k = 0; k < NCH; ++k) {
-                ok[k] = (int64_t)slot_chunk<NCH, NT, true>(k, q) * E < pg.nbe;
-                // slots past the body take chunk 0's weights (never stored)
-                const int64_t j0 = ok[k] ? (int64_t)slot_chunk<NCH, NT, true>(k, q) * E : 0;
-                load_weights<E, true>(gh, j0, pg.nbe, gw + k * E);
-                load_weights<E, true>(bh, j0, pg.nbe, bw + k * E);
-            }
             const int64_t we = pg.idx >= 0 ? pg.idx : 0;
-            const float ge = weight_one(g, we), be = weight_one(b, we);
+            float ge, be;
+#pragma unroll
+            for (int k = 0; k < NCH; ++k)
+                ok[k] = (int64_t)slot_chunk<NCH, NT, true>(k, q) * E < pg.nbe;
+            if constexpr (!LDSW) {
+                // the row's weights first, so that their loads are in flight
+                // while the statistics are formed
+                const Weights gh = shifted(g, pg.h), bh = shifted(b, pg.h);
+#pragma unroll
+                for (int k = 0; k < NCH; ++k) {
+                    // slots past the body take chunk 0's weights (never stored)
+                    const int64_t j0 = ok[k] ? (int64_t)slot_chunk<NCH, NT, true>(k, q) * E : 0;
+                    load_weights<E, true>(gh, j0, pg.nbe, gw + k * E);
+                    load_weights<E, true>(bh, j0, pg.nbe, bw + k * E);
+                }
+                ge = weight_one(g, we);
+                be = weight_one(b, we);
+            }
             float v[NCH * E];
 #pragma unroll
             for (int k = 0; k < NCH; ++k) {
@@ -449,6 +468,27 @@ __global__ __launch_bounds__(NT) void k_layernorm_rows_peel(
             const LnRow st = row_stats_in_registers<NCH, E, NT>(
                 v, cols, eps, slot[0], slot[1], [&](int k, int) { return ok[k]; }, &e, has_e);
             so.write(r, st);
+            if constexpr (LDSW) {
+                // columns h + j0 + i of the body's chunks (j0 = m E): words
+                // h + j0 + m + i, plus one where h + i passes E (the same
+                // for every chunk of the row); slots past the body read
+                // from word 0 (never stored); then the head or tail element
+                const uint32_t h = (uint32_t)pg.h;
+#pragma unroll
+                for (int k = 0; k < NCH; ++k) {
+                    const uint32_t m = (uint32_t)slot_chunk<NCH, NT, true>(k, q);
+                    const uint32_t w0 = ok[k] ? h + m * (E + 1) : 0u;
+#pragma unroll
+                    for (int i = 0; i < E; ++i) {
+                        const uint32_t w = w0 + i + (h + i >= (uint32_t)E ? 1u : 0u);
+                        gw[k * E + i] = ldsw[w];
+                        bw[k * E + i] = ldsw[bw0 + w];
+                    }
+                }
+                const uint32_t wc = (uint32_t)we + (uint32_t)we / E;
+                ge = ldsw[wc];
+                be = ldsw[bw0 + wc];
+            }
             const LnMap<YT> map{st.mean, st.rstd};
 #pragma unroll
             for (int k = 0; k < NCH; ++k)
@@ -959,13 +999,22 @@ static rr_status launch_pf(const XT* x, YT* y, const Weights& g, const Weights& 
                            const rr_plan& p, const LayernormLaunch& a)
 {
     if (!(a.rows16 && a.cols % XIn<XT>::kChunk == 0)) {
-        dim3 grid;
-        const rr_status st = persistent_grid(k_layernorm_rows_peel<XT, YT, NCH, NT>, NT, p, a, &grid);
-        if (st != RR_OK)
-            return st;
-        return launch_kernel(k_layernorm_rows_peel<XT, YT, NCH, NT>, grid, dim3(NT), 0, a.stream,
-                             x, y, g, b, a.mean_out, a.rstd_out, a.rows, a.cols, a.ld_x, a.ld_y,
-                             a.eps);
+        // gamma and beta (when given) through LDS when both fit: cols words
+        // each plus one pad word per chunk, rounded up to 1 KiB (the occupancy
+        // query takes the same size as the launch)
+        const int64_t wbytes =
+            2 * (a.cols + a.cols / XIn<XT>::kChunk + 1) * (int64_t)sizeof(float);
+        const bool ldsw = (g.p || b.p) && wbytes <= kLnLdsWeightBytes;
+        auto kernel = ldsw ? k_layernorm_rows_peel<XT, YT, NCH, NT, true>
+                           : k_layernorm_rows_peel<XT, YT, NCH, NT, false>;
+        const size_t lds = ldsw ? (size_t)((wbytes + 1023) / 1024 * 1024) : 0;
+        int per_cu = 0;
+        if (blocks_per_cu(kernel, NT, &per_cu, lds) != RR_OK)
+            return RR_ERR_HIP;
+        const int64_t cap = (int64_t)per_cu * a.cu;
+        const dim3 grid((unsigned)(p.grid < cap ? p.grid : cap));
+        return launch_kernel(kernel, grid, dim3(NT), lds, a.stream, x, y, g, b, a.mean_out,
+                             a.rstd_out, a.rows, a.cols, a.ld_x, a.ld_y, a.eps);
     }
     if (g.p || b.p)
         return launch_pf_aff<XT, YT, NCH, NT, true>(x, y, g, b, p, a);
