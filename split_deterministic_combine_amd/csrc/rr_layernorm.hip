@@ -274,7 +274,10 @@ struct RawWeights {
 // *e: one more element of the row held by this thread (a misaligned row's
 // head element) when has_e; else unused.  The values stay as they are: the
 // sum of squared deviations takes x - mean in double, element by element.
-template <int NCH, int E, int NT, class Valid>
+// CHUNKWISE: validity is per chunk (valid(k, 0) speaks for the chunk), so
+// each chunk's squared deviations are summed unconditionally and the chunk
+// is kept or dropped once.
+template <int NCH, int E, int NT, bool CHUNKWISE = false, class Valid>
 __device__ __forceinline__ LnRow row_stats_in_registers(const float* v, int64_t cols, float eps,
                                                         double* slot_a, double* slot_b,
                                                         Valid valid, const float* e = nullptr,
@@ -289,12 +292,23 @@ __device__ __forceinline__ LnRow row_stats_in_registers(const float* v, int64_t 
     const double mean = block_reduce<SumF32, NT>(s, slot_a) / (double)cols;
     double q = 0.0;
 #pragma unroll
-    for (int k = 0; k < NCH; ++k)
+    for (int k = 0; k < NCH; ++k) {
+        if constexpr (CHUNKWISE) {
+            double qk = 0.0;
 #pragma unroll
-        for (int i = 0; i < E; ++i) {
-            const double d = (double)v[k * E + i] - mean;
-            q = valid(k, i) ? __builtin_fma(d, d, q) : q;
+            for (int i = 0; i < E; ++i) {
+                const double d = (double)v[k * E + i] - mean;
+                qk = __builtin_fma(d, d, qk);
+            }
+            q = valid(k, 0) ? q + qk : q;
+        } else {
+#pragma unroll
+            for (int i = 0; i < E; ++i) {
+                const double d = (double)v[k * E + i] - mean;
+                q = valid(k, i) ? __builtin_fma(d, d, q) : q;
+            }
         }
+    }
     if (has_e) {
         const double d = (double)*e - mean;
         q = __builtin_fma(d, d, q);
@@ -326,7 +340,7 @@ __device__ __forceinline__ void ln_row_from_chunks(const uint4* raw, YT* yr, int
                 v[k * E + i] = 0.0f;
         }
     }
-    const LnRow st = row_stats_in_registers<NCH, E, NT>(
+    const LnRow st = row_stats_in_registers<NCH, E, NT, true>(
         v, cols, eps, slot_a, slot_b, [&](int k, int) {
             return EXACT || ((int64_t)threadIdx.x + (int64_t)k * NT) * E < cols;
         });
@@ -465,7 +479,7 @@ __global__ __launch_bounds__(NT) void k_layernorm_rows_peel(
             }
             const bool has_e = pg.idx >= 0;
             float e = has_e ? buf.e : 0.0f;
-            const LnRow st = row_stats_in_registers<NCH, E, NT>(
+            const LnRow st = row_stats_in_registers<NCH, E, NT, true>(
                 v, cols, eps, slot[0], slot[1], [&](int k, int) { return ok[k]; }, &e, has_e);
             so.write(r, st);
             if constexpr (LDSW) {
