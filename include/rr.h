@@ -473,8 +473,9 @@ rr_status rr_splitk_attention_partials(const void* q, const void* k, const void*
  *                 empty sequence); a sequence may have no query or no key.
  *   o_part        device, float32 [P][total_q][heads][depth] (written)
  *   m_part, l_part  device, float32 [P][total_q][heads] (written)
- *   max_q_rows    at least the longest sequence's query count: query rows
- *                 of a sequence past max_q_rows are not computed
+ *   max_q_rows    the query rows computed per sequence, normally the
+ *                 longest sequence's count: a sequence's query rows past
+ *                 it are not computed (left unwritten)
  *   depth, P, scale  as rr_splitk_attention_partials;
  *                 heads * depth * 512 < 2^31;  total_q, total_k < 2^31
  * For sequence b its keys are cut into P contiguous partitions as

@@ -553,9 +553,10 @@ def splitk_attention_partials_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_q_
     """Split-K attention partials of sequences packed token after token: q bf16
     [total_q, heads, depth], k and v bf16 [total_k, kv_heads, depth], and int32
     GPU offsets cu_seqlens_q, cu_seqlens_k [batch + 1] (sequence b owns tokens
-    cu[b] .. cu[b+1] - 1 of each).  ``max_q_rows`` is at least the longest
-    sequence's query count (read by the host as given; the offsets stay on
-    the device).
+    cu[b] .. cu[b+1] - 1 of each).  ``max_q_rows``: the query rows computed
+    per sequence, normally the longest sequence's count (a sequence's rows
+    past it are left unwritten; read by the host as given, the offsets stay
+    on the device).
 
     Returns (o_part [P, total_q, heads, depth], m_part [P, total_q, heads],
     l_part [P, total_q, heads]) in float32; tokens outside every sequence are

@@ -33,6 +33,18 @@ int main(void)
     printf("empty softmax -> %d\n", (int)s);
     s = rr_splitk_lse_merge(NULL, NULL, NULL, NULL, 0, 4, 8, 1.0f, RR_BF16, NULL);
     printf("P=0 merge -> %d\n", (int)s);
+    s = rr_reduce_rows_noalloc(NULL, NULL, 4, 8, 4, RR_F32, RR_SUM, RR_TIER_AUTO, NULL);
+    printf("noalloc bad ld -> %d\n", (int)s);
+    s = rr_splitk_attention_partials_varlen(NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 2, 4, 2,
+                                            10, 10, 8, 64, 4, 0.125f, NULL);
+    printf("varlen without buffers -> %d\n", (int)s);
+    s = rr_splitk_attention_partials_varlen(NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 2, 4, 3,
+                                            10, 10, 8, 64, 4, 0.125f, NULL);
+    printf("varlen heads not a multiple of kv heads -> %d\n", (int)s);
+    size_t ws = 0, tickets = 0;
+    s = rr_splitk_attention_workspace_bytes(8, 32, 32, 128, 8192, 128, 8, &ws, &tickets);
+    printf("attention workspace %d %llu %llu\n", (int)s, (unsigned long long)ws,
+           (unsigned long long)tickets);
     printf("version %d\n", rr_version());
     return 0;
 }

@@ -57,6 +57,11 @@ def test_plain_c_consumer_compiles_links_and_runs(tmp_path):
     assert "axis tier=5 slices=2" in out
     assert "bad ld -> 2 (invalid shape" in out
     assert "empty softmax -> 0" in out and "P=0 merge -> 2" in out
+    assert "noalloc bad ld -> 2" in out
+    assert "varlen without buffers -> 1" in out
+    assert "varlen heads not a multiple of kv heads -> 2" in out
+    # one 4-byte ticket per (head, 128 query rows): 256 groups, 1024 bytes
+    assert re.search(r"attention workspace 0 \d+ 1024\b", out), out
 
 
 def test_status_strings_are_distinct():

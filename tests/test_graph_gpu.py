@@ -37,6 +37,13 @@ def test_graph_replays_match_eager_bit_for_bit():
     o, m, l = to_gpu(o), to_gpu(m), to_gpu(l)
     aq, ak, av = (to_gpu(a) for a in synth.attention(50, batch=1, heads=4, kv_heads=2, q_rows=130,
                                                      kv_len=777, depth=128))
+    # packed sequences (longest-first work order: 4 x 2 units per sequence)
+    vq, vk, vv, cq, ck = synth.attention_varlen(51, [130, 0, 77], [300, 20, 1000], 4, 2, 128, 1, 0)
+    vq, vk, vv, cq, ck = (to_gpu(a) for a in (vq, vk, vv, cq, ck))
+    # misaligned layernorm rows (odd stride) with weights staged in LDS
+    x_lnm = to_gpu(synth.normal_bf16(52, (1024, 4095)))
+    g_lnm = to_gpu(synth.uniform_f32(53, (4095,), 0.5, 1.5))
+    b_lnm = to_gpu(synth.uniform_f32(54, (4095,), -0.5, 0.5))
 
     outs = {
         "long_sum": torch.empty(16, device=dev),
@@ -53,7 +60,15 @@ def test_graph_replays_match_eager_bit_for_bit():
         "attn": {"o": torch.empty((4, 520, 128), device=dev), "m": torch.empty((4, 520), device=dev),
                  "l": torch.empty((4, 520), device=dev)},
         "attn_fused": torch.empty((1, 4, 130, 128), dtype=torch.bfloat16, device=dev),
+        "varlen": {"o": torch.empty((4, 208, 4, 128), device=dev),
+                   "m": torch.empty((4, 208, 4), device=dev), "l": torch.empty((4, 208, 4), device=dev)},
+        "ln_peel": torch.empty_like(x_lnm),
     }
+    # tokens of no sequence are never written: every output starts from the
+    # bytes each replay's scribble leaves
+    for v in outs.values():
+        for t in (v.values() if isinstance(v, dict) else (v,)):
+            t.view(torch.uint8).fill_(0x7F)
 
     def run_all():
         rr.reduce_rows(x_long, "sum", out=outs["long_sum"])
@@ -69,6 +84,10 @@ def test_graph_replays_match_eager_bit_for_bit():
         rr.splitk_attention_partials(aq, ak, av, 4, out=(outs["attn"]["o"], outs["attn"]["m"],
                                                          outs["attn"]["l"]))
         rr.splitk_attention(aq, ak, av, 4, out=outs["attn_fused"])
+        rr.splitk_attention_partials_varlen(vq, vk, vv, cq, ck, 130, 4,
+                                            out=(outs["varlen"]["o"], outs["varlen"]["m"],
+                                                 outs["varlen"]["l"]))
+        rr.layernorm_rows(x_lnm, g_lnm, b_lnm, 1e-5, out=outs["ln_peel"])
 
     def snapshot():
         flat = {}
