@@ -94,19 +94,9 @@ struct AttnStage {
 };
 
 template <int D>
-__device__ __forceinline__ int k_slot_byte(int row, int chunk)
-{
-    return row * D * 2 + 16 * (chunk ^ (row & (D / 8 - 1)));
-}
-template <int D>
 __device__ __forceinline__ int v_swz(int row)
 {
     return D == 128 ? (row & 3) << 2 : (row & 3) << 1;
-}
-template <int D>
-__device__ __forceinline__ int v_slot_byte(int row, int chunk)
-{
-    return row * D * 2 + 16 * (chunk ^ v_swz<D>(row));
 }
 
 // s_waitcnt on the vector-memory counter only (N < 16): expcnt and lgkmcnt
