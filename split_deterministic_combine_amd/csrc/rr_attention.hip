@@ -355,13 +355,15 @@ __global__ __launch_bounds__(kBlockThreads, (attn_workgroups_per_cu<D, FUSED>())
     int64_t g, kvl, b;
     if constexpr (RAGGED) {
         // Sequences of different lengths.  A unit of work is (sequence, kv
-        // head, partition); its q_tiles * group items share the unit's keys
-        // and run one after another on one XCD.  When a sequence's units
-        // divide evenly over the XCDs (and the batch fits the workgroup),
-        // XCD x takes units x, x + 8, ... of every sequence, the sequences
-        // in order of key count, most first (longest-processing-time
-        // order); else the sequence index varies fastest, so that every
-        // XCD's range of work still takes its share of each sequence.
+        // head, partition), numbered partition fastest; its q_tiles * group
+        // items share the unit's keys and run one after another on one XCD.
+        // When a sequence's units divide evenly over the XCDs (and the batch
+        // fits the workgroup), XCD x takes the x-th eighth of every
+        // sequence's units (whole kv heads where they divide, so a query
+        // tile's partitions meet its q in that XCD's L2), the sequences in
+        // order of key count, most first (longest-processing-time order);
+        // else the sequence index varies fastest, so that every XCD's range
+        // of work still takes its share of each sequence.
         __shared__ int32_t seq_slot;
         const int64_t inner = (int64_t)q_tiles * group;
         const int64_t per_seq = (int64_t)P * kv_heads;
@@ -370,7 +372,7 @@ __global__ __launch_bounds__(kBlockThreads, (attn_workgroups_per_cu<D, FUSED>())
         if (per_seq % kXcds == 0 && batch <= kBlockThreads) {
             const int64_t span = per_seq / kXcds * inner;  // a sequence's items on one XCD
             i = idx % inner;
-            unit = (idx % span) / inner * kXcds + xcd;
+            unit = xcd * (per_seq / kXcds) + (idx % span) / inner;
             b = attn_sequence_of_rank(idx / span, cu_k, batch, kv_len, &seq_slot);
         } else {
             i = w % inner;
