@@ -479,16 +479,16 @@ def main():
                             torch.empty((ap, tq, ah), device=dev), torch.empty((ap, tq, ah), device=dev))
     if not args.no_next:
         # odd-stride rows and their aligned neighbours, drawn on the device
-        # (standard normal, seeded); two sets each so consecutive launches
-        # touch more than the 256 MB of last-level cache
+        # (standard normal, seeded); three sets each, so that consecutive
+        # launches of one op touch well over the 256 MB of last-level cache
         gen = torch.Generator(device=dev)
         gen.manual_seed(9)
         for key, shape, dt in (("sum_47", (1048576, 47), torch.float32),
                                ("sum_1001", (65536, 1001), torch.float32),
                                ("sum_1000", (65536, 1000), torch.float32),
                                ("softmax_8191", (8192, 8191), torch.bfloat16)):
-            dx[key] = [torch.randn(shape, generator=gen, device=dev).to(dt) for _ in range(2)]
-        dx["softmax_8191_out"] = [torch.empty_like(dx["softmax_8191"][0]) for _ in range(2)]
+            dx[key] = [torch.randn(shape, generator=gen, device=dev).to(dt) for _ in range(3)]
+        dx["softmax_8191_out"] = [torch.empty_like(dx["softmax_8191"][0]) for _ in range(3)]
         dx["sum_47_out"] = torch.empty(1048576, device=dev)
         dx["sum_1001_out"] = torch.empty(65536, device=dev)
     y_short_sum = torch.empty(1048576, dtype=torch.float32, device=dev)
@@ -533,11 +533,11 @@ def main():
         # the partials of packed sequences of mixed key lengths
         "attention_varlen": lambda i: rr.splitk_attention_partials_varlen(
             *dx["varlen_qkv"], *dx["varlen_cu"], ATTN[2], ATTN[5], out=dx["varlen_out"]),
-        "sum_47": lambda i: rr.reduce_rows(dx["sum_47"][i % 2], "sum", out=dx["sum_47_out"]),
-        "sum_1001": lambda i: rr.reduce_rows(dx["sum_1001"][i % 2], "sum", out=dx["sum_1001_out"]),
-        "sum_1000": lambda i: rr.reduce_rows(dx["sum_1000"][i % 2], "sum", out=dx["sum_1001_out"]),
-        "softmax_8191": lambda i: rr.softmax_rows(dx["softmax_8191"][i % 2],
-                                                  out=dx["softmax_8191_out"][i % 2]),
+        "sum_47": lambda i: rr.reduce_rows(dx["sum_47"][i % 3], "sum", out=dx["sum_47_out"]),
+        "sum_1001": lambda i: rr.reduce_rows(dx["sum_1001"][i % 3], "sum", out=dx["sum_1001_out"]),
+        "sum_1000": lambda i: rr.reduce_rows(dx["sum_1000"][i % 3], "sum", out=dx["sum_1001_out"]),
+        "softmax_8191": lambda i: rr.softmax_rows(dx["softmax_8191"][i % 3],
+                                                  out=dx["softmax_8191_out"][i % 3]),
     }
     only = args.only.split(",") if args.only else None
     names = [n for n in ops if only is None or n in only]
@@ -689,9 +689,10 @@ def main():
     # reductions move the same bytes), so the choice does not flip between runs.
     if not names and next_names:
         # a profiling run of operations outside the step (under rocprofv3):
-        # each selected one launched warmup + steps times; nothing is timed
-        for i in range(args.warmup + args.steps):
-            for n in next_names:
+        # each selected one launched warmup + steps times in a row, as the
+        # next-row timing below runs them; nothing is timed
+        for n in next_names:
+            for i in range(args.warmup + args.steps):
                 next_ops[n](i)
         torch.cuda.synchronize()
         print(json.dumps({"profile_run": next_names, "launches_each": args.warmup + args.steps}))
@@ -737,23 +738,25 @@ def main():
                      "GBps": round(B[n] / (mean * 1e-3) / 1e9, 1),
                      "pct_peak": round(100 * B[n] / (mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 1),
                      "timed_in": "timed region" if n == dom else "instrumented pass"}
-    # Operations outside the step: each timed alone with HIP events on the stream.
+    # Operations outside the step: each timed alone with HIP events on the
+    # stream -- its warmup launches, then its timed launches in a row (every
+    # op rotates buffer sets larger than the last-level cache), before the
+    # next op starts.
     next_rows = {}
     if next_names:
         log("timing next-row operations")
-        for i in range(max(args.warmup, 1)):
-            for n in next_names:
-                next_ops[n](i)
         reps = max(K, 10)
         evs = {n: [] for n in next_names}
-        for i in range(reps):
-            for n in next_names:
+        for n in next_names:
+            for i in range(max(args.warmup, 1)):
+                next_ops[n](i)
+            for i in range(reps):
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record(stream)
                 next_ops[n](i)
                 b.record(stream)
                 evs[n].append((a, b))
-        torch.cuda.synchronize()
+            torch.cuda.synchronize()
         for n in next_names:
             ts = sorted(a.elapsed_time(b) for a, b in evs[n])
             mean = sum(ts) / len(ts)
