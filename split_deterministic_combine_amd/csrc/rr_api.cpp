@@ -121,7 +121,7 @@ static rr_status reduce_rows_common(const void* x, void* y, int64_t rows, int64_
 
     rr::ReduceLaunch a{x, y, rows, cols, ld, dtype, op, false, {nullptr, nullptr, nullptr}, vec,
                        rows_aligned16(x, ld, rows, 4), workspace,
-                       g_splitk_skew.load(std::memory_order_relaxed), as_stream(stream)};
+                       g_splitk_skew.load(std::memory_order_relaxed), as_stream(stream), cu};
     if (cols == 0) return rr::launch_reduce_identity(a);
     if (p.tier == RR_TIER_SPLITK) {
         if (noalloc) {

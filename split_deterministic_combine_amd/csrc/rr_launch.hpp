@@ -23,6 +23,7 @@ struct ReduceLaunch {
     void* workspace;      // split-K only
     int skew;             // test hook: split-K arrival skew (0 = off)
     hipStream_t stream;
+    int32_t cu = 0;       // compute units the plan was made for (block tier: persistent rows)
 };
 
 struct SoftmaxLaunch {

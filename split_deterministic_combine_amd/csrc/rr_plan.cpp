@@ -84,6 +84,13 @@ static void fill_rowwise_geometry(rr_tier tier, int64_t rows, int64_t cols, int 
     if (p->grid > kMaxGrid) p->grid = kMaxGrid;
 }
 
+RowPfShape reduce_pf_shape(int64_t rows, int64_t cols, rr_op op, int32_t cu_count, bool vec)
+{
+    if (!vec || op == RR_SUM_MAX_MIN || cols < 1 || rows < kReducePfMinRowsPerCU * cu_count)
+        return RowPfShape{0, 0};
+    return row_pf_shape(ceil_div(cols, 4));
+}
+
 rr_status plan_reduce(int64_t rows, int64_t cols, int64_t ld, rr_dtype dtype, rr_op op,
                       rr_tier tier, int32_t cu_count, bool vec, rr_plan* out)
 {
@@ -103,6 +110,13 @@ rr_status plan_reduce(int64_t rows, int64_t cols, int64_t ld, rr_dtype dtype, rr
         // the wave tier takes 128-bit chunks for rows of at least 7 elements
         // (every row then has a whole chunk after its head)
         fill_rowwise_geometry(t, rows, cols, t == RR_TIER_WAVE && cols < 7 ? 1 : vec_elems, out);
+        const RowPfShape sh = reduce_pf_shape(rows, cols, op, cu_count, vec);
+        if (t == RR_TIER_BLOCK && sh.nt > 0) {
+            // persistent rows: workgroups sized to the row, grid sized to the CUs
+            out->block = sh.nt;
+            const int64_t g = (int64_t)cu_count * row_pf_blocks_per_cu(sh, kReducePfLoadsPerCU);
+            out->grid = rows < g ? rows : g;
+        }
         return RR_OK;
     }
     fill_splitk_geometry(rows, cols, (int64_t)kSplitKUnroll * kBlockThreads * vec_elems, cu_count,

@@ -19,6 +19,8 @@
 #include "rr_device.hpp"
 #include "rr_launch.hpp"
 #include "rr_launch_util.hpp"
+#include "rr_plan.hpp"
+#include "rr_rowio.hpp"
 
 namespace rr {
 
@@ -115,6 +117,102 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce_block(
         if (threadIdx.x == 0)
             M::store(y, r, acc);
     }
+}
+
+// ------------------------------------- block tier, persistent rows
+// Rows that fit a workgroup's registers (row_pf_shape: NT threads, NCH
+// 16-byte chunks each), on a persistent grid: workgroup b takes rows b,
+// b + grid, ... and loads the next row while it folds the current one
+// (persistent_rows).  Each row's body, from its first 16-byte boundary, sits
+// in chunk slots rotated onto 128-byte lines (slot_chunk), so every load
+// instruction covers whole lines; PEEL: the head and tail elements (rows that
+// do not all start 16-byte aligned or do not end on a chunk) one to each of
+// the first threads, in their own element load through the same buffer
+// descriptor.  Chunks past the body read nothing (an offset past the
+// descriptor's range) and are dropped from the fold as a whole.
+template <int NCH>
+struct ReduceRowBuf {
+    uint4 c[NCH];
+    uint32_t e;
+};
+
+template <class M>
+__device__ __forceinline__ typename M::acc_t lift_bits(uint32_t u)
+{
+    if constexpr (std::is_same<typename M::in_t, float>::value)
+        return M::lift(__uint_as_float(u));
+    else
+        return M::lift((typename M::in_t)u);
+}
+
+template <class M, int NCH, int NT, bool PEEL>
+__global__ __launch_bounds__(NT) void k_reduce_rows_pf(const typename M::in_t* __restrict__ x,
+                                                       typename M::out_t y, int64_t rows,
+                                                       int64_t cols, int64_t ld)
+{
+    using T = typename M::in_t;
+    using A = typename M::acc_t;
+    static_assert(sizeof(T) == 4, "4-byte elements");
+    __shared__ A slot[2][NT / kWave > 1 ? NT / kWave : 1];
+    if ((int64_t)blockIdx.x >= rows)
+        return;
+    const int row_bytes = (int)(cols * 4);
+    persistent_rows<ReduceRowBuf<NCH>>(
+        blockIdx.x, gridDim.x, rows,
+        [&](int64_t r, bool live, ReduceRowBuf<NCH>& buf) {
+            const T* xr = x + r * ld;
+            const int64_t h = PEEL ? head_elems(xr, cols) : 0;
+            const int nbe = (int)((cols - h) & ~(int64_t)3);
+            const int bytes = live ? row_bytes : 0;
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<T*>(xr), 0, bytes, kBufferWord3);
+            const int q = line_phase(xr + h);
+#pragma unroll
+            for (int k = 0; k < NCH; ++k) {
+                const int off = slot_chunk<NCH, NT, true>(k, q) * 16;
+                const int o = off + 16 <= nbe * 4 ? (int)h * 4 + off : bytes + 16;
+                const rr_u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, o, 0,
+                                                                          kBufferNonTemporal);
+                buf.c[k] = make_uint4(v.x, v.y, v.z, v.w);
+            }
+            if constexpr (PEEL) {
+                // thread t < h: head element t; h <= t < h + tail: element nbe + t
+                const int64_t t = threadIdx.x, tl = cols - h - nbe;
+                const int64_t idx = t < h ? t : t < h + tl ? nbe + t : -1;
+                const int eo = idx >= 0 ? (int)idx * 4 : bytes + 16;
+                buf.e = __builtin_amdgcn_raw_buffer_load_b32(rs, eo, 0, kBufferNonTemporal);
+            }
+        },
+        [] {},
+        [&](const ReduceRowBuf<NCH>& buf, int64_t r, int par) {
+            const T* xr = x + r * ld;
+            const int64_t h = PEEL ? head_elems(xr, cols) : 0;
+            const int64_t nb = (cols - h) >> 2;
+            const int q = line_phase(xr + h);
+            A acc = M::identity();
+#pragma unroll
+            for (int k = 0; k < NCH; ++k) {
+                const uint4 u = buf.c[k];
+                A ck = lift_bits<M>(u.x);
+                ck = M::combine(ck, lift_bits<M>(u.y));
+                ck = M::combine(ck, lift_bits<M>(u.z));
+                ck = M::combine(ck, lift_bits<M>(u.w));
+                acc = (int64_t)slot_chunk<NCH, NT, true>(k, q) < nb ? M::combine(acc, ck) : acc;
+            }
+            if constexpr (PEEL) {
+                const int64_t t = threadIdx.x, tl = cols - h - (nb << 2);
+                if (t < h + tl)
+                    acc = M::combine(acc, lift_bits<M>(buf.e));
+            }
+            // every thread issues the result's store, thread 0's in range
+            // (a store behind a branch would make the loop's waits count it)
+            const typename M::in_t res = M::finish(block_reduce<M, NT>(acc, slot[par]));
+            uint32_t bits;
+            __builtin_memcpy(&bits, &res, 4);
+            const __amdgpu_buffer_rsrc_t ry =
+                __builtin_amdgcn_make_buffer_rsrc(y + r, 0, 4, kBufferWord3);
+            __builtin_amdgcn_raw_buffer_store_b32(bits, ry, threadIdx.x == 0 ? 0 : 16, 0, 0);
+        });
 }
 
 // ------------------------------------------------------------- wave tier
@@ -570,6 +668,39 @@ static rr_status launch_wave(dim3 grid, dim3 block, hipStream_t s, const typenam
     return launch_kernel(k_reduce_wave<M, 4, S, kPeelElements>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld);
 }
 
+// Block tier, persistent rows: the plan's grid, lowered to the workgroups
+// that can be resident at once.
+template <class M, int NCH, int NT>
+static rr_status launch_rows_pf(const rr_plan& p, const ReduceLaunch& a)
+{
+    const auto* x = static_cast<const typename M::in_t*>(a.x);
+    const auto y = static_cast<typename M::out_t>(a.y);
+    auto kernel = a.rows16 && a.cols % 4 == 0 ? k_reduce_rows_pf<M, NCH, NT, false>
+                                              : k_reduce_rows_pf<M, NCH, NT, true>;
+    int per_cu = 0;
+    if (blocks_per_cu(kernel, NT, &per_cu) != RR_OK)
+        return RR_ERR_HIP;
+    const int64_t cap = (int64_t)per_cu * a.cu;
+    const dim3 grid((unsigned)(p.grid < cap ? p.grid : cap));
+    return launch_kernel(kernel, grid, dim3(NT), 0, a.stream, x, y, a.rows, a.cols, a.ld);
+}
+
+template <class M>
+static rr_status launch_rows_pf_shape(const rr_plan& p, const ReduceLaunch& a, RowPfShape sh)
+{
+    if (sh.nt != p.block)
+        return RR_ERR_TIER;  // plan and launch disagree: refuse, launch nothing
+    switch (sh.nt * 16 + sh.nch) {
+    case 64 * 16 + 1: return launch_rows_pf<M, 1, 64>(p, a);
+    case 64 * 16 + 2: return launch_rows_pf<M, 2, 64>(p, a);
+    case 64 * 16 + 4: return launch_rows_pf<M, 4, 64>(p, a);
+    case 128 * 16 + 4: return launch_rows_pf<M, 4, 128>(p, a);
+    case 256 * 16 + 4: return launch_rows_pf<M, 4, 256>(p, a);
+    case 512 * 16 + 4: return launch_rows_pf<M, 4, 512>(p, a);
+    default: return RR_ERR_TIER;
+    }
+}
+
 template <class M>
 static rr_status launch_monoid(const rr_plan& p, const ReduceLaunch& a)
 {
@@ -581,6 +712,11 @@ static rr_status launch_monoid(const rr_plan& p, const ReduceLaunch& a)
     const hipStream_t s = a.stream;
     switch (p.tier) {
     case RR_TIER_BLOCK:
+        if constexpr (std::is_pointer<typename M::out_t>::value) {
+            const RowPfShape sh = reduce_pf_shape(a.rows, a.cols, a.op, a.cu, a.vec);
+            if (sh.nt > 0 && a.cu > 0)
+                return launch_rows_pf_shape<M>(p, a, sh);
+        }
         return !a.vec ? launch_kernel(k_reduce_block<M, 1, false>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld)
                : a.rows16 ? launch_kernel(k_reduce_block<M, 4, false>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld)
                           : launch_kernel(k_reduce_block<M, 4, true>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld);

@@ -109,6 +109,37 @@ def test_reduce_splitk_shapes(rows, cols):
             _check_reduce(_run_reduce(x, op, tier), ref, dtype, op, "%dx%d %s" % (rows, cols, tier))
 
 
+# Block tier on persistent rows: calls with at least 4 rows per CU whose rows
+# fit a workgroup's registers (up to 2048 16-byte chunks) walk several rows
+# per workgroup with the next row's loads in flight; every row shape, aligned,
+# strided and starting at every element offset.
+PF_REDUCE_SHAPES = [  # rows, cols, pad, offset
+    (20000, 65, 0, 0), (20000, 100, 0, 1), (20000, 256, 0, 0), (20000, 257, 2, 3),
+    (5000, 1000, 0, 0), (5000, 1001, 0, 0), (3000, 2048, 4, 0), (1100, 4095, 0, 2),
+    (1030, 8192, 0, 0), (1030, 8191, 1, 1)]
+
+
+def _pf_threads(cols):
+    chunks = -(-cols // 4)
+    return 64 if chunks <= 256 else 128 if chunks <= 512 else 256 if chunks <= 1024 else 512
+
+
+@pytest.mark.parametrize("rows,cols,pad,offset", PF_REDUCE_SHAPES)
+def test_reduce_block_tier_persistent_rows(rows, cols, pad, offset):
+    cu = rr.device_cu_count()
+    plan = rr.plan_reduce(rows, cols, cu_count=cu, tier="block")
+    assert rows >= 4 * cu and plan["block"] == _pf_threads(cols), plan
+    assert plan["grid"] < rows, plan                      # every workgroup walks several rows
+    for dtype, op in REDUCE_OPS:
+        x = _make_reduce_input(dtype, rows, cols, rows + 3 * cols + offset)
+        ref = oracle.reduce_rows(x, op)
+        first = _run_reduce(x, op, "block", pad, offset)
+        _check_reduce(first, ref, dtype, op, "%dx%d pad %d off %d %s" % (rows, cols, pad, offset, op))
+        again = _run_reduce(x, op, "auto" if cols > 64 else "block", pad, offset)
+        if rr.plan_reduce(rows, cols, cu_count=cu)["tier"] == "block":
+            assert np.array_equal(first.view(np.int32), again.view(np.int32)), (rows, cols, op)
+
+
 def test_splitk_with_one_slice_equals_block_tier_bitwise():
     for cols in (100, 1000, 4097, 16384):
         x = synth.uniform_f32(cols, (40, cols))
