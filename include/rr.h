@@ -101,7 +101,7 @@ typedef enum { RR_SUM = 0, RR_MAX = 1, RR_MIN = 2, RR_SUM_MAX_MIN = 3 } rr_op;
 typedef enum {
     RR_TIER_AUTO = 0,   /* pick by the rule documented at rr_plan_reduce */
     RR_TIER_WAVE = 1,   /* a group of lanes of one 64-wide wavefront per row (cols <= 64) */
-    RR_TIER_BLOCK = 2,  /* one workgroup per row, strided 128-bit loads */
+    RR_TIER_BLOCK = 2,  /* a workgroup per row at a time, strided 128-bit loads */
     RR_TIER_TILED = 3,  /* one thread owns RR_TILED_ROWS adjacent rows, no cross-thread combine */
     RR_TIER_SERIAL = 4, /* one thread per row, element by element */
     RR_TIER_SPLITK = 5  /* several workgroups per row, rank-order fold of partials */
@@ -148,6 +148,12 @@ typedef struct {
  *   WAVE    if cols <= 64
  *   BLOCK   otherwise
  * SERIAL is used only when forced.  WAVE is legal for cols <= 64 only.
+ * BLOCK with at least 4 * cu_count rows of c <= 2048 16-byte chunks and a
+ * single statistic: persistent workgroups sized to the row -- 64 threads
+ * with n = 1, 2 or 4 chunks each for c <= 64, 128 or 256, then 128, 256 and
+ * 512 threads with n = 4 for c <= 512, 1024 and 2048 -- and grid =
+ * min(rows, cu_count * max(1, 64 / (block / 64 * n))); otherwise one
+ * workgroup of 256 threads per row.
  * SPLITK: G = clamp(ceil(2*cu_count/rows), 1, min(256, ceil(cols/16384), tiles))
  * with tiles = ceil(cols / tile_cols), tile_cols = 8192 (2048 on the scalar path).
  * Workspace: rows * 4 ticket bytes padded to 256, then rows * G partials of 8
