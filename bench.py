@@ -77,8 +77,8 @@ KERNEL_OF_OP = {
     "attention_varlen": "k_attn_staged<128, 32, 3, false, float, true>",
     # rows at every offset from a 16-byte boundary and their aligned neighbour
     "sum_47": "k_reduce_wave<rr::SumF32, 4, 16, 2>",
-    "sum_1001": "k_reduce_block<rr::SumF32, 4, true>",
-    "sum_1000": "k_reduce_block<rr::SumF32, 4, false>",
+    "sum_1001": "k_reduce_rows_pf<rr::SumF32, 4, 64, true>",
+    "sum_1000": "k_reduce_rows_pf<rr::SumF32, 4, 64, false>",
     "softmax_8191": "k_softmax_rows_pf<unsigned short, unsigned short, 4, 256, false, true, true>",
     # reference streams of known size (not ops of the step): rr_test_stream;
     # launches of one kernel at two sizes are told apart by their bytes
@@ -838,8 +838,10 @@ def main():
                     next_rows[n]["frac_of_neighbour"] = round(next_rows[n]["GBps"] / ref["GBps"], 4)
         for n, cfg in (("sum_47", "f32 row sum [1048576, 47] (row stride 47: rows at every "
                                   "offset from a 16-byte boundary), wave tier"),
-                       ("sum_1001", "f32 row sum [65536, 1001] (odd row stride), block tier"),
-                       ("sum_1000", "f32 row sum [65536, 1000] (aligned rows), block tier"),
+                       ("sum_1001", "f32 row sum [65536, 1001] (odd row stride), block tier, "
+                                    "persistent rows"),
+                       ("sum_1000", "f32 row sum [65536, 1000] (aligned rows), block tier, "
+                                    "persistent rows"),
                        ("softmax_8191", "bf16 softmax [8192, 8191] -> bf16 (odd row stride), "
                                         "block tier, persistent rows")):
             if n in next_rows:
