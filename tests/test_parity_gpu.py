@@ -116,7 +116,9 @@ def test_reduce_splitk_shapes(rows, cols):
 PF_REDUCE_SHAPES = [  # rows, cols, pad, offset
     (20000, 65, 0, 0), (20000, 100, 0, 1), (20000, 256, 0, 0), (20000, 257, 2, 3),
     (5000, 1000, 0, 0), (5000, 1001, 0, 0), (3000, 2048, 4, 0), (1100, 4095, 0, 2),
-    (1030, 8192, 0, 0), (1030, 8191, 1, 1)]
+    (1030, 8192, 0, 0), (1030, 8191, 1, 1),
+    # rows shorter than a chunk (head and tail elements only), forced to the block tier
+    (20000, 1, 0, 1), (20000, 3, 1, 2), (20000, 5, 0, 3), (20000, 7, 2, 1)]
 
 
 def _pf_threads(cols):
