@@ -77,7 +77,7 @@ static void fill_rowwise_geometry(rr_tier tier, int64_t rows, int64_t cols, int 
     case RR_TIER_SERIAL:
         p->grid = ceil_div(rows, (int64_t)kBlockThreads);
         break;
-    default:  // BLOCK: one workgroup per row
+    default:  // BLOCK: one workgroup per row (persistent rows set their own grid)
         p->grid = rows;
         break;
     }
