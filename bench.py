@@ -32,6 +32,7 @@ the stream the kernels are launched on.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
 import argparse
+import gc
 import hashlib
 import json
 import math
@@ -700,6 +701,9 @@ def main():
     log("warmup %d steps" % args.warmup)
     if not names:
         sys.exit("bench.py: --only selected no operation of the step")
+    # no garbage-collection pause of the host may hold back the launches the
+    # HIP events time (the launches run at most a few steps ahead of it)
+    gc.disable()
     instrumented(max(args.warmup, 1), 0)
     dom = max(names, key=lambda n: (B[n], -names.index(n)))
 
@@ -932,6 +936,7 @@ def main():
 
     # ------------------------------------------------------------ CPU baseline
     cpu = None
+    gc.enable()  # the GPU timing is over
     if not args.no_cpu_baseline:
         import oracle
 
