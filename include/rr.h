@@ -148,8 +148,8 @@ typedef struct {
  *   WAVE    if cols <= 64
  *   BLOCK   otherwise
  * SERIAL is used only when forced.  WAVE is legal for cols <= 64 only.
- * BLOCK with at least 4 * cu_count rows of c <= 2048 16-byte chunks and a
- * single statistic: persistent workgroups sized to the row -- 64 threads
+ * BLOCK with at least 4 * cu_count rows of c <= 2048 16-byte chunks (also
+ * for RR_SUM_MAX_MIN): persistent workgroups sized to the row -- 64 threads
  * with n = 1, 2 or 4 chunks each for c <= 64, 128 or 256, then 128, 256 and
  * 512 threads with n = 4 for c <= 512, 1024 and 2048 -- and grid =
  * min(rows, cu_count * max(1, 64 / (block / 64 * n))); otherwise one

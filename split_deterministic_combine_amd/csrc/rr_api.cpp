@@ -176,7 +176,7 @@ extern "C" rr_status rr_reduce_rows_multi(const void* x, void* y_sum, void* y_ma
         return st;
     rr::ReduceLaunch a{x, nullptr, rows, cols, ld, dtype, RR_SUM, true, {y_sum, y_max, y_min},
                        vec, rows_aligned16(x, ld, rows, 4), workspace,
-                       g_splitk_skew.load(std::memory_order_relaxed), as_stream(stream)};
+                       g_splitk_skew.load(std::memory_order_relaxed), as_stream(stream), cu};
     if (cols == 0) return rr::launch_reduce_identity(a);
     if (p.tier == RR_TIER_SPLITK) {
         if (!workspace || workspace_bytes < p.workspace_bytes || !aligned(workspace, 8))

@@ -190,6 +190,13 @@ struct MultiF32 {
         return acc_t{a.sum + b.sum, a.maxk > b.maxk ? a.maxk : b.maxk,
                      a.mink < b.mink ? a.mink : b.mink};
     }
+    // the three results, in the order sum, max, min
+    __device__ static void finish3(acc_t a, float* o)
+    {
+        o[0] = (float)a.sum;
+        o[1] = f32_from_order_key(a.maxk);
+        o[2] = f32_from_order_key(a.mink);
+    }
     __device__ static void store(out_t y, int64_t r, acc_t a)
     {
         if (y.sum) y.sum[r] = (float)a.sum;
@@ -209,6 +216,12 @@ struct MultiI32 {
     __device__ static acc_t combine(acc_t a, acc_t b)
     {
         return acc_t{a.sum + b.sum, a.max > b.max ? a.max : b.max, a.min < b.min ? a.min : b.min};
+    }
+    __device__ static void finish3(acc_t a, int32_t* o)
+    {
+        o[0] = (int32_t)a.sum;
+        o[1] = a.max;
+        o[2] = a.min;
     }
     __device__ static void store(out_t y, int64_t r, acc_t a)
     {

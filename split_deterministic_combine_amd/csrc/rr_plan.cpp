@@ -86,7 +86,8 @@ static void fill_rowwise_geometry(rr_tier tier, int64_t rows, int64_t cols, int 
 
 RowPfShape reduce_pf_shape(int64_t rows, int64_t cols, rr_op op, int32_t cu_count, bool vec)
 {
-    if (!vec || op == RR_SUM_MAX_MIN || cols < 1 || rows < kReducePfMinRowsPerCU * cu_count)
+    (void)op;  // every statistic, the three-statistic tuple too
+    if (!vec || cols < 1 || rows < kReducePfMinRowsPerCU * cu_count)
         return RowPfShape{0, 0};
     return row_pf_shape(ceil_div(cols, 4));
 }

@@ -10,8 +10,8 @@ namespace rr {
 rr_status plan_reduce(int64_t rows, int64_t cols, int64_t ld, rr_dtype dtype, rr_op op,
                       rr_tier tier, int32_t cu_count, bool vec, rr_plan* out);
 // The block tier's persistent-row shape for a row reduction (nt == 0: one
-// workgroup per row): element-aligned rows that fit row_pf_shape, a single
-// statistic, and at least kReducePfMinRowsPerCU rows per CU.
+// workgroup per row): element-aligned rows that fit row_pf_shape and at least
+// kReducePfMinRowsPerCU rows per CU.
 RowPfShape reduce_pf_shape(int64_t rows, int64_t cols, rr_op op, int32_t cu_count, bool vec);
 // vec: x (and y) are aligned to their element size, so the block and split-K
 // tiers take each row's body from its first 16-byte boundary in 128-bit

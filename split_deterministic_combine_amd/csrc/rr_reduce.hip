@@ -145,6 +145,37 @@ __device__ __forceinline__ typename M::acc_t lift_bits(uint32_t u)
         return M::lift((typename M::in_t)u);
 }
 
+// Row r's result(s) stored by every thread, thread 0's store in range and
+// the others' past it (a store behind a branch would make the persistent
+// loop's waits count it); the three statistics' outputs may be NULL (range 0).
+__device__ __forceinline__ void store_word(void* p, uint32_t bits, bool on)
+{
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(p, 0, on ? 4 : 0,
+                                                                        kBufferWord3);
+    __builtin_amdgcn_raw_buffer_store_b32(bits, rs, threadIdx.x == 0 ? 0 : 16, 0, 0);
+}
+template <class M>
+__device__ __forceinline__ void store_row_result(typename M::out_t y, int64_t r,
+                                                 typename M::acc_t a)
+{
+    using T = typename M::in_t;
+    uint32_t bits;
+    if constexpr (std::is_pointer<typename M::out_t>::value) {
+        const T res = M::finish(a);
+        __builtin_memcpy(&bits, &res, 4);
+        store_word(y + r, bits, true);
+    } else {
+        T res[3];
+        M::finish3(a, res);
+        T* outs[3] = {y.sum, y.max, y.min};
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            __builtin_memcpy(&bits, &res[i], 4);
+            store_word(outs[i] ? outs[i] + r : nullptr, bits, outs[i] != nullptr);
+        }
+    }
+}
+
 template <class M, int NCH, int NT, bool PEEL>
 __global__ __launch_bounds__(NT) void k_reduce_rows_pf(const typename M::in_t* __restrict__ x,
                                                        typename M::out_t y, int64_t rows,
@@ -204,14 +235,7 @@ __global__ __launch_bounds__(NT) void k_reduce_rows_pf(const typename M::in_t* _
                 if (t < h + tl)
                     acc = M::combine(acc, lift_bits<M>(buf.e));
             }
-            // every thread issues the result's store, thread 0's in range
-            // (a store behind a branch would make the loop's waits count it)
-            const typename M::in_t res = M::finish(block_reduce<M, NT>(acc, slot[par]));
-            uint32_t bits;
-            __builtin_memcpy(&bits, &res, 4);
-            const __amdgpu_buffer_rsrc_t ry =
-                __builtin_amdgcn_make_buffer_rsrc(y + r, 0, 4, kBufferWord3);
-            __builtin_amdgcn_raw_buffer_store_b32(bits, ry, threadIdx.x == 0 ? 0 : 16, 0, 0);
+            store_row_result<M>(y, r, block_reduce<M, NT>(acc, slot[par]));
         });
 }
 
@@ -670,11 +694,14 @@ static rr_status launch_wave(dim3 grid, dim3 block, hipStream_t s, const typenam
 
 // Block tier, persistent rows: the plan's grid, lowered to the workgroups
 // that can be resident at once.
+template <class M>
+static typename M::out_t outputs_of(const ReduceLaunch& a);
+
 template <class M, int NCH, int NT>
 static rr_status launch_rows_pf(const rr_plan& p, const ReduceLaunch& a)
 {
     const auto* x = static_cast<const typename M::in_t*>(a.x);
-    const auto y = static_cast<typename M::out_t>(a.y);
+    const typename M::out_t y = outputs_of<M>(a);
     auto kernel = a.rows16 && a.cols % 4 == 0 ? k_reduce_rows_pf<M, NCH, NT, false>
                                               : k_reduce_rows_pf<M, NCH, NT, true>;
     int per_cu = 0;
@@ -711,12 +738,12 @@ static rr_status launch_monoid(const rr_plan& p, const ReduceLaunch& a)
     const dim3 grid((unsigned)p.grid), block(kBlockThreads);
     const hipStream_t s = a.stream;
     switch (p.tier) {
-    case RR_TIER_BLOCK:
-        if constexpr (std::is_pointer<typename M::out_t>::value) {
-            const RowPfShape sh = reduce_pf_shape(a.rows, a.cols, a.op, a.cu, a.vec);
-            if (sh.nt > 0 && a.cu > 0)
-                return launch_rows_pf_shape<M>(p, a, sh);
-        }
+    case RR_TIER_BLOCK: {
+        const RowPfShape sh =
+            reduce_pf_shape(a.rows, a.cols, a.multi ? RR_SUM_MAX_MIN : a.op, a.cu, a.vec);
+        if (sh.nt > 0 && a.cu > 0)
+            return launch_rows_pf_shape<M>(p, a, sh);
+    }
         return !a.vec ? launch_kernel(k_reduce_block<M, 1, false>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld)
                : a.rows16 ? launch_kernel(k_reduce_block<M, 4, false>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld)
                           : launch_kernel(k_reduce_block<M, 4, true>, grid, block, 0, s, x, y, a.rows, a.cols, a.ld);

@@ -70,7 +70,7 @@ def test_plain_c_consumer_compiles_links_and_runs(tmp_path):
     (20000, 65, "min", 64, 16384),        # 17 chunks: 64 threads x 1, 64 per CU
     (1023, 1000, "sum", 256, 1023),       # fewer than 4 rows per CU: a workgroup per row
     (65536, 8193, "sum", 256, 65536),     # beyond 2048 chunks
-    (65536, 1000, "sum_max_min", 256, 65536),  # three statistics: a workgroup per row
+    (65536, 1000, "sum_max_min", 64, 4096),   # the three statistics alike
 ])
 def test_block_tier_reduce_persistent_plan(rows, cols, op, block, grid):
     p = rr.plan_reduce(rows, cols, torch.float32, op, cu_count=256)

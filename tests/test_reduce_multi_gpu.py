@@ -84,6 +84,35 @@ def test_multi_strided_and_misaligned_rows(pad, offset):
             _check(name, "f32", to_host(got[name]), x, "strided %s %s" % (name, tier))
 
 
+@pytest.mark.parametrize("rows,cols,pad,offset", [(5000, 1000, 0, 0), (5000, 1001, 0, 0),
+                                                   (3000, 2048, 4, 1), (20000, 65, 0, 3)])
+@pytest.mark.parametrize("dt", ["f32", "i32"])
+def test_multi_block_tier_persistent_rows(rows, cols, pad, offset, dt):
+    # at least 4 rows per CU: persistent workgroups walk several rows; each
+    # output equals the single-op kernel's bits, unrequested ones stay as
+    # they were
+    cu = rr.device_cu_count()
+    plan = rr.plan_reduce(rows, cols, torch.float32 if dt == "f32" else torch.int32,
+                          "sum_max_min", "block", cu_count=cu)
+    assert plan["grid"] < rows, plan
+    x = _input(dt, rows, cols, 1450 + cols + offset)
+    big = np.zeros((rows, cols + pad + offset), dtype=x.dtype)
+    big[:, offset:offset + cols] = x
+    g = to_gpu(big)[:, offset:offset + cols]
+    got = rr.reduce_rows_multi(g, tier="block")
+    for name in ("sum", "max", "min"):
+        single = rr.reduce_rows(g, name, "block")
+        what = "%s %s %dx%d pad %d off %d" % (dt, name, rows, cols, pad, offset)
+        assert torch.equal(got[name].view(torch.int32), single.view(torch.int32)), what
+        _check(name, dt, to_host(got[name]), x, what)
+    fill = 12345 if dt == "i32" else 12345.0
+    sentinel = {k: torch.full((rows,), fill, dtype=got["sum"].dtype, device="cuda")
+                for k in ("sum", "max", "min")}
+    part = rr.reduce_rows_multi(g, ("min",), tier="block", out=dict(sentinel))
+    assert torch.equal(part["min"].view(torch.int32), got["min"].view(torch.int32))
+    assert torch.all(sentinel["sum"] == fill) and torch.all(sentinel["max"] == fill)
+
+
 def test_multi_special_values_total_order():
     x = np.array([[-0.0, 0.0, -0.0, 1.0, -1.0] * 12,
                   [np.nan, 1.0, -np.inf, np.inf, 2.0] * 12,
