@@ -149,11 +149,14 @@ typedef struct {
  *   BLOCK   otherwise
  * SERIAL is used only when forced.  WAVE is legal for cols <= 64 only.
  * BLOCK with at least 4 * cu_count rows of c <= 2048 16-byte chunks (also
- * for RR_SUM_MAX_MIN): persistent workgroups sized to the row -- 64 threads
- * with n = 1, 2 or 4 chunks each for c <= 64, 128 or 256, then 128, 256 and
- * 512 threads with n = 4 for c <= 512, 1024 and 2048 -- and grid =
- * min(rows, cu_count * max(1, 64 / (block / 64 * n))); otherwise one
- * workgroup of 256 threads per row.
+ * for RR_SUM_MAX_MIN): persistent workgroups sized to the row, n = 4 chunks
+ * per thread -- a wavefront over 4 rows of 16 lanes (lanes_per_row = 16) for
+ * c <= 64 or over 2 rows of 32 lanes for c <= 128 (when 3 or 1 row strides
+ * plus the row stay below 2^31 bytes; else one row of 64 lanes), 64 threads
+ * for c <= 256, then 128, 256 and 512 threads for c <= 512, 1024 and 2048 --
+ * and grid = min(steps, cu_count * max(1, 64 / (block / 64 * n))), steps =
+ * rows divided by the rows per step, rounded up; otherwise one workgroup of
+ * 256 threads per row.
  * SPLITK: G = clamp(ceil(2*cu_count/rows), 1, min(256, ceil(cols/16384), tiles))
  * with tiles = ceil(cols / tile_cols), tile_cols = 8192 (2048 on the scalar path).
  * Workspace: rows * 4 ticket bytes padded to 256, then rows * G partials of 8

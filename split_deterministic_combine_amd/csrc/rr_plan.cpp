@@ -89,7 +89,19 @@ RowPfShape reduce_pf_shape(int64_t rows, int64_t cols, rr_op op, int32_t cu_coun
     (void)op;  // every statistic, the three-statistic tuple too
     if (!vec || cols < 1 || rows < kReducePfMinRowsPerCU * cu_count)
         return RowPfShape{0, 0};
-    return row_pf_shape(ceil_div(cols, 4));
+    const int64_t chunks = ceil_div(cols, 4);
+    // up to 128 chunks: a wavefront of 4 chunks per lane over 2 or 4 rows
+    return chunks <= 128 ? RowPfShape{64, 4} : row_pf_shape(chunks);
+}
+
+int reduce_pf_lanes(int64_t cols, int64_t ld)
+{
+    const int64_t chunks = ceil_div(cols, 4);
+    const int lanes = chunks <= 64 ? 16 : chunks <= 128 ? 32 : 0;
+    // a step's rows share one buffer descriptor: its bytes must stay below 2^31
+    if (lanes && ((int64_t)(64 / lanes - 1) * ld + cols) * 4 + 64 > (int64_t)INT32_MAX)
+        return 0;
+    return lanes;
 }
 
 rr_status plan_reduce(int64_t rows, int64_t cols, int64_t ld, rr_dtype dtype, rr_op op,
@@ -113,10 +125,14 @@ rr_status plan_reduce(int64_t rows, int64_t cols, int64_t ld, rr_dtype dtype, rr
         fill_rowwise_geometry(t, rows, cols, t == RR_TIER_WAVE && cols < 7 ? 1 : vec_elems, out);
         const RowPfShape sh = reduce_pf_shape(rows, cols, op, cu_count, vec);
         if (t == RR_TIER_BLOCK && sh.nt > 0) {
-            // persistent rows: workgroups sized to the row, grid sized to the CUs
+            // persistent rows: workgroups sized to the row (or a wavefront
+            // over 2 or 4 short rows), grid sized to the CUs
+            const int lanes = reduce_pf_lanes(cols, ld);
+            const int64_t steps = lanes ? ceil_div(rows, (int64_t)(sh.nt / lanes)) : rows;
             out->block = sh.nt;
+            out->lanes_per_row = lanes;
             const int64_t g = (int64_t)cu_count * row_pf_blocks_per_cu(sh, kReducePfLoadsPerCU);
-            out->grid = rows < g ? rows : g;
+            out->grid = steps < g ? steps : g;
         }
         return RR_OK;
     }

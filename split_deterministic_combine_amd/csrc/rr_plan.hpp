@@ -13,6 +13,10 @@ rr_status plan_reduce(int64_t rows, int64_t cols, int64_t ld, rr_dtype dtype, rr
 // workgroup per row): element-aligned rows that fit row_pf_shape and at least
 // kReducePfMinRowsPerCU rows per CU.
 RowPfShape reduce_pf_shape(int64_t rows, int64_t cols, rr_op op, int32_t cu_count, bool vec);
+// Lanes per row of that shape when a wavefront takes several rows (rows of
+// up to 64 chunks: 16; up to 128: 32), else 0 (the workgroup's threads; also
+// when a step's rows, ld elements apart, would span 2^31 bytes).
+int reduce_pf_lanes(int64_t cols, int64_t ld);
 // vec: x (and y) are aligned to their element size, so the block and split-K
 // tiers take each row's body from its first 16-byte boundary in 128-bit
 // chunks; rows16: every row of x and y starts 16-byte aligned (the wave tier

@@ -145,25 +145,28 @@ __device__ __forceinline__ typename M::acc_t lift_bits(uint32_t u)
         return M::lift((typename M::in_t)u);
 }
 
-// Row r's result(s) stored by every thread, thread 0's store in range and
-// the others' past it (a store behind a branch would make the persistent
-// loop's waits count it); the three statistics' outputs may be NULL (range 0).
-__device__ __forceinline__ void store_word(void* p, uint32_t bits, bool on)
+// The results of a step's rows r0 .. r0 + nr - 1, row r0 + seg's by the
+// first lane of its segment: every thread issues the stores, through one
+// descriptor per output over the step's nr results, and the others' go past
+// the range (a store behind a branch would make the persistent loop's waits
+// count it); the three statistics' outputs may be NULL (range 0).
+__device__ __forceinline__ void store_word(void* p, int nr, uint32_t bits, int seg, bool first)
 {
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(p, 0, on ? 4 : 0,
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(p, 0, nr * 4,
                                                                         kBufferWord3);
-    __builtin_amdgcn_raw_buffer_store_b32(bits, rs, threadIdx.x == 0 ? 0 : 16, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(bits, rs, first && seg < nr ? seg * 4 : nr * 4 + 16,
+                                          0, 0);
 }
 template <class M>
-__device__ __forceinline__ void store_row_result(typename M::out_t y, int64_t r,
-                                                 typename M::acc_t a)
+__device__ __forceinline__ void store_row_results(typename M::out_t y, int64_t r0, int nr,
+                                                  int seg, bool first, typename M::acc_t a)
 {
     using T = typename M::in_t;
     uint32_t bits;
     if constexpr (std::is_pointer<typename M::out_t>::value) {
         const T res = M::finish(a);
         __builtin_memcpy(&bits, &res, 4);
-        store_word(y + r, bits, true);
+        store_word(y + r0, nr, bits, seg, first);
     } else {
         T res[3];
         M::finish3(a, res);
@@ -171,12 +174,12 @@ __device__ __forceinline__ void store_row_result(typename M::out_t y, int64_t r,
 #pragma unroll
         for (int i = 0; i < 3; ++i) {
             __builtin_memcpy(&bits, &res[i], 4);
-            store_word(outs[i] ? outs[i] + r : nullptr, bits, outs[i] != nullptr);
+            store_word(outs[i] ? outs[i] + r0 : nullptr, outs[i] ? nr : 0, bits, seg, first);
         }
     }
 }
 
-template <class M, int NCH, int NT, bool PEEL>
+template <class M, int NCH, int NT, bool PEEL, int S = NT>
 __global__ __launch_bounds__(NT) void k_reduce_rows_pf(const typename M::in_t* __restrict__ x,
                                                        typename M::out_t y, int64_t rows,
                                                        int64_t cols, int64_t ld)
@@ -184,39 +187,54 @@ __global__ __launch_bounds__(NT) void k_reduce_rows_pf(const typename M::in_t* _
     using T = typename M::in_t;
     using A = typename M::acc_t;
     static_assert(sizeof(T) == 4, "4-byte elements");
+    static_assert(S == NT || (NT == kWave && (S == 16 || S == 32)), "row segments of a wavefront");
+    constexpr int RPS = NT / S;     // rows per step
+    constexpr int NS = S * NCH;     // chunk slots per row
+    static_assert((NS & (NS - 1)) == 0, "a power-of-two slot count");
     __shared__ A slot[2][NT / kWave > 1 ? NT / kWave : 1];
-    if ((int64_t)blockIdx.x >= rows)
+    const int64_t steps = (rows + RPS - 1) / RPS;
+    if ((int64_t)blockIdx.x >= steps)
         return;
-    const int row_bytes = (int)(cols * 4);
+    const int ls = (int)threadIdx.x % S;        // lane within the row's segment
+    const int seg = (int)threadIdx.x / S;       // the segment's row within the step
+    auto slot_of = [&](int k, int q) { return (ls + k * S - q) & (NS - 1); };
+    auto live_rows = [&](int64_t g) {           // rows of step g inside the call
+        const int64_t n = rows - g * RPS;
+        return (int)(n < RPS ? n : RPS);
+    };
     persistent_rows<ReduceRowBuf<NCH>>(
-        blockIdx.x, gridDim.x, rows,
-        [&](int64_t r, bool live, ReduceRowBuf<NCH>& buf) {
-            const T* xr = x + r * ld;
-            const int64_t h = PEEL ? head_elems(xr, cols) : 0;
-            const int nbe = (int)((cols - h) & ~(int64_t)3);
-            const int bytes = live ? row_bytes : 0;
+        blockIdx.x, gridDim.x, steps,
+        [&](int64_t g, bool live, ReduceRowBuf<NCH>& buf) {
+            const int nr = live ? live_rows(g) : 0;
+            const T* x0 = x + g * RPS * ld;
+            const int range = nr > 0 ? (int)(((int64_t)nr - 1) * ld * 4 + cols * 4) : 0;
             const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-                const_cast<T*>(xr), 0, bytes, kBufferWord3);
+                const_cast<T*>(x0), 0, range, kBufferWord3);
+            const T* xr = x0 + (int64_t)seg * ld;
+            const int64_t h = PEEL ? head_elems(xr, cols) : 0;
+            const int nbe = seg < nr ? (int)((cols - h) & ~(int64_t)3) : 0;
+            const int base = (int)((int64_t)seg * ld * 4 + h * 4);
             const int q = line_phase(xr + h);
 #pragma unroll
             for (int k = 0; k < NCH; ++k) {
-                const int off = slot_chunk<NCH, NT, true>(k, q) * 16;
-                const int o = off + 16 <= nbe * 4 ? (int)h * 4 + off : bytes + 16;
+                const int off = slot_of(k, q) * 16;
+                const int o = off + 16 <= nbe * 4 ? base + off : range + 16;
                 const rr_u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, o, 0,
                                                                           kBufferNonTemporal);
                 buf.c[k] = make_uint4(v.x, v.y, v.z, v.w);
             }
             if constexpr (PEEL) {
-                // thread t < h: head element t; h <= t < h + tail: element nbe + t
-                const int64_t t = threadIdx.x, tl = cols - h - nbe;
-                const int64_t idx = t < h ? t : t < h + tl ? nbe + t : -1;
-                const int eo = idx >= 0 ? (int)idx * 4 : bytes + 16;
+                // lane l < h: head element l; h <= l < h + tail: element nbe + l
+                const int64_t t = ls, tl = cols - h - nbe;
+                const int64_t idx = seg >= nr ? -1 : t < h ? t : t < h + tl ? nbe + t : -1;
+                const int eo = idx >= 0 ? (int)((int64_t)seg * ld * 4 + idx * 4) : range + 16;
                 buf.e = __builtin_amdgcn_raw_buffer_load_b32(rs, eo, 0, kBufferNonTemporal);
             }
         },
         [] {},
-        [&](const ReduceRowBuf<NCH>& buf, int64_t r, int par) {
-            const T* xr = x + r * ld;
+        [&](const ReduceRowBuf<NCH>& buf, int64_t g, int par) {
+            const int nr = live_rows(g);
+            const T* xr = x + (g * RPS + seg) * ld;
             const int64_t h = PEEL ? head_elems(xr, cols) : 0;
             const int64_t nb = (cols - h) >> 2;
             const int q = line_phase(xr + h);
@@ -228,14 +246,18 @@ __global__ __launch_bounds__(NT) void k_reduce_rows_pf(const typename M::in_t* _
                 ck = M::combine(ck, lift_bits<M>(u.y));
                 ck = M::combine(ck, lift_bits<M>(u.z));
                 ck = M::combine(ck, lift_bits<M>(u.w));
-                acc = (int64_t)slot_chunk<NCH, NT, true>(k, q) < nb ? M::combine(acc, ck) : acc;
+                acc = (int64_t)slot_of(k, q) < nb ? M::combine(acc, ck) : acc;
             }
             if constexpr (PEEL) {
-                const int64_t t = threadIdx.x, tl = cols - h - (nb << 2);
-                if (t < h + tl)
+                const int64_t tl = cols - h - (nb << 2);
+                if (ls < h + tl)
                     acc = M::combine(acc, lift_bits<M>(buf.e));
             }
-            store_row_result<M>(y, r, block_reduce<M, NT>(acc, slot[par]));
+            if constexpr (S == NT)
+                acc = block_reduce<M, NT>(acc, slot[par]);
+            else
+                acc = segment_reduce<M, S>(acc);
+            store_row_results<M>(y, g * RPS, nr, seg, ls == 0, acc);
         });
 }
 
@@ -697,13 +719,13 @@ static rr_status launch_wave(dim3 grid, dim3 block, hipStream_t s, const typenam
 template <class M>
 static typename M::out_t outputs_of(const ReduceLaunch& a);
 
-template <class M, int NCH, int NT>
+template <class M, int NCH, int NT, int S = NT>
 static rr_status launch_rows_pf(const rr_plan& p, const ReduceLaunch& a)
 {
     const auto* x = static_cast<const typename M::in_t*>(a.x);
     const typename M::out_t y = outputs_of<M>(a);
-    auto kernel = a.rows16 && a.cols % 4 == 0 ? k_reduce_rows_pf<M, NCH, NT, false>
-                                              : k_reduce_rows_pf<M, NCH, NT, true>;
+    auto kernel = a.rows16 && a.cols % 4 == 0 ? k_reduce_rows_pf<M, NCH, NT, false, S>
+                                              : k_reduce_rows_pf<M, NCH, NT, true, S>;
     int per_cu = 0;
     if (blocks_per_cu(kernel, NT, &per_cu) != RR_OK)
         return RR_ERR_HIP;
@@ -717,10 +739,14 @@ static rr_status launch_rows_pf_shape(const rr_plan& p, const ReduceLaunch& a, R
 {
     if (sh.nt != p.block)
         return RR_ERR_TIER;  // plan and launch disagree: refuse, launch nothing
+    const int lanes = reduce_pf_lanes(a.cols, a.ld);
+    if (lanes != p.lanes_per_row)
+        return RR_ERR_TIER;
     switch (sh.nt * 16 + sh.nch) {
-    case 64 * 16 + 1: return launch_rows_pf<M, 1, 64>(p, a);
-    case 64 * 16 + 2: return launch_rows_pf<M, 2, 64>(p, a);
-    case 64 * 16 + 4: return launch_rows_pf<M, 4, 64>(p, a);
+    case 64 * 16 + 4:
+        return lanes == 16   ? launch_rows_pf<M, 4, 64, 16>(p, a)
+               : lanes == 32 ? launch_rows_pf<M, 4, 64, 32>(p, a)
+                             : launch_rows_pf<M, 4, 64>(p, a);
     case 128 * 16 + 4: return launch_rows_pf<M, 4, 128>(p, a);
     case 256 * 16 + 4: return launch_rows_pf<M, 4, 256>(p, a);
     case 512 * 16 + 4: return launch_rows_pf<M, 4, 512>(p, a);

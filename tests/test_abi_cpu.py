@@ -64,17 +64,19 @@ def test_plain_c_consumer_compiles_links_and_runs(tmp_path):
     assert re.search(r"attention workspace 0 \d+ 1024\b", out), out
 
 
-@pytest.mark.parametrize("rows,cols,op,block,grid", [
-    (65536, 1000, "sum", 64, 4096),       # 250 chunks: 64 threads x 4, 16 per CU
-    (1024, 8192, "max", 512, 512),        # 2048 chunks: 512 threads x 4, 2 per CU
-    (20000, 65, "min", 64, 16384),        # 17 chunks: 64 threads x 1, 64 per CU
-    (1023, 1000, "sum", 256, 1023),       # fewer than 4 rows per CU: a workgroup per row
-    (65536, 8193, "sum", 256, 65536),     # beyond 2048 chunks
-    (65536, 1000, "sum_max_min", 64, 4096),   # the three statistics alike
+@pytest.mark.parametrize("rows,cols,op,block,lanes,grid", [
+    (65536, 1000, "sum", 64, 0, 4096),    # 250 chunks: 64 threads x 4, 16 per CU
+    (1024, 8192, "max", 512, 0, 512),     # 2048 chunks: 512 threads x 4, 2 per CU
+    (20000, 65, "min", 64, 16, 4096),     # 17 chunks: 16 lanes x 4 per row, 4 rows a step
+    (6000, 500, "sum", 64, 32, 3000),     # 125 chunks: 32 lanes x 4 per row, 2 rows a step
+    (1023, 1000, "sum", 256, 0, 1023),    # fewer than 4 rows per CU: a workgroup per row
+    (65536, 8193, "sum", 256, 0, 65536),  # beyond 2048 chunks
+    (65536, 1000, "sum_max_min", 64, 0, 4096),   # the three statistics alike
 ])
-def test_block_tier_reduce_persistent_plan(rows, cols, op, block, grid):
+def test_block_tier_reduce_persistent_plan(rows, cols, op, block, lanes, grid):
     p = rr.plan_reduce(rows, cols, torch.float32, op, cu_count=256)
-    assert (p["tier"], p["block"], p["grid"]) == ("block", block, grid), p
+    assert (p["tier"], p["block"], p["lanes_per_row"], p["grid"]) == \
+        ("block", block, lanes, grid), p
 
 
 def test_status_strings_are_distinct():

@@ -118,7 +118,9 @@ PF_REDUCE_SHAPES = [  # rows, cols, pad, offset
     (5000, 1000, 0, 0), (5000, 1001, 0, 0), (3000, 2048, 4, 0), (1100, 4095, 0, 2),
     (1030, 8192, 0, 0), (1030, 8191, 1, 1),
     # rows shorter than a chunk (head and tail elements only), forced to the block tier
-    (20000, 1, 0, 1), (20000, 3, 1, 2), (20000, 5, 0, 3), (20000, 7, 2, 1)]
+    (20000, 1, 0, 1), (20000, 3, 1, 2), (20000, 5, 0, 3), (20000, 7, 2, 1),
+    # 2 and 4 rows per wavefront, with a last step that has fewer rows
+    (20001, 300, 0, 1), (20003, 120, 0, 0), (20002, 96, 3, 2), (20001, 512, 0, 0)]
 
 
 def _pf_threads(cols):
