@@ -423,7 +423,9 @@ __global__ __launch_bounds__(kBlockThreads, (attn_workgroups_per_cu<D, FUSED>())
     }
     const int lane = lane_id();
     const int hf = lane / 32;
-    const int wave = threadIdx.x / kWave;
+    // wave-uniform by construction; said so, so that the per-wavefront O
+    // descriptor below is a scalar one (no loop over lanes' descriptors)
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t qrow = (int64_t)qt * kAttnRows + wave * 32 + lane % 32;
     const bool row_ok = qrow < nq;
     const int64_t row = prow0 + qrow * rs;
