@@ -752,8 +752,15 @@ def main():
         reps = max(K, 10)
         evs = {n: [] for n in next_names}
         for n in next_names:
-            for i in range(max(args.warmup, 1)):
+            # warmup: at least --warmup launches and 20 ms of them, so that the
+            # clocks have settled for the op before its timed launches
+            t_w, i = time.perf_counter(), 0
+            while i < max(args.warmup, 1) or time.perf_counter() - t_w < 0.02:
                 next_ops[n](i)
+                i += 1
+                if i % 4 == 0:
+                    torch.cuda.synchronize()
+            torch.cuda.synchronize()
             for i in range(reps):
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record(stream)
