@@ -349,7 +349,17 @@ __device__ __forceinline__ void ln_row_from_chunks(const uint4* raw, YT* yr, int
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
         if constexpr (AFF) {
-            map.template chunk<E>(v + k * E, gw + k * E, bw + k * E);
+            // the weights pass through an empty asm per row, so that their
+            // conversions to double are not hoisted out of the row loop
+            // (that kept 2 x NCH x E doubles live: spills at 512 threads)
+            float gl[E], bl[E];
+#pragma unroll
+            for (int i = 0; i < E; ++i) {
+                gl[i] = gw[k * E + i];
+                bl[i] = bw[k * E + i];
+                __asm__ volatile("" : "+v"(gl[i]), "+v"(bl[i]));
+            }
+            map.template chunk<E>(v + k * E, gl, bl);
         } else {
             float ones[E], zeros[E];
 #pragma unroll

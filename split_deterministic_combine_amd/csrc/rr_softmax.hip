@@ -32,12 +32,21 @@ constexpr float kNegInf = -__builtin_inff();
 // different in every thread).  The hardware exponential is exact for normal
 // results; when any argument falls below -126 (a subnormal or vanishing
 // result, or a -inf entry) the thread takes exp2_sub, which scales such
-// arguments into the normal range.  m is the thread's maximum.  live(i):
+// arguments into the normal range.  m is the thread's maximum.  live(i, t):
 // whether value i is a row element; the others (-inf padding, whose
 // exponential the hardware gives as 0 exactly) leave the range check alone,
-// so padding alone does not send a thread to the slow path.
+// so padding alone does not send a thread to the slow path.  It is given
+// i and the exponent argument t of value i.
 struct AllLive {
-    __device__ bool operator()(int) const { return true; }
+    __device__ bool operator()(int, float) const { return true; }
+};
+// Every -inf value treated as padding: both exponentials give exactly 0 for
+// it, and on arguments down to -126 they agree bit for bit, so a thread
+// whose only low arguments are -inf may take the hardware path.  A test on
+// the value, where a test on the position would cost 64-bit index
+// arithmetic per element.
+struct FiniteLive {
+    __device__ bool operator()(int, float t) const { return t != kNegInf; }
 };
 template <int N, class Live = AllLive>
 __device__ __forceinline__ MS exp_sum_from(float* v, float m, Live live = Live())
@@ -48,7 +57,7 @@ __device__ __forceinline__ MS exp_sum_from(float* v, float m, Live live = Live()
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             v[i] = (v[i] - m) * kLog2e;
-            tmin = fminf(tmin, live(i) ? v[i] : 0.0f);
+            tmin = fminf(tmin, live(i, v[i]) ? v[i] : 0.0f);
         }
         if (tmin >= -126.0f) {
 #pragma unroll
@@ -155,9 +164,7 @@ __global__ __launch_bounds__(NT) void k_softmax_block(const XT* __restrict__ x,
         const bool has_e = (int64_t)threadIdx.x < h;
         const float e = has_e ? XIn<XT>::one(xr + threadIdx.x) : kNegInf;
         float pe;
-        const MS own = local_exp_sum_plus<NCH * E>(v, e, &pe, [&](int i) {
-            return ((int64_t)threadIdx.x + (int64_t)(i / E) * NT) * E + i % E < cb;
-        });
+        const MS own = local_exp_sum_plus<NCH * E>(v, e, &pe, FiniteLive());
         float e_t;
         const MS tot = block_softmax_stats<NT>(own, slot[par], &e_t);
         par ^= 1;
@@ -214,7 +221,7 @@ __device__ __forceinline__ void softmax_row_from_chunks(const RowBuf<NCH>& buf, 
         }
     }
     float pe = 0.0f;
-    const auto live = [&](int i) { return ok[i / E]; };
+    const auto live = [&](int i, float) { return ok[i / E]; };
     const MS own = PEEL ? local_exp_sum_plus<NCH * E>(v, buf.e, &pe, live)
                         : local_exp_sum<NCH * E>(v, live);
     float e_t;
@@ -354,7 +361,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_softmax_wave(const XT* __rest
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const MS own = local_exp_sum<E>(v[u], [&](int i) { return j0 + i < cols; });
+            const MS own = local_exp_sum<E>(v[u], [&](int i, float) { return j0 + i < cols; });
             const MS tot = segment_reduce<SoftmaxMS, S>(own);
             const float sc = exp2_f32((own.m - tot.m) * kLog2e) / tot.s;
 #pragma unroll
