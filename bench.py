@@ -27,7 +27,10 @@ to the next so that the data touched by consecutive launches exceeds the
 `value` is whole-step throughput in GB/s: algorithmic bytes of all launches
 (each input element read once, each output written once) divided by the
 measured step time.  Per-launch durations come from HIP events recorded on
-the stream the kernels are launched on.
+the stream the kernels are launched on; each operation's GB/s is taken from
+its median launch, the roofline's from the dominant kernel's mean launch in
+the timed region, and each next-row operation also reports its launches run
+back to back between one pair of events (the sustained rate).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -736,11 +739,14 @@ def main():
     for n in names:
         ts = sorted(dom_ms if n == dom else brk[n])
         mean = sum(ts) / len(ts)
-        per_op[n] = {"ms_mean": round(mean, 5), "ms_median": round(ts[len(ts) // 2], 5),
+        med = ts[len(ts) // 2]
+        # rates from the median launch (mean, min and p90 beside it); the
+        # roofline below divides by the mean launch instead
+        per_op[n] = {"ms_mean": round(mean, 5), "ms_median": round(med, 5),
                      "ms_min": round(ts[0], 5),
                      "ms_p90": round(ts[min(len(ts) - 1, (9 * len(ts)) // 10)], 5), "bytes": B[n],
-                     "GBps": round(B[n] / (mean * 1e-3) / 1e9, 1),
-                     "pct_peak": round(100 * B[n] / (mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 1),
+                     "GBps": round(B[n] / (med * 1e-3) / 1e9, 1),
+                     "pct_peak": round(100 * B[n] / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 1),
                      "timed_in": "timed region" if n == dom else "instrumented pass"}
     # Operations outside the step: each timed alone with HIP events on the
     # stream -- its warmup launches, then its timed launches in a row (every
@@ -751,6 +757,7 @@ def main():
         log("timing next-row operations")
         reps = max(K, 10)
         evs = {n: [] for n in next_names}
+        run_evs = {}
         for n in next_names:
             # warmup: at least --warmup launches and 20 ms of them, so that the
             # clocks have settled for the op before its timed launches
@@ -767,14 +774,28 @@ def main():
                 next_ops[n](i)
                 b.record(stream)
                 evs[n].append((a, b))
+            # then the same launches back to back between one pair of events:
+            # the sustained rate (no event between launches; clocks under
+            # continuous load)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for i in range(reps):
+                next_ops[n](i)
+            b.record(stream)
+            run_evs[n] = (a, b)
             torch.cuda.synchronize()
         for n in next_names:
             ts = sorted(a.elapsed_time(b) for a, b in evs[n])
             mean = sum(ts) / len(ts)
-            gbs = NEXT_BYTES[n] / (mean * 1e-3) / 1e9
-            next_rows[n] = {"ms_mean": round(mean, 5), "ms_median": round(ts[len(ts) // 2], 5),
+            med = ts[len(ts) // 2]
+            gbs = NEXT_BYTES[n] / (med * 1e-3) / 1e9
+            run_ms = run_evs[n][0].elapsed_time(run_evs[n][1]) / reps
+            next_rows[n] = {"ms_mean": round(mean, 5), "ms_median": round(med, 5),
                             "ms_min": round(ts[0], 5), "bytes": NEXT_BYTES[n],
-                            "GBps": round(gbs, 1), "pct_peak": round(100 * gbs / PEAK_HBM_GBS, 1)}
+                            "GBps": round(gbs, 1), "pct_peak": round(100 * gbs / PEAK_HBM_GBS, 1),
+                            "ms_back_to_back": round(run_ms, 5),
+                            "pct_peak_back_to_back": round(
+                                100 * NEXT_BYTES[n] / (run_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 1)}
         cu = rr.device_cu_count()
         if "axis_cols" in next_rows:
             pa = rr.plan_axis(1, 16384, 16384, torch.float32, "sum", cu_count=cu)
@@ -795,7 +816,7 @@ def main():
                 "kernels": [KERNEL_OF_OP["layernorm"]]})
         if "attention" in next_rows:
             ab, ah, asq, ad, an, ap = ATTN
-            t_s = next_rows["attention"]["ms_mean"] * 1e-3
+            t_s = next_rows["attention"]["ms_median"] * 1e-3
             next_rows["attention"].update({
                 "config": "split-K attention partials: bf16 q [%d, %d, %d, %d], k and v over %d "
                           "keys in %d partitions -> float32 O, m, l (matrix cores, "
@@ -806,7 +827,7 @@ def main():
                 "pct_peak_bf16_mfma": round(100 * _attn_flops() / t_s / 2.5e15, 1)})
         if "attention_varlen" in next_rows:
             ab, ah, asq, ad, an, ap = ATTN
-            t_s = next_rows["attention_varlen"]["ms_mean"] * 1e-3
+            t_s = next_rows["attention_varlen"]["ms_median"] * 1e-3
             next_rows["attention_varlen"].update({
                 "config": "split-K attention partials of %d packed sequences of %d queries, key "
                           "lengths %s, %d heads of depth %d, %d partitions per sequence -> float32 "
@@ -817,10 +838,10 @@ def main():
                 "TFLOPs": round(_attn_flops() / t_s / 1e12, 1)})
             if "attention" in next_rows:
                 next_rows["attention_varlen"]["frac_of_dense"] = round(
-                    next_rows["attention"]["ms_mean"] / next_rows["attention_varlen"]["ms_mean"], 4)
+                    next_rows["attention"]["ms_median"] / next_rows["attention_varlen"]["ms_median"], 4)
         if "attention_merged" in next_rows:
             ab, ah, asq, ad, an, ap = ATTN
-            t_s = next_rows["attention_merged"]["ms_mean"] * 1e-3
+            t_s = next_rows["attention_merged"]["ms_median"] * 1e-3
             next_rows["attention_merged"].update({
                 "config": "split-K attention end to end: the partials above, then their LSE merge "
                           "into bf16 [%d, %d, %d, %d] (two launches)" % (ab, ah, asq, ad),
@@ -831,7 +852,7 @@ def main():
                               "partials (130 MiB) go through HBM between the launches"})
         if "attention_fused" in next_rows:
             ab, ah, asq, ad, an, ap = ATTN
-            t_s = next_rows["attention_fused"]["ms_mean"] * 1e-3
+            t_s = next_rows["attention_fused"]["ms_median"] * 1e-3
             next_rows["attention_fused"].update({
                 "config": "split-K attention in one launch: the partials of every (head, 128 "
                           "query rows) folded in partition order by the last of its %d "
@@ -915,7 +936,9 @@ def main():
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
     # dominant kernel: the launch with the largest share of the step
-    achieved = per_op[dom]["GBps"]
+    # achieved: algorithmic bytes over the dominant kernel's mean launch
+    # duration in the timed region (HIP events on its stream)
+    achieved = round(B[dom] / (per_op[dom]["ms_mean"] * 1e-3) / 1e9, 1)
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
