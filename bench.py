@@ -81,8 +81,8 @@ KERNEL_OF_OP = {
     "attention_varlen": "k_attn_staged<128, 32, 3, false, float, true>",
     # rows at every offset from a 16-byte boundary and their aligned neighbour
     "sum_47": "k_reduce_wave<rr::SumF32, 4, 16, 2>",
-    "sum_1001": "k_reduce_rows_pf<rr::SumF32, 4, 64, true>",
-    "sum_1000": "k_reduce_rows_pf<rr::SumF32, 4, 64, false>",
+    "sum_1001": "k_reduce_rows_pf<rr::SumF32, 4, 64, true, 64>",
+    "sum_1000": "k_reduce_rows_pf<rr::SumF32, 4, 64, false, 64>",
     "softmax_8191": "k_softmax_rows_pf<unsigned short, unsigned short, 4, 256, false, true, true>",
     # reference streams of known size (not ops of the step): rr_test_stream;
     # launches of one kernel at two sizes are told apart by their bytes
