@@ -273,11 +273,11 @@ def ingest_counters(trace_dir, fetch_dir, write_dir):
     prof = os.path.dirname(TRAFFIC_FILE)
     with open(os.path.join(prof, "kernels_rowwise_suite.md"), "w") as f:
         f.write("# Kernel durations, row-wise suite (one MI355X)\n\n"
-                "Command (from the repository root on the GPU host):\n\n"
+                "Command (`R` the repository root, `OUT` an output directory):\n\n"
                 "    cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -f csv "
-                "-d $R/gpurun_out/prof_trace -o trace -- python3 $R/bench.py\n\n"
-                "with `R` the repository root; summarised by `python bench.py --ingest-counters "
-                "gpurun_out/prof_trace gpurun_out/prof_fetch gpurun_out/prof_write`.\n"
+                "-d $OUT/prof_trace -o trace -- python3 $R/bench.py\n\n"
+                "summarised by `python bench.py --ingest-counters "
+                "$OUT/prof_trace $OUT/prof_fetch $OUT/prof_write`.\n"
                 "GB/s = algorithmic bytes per launch / average kernel duration (the "
                 "trace's per-dispatch times).\n\n" + table + "\n")
     tl = ["| op | kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (scaled) | algorithmic bytes | ratio |",
@@ -289,12 +289,13 @@ def ingest_counters(trace_dir, fetch_dir, write_dir):
     cal = out["calibration"]
     with open(os.path.join(prof, "traffic_rowwise_suite.md"), "w") as f:
         f.write("# HBM traffic per launch, row-wise suite (one MI355X)\n\n"
-                "Two counter passes, one counter each (from the repository root `R`):\n\n"
+                "Two counter passes, one counter each (`R` the repository root, `OUT` an "
+                "output directory):\n\n"
                 "    cd /tmp && export TMPDIR=/tmp && timeout -s KILL 240 rocprofv3 --pmc FETCH_SIZE "
-                "-f csv -d $R/gpurun_out/prof_fetch -o fetch -- python3 $R/bench.py --steps 2 "
+                "-f csv -d $OUT/prof_fetch -o fetch -- python3 $R/bench.py --steps 2 "
                 "--warmup 1 --no-cpu-baseline --no-parity --calibrate-copy\n"
                 "    cd /tmp && export TMPDIR=/tmp && timeout -s KILL 240 rocprofv3 --pmc WRITE_SIZE "
-                "-f csv -d $R/gpurun_out/prof_write -o write -- python3 $R/bench.py --steps 2 "
+                "-f csv -d $OUT/prof_write -o write -- python3 $R/bench.py --steps 2 "
                 "--warmup 1 --no-cpu-baseline --no-parity --calibrate-copy\n\n"
                 "Counters are KiB per dispatch (mean over dispatches).  `--calibrate-copy` runs a "
                 "plain elementwise pass (torch `neg`) that reads and writes %d bytes; its readings "
@@ -328,20 +329,21 @@ def sq_summary(op, dirs):
                 vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
     cmds = "\n".join(
         "    cd /tmp && export TMPDIR=/tmp && timeout -s KILL 120 rocprofv3 --pmc %s -f csv "
-        "-d $R/gpurun_out/sq_%s_%d -o sq -- python3 $R/bench.py --only %s --steps 3 --warmup 0 "
+        "-d $OUT/sq_%s_%d -o sq -- python3 $R/bench.py --only %s --steps 3 --warmup 0 "
         "--no-parity --no-cpu-baseline" % (" ".join(c), op, i, op) for i, c in enumerate(SQ_PASSES))
     rows = ["| counter | mean per dispatch | dispatches |", "|---|---|---|"]
     for k in sorted(vals):
         rows.append("| %s | %.4g | %d |" % (k, sum(vals[k]) / len(vals[k]), len(vals[k])))
     path = os.path.join(os.path.dirname(TRAFFIC_FILE), "counters_%s.md" % op)
     with open(path, "w") as f:
-        f.write("# SQ counters, `%s` (%s, one MI355X)\n\nTwo counter passes from the repository "
-                "root `R`:\n\n%s\n\nsummarised by `python bench.py --sq-summary %s DIR DIR`. "
+        f.write("# SQ counters, `%s` (%s, one MI355X)\n\nTwo counter passes (`R` the repository "
+                "root, `OUT` an output directory):\n\n%s\n\nsummarised by `python bench.py "
+                "--sq-summary %s $OUT/sq_%s_0 $OUT/sq_%s_1`. "
                 "Values as rocprofv3 reports them per dispatch (accumulated over the chip); "
                 "read them as ratios of one another (bank-conflict cycles against LDS-active "
                 "cycles, waiting against wave cycles, instructions per dispatch)."
-                "\n\n%s\n\nKernel sources hash: `%s`.\n" % (pat, op, cmds, op, "\n".join(rows),
-                                                             kernel_source_hash()))
+                "\n\n%s\n\nKernel sources hash: `%s`.\n" % (pat, op, cmds, op, op, op,
+                                                             "\n".join(rows), kernel_source_hash()))
     return path
 
 
