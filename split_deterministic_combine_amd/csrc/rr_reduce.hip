@@ -811,12 +811,14 @@ rr_status launch_reduce(const rr_plan& p, const ReduceLaunch& a)
         case RR_SUM: return launch_monoid<SumF32>(p, a);
         case RR_MAX: return launch_monoid<MaxF32>(p, a);
         case RR_MIN: return launch_monoid<MinF32>(p, a);
+        default: return RR_ERR_OP;  // the three statistics take the multi path above
         }
     } else if (a.dtype == RR_I32) {
         switch (a.op) {
         case RR_SUM: return launch_monoid<SumI32>(p, a);
         case RR_MAX: return launch_monoid<MaxI32>(p, a);
         case RR_MIN: return launch_monoid<MinI32>(p, a);
+        default: return RR_ERR_OP;
         }
     }
     return RR_ERR_DTYPE;
