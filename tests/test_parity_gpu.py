@@ -160,6 +160,24 @@ def test_int_results_identical_across_tiers():
             assert_exact(o, outs[0], op)
 
 
+@pytest.mark.parametrize("rows,cols", [(37, 4097), (3, 70001), (600, 48)])
+def test_int_results_invariant_under_column_permutation(rows, cols):
+    """The combine is associative and commutative for int32 sum (wrapping),
+    max and min ("cluster_allreduce", description of combine_fn), so a row
+    and its columns in any order give the same bits, on every tier."""
+    x = synth.ints_i32(31 + cols, (rows, cols), -(2 ** 31), 2 ** 31 - 1)
+    xp = np.ascontiguousarray(x[:, np.random.default_rng(cols).permutation(cols)])
+    tiers = ["auto", "block", "tiled", "splitk"] + (["wave"] if cols <= 64 else [])
+    if cols <= 4096:
+        tiers.append("serial")
+    for op in ("sum", "max", "min"):
+        ref = oracle.reduce_rows(x, op)
+        for t in tiers:
+            a, b = _run_reduce(x, op, t), _run_reduce(xp, op, t)
+            assert_exact(a, ref, "%s %s" % (op, t))
+            assert_exact(b, a, "%s %s permuted" % (op, t))
+
+
 def test_reduce_rows_zero_is_noop_and_empty_rows_get_identity():
     g = torch.zeros((0, 16), device="cuda")
     assert rr.reduce_rows(g).shape == (0,)
