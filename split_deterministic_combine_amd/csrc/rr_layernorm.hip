@@ -425,8 +425,9 @@ __global__ __launch_bounds__(NT) void k_layernorm_rows_pf(
 // so that the lanes of a chunk read (E columns apart) fall in distinct
 // banks -- and each row reads its columns there; else from global memory
 // (whole 16-byte words at any element alignment; every row reads the same
-// vectors, which stay in the caches).
-template <class XT, class YT, int NCH, int NT, bool LDSW>
+// vectors, which stay in the caches).  AFF false: the call has neither
+// gamma nor beta, and the kernel holds no weight code.
+template <class XT, class YT, int NCH, int NT, bool LDSW, bool AFF>
 __global__ __launch_bounds__(NT) void k_layernorm_rows_peel(
     const XT* __restrict__ x, YT* __restrict__ y, Weights g, Weights b, float* mean_out,
     float* rstd_out, int64_t rows, int64_t cols, int64_t ldx, int64_t ldy, float eps)
@@ -462,7 +463,19 @@ __global__ __launch_bounds__(NT) void k_layernorm_rows_peel(
 #pragma unroll
             for (int k = 0; k < NCH; ++k)
                 ok[k] = (int64_t)slot_chunk<NCH, NT, true>(k, q) * E < pg.nbe;
-            if constexpr (!LDSW) {
+            if constexpr (!AFF) {
+                // no gamma or beta: 1 and 0, and no weight code in the kernel
+                // (the dispatch over weight types and alignments, compiled in
+                // and skipped, had cost 13 us at [16384, 4095])
+                (void)we;
+#pragma unroll
+                for (int i = 0; i < NCH * E; ++i) {
+                    gw[i] = 1.0f;
+                    bw[i] = 0.0f;
+                }
+                ge = 1.0f;
+                be = 0.0f;
+            } else if constexpr (!LDSW) {
                 // the row's weights first, so that their loads are in flight
                 // while the statistics are formed
                 const Weights gh = shifted(g, pg.h), bh = shifted(b, pg.h);
@@ -1029,8 +1042,9 @@ static rr_status launch_pf(const XT* x, YT* y, const Weights& g, const Weights& 
         const int64_t wbytes =
             2 * (a.cols + a.cols / XIn<XT>::kChunk + 1) * (int64_t)sizeof(float);
         const bool ldsw = (g.p || b.p) && wbytes <= kLnLdsWeightBytes;
-        auto kernel = ldsw ? k_layernorm_rows_peel<XT, YT, NCH, NT, true>
-                           : k_layernorm_rows_peel<XT, YT, NCH, NT, false>;
+        auto kernel = ldsw ? k_layernorm_rows_peel<XT, YT, NCH, NT, true, true>
+                      : (g.p || b.p) ? k_layernorm_rows_peel<XT, YT, NCH, NT, false, true>
+                                     : k_layernorm_rows_peel<XT, YT, NCH, NT, false, false>;
         const size_t lds = ldsw ? (size_t)((wbytes + 1023) / 1024 * 1024) : 0;
         int per_cu = 0;
         if (blocks_per_cu(kernel, NT, &per_cu, lds) != RR_OK)
