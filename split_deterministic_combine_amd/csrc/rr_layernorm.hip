@@ -420,10 +420,10 @@ __global__ __launch_bounds__(NT) void k_layernorm_rows_pf(
 // in chunk slots rotated onto 128-byte lines, one head or tail element per
 // thread).  A thread's columns then move with the row's phase, so gamma and
 // beta are read per row at the body's columns.  LDSW: the workgroup first
-// copies them, as float, into LDS, column c of gamma at word c + c / E and
-// of beta as many words further on -- one pad word after every E columns,
-// so that the lanes of a chunk read (E columns apart) fall in distinct
-// banks -- and each row reads its columns there; else from global memory
+// copies them, as float, into LDS, column c's (gamma, beta) pair at pair
+// c + c / E -- one pad pair after every E columns, so that the lanes of a
+// chunk read (E columns apart) fall in distinct banks -- and each row reads
+// its columns there, one 8-byte read per column; else from global memory
 // (whole 16-byte words at any element alignment; every row reads the same
 // vectors, which stay in the caches).  AFF false: the call has neither
 // gamma nor beta, and the kernel holds no weight code.
@@ -434,15 +434,13 @@ __global__ __launch_bounds__(NT) void k_layernorm_rows_peel(
 {
     constexpr int E = XIn<XT>::kChunk;
     __shared__ double slot[2][NT / kWave];
-    extern __shared__ float ldsw[];
+    extern __shared__ float2 ldsw[];
     if ((int64_t)blockIdx.x >= rows)
         return;
     const StatsOut so(mean_out, rstd_out, rows);
-    const uint32_t bw0 = (uint32_t)(cols + cols / E);  // beta's first word
     if constexpr (LDSW) {
         for (uint32_t j = threadIdx.x; j < (uint32_t)cols; j += NT) {
-            ldsw[j + j / E] = weight_one(g, j);
-            ldsw[bw0 + j + j / E] = weight_one(b, j);
+            ldsw[j + j / E] = make_float2(weight_one(g, j), weight_one(b, j));
         }
         __syncthreads();
     }
@@ -506,10 +504,10 @@ __global__ __launch_bounds__(NT) void k_layernorm_rows_peel(
                 v, cols, eps, slot[0], slot[1], [&](int k, int) { return ok[k]; }, &e, has_e);
             so.write(r, st);
             if constexpr (LDSW) {
-                // columns h + j0 + i of the body's chunks (j0 = m E): words
+                // columns h + j0 + i of the body's chunks (j0 = m E): pairs
                 // h + j0 + m + i, plus one where h + i passes E (the same
                 // for every chunk of the row); slots past the body read
-                // from word 0 (never stored); then the head or tail element
+                // from pair 0 (never stored); then the head or tail element
                 const uint32_t h = (uint32_t)pg.h;
 #pragma unroll
                 for (int k = 0; k < NCH; ++k) {
@@ -518,13 +516,15 @@ __global__ __launch_bounds__(NT) void k_layernorm_rows_peel(
 #pragma unroll
                     for (int i = 0; i < E; ++i) {
                         const uint32_t w = w0 + i + (h + i >= (uint32_t)E ? 1u : 0u);
-                        gw[k * E + i] = ldsw[w];
-                        bw[k * E + i] = ldsw[bw0 + w];
+                        const float2 gb = ldsw[w];
+                        gw[k * E + i] = gb.x;
+                        bw[k * E + i] = gb.y;
                     }
                 }
                 const uint32_t wc = (uint32_t)we + (uint32_t)we / E;
-                ge = ldsw[wc];
-                be = ldsw[bw0 + wc];
+                const float2 gbe = ldsw[wc];
+                ge = gbe.x;
+                be = gbe.y;
             }
             const LnMap<YT> map{st.mean, st.rstd};
 #pragma unroll
@@ -1036,9 +1036,9 @@ static rr_status launch_pf(const XT* x, YT* y, const Weights& g, const Weights& 
                            const rr_plan& p, const LayernormLaunch& a)
 {
     if (!(a.rows16 && a.cols % XIn<XT>::kChunk == 0)) {
-        // gamma and beta (when given) through LDS when both fit: cols words
-        // each plus one pad word per chunk, rounded up to 1 KiB (the occupancy
-        // query takes the same size as the launch)
+        // gamma and beta (when given) through LDS when both fit: a (gamma,
+        // beta) pair per column plus one pad pair per chunk, rounded up to
+        // 1 KiB (the occupancy query takes the same size as the launch)
         const int64_t wbytes =
             2 * (a.cols + a.cols / XIn<XT>::kChunk + 1) * (int64_t)sizeof(float);
         const bool ldsw = (g.p || b.p) && wbytes <= kLnLdsWeightBytes;
